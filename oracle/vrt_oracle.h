@@ -1,0 +1,124 @@
+/* CPU oracle for draft-tree construction and lossless tree verification.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library. It shares no code,
+ * header, table or constant generator with the HIP path; it is written from
+ * the method's definition:
+ *   - RheoSampling (NeurIPS 2026 paper notes): key design 1 (top-128 truncation
+ *     of the draft logits), key design 2 (dual-identity slot fill, proxy
+ *     probability, the local-ranking lemma), key design 3 (probe-first
+ *     optimal-transport verification, residual recursion, final residual
+ *     sample), and the training-free settings paragraph (raw probabilities
+ *     for ranking, temperature for the probe draw and verification).
+ *   - SMART (ECCV 2026 paper notes): key designs 1-3 (speedup objective, cost
+ *     models, marginal keep rule with discount alpha), framework flowchart
+ *     (layer-wise greedy loop).
+ *
+ * Precision: sampling quantities (tempered draft probabilities, target
+ * probabilities, residuals, CDFs) are fp64. Ranking quantities (untempered
+ * draft probabilities, proxies, path scores) follow a fixed fp32 recipe so
+ * that tree topology is a well-defined integer result: exp via exp_rank (a
+ * Cody-Waite reduction plus degree-7 Taylor polynomial, pinned against the
+ * fp64 exponential), 128-wide pairwise sums, IEEE division, no contraction.
+ *
+ * Parity pins: every function is pinned by the tests in tests/test_oracle_*.py
+ * (Philox known-answer vectors, exp_rank error bound, support vs lexsort,
+ * the lemma, chi-square losslessness, closed-form acceptance, the textbook
+ * speculative-sampling case, the identity case, the T->0 limit). The SMART
+ * keep rule's readings (|P| = leaf count, L starts at 0, |T| counts the root)
+ * are pinned only by hand-worked cases: parity unpinned beyond those.
+ */
+#ifndef VRT_ORACLE_H
+#define VRT_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ORC_ROOT = 0, ORC_DET = 1, ORC_PROBE = 2, ORC_FILL = 3 };
+enum { ORC_TOPR = 0, ORC_SMART = 1 };
+enum { ORC_PURPOSE_PROBE = 1, ORC_PURPOSE_TEST = 2, ORC_PURPOSE_FINAL = 3 };
+#define ORC_MAXSUP 1024
+#define ORC_EXEMPT_BAND 1e-6
+
+typedef struct {
+  int32_t V, trunc, K, m, probe, D, W, R, mode, budget;
+  float T, eps_m0;
+  double alpha, lambda_, gamma_, delta_, rho_;
+} orc_cfg;
+
+/* One candidate: a child created by one expansion. */
+typedef struct {
+  int32_t token, parent, depth, kind, slot, row, live;
+  float score;
+} orc_cand;
+
+/* One expansion of a node over its draft row. */
+typedef struct {
+  int32_t node; /* creation index of the expanded node, -1 for the root */
+  int32_t n_sup, probe_rank, n_child, exempt, flags;
+  int32_t sup_id[ORC_MAXSUP];
+  float sup_logit[ORC_MAXSUP];
+  float q_raw[ORC_MAXSUP];
+  double q_T[ORC_MAXSUP];
+  float z_raw, proxy;
+  double z_T, u;
+} orc_exp;
+
+typedef struct orc_tree orc_tree;
+
+/* Per-node verification outcome. */
+typedef struct {
+  int32_t accept;  /* accepted child (node index) or -1 */
+  int32_t token;   /* residual/bonus token if accept == -1, else -1 */
+  int32_t exempt;  /* number of draws at this node within the exemption band */
+  int32_t n_tests; /* number of uniforms consumed by accept/reject tests */
+  double W;        /* residual mass when the final sample was taken (1 at a leaf) */
+} orc_node_out;
+
+void orc_philox(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]);
+double orc_uniform(uint64_t seed, uint32_t idx, uint32_t b, uint32_t step, uint32_t purpose);
+float orc_exp_rank(float x);
+void orc_exp_rank_array(const float* x, float* y, int64_t n);
+float orc_pairwise128(const float* v);
+int32_t orc_support(const float* row, int32_t V, int32_t trunc, int32_t* ids, float* vals);
+
+orc_tree* orc_tree_create(const orc_cfg* cfg, uint64_t seed, int32_t b, uint32_t step);
+void orc_tree_free(orc_tree* t);
+int32_t orc_expand_layer(orc_tree* t, int32_t layer, const float* rows, int64_t ld);
+int32_t orc_frontier(const orc_tree* t, int32_t* cand_out);
+int32_t orc_finish(orc_tree* t);
+int32_t orc_n_cand(const orc_tree* t);
+const orc_cand* orc_cands(const orc_tree* t);
+int32_t orc_n_rows(const orc_tree* t);
+const orc_exp* orc_row(const orc_tree* t, int32_t row);
+int32_t orc_layer_base(const orc_tree* t, int32_t layer);
+int32_t orc_row_base(const orc_tree* t, int32_t layer);
+int32_t orc_n_exempt(const orc_tree* t);
+int32_t orc_flags(const orc_tree* t);
+
+/* Verification view of the emitted tree. Arrays have n_nodes entries, node 0
+ * is the root; child lists are in slot order; tail tables hold (token, q~) of
+ * the probe's tail for nodes whose probe child is kept (tail_n = 0 otherwise). */
+int32_t orc_tree_view(const orc_tree* t, int32_t cap, int32_t tail_cap, int32_t* n_nodes,
+                      int32_t* token, int32_t* parent, int32_t* depth, int32_t* kind,
+                      int32_t* cand, int32_t* child_off, int32_t* child, int32_t* tail_n,
+                      int32_t* tail_id, double* tail_q);
+
+int32_t orc_verify(const orc_cfg* cfg, int32_t n_nodes, const int32_t* token, const int32_t* parent,
+                   const int32_t* depth, const int32_t* kind, const int32_t* child_off,
+                   const int32_t* child, const int32_t* tail_n, const int32_t* tail_id,
+                   const double* tail_q, int32_t tail_cap, const float* target, int64_t ld,
+                   uint64_t seed, int32_t b, uint32_t step, int32_t* out_tokens,
+                   int32_t* out_nodes, int32_t* out_len, orc_node_out* per_node);
+
+int32_t orc_table_trials(const orc_cfg* cfg, int32_t max_len, const float* draft_tab,
+                         const float* target_tab, uint64_t seed, int32_t b, uint32_t step0,
+                         int32_t n_trials, int32_t two, int32_t* out, int32_t* n_first,
+                         int32_t* n_exempt);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

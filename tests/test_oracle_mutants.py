@@ -1,0 +1,113 @@
+"""The pins have power: each test plants one plausible mistake in a copy of the
+oracle's source (on the CPU), builds it, and checks that a pin now fails while
+the unmodified oracle passes the same check."""
+import os
+import shutil
+
+import numpy as np
+import pytest
+from scipy.stats import chisquare
+
+from oracle import build as obuild
+from oracle import oracle as orc
+
+SRC = os.path.join(os.path.dirname(obuild.__file__), "vrt_oracle.c")
+V = 16
+
+
+def _tables(D, seed):
+    n = sum(V ** k for k in range(D + 2))
+    rng = np.random.default_rng(seed)
+    dt = (rng.normal(size=(n, V)) * 1.5).astype(np.float32)
+    tt = (dt + rng.normal(size=(n, V)) * 0.8).astype(np.float32)
+    return dt, tt
+
+
+def _softmax(x, T):
+    invT = np.float64(np.float32(1.0) / np.float32(T))
+    e = np.exp((x.astype(np.float64) - x.max()) * invT)
+    return e / e.sum()
+
+
+def lossless_ok(T=1.0, m=1, trials=200_000):
+    cfg = orc.make_cfg(V=V, trunc=16, K=3, m=m, D=2, W=3, R=6, T=T)
+    dt, tt = _tables(2, 5)
+    out, nf, _ = orc.table_trials(cfg, 2, dt, tt, 4242, 0, 0, trials)
+    p = _softmax(tt[0], T)
+    obs = np.bincount(out[:, 0], minlength=V).astype(np.float64)
+    return chisquare(obs, p * obs.sum()).pvalue > 0.01
+
+
+def acceptance_ok(trials=200_000):
+    from tests.test_oracle_lossless import _depth1_acceptance
+    cfg = orc.make_cfg(V=V, trunc=16, K=4, m=1, D=1, R=4, T=1.0)
+    dt, tt = _tables(1, 78)
+    out, nf, _ = orc.table_trials(cfg, 1, dt, tt, 4343, 0, 0, trials)
+    P = _depth1_acceptance(cfg, dt[0], tt[0])
+    z = ((nf >= 1).mean() - P) / np.sqrt(P * (1 - P) / trials)
+    return abs(z) < 4.0
+
+
+def slots_ok():
+    from tests.test_oracle_units import test_expansion_probabilities_and_slots
+    try:
+        for m in (0, 1, 3):
+            test_expansion_probabilities_and_slots(m, 1.0)
+    except AssertionError:
+        return False
+    return True
+
+
+def support_ok():
+    from tests.test_oracle_units import test_support_matches_lexsort
+    try:
+        test_support_matches_lexsort(1000, 128)
+    except AssertionError:
+        return False
+    return True
+
+
+def smart_ok():
+    from tests import test_oracle_smart as ts
+    try:
+        ts.test_linear_cost_keeps_above_average_gain()
+        ts.test_two_layers_hand_worked()
+    except AssertionError:
+        return False
+    return True
+
+
+MUTANTS = [
+    ("residual_mass_ignores_overlap", "    W = 1.0 - overlap;", "    W = 1.0;",
+     lambda: lossless_ok() and acceptance_ok()),
+    ("probe_ratio_inverted", "const double a = w[xs] / qs;", "const double a = qs / w[xs];",
+     lambda: lossless_ok() and acceptance_ok()),
+    ("tail_residual_not_clipped", "w[y] = (p > q) ? p - q : 0.0;", "w[y] = p;",
+     lambda: lossless_ok() and acceptance_ok()),
+    ("rejected_sibling_not_removed", "    W -= wx;\n    w[xt] = 0.0;", "    W -= wx;",
+     lambda: lossless_ok() and acceptance_ok()),
+    ("verify_ignores_temperature", "w[v] = exp(((double)x[v] - (double)M) * invT);",
+     "w[v] = exp((double)x[v] - (double)M);", lambda: lossless_ok(T=0.6)),
+    ("tail_mass_includes_top_m", "for (int32_t i = m; i < n; ++i) zT += e->q_T[i];",
+     "for (int32_t i = 0; i < n; ++i) zT += e->q_T[i];", lambda: slots_ok() and lossless_ok()),
+    ("proxy_takes_max", "e->proxy = e->q_raw[m - 1] < e->z_raw ? e->q_raw[m - 1] : e->z_raw;",
+     "e->proxy = e->q_raw[m - 1] > e->z_raw ? e->q_raw[m - 1] : e->z_raw;", slots_ok),
+    ("fillers_repeat_probe", "if (i != js) add_child", "if (i >= 0) add_child", slots_ok),
+    ("support_tie_break_reversed", "return (x->id < y->id) ? -1 : (x->id > y->id);",
+     "return (x->id > y->id) ? -1 : (x->id < y->id);", support_ok),
+    ("smart_leaf_count_inverted", "if (t->has_child[par + 1]) t->n_paths += 1;",
+     "if (!t->has_child[par + 1]) t->n_paths += 1;", smart_ok),
+]
+
+
+@pytest.mark.parametrize("name,old,new,check", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pin_catches_planted_mistake(tmp_path, name, old, new, check):
+    src = open(SRC).read()
+    assert src.count(old) == 1, name
+    assert check(), "the unmodified oracle must pass the check"
+    mut = tmp_path / "vrt_oracle.c"
+    mut.write_text(src.replace(old, new))
+    shutil.copy(os.path.join(os.path.dirname(SRC), "vrt_oracle.h"), tmp_path / "vrt_oracle.h")
+    lib = obuild.build(src=str(mut), out=str(tmp_path / f"liboracle_{name}.so"))
+    with orc.using(lib):
+        assert not check(), f"planted mistake {name} went unnoticed"
