@@ -1,0 +1,208 @@
+/* vrt.h — C ABI of libvrt: one speculative-decoding step on MI355X (gfx950).
+ *
+ * The library builds a dynamic draft tree from batched draft logits and verifies
+ * it losslessly against batched target logits:
+ *
+ *   build (per layer, then finish)             RheoSampling, framework flowchart
+ *     - top-`trunc` truncation of each expanded parent's draft row (key design 1)
+ *     - dual-identity slot fill: top-m deterministic tokens, one probe drawn from
+ *       the renormalised tempered tail carrying proxy min{q(x_m), z}, then the
+ *       next-ranked filler tokens (key design 2)
+ *     - path-product scores; per-layer beam and global top-R prune, or SMART's
+ *       marginal keep rule (SMART key designs 1-3) in VRT_MODE_SMART
+ *   verify                                      RheoSampling, key design 3
+ *     - full-vocabulary temperature softmax of every node's target row
+ *     - probe-first optimal-transport test, recursive rejection of the remaining
+ *       kept siblings under norm(max(0, p - q~)), final residual (or bonus) sample
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked "device" are HIP device pointers owned by the caller; the
+ *     library never allocates or frees memory and keeps no device state between
+ *     calls except what the caller's tree blob and workspace hold.
+ *   - Work is enqueued on `stream` (a hipStream_t, NULL = default stream) and is
+ *     asynchronous: the return code covers host-side validation and launch errors
+ *     only. No entry point synchronises the device.
+ *   - Data faults in the logits (NaN, +Inf, an all -inf row) do not abort: they set
+ *     bits in the per-tree status word (stats[b][0]); outputs of that tree are then
+ *     unspecified but every access stays in bounds.
+ *   - On error the call enqueues nothing and vrt_last_error() describes the cause
+ *     (thread-local, valid until the next call on that thread).
+ *   - Random draws are Philox4x32-10 (Salmon et al., SC'11) with key = seed and
+ *     counter (idx, b, step, purpose): purpose 1 = probe draw (idx = creation index
+ *     of the expanded node + 1, root 0), 2 = accept/reject test (idx = 32*depth + j,
+ *     j = 0 probe, 1.. remaining siblings in slot order), 3 = final sample
+ *     (idx = depth). u = (out0 >> 8) * 2^-24; a draw accepts iff u < threshold.
+ */
+#ifndef VRT_H
+#define VRT_H
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  VRT_OK = 0,
+  VRT_EINVAL = -1,  /* invalid argument or configuration */
+  VRT_EDTYPE = -2,  /* unsupported logits dtype */
+  VRT_ENOMEM = -3,  /* workspace or tree blob smaller than the sizing call returned */
+  VRT_EHIP = -4     /* a HIP launch failed */
+} vrt_status;
+
+typedef enum { VRT_F32 = 0, VRT_BF16 = 1 } vrt_dtype;
+typedef enum { VRT_MODE_TOPR = 0, VRT_MODE_SMART = 1 } vrt_mode;
+enum { VRT_ROOT = 0, VRT_DET = 1, VRT_PROBE = 2, VRT_FILL = 3 };
+#define VRT_FINISH (-1)
+
+/* status bits, stats[b][0] */
+#define VRT_ST_DRAFT_NONFINITE 0x1u  /* NaN or +Inf in an expanded draft row */
+#define VRT_ST_DRAFT_EMPTY 0x2u      /* a draft row is entirely -inf */
+#define VRT_ST_TARGET_BAD 0x4u       /* NaN/+Inf in a target row, or a row entirely -inf */
+
+/* Method configuration (plain data; identical for every call of one step).
+ *   B        trees in the batch (>= 1)
+ *   V        vocabulary size (1 .. 2^20)
+ *   dtype    VRT_F32 or VRT_BF16 logits
+ *   trunc    support size of the draft truncation (1 .. 1024; the pages use 128)
+ *   K        slots per expanded parent (1 .. 30)
+ *   m        deterministic top-m slots (probe mode: 0 <= m <= K-1)
+ *   probe    1 = RheoSampling dual-identity slots, 0 = plain top-K (all deterministic)
+ *   D        tree depth, the number of expansion layers (1 .. 32)
+ *   W        parents expanded per layer in top-R mode (0 -> K); W*K <= 4096 and
+ *            K + (D-1)*W*K <= 4096
+ *   R        nodes kept by the global prune, root excluded (top-R mode, 1 .. 1024)
+ *   mode     VRT_MODE_TOPR or VRT_MODE_SMART
+ *   budget   SMART: maximum kept nodes, root excluded (1 .. 1024); budget*K <= 4096
+ *   T        temperature of the probe draw and of verification (> 0)
+ *   eps_m0   proxy offset for m = 0 (proxy = min(1, q(x_1) + eps_m0))
+ *   alpha, lambda_, gamma_, delta_, rho_
+ *            SMART discount and cost models C(n) = lambda n + gamma (exp(delta n^rho) - 1),
+ *            C'(n) = lambda + gamma delta rho n^(rho-1) exp(delta n^rho) (SMART key design 2) */
+typedef struct {
+  int32_t B, V, dtype, trunc, K, m, probe, D, W, R, mode, budget;
+  float T, eps_m0;
+  double alpha, lambda_, gamma_, delta_, rho_;
+} vrt_config;
+
+/* Byte offsets of the arrays inside the caller-owned tree blob. Every array is
+ * [B][...] row-major, 256-byte aligned. Capacities:
+ *   NC  = K + (D-1)*P*K candidates (P = W in top-R mode, budget in SMART mode)
+ *   NR  = 1 + (D-1)*P expansion rows
+ *   N   = R + 1 (top-R) or budget + 1 (SMART) emitted nodes, root included
+ *   TC  = trunc tail entries
+ *   FP  = P frontier slots
+ * Candidate c of layer l sits at c = base(l) + pos*K + slot with base(0) = 0,
+ * base(l) = K + (l-1)*P*K; pos is the expanding parent's frontier position, slot its
+ * slot. Expansion row r = 0 (root) or 1 + (l-1)*P + pos expanded frontier position
+ * pos at layer l >= 1.
+ *
+ * Build state (written by vrt_build_tree, read by the next layer and by finish):
+ *   cand_token  i32 [B][NC]  token of the candidate
+ *   cand_parent i32 [B][NC]  creation index of its parent, -1 = root
+ *   cand_score  f32 [B][NC]  path score (fp32 product of ranking probabilities)
+ *   cand_kind   i32 [B][NC]  bits 0-7: 0 = no candidate in this slot, else
+ *                            VRT_DET/PROBE/FILL; bit 8 (SMART): it has an admitted child
+ *   row_tail_n  i32 [B][NR]  number of tail entries of the row's support (0: no probe)
+ *   row_tail_id i32 [B][NR][TC]  tail tokens in rank order (support ranks m+1..)
+ *   row_tail_q  f32 [B][NR][TC]  q~ = q_T / z_T of those tokens
+ *   front       i32 [B][FP]  creation indices of the parents the next layer expands,
+ *                            in frontier-position order (the caller supplies their
+ *                            draft rows in this order)
+ *   n_front     i32 [B]      number of valid entries of front (0: no further layer)
+ *   smart       f64 [B][8]   SMART state (L, |T|, |P|, admitted count, root has a child)
+ *   admitted    i32 [B][N]   SMART: admitted creation indices in admission order
+ * Emitted tree (written by finish; the verification input, writable by the caller):
+ *   n_nodes     i32 [B]      emitted nodes, root included (1 .. N)
+ *   node_token  i32 [B][N]   token (root: -1)
+ *   node_parent i32 [B][N]   parent node index (root: -1); parent < child
+ *   node_depth  i32 [B][N]   depth (root 0)
+ *   node_kind   i32 [B][N]   VRT_ROOT/DET/PROBE/FILL
+ *   node_cand   i32 [B][N]   creation index (root: -1)
+ *   child_off   i32 [B][N+1] children of node i are child[child_off[i] .. child_off[i+1])
+ *   child       i32 [B][N]   child node indices, in slot order
+ *   tail_n      i32 [B][N]   tail entries of node i's expansion if its probe child is
+ *                            kept, else 0
+ *   tail_id     i32 [B][N][TC], tail_q f32 [B][N][TC]  that tail (q~ values) */
+typedef struct {
+  int64_t NC, NR, N, TC, FP;
+  int64_t cand_token, cand_parent, cand_score, cand_kind;
+  int64_t row_tail_n, row_tail_id, row_tail_q;
+  int64_t front, n_front, smart, admitted;
+  int64_t n_nodes, node_token, node_parent, node_depth, node_kind, node_cand;
+  int64_t child_off, child, tail_n, tail_id, tail_q;
+  int64_t total_bytes;
+} vrt_tree_layout;
+
+/* Checks the configuration. Returns VRT_OK or VRT_EINVAL (reason in vrt_last_error). */
+vrt_status vrt_check_config(const vrt_config* cfg);
+
+/* Fills *out with the tree-blob layout for cfg. */
+vrt_status vrt_tree_layout_of(const vrt_config* cfg, vrt_tree_layout* out);
+
+/* Size in bytes of the tree blob (the caller allocates it on the device). 0 if cfg is invalid. */
+size_t vrt_tree_bytes(const vrt_config* cfg);
+
+/* Size in bytes of the device workspace both entry points need. 0 if cfg is invalid.
+ * The workspace needs no initialisation and holds nothing between calls. */
+size_t vrt_workspace_bytes(const vrt_config* cfg);
+
+/* One layer of tree construction (RheoSampling framework flowchart, key designs 1-2;
+ * SMART key design 3 in VRT_MODE_SMART), or the final prune.
+ *   layer         0 .. D-1 in order (layer 0 resets the tree), or VRT_FINISH after the
+ *                 last layer (or once n_front is 0 for every tree) to emit the tree
+ *   draft_logits  device, dtype cfg->dtype: the draft row of frontier position j of
+ *                 tree b starts at element b*tree_stride + j*ld. Layer 0 reads one row
+ *                 per tree (the root); layer l reads n_front[b] rows. Unused for
+ *                 VRT_FINISH (may be NULL). Rows must be 16-byte aligned: the base
+ *                 pointer 16-byte aligned and ld, tree_stride multiples of 16 bytes;
+ *                 every row read must have ld addressable elements.
+ *   ld, tree_stride  in elements, ld >= V
+ *   seed, step    Philox key and counter word (the step counter, low 32 bits used)
+ *   tree          device, vrt_tree_bytes(cfg) bytes, caller-owned, persists across
+ *                 the layers of one step
+ *   ws            device workspace of ws_bytes >= vrt_workspace_bytes(cfg)
+ *   stats         device u32 [B][8] or NULL: status bits are OR-ed into stats[b][0]
+ *   stream        hipStream_t
+ * Layers must be called 0, 1, .., then VRT_FINISH: each layer expands the frontier
+ * the previous one stored in the blob (indices read back from the blob are
+ * range-checked on the device, so a wrong order gives wrong trees, never an
+ * out-of-bounds access).
+ * Errors: VRT_EINVAL (config, layer number, alignment, NULL pointers), VRT_ENOMEM
+ * (ws_bytes too small), VRT_EHIP. */
+vrt_status vrt_build_tree(const vrt_config* cfg, int32_t layer, const void* draft_logits,
+                          int64_t ld, int64_t tree_stride, uint64_t seed, uint64_t step,
+                          void* tree, void* ws, size_t ws_bytes, uint32_t* stats, void* stream);
+
+/* Verification of an emitted tree (RheoSampling key design 3).
+ *   target_logits device, dtype cfg->dtype: the target row of node i of tree b starts
+ *                 at element b*tree_stride + i*ld (rows i < n_nodes[b] are read);
+ *                 same alignment rules as the draft rows
+ *   tree          device tree blob whose emitted-tree arrays are filled (by finish or
+ *                 by the caller following the layout)
+ *   out_tokens    device i32 [B][D+1]: emitted tokens (accepted path, then the final
+ *                 residual or bonus token); entries past out_len[b] are -1
+ *   out_nodes     device i32 [B][D]: accepted node indices (entries past out_len[b]-1 are -1)
+ *   out_len       device i32 [B]: number of emitted tokens (1 .. D+1)
+ *   stats         device u32 [B][8]: [0] status bits, [1] accepted tree tokens,
+ *                 [2] 1 if the probe was accepted somewhere on the path,
+ *                 [3] draws on the path within 1e-6 of their threshold (near ties),
+ *                 [4] nodes visited; [5..7] reserved (0)
+ *   node_out      device i32 [B][N][4] or NULL: per node, decided as if the walk
+ *                 reached it: [0] accepted child node or -1, [1] residual/bonus token
+ *                 or -1, [2] tests taken (bits 0-7) | near ties (bits 8-15) | status
+ *                 bits (from bit 16), [3] fp32 bits of the residual mass W the final
+ *                 sample used (0 if a child was accepted)
+ * Errors: as vrt_build_tree. */
+vrt_status vrt_verify_tree(const vrt_config* cfg, const void* target_logits, int64_t ld,
+                           int64_t tree_stride, const void* tree, uint64_t seed, uint64_t step,
+                           void* ws, size_t ws_bytes, int32_t* out_tokens, int32_t* out_nodes,
+                           int32_t* out_len, uint32_t* stats, int32_t* node_out, void* stream);
+
+/* Description of the last error on this host thread ("" if none). */
+const char* vrt_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

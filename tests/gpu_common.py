@@ -1,0 +1,92 @@
+"""Helpers for the GPU parity tests: move generator rows and oracle trees into
+the library's device layout, run the HIP path through the C ABI, read back."""
+import numpy as np
+import torch
+
+import synth
+from verify_row_top_amd import vrt
+
+
+def lib_config(w, **kw):
+    c = dict(B=w.B, V=w.V, dtype=w.dtype, trunc=w.trunc, K=w.K, m=w.m, probe=w.probe, D=w.D, W=w.W,
+             R=w.R, mode=w.mode, budget=w.budget, T=w.T, eps_m0=w.eps_m0, alpha=w.alpha, lam=w.lam,
+             gamma=w.gamma, delta=w.delta, rho=w.rho)
+    c.update(kw)
+    return vrt.make_config(**c)
+
+
+def row_ld(w):
+    """Row stride in elements: V rounded up to 16 bytes."""
+    per = 8 if w.dtype == synth.BF16 else 4
+    return (w.V + per - 1) // per * per
+
+
+def to_device_rows(rows_list, w, n_rows, dev):
+    """rows_list[b] is an [n_b, V] host array (bf16 bits or fp32); returns a
+    [B, n_rows, ld] device tensor (int16 bits for bf16), rows past n_b zero."""
+    ld = row_ld(w)
+    if w.dtype == synth.BF16:
+        host = np.zeros((len(rows_list), n_rows, ld), np.uint16)
+    else:
+        host = np.zeros((len(rows_list), n_rows, ld), np.float32)
+    for b, r in enumerate(rows_list):
+        if r is None:
+            continue
+        host[b, :r.shape[0], :w.V] = r
+    t = torch.from_numpy(host.view(np.int16) if w.dtype == synth.BF16 else host)
+    return t.to(dev), ld
+
+
+class Lib:
+    """Device buffers for one configuration."""
+
+    def __init__(self, cfg, dev):
+        self.cfg = cfg
+        self.dev = dev
+        self.tree = torch.zeros(vrt.tree_bytes(cfg), dtype=torch.uint8, device=dev)
+        self.ws = torch.zeros(vrt.workspace_bytes(cfg), dtype=torch.uint8, device=dev)
+        self.views = vrt.tree_views(cfg, self.tree)
+        L = vrt.tree_layout_of(cfg)
+        self.N = L.N
+        self.TC = L.TC
+        self.FP = L.FP
+        self.stats = torch.zeros((cfg.B, 8), dtype=torch.int32, device=dev)
+        self.out_tokens = torch.zeros((cfg.B, cfg.D + 1), dtype=torch.int32, device=dev)
+        self.out_nodes = torch.zeros((cfg.B, cfg.D), dtype=torch.int32, device=dev)
+        self.out_len = torch.zeros(cfg.B, dtype=torch.int32, device=dev)
+        self.node_out = torch.zeros((cfg.B, self.N, 4), dtype=torch.int32, device=dev)
+
+    def write_view(self, b, view):
+        """Write an oracle verification view into tree b's emitted-tree arrays."""
+        n = view["n_nodes"]
+        v = self.views
+        v["n_nodes"][b] = n
+        for k in ("token", "parent", "depth", "kind"):
+            v["node_" + k][b, :n] = torch.from_numpy(view[k].astype(np.int32))
+        v["node_cand"][b, :n] = torch.from_numpy(view["cand"].astype(np.int32))
+        v["child_off"][b, :n + 1] = torch.from_numpy(view["child_off"].astype(np.int32))
+        nch = view["child"].size
+        if nch:
+            v["child"][b, :nch] = torch.from_numpy(view["child"].astype(np.int32))
+        v["tail_n"][b, :n] = torch.from_numpy(view["tail_n"].astype(np.int32))
+        tc = view["tail_id"].shape[1]
+        v["tail_id"][b, :n, :tc] = torch.from_numpy(view["tail_id"].astype(np.int32))
+        v["tail_q"][b, :n, :tc] = torch.from_numpy(view["tail_q"].astype(np.float32))
+
+    def verify(self, target, ld, seed, step, zero_stats=True):
+        if zero_stats:
+            self.stats.zero_()
+        vrt.verify_tree(self.cfg, target, ld, target.stride(0), self.tree, seed, step, self.ws,
+                        self.out_tokens, self.out_nodes, self.out_len, self.stats, self.node_out)
+        torch.cuda.synchronize()
+
+    def build_layer(self, layer, rows, ld, seed, step):
+        vrt.build_tree(self.cfg, layer, rows, ld, rows.stride(0), seed, step, self.tree, self.ws,
+                       self.stats)
+
+    def finish(self, seed=0, step=0):
+        vrt.build_tree(self.cfg, vrt.FINISH, None, 0, 0, seed, step, self.tree, self.ws, self.stats)
+        torch.cuda.synchronize()
+
+    def host(self, name):
+        return self.views[name].cpu().numpy()

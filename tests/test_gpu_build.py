@@ -1,0 +1,139 @@
+"""GPU parity of vrt_build_tree (every layer, then finish) and of the whole step
+(build, then verify on the tree the GPU built) against the oracle.
+
+Draft rows come from the generator along the oracle's frontier; the GPU must
+produce the same frontier to read the right rows, so any divergence shows up.
+Bit-exact: candidate tokens, parents, kinds and path scores (fp32 bits), the
+frontier, the emitted tree and child lists. Tail probabilities q~ within 1e-5
+relative. Trees whose oracle build had a probe draw within 1e-6 of a CDF
+boundary are exempt and counted.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from synth import workloads
+from tests.gpu_common import Lib, lib_config, to_device_rows
+from tests.harness import OracleStep
+
+pytestmark = pytest.mark.gpu
+
+
+def _small(**kw):
+    base = dict(name="small", B=4, V=5000, dtype=synth.BF16, R=40, D=5, K=6, m=1, T=1.0,
+                zipf=(1.1,), sigma=0.7)
+    base.update(kw)
+    return workloads.Workload(**base)
+
+
+def _smart_small(**kw):
+    base = dict(name="smart_small", B=4, V=6000, dtype=synth.BF16, mode=workloads.SMART, K=8,
+                budget=40, D=6, alpha=1.0, lam=0.02, gamma=0.01, delta=0.004, rho=1.3, m=1,
+                T=1.0, zipf=(1.1,), sigma=0.7)
+    base.update(kw)
+    return workloads.Workload(**base)
+
+
+CASES = [
+    ("tiny", workloads.get("tiny")),
+    ("tiny_m0_T06", workloads.get("tiny").replace(m=0, T=0.6)),
+    ("small_bf16_ragged", _small()),
+    ("small_m3_K8", _small(m=3, K=8, R=50)),
+    ("small_probe_off", _small(probe=0)),
+    ("small_trunc4", _small(V=300, trunc=4, K=3, R=12, D=4)),
+    ("small_tiny_vocab", _small(V=7, trunc=128, K=5, R=20, D=3, dtype=synth.F32)),
+    ("small_T06_trunc256", _small(T=0.6, trunc=256, V=3000)),
+    ("small_fp32_flat", _small(dtype=synth.F32, zipf=(0.8,), V=4100, R=30)),
+    ("small_peaked_W3", _small(zipf=(1.5,), W=3, R=25, D=7)),
+    ("stress_mixed_m0", _small(B=4, V=9000, zipf=(1.5, 0.8), split=2, R=64, D=6, K=8, m=0)),
+    ("smart_small", _smart_small()),
+    ("smart_small_m0_alpha08", _smart_small(m=0, alpha=0.8, budget=24)),
+]
+
+
+def gpu_build(w, steps, seed, step, dev):
+    cfg = lib_config(w)
+    L = Lib(cfg, dev)
+    for layer in range(w.D):
+        rows_list = [s.layer_rows[layer] if layer < len(s.layer_rows) else None for s in steps]
+        n_rows = 1 if layer == 0 else L.FP
+        rows, ld = to_device_rows(rows_list, w, n_rows, dev)
+        L.build_layer(layer, rows, ld, seed, step)
+    L.finish(seed, step)
+    return L
+
+
+def compare_tree(w, s, L, b):
+    v = L.views
+    cands = s.cands
+    NC = cands.size
+    kind = v["cand_kind"][b].cpu().numpy() & 0xFF
+    live = cands["live"] == 1
+    np.testing.assert_array_equal(kind != 0, live, err_msg="live candidate slots")
+    np.testing.assert_array_equal(kind[live], cands["kind"][live])
+    np.testing.assert_array_equal(v["cand_token"][b].cpu().numpy()[live], cands["token"][live])
+    np.testing.assert_array_equal(v["cand_parent"][b].cpu().numpy()[live], cands["parent"][live])
+    gs = v["cand_score"][b].cpu().numpy()[live]
+    np.testing.assert_array_equal(gs.view(np.uint32), cands["score"][live].view(np.uint32))
+    # emitted tree
+    ov = s.view
+    n = ov["n_nodes"]
+    assert v["n_nodes"][b].item() == n
+    for k in ("token", "parent", "depth", "kind", "cand"):
+        np.testing.assert_array_equal(v["node_" + k][b, :n].cpu().numpy(), ov[k], err_msg=k)
+    np.testing.assert_array_equal(v["child_off"][b, :n + 1].cpu().numpy(), ov["child_off"])
+    nch = ov["child"].size
+    np.testing.assert_array_equal(v["child"][b, :nch].cpu().numpy(), ov["child"])
+    np.testing.assert_array_equal(v["tail_n"][b, :n].cpu().numpy(), ov["tail_n"])
+    tq = v["tail_q"][b].cpu().numpy()
+    ti = v["tail_id"][b].cpu().numpy()
+    for i in range(n):
+        k = ov["tail_n"][i]
+        if k:
+            np.testing.assert_array_equal(ti[i, :k], ov["tail_id"][i, :k])
+            np.testing.assert_allclose(tq[i, :k], ov["tail_q"][i, :k], rtol=1e-5, atol=1e-30)
+
+
+@pytest.mark.parametrize("name,w", CASES, ids=[c[0] for c in CASES])
+def test_build_and_step_match_oracle(gpu, name, w):
+    exempt = total = 0
+    for seed, step in [(1, 0), (2, 3)]:
+        steps = [OracleStep(w, seed, b, step) for b in range(w.B)]
+        print(f"build parity: {name} seed={seed} step={step} B={w.B} V={w.V}", flush=True)
+        L = gpu_build(w, steps, seed, step, gpu)
+        assert (L.stats.cpu().numpy()[:, 0] == 0).all()
+        # the whole step: GPU verify on the GPU-built tree, target rows of the oracle tree
+        target, ld = to_device_rows([s.target_rows for s in steps], w, L.N, gpu)
+        L.verify(target, ld, seed, step, zero_stats=False)
+        for b, s in enumerate(steps):
+            total += 1
+            if s.build_exempt:
+                exempt += 1
+                continue
+            compare_tree(w, s, L, b)
+            if s.verify_exempt == 0:
+                Lt = len(s.out_tokens)
+                assert L.out_len[b].item() == Lt
+                np.testing.assert_array_equal(L.out_tokens[b, :Lt].cpu().numpy(), s.out_tokens)
+    assert exempt <= max(1, total // 10), (exempt, total)
+
+
+def test_bad_draft_rows_set_status_and_stay_in_bounds(gpu):
+    w = _small(B=3, D=2, R=10)
+    steps = [OracleStep(w, 5, b, 0, verify=False) for b in range(w.B)]
+    rows0 = [s.layer_rows[0].copy() for s in steps]
+    rows0[0][0, 11] = 0x7FC0          # NaN in tree 0's root row
+    rows0[1][0, :] = 0xFF80           # tree 1's root row entirely -inf
+    cfg = lib_config(w)
+    L = Lib(cfg, gpu)
+    rows, ld = to_device_rows(rows0, w, 1, gpu)
+    L.build_layer(0, rows, ld, 5, 0)
+    rows1, _ = to_device_rows([s.layer_rows[1] if len(s.layer_rows) > 1 else None for s in steps],
+                              w, L.FP, gpu)
+    L.build_layer(1, rows1, ld, 5, 0)
+    L.finish()
+    st = L.stats.cpu().numpy()[:, 0]
+    assert st[0] & 0x1 and st[1] & 0x2 and st[2] == 0
+    n = L.views["n_nodes"].cpu().numpy()
+    assert n[0] == 1 and n[1] == 1 and n[2] > 1

@@ -1,0 +1,166 @@
+// Device building blocks for the gfx950 kernels: counter-based uniforms, the
+// ranking exponential, wave64 reductions and scans, bf16 unpacking, sort keys.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vrt {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11). Each round multiplies
+// words 0 and 2 by the two Philox constants, swaps the halves into place and
+// mixes the round key; the key advances by the Weyl constants between rounds.
+struct U4 {
+  uint32_t x, y, z, w;
+};
+
+__device__ __forceinline__ U4 philox10(U4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t lo_a = 0xD2511F53u * c.x;
+    const uint32_t hi_a = __umulhi(0xD2511F53u, c.x);
+    const uint32_t lo_b = 0xCD9E8D57u * c.z;
+    const uint32_t hi_b = __umulhi(0xCD9E8D57u, c.z);
+    c = U4{hi_b ^ c.y ^ k0, lo_b, hi_a ^ c.w ^ k1, lo_a};
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c;
+}
+
+enum : uint32_t { kPurposeProbe = 1, kPurposeTest = 2, kPurposeFinal = 3 };
+
+// u in [0, 1 - 2^-24]: the top 24 bits of the first output word.
+__device__ __forceinline__ float uniform24(uint64_t seed, uint32_t idx, uint32_t b, uint32_t step,
+                                           uint32_t purpose) {
+  const U4 o = philox10(U4{idx, b, step, purpose}, (uint32_t)seed, (uint32_t)(seed >> 32));
+  return (float)(o.x >> 8) * 5.9604644775390625e-08f;  // exact
+}
+
+// ---------------------------------------------------------------------------
+// Ranking exponential: a fixed recipe so that draft ranking is reproducible
+// bit for bit on any IEEE machine (no contraction; every step correctly rounded).
+// Cody-Waite reduction by ln 2 split in two parts, e^r by its degree-7 Taylor
+// polynomial evaluated with fma, exact scaling by 2^k. Inputs below -80 give 0.
+__device__ __forceinline__ float exp_rank(float x) {
+  if (!(x >= -80.0f)) return 0.0f;
+  const float k = __builtin_rintf(x * 1.44269504f);
+  float r = __builtin_fmaf(-k, 0.693145751953125f, x);
+  r = __builtin_fmaf(-k, 1.428606765330187e-06f, r);
+  // coefficients 1/7!, 1/6!, ..., 1/1!, 1/0!, each the correctly rounded fp32 quotient
+  float p = __builtin_fmaf(1.0f / 5040.0f, r, 1.0f / 720.0f);
+  p = __builtin_fmaf(p, r, 1.0f / 120.0f);
+  p = __builtin_fmaf(p, r, 1.0f / 24.0f);
+  p = __builtin_fmaf(p, r, 1.0f / 6.0f);
+  p = __builtin_fmaf(p, r, 0.5f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  return __builtin_ldexpf(p, (int)k);
+}
+
+// ---------------------------------------------------------------------------
+// wave64 reductions by xor butterflies: every lane ends with the same value, and
+// for a sum the combination order is the aligned pairwise tree over lanes.
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) v = v + __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// inclusive prefix sum over lanes (Hillis-Steele)
+template <typename T>
+__device__ __forceinline__ T wave_incl_scan(T v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const T t = __shfl_up(v, o, kWave);
+    if (lane >= o) v = v + t;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Orders LDS accesses between the lanes of one wave (no block barrier: usable
+// after the other waves of the block have exited).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32 and order-preserving keys
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Monotone map of an fp32 value to uint32 (NaN maps to 0, below -inf).
+__device__ __forceinline__ uint32_t ord32(float f) {
+  if (f != f) return 0u;
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float unord32(uint32_t k) {
+  const uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return __uint_as_float(u);
+}
+
+// Support key: larger is better; value descending, then token id ascending.
+__device__ __forceinline__ uint64_t sup_key(float v, uint32_t id) {
+  return ((uint64_t)ord32(v) << 32) | (uint64_t)(0xFFFFFFFFu - id);
+}
+__device__ __forceinline__ uint32_t sup_key_id(uint64_t k) { return 0xFFFFFFFFu - (uint32_t)k; }
+__device__ __forceinline__ float sup_key_val(uint64_t k) { return unord32((uint32_t)(k >> 32)); }
+
+// Node key: path score descending (non-negative fp32 bits are ordered), then
+// creation index ascending.
+__device__ __forceinline__ uint64_t node_key(float score, uint32_t cidx) {
+  return ((uint64_t)__float_as_uint(score) << 32) | (uint64_t)(0xFFFFFFFFu - cidx);
+}
+
+// ---------------------------------------------------------------------------
+// In-LDS bitonic sort of n (a power of two) 64-bit keys into descending order,
+// by all threads of the block.
+__device__ inline void bitonic_desc(uint64_t* a, int n) {
+  for (int k = 2; k <= n; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int t = threadIdx.x; t < (n >> 1); t += blockDim.x) {
+        const int i = ((t & ~(j - 1)) << 1) | (t & (j - 1));
+        const int p = i | j;
+        const uint64_t x = a[i], y = a[p];
+        const bool desc = ((i & k) == 0);
+        if (desc ? (x < y) : (x > y)) {
+          a[i] = y;
+          a[p] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+__host__ __device__ inline int next_pow2(int n) {
+  int p = 1;
+  while (p < n) p <<= 1;
+  return p;
+}
+
+}  // namespace vrt

@@ -1,0 +1,77 @@
+// Internal types shared by the host entry points and the kernels of libvrt.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/vrt.h"
+
+namespace vrt {
+
+// Kernel-side copy of the configuration with derived capacities.
+struct Cfg {
+  int B, V, dtype, trunc, K, m, probe, D, W, R, mode, budget;
+  int P;   // parents per layer >= 1 (W in top-R mode, budget in SMART mode)
+  int NC;  // candidates per tree
+  int NR;  // expansion rows per tree
+  int N;   // emitted nodes per tree, root included
+  int TC;  // tail capacity (= trunc)
+  int FP;  // frontier slots
+  float invT;  // fl32(1 / T)
+  float c2;    // fl32(invT * log2(e)): exp((x - M)/T) = exp2(x*c2 - M*c2)
+  float eps_m0;
+  double alpha, lam, gam, del, rho;
+};
+
+// Typed views of the caller's tree blob (see vrt_tree_layout in vrt.h).
+struct TreePtrs {
+  int* cand_token;
+  int* cand_parent;
+  float* cand_score;
+  int* cand_kind;
+  int* row_tail_n;
+  int* row_tail_id;
+  float* row_tail_q;
+  int* front;
+  int* n_front;
+  double* smart;
+  int* admitted;
+  int* n_nodes;
+  int* node_token;
+  int* node_parent;
+  int* node_depth;
+  int* node_kind;
+  int* node_cand;
+  int* child_off;
+  int* child;
+  int* tail_n;
+  int* tail_id;
+  float* tail_q;
+};
+
+// Per-node verification outcome: accepted child node (-1: none), final token
+// (-1: none), flags = tests taken (bits 0-7) | near ties (bits 8-15) | status
+// bits (from bit 16), and the residual mass W of the final sample (0 otherwise).
+struct NodeOut {
+  int accept, token, flags;
+  float W;
+};
+
+Cfg make_cfg(const vrt_config& c);
+TreePtrs tree_ptrs(const vrt_config& c, void* blob);
+
+hipError_t launch_verify(const Cfg& c, const TreePtrs& t, const void* logits, int64_t ld,
+                         int64_t tstride, uint64_t seed, uint32_t step, NodeOut* node_out,
+                         int32_t* out_tokens, int32_t* out_nodes, int32_t* out_len, uint32_t* stats,
+                         hipStream_t stream);
+
+// Workspace of the build: per-row support lists, beam scratch.
+struct BuildWs {
+  uint64_t* seg_keys;  // unused placeholder for split-row selection
+};
+
+hipError_t launch_build_layer(const Cfg& c, const TreePtrs& t, int layer, const void* logits,
+                              int64_t ld, int64_t tstride, uint64_t seed, uint32_t step,
+                              uint32_t* stats, void* ws, hipStream_t stream);
+hipError_t launch_build_finish(const Cfg& c, const TreePtrs& t, void* ws, hipStream_t stream);
+
+}  // namespace vrt

@@ -1,0 +1,175 @@
+"""ctypes binding of libvrt (include/vrt.h): argument marshalling only.
+
+Every entry point keeps the C name without its `vrt_` prefix. Tensors are passed
+as raw device pointers; PyTorch only owns the memory and supplies the stream.
+Loading fails loudly when libvrt.so is missing or does not load: there is no
+fallback path.
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libvrt.so")
+
+OK, EINVAL, EDTYPE, ENOMEM, EHIP = 0, -1, -2, -3, -4
+F32, BF16 = 0, 1
+MODE_TOPR, MODE_SMART = 0, 1
+ROOT, DET, PROBE, FILL = 0, 1, 2, 3
+FINISH = -1
+ST_DRAFT_NONFINITE, ST_DRAFT_EMPTY, ST_TARGET_BAD = 0x1, 0x2, 0x4
+EXPORTS = ("vrt_check_config", "vrt_tree_layout_of", "vrt_tree_bytes", "vrt_workspace_bytes",
+           "vrt_build_tree", "vrt_verify_tree", "vrt_last_error")
+
+
+class VrtError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"vrt error {code}: {msg}")
+        self.code = code
+
+
+class Config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("B", "V", "dtype", "trunc", "K", "m", "probe", "D", "W", "R", "mode", "budget")] + \
+               [("T", ctypes.c_float), ("eps_m0", ctypes.c_float)] + \
+               [(n, ctypes.c_double) for n in ("alpha", "lambda_", "gamma_", "delta_", "rho_")]
+
+
+class TreeLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "NC", "NR", "N", "TC", "FP", "cand_token", "cand_parent", "cand_score", "cand_kind",
+        "row_tail_n", "row_tail_id", "row_tail_q", "front", "n_front", "smart", "admitted",
+        "n_nodes", "node_token", "node_parent", "node_depth", "node_kind", "node_cand",
+        "child_off", "child", "tail_n", "tail_id", "tail_q", "total_bytes")]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            from . import build as _build
+            _build.build()
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, u64, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64,
+                                 ctypes.c_size_t)
+        P = ctypes.POINTER
+        L.vrt_check_config.argtypes = [P(Config)]
+        L.vrt_check_config.restype = i32
+        L.vrt_tree_layout_of.argtypes = [P(Config), P(TreeLayout)]
+        L.vrt_tree_layout_of.restype = i32
+        L.vrt_tree_bytes.argtypes = [P(Config)]
+        L.vrt_tree_bytes.restype = sz
+        L.vrt_workspace_bytes.argtypes = [P(Config)]
+        L.vrt_workspace_bytes.restype = sz
+        L.vrt_build_tree.argtypes = [P(Config), i32, vp, i64, i64, u64, u64, vp, vp, sz, vp, vp]
+        L.vrt_build_tree.restype = i32
+        L.vrt_verify_tree.argtypes = [P(Config), vp, i64, i64, vp, u64, u64, vp, sz, vp, vp, vp, vp,
+                                      vp, vp]
+        L.vrt_verify_tree.restype = i32
+        L.vrt_last_error.argtypes = []
+        L.vrt_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def make_config(B, V, dtype=BF16, trunc=128, K=10, m=1, probe=1, D=8, W=0, R=60, mode=MODE_TOPR,
+                budget=128, T=1.0, eps_m0=1e-6, alpha=1.0, lam=0.0, gamma=0.0, delta=0.0, rho=1.0):
+    return Config(B, V, dtype, trunc, K, m, probe, D, W, R, mode, budget, T, eps_m0, alpha, lam,
+                  gamma, delta, rho)
+
+
+def last_error():
+    return lib().vrt_last_error().decode()
+
+
+def _check(code):
+    if code != OK:
+        raise VrtError(code, last_error())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return ctypes.c_void_p(getattr(stream, "cuda_stream", stream))
+
+
+def check_config(cfg):
+    _check(lib().vrt_check_config(ctypes.byref(cfg)))
+
+
+def tree_layout_of(cfg):
+    L = TreeLayout()
+    _check(lib().vrt_tree_layout_of(ctypes.byref(cfg), ctypes.byref(L)))
+    return L
+
+
+def tree_bytes(cfg):
+    n = lib().vrt_tree_bytes(ctypes.byref(cfg))
+    if n == 0:
+        raise VrtError(EINVAL, last_error())
+    return n
+
+
+def workspace_bytes(cfg):
+    n = lib().vrt_workspace_bytes(ctypes.byref(cfg))
+    if n == 0:
+        raise VrtError(EINVAL, last_error())
+    return n
+
+
+def build_tree(cfg, layer, draft_logits, ld, tree_stride, seed, step, tree, ws, stats=None,
+               stream=None):
+    """vrt_build_tree; draft_logits may be None for FINISH."""
+    _check(lib().vrt_build_tree(ctypes.byref(cfg), layer, _ptr(draft_logits), ld, tree_stride, seed,
+                                step, _ptr(tree), _ptr(ws), ws.numel() * ws.element_size(),
+                                _ptr(stats), _stream(stream)))
+
+
+def verify_tree(cfg, target_logits, ld, tree_stride, tree, seed, step, ws, out_tokens, out_nodes,
+                out_len, stats, node_out=None, stream=None):
+    """vrt_verify_tree."""
+    _check(lib().vrt_verify_tree(ctypes.byref(cfg), _ptr(target_logits), ld, tree_stride, _ptr(tree),
+                                 seed, step, _ptr(ws), ws.numel() * ws.element_size(),
+                                 _ptr(out_tokens), _ptr(out_nodes), _ptr(out_len), _ptr(stats),
+                                 _ptr(node_out), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# Views of the tree blob as typed tensors (no copies), following vrt_tree_layout.
+_FIELDS = {
+    # name: (dtype, shape per tree in terms of the layout capacities)
+    "cand_token": ("i32", ("NC",)), "cand_parent": ("i32", ("NC",)), "cand_score": ("f32", ("NC",)),
+    "cand_kind": ("i32", ("NC",)), "row_tail_n": ("i32", ("NR",)),
+    "row_tail_id": ("i32", ("NR", "TC")), "row_tail_q": ("f32", ("NR", "TC")),
+    "front": ("i32", ("FP",)), "n_front": ("i32", ()), "smart": ("f64", (8,)),
+    "admitted": ("i32", ("N",)), "n_nodes": ("i32", ()), "node_token": ("i32", ("N",)),
+    "node_parent": ("i32", ("N",)), "node_depth": ("i32", ("N",)), "node_kind": ("i32", ("N",)),
+    "node_cand": ("i32", ("N",)), "child_off": ("i32", ("N+1",)), "child": ("i32", ("N",)),
+    "tail_n": ("i32", ("N",)), "tail_id": ("i32", ("N", "TC")), "tail_q": ("f32", ("N", "TC")),
+}
+
+
+def tree_views(cfg, tree):
+    """Dict of tensor views into the tree blob (a uint8 tensor of tree_bytes(cfg))."""
+    import torch
+    L = tree_layout_of(cfg)
+    dt = {"i32": torch.int32, "f32": torch.float32, "f64": torch.float64}
+    es = {"i32": 4, "f32": 4, "f64": 8}
+    out = {}
+    for name, (t, shape) in _FIELDS.items():
+        dims = []
+        for d in shape:
+            dims.append(d if isinstance(d, int) else (getattr(L, "N") + 1 if d == "N+1" else getattr(L, d)))
+        n = cfg.B
+        for d in dims:
+            n *= d
+        off = getattr(L, name)
+        out[name] = tree[off:off + n * es[t]].view(dt[t]).view(cfg.B, *dims)
+    return out
