@@ -1,0 +1,197 @@
+#!/usr/bin/env python3
+"""Benchmark of one speculative step on one MI355X: draft-tree construction over
+all D layers (support truncation, dual-identity expansion, beam, global top-R
+prune) followed by probe-first verification, on seeded synthetic logits already
+resident in HBM.
+
+Prints ONE JSON line. `value` is verified draft trees per second for the whole
+step; the roofline object is the verification call (the pass that streams every
+node's target row), whose algorithmic bytes are sum_b n_nodes[b] * V * 2.
+The CPU baseline times the oracle (oracle/) on a bounded sample of the same
+workload on the host's cores.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="headline")
+    ap.add_argument("--T", type=float, default=1.0)
+    ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--cpu-trees", type=int, default=6, help="trees in the oracle's timed sample")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
+    ap.add_argument("--verify-only", action="store_true",
+                    help="time only the verification call (for profiling it alone)")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, seed, n_trees):
+    """The oracle as it stands, one host thread, on n_trees trees of the workload."""
+    from oracle.drive import OracleStep
+    t = 0.0
+    for b in range(n_trees):
+        s = OracleStep(w, seed, b, 0)
+        t += s.t_oracle
+    return {"value": n_trees / t, "unit": "trees/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_trees} trees (b=0..{n_trees - 1}, seed {seed}, step 0) of the same "
+                      f"workload, build + verify, oracle time only, 1 thread"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (trees are "
+              f"independent: shard the batch, one process per GPU)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import synth
+    from synth import workloads
+    from verify_row_top_amd import vrt
+
+    w = workloads.get(args.workload, T=args.T)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = vrt.make_config(B=w.B, V=w.V, dtype=w.dtype, trunc=w.trunc, K=w.K, m=w.m, probe=w.probe,
+                          D=w.D, W=w.W, R=w.R, mode=w.mode, budget=w.budget, T=w.T, eps_m0=w.eps_m0,
+                          alpha=w.alpha, lam=w.lam, gamma=w.gamma, delta=w.delta, rho=w.rho)
+    L = vrt.tree_layout_of(cfg)
+    B, V, D, N, FP, K = w.B, w.V, w.D, L.N, L.FP, w.K
+    esz = 2 if w.dtype == synth.BF16 else 4
+    per = 16 // esz
+    ld = (V + per - 1) // per * per
+    tdt = torch.int16 if w.dtype == synth.BF16 else torch.float32
+    n_draft = 1 + (D - 1) * FP
+    draft = torch.empty((B, n_draft, ld), dtype=tdt, device=dev)
+    target = torch.empty((B, N, ld), dtype=tdt, device=dev)
+    tree = torch.zeros(vrt.tree_bytes(cfg), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(vrt.workspace_bytes(cfg), dtype=torch.uint8, device=dev)
+    views = vrt.tree_views(cfg, tree)
+    stats = torch.zeros((B, 8), dtype=torch.int32, device=dev)
+    out_tokens = torch.zeros((B, D + 1), dtype=torch.int32, device=dev)
+    out_nodes = torch.zeros((B, D), dtype=torch.int32, device=dev)
+    out_len = torch.zeros(B, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    # ---- inputs: the generator plays the draft model along the GPU's own frontier,
+    # layer by layer, then the target model on the emitted tree (untimed)
+    p = w.params()
+    zipf = torch.from_numpy(w.tables()).to(dev)
+    rk = [synth.root_key(w.gen_seed, b) for b in range(B)]
+    root_keys = torch.tensor([k - (1 << 64) if k >= (1 << 63) else k for k in rk],
+                             dtype=torch.int64, device=dev)
+    tree_of = torch.arange(B, dtype=torch.int32, device=dev)
+    tmp = torch.empty((B, FP, ld), dtype=tdt, device=dev)
+    seed, step = args.seed, 0
+
+    def layer_rows(layer):
+        r0 = 0 if layer == 0 else 1 + (layer - 1) * FP
+        return draft[:, r0:]
+
+    def layer_base(l):
+        return 0 if l == 0 else K + (l - 1) * FP * K
+
+    keys_prev = root_keys.view(B, 1)
+    synth.rows_dev(p, zipf, keys_prev.reshape(-1), tree_of, tmp[:, 0], synth.DRAFT, stream)
+    draft[:, 0].copy_(tmp[:, 0])
+    vrt.build_tree(cfg, 0, layer_rows(0), ld, n_draft * ld, seed, step, tree, ws, stats)
+    for layer in range(1, D):
+        keys = torch.zeros((B, FP), dtype=torch.int64, device=dev)
+        synth.frontier_keys_dev(B, K, layer_base(layer - 1), keys_prev, views["front"],
+                                views["n_front"], views["cand_token"], keys, stream)
+        synth.rows_dev(p, zipf, keys.reshape(-1), tree_of.repeat_interleave(FP),
+                       tmp.view(B * FP, ld), synth.DRAFT, stream)
+        r0 = 1 + (layer - 1) * FP
+        draft[:, r0:r0 + FP].copy_(tmp)
+        vrt.build_tree(cfg, layer, layer_rows(layer), ld, n_draft * ld, seed, step, tree, ws, stats)
+        keys_prev = keys
+    vrt.build_tree(cfg, vrt.FINISH, None, 0, 0, seed, step, tree, ws, stats)
+    node_keys = torch.zeros((B, N), dtype=torch.int64, device=dev)
+    synth.tree_keys_dev(B, N, root_keys, views["n_nodes"], views["node_token"], views["node_parent"],
+                        node_keys, stream)
+    synth.rows_dev(p, zipf, node_keys.reshape(-1), tree_of.repeat_interleave(N), target.view(B * N, ld),
+                   synth.TARGET, stream)
+    torch.cuda.synchronize()
+    n_nodes = views["n_nodes"].cpu()
+    del tmp
+
+    # ---- timed: K whole steps (every build layer, finish, verification)
+    def one_step(evs=None):
+        if evs:
+            evs[0].record()
+        if not args.verify_only:
+            for layer in range(D):
+                vrt.build_tree(cfg, layer, layer_rows(layer), ld, n_draft * ld, seed, step, tree, ws,
+                               stats)
+            vrt.build_tree(cfg, vrt.FINISH, None, 0, 0, seed, step, tree, ws, stats)
+        if evs:
+            evs[1].record()
+        vrt.verify_tree(cfg, target, ld, N * ld, tree, seed, step, ws, out_tokens, out_nodes, out_len,
+                        stats)
+        if evs:
+            evs[2].record()
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        one_step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    build_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    verify_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+
+    st = stats.cpu()
+    lens = out_len.cpu().float()
+    verify_bytes = int(n_nodes.sum()) * V * esz
+    draft_rows = B * (1 + (D - 1) * FP) if w.mode == workloads.TOPR else None
+    build_bytes = draft_rows * V * esz if draft_rows else None
+    verify_gbs = verify_bytes / (verify_ms * 1e-3) / 1e9
+    result = {
+        "metric": "verified draft trees/sec and HBM GB/s (% peak) at B=32, V=128256, R=60",
+        "value": B / (ms_per_step * 1e-3) if not args.verify_only else B / (verify_ms * 1e-3),
+        "unit": "trees/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: B={B}, V={V} {'bf16' if esz == 2 else 'fp32'} logits, "
+                               f"R={w.R}, D={D}, K=W={w.width}, m={w.m}, T={w.T}, trunc={w.trunc}",
+                   "B": B, "V": V, "R": w.R, "D": D, "K": K, "m": w.m, "T": w.T},
+        "roofline": {"bound": "hbm", "kernel": "vrt_verify_tree (row pass + walk)",
+                     "achieved": verify_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": verify_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": verify_bytes, "avg_launch_ms": verify_ms},
+        "verify_ms": verify_ms,
+        "verify_trees_per_s": B / (verify_ms * 1e-3),
+        "build_ms": build_ms if not args.verify_only else None,
+        "build_gbps": (build_bytes / (build_ms * 1e-3) / 1e9) if (build_bytes and not args.verify_only)
+        else None,
+        "verified_tokens_per_s": float(lens.sum()) / (ms_per_step * 1e-3),
+        "mean_tokens_per_tree": float(lens.mean()),
+        "status_bits": int((st[:, 0] != 0).sum()),
+    }
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(w, seed, args.cpu_trees)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -108,14 +108,19 @@ def test_build_and_step_match_oracle(gpu, name, w):
         L.verify(target, ld, seed, step, zero_stats=False)
         for b, s in enumerate(steps):
             total += 1
-            if s.build_exempt:
+            try:
+                compare_tree(w, s, L, b)
+            except AssertionError:
+                # a mismatch is allowed only after a probe draw within 1e-6 of a boundary
+                if not s.build_exempt:
+                    raise
                 exempt += 1
                 continue
-            compare_tree(w, s, L, b)
-            if s.verify_exempt == 0:
-                Lt = len(s.out_tokens)
-                assert L.out_len[b].item() == Lt
-                np.testing.assert_array_equal(L.out_tokens[b, :Lt].cpu().numpy(), s.out_tokens)
+            Lt = len(s.out_tokens)
+            same = L.out_len[b].item() == Lt and np.array_equal(
+                L.out_tokens[b, :Lt].cpu().numpy(), s.out_tokens)
+            assert same or s.verify_exempt > 0, (b, L.out_tokens[b], s.out_tokens)
+    print(f"{name}: {total} trees, {exempt} differ after a near-boundary probe draw")
     assert exempt <= max(1, total // 10), (exempt, total)
 
 

@@ -52,46 +52,49 @@ def run_case(w, seed, step, dev):
 
 
 def check(steps, L):
+    """Compare every node; a mismatch is allowed only at a node the oracle marks
+    as having a draw within 1e-6 of its threshold. Returns (exempt, mismatched, nodes)."""
     node_out = L.node_out.cpu().numpy()
     out_tok = L.out_tokens.cpu().numpy()
     out_len = L.out_len.cpu().numpy()
     out_nodes = L.out_nodes.cpu().numpy()
     stats = L.stats.cpu().numpy()
-    n_exempt = n_nodes = 0
+    n_exempt = n_miss = n_nodes = 0
     for b, s in enumerate(steps):
         pn = s.per_node
         n = s.view["n_nodes"]
         assert stats[b, 0] == 0, f"status bits {stats[b, 0]:#x} on tree {b}"
         for i in range(n):
             n_nodes += 1
+            g = node_out[b, i]
+            same = g[0] == pn["accept"][i] and (pn["accept"][i] >= 0 or g[1] == pn["token"][i])
             if pn["exempt"][i]:
                 n_exempt += 1
+                n_miss += not same
                 continue
-            g = node_out[b, i]
-            assert g[0] == pn["accept"][i], (b, i, g, pn[i])
+            assert same, (b, i, g, pn[i])
             if pn["accept"][i] < 0:
-                assert g[1] == pn["token"][i], (b, i, g, pn[i])
                 W = np.array([g[3]], np.int32).view(np.float32)[0]
                 assert abs(W - pn["W"][i]) <= 1e-5, (b, i, W, pn["W"][i])
             assert (g[2] & 0xFF) == pn["n_tests"][i], (b, i, g, pn[i])
-        if s.verify_exempt == 0:
-            L_ = len(s.out_tokens)
-            assert out_len[b] == L_
-            np.testing.assert_array_equal(out_tok[b, :L_], s.out_tokens)
-            np.testing.assert_array_equal(out_nodes[b, :L_ - 1], s.out_nodes)
-            assert np.all(out_tok[b, L_:] == -1)
-    return n_exempt, n_nodes
+        L_ = len(s.out_tokens)
+        same = out_len[b] == L_ and np.array_equal(out_tok[b, :L_], s.out_tokens) and \
+            np.array_equal(out_nodes[b, :L_ - 1], s.out_nodes) and np.all(out_tok[b, L_:] == -1)
+        assert same or s.verify_exempt > 0, (b, out_tok[b], s.out_tokens)
+    return n_exempt, n_miss, n_nodes
 
 
 @pytest.mark.parametrize("name,w", CASES, ids=[c[0] for c in CASES])
 def test_verify_matches_oracle(gpu, name, w):
-    tot_ex = tot = 0
+    tot_ex = tot_miss = tot = 0
     for seed, step in [(1, 0), (2, 5), (3, 77)]:
         steps, L = run_case(w, seed, step, gpu)
-        ex, n = check(steps, L)
+        ex, miss, n = check(steps, L)
         tot_ex += ex
+        tot_miss += miss
         tot += n
-    assert tot_ex <= max(2, tot // 100), (tot_ex, tot)
+    print(f"{name}: {tot} nodes, {tot_ex} with a near-threshold draw, {tot_miss} of those differ")
+    assert tot_miss <= max(1, tot_ex // 10), (tot_miss, tot_ex)
 
 
 def test_verify_bad_target_rows_set_status(gpu):

@@ -484,10 +484,10 @@ __global__ __launch_bounds__(256) void k_finish(const Cfg c, const TreePtrs t) {
     for (int i = 0; i < n; ++i) {
       const int k = s_cnt[i];
       s_cnt[i] = off;
-      t.child_off[nb + i] = off;
+      t.child_off[(int64_t)b * (c.N + 1) + i] = off;
       off += k;
     }
-    t.child_off[nb + n] = off;
+    t.child_off[(int64_t)b * (c.N + 1) + n] = off;
     t.n_nodes[b] = n;
   }
   __syncthreads();

@@ -189,7 +189,8 @@ __global__ __launch_bounds__(kVB) void k_vrow(const VArgs a) {
 
   // ---- 3. the node's kept children, in slot order
   const int64_t nb = (int64_t)b * c.N;
-  int co = a.t.child_off[nb + i], ce = a.t.child_off[nb + i + 1];
+  const int64_t cob = (int64_t)b * (c.N + 1);  // child_off rows hold N + 1 entries
+  int co = a.t.child_off[cob + i], ce = a.t.child_off[cob + i + 1];
   int nc = ce - co;
   if (co < 0 || co > c.N || nc < 0) nc = 0;
   if (nc > c.K) nc = c.K;
