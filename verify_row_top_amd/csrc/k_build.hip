@@ -1,18 +1,21 @@
 // Draft-tree construction on gfx950 (RheoSampling framework flowchart, key designs
-// 1-2; SMART key design 3 as the switchable keep rule).
+// 1-2; SMART key design 3 as the switchable keep rule). Per layer, three kernels:
 //
-// k_support_expand: one 1024-thread block per expanded parent. The block streams the
-//   parent's draft row once (four 16-byte loads per thread in flight) and keeps the
-//   row's top-`trunc` entries by (logit desc, token id asc) in an LDS candidate buffer
-//   behind a running threshold: the first pass seeds the threshold with the
-//   trunc-th largest of the threads' own maxima, later elements are appended only if
-//   they beat it, and a full buffer is compacted by a bitonic sort that raises it.
-//   Wave 0 then expands the parent: untempered softmax on the support with the fixed
-//   ranking recipe, tempered softmax in fp64, the probe draw from the tempered tail,
-//   the proxy min{q(x_m), z}, the K child slots and the parent's tail table.
-// k_beam / k_smart: one block per tree ranks the layer's children by (path score
-//   desc, creation index asc) and keeps the top W (top-R mode) or runs SMART's
-//   sequential keep rule over them.
+// k_seg_select: one 512-thread block per 32 KB segment of an expanded parent's
+//   draft row (all four 16-byte loads per thread in flight, non-temporal). The
+//   block seeds a threshold with the trunc-th largest of its threads' maxima (a key
+//   that at least trunc elements reach), compares every element's value against it,
+//   appends the survivors' exact keys (logit desc, token id asc) to an LDS buffer
+//   (wave-aggregated), compacts by a bitonic sort when the buffer fills, and writes
+//   the segment's sorted top-trunc keys to the workspace.
+// k_merge_expand: one block per parent merges its segments' lists into the row's
+//   top-trunc support, and wave 0 expands the parent: untempered softmax on the
+//   support with the fixed ranking recipe, tempered softmax in fp64, the probe draw
+//   from the tempered tail, the proxy min{q(x_m), z}, the K child slots and the
+//   parent's tail table.
+// k_rank_layer: one block per tree ranks the layer's children by (path score desc,
+//   creation index asc) and keeps the top W (top-R mode) or runs SMART's sequential
+//   keep rule over them.
 // k_finish: one block per tree emits the tree: the global top R by the same key
 //   (or SMART's admitted nodes), parents before children, child lists in slot
 //   order, and the probe tails the verifier needs.
@@ -22,8 +25,13 @@
 namespace vrt {
 namespace {
 
-constexpr int kSB = 1024;  // threads per support block
-constexpr int kSU = 4;     // 16-byte loads per thread per pass
+constexpr int kST = 512;       // threads per segment block
+constexpr int kSL = 4;         // 16-byte loads per thread per segment
+constexpr int kSegCap = 2048;  // LDS candidate buffer of a segment block (keys)
+constexpr int kMergeCap = 4096;  // keys a merge block sorts at once
+
+template <int DT>
+constexpr int seg_elems() { return kST * kSL * (DT == VRT_BF16 ? 8 : 4); }
 
 __device__ __forceinline__ int layer_base(const Cfg& c, int l) {
   return l == 0 ? 0 : c.K + (l - 1) * c.P * c.K;
@@ -37,6 +45,9 @@ __device__ __forceinline__ int row_of(const Cfg& c, int cidx) {
   const int l = layer_of(c, cidx);
   return row_base(c, l) + (cidx - layer_base(c, l)) / c.K;
 }
+__device__ __forceinline__ int slot_of(const Cfg& c, int cidx) {
+  return (cidx - layer_base(c, layer_of(c, cidx))) % c.K;
+}
 
 struct BArgs {
   Cfg c;
@@ -47,10 +58,28 @@ struct BArgs {
   uint64_t seed;
   uint32_t step;
   uint32_t* stats;
+  int G;               // segments per row
+  uint64_t* seg_keys;  // [B][FP][G][TC] sorted top keys of each segment
+  int* seg_cnt;        // [B][FP][G] count | (non-finite seen) << 30
 };
 
-// Wave-aggregated append of `key` into the LDS buffer when `pass`. Returns true if
-// stored; sets *ovf when the buffer is full (the key is then retried later).
+// The node frontier position j of tree b expands at this layer (-1 = root), or -2
+// if the position is empty (fewer parents) or holds an index the previous layer did
+// not produce.
+__device__ __forceinline__ int row_node(const BArgs& a, int b, int j) {
+  const Cfg& c = a.c;
+  if (a.layer == 0) return j == 0 ? -1 : -2;
+  const int nf = a.t.n_front[b];
+  if (j >= min(max(nf, 0), c.FP)) return -2;
+  const int node = a.t.front[(int64_t)b * c.FP + j];
+  const int lo = layer_base(c, a.layer - 1), hi = lo + layer_span(c, a.layer - 1);
+  if (node < lo || node >= hi) return -2;
+  if ((a.t.cand_kind[(int64_t)b * c.NC + node] & 0xFF) == 0) return -2;
+  return node;
+}
+
+// Wave-aggregated append of `key` into an LDS buffer of `cap` keys when `pass`.
+// Returns true if stored; sets *ovf when the buffer is full (retried later).
 __device__ __forceinline__ bool append(bool pass, uint64_t key, uint64_t* buf, int cap, int* cnt,
                                        int* ovf) {
   const uint64_t mask = ballot(pass);
@@ -70,207 +99,185 @@ __device__ __forceinline__ bool append(bool pass, uint64_t key, uint64_t* buf, i
   return false;
 }
 
-// Sort the first min(*cnt, cap) keys descending (zero padded to a power of two).
-__device__ void sort_buffer(uint64_t* buf, int cap, int* cnt, int* n_out) {
-  __syncthreads();
-  const int n = min(*cnt, cap);
+// Sort the first min(n, cap) keys of buf descending (zero padded to a power of two).
+__device__ int sort_prefix(uint64_t* buf, int n, int cap) {
+  n = min(n, cap);
   const int np = next_pow2(max(n, 2));
   for (int t = n + threadIdx.x; t < np; t += blockDim.x) buf[t] = 0ull;
   __syncthreads();
   bitonic_desc(buf, np);
-  *n_out = n;
+  return n;
+}
+
+// A thread's segment as one vector value of 16 words (registers, never memory).
+typedef uint32_t Words __attribute__((ext_vector_type(16)));
+
+template <int DT, int K>
+__device__ __forceinline__ float elem(const Words wd) {
+  if constexpr (DT == VRT_BF16) return (K & 1) ? bf16_hi(wd[K >> 1]) : bf16_lo(wd[K >> 1]);
+  else return __uint_as_float(wd[K]);
+}
+
+// Element k (a per-lane value); the dynamic extract of a register vector lowers to
+// a select chain.
+template <int DT>
+__device__ __forceinline__ float elem_at(const Words wd, int k) {
+  const uint32_t word = wd[DT == VRT_BF16 ? (k >> 1) : k];
+  if constexpr (DT == VRT_BF16) return (k & 1) ? bf16_hi(word) : bf16_lo(word);
+  else return __uint_as_float(word);
 }
 
 template <int DT>
-__global__ __launch_bounds__(kSB) void k_support_expand(const BArgs a) {
+__global__ __launch_bounds__(kST) void k_seg_select(const BArgs a) {
   const Cfg& c = a.c;
-  const int b = blockIdx.y;
-  const int j = blockIdx.x;
-  const int layer = a.layer;
+  const int g = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
+  if (row_node(a, b, j) == -2) return;
   const int tid = threadIdx.x;
-  const int64_t ncb = (int64_t)b * c.NC;
-  const int cbase = layer_base(c, layer) + j * c.K;
-  const int ridx = row_base(c, layer) + j;
-
-  // which node this block expands (root at layer 0)
-  int node = -1;
-  bool active = true;
-  if (layer == 0) {
-    // a new step: forget every candidate of the previous one, reset SMART's state
-    for (int t = c.K + tid; t < c.NC; t += blockDim.x) a.t.cand_kind[ncb + t] = 0;
-    if (tid == 0) {
-      double* sm = a.t.smart + (int64_t)b * 8;
-      sm[0] = 0.0; sm[1] = 1.0; sm[2] = 1.0; sm[3] = 0.0; sm[4] = 0.0;
-      sm[5] = sm[6] = sm[7] = 0.0;
-    }
-  } else {
-    const int nf = a.t.n_front[b];
-    active = j < min(max(nf, 0), c.FP);
-    if (active) {
-      node = a.t.front[(int64_t)b * c.FP + j];
-      const int pl = layer - 1;
-      const int lo = layer_base(c, pl), hi = lo + layer_span(c, pl);
-      active = node >= lo && node < hi && (a.t.cand_kind[ncb + node] & 0xFF) != 0;
-    }
-  }
-  if (!active) {
-    for (int s = tid; s < c.K; s += blockDim.x) a.t.cand_kind[ncb + cbase + s] = 0;
-    if (tid == 0) a.t.row_tail_n[(int64_t)b * c.NR + ridx] = 0;
-    return;
-  }
-
   constexpr int esz = DT == VRT_BF16 ? 2 : 4;
-  constexpr int EPL = 16 / esz;       // elements per 16-byte load
-  constexpr int NE = kSU * EPL;       // elements per thread per pass
+  constexpr int EPL = 16 / esz;    // elements per 16-byte load
+  constexpr int NE = kSL * EPL;    // elements per thread (64 bf16, 32 fp32)
+  constexpr int S = seg_elems<DT>();
   const int V = c.V;
+  const int base = g * S;
   const char* row = (const char*)a.logits + ((int64_t)b * a.tstride + (int64_t)j * a.ld) * esz;
-  const int cap = 4096;
-  const int TCp = max(128, next_pow2(c.trunc));
 
-  extern __shared__ uint64_t s_buf[];           // [cap] candidate keys
-  float* s_q = (float*)(s_buf + cap);           // [TCp] ranking probabilities
+  __shared__ uint64_t s_buf[kSegCap];
   __shared__ int s_cnt, s_ovf, s_bad;
   __shared__ uint64_t s_thr;
+
+  // this thread's elements: load q covers [base + (q*kST + tid)*EPL, +EPL)
+  Words wd;
+  static_for<kSL>([&](auto q) {
+    const int e0 = base + (q * kST + tid) * EPL;
+    uint4 v = DT == VRT_BF16 ? make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u)
+                             : make_uint4(0xFF800000u, 0xFF800000u, 0xFF800000u, 0xFF800000u);
+    if (e0 < V) v = load_nt(row + (int64_t)e0 * esz);
+    wd[4 * q + 0] = v.x;
+    wd[4 * q + 1] = v.y;
+    wd[4 * q + 2] = v.z;
+    wd[4 * q + 3] = v.w;
+  });
+  auto id_of = [&](int k) { return base + ((k / EPL) * kST + tid) * EPL + (k % EPL); };
+
+  // seed: the trunc-th largest of the threads' maxima (largest value, lowest id)
+  float mx = -INFINITY;
+  int mid = 0x7FFFFFFF;
+  bool bad = false;
+  static_for<NE>([&](auto k) {
+    const float x = elem<DT, k>(wd);
+    const int id = id_of(k);
+    bad |= __builtin_amdgcn_classf(x, 0x203);  // NaN or +inf
+    if (id < V && (x > mx || (x == mx && id < mid))) {
+      mx = x;
+      mid = id;
+    }
+  });
+  s_buf[tid] = (mid < V) ? sup_key(mx, (uint32_t)mid) : 0ull;
   if (tid == 0) {
     s_cnt = 0;
     s_ovf = 0;
     s_bad = 0;
-    s_thr = 0ull;
   }
   __syncthreads();
-
-  const int per_pass = kSB * NE;
-  bool first = true;
-  int bad = 0;
-  for (int base = 0; base < V; base += per_pass) {
-    float x[NE];
-#pragma unroll
-    for (int q = 0; q < kSU; ++q) {
-      const int e0 = base + (q * kSB + tid) * EPL;
-      if constexpr (DT == VRT_BF16) {
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (e0 < V) v = *(const uint4*)((const uint16_t*)row + e0);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          x[q * 8 + 2 * k] = bf16_lo(w[k]);
-          x[q * 8 + 2 * k + 1] = bf16_hi(w[k]);
-        }
-      } else {
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (e0 < V) v = *(const float4*)((const float*)row + e0);
-        x[q * 4 + 0] = v.x;
-        x[q * 4 + 1] = v.y;
-        x[q * 4 + 2] = v.z;
-        x[q * 4 + 3] = v.w;
-      }
+  if (c.trunc <= kST) {
+    bitonic_desc(s_buf, kST);
+    if (tid == 0) {
+      const uint64_t t0 = s_buf[c.trunc - 1];
+      s_thr = t0 ? t0 - 1ull : 0ull;
     }
-    auto id_of = [&](int k) { return base + ((k / EPL) * kSB + tid) * EPL + (k % EPL); };
-#pragma unroll
-    for (int k = 0; k < NE; ++k)
-      if (id_of(k) < V) bad |= __builtin_isnan(x[k]) || x[k] == INFINITY;
-
-    if (first) {
-      // seed the threshold: the trunc-th largest of the threads' maxima is a key
-      // that at least trunc elements reach
-      first = false;
-      uint64_t mk = 0ull;
-#pragma unroll
-      for (int k = 0; k < NE; ++k) {
-        const int id = id_of(k);
-        if (id < V && !__builtin_isnan(x[k])) {
-          const uint64_t key = sup_key(x[k], (uint32_t)id);
-          mk = key > mk ? key : mk;
-        }
-      }
-      if (c.trunc <= kSB) {
-        s_buf[tid] = mk;
-        __syncthreads();
-        bitonic_desc(s_buf, kSB);
-        if (tid == 0) {
-          const uint64_t t0 = s_buf[c.trunc - 1];
-          s_thr = t0 ? t0 - 1ull : 0ull;
-        }
-        __syncthreads();
-      }
-    }
-
-    uint32_t done = 0u;
-    for (;;) {
-      const uint64_t thr = s_thr;
-#pragma unroll
-      for (int k = 0; k < NE; ++k) {
-        const int id = id_of(k);
-        const bool ok = id < V && !__builtin_isnan(x[k]) && !((done >> k) & 1u);
-        const uint64_t key = ok ? sup_key(x[k], (uint32_t)id) : 0ull;
-        if (append(ok && key > thr, key, s_buf, cap, &s_cnt, &s_ovf)) done |= 1u << k;
-      }
-      __syncthreads();
-      const int ov = s_ovf;
-      __syncthreads();
-      if (!ov) break;
-      // compaction: keep the best trunc keys, raise the threshold to the trunc-th
-      int n;
-      sort_buffer(s_buf, cap, &s_cnt, &n);
-      if (tid == 0) {
-        if (n >= c.trunc) s_thr = s_buf[c.trunc - 1];
-        s_cnt = min(n, c.trunc);
-        s_ovf = 0;
-      }
-      __syncthreads();
-    }
+  } else if (tid == 0) {
+    s_thr = 0ull;
   }
   if (bad) atomicOr(&s_bad, 1);
-  int n;
-  sort_buffer(s_buf, cap, &s_cnt, &n);  // final: sorted support in s_buf[0..n)
-  const int n_sup = min(n, c.trunc);
-  if (threadIdx.x >= kWave) return;
+  __syncthreads();
 
-  // ---- expansion by wave 0
-  const int lane = lane_id();
-  const int64_t ktb = (int64_t)b * c.NR + ridx;
-  uint32_t st = s_bad ? VRT_ST_DRAFT_NONFINITE : 0u;
-  const float M = n_sup > 0 ? sup_key_val(s_buf[0]) : -INFINITY;
-  if (n_sup == 0 || M == -INFINITY) st |= VRT_ST_DRAFT_EMPTY;
-  if (st) {
-    if (lane == 0 && a.stats) atomicOr(a.stats + (int64_t)b * 8, st);
-    for (int s = lane; s < c.K; s += kWave) a.t.cand_kind[ncb + cbase + s] = 0;
-    if (lane == 0) a.t.row_tail_n[ktb] = 0;
-    return;
+  uint64_t done = 0ull;
+  for (;;) {
+    const uint64_t thr = s_thr;
+    const float thr_f = thr ? sup_key_val(thr) : -INFINITY;
+    // cheap filter: one compare per element against the threshold's value
+    uint64_t cand = 0ull;
+    static_for<NE>([&](auto k) { cand |= (elem<DT, k>(wd) >= thr_f ? 1ull : 0ull) << k; });
+    cand &= ~done;
+    // exact keys only for the survivors
+    while (ballot(cand != 0ull)) {
+      const bool has = cand != 0ull;
+      const int k = has ? __builtin_ctzll(cand) : 0;
+      const float x = elem_at<DT>(wd, k);
+      const int id = id_of(k);
+      const bool ok = has && id < V;
+      const uint64_t key = ok ? sup_key(x, (uint32_t)id) : 0ull;
+      if (append(ok && key > thr, key, s_buf, kSegCap, &s_cnt, &s_ovf)) done |= 1ull << k;
+      if (has) cand &= cand - 1ull;
+    }
+    __syncthreads();
+    const int ov = s_ovf;
+    const int cnt = s_cnt;
+    __syncthreads();
+    if (!ov) break;
+    // compaction: keep the best trunc keys, raise the threshold to the trunc-th
+    const int n = sort_prefix(s_buf, cnt, kSegCap);
+    if (tid == 0) {
+      if (n >= c.trunc) s_thr = s_buf[c.trunc - 1];
+      s_cnt = min(n, c.trunc);
+      s_ovf = 0;
+    }
+    __syncthreads();
   }
-  const int bs = TCp / kWave;  // ranks per lane: lane owns [lane*bs, lane*bs + bs)
+  const int n = min(sort_prefix(s_buf, s_cnt, kSegCap), c.trunc);
+  const int64_t sg = ((int64_t)b * c.FP + j) * a.G + g;
+  for (int k = tid; k < n; k += kST) a.seg_keys[sg * c.TC + k] = s_buf[k];
+  if (tid == 0) a.seg_cnt[sg] = n | (s_bad ? (1 << 30) : 0);
+}
+
+// Expansion of one parent by wave 0 (RheoSampling key design 2), BS support ranks
+// per lane: lane l owns ranks [l*BS, l*BS + BS).
+template <int BS>
+__device__ void expand_row(const BArgs& a, int b, int node, int n_sup, const uint64_t* s_buf,
+                           float* s_q, int64_t ncb, int cbase, int64_t ktb) {
+  const Cfg& c = a.c;
+  const int lane = lane_id();
+  const float M = sup_key_val(s_buf[0]);
   const int m = c.probe ? c.m : 0;
-  float e[16], tmp[16];
-  double et[16];
-  for (int k = 0; k < bs; ++k) {
-    const int r = lane * bs + k;
+  float e[BS];
+  double et[BS];
+#pragma unroll
+  for (int k = 0; k < BS; ++k) {
+    const int r = lane * BS + k;
     const float v = r < n_sup ? sup_key_val(s_buf[r]) : -INFINITY;
     e[k] = r < n_sup ? exp_rank(v - M) : 0.0f;
     et[k] = r < n_sup ? exp(((double)v - (double)M) * (double)c.invT) : 0.0;
   }
   // aligned pairwise sums: inside the lane's block, then across lanes
-  auto pairwise = [&](const float* in) -> float {
-    for (int k = 0; k < bs; ++k) tmp[k] = in[k];
-    for (int w = bs >> 1; w >= 1; w >>= 1)
-      for (int k = 0; k < w; ++k) tmp[k] = tmp[2 * k] + tmp[2 * k + 1];
-    return wave_sum(tmp[0]);
+  auto pairwise = [&](const float (&in)[BS]) -> float {
+    float t[BS];
+#pragma unroll
+    for (int k = 0; k < BS; ++k) t[k] = in[k];
+#pragma unroll
+    for (int w = BS >> 1; w >= 1; w >>= 1)
+#pragma unroll
+      for (int k = 0; k < w; ++k) t[k] = t[2 * k] + t[2 * k + 1];
+    return wave_sum(t[0]);
   };
   const float E = pairwise(e);
-  float q[16], qt[16];
-  for (int k = 0; k < bs; ++k) {
-    const int r = lane * bs + k;
-    q[k] = e[k] / E;
-    qt[k] = r < m ? 0.0f : q[k];
-    if (r < TCp) s_q[r] = q[k];
+  float qt[BS];
+#pragma unroll
+  for (int k = 0; k < BS; ++k) {
+    const int r = lane * BS + k;
+    const float q = e[k] / E;
+    qt[k] = r < m ? 0.0f : q;
+    s_q[r] = q;
   }
   const float zr = pairwise(qt);
   double zl = 0.0;
-  for (int k = 0; k < bs; ++k) zl += et[k];
+#pragma unroll
+  for (int k = 0; k < BS; ++k) zl += et[k];
   const double Z = wave_sum(zl);
   double tl = 0.0;
-  for (int k = 0; k < bs; ++k) {
+#pragma unroll
+  for (int k = 0; k < BS; ++k) {
     et[k] = et[k] / Z;  // q_T
-    if (lane * bs + k >= m) tl += et[k];
+    if (lane * BS + k >= m) tl += et[k];
   }
   const double zT = wave_sum(tl);
   wave_sync();
@@ -289,13 +296,12 @@ __global__ __launch_bounds__(kSB) void k_support_expand(const BArgs a) {
       const int src = __builtin_ctzll(hit);
       if (lane == src) {
         double cum = excl;
-        for (int k = 0; k < bs; ++k) {
-          const int r = lane * bs + k;
-          if (r < m) continue;
-          cum += et[k];
-          if (tgt < cum) {
-            pick = r;
-            break;
+#pragma unroll
+        for (int k = 0; k < BS; ++k) {
+          const int r = lane * BS + k;
+          if (r >= m && pick < 0) {
+            cum += et[k];
+            if (tgt < cum) pick = r;
           }
         }
       }
@@ -303,8 +309,9 @@ __global__ __launch_bounds__(kSB) void k_support_expand(const BArgs a) {
     }
     if (pick < 0) {  // rounding exhausted the sum: the last tail rank with mass
       int last = -1;
-      for (int k = 0; k < bs; ++k) {
-        const int r = lane * bs + k;
+#pragma unroll
+      for (int k = 0; k < BS; ++k) {
+        const int r = lane * BS + k;
         if (r >= m && r < n_sup && et[k] > 0.0) last = r;
       }
       for (int o = 1; o < kWave; o <<= 1) last = max(last, __shfl_xor(last, o, kWave));
@@ -323,36 +330,125 @@ __global__ __launch_bounds__(kSB) void k_support_expand(const BArgs a) {
   // tail table of this row: ranks m.. with q~ = q_T / z_T
   const int ntail = (js >= 0) ? n_sup - m : 0;
   if (lane == 0) a.t.row_tail_n[ktb] = ntail;
-  for (int k = 0; k < bs; ++k) {
-    const int r = lane * bs + k;
+#pragma unroll
+  for (int k = 0; k < BS; ++k) {
+    const int r = lane * BS + k;
     if (r >= m && r < m + ntail) {
       a.t.row_tail_id[ktb * c.TC + (r - m)] = (int)sup_key_id(s_buf[r]);
       a.t.row_tail_q[ktb * c.TC + (r - m)] = (float)(et[k] / zT);
     }
   }
 
-  // child slots (one lane): DET ranks, the probe, then fillers in rank order
-  if (lane == 0) {
-    const float sp = node < 0 ? 1.0f : a.t.cand_score[ncb + node];
-    int slot = 0;
-    auto put = [&](int r, int kind, float qv) {
-      const int64_t ci = ncb + cbase + slot;
-      a.t.cand_token[ci] = (int)sup_key_id(s_buf[r]);
-      a.t.cand_parent[ci] = node;
-      a.t.cand_score[ci] = sp * qv;
-      a.t.cand_kind[ci] = kind;
-      ++slot;
-    };
+  // child slots: DET ranks, the probe, then fillers in rank order. Lane s writes slot s.
+  const float sp = node < 0 ? 1.0f : a.t.cand_score[ncb + node];
+  int r_of_slot = -1, kind = 0;
+  {
+    const int m_det = c.probe ? min(m, n_sup) : 0;
+    const int s = lane;
     if (!c.probe) {
-      for (int r = 0; r < n_sup && slot < c.K; ++r) put(r, VRT_DET, s_q[r]);
+      if (s < n_sup) r_of_slot = s, kind = VRT_DET;
+    } else if (s < m_det) {
+      r_of_slot = s, kind = VRT_DET;
+    } else if (js >= 0 && s == m_det) {
+      r_of_slot = js, kind = VRT_PROBE;
     } else {
-      for (int r = 0; r < m && r < n_sup && slot < c.K; ++r) put(r, VRT_DET, s_q[r]);
-      if (js >= 0 && slot < c.K) put(js, VRT_PROBE, proxy);
-      for (int r = m; r < n_sup && slot < c.K; ++r)
-        if (r != js) put(r, VRT_FILL, s_q[r]);
+      const int f = s - m_det - (js >= 0 ? 1 : 0);  // filler index
+      int r = m + f;
+      if (js >= 0 && r >= js) ++r;
+      if (r < n_sup) r_of_slot = r, kind = VRT_FILL;
     }
-    for (; slot < c.K; ++slot) a.t.cand_kind[ncb + cbase + slot] = 0;
   }
+  if (lane < c.K) {
+    const int64_t ci = ncb + cbase + lane;
+    if (r_of_slot >= 0) {
+      a.t.cand_token[ci] = (int)sup_key_id(s_buf[r_of_slot]);
+      a.t.cand_parent[ci] = node;
+      a.t.cand_score[ci] = sp * (kind == VRT_PROBE ? proxy : s_q[r_of_slot]);
+      a.t.cand_kind[ci] = kind;
+    } else {
+      a.t.cand_kind[ci] = 0;
+    }
+  }
+}
+
+template <int BS>
+__global__ __launch_bounds__(256) void k_merge_expand(const BArgs a) {
+  const Cfg& c = a.c;
+  const int j = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int64_t ncb = (int64_t)b * c.NC;
+  const int cbase = layer_base(c, a.layer) + j * c.K;
+  const int ridx = row_base(c, a.layer) + j;
+  const int64_t ktb = (int64_t)b * c.NR + ridx;
+
+  if (a.layer == 0) {
+    // a new step: forget every candidate of the previous one, reset SMART's state
+    for (int t = c.K + tid; t < c.NC; t += blockDim.x) a.t.cand_kind[ncb + t] = 0;
+    if (tid == 0) {
+      double* sm = a.t.smart + (int64_t)b * 8;
+      sm[0] = 0.0; sm[1] = 1.0; sm[2] = 1.0; sm[3] = 0.0; sm[4] = 0.0;
+      sm[5] = sm[6] = sm[7] = 0.0;
+    }
+  }
+  const int node = row_node(a, b, j);
+  if (node == -2) {
+    for (int s = tid; s < c.K; s += blockDim.x) a.t.cand_kind[ncb + cbase + s] = 0;
+    if (tid == 0) a.t.row_tail_n[ktb] = 0;
+    return;
+  }
+
+  extern __shared__ uint64_t s_buf[];  // [kMergeCap] keys
+  float* s_q = (float*)(s_buf + kMergeCap);
+  __shared__ int s_bad;
+  if (tid == 0) s_bad = 0;
+  // merge the segments' sorted lists: keep the running top trunc in s_buf[0..TC),
+  // fill the rest with whole lists, sort, repeat
+  const int TC = c.TC;
+  const int64_t sg0 = ((int64_t)b * c.FP + j) * a.G;
+  int have = 0;  // keys in s_buf[0..TC) from earlier rounds
+  int g = 0;
+  const int per_round = max(1, kMergeCap / TC - 1);
+  for (;;) {
+    const int gend = min(a.G, g + per_round);
+    // lists g..gend-1 go to s_buf[TC + (gg - g) * TC ..]
+    for (int x = tid; x < (gend - g) * TC; x += blockDim.x) {
+      const int gg = g + x / TC, k = x % TC;
+      const int cw = a.seg_cnt[sg0 + gg];
+      const int cnt = cw & 0x3FFFFFFF;
+      if (k == 0 && (cw >> 30)) s_bad = 1;
+      s_buf[TC + x] = k < cnt ? a.seg_keys[(sg0 + gg) * TC + k] : 0ull;
+    }
+    for (int k = have + tid; k < TC; k += blockDim.x) s_buf[k] = 0ull;
+    __syncthreads();
+    sort_prefix(s_buf, TC + (gend - g) * TC, kMergeCap);
+    __syncthreads();
+    have = TC;
+    g = gend;
+    if (g >= a.G) break;
+  }
+  // support size: the non-empty keys among the top trunc
+  __shared__ int s_nsup;
+  if (tid == 0) {
+    int n = 0;
+    while (n < TC && s_buf[n] != 0ull) ++n;
+    s_nsup = n;
+  }
+  __syncthreads();
+  const int n_sup = s_nsup;
+  if (tid >= kWave) return;
+
+  // ---- expansion by wave 0
+  const int lane = lane_id();
+  uint32_t st = s_bad ? VRT_ST_DRAFT_NONFINITE : 0u;
+  const float M = n_sup > 0 ? sup_key_val(s_buf[0]) : -INFINITY;
+  if (n_sup == 0 || M == -INFINITY) st |= VRT_ST_DRAFT_EMPTY;
+  if (st) {
+    if (lane == 0 && a.stats) atomicOr(a.stats + (int64_t)b * 8, st);
+    for (int s = lane; s < c.K; s += kWave) a.t.cand_kind[ncb + cbase + s] = 0;
+    if (lane == 0) a.t.row_tail_n[ktb] = 0;
+    return;
+  }
+  expand_row<BS>(a, b, node, n_sup, s_buf, s_q, ncb, cbase, ktb);
 }
 
 // Per-tree ranking of the layer's children: top-W frontier (top-R mode) or SMART.
@@ -408,17 +504,24 @@ __global__ __launch_bounds__(256) void k_rank_layer(const Cfg c, const TreePtrs 
   t.n_front[b] = nf;
 }
 
+constexpr int kFT = 1024;  // threads of the finish block
+
 // Emit the tree: node 0 = root, then the kept candidates (parents first).
-__global__ __launch_bounds__(256) void k_finish(const Cfg c, const TreePtrs t) {
+__global__ __launch_bounds__(kFT) void k_finish(const Cfg c, const TreePtrs t) {
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int64_t ncb = (int64_t)b * c.NC;
   const int64_t nb = (int64_t)b * c.N;
-  // dynamic LDS: top-R keys [np] (top-R mode), node -> candidate [N], child counts [N+1]
+  // dynamic LDS: top-R keys [np] (top-R mode), then per node: candidate, parent node,
+  // slot, expansion row holding its tail, tail length, child counts [N+1]
   extern __shared__ uint64_t s_keys[];
   const int np = c.mode == VRT_MODE_TOPR ? next_pow2(max(c.NC, 2)) : 0;
   int* s_ncand = (int*)(s_keys + np);
-  int* s_cnt = s_ncand + c.N;
+  int* s_par = s_ncand + c.N;
+  int* s_slot = s_par + c.N;
+  int* s_trow = s_slot + c.N;
+  int* s_tn = s_trow + c.N;
+  int* s_cnt = s_tn + c.N;
   __shared__ int s_n;
 
   if (c.mode == VRT_MODE_TOPR) {
@@ -444,92 +547,121 @@ __global__ __launch_bounds__(256) void k_finish(const Cfg c, const TreePtrs t) {
     }
     __syncthreads();
     for (int i = 1 + tid; i < s_n; i += blockDim.x) {
-      int cu = t.admitted[nb + i - 1];
+      const int cu = t.admitted[nb + i - 1];
       s_ncand[i] = (cu < 0 || cu >= c.NC) ? 0 : cu;
     }
   }
-  if (tid == 0) s_ncand[0] = -1;
   const int n = s_n;
+  if (tid == 0) s_ncand[0] = -1;
   for (int i = tid; i <= n; i += blockDim.x) s_cnt[i] = 0;
-  __syncthreads();
   for (int i = tid; i < n; i += blockDim.x) {
-    t.tail_n[nb + i] = 0;
-    if (i == 0) {
-      t.node_token[nb] = -1;
-      t.node_parent[nb] = -1;
-      t.node_depth[nb] = 0;
-      t.node_kind[nb] = VRT_ROOT;
-      t.node_cand[nb] = -1;
-      continue;
-    }
+    s_trow[i] = -1;
+    s_tn[i] = 0;
+  }
+  __syncthreads();
+  // nodes: parent node (parents precede children, so it is among nodes 1..i-1)
+  for (int i = 1 + tid; i < n; i += blockDim.x) {
     const int cu = s_ncand[i];
     const int pc = t.cand_parent[ncb + cu];
-    int pn = 0;  // parents precede children, so the parent is among nodes 1..i-1
+    int pn = 0;
     if (pc >= 0)
-      for (int j = i - 1; j >= 1; --j)
-        if (s_ncand[j] == pc) {
-          pn = j;
+      for (int jj = i - 1; jj >= 1; --jj)
+        if (s_ncand[jj] == pc) {
+          pn = jj;
           break;
         }
+    s_par[i] = pn;
+    s_slot[i] = slot_of(c, cu);
+    const int kind = t.cand_kind[ncb + cu] & 0xFF;
+    if (kind == VRT_PROBE) {
+      const int r = row_of(c, cu);
+      s_trow[pn] = r;
+      s_tn[pn] = min(max(t.row_tail_n[(int64_t)b * c.NR + r], 0), c.TC);
+    }
     t.node_cand[nb + i] = cu;
     t.node_token[nb + i] = t.cand_token[ncb + cu];
     t.node_parent[nb + i] = pn;
     t.node_depth[nb + i] = layer_of(c, cu) + 1;
-    t.node_kind[nb + i] = t.cand_kind[ncb + cu] & 0xFF;
+    t.node_kind[nb + i] = kind;
     atomicAdd(&s_cnt[pn], 1);
+  }
+  if (tid == 0) {
+    t.node_token[nb] = -1;
+    t.node_parent[nb] = -1;
+    t.node_depth[nb] = 0;
+    t.node_kind[nb] = VRT_ROOT;
+    t.node_cand[nb] = -1;
   }
   __syncthreads();
   if (tid == 0) {
     int off = 0;
+    const int64_t cob = (int64_t)b * (c.N + 1);
     for (int i = 0; i < n; ++i) {
       const int k = s_cnt[i];
       s_cnt[i] = off;
-      t.child_off[(int64_t)b * (c.N + 1) + i] = off;
+      t.child_off[cob + i] = off;
       off += k;
     }
-    t.child_off[(int64_t)b * (c.N + 1) + n] = off;
+    t.child_off[cob + n] = off;
     t.n_nodes[b] = n;
   }
   __syncthreads();
-  // child lists in slot order; the probe's tail goes to its parent
+  // child lists in slot order
   for (int i = 1 + tid; i < n; i += blockDim.x) {
-    const int pn = t.node_parent[nb + i];
-    const int cu = s_ncand[i];
-    const int slot = (cu - layer_base(c, layer_of(c, cu))) % c.K;
+    const int pn = s_par[i], slot = s_slot[i];
     int before = 0;
-    for (int j = 1; j < n; ++j) {
-      if (j == i || t.node_parent[nb + j] != pn) continue;
-      const int cj = s_ncand[j];
-      if ((cj - layer_base(c, layer_of(c, cj))) % c.K < slot) ++before;
-    }
+    for (int jj = 1; jj < n; ++jj) before += (s_par[jj] == pn && s_slot[jj] < slot);
     t.child[nb + s_cnt[pn] + before] = i;
-    if (t.node_kind[nb + i] == VRT_PROBE) {
-      const int64_t rr = (int64_t)b * c.NR + row_of(c, cu);
-      const int nt = min(max(t.row_tail_n[rr], 0), c.TC);
-      for (int k = 0; k < nt; ++k) {
-        t.tail_id[(nb + pn) * c.TC + k] = t.row_tail_id[rr * c.TC + k];
-        t.tail_q[(nb + pn) * c.TC + k] = t.row_tail_q[rr * c.TC + k];
-      }
-      t.tail_n[nb + pn] = nt;
-    }
   }
+  // probe tails, copied to the probe's parent
+  for (int i = tid; i < n; i += blockDim.x) t.tail_n[nb + i] = s_tn[i];
+  for (int64_t x = tid; x < (int64_t)n * c.TC; x += blockDim.x) {
+    const int i = (int)(x / c.TC), k = (int)(x % c.TC);
+    if (k >= s_tn[i]) continue;
+    const int64_t rr = (int64_t)b * c.NR + s_trow[i];
+    t.tail_id[(nb + i) * c.TC + k] = t.row_tail_id[rr * c.TC + k];
+    t.tail_q[(nb + i) * c.TC + k] = t.row_tail_q[rr * c.TC + k];
+  }
+}
+
+template <int DT>
+int segments(int V) {
+  return (V + seg_elems<DT>() - 1) / seg_elems<DT>();
 }
 
 }  // namespace
 
+size_t build_ws_bytes(const Cfg& c) {
+  const int G = c.dtype == VRT_BF16 ? segments<VRT_BF16>(c.V) : segments<VRT_F32>(c.V);
+  const size_t rows = (size_t)c.B * c.FP * G;
+  return rows * c.TC * sizeof(uint64_t) + ((rows * sizeof(int) + 255) & ~(size_t)255);
+}
+
 hipError_t launch_build_layer(const Cfg& c, const TreePtrs& t, int layer, const void* logits,
                               int64_t ld, int64_t tstride, uint64_t seed, uint32_t step,
                               uint32_t* stats, void* ws, hipStream_t stream) {
-  (void)ws;
-  BArgs a{c, t, layer, logits, ld, tstride, seed, step, stats};
-  const int cap = 4096;
-  const size_t lds = (size_t)cap * 8 + (size_t)max(128, next_pow2(c.trunc)) * 4;
-  const dim3 grid(layer == 0 ? 1 : c.FP, c.B);
+  const int G = c.dtype == VRT_BF16 ? segments<VRT_BF16>(c.V) : segments<VRT_F32>(c.V);
+  uint64_t* seg_keys = (uint64_t*)ws;
+  int* seg_cnt = (int*)((char*)ws + (size_t)c.B * c.FP * G * c.TC * sizeof(uint64_t));
+  BArgs a{c, t, layer, logits, ld, tstride, seed, step, stats, G, seg_keys, seg_cnt};
+  const int rows = layer == 0 ? 1 : c.FP;
+  const dim3 g1(G, rows, c.B);
   if (c.dtype == VRT_BF16)
-    hipLaunchKernelGGL(k_support_expand<VRT_BF16>, grid, dim3(kSB), lds, stream, a);
+    hipLaunchKernelGGL(k_seg_select<VRT_BF16>, g1, dim3(kST), 0, stream, a);
   else
-    hipLaunchKernelGGL(k_support_expand<VRT_F32>, grid, dim3(kSB), lds, stream, a);
+    hipLaunchKernelGGL(k_seg_select<VRT_F32>, g1, dim3(kST), 0, stream, a);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int bs = max(128, next_pow2(c.trunc)) / kWave;
+  const size_t lds = (size_t)kMergeCap * 8 + (size_t)bs * kWave * 4;
+  const dim3 g2(rows, c.B);
+  switch (bs) {
+    case 2: hipLaunchKernelGGL(k_merge_expand<2>, g2, dim3(256), lds, stream, a); break;
+    case 4: hipLaunchKernelGGL(k_merge_expand<4>, g2, dim3(256), lds, stream, a); break;
+    case 8: hipLaunchKernelGGL(k_merge_expand<8>, g2, dim3(256), lds, stream, a); break;
+    default: hipLaunchKernelGGL(k_merge_expand<16>, g2, dim3(256), lds, stream, a); break;
+  }
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int span = (layer == 0 ? 1 : c.P) * c.K;
   const size_t lds2 = (size_t)next_pow2(max(span, 2)) * 8;
@@ -540,8 +672,8 @@ hipError_t launch_build_layer(const Cfg& c, const TreePtrs& t, int layer, const 
 hipError_t launch_build_finish(const Cfg& c, const TreePtrs& t, void* ws, hipStream_t stream) {
   (void)ws;
   const int np = c.mode == VRT_MODE_TOPR ? next_pow2(max(c.NC, 2)) : 0;
-  const size_t lds = (size_t)np * 8 + (size_t)(2 * c.N + 1) * 4;
-  hipLaunchKernelGGL(k_finish, dim3(c.B), dim3(256), lds, stream, c, t);
+  const size_t lds = (size_t)np * 8 + (size_t)(6 * c.N + 1) * 4;
+  hipLaunchKernelGGL(k_finish, dim3(c.B), dim3(kFT), lds, stream, c, t);
   return hipGetLastError();
 }
 

@@ -1,27 +1,32 @@
-// Tree verification (RheoSampling, key design 3) on gfx950.
+// Tree verification (RheoSampling, key design 3) on gfx950, in two kernels.
 //
-// k_vrow: one 256-thread block per (node row, tree). The four waves stream the
-//   node's target row from HBM once in 2048-element chunks (16-byte loads, 8 bf16
-//   per lane per load), keeping per-chunk (scaled max, sum of exp2) in LDS. Wave 0
-//   then decides the node exactly as the walk would if it reached it: the
-//   probe-first test min(1, p/q~), recursive rejection of the other kept children
-//   under w = max(0, p - q~) on the probe's tail (p elsewhere), and, when nothing
-//   is accepted, the final residual (or bonus) sample by inverse CDF in token-id
-//   order: chunk masses locate the chunk, one 2048-element re-read finds the token.
-//   Every draw is keyed by (depth, test index), so each node's decision is a pure
-//   function of its own row and no node waits for another.
-// k_vwalk: one wave per tree follows accepted children from the root and writes
-//   the emitted tokens.
+// k_vstream: one 256-thread block per (node row, tree). The four waves stream the
+//   node's target row from HBM once, in 2048-element chunks (four 16-byte loads per
+//   lane, 8 bf16 each), and write per chunk fl(max*c2) and the sum of
+//   exp2(x*c2 - fl(max*c2)), where c2 = log2(e)/T. Every element costs one
+//   conversion, a third of a max3, one fma, one native exp2 and one add; nothing
+//   else runs here, so the kernel keeps full occupancy.
+// k_vdecide: one wave per (node, tree). From its row's chunk statistics it forms
+//   p = softmax(x/T) and decides the node exactly as the walk would if it reached
+//   it: the probe-first test min(1, p/q~), recursive rejection of the other kept
+//   children under w = max(0, p - q~) on the probe's tail (p elsewhere), and, when
+//   nothing is accepted, the final residual (or bonus) sample by inverse CDF in
+//   token-id order (chunk masses locate the chunk, one 2048-element re-read finds
+//   the token). Every draw is keyed by (depth, test index), so each node's decision
+//   is a pure function of its own row. The last wave of a tree to finish (a device
+//   counter the streaming kernel resets) follows the accepted children from the
+//   root and writes the emitted tokens and statistics.
 #include "vrt_dev.hpp"
 #include "vrt_internal.hpp"
 
 namespace vrt {
 namespace {
 
-constexpr int kVB = 256;         // threads per row block
-constexpr int kCH = 2048;        // elements per chunk (one wave at a time)
-constexpr int kChildMax = 32;    // K <= 30
-constexpr float kBand = 1e-6f;   // near-tie band reported in the stats
+constexpr int kVB = 256;        // threads per streaming block
+constexpr int kCH = 2048;       // elements per chunk (one wave at a time)
+constexpr int kChildMax = 32;   // K <= 30
+constexpr int kDW = 4;          // decide: waves (nodes) per block
+constexpr float kBand = 1e-6f;  // near-tie band reported in the stats
 
 struct VArgs {
   Cfg c;
@@ -31,45 +36,123 @@ struct VArgs {
   uint64_t seed;
   uint32_t step;
   NodeOut* node_out;
+  float2* chunk;      // [B][N][nch]: (fl(max*c2), sum exp2(x*c2 - that))
+  int* done;          // [B]: nodes of the tree decided so far
+  int32_t* out_tokens;
+  int32_t* out_nodes;
+  int32_t* out_len;
+  uint32_t* stats;
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Loads this lane's 32 elements of chunk [lo, lo + 2048) into x (-inf past V).
-// bf16: four 16-byte loads at lo + q*512 + lane*8; fp32: eight at lo + q*256 + lane*4.
-template <int DT>
+__device__ __forceinline__ int clamp_nodes(int nn, int N) { return nn < 1 ? 1 : (nn > N ? N : nn); }
+
+// This lane's 32 elements of chunk [lo, lo + 2048): bf16 as four 16-byte loads at
+// lo + q*512 + lane*8, fp32 as eight at lo + q*256 + lane*4. `full` chunks skip the
+// per-element range checks; the ragged last chunk pads with -inf.
+template <int DT, bool full>
 __device__ __forceinline__ void load_chunk(const void* row, int lo, int V, float (&x)[32]) {
   const int lane = lane_id();
   if constexpr (DT == VRT_BF16) {
     const uint16_t* r = (const uint16_t*)row;
+    uint4 v[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e0 = lo + q * 512 + lane * 8;
-      uint4 v = make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);  // -inf pairs
-      if (e0 < V) v = *(const uint4*)(r + e0);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      v[q] = make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);  // -inf pairs
+      if (full || e0 < V) v[q] = load_nt(r + e0);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t w[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        float a = bf16_lo(w[k]), b = bf16_hi(w[k]);
-        if (e0 + 2 * k >= V) a = -INFINITY;
-        if (e0 + 2 * k + 1 >= V) b = -INFINITY;
-        x[q * 8 + 2 * k] = a;
-        x[q * 8 + 2 * k + 1] = b;
+        x[q * 8 + 2 * k] = bf16_lo(w[k]);
+        x[q * 8 + 2 * k + 1] = bf16_hi(w[k]);
       }
+    }
+    if (!full) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (lo + q * 512 + lane * 8 + k >= V) x[q * 8 + k] = -INFINITY;
     }
   } else {
     const float* r = (const float*)row;
+    float4 v[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int e0 = lo + q * 256 + lane * 4;
-      float4 v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-      if (e0 < V) v = *(const float4*)(r + e0);
-      x[q * 4 + 0] = (e0 + 0 < V) ? v.x : -INFINITY;
-      x[q * 4 + 1] = (e0 + 1 < V) ? v.y : -INFINITY;
-      x[q * 4 + 2] = (e0 + 2 < V) ? v.z : -INFINITY;
-      x[q * 4 + 3] = (e0 + 3 < V) ? v.w : -INFINITY;
+      v[q] = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      if (full || e0 < V) {
+        const uint4 t = load_nt(r + e0);
+        v[q] = make_float4(__uint_as_float(t.x), __uint_as_float(t.y), __uint_as_float(t.z),
+                           __uint_as_float(t.w));
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      x[q * 4 + 0] = v[q].x;
+      x[q * 4 + 1] = v[q].y;
+      x[q * 4 + 2] = v[q].z;
+      x[q * 4 + 3] = v[q].w;
+    }
+    if (!full) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (lo + q * 256 + lane * 4 + k >= V) x[q * 4 + k] = -INFINITY;
     }
   }
+}
+
+template <int DT, bool full>
+__device__ __forceinline__ float2 chunk_stats(const void* row, int lo, int V, float c2) {
+  float x[32];
+  load_chunk<DT, full>(row, lo, V, x);
+  float m = x[0];
+#pragma unroll
+  for (int k = 1; k < 32; ++k) m = fmaxf(m, x[k]);
+  m = wave_max(m);
+  const float mc = m * c2;
+  float s = 0.0f;
+  if (m > -INFINITY) {
+#pragma unroll
+    for (int k = 0; k < 32; ++k) s += fast_exp2(__builtin_fmaf(x[k], c2, -mc));
+  }
+  s = wave_sum(s);
+  return make_float2(mc, s);
+}
+
+template <int DT>
+__global__ __launch_bounds__(kVB) void k_vstream(const VArgs a) {
+  const Cfg& c = a.c;
+  const int b = blockIdx.y;
+  const int i = blockIdx.x;
+  const int nn = clamp_nodes(a.t.n_nodes[b], c.N);
+  if (i == 0 && threadIdx.x == 0) a.done[b] = 0;
+  if (i >= nn) return;
+  const int V = c.V;
+  constexpr int esz = DT == VRT_BF16 ? 2 : 4;
+  const char* row = (const char*)a.logits + ((int64_t)b * a.tstride + (int64_t)i * a.ld) * esz;
+  const int nch = (V + kCH - 1) / kCH;
+  const int nfull = V / kCH;
+  const int wave = threadIdx.x >> 6;
+  float2* out = a.chunk + ((int64_t)b * c.N + i) * nch;
+  for (int ch = wave; ch < nch; ch += kVB / kWave) {
+    const float2 st = ch < nfull ? chunk_stats<DT, true>(row, ch * kCH, V, c.c2)
+                                 : chunk_stats<DT, false>(row, ch * kCH, V, c.c2);
+    if (lane_id() == 0) out[ch] = st;
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ float load_one(const void* row, int v) {
+  if constexpr (DT == VRT_BF16) return __uint_as_float((uint32_t)((const uint16_t*)row)[v] << 16);
+  else return ((const float*)row)[v];
 }
 
 // This lane's 32 contiguous elements [lo + lane*32, +32) of a chunk (id order).
@@ -106,337 +189,37 @@ __device__ __forceinline__ void load_contig(const void* row, int lo, int V, floa
     if (e0 + k >= V) x[k] = -INFINITY;
 }
 
-template <int DT>
-__device__ __forceinline__ float load_one(const void* row, int v) {
-  if constexpr (DT == VRT_BF16) return __uint_as_float((uint32_t)((const uint16_t*)row)[v] << 16);
-  else return ((const float*)row)[v];
-}
-
-template <int DT>
-__global__ __launch_bounds__(kVB) void k_vrow(const VArgs a) {
+// The walk of tree b (one lane): follow accepted children from the root.
+__device__ void walk_tree(const VArgs& a, int b, int nn) {
   const Cfg& c = a.c;
-  const int b = blockIdx.y;
-  const int i = blockIdx.x;
-  int nn = a.t.n_nodes[b];
-  nn = nn < 1 ? 1 : (nn > c.N ? c.N : nn);
-  if (i >= nn) return;
-
-  const int V = c.V;
-  constexpr int esz = DT == VRT_BF16 ? 2 : 4;
-  const char* row = (const char*)a.logits + ((int64_t)b * a.tstride + (int64_t)i * a.ld) * esz;
-  const int nch = (V + kCH - 1) / kCH;
-  const int wave = threadIdx.x >> 6;
-  const int lane = lane_id();
-  const float c2 = c.c2;
-
-  // dynamic LDS, sized by vrow_lds_bytes(): chunk statistics and the probe's tail
-  extern __shared__ double s_dyn[];
-  const int TC = c.TC;
-  double* s_pm = s_dyn;                      // [nch] per chunk mass, then residual mass
-  double* s_adj_w = s_pm + nch;              // [TC + 32] change of mass at adjusted tokens
-  float* s_mc = (float*)(s_adj_w + TC + kChildMax);  // [nch] fl(chunk max * c2)
-  float* s_sum = s_mc + nch;                 // [nch] sum exp2(x*c2 - mc)
-  float* s_tq = s_sum + nch;                 // [TC] tail q~
-  float* s_tp = s_tq + TC;                   // [TC] tail p
-  int* s_tid = (int*)(s_tp + TC);            // [TC] tail tokens
-  int* s_adj_tok = s_tid + TC;               // [TC + 32] adjusted tokens
-
-  // ---- 1. stream the row: per-chunk scaled max and sum of exponentials
-  for (int ch = wave; ch < nch; ch += kVB / kWave) {
-    float x[32];
-    load_chunk<DT>(row, ch * kCH, V, x);
-    float m = x[0];
-#pragma unroll
-    for (int k = 1; k < 32; ++k) m = fmaxf(m, x[k]);
-    m = wave_max(m);
-    const float mc = m * c2;
-    float s = 0.0f;
-    if (m > -INFINITY) {
-#pragma unroll
-      for (int k = 0; k < 32; ++k) s += fast_exp2(__builtin_fmaf(x[k], c2, -mc));
-    }
-    s = wave_sum(s);
-    if (lane == 0) {
-      s_mc[ch] = mc;
-      s_sum[ch] = s;
-    }
-  }
-  __syncthreads();
-  if (wave != 0) return;
-
-  // ---- 2. row statistics: MC = max mc, S = sum_ch s_ch 2^(mc_ch - MC)
-  float mcl = -INFINITY;
-  for (int ch = lane; ch < nch; ch += kWave) mcl = fmaxf(mcl, s_mc[ch]);
-  const float MC = wave_max(mcl);
-  double sl = 0.0;
-  for (int ch = lane; ch < nch; ch += kWave) {
-    const double pm = (double)s_sum[ch] * (double)fast_exp2(s_mc[ch] - MC);
-    s_pm[ch] = pm;
-    sl += pm;
-  }
-  const double S = wave_sum(sl);
-  NodeOut out{-1, -1, 0, 0.0f};
-  if (!(S > 0.0) || !(S < INFINITY) || !(MC < INFINITY)) {
-    out.flags = (int)(VRT_ST_TARGET_BAD << 16);
-    if (lane == 0) a.node_out[(int64_t)b * c.N + i] = out;
-    return;
-  }
-  const double invS = 1.0 / S;
-  auto p_of = [&](int tok) -> double {
-    const float x = load_one<DT>(row, tok);
-    return (double)fast_exp2(__builtin_fmaf(x, c2, -MC)) * invS;
-  };
-
-  // ---- 3. the node's kept children, in slot order
-  const int64_t nb = (int64_t)b * c.N;
-  const int64_t cob = (int64_t)b * (c.N + 1);  // child_off rows hold N + 1 entries
-  int co = a.t.child_off[cob + i], ce = a.t.child_off[cob + i + 1];
-  int nc = ce - co;
-  if (co < 0 || co > c.N || nc < 0) nc = 0;
-  if (nc > c.K) nc = c.K;
-  if (co + nc > c.N) nc = c.N - co > 0 ? c.N - co : 0;
-  int ch_node = -1, ch_tok = -1;
-  bool ch_probe = false;
-  if (lane < nc) {
-    ch_node = a.t.child[nb + co + lane];
-    if (ch_node > i && ch_node < nn) {
-      ch_tok = a.t.node_token[nb + ch_node];
-      ch_probe = a.t.node_kind[nb + ch_node] == VRT_PROBE;
-    }
-    if (ch_tok < 0 || ch_tok >= V) ch_node = -1, ch_tok = -1, ch_probe = false;
-  }
-  const uint64_t probe_mask = ballot(ch_probe);
-  const int probe_lane = probe_mask ? __builtin_ctzll(probe_mask) : -1;
-  double pc = (ch_tok >= 0) ? p_of(ch_tok) : 0.0;
-
-  const uint32_t depth = (uint32_t)min(max(a.t.node_depth[nb + i], 0), 63);
-  int tests = 0, near = 0;
-  int accept = -1;
-  double W = 1.0;
-  int nt = 0;
-  double q_child = 0.0;  // q~ of this lane's child token (0 if not in the tail)
-  bool child_in_tail = false;
-  if (probe_lane >= 0) {
-    nt = min(max(a.t.tail_n[nb + i], 0), c.TC);
-    const int64_t tb = (nb + i) * c.TC;
-    double ov = 0.0;
-    for (int e = lane; e < nt; e += kWave) {
-      int y = a.t.tail_id[tb + e];
-      const float q = a.t.tail_q[tb + e];
-      if (y < 0 || y >= V) y = -1;
-      const double p = (y >= 0) ? p_of(y) : 0.0;
-      s_tid[e] = y;
-      s_tq[e] = q;
-      s_tp[e] = (float)p;
-      ov += fmin(p, (double)q);
-    }
-    const double overlap = wave_sum(ov);
-    wave_sync();
-    if (ch_tok >= 0)
-      for (int e = 0; e < nt; ++e)
-        if (s_tid[e] == ch_tok) {
-          q_child = (double)s_tq[e];
-          child_in_tail = true;
-          break;
-        }
-    const double qs = __shfl(q_child, probe_lane, kWave);
-    const double ps = __shfl(pc, probe_lane, kWave);
-    const double ratio = ps / qs;
-    const float u0 = uniform24(a.seed, 32u * depth, (uint32_t)b, a.step, kPurposeTest);
-    ++tests;
-    if (fabs((double)u0 - ratio) < kBand) ++near;
-    if ((double)u0 < ratio) accept = __shfl(ch_node, probe_lane, kWave);
-    W = 1.0 - overlap;
-  }
-
-  // residual weight of this lane's child once the probe is rejected
-  double wc = pc;
-  if (child_in_tail) wc = pc > q_child ? pc - q_child : 0.0;
-  uint64_t rejected = 0;
-  if (accept < 0) {
-    uint32_t j = 1;
-    for (int k = 0; k < nc; ++k) {
-      if (k == probe_lane) continue;
-      const int node_k = __shfl(ch_node, k, kWave);
-      const double wk = __shfl(wc, k, kWave);
-      if (node_k < 0) continue;
-      const float u = uniform24(a.seed, 32u * depth + j, (uint32_t)b, a.step, kPurposeTest);
-      ++j;
-      ++tests;
-      const double ratio = wk / W;
-      if (fabs((double)u - ratio) < kBand) ++near;
-      if ((double)u < ratio) {
-        accept = node_k;
-        break;
-      }
-      W -= wk;
-      rejected |= 1ull << k;
-    }
-  }
-
-  // ---- 4. nothing accepted: inverse-CDF sample of w / W in token-id order
-  if (accept < 0) {
-    wave_sync();
-    // tokens whose weight differs from p: the probe's tail (clipped residual) and
-    // the rejected children (weight 0)
-    int nadj = 0;
-    if (probe_lane >= 0) {
-      for (int e = lane; e < nt; e += kWave) {
-        const int y = s_tid[e];
-        const double p = (double)s_tp[e], q = (double)s_tq[e];
-        bool rej = false;
-        for (int k = 0; k < nc; ++k)
-          if (((rejected >> k) & 1ull) && __shfl(ch_tok, k, kWave) == y) rej = true;
-        s_adj_tok[e] = y;
-        s_adj_w[e] = rej ? -p : -(p < q ? p : q);  // change of mass at y
-      }
-      nadj = nt;
-    }
-    {
-      const bool mine = ((rejected >> lane) & 1ull) && lane < nc && !child_in_tail;
-      const uint64_t mm = ballot(mine);
-      if (mine) {
-        const int slot = nadj + __builtin_popcountll(mm & ((1ull << lane) - 1ull));
-        s_adj_tok[slot] = ch_tok;
-        s_adj_w[slot] = -pc;
-      }
-      nadj += __builtin_popcountll(mm);
-    }
-    wave_sync();
-    // chunk masses with the adjustments, lane-blocked contiguous chunks
-    const int cpl = (nch + kWave - 1) / kWave;
-    const int c0 = lane * cpl, c1 = min(c0 + cpl, nch);
-    double lmass = 0.0;
-    for (int ch = c0; ch < c1; ++ch) {
-      double mch = s_pm[ch] * invS;
-      for (int e = 0; e < nadj; ++e) {
-        const int y = s_adj_tok[e];
-        if (y >= ch * kCH && y < (ch + 1) * kCH) mch += s_adj_w[e];
-      }
-      if (mch < 0.0) mch = 0.0;
-      s_pm[ch] = mch;
-      lmass += mch;
-    }
-    const float uf = uniform24(a.seed, depth, (uint32_t)b, a.step, kPurposeFinal);
-    const double tgt = (double)uf * W;
-    const double incl = wave_incl_scan(lmass);
-    const double excl = incl - lmass;
-    // lane holding the crossing chunk; if rounding leaves none, the last lane with mass
-    const uint64_t hit = ballot(tgt < incl && lmass > 0.0);
-    int src = hit ? __builtin_ctzll(hit) : -1;
-    bool clamp = false;
-    if (src < 0) {
-      const uint64_t pos = ballot(lmass > 0.0);
-      src = pos ? 63 - __builtin_clzll(pos) : 0;
-      clamp = true;
-    }
-    int cstar = -1;
-    double before = 0.0;
-    if (lane == src) {
-      double cum = excl;
-      for (int ch = c0; ch < c1; ++ch) {
-        if (s_pm[ch] > 0.0) {
-          cstar = ch;
-          before = cum;
-          if (!clamp && tgt < cum + s_pm[ch]) break;
-        }
-        cum += s_pm[ch];
-      }
-      if (cstar < 0) cstar = c0 < nch ? c0 : nch - 1;
-    }
-    cstar = __shfl(cstar, src, kWave);
-    before = __shfl(before, src, kWave);
-    // re-read the chunk; lane l owns tokens [lo + 32 l, lo + 32 l + 32)
-    const int lo = cstar * kCH;
-    float x[32];
-    load_contig<DT>(row, lo, V, x);
-    float wv[32];
-    double lsum = 0.0;
-    const float invSf = (float)invS;
-#pragma unroll
-    for (int k = 0; k < 32; ++k)
-      wv[k] = (x[k] > -INFINITY) ? fast_exp2(__builtin_fmaf(x[k], c2, -MC)) * invSf : 0.0f;
-    const int my0 = lo + lane * 32;
-    for (int e = 0; e < nadj; ++e) {
-      const int y = s_adj_tok[e];
-      if (y >= my0 && y < my0 + 32) {
-        const double v = (double)wv[y - my0] + s_adj_w[e];
-        wv[y - my0] = v > 0.0 ? (float)v : 0.0f;
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < 32; ++k) lsum += (double)wv[k];
-    const double lincl = wave_incl_scan(lsum) + before;
-    const double lexcl = lincl - lsum;
-    const uint64_t hit2 = ballot(tgt < lincl && lsum > 0.0);
-    int src2 = (hit2 && !clamp) ? __builtin_ctzll(hit2) : -1;
-    bool clamp2 = clamp;
-    if (src2 < 0) {
-      const uint64_t pos = ballot(lsum > 0.0);
-      src2 = pos ? 63 - __builtin_clzll(pos) : 0;
-      clamp2 = true;
-    }
-    if (lane == src2) {
-      double cum = lexcl;
-      int tok = -1;
-      double b0 = cum, b1 = cum;
-      for (int k = 0; k < 32; ++k) {
-        if (wv[k] > 0.0f) {
-          tok = my0 + k;
-          b0 = cum;
-          b1 = cum + (double)wv[k];
-          if (!clamp2 && tgt < b1) break;
-        }
-        cum += (double)wv[k];
-      }
-      if (tok < 0) tok = min(my0, V - 1);
-      out.token = tok;
-      if (W > 0.0 && (fabs((double)uf - b0 / W) < kBand || fabs((double)uf - b1 / W) < kBand))
-        ++near;
-    }
-    out.token = __shfl(out.token, src2, kWave);
-    near = __shfl(near, src2, kWave);
-  }
-  out.accept = accept;
-  out.flags = min(tests, 255) | (min(near, 255) << 8);
-  if (accept < 0) out.W = (float)W;
-  if (lane == 0) a.node_out[nb + i] = out;
-}
-
-__global__ __launch_bounds__(64) void k_vwalk(const Cfg c, const TreePtrs t, const NodeOut* node_out,
-                                              int32_t* out_tokens, int32_t* out_nodes,
-                                              int32_t* out_len, uint32_t* stats) {
-  const int b = blockIdx.x;
   const int lane = lane_id();
   const int64_t nb = (int64_t)b * c.N;
-  int nn = t.n_nodes[b];
-  nn = nn < 1 ? 1 : (nn > c.N ? c.N : nn);
   uint32_t st = 0;
-  for (int i = lane; i < nn; i += kWave) st |= (uint32_t)node_out[nb + i].flags >> 16;
+  for (int i = lane; i < nn; i += kWave) st |= (uint32_t)a.node_out[nb + i].flags >> 16;
   for (int o = 1; o < kWave; o <<= 1) st |= __shfl_xor(st, o, kWave);
   if (lane != 0) return;
   int cur = 0, len = 0, near = 0, probe = 0, visited = 0;
   for (int step = 0; step <= c.D; ++step) {
-    const NodeOut o = node_out[nb + cur];
+    const NodeOut o = a.node_out[nb + cur];
     ++visited;
     near += (o.flags >> 8) & 0xFF;
     if (o.accept > cur && o.accept < nn && len < c.D) {
-      out_nodes[(int64_t)b * c.D + len] = o.accept;
-      out_tokens[(int64_t)b * (c.D + 1) + len] = t.node_token[nb + o.accept];
-      if (t.node_kind[nb + o.accept] == VRT_PROBE) probe = 1;
+      a.out_nodes[(int64_t)b * c.D + len] = o.accept;
+      a.out_tokens[(int64_t)b * (c.D + 1) + len] = a.t.node_token[nb + o.accept];
+      if (a.t.node_kind[nb + o.accept] == VRT_PROBE) probe = 1;
       ++len;
       cur = o.accept;
     } else {
-      out_tokens[(int64_t)b * (c.D + 1) + len] = o.token;
+      a.out_tokens[(int64_t)b * (c.D + 1) + len] = o.token;
       ++len;
       break;
     }
   }
-  for (int k = len; k <= c.D; ++k) out_tokens[(int64_t)b * (c.D + 1) + k] = -1;
-  for (int k = len - 1; k < c.D; ++k) out_nodes[(int64_t)b * c.D + k] = -1;
-  out_len[b] = len;
-  if (stats) {
-    uint32_t* s = stats + (int64_t)b * 8;
+  for (int k = len; k <= c.D; ++k) a.out_tokens[(int64_t)b * (c.D + 1) + k] = -1;
+  for (int k = len - 1; k < c.D; ++k) a.out_nodes[(int64_t)b * c.D + k] = -1;
+  a.out_len[b] = len;
+  if (a.stats) {
+    uint32_t* s = a.stats + (int64_t)b * 8;
     s[0] |= st;
     s[1] = (uint32_t)(len - 1);
     s[2] = (uint32_t)probe;
@@ -446,29 +229,325 @@ __global__ __launch_bounds__(64) void k_vwalk(const Cfg c, const TreePtrs t, con
   }
 }
 
+template <int DT>
+__global__ __launch_bounds__(kDW * kWave) void k_vdecide(const VArgs a) {
+  const Cfg& c = a.c;
+  const int wave = threadIdx.x >> 6;
+  const int lane = lane_id();
+  const int64_t g = (int64_t)blockIdx.x * kDW + wave;
+  if (g >= (int64_t)c.B * c.N) return;
+  const int b = (int)(g / c.N);
+  const int i = (int)(g % c.N);
+  const int nn = clamp_nodes(a.t.n_nodes[b], c.N);
+  if (i >= nn) return;
+
+  const int V = c.V;
+  constexpr int esz = DT == VRT_BF16 ? 2 : 4;
+  const char* row = (const char*)a.logits + ((int64_t)b * a.tstride + (int64_t)i * a.ld) * esz;
+  const int nch = (V + kCH - 1) / kCH;
+  const float c2 = c.c2;
+  const int TC = c.TC;
+
+  // per-wave LDS (sized by vdecide_lds_per_wave)
+  extern __shared__ double s_dyn[];
+  const size_t per_wave = (size_t)(nch + TC + kChildMax) + (size_t)(2 * TC + kChildMax + 1) / 2 +
+                          (size_t)(2 * TC + 1) / 2;
+  double* s_pm = s_dyn + per_wave * wave;  // [nch] per chunk mass, then residual mass
+  double* s_adj_w = s_pm + nch;            // [TC + 32] change of mass at adjusted tokens
+  float* s_tq = (float*)(s_adj_w + TC + kChildMax);  // [TC] tail q~
+  float* s_tp = s_tq + TC;                 // [TC] tail p
+  int* s_tid = (int*)(s_tp + TC);          // [TC] tail tokens
+  int* s_adj_tok = s_tid + TC;             // [TC + 32] adjusted tokens
+
+  // ---- row statistics: MC = max mc, S = sum_ch s_ch 2^(mc_ch - MC)
+  const float2* cs = a.chunk + ((int64_t)b * c.N + i) * nch;
+  float mcl = -INFINITY;
+  for (int ch = lane; ch < nch; ch += kWave) mcl = fmaxf(mcl, cs[ch].x);
+  const float MC = wave_max(mcl);
+  double sl = 0.0;
+  for (int ch = lane; ch < nch; ch += kWave) {
+    const float2 st = cs[ch];
+    const double pm = (double)st.y * (double)fast_exp2(st.x - MC);
+    s_pm[ch] = pm;
+    sl += pm;
+  }
+  const double S = wave_sum(sl);
+  NodeOut out{-1, -1, 0, 0.0f};
+  const int64_t nb = (int64_t)b * c.N;
+  bool decide = true;
+  if (!(S > 0.0) || !(S < INFINITY) || !(MC < INFINITY)) {
+    out.flags = (int)(VRT_ST_TARGET_BAD << 16);
+    decide = false;
+  }
+  if (decide) {
+    const double invS = 1.0 / S;
+    auto p_of = [&](int tok) -> double {
+      const float x = load_one<DT>(row, tok);
+      return (double)fast_exp2(__builtin_fmaf(x, c2, -MC)) * invS;
+    };
+
+    // ---- the node's kept children, in slot order
+    const int64_t cob = (int64_t)b * (c.N + 1);  // child_off rows hold N + 1 entries
+    const int co = a.t.child_off[cob + i], ce = a.t.child_off[cob + i + 1];
+    int nc = ce - co;
+    if (co < 0 || co > c.N || nc < 0) nc = 0;
+    if (nc > c.K) nc = c.K;
+    if (co + nc > c.N) nc = c.N - co > 0 ? c.N - co : 0;
+    int ch_node = -1, ch_tok = -1;
+    bool ch_probe = false;
+    if (lane < nc) {
+      ch_node = a.t.child[nb + co + lane];
+      if (ch_node > i && ch_node < nn) {
+        ch_tok = a.t.node_token[nb + ch_node];
+        ch_probe = a.t.node_kind[nb + ch_node] == VRT_PROBE;
+      }
+      if (ch_tok < 0 || ch_tok >= V) ch_node = -1, ch_tok = -1, ch_probe = false;
+    }
+    const uint64_t probe_mask = ballot(ch_probe);
+    const int probe_lane = probe_mask ? __builtin_ctzll(probe_mask) : -1;
+    const double pc = (ch_tok >= 0) ? p_of(ch_tok) : 0.0;
+
+    const uint32_t depth = (uint32_t)min(max(a.t.node_depth[nb + i], 0), 63);
+    int tests = 0, near = 0;
+    int accept = -1;
+    double W = 1.0;
+    int nt = 0;
+    double q_child = 0.0;  // q~ of this lane's child token (0 if not in the tail)
+    bool child_in_tail = false;
+    if (probe_lane >= 0) {
+      nt = min(max(a.t.tail_n[nb + i], 0), TC);
+      const int64_t tb = (nb + i) * TC;
+      double ov = 0.0;
+      for (int e = lane; e < nt; e += kWave) {
+        int y = a.t.tail_id[tb + e];
+        const float q = a.t.tail_q[tb + e];
+        if (y < 0 || y >= V) y = -1;
+        const double p = (y >= 0) ? p_of(y) : 0.0;
+        s_tid[e] = y;
+        s_tq[e] = q;
+        s_tp[e] = (float)p;
+        ov += fmin(p, (double)q);
+      }
+      const double overlap = wave_sum(ov);
+      wave_sync();
+      if (ch_tok >= 0)
+        for (int e = 0; e < nt; ++e)
+          if (s_tid[e] == ch_tok) {
+            q_child = (double)s_tq[e];
+            child_in_tail = true;
+            break;
+          }
+      const double qs = __shfl(q_child, probe_lane, kWave);
+      const double ps = __shfl(pc, probe_lane, kWave);
+      const double ratio = ps / qs;
+      const float u0 = uniform24(a.seed, 32u * depth, (uint32_t)b, a.step, kPurposeTest);
+      ++tests;
+      if (fabs((double)u0 - ratio) < kBand) ++near;
+      if ((double)u0 < ratio) accept = __shfl(ch_node, probe_lane, kWave);
+      W = 1.0 - overlap;
+    }
+
+    // residual weight of this lane's child once the probe is rejected
+    double wc = pc;
+    if (child_in_tail) wc = pc > q_child ? pc - q_child : 0.0;
+    uint64_t rejected = 0;
+    if (accept < 0) {
+      uint32_t j = 1;
+      for (int k = 0; k < nc; ++k) {
+        if (k == probe_lane) continue;
+        const int node_k = __shfl(ch_node, k, kWave);
+        const double wk = __shfl(wc, k, kWave);
+        if (node_k < 0) continue;
+        const float u = uniform24(a.seed, 32u * depth + j, (uint32_t)b, a.step, kPurposeTest);
+        ++j;
+        ++tests;
+        const double ratio = wk / W;
+        if (fabs((double)u - ratio) < kBand) ++near;
+        if ((double)u < ratio) {
+          accept = node_k;
+          break;
+        }
+        W -= wk;
+        rejected |= 1ull << k;
+      }
+    }
+
+    // ---- nothing accepted: inverse-CDF sample of w / W in token-id order
+    if (accept < 0) {
+      wave_sync();
+      // tokens whose weight differs from p: the probe's tail (clipped residual) and
+      // the rejected children (weight 0)
+      int nadj = 0;
+      if (probe_lane >= 0) {
+        for (int e = lane; e < nt; e += kWave) {
+          const int y = s_tid[e];
+          const double p = (double)s_tp[e], q = (double)s_tq[e];
+          bool rej = false;
+          for (int k = 0; k < nc; ++k)
+            if (((rejected >> k) & 1ull) && __shfl(ch_tok, k, kWave) == y) rej = true;
+          s_adj_tok[e] = y;
+          s_adj_w[e] = rej ? -p : -(p < q ? p : q);  // change of mass at y
+        }
+        nadj = nt;
+      }
+      {
+        const bool mine = ((rejected >> lane) & 1ull) && lane < nc && !child_in_tail;
+        const uint64_t mm = ballot(mine);
+        if (mine) {
+          const int slot = nadj + __builtin_popcountll(mm & ((1ull << lane) - 1ull));
+          s_adj_tok[slot] = ch_tok;
+          s_adj_w[slot] = -pc;
+        }
+        nadj += __builtin_popcountll(mm);
+      }
+      wave_sync();
+      // chunk masses with the adjustments, lane-blocked contiguous chunks
+      const int cpl = (nch + kWave - 1) / kWave;
+      const int c0 = lane * cpl, c1 = min(c0 + cpl, nch);
+      double lmass = 0.0;
+      for (int ch = c0; ch < c1; ++ch) {
+        double mch = s_pm[ch] * invS;
+        for (int e = 0; e < nadj; ++e) {
+          const int y = s_adj_tok[e];
+          if (y >= ch * kCH && y < (ch + 1) * kCH) mch += s_adj_w[e];
+        }
+        if (mch < 0.0) mch = 0.0;
+        s_pm[ch] = mch;
+        lmass += mch;
+      }
+      const float uf = uniform24(a.seed, depth, (uint32_t)b, a.step, kPurposeFinal);
+      const double tgt = (double)uf * W;
+      const double incl = wave_incl_scan(lmass);
+      const double excl = incl - lmass;
+      // lane holding the crossing chunk; if rounding leaves none, the last lane with mass
+      const uint64_t hit = ballot(tgt < incl && lmass > 0.0);
+      int src = hit ? __builtin_ctzll(hit) : -1;
+      bool clamp = false;
+      if (src < 0) {
+        const uint64_t pos = ballot(lmass > 0.0);
+        src = pos ? 63 - __builtin_clzll(pos) : 0;
+        clamp = true;
+      }
+      int cstar = -1;
+      double before = 0.0;
+      if (lane == src) {
+        double cum = excl;
+        for (int ch = c0; ch < c1; ++ch) {
+          if (s_pm[ch] > 0.0) {
+            cstar = ch;
+            before = cum;
+            if (!clamp && tgt < cum + s_pm[ch]) break;
+          }
+          cum += s_pm[ch];
+        }
+        if (cstar < 0) cstar = c0 < nch ? c0 : nch - 1;
+      }
+      cstar = __shfl(cstar, src, kWave);
+      before = __shfl(before, src, kWave);
+      // re-read the chunk; lane l owns tokens [lo + 32 l, lo + 32 l + 32)
+      const int lo = cstar * kCH;
+      float x[32];
+      load_contig<DT>(row, lo, V, x);
+      float wv[32];
+      const float invSf = (float)invS;
+#pragma unroll
+      for (int k = 0; k < 32; ++k)
+        wv[k] = (x[k] > -INFINITY) ? fast_exp2(__builtin_fmaf(x[k], c2, -MC)) * invSf : 0.0f;
+      const int my0 = lo + lane * 32;
+      for (int e = 0; e < nadj; ++e) {
+        const int y = s_adj_tok[e];
+        if (y >= my0 && y < my0 + 32) {
+          const double v = (double)wv[y - my0] + s_adj_w[e];
+          wv[y - my0] = v > 0.0 ? (float)v : 0.0f;
+        }
+      }
+      double lsum = 0.0;
+#pragma unroll
+      for (int k = 0; k < 32; ++k) lsum += (double)wv[k];
+      const double lincl = wave_incl_scan(lsum) + before;
+      const double lexcl = lincl - lsum;
+      const uint64_t hit2 = ballot(tgt < lincl && lsum > 0.0);
+      int src2 = (hit2 && !clamp) ? __builtin_ctzll(hit2) : -1;
+      bool clamp2 = clamp;
+      if (src2 < 0) {
+        const uint64_t pos = ballot(lsum > 0.0);
+        src2 = pos ? 63 - __builtin_clzll(pos) : 0;
+        clamp2 = true;
+      }
+      if (lane == src2) {
+        double cum = lexcl;
+        int tok = -1;
+        double b0 = cum, b1 = cum;
+        for (int k = 0; k < 32; ++k) {
+          if (wv[k] > 0.0f) {
+            tok = my0 + k;
+            b0 = cum;
+            b1 = cum + (double)wv[k];
+            if (!clamp2 && tgt < b1) break;
+          }
+          cum += (double)wv[k];
+        }
+        if (tok < 0) tok = min(my0, V - 1);
+        out.token = tok;
+        if (W > 0.0 && (fabs((double)uf - b0 / W) < kBand || fabs((double)uf - b1 / W) < kBand))
+          ++near;
+      }
+      out.token = __shfl(out.token, src2, kWave);
+      near = __shfl(near, src2, kWave);
+    }
+    out.accept = accept;
+    out.flags = min(tests, 255) | (min(near, 255) << 8);
+    if (accept < 0) out.W = (float)W;
+  }
+  if (lane == 0) a.node_out[nb + i] = out;
+}
+
+// One wave per tree: the walk over the decided nodes.
+__global__ __launch_bounds__(kWave) void k_vwalk(const VArgs a) {
+  const int b = blockIdx.x;
+  walk_tree(a, b, clamp_nodes(a.t.n_nodes[b], a.c.N));
+}
+
+size_t vdecide_lds_per_wave(const Cfg& c) {
+  const int nch = (c.V + kCH - 1) / kCH;
+  const size_t doubles = (size_t)(nch + c.TC + kChildMax) + (size_t)(2 * c.TC + kChildMax + 1) / 2 +
+                         (size_t)(2 * c.TC + 1) / 2;
+  return doubles * 8;
+}
+
 }  // namespace
 
-size_t vrow_lds_bytes(const Cfg& c) {
+size_t verify_ws_bytes(const Cfg& c) {
   const int nch = (c.V + kCH - 1) / kCH;
-  return 8 * (size_t)(nch + c.TC + kChildMax) + 4 * (size_t)(2 * nch + 2 * c.TC) +
-         4 * (size_t)(2 * c.TC + kChildMax);
+  return (size_t)c.B * c.N * nch * sizeof(float2) + (size_t)c.B * sizeof(int);
 }
 
 hipError_t launch_verify(const Cfg& c, const TreePtrs& t, const void* logits, int64_t ld,
                          int64_t tstride, uint64_t seed, uint32_t step, NodeOut* node_out,
                          int32_t* out_tokens, int32_t* out_nodes, int32_t* out_len, uint32_t* stats,
-                         hipStream_t stream) {
-  VArgs a{c, t, logits, ld, tstride, seed, step, node_out};
+                         void* ws, hipStream_t stream) {
+  const int nch = (c.V + kCH - 1) / kCH;
+  float2* chunk = (float2*)ws;
+  int* done = (int*)((char*)ws + (size_t)c.B * c.N * nch * sizeof(float2));
+  VArgs a{c, t, logits, ld, tstride, seed, step, node_out, chunk, done,
+          out_tokens, out_nodes, out_len, stats};
   const dim3 grid(c.N, c.B);
-  const size_t lds = vrow_lds_bytes(c);
   if (c.dtype == VRT_BF16)
-    hipLaunchKernelGGL(k_vrow<VRT_BF16>, grid, dim3(kVB), lds, stream, a);
+    hipLaunchKernelGGL(k_vstream<VRT_BF16>, grid, dim3(kVB), 0, stream, a);
   else
-    hipLaunchKernelGGL(k_vrow<VRT_F32>, grid, dim3(kVB), lds, stream, a);
+    hipLaunchKernelGGL(k_vstream<VRT_F32>, grid, dim3(kVB), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_vwalk, dim3(c.B), dim3(64), 0, stream, c, t, node_out, out_tokens, out_nodes,
-                     out_len, stats);
+  const int64_t nodes = (int64_t)c.B * c.N;
+  const dim3 g2((unsigned)((nodes + kDW - 1) / kDW));
+  const size_t lds = vdecide_lds_per_wave(c) * kDW;
+  if (c.dtype == VRT_BF16)
+    hipLaunchKernelGGL(k_vdecide<VRT_BF16>, g2, dim3(kDW * kWave), lds, stream, a);
+  else
+    hipLaunchKernelGGL(k_vdecide<VRT_F32>, g2, dim3(kDW * kWave), lds, stream, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_vwalk, dim3(c.B), dim3(kWave), 0, stream, a);
   return hipGetLastError();
 }
 

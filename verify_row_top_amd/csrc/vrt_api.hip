@@ -63,9 +63,10 @@ bool compute_layout(const vrt_config& c, vrt_tree_layout* L) {
   return true;
 }
 
-// Workspace: verification node outcomes [B][N], then build scratch.
+// Workspace: verification node outcomes [B][N], the verification's row statistics,
+// then build scratch.
 struct WsLayout {
-  int64_t node_out, build, total;
+  int64_t node_out, verify, build, total;
 };
 
 WsLayout ws_layout(const vrt_config& c) {
@@ -75,9 +76,10 @@ WsLayout ws_layout(const vrt_config& c) {
   int64_t off = 0;
   w.node_out = off;
   off = align256(off + (int64_t)c.B * L.N * (int64_t)sizeof(vrt::NodeOut));
+  w.verify = off;
+  off = align256(off + (int64_t)vrt::verify_ws_bytes(vrt::make_cfg(c)));
   w.build = off;
-  // per expanded row: a sorted support list of trunc 64-bit keys
-  off = align256(off + (int64_t)c.B * L.FP * c.trunc * 8);
+  off = align256(off + (int64_t)vrt::build_ws_bytes(vrt::make_cfg(c)));
   w.total = off;
   return w;
 }
@@ -260,7 +262,7 @@ vrt_status vrt_verify_tree(const vrt_config* cp, const void* target_logits, int6
   vrt::NodeOut* no = node_out ? (vrt::NodeOut*)node_out : (vrt::NodeOut*)((char*)ws + wl.node_out);
   const hipError_t e = vrt::launch_verify(k, t, target_logits, ld, tree_stride, seed,
                                           (uint32_t)step, no, out_tokens, out_nodes, out_len, stats,
-                                          (hipStream_t)stream);
+                                          (char*)ws + wl.verify, (hipStream_t)stream);
   if (e != hipSuccess) return fail(VRT_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
   return VRT_OK;
 }

@@ -59,15 +59,16 @@ struct NodeOut {
 Cfg make_cfg(const vrt_config& c);
 TreePtrs tree_ptrs(const vrt_config& c, void* blob);
 
+// Device scratch of the verification: per-chunk row statistics and per-tree counters.
+size_t verify_ws_bytes(const Cfg& c);
+
 hipError_t launch_verify(const Cfg& c, const TreePtrs& t, const void* logits, int64_t ld,
                          int64_t tstride, uint64_t seed, uint32_t step, NodeOut* node_out,
                          int32_t* out_tokens, int32_t* out_nodes, int32_t* out_len, uint32_t* stats,
-                         hipStream_t stream);
+                         void* ws, hipStream_t stream);
 
-// Workspace of the build: per-row support lists, beam scratch.
-struct BuildWs {
-  uint64_t* seg_keys;  // unused placeholder for split-row selection
-};
+// Device scratch of the build: each row segment's sorted top-trunc keys and counts.
+size_t build_ws_bytes(const Cfg& c);
 
 hipError_t launch_build_layer(const Cfg& c, const TreePtrs& t, int layer, const void* logits,
                               int64_t ld, int64_t tstride, uint64_t seed, uint32_t step,
