@@ -1,18 +1,16 @@
 // Draft-tree construction on gfx950 (RheoSampling framework flowchart, key designs
 // 1-2; SMART key design 3 as the switchable keep rule). Per layer, three kernels:
 //
-// k_seg_select: one 512-thread block per 32 KB segment of an expanded parent's
-//   draft row (all four 16-byte loads per thread in flight, non-temporal). The
-//   block seeds a threshold with the trunc-th largest of its threads' maxima (a key
-//   that at least trunc elements reach), compares every element's value against it,
-//   appends the survivors' exact keys (logit desc, token id asc) to an LDS buffer
-//   (wave-aggregated), compacts by a bitonic sort when the buffer fills, and writes
-//   the segment's sorted top-trunc keys to the workspace.
-// k_merge_expand: one block per parent merges its segments' lists into the row's
-//   top-trunc support, and wave 0 expands the parent: untempered softmax on the
-//   support with the fixed ranking recipe, tempered softmax in fp64, the probe draw
-//   from the tempered tail, the proxy min{q(x_m), z}, the K child slots and the
-//   parent's tail table.
+// k_seg_topk: one wave per 16 KB segment of an expanded parent's draft row streams
+//   the segment once (non-temporal 16-byte loads, next batch in flight) and keeps the
+//   segment's best keys (logit desc, token id asc) sorted in registers: one compare
+//   per element against a threshold, exact keys only for survivors, bitonic sorts and
+//   merges by cross-lane shuffles.
+// k_merge_expand: one wave per parent merges its segments' lists into the row's
+//   top-trunc support and expands the parent: untempered softmax on the support with
+//   the fixed ranking recipe, tempered softmax in fp64, the probe draw from the
+//   tempered tail, the proxy min{q(x_m), z}, the K child slots and the parent's tail
+//   table.
 // k_rank_layer: one block per tree ranks the layer's children by (path score desc,
 //   creation index asc) and keeps the top W (top-R mode) or runs SMART's sequential
 //   keep rule over them.
@@ -24,14 +22,6 @@
 
 namespace vrt {
 namespace {
-
-constexpr int kST = 512;       // threads per segment block
-constexpr int kSL = 4;         // 16-byte loads per thread per segment
-constexpr int kSegCap = 2048;  // LDS candidate buffer of a segment block (keys)
-constexpr int kMergeCap = 4096;  // keys a merge block sorts at once
-
-template <int DT>
-constexpr int seg_elems() { return kST * kSL * (DT == VRT_BF16 ? 8 : 4); }
 
 __device__ __forceinline__ int layer_base(const Cfg& c, int l) {
   return l == 0 ? 0 : c.K + (l - 1) * c.P * c.K;
@@ -59,8 +49,8 @@ struct BArgs {
   uint32_t step;
   uint32_t* stats;
   int G;               // segments per row
-  uint64_t* seg_keys;  // [B][FP][G][TC] sorted top keys of each segment
-  int* seg_cnt;        // [B][FP][G] count | (non-finite seen) << 30
+  uint64_t* seg_keys;  // [B][FP][G][N] sorted top keys of each segment, N = 64 * PL
+  int* seg_bad;        // [B][FP][G] a NaN or +inf logit was seen
 };
 
 // The node frontier position j of tree b expands at this layer (-1 = root), or -2
@@ -78,156 +68,158 @@ __device__ __forceinline__ int row_node(const BArgs& a, int b, int j) {
   return node;
 }
 
-// Wave-aggregated append of `key` into an LDS buffer of `cap` keys when `pass`.
-// Returns true if stored; sets *ovf when the buffer is full (retried later).
-__device__ __forceinline__ bool append(bool pass, uint64_t key, uint64_t* buf, int cap, int* cnt,
-                                       int* ovf) {
-  const uint64_t mask = ballot(pass);
-  if (!mask) return false;
-  const int lane = lane_id();
-  const int leader = __builtin_ctzll(mask);
-  int base = 0;
-  if (lane == leader) base = atomicAdd(cnt, __builtin_popcountll(mask));
-  base = __shfl(base, leader, kWave);
-  if (!pass) return false;
-  const int slot = base + __builtin_popcountll(mask & ((1ull << lane) - 1ull));
-  if (slot < cap) {
-    buf[slot] = key;
-    return true;
-  }
-  *ovf = 1;
-  return false;
-}
-
-// Sort the first min(n, cap) keys of buf descending (zero padded to a power of two).
-__device__ int sort_prefix(uint64_t* buf, int n, int cap) {
-  n = min(n, cap);
-  const int np = next_pow2(max(n, 2));
-  for (int t = n + threadIdx.x; t < np; t += blockDim.x) buf[t] = 0ull;
-  __syncthreads();
-  bitonic_desc(buf, np);
-  return n;
-}
-
-// A thread's segment as one vector value of 16 words (registers, never memory).
-typedef uint32_t Words __attribute__((ext_vector_type(16)));
-
-template <int DT, int K>
-__device__ __forceinline__ float elem(const Words wd) {
-  if constexpr (DT == VRT_BF16) return (K & 1) ? bf16_hi(wd[K >> 1]) : bf16_lo(wd[K >> 1]);
-  else return __uint_as_float(wd[K]);
-}
-
-// Element k (a per-lane value); the dynamic extract of a register vector lowers to
-// a select chain.
-template <int DT>
-__device__ __forceinline__ float elem_at(const Words wd, int k) {
-  const uint32_t word = wd[DT == VRT_BF16 ? (k >> 1) : k];
-  if constexpr (DT == VRT_BF16) return (k & 1) ? bf16_hi(word) : bf16_lo(word);
-  else return __uint_as_float(word);
-}
+constexpr int kSegWaves = 4;  // waves (one segment each) per selection block
+constexpr int kSegLoads = 16; // 16-byte loads per lane per segment, all in flight at once
 
 template <int DT>
-__global__ __launch_bounds__(kST) void k_seg_select(const BArgs a) {
+constexpr int seg_elems() { return kWave * kSegLoads * (DT == VRT_BF16 ? 8 : 4); }
+
+// Segment top-N (N = 64*PL >= trunc): one wave per segment of an expanded parent's
+// draft row. The wave issues all of its loads at once (the segment lives in 64
+// registers per lane), then:
+//  1. every lane finds the PL-th largest of its own values; the minimum of these over
+//     the wave, v0, is reached by at least N elements of the segment, so nothing
+//     below v0 can be among its N best;
+//  2. elements at or above the current threshold value have their exact keys (logit
+//     desc, token id asc) staged in wave-local LDS;
+//  3. once N keys are staged they are sorted and merged into a sorted list of N keys
+//     held in registers (bitonic networks over cross-lane shuffles), whose N-th key
+//     becomes the exact threshold.
+// No block barriers; the merge code is emitted once (the load loop resumes after it).
+template <int DT, int PL>
+__global__ __launch_bounds__(kSegWaves * kWave) void k_seg_topk(const BArgs a) {
   const Cfg& c = a.c;
-  const int g = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
-  if (row_node(a, b, j) == -2) return;
-  const int tid = threadIdx.x;
+  const int wave = threadIdx.x >> 6;
+  const int lane = lane_id();
+  const int g = blockIdx.x * kSegWaves + wave;
+  const int j = blockIdx.y, b = blockIdx.z;
+  if (g >= a.G || row_node(a, b, j) == -2) return;
+  constexpr int N = PL * kWave;
   constexpr int esz = DT == VRT_BF16 ? 2 : 4;
-  constexpr int EPL = 16 / esz;    // elements per 16-byte load
-  constexpr int NE = kSL * EPL;    // elements per thread (64 bf16, 32 fp32)
-  constexpr int S = seg_elems<DT>();
+  constexpr int EPL = 16 / esz;         // elements per load
+  constexpr int CAP = N + EPL * kWave;  // stage capacity: one load's worth past N
   const int V = c.V;
-  const int base = g * S;
+  const int seg0 = g * seg_elems<DT>();
   const char* row = (const char*)a.logits + ((int64_t)b * a.tstride + (int64_t)j * a.ld) * esz;
+  __shared__ uint64_t s_stage[kSegWaves][CAP];
+  uint64_t* stage = s_stage[wave];
 
-  __shared__ uint64_t s_buf[kSegCap];
-  __shared__ int s_cnt, s_ovf, s_bad;
-  __shared__ uint64_t s_thr;
-
-  // this thread's elements: load q covers [base + (q*kST + tid)*EPL, +EPL)
-  Words wd;
-  static_for<kSL>([&](auto q) {
-    const int e0 = base + (q * kST + tid) * EPL;
-    uint4 v = DT == VRT_BF16 ? make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u)
-                             : make_uint4(0xFF800000u, 0xFF800000u, 0xFF800000u, 0xFF800000u);
-    if (e0 < V) v = load_nt(row + (int64_t)e0 * esz);
-    wd[4 * q + 0] = v.x;
-    wd[4 * q + 1] = v.y;
-    wd[4 * q + 2] = v.z;
-    wd[4 * q + 3] = v.w;
+  // load q of this lane covers elements [seg0 + (q*64 + lane)*EPL, +EPL); elements at
+  // or past V read as -inf
+  u32x4_t d[kSegLoads];
+  static_for<kSegLoads>([&](auto q) {
+    const int e0 = seg0 + (q * kWave + lane) * EPL;
+    const uint32_t ninf = DT == VRT_BF16 ? 0xFF80FF80u : 0xFF800000u;
+    u32x4_t v = {ninf, ninf, ninf, ninf};
+    if (e0 < V) v = __builtin_nontemporal_load((const u32x4_t*)(row + (int64_t)e0 * esz));
+    d[q] = v;
   });
-  auto id_of = [&](int k) { return base + ((k / EPL) * kST + tid) * EPL + (k % EPL); };
+  auto val = [&](const u32x4_t& v, int e) -> float {  // e: compile-time in every use
+    if constexpr (DT == VRT_BF16) return (e & 1) ? bf16_hi(v[e >> 1]) : bf16_lo(v[e >> 1]);
+    else return __uint_as_float(v[e]);
+  };
+  if (seg0 + seg_elems<DT>() > V) {  // the row's last segment: mask a straddling load
+    static_for<kSegLoads>([&](auto q) {
+      const int e0 = seg0 + (q * kWave + lane) * EPL;
+      if (e0 < V && e0 + EPL > V) {
+        static_for<EPL>([&](auto e) {
+          if (e0 + e >= V) {
+            if constexpr (DT == VRT_BF16)
+              d[q][e >> 1] = (e & 1) ? ((d[q][e >> 1] & 0xFFFFu) | 0xFF800000u)
+                                     : ((d[q][e >> 1] & 0xFFFF0000u) | 0xFF80u);
+            else
+              d[q][(int)e] = 0xFF800000u;
+          }
+        });
+      }
+    });
+  }
 
-  // seed: the trunc-th largest of the threads' maxima (largest value, lowest id)
-  float mx = -INFINITY;
-  int mid = 0x7FFFFFFF;
+  // 1. non-finite scan and the lane's PL largest values
   bool bad = false;
-  static_for<NE>([&](auto k) {
-    const float x = elem<DT, k>(wd);
-    const int id = id_of(k);
-    bad |= __builtin_amdgcn_classf(x, 0x203);  // NaN or +inf
-    if (id < V && (x > mx || (x == mx && id < mid))) {
-      mx = x;
-      mid = id;
-    }
+  float lv[PL];
+  static_for<PL>([&](auto s) { lv[s] = -INFINITY; });
+  static_for<kSegLoads>([&](auto q) {
+    static_for<EPL>([&](auto e) {
+      float x = val(d[q], e);
+      bad |= __builtin_amdgcn_classf(x, 0x203);  // NaN or +inf
+      static_for<PL>([&](auto s) {
+        const float hi = fmaxf(lv[s], x);
+        x = fminf(lv[s], x);
+        lv[s] = hi;
+      });
+    });
   });
-  s_buf[tid] = (mid < V) ? sup_key(mx, (uint32_t)mid) : 0ull;
-  if (tid == 0) {
-    s_cnt = 0;
-    s_ovf = 0;
-    s_bad = 0;
-  }
-  __syncthreads();
-  if (c.trunc <= kST) {
-    bitonic_desc(s_buf, kST);
-    if (tid == 0) {
-      const uint64_t t0 = s_buf[c.trunc - 1];
-      s_thr = t0 ? t0 - 1ull : 0ull;
-    }
-  } else if (tid == 0) {
-    s_thr = 0ull;
-  }
-  if (bad) atomicOr(&s_bad, 1);
-  __syncthreads();
+  const bool any_bad = ballot(bad) != 0ull;
+  float v0 = lv[PL - 1];
+  for (int o = 1; o < kWave; o <<= 1) v0 = fminf(v0, __shfl_xor(v0, o, kWave));
 
-  uint64_t done = 0ull;
+  uint64_t top[PL];
+  static_for<PL>([&](auto s) { top[s] = 0ull; });
+  uint64_t thr = 0ull;  // N-th key of the list once it is full
+  float thr_f = v0;
+  int nst = 0;          // staged keys (wave-uniform)
+  int q_next = 0;       // first load not yet scanned (wave-uniform)
   for (;;) {
-    const uint64_t thr = s_thr;
-    const float thr_f = thr ? sup_key_val(thr) : -INFINITY;
-    // cheap filter: one compare per element against the threshold's value
-    uint64_t cand = 0ull;
-    static_for<NE>([&](auto k) { cand |= (elem<DT, k>(wd) >= thr_f ? 1ull : 0ull) << k; });
-    cand &= ~done;
-    // exact keys only for the survivors
-    while (ballot(cand != 0ull)) {
-      const bool has = cand != 0ull;
-      const int k = has ? __builtin_ctzll(cand) : 0;
-      const float x = elem_at<DT>(wd, k);
-      const int id = id_of(k);
-      const bool ok = has && id < V;
-      const uint64_t key = ok ? sup_key(x, (uint32_t)id) : 0ull;
-      if (append(ok && key > thr, key, s_buf, kSegCap, &s_cnt, &s_ovf)) done |= 1ull << k;
-      if (has) cand &= cand - 1ull;
+    // the data is opaque to the optimiser here, so that unpacked values are not kept
+    // live across the phases (they are recomputed: one ALU op each)
+#pragma unroll
+    for (int q = 0; q < kSegLoads; ++q) asm volatile("" : "+v"(d[q]));
+    // 2. scan loads q_next.. until the stage holds N keys
+    static_for<kSegLoads>([&](auto q) {
+      if (q >= q_next && nst < N) {
+        uint32_t cm = 0;
+        static_for<EPL>([&](auto e) { cm |= (val(d[q], e) >= thr_f ? 1u : 0u) << e; });
+        while (ballot(cm != 0u)) {
+          const bool has = cm != 0u;
+          const int e = has ? __builtin_ctz(cm) : 0;
+          const uint32_t w = d[q][DT == VRT_BF16 ? (e >> 1) : e];
+          const float x = DT == VRT_BF16 ? ((e & 1) ? bf16_hi(w) : bf16_lo(w)) : __uint_as_float(w);
+          const int id = seg0 + (q * kWave + lane) * EPL + e;
+          const uint64_t key = sup_key(x, (uint32_t)id);
+          const bool pass = has && id < V && key > thr;
+          const uint64_t mask = ballot(pass);
+          if (pass) stage[nst + __builtin_popcountll(mask & ((1ull << lane) - 1ull))] = key;
+          nst += __builtin_popcountll(mask);
+          if (has) cm &= cm - 1u;
+        }
+        q_next = q + 1;
+      }
+    });
+    const bool last = q_next >= kSegLoads;
+    // 3. merge full stages (all of it after the last load) into the list
+    int off = 0;
+    while (nst - off >= N || (last && nst > off)) {
+      const int cnt = min(N, nst - off);
+      wave_sync();
+      uint64_t add[PL];
+      static_for<PL>([&](auto s) {
+        const int p = lane * PL + s;
+        add[s] = p < cnt ? stage[off + p] : 0ull;
+      });
+      wave_sort_desc<PL>(add);
+      wave_merge_top<PL>(top, add);
+      off += cnt;
+      const uint64_t t = shfl64(top[PL - 1], kWave - 1);
+      if (t) {
+        thr = t;
+        thr_f = sup_key_val(t);
+      }
     }
-    __syncthreads();
-    const int ov = s_ovf;
-    const int cnt = s_cnt;
-    __syncthreads();
-    if (!ov) break;
-    // compaction: keep the best trunc keys, raise the threshold to the trunc-th
-    const int n = sort_prefix(s_buf, cnt, kSegCap);
-    if (tid == 0) {
-      if (n >= c.trunc) s_thr = s_buf[c.trunc - 1];
-      s_cnt = min(n, c.trunc);
-      s_ovf = 0;
-    }
-    __syncthreads();
+    if (last) break;
+    // the rest (fewer than N keys, at positions >= N) moves to the front
+    const int rem = nst - off;
+    wave_sync();
+    for (int i = lane; i < rem; i += kWave) stage[i] = stage[off + i];
+    nst = rem;
   }
-  const int n = min(sort_prefix(s_buf, s_cnt, kSegCap), c.trunc);
+  // the segment's list, positions >= trunc cleared
   const int64_t sg = ((int64_t)b * c.FP + j) * a.G + g;
-  for (int k = tid; k < n; k += kST) a.seg_keys[sg * c.TC + k] = s_buf[k];
-  if (tid == 0) a.seg_cnt[sg] = n | (s_bad ? (1 << 30) : 0);
+  static_for<PL>([&](auto s) {
+    const int p = lane * PL + s;
+    a.seg_keys[sg * N + p] = p < c.TC ? top[s] : 0ull;
+  });
+  if (lane == 0) a.seg_bad[sg] = any_bad ? 1 : 0;
 }
 
 // Expansion of one parent by wave 0 (RheoSampling key design 2), BS support ranks
@@ -371,11 +363,14 @@ __device__ void expand_row(const BArgs& a, int b, int node, int n_sup, const uin
   }
 }
 
-template <int BS>
-__global__ __launch_bounds__(256) void k_merge_expand(const BArgs a) {
+// One wave per parent: merge its segments' sorted lists (the row's top trunc is in
+// the union of the segments' top trunc), then expand the parent.
+template <int PL>
+__global__ __launch_bounds__(kWave) void k_merge_expand(const BArgs a) {
   const Cfg& c = a.c;
   const int j = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  constexpr int N = PL * kWave;
   const int64_t ncb = (int64_t)b * c.NC;
   const int cbase = layer_base(c, a.layer) + j * c.K;
   const int ridx = row_base(c, a.layer) + j;
@@ -383,8 +378,8 @@ __global__ __launch_bounds__(256) void k_merge_expand(const BArgs a) {
 
   if (a.layer == 0) {
     // a new step: forget every candidate of the previous one, reset SMART's state
-    for (int t = c.K + tid; t < c.NC; t += blockDim.x) a.t.cand_kind[ncb + t] = 0;
-    if (tid == 0) {
+    for (int t = c.K + lane; t < c.NC; t += kWave) a.t.cand_kind[ncb + t] = 0;
+    if (lane == 0) {
       double* sm = a.t.smart + (int64_t)b * 8;
       sm[0] = 0.0; sm[1] = 1.0; sm[2] = 1.0; sm[3] = 0.0; sm[4] = 0.0;
       sm[5] = sm[6] = sm[7] = 0.0;
@@ -392,54 +387,41 @@ __global__ __launch_bounds__(256) void k_merge_expand(const BArgs a) {
   }
   const int node = row_node(a, b, j);
   if (node == -2) {
-    for (int s = tid; s < c.K; s += blockDim.x) a.t.cand_kind[ncb + cbase + s] = 0;
-    if (tid == 0) a.t.row_tail_n[ktb] = 0;
+    for (int s = lane; s < c.K; s += kWave) a.t.cand_kind[ncb + cbase + s] = 0;
+    if (lane == 0) a.t.row_tail_n[ktb] = 0;
     return;
   }
 
-  extern __shared__ uint64_t s_buf[];  // [kMergeCap] keys
-  float* s_q = (float*)(s_buf + kMergeCap);
-  __shared__ int s_bad;
-  if (tid == 0) s_bad = 0;
-  // merge the segments' sorted lists: keep the running top trunc in s_buf[0..TC),
-  // fill the rest with whole lists, sort, repeat
-  const int TC = c.TC;
+  __shared__ uint64_t s_buf[N];
+  __shared__ float s_q[N];
   const int64_t sg0 = ((int64_t)b * c.FP + j) * a.G;
-  int have = 0;  // keys in s_buf[0..TC) from earlier rounds
-  int g = 0;
-  const int per_round = max(1, kMergeCap / TC - 1);
-  for (;;) {
-    const int gend = min(a.G, g + per_round);
-    // lists g..gend-1 go to s_buf[TC + (gg - g) * TC ..]
-    for (int x = tid; x < (gend - g) * TC; x += blockDim.x) {
-      const int gg = g + x / TC, k = x % TC;
-      const int cw = a.seg_cnt[sg0 + gg];
-      const int cnt = cw & 0x3FFFFFFF;
-      if (k == 0 && (cw >> 30)) s_bad = 1;
-      s_buf[TC + x] = k < cnt ? a.seg_keys[(sg0 + gg) * TC + k] : 0ull;
-    }
-    for (int k = have + tid; k < TC; k += blockDim.x) s_buf[k] = 0ull;
-    __syncthreads();
-    sort_prefix(s_buf, TC + (gend - g) * TC, kMergeCap);
-    __syncthreads();
-    have = TC;
-    g = gend;
-    if (g >= a.G) break;
+  auto load_list = [&](int g, uint64_t (&l)[PL]) {
+    const uint64_t* src = a.seg_keys + (sg0 + g) * N + lane * PL;
+    static_for<PL>([&](auto s) { l[s] = src[s]; });
+  };
+  uint64_t top[PL], nxt[PL];
+  load_list(0, top);
+  if (a.G > 1) load_list(1, nxt);
+  for (int g = 1; g < a.G; ++g) {
+    uint64_t cur[PL];
+    static_for<PL>([&](auto s) { cur[s] = nxt[s]; });
+    if (g + 1 < a.G) load_list(g + 1, nxt);
+    wave_merge_top<PL>(top, cur);
   }
-  // support size: the non-empty keys among the top trunc
-  __shared__ int s_nsup;
-  if (tid == 0) {
-    int n = 0;
-    while (n < TC && s_buf[n] != 0ull) ++n;
-    s_nsup = n;
-  }
-  __syncthreads();
-  const int n_sup = s_nsup;
-  if (tid >= kWave) return;
+  int bad = 0;
+  for (int g = lane; g < a.G; g += kWave) bad |= a.seg_bad[sg0 + g];
+  // support: the non-empty keys among the first trunc positions
+  int cnt = 0;
+  static_for<PL>([&](auto s) {
+    const int p = lane * PL + s;
+    const uint64_t k = p < c.TC ? top[s] : 0ull;
+    s_buf[p] = k;
+    cnt += k != 0ull;
+  });
+  const int n_sup = wave_sum_i(cnt);
+  wave_sync();
 
-  // ---- expansion by wave 0
-  const int lane = lane_id();
-  uint32_t st = s_bad ? VRT_ST_DRAFT_NONFINITE : 0u;
+  uint32_t st = ballot(bad != 0) ? VRT_ST_DRAFT_NONFINITE : 0u;
   const float M = n_sup > 0 ? sup_key_val(s_buf[0]) : -INFINITY;
   if (n_sup == 0 || M == -INFINITY) st |= VRT_ST_DRAFT_EMPTY;
   if (st) {
@@ -448,7 +430,7 @@ __global__ __launch_bounds__(256) void k_merge_expand(const BArgs a) {
     if (lane == 0) a.t.row_tail_n[ktb] = 0;
     return;
   }
-  expand_row<BS>(a, b, node, n_sup, s_buf, s_q, ncb, cbase, ktb);
+  expand_row<PL>(a, b, node, n_sup, s_buf, s_q, ncb, cbase, ktb);
 }
 
 // Per-tree ranking of the layer's children: top-W frontier (top-R mode) or SMART.
@@ -629,39 +611,57 @@ int segments(int V) {
   return (V + seg_elems<DT>() - 1) / seg_elems<DT>();
 }
 
+int list_len(const Cfg& c) { return max(128, next_pow2(c.trunc)); }
+
+template <int DT>
+hipError_t launch_layer(const BArgs& a, int rows, hipStream_t stream) {
+  const Cfg& c = a.c;
+  const dim3 g1((a.G + kSegWaves - 1) / kSegWaves, rows, c.B);
+  const dim3 g2(rows, c.B);
+  const dim3 t1(kSegWaves * kWave), t2(kWave);
+  switch (list_len(c) / kWave) {
+    case 2:
+      hipLaunchKernelGGL((k_seg_topk<DT, 2>), g1, t1, 0, stream, a);
+      hipLaunchKernelGGL(k_merge_expand<2>, g2, t2, 0, stream, a);
+      break;
+    case 4:
+      hipLaunchKernelGGL((k_seg_topk<DT, 4>), g1, t1, 0, stream, a);
+      hipLaunchKernelGGL(k_merge_expand<4>, g2, t2, 0, stream, a);
+      break;
+    case 8:
+      hipLaunchKernelGGL((k_seg_topk<DT, 8>), g1, t1, 0, stream, a);
+      hipLaunchKernelGGL(k_merge_expand<8>, g2, t2, 0, stream, a);
+      break;
+    default:
+      hipLaunchKernelGGL((k_seg_topk<DT, 16>), g1, t1, 0, stream, a);
+      hipLaunchKernelGGL(k_merge_expand<16>, g2, t2, 0, stream, a);
+      break;
+  }
+  return hipGetLastError();
+}
+
+int segments_of(const Cfg& c) {
+  return c.dtype == VRT_BF16 ? segments<VRT_BF16>(c.V) : segments<VRT_F32>(c.V);
+}
+
 }  // namespace
 
 size_t build_ws_bytes(const Cfg& c) {
-  const int G = c.dtype == VRT_BF16 ? segments<VRT_BF16>(c.V) : segments<VRT_F32>(c.V);
-  const size_t rows = (size_t)c.B * c.FP * G;
-  return rows * c.TC * sizeof(uint64_t) + ((rows * sizeof(int) + 255) & ~(size_t)255);
+  const size_t lists = (size_t)c.B * c.FP * segments_of(c);
+  return lists * list_len(c) * sizeof(uint64_t) + ((lists * sizeof(int) + 255) & ~(size_t)255);
 }
 
 hipError_t launch_build_layer(const Cfg& c, const TreePtrs& t, int layer, const void* logits,
                               int64_t ld, int64_t tstride, uint64_t seed, uint32_t step,
                               uint32_t* stats, void* ws, hipStream_t stream) {
-  const int G = c.dtype == VRT_BF16 ? segments<VRT_BF16>(c.V) : segments<VRT_F32>(c.V);
+  const int G = segments_of(c);
+  const size_t lists = (size_t)c.B * c.FP * G;
   uint64_t* seg_keys = (uint64_t*)ws;
-  int* seg_cnt = (int*)((char*)ws + (size_t)c.B * c.FP * G * c.TC * sizeof(uint64_t));
-  BArgs a{c, t, layer, logits, ld, tstride, seed, step, stats, G, seg_keys, seg_cnt};
+  int* seg_bad = (int*)((char*)ws + lists * list_len(c) * sizeof(uint64_t));
+  BArgs a{c, t, layer, logits, ld, tstride, seed, step, stats, G, seg_keys, seg_bad};
   const int rows = layer == 0 ? 1 : c.FP;
-  const dim3 g1(G, rows, c.B);
-  if (c.dtype == VRT_BF16)
-    hipLaunchKernelGGL(k_seg_select<VRT_BF16>, g1, dim3(kST), 0, stream, a);
-  else
-    hipLaunchKernelGGL(k_seg_select<VRT_F32>, g1, dim3(kST), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int bs = max(128, next_pow2(c.trunc)) / kWave;
-  const size_t lds = (size_t)kMergeCap * 8 + (size_t)bs * kWave * 4;
-  const dim3 g2(rows, c.B);
-  switch (bs) {
-    case 2: hipLaunchKernelGGL(k_merge_expand<2>, g2, dim3(256), lds, stream, a); break;
-    case 4: hipLaunchKernelGGL(k_merge_expand<4>, g2, dim3(256), lds, stream, a); break;
-    case 8: hipLaunchKernelGGL(k_merge_expand<8>, g2, dim3(256), lds, stream, a); break;
-    default: hipLaunchKernelGGL(k_merge_expand<16>, g2, dim3(256), lds, stream, a); break;
-  }
-  e = hipGetLastError();
+  hipError_t e = c.dtype == VRT_BF16 ? launch_layer<VRT_BF16>(a, rows, stream)
+                                     : launch_layer<VRT_F32>(a, rows, stream);
   if (e != hipSuccess) return e;
   const int span = (layer == 0 ? 1 : c.P) * c.K;
   const size_t lds2 = (size_t)next_pow2(max(span, 2)) * 8;

@@ -180,6 +180,80 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
+// ---------------------------------------------------------------------------
+// Sorted key lists held in a wave's registers: PL keys per lane, position
+// p = lane*PL + s, N = 64*PL keys. Bitonic networks run on these with cross-lane
+// shuffles only (no LDS, no barriers).
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
+  const uint32_t lo = __shfl_xor((uint32_t)v, m, kWave);
+  const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, kWave);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t shfl64(uint64_t v, int src) {
+  const uint32_t lo = __shfl((uint32_t)v, src, kWave);
+  const uint32_t hi = __shfl((uint32_t)(v >> 32), src, kWave);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// One compare-exchange stage of a bitonic network: partner q = p ^ J; pairs inside
+// blocks with (p & SIZE) == 0 are ordered descending, the others ascending.
+template <int PL, int SIZE, int J>
+__device__ __forceinline__ void bitonic_stage(uint64_t (&k)[PL], int lane) {
+  if constexpr (J < PL) {
+    static_for<PL>([&](auto s) {
+      constexpr int t = s ^ J;
+      if constexpr (s < t) {
+        const bool desc = ((lane * PL + s) & SIZE) == 0;
+        const uint64_t x = k[s], y = k[t];
+        const bool sw = desc ? (x < y) : (x > y);
+        k[s] = sw ? y : x;
+        k[t] = sw ? x : y;
+      }
+    });
+  } else {
+    constexpr int LJ = J / PL;
+    static_for<PL>([&](auto s) {
+      const uint64_t x = k[s];
+      const uint64_t y = shfl_xor64(x, LJ);
+      const bool desc = ((lane * PL + s) & SIZE) == 0;
+      const bool lower = (lane & LJ) == 0;
+      const bool keep_max = lower == desc;
+      k[s] = keep_max ? (x > y ? x : y) : (x < y ? x : y);
+    });
+  }
+}
+
+template <int PL, int SIZE, int J>
+__device__ __forceinline__ void bitonic_stages(uint64_t (&k)[PL], int lane) {
+  bitonic_stage<PL, SIZE, J>(k, lane);
+  if constexpr (J > 1) bitonic_stages<PL, SIZE, J / 2>(k, lane);
+}
+
+template <int PL, int SIZE>
+__device__ __forceinline__ void bitonic_sort_from(uint64_t (&k)[PL], int lane) {
+  bitonic_stages<PL, SIZE, SIZE / 2>(k, lane);
+  if constexpr (SIZE < PL * kWave) bitonic_sort_from<PL, SIZE * 2>(k, lane);
+}
+
+// Sort the wave list descending.
+template <int PL>
+__device__ __forceinline__ void wave_sort_desc(uint64_t (&k)[PL]) {
+  bitonic_sort_from<PL, 2>(k, lane_id());
+}
+
+// top <- the N largest of top and add, both sorted descending; result sorted
+// descending. (max of top[p] and add[N-1-p] is a bitonic sequence holding the N
+// largest; one bitonic merge orders it.)
+template <int PL>
+__device__ __forceinline__ void wave_merge_top(uint64_t (&top)[PL], const uint64_t (&add)[PL]) {
+  const int lane = lane_id();
+  static_for<PL>([&](auto s) {
+    const uint64_t r = shfl64(add[PL - 1 - s], kWave - 1 - lane);
+    top[s] = top[s] > r ? top[s] : r;
+  });
+  bitonic_stages<PL, 2 * PL * kWave, PL * kWave / 2>(top, lane);
+}
+
 __host__ __device__ inline int next_pow2(int n) {
   int p = 1;
   while (p < n) p <<= 1;
