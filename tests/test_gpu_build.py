@@ -47,6 +47,11 @@ CASES = [
     ("small_fp32_flat", _small(dtype=synth.F32, zipf=(0.8,), V=4100, R=30)),
     ("small_peaked_W3", _small(zipf=(1.5,), W=3, R=25, D=7)),
     ("stress_mixed_m0", _small(B=4, V=9000, zipf=(1.5, 0.8), split=2, R=64, D=6, K=8, m=0)),
+    ("small_trunc512_fp32", _small(trunc=512, V=20000, dtype=synth.F32, R=30, D=4)),
+    ("small_trunc1024", _small(trunc=1024, V=20000, R=30, D=3, K=12)),
+    ("small_all_ties", _small(zipf=(), draft_scale=0.0, V=9000, R=20, D=3)),
+    ("small_all_ties_fp32_trunc256", _small(zipf=(), draft_scale=0.0, V=9000, R=20, D=3,
+                                           dtype=synth.F32, trunc=256)),
     ("smart_small", _smart_small()),
     ("smart_small_m0_alpha08", _smart_small(m=0, alpha=0.8, budget=24)),
 ]

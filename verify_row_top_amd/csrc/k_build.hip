@@ -1,16 +1,15 @@
 // Draft-tree construction on gfx950 (RheoSampling framework flowchart, key designs
-// 1-2; SMART key design 3 as the switchable keep rule). Per layer, three kernels:
+// 1-2; SMART key design 3 as the switchable keep rule). Per layer, two kernels;
+// then one to emit the tree:
 //
-// k_seg_topk: one wave per 16 KB segment of an expanded parent's draft row streams
-//   the segment once (non-temporal 16-byte loads, next batch in flight) and keeps the
-//   segment's best keys (logit desc, token id asc) sorted in registers: one compare
-//   per element against a threshold, exact keys only for survivors, bitonic sorts and
-//   merges by cross-lane shuffles.
-// k_merge_expand: one wave per parent merges its segments' lists into the row's
-//   top-trunc support and expands the parent: untempered softmax on the support with
-//   the fixed ranking recipe, tempered softmax in fp64, the probe draw from the
-//   tempered tail, the proxy min{q(x_m), z}, the K child slots and the parent's tail
-//   table.
+// k_select_expand: one 8-wave block per expanded parent. Each wave selects the top
+//   keys (logit desc, token id asc) of 16 KB segments of the parent's draft row: all
+//   loads in flight at once (non-temporal), a threshold from the lanes' largest values
+//   that at least N elements reach, exact keys only for the few survivors, bitonic
+//   sorts by cross-lane shuffles. The waves' lists merge pairwise through LDS; wave 0
+//   then expands the parent: untempered softmax on the top-trunc support with the
+//   fixed ranking recipe, tempered softmax in fp64, the probe draw from the tempered
+//   tail, the proxy min{q(x_m), z}, the K child slots and the parent's tail table.
 // k_rank_layer: one block per tree ranks the layer's children by (path score desc,
 //   creation index asc) and keeps the top W (top-R mode) or runs SMART's sequential
 //   keep rule over them.
@@ -48,9 +47,6 @@ struct BArgs {
   uint64_t seed;
   uint32_t step;
   uint32_t* stats;
-  int G;               // segments per row
-  uint64_t* seg_keys;  // [B][FP][G][N] sorted top keys of each segment, N = 64 * PL
-  int* seg_bad;        // [B][FP][G] a NaN or +inf logit was seen
 };
 
 // The node frontier position j of tree b expands at this layer (-1 = root), or -2
@@ -68,63 +64,104 @@ __device__ __forceinline__ int row_node(const BArgs& a, int b, int j) {
   return node;
 }
 
-constexpr int kSegWaves = 4;  // waves (one segment each) per selection block
-constexpr int kSegLoads = 16; // 16-byte loads per lane per segment, all in flight at once
+constexpr int kSegLoads = 16;  // 16-byte loads per lane per segment, all in flight at once
 
 template <int DT>
 constexpr int seg_elems() { return kWave * kSegLoads * (DT == VRT_BF16 ? 8 : 4); }
 
-// Segment top-N (N = 64*PL >= trunc): one wave per segment of an expanded parent's
-// draft row. The wave issues all of its loads at once (the segment lives in 64
-// registers per lane), then:
-//  1. every lane finds the PL-th largest of its own values; the minimum of these over
-//     the wave, v0, is reached by at least N elements of the segment, so nothing
-//     below v0 can be among its N best;
-//  2. elements at or above the current threshold value have their exact keys (logit
-//     desc, token id asc) staged in wave-local LDS;
-//  3. once N keys are staged they are sorted and merged into a sorted list of N keys
-//     held in registers (bitonic networks over cross-lane shuffles), whose N-th key
-//     becomes the exact threshold.
-// No block barriers; the merge code is emitted once (the load loop resumes after it).
-template <int DT, int PL>
-__global__ __launch_bounds__(kSegWaves * kWave) void k_seg_topk(const BArgs a) {
-  const Cfg& c = a.c;
-  const int wave = threadIdx.x >> 6;
-  const int lane = lane_id();
-  const int g = blockIdx.x * kSegWaves + wave;
-  const int j = blockIdx.y, b = blockIdx.z;
-  if (g >= a.G || row_node(a, b, j) == -2) return;
-  constexpr int N = PL * kWave;
-  constexpr int esz = DT == VRT_BF16 ? 2 : 4;
-  constexpr int EPL = 16 / esz;         // elements per load
-  constexpr int CAP = N + EPL * kWave;  // stage capacity: one load's worth past N
-  const int V = c.V;
-  const int seg0 = g * seg_elems<DT>();
-  const char* row = (const char*)a.logits + ((int64_t)b * a.tstride + (int64_t)j * a.ld) * esz;
-  __shared__ uint64_t s_stage[kSegWaves][CAP];
-  uint64_t* stage = s_stage[wave];
+// Waves of a row block: fewer for long lists, whose stages need more LDS.
+template <int PL>
+constexpr int sel_waves() { return PL <= 4 ? 8 : (PL == 8 ? 4 : 2); }
+// Working-list keys per lane while a segment is selected: twice the output list when
+// that stays small, so that the usual survivor count (a little over N) needs one sort.
+template <int PL>
+constexpr int work_pl() { return PL <= 4 ? 2 * PL : PL; }
 
-  // load q of this lane covers elements [seg0 + (q*64 + lane)*EPL, +EPL); elements at
-  // or past V read as -inf
+// Segment keys. bf16 rows: 32 bits, the order-preserving image of the 16-bit value
+// above 0xFFFF - (index within the segment); fp32 rows: the 64-bit row key (value,
+// token id). Larger is better; zero is empty.
+template <int DT>
+using SegKey = std::conditional_t<DT == VRT_BF16, uint32_t, uint64_t>;
+
+template <int DT, int PL>
+constexpr int kstage_cap() {
+  // staged keys: below one working list plus one round; also holds the output as row keys
+  const int stage = work_pl<PL>() * kWave + kWave * (DT == VRT_BF16 ? 8 : 4);
+  const int out = PL * kWave * 8 / (DT == VRT_BF16 ? 4 : 8);
+  return stage > out ? stage : out;
+}
+constexpr int kRing = 5 * kWave;  // group ring: fewer than 64 left over + 4 loads' groups
+
+// Order-preserving 16-bit images of the two bf16 halves of a word.
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t ord16x2(uint32_t w) {
+  const s16x2 v = __builtin_bit_cast(s16x2, w);
+  const s16x2 sg = v >> (s16x2){15, 15};
+  const uint32_t m = (__builtin_bit_cast(uint32_t, sg) & 0x7FFF7FFFu) | 0x80008000u;
+  return w ^ m;
+}
+
+__device__ __forceinline__ float max3n(float a, float b, float c) {  // NaN-propagating
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+
+// Per-wave LDS of the segment selection.
+template <int DT, int PL>
+struct SegLds {
+  SegKey<DT> keys[kstage_cap<DT, PL>()];
+  u32x4_t grp[kRing];    // staged groups (one lane's 16-byte load)
+  uint16_t gidx[kRing];  // their load index * 64 + lane
+};
+
+// Top N = 64*PL keys (logit desc, token id asc) of segment g of a draft row, by one
+// wave, into cur[] (row keys, position p = lane*PL + s, sorted descending, zero =
+// empty).
+//  1. All 16 loads of the lane are issued at once: the segment lives in 64 registers.
+//     A group is one lane's load (8 bf16 or 4 fp32 elements).
+//  2. Each lane keeps the LV largest of its 16 group maxima; the N-th largest of
+//     these 64*LV values, v0 (bitwise search over ballot counts), is reached by at
+//     least N distinct elements, so no element below v0 is among the segment's N
+//     best. The group maxima propagate NaN, which flags non-finite rows cheaply.
+//  3. Groups whose maximum reaches the threshold are copied to an LDS ring, four
+//     loads at a time; lane i then takes the i-th staged group and stages the exact
+//     keys of its elements above the threshold.
+//  4. Staged keys are sorted (bitonic network over lane exchanges) into a working
+//     list; should more survive than it holds (ties, flat rows), full stages are
+//     merged into it and its N-th key becomes an exact threshold.
+// No block barriers; the code of steps 3-4 is emitted once (the loop resumes).
+template <int DT, int PL>
+__device__ __forceinline__ void seg_select(const char* row, int g, int V, SegLds<DT, PL>& L,
+                                           uint64_t (&cur)[PL], bool& bad) {
+  using K = SegKey<DT>;
+  constexpr bool BF = DT == VRT_BF16;
+  constexpr int N = PL * kWave;
+  constexpr int QL = work_pl<PL>();
+  constexpr int QN = QL * kWave;
+  constexpr int LV = QL;
+  constexpr int esz = BF ? 2 : 4;
+  constexpr int EPL = 16 / esz;  // elements per group
+  constexpr int KCAP = kstage_cap<DT, PL>();
+  const int lane = lane_id();
+  const int seg0 = g * seg_elems<DT>();
+  const int vlim = V - seg0;  // elements of this segment inside the row
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
+
+  // 1. loads; elements at or past V read as -inf
   u32x4_t d[kSegLoads];
   static_for<kSegLoads>([&](auto q) {
     const int e0 = seg0 + (q * kWave + lane) * EPL;
-    const uint32_t ninf = DT == VRT_BF16 ? 0xFF80FF80u : 0xFF800000u;
+    const uint32_t ninf = BF ? 0xFF80FF80u : 0xFF800000u;
     u32x4_t v = {ninf, ninf, ninf, ninf};
     if (e0 < V) v = __builtin_nontemporal_load((const u32x4_t*)(row + (int64_t)e0 * esz));
     d[q] = v;
   });
-  auto val = [&](const u32x4_t& v, int e) -> float {  // e: compile-time in every use
-    if constexpr (DT == VRT_BF16) return (e & 1) ? bf16_hi(v[e >> 1]) : bf16_lo(v[e >> 1]);
-    else return __uint_as_float(v[e]);
-  };
-  if (seg0 + seg_elems<DT>() > V) {  // the row's last segment: mask a straddling load
+  if (vlim < seg_elems<DT>()) {  // the row's last segment: mask a straddling load
     static_for<kSegLoads>([&](auto q) {
       const int e0 = seg0 + (q * kWave + lane) * EPL;
       if (e0 < V && e0 + EPL > V) {
         static_for<EPL>([&](auto e) {
           if (e0 + e >= V) {
-            if constexpr (DT == VRT_BF16)
+            if constexpr (BF)
               d[q][e >> 1] = (e & 1) ? ((d[q][e >> 1] & 0xFFFFu) | 0xFF800000u)
                                      : ((d[q][e >> 1] & 0xFFFF0000u) | 0xFF80u);
             else
@@ -135,91 +172,182 @@ __global__ __launch_bounds__(kSegWaves * kWave) void k_seg_topk(const BArgs a) {
     });
   }
 
-  // 1. non-finite scan and the lane's PL largest values
-  bool bad = false;
-  float lv[PL];
-  static_for<PL>([&](auto s) { lv[s] = -INFINITY; });
+  // 2. group maxima, the non-finite check, the lane's LV largest, the threshold
+  float gm[kSegLoads];
   static_for<kSegLoads>([&](auto q) {
-    static_for<EPL>([&](auto e) {
-      float x = val(d[q], e);
-      bad |= __builtin_amdgcn_classf(x, 0x203);  // NaN or +inf
-      static_for<PL>([&](auto s) {
-        const float hi = fmaxf(lv[s], x);
-        x = fminf(lv[s], x);
-        lv[s] = hi;
-      });
+    if constexpr (BF) {
+      auto lo = [&](int i) { return bf16_lo(d[q][i]); };
+      auto hi = [&](int i) { return bf16_hi(d[q][i]); };
+      const float t1 = max3n(lo(0), hi(0), lo(1));
+      const float t2 = max3n(hi(1), lo(2), hi(2));
+      gm[q] = __builtin_elementwise_maximum(max3n(lo(3), hi(3), t1), t2);
+    } else {
+      auto f = [&](int i) { return __uint_as_float(d[q][i]); };
+      gm[q] = __builtin_elementwise_maximum(max3n(f(0), f(1), f(2)), f(3));
+    }
+  });
+  bool nf = false;
+  static_for<kSegLoads>([&](auto q) { nf |= __builtin_amdgcn_classf(gm[q], 0x203); });  // NaN, +inf
+  bad |= ballot(nf) != 0ull;
+  float lv[LV];
+  static_for<LV>([&](auto s) { lv[s] = -INFINITY; });
+  static_for<kSegLoads>([&](auto q) {
+    float x = gm[q];
+    static_for<LV>([&](auto s) {
+      const float h = fmaxf(lv[s], x);
+      x = fminf(lv[s], x);
+      lv[s] = h;
     });
   });
-  const bool any_bad = ballot(bad) != 0ull;
-  float v0 = lv[PL - 1];
-  for (int o = 1; o < kWave; o <<= 1) v0 = fminf(v0, __shfl_xor(v0, o, kWave));
+  constexpr int RB = BF ? 16 : 32;  // significant bits of the order-preserving image
+  uint32_t o[LV];
+  static_for<LV>([&](auto s) { o[s] = ord32(lv[s]) >> (32 - RB); });
+  uint32_t pre = 0u;  // largest t with at least N candidates at or above t
+  static_for<RB>([&](auto i) {
+    const uint32_t t = pre | (1u << (RB - 1 - i));
+    int cnt = 0;
+    static_for<LV>([&](auto s) { cnt += __builtin_popcountll(ballot(o[s] >= t)); });
+    if (cnt >= N) pre = t;
+  });
+  K thr;  // a key is kept iff key > thr
+  if constexpr (BF) thr = pre ? (pre << 16) - 1u : 0u;
+  else thr = pre ? ((uint64_t)pre << 32) - 1ull : 0ull;
+  // the value of the threshold (a pre-test on values; exact for bf16 images too)
+  auto value_of = [&](uint32_t img) -> float {
+    if constexpr (BF) {
+      const uint32_t h = (img & 0x8000u) ? (img & 0x7FFFu) : (~img & 0xFFFFu);
+      return __uint_as_float(h << 16);
+    } else {
+      return unord32(img);
+    }
+  };
+  float thr_f = pre ? value_of(pre) : -INFINITY;
 
-  uint64_t top[PL];
-  static_for<PL>([&](auto s) { top[s] = 0ull; });
-  uint64_t thr = 0ull;  // N-th key of the list once it is full
-  float thr_f = v0;
-  int nst = 0;          // staged keys (wave-uniform)
-  int q_next = 0;       // first load not yet scanned (wave-uniform)
+  K work[QL];
+  static_for<QL>([&](auto s) { work[s] = 0; });
+  bool have = false;
+  int nst = 0, ngrp = 0, head = 0, qb_next = 0;
+  wave_sync();
   for (;;) {
-    // the data is opaque to the optimiser here, so that unpacked values are not kept
-    // live across the phases (they are recomputed: one ALU op each)
-#pragma unroll
-    for (int q = 0; q < kSegLoads; ++q) asm volatile("" : "+v"(d[q]));
-    // 2. scan loads q_next.. until the stage holds N keys
-    static_for<kSegLoads>([&](auto q) {
-      if (q >= q_next && nst < N) {
-        uint32_t cm = 0;
-        static_for<EPL>([&](auto e) { cm |= (val(d[q], e) >= thr_f ? 1u : 0u) << e; });
-        while (ballot(cm != 0u)) {
-          const bool has = cm != 0u;
-          const int e = has ? __builtin_ctz(cm) : 0;
-          const uint32_t w = d[q][DT == VRT_BF16 ? (e >> 1) : e];
-          const float x = DT == VRT_BF16 ? ((e & 1) ? bf16_hi(w) : bf16_lo(w)) : __uint_as_float(w);
-          const int id = seg0 + (q * kWave + lane) * EPL + e;
-          const uint64_t key = sup_key(x, (uint32_t)id);
-          const bool pass = has && id < V && key > thr;
-          const uint64_t mask = ballot(pass);
-          if (pass) stage[nst + __builtin_popcountll(mask & ((1ull << lane) - 1ull))] = key;
-          nst += __builtin_popcountll(mask);
-          if (has) cm &= cm - 1u;
+    // 3a. candidate groups of the next four loads go to the ring
+    if (ngrp < kWave && qb_next < kSegLoads / 4) {
+      static_for<kSegLoads / 4>([&](auto qb) {
+        if (qb == qb_next) {
+          static_for<4>([&](auto i) {
+            constexpr int q = 4 * qb + i;
+            const bool cg = gm[q] >= thr_f;
+            const uint64_t m = ballot(cg);
+            int pos = head + ngrp + (int)__builtin_popcountll(m & lt_mask);
+            pos = pos >= kRing ? pos - kRing : pos;
+            if (cg) {
+              L.grp[pos] = d[q];
+              L.gidx[pos] = (uint16_t)(q * kWave + lane);
+            }
+            ngrp += __builtin_popcountll(m);
+          });
         }
-        q_next = q + 1;
-      }
-    });
-    const bool last = q_next >= kSegLoads;
-    // 3. merge full stages (all of it after the last load) into the list
-    int off = 0;
-    while (nst - off >= N || (last && nst > off)) {
-      const int cnt = min(N, nst - off);
-      wave_sync();
-      uint64_t add[PL];
-      static_for<PL>([&](auto s) {
-        const int p = lane * PL + s;
-        add[s] = p < cnt ? stage[off + p] : 0ull;
       });
-      wave_sort_desc<PL>(add);
-      wave_merge_top<PL>(top, add);
+      ++qb_next;
+    }
+    const bool loads_done = qb_next >= kSegLoads / 4;
+    // 3b. one round: lane i takes the i-th staged group and stages its keys
+    if (ngrp >= kWave || (loads_done && ngrp > 0)) {
+      const int take = min(ngrp, kWave);
+      wave_sync();
+      const bool has = lane < take;
+      int slot = head + lane;
+      slot = slot >= kRing ? slot - kRing : slot;
+      u32x4_t gw = {0u, 0u, 0u, 0u};
+      int li0 = 0;
+      if (has) {
+        gw = L.grp[slot];
+        li0 = L.gidx[slot] * EPL;
+      }
+      K* dump = L.keys + KCAP - 1;  // never holds a staged key
+      auto stage = [&](bool pass, K key) {
+        const uint64_t mask = ballot(pass);
+        const int pos = nst + (int)__builtin_popcountll(mask & lt_mask);
+        *(pass ? L.keys + pos : dump) = key;
+        nst += __builtin_popcountll(mask);
+      };
+      if constexpr (BF) {
+        const uint32_t c0 = 0xFFFFu - (uint32_t)li0;
+        static_for<4>([&](auto wi) {
+          const uint32_t od = ord16x2(gw[(int)wi]);
+          static_for<2>([&](auto hf) {
+            constexpr int e = 2 * wi + hf;
+            const uint32_t key = hf ? ((od & 0xFFFF0000u) | (c0 - e)) : ((od << 16) | (c0 - e));
+            stage(has && key > thr && li0 + e < vlim, key);
+          });
+        });
+      } else {
+        static_for<4>([&](auto e) {
+          const int id = seg0 + li0 + e;
+          const uint64_t key = sup_key(__uint_as_float(gw[(int)e]), (uint32_t)id);
+          stage(has && key > thr && li0 + e < vlim, key);
+        });
+      }
+      head += take;
+      head = head >= kRing ? head - kRing : head;
+      ngrp -= take;
+    }
+    const bool done = loads_done && ngrp == 0;
+    // 4. sort staged keys into the working list: full stages, everything at the end
+    int off = 0;
+    while (nst - off >= QN || (done && nst > off)) {
+      const int cnt = min(QN, nst - off);
+      wave_sync();
+      K add[QL];
+      static_for<QL>([&](auto s) {
+        const int p = lane * QL + s;
+        add[s] = p < cnt ? L.keys[off + p] : (K)0;
+      });
+      wave_sort_desc<QL>(add);
+      if (have) {
+        wave_merge_top<QL>(work, add);
+      } else {
+        static_for<QL>([&](auto s) { work[s] = add[s]; });
+        have = true;
+      }
       off += cnt;
-      const uint64_t t = shfl64(top[PL - 1], kWave - 1);
+      const K t = shflk(work[(N - 1) % QL], (N - 1) / QL);
       if (t) {
         thr = t;
-        thr_f = sup_key_val(t);
+        if constexpr (BF) thr_f = value_of(t >> 16);
+        else thr_f = sup_key_val(t);
       }
     }
-    if (last) break;
-    // the rest (fewer than N keys, at positions >= N) moves to the front
-    const int rem = nst - off;
-    wave_sync();
-    for (int i = lane; i < rem; i += kWave) stage[i] = stage[off + i];
-    nst = rem;
+    if (done) break;
+    if (off > 0) {  // the rest (fewer than QN keys) moves to the front
+      const int rem = nst - off;
+      wave_sync();
+      for (int i = lane; i < rem; i += kWave) L.keys[i] = L.keys[off + i];
+      nst = rem;
+    }
   }
-  // the segment's list, positions >= trunc cleared
-  const int64_t sg = ((int64_t)b * c.FP + j) * a.G + g;
-  static_for<PL>([&](auto s) {
-    const int p = lane * PL + s;
-    a.seg_keys[sg * N + p] = p < c.TC ? top[s] : 0ull;
-  });
-  if (lane == 0) a.seg_bad[sg] = any_bad ? 1 : 0;
+  // the first N positions, as row keys, in the output layout
+  auto row_key = [&](K k) -> uint64_t {
+    if constexpr (BF) {
+      if (!k) return 0ull;
+      return sup_key(value_of(k >> 16), (uint32_t)(seg0 + (int)(0xFFFFu - (k & 0xFFFFu))));
+    } else {
+      return k;
+    }
+  };
+  if constexpr (QL == PL && !BF) {
+    static_for<PL>([&](auto s) { cur[s] = work[s]; });
+  } else {
+    static_assert(sizeof(L.keys) >= N * sizeof(uint64_t), "stage too small for the output");
+    uint64_t* ost = (uint64_t*)L.keys;
+    wave_sync();
+    static_for<QL>([&](auto s) {
+      const int p = lane * QL + s;
+      if (p < N) ost[p] = row_key(work[s]);
+    });
+    wave_sync();
+    static_for<PL>([&](auto s) { cur[s] = ost[lane * PL + s]; });
+    wave_sync();
+  }
 }
 
 // Expansion of one parent by wave 0 (RheoSampling key design 2), BS support ranks
@@ -363,12 +491,16 @@ __device__ void expand_row(const BArgs& a, int b, int node, int n_sup, const uin
   }
 }
 
-// One wave per parent: merge its segments' sorted lists (the row's top trunc is in
-// the union of the segments' top trunc), then expand the parent.
-template <int PL>
-__global__ __launch_bounds__(kWave) void k_merge_expand(const BArgs a) {
+// One block per expanded parent: the waves select the top N of the row's segments
+// (a wave takes segments wave, wave + 8, ...), their lists are merged pairwise through
+// LDS (the row's top trunc is in the union of the segments' top trunc), and wave 0
+// expands the parent.
+template <int DT, int PL>
+__global__ __launch_bounds__(sel_waves<PL>() * kWave)
+__attribute__((amdgpu_waves_per_eu(PL == 2 ? 4 : 2, 8))) void k_select_expand(const BArgs a) {
   const Cfg& c = a.c;
   const int j = blockIdx.x, b = blockIdx.y;
+  const int wave = threadIdx.x >> 6;
   const int lane = lane_id();
   constexpr int N = PL * kWave;
   const int64_t ncb = (int64_t)b * c.NC;
@@ -376,7 +508,7 @@ __global__ __launch_bounds__(kWave) void k_merge_expand(const BArgs a) {
   const int ridx = row_base(c, a.layer) + j;
   const int64_t ktb = (int64_t)b * c.NR + ridx;
 
-  if (a.layer == 0) {
+  if (a.layer == 0 && wave == 0) {
     // a new step: forget every candidate of the previous one, reset SMART's state
     for (int t = c.K + lane; t < c.NC; t += kWave) a.t.cand_kind[ncb + t] = 0;
     if (lane == 0) {
@@ -387,41 +519,61 @@ __global__ __launch_bounds__(kWave) void k_merge_expand(const BArgs a) {
   }
   const int node = row_node(a, b, j);
   if (node == -2) {
-    for (int s = lane; s < c.K; s += kWave) a.t.cand_kind[ncb + cbase + s] = 0;
-    if (lane == 0) a.t.row_tail_n[ktb] = 0;
+    if (wave == 0) {
+      for (int s = lane; s < c.K; s += kWave) a.t.cand_kind[ncb + cbase + s] = 0;
+      if (lane == 0) a.t.row_tail_n[ktb] = 0;
+    }
     return;
   }
 
-  __shared__ uint64_t s_buf[N];
+  constexpr int SW = sel_waves<PL>();
+  __shared__ __align__(16) SegLds<DT, PL> s_seg[SW];
+  __shared__ uint64_t s_list[SW / 2][N];
   __shared__ float s_q[N];
-  const int64_t sg0 = ((int64_t)b * c.FP + j) * a.G;
-  auto load_list = [&](int g, uint64_t (&l)[PL]) {
-    const uint64_t* src = a.seg_keys + (sg0 + g) * N + lane * PL;
-    static_for<PL>([&](auto s) { l[s] = src[s]; });
-  };
-  uint64_t top[PL], nxt[PL];
-  load_list(0, top);
-  if (a.G > 1) load_list(1, nxt);
-  for (int g = 1; g < a.G; ++g) {
+  __shared__ int s_bad[SW];
+  constexpr int esz = DT == VRT_BF16 ? 2 : 4;
+  const char* row = (const char*)a.logits + ((int64_t)b * a.tstride + (int64_t)j * a.ld) * esz;
+  const int G = (c.V + seg_elems<DT>() - 1) / seg_elems<DT>();
+
+  uint64_t acc[PL];
+  static_for<PL>([&](auto s) { acc[s] = 0ull; });
+  bool bad = false;
+  for (int g = wave; g < G; g += SW) {
     uint64_t cur[PL];
-    static_for<PL>([&](auto s) { cur[s] = nxt[s]; });
-    if (g + 1 < a.G) load_list(g + 1, nxt);
-    wave_merge_top<PL>(top, cur);
+    seg_select<DT, PL>(row, g, c.V, s_seg[wave], cur, bad);
+    if (g == wave) static_for<PL>([&](auto s) { acc[s] = cur[s]; });
+    else wave_merge_top<PL>(acc, cur);
   }
-  int bad = 0;
-  for (int g = lane; g < a.G; g += kWave) bad |= a.seg_bad[sg0 + g];
+  if (lane == 0) s_bad[wave] = bad ? 1 : 0;
+  // pairwise merges: at distance st, wave w + st hands its list to wave w
+  for (int st = 1; st < SW; st <<= 1) {
+    if ((wave & (2 * st - 1)) == st)
+      static_for<PL>([&](auto s) { s_list[wave / (2 * st)][lane * PL + s] = acc[s]; });
+    __syncthreads();
+    if ((wave & (2 * st - 1)) == 0) {
+      uint64_t oth[PL];
+      static_for<PL>([&](auto s) { oth[s] = s_list[wave / (2 * st)][lane * PL + s]; });
+      wave_merge_top<PL>(acc, oth);
+    }
+    __syncthreads();
+  }
+  if (wave != 0) return;
+
   // support: the non-empty keys among the first trunc positions
+  uint64_t* s_buf = s_list[0];
   int cnt = 0;
   static_for<PL>([&](auto s) {
     const int p = lane * PL + s;
-    const uint64_t k = p < c.TC ? top[s] : 0ull;
+    const uint64_t k = p < c.TC ? acc[s] : 0ull;
     s_buf[p] = k;
     cnt += k != 0ull;
   });
   const int n_sup = wave_sum_i(cnt);
+  int any_bad = 0;
+  for (int w = 0; w < SW; ++w) any_bad |= s_bad[w];
   wave_sync();
 
-  uint32_t st = ballot(bad != 0) ? VRT_ST_DRAFT_NONFINITE : 0u;
+  uint32_t st = any_bad ? VRT_ST_DRAFT_NONFINITE : 0u;
   const float M = n_sup > 0 ? sup_key_val(s_buf[0]) : -INFINITY;
   if (n_sup == 0 || M == -INFINITY) st |= VRT_ST_DRAFT_EMPTY;
   if (st) {
@@ -606,59 +758,32 @@ __global__ __launch_bounds__(kFT) void k_finish(const Cfg c, const TreePtrs t) {
   }
 }
 
-template <int DT>
-int segments(int V) {
-  return (V + seg_elems<DT>() - 1) / seg_elems<DT>();
-}
-
 int list_len(const Cfg& c) { return max(128, next_pow2(c.trunc)); }
 
 template <int DT>
 hipError_t launch_layer(const BArgs& a, int rows, hipStream_t stream) {
-  const Cfg& c = a.c;
-  const dim3 g1((a.G + kSegWaves - 1) / kSegWaves, rows, c.B);
-  const dim3 g2(rows, c.B);
-  const dim3 t1(kSegWaves * kWave), t2(kWave);
-  switch (list_len(c) / kWave) {
-    case 2:
-      hipLaunchKernelGGL((k_seg_topk<DT, 2>), g1, t1, 0, stream, a);
-      hipLaunchKernelGGL(k_merge_expand<2>, g2, t2, 0, stream, a);
-      break;
-    case 4:
-      hipLaunchKernelGGL((k_seg_topk<DT, 4>), g1, t1, 0, stream, a);
-      hipLaunchKernelGGL(k_merge_expand<4>, g2, t2, 0, stream, a);
-      break;
-    case 8:
-      hipLaunchKernelGGL((k_seg_topk<DT, 8>), g1, t1, 0, stream, a);
-      hipLaunchKernelGGL(k_merge_expand<8>, g2, t2, 0, stream, a);
-      break;
-    default:
-      hipLaunchKernelGGL((k_seg_topk<DT, 16>), g1, t1, 0, stream, a);
-      hipLaunchKernelGGL(k_merge_expand<16>, g2, t2, 0, stream, a);
-      break;
+  const dim3 grid(rows, a.c.B);
+  switch (list_len(a.c) / kWave) {
+    case 2: hipLaunchKernelGGL((k_select_expand<DT, 2>), grid, dim3(sel_waves<2>() * kWave), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((k_select_expand<DT, 4>), grid, dim3(sel_waves<4>() * kWave), 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((k_select_expand<DT, 8>), grid, dim3(sel_waves<8>() * kWave), 0, stream, a); break;
+    default: hipLaunchKernelGGL((k_select_expand<DT, 16>), grid, dim3(sel_waves<16>() * kWave), 0, stream, a); break;
   }
   return hipGetLastError();
-}
-
-int segments_of(const Cfg& c) {
-  return c.dtype == VRT_BF16 ? segments<VRT_BF16>(c.V) : segments<VRT_F32>(c.V);
 }
 
 }  // namespace
 
 size_t build_ws_bytes(const Cfg& c) {
-  const size_t lists = (size_t)c.B * c.FP * segments_of(c);
-  return lists * list_len(c) * sizeof(uint64_t) + ((lists * sizeof(int) + 255) & ~(size_t)255);
+  (void)c;
+  return 0;
 }
 
 hipError_t launch_build_layer(const Cfg& c, const TreePtrs& t, int layer, const void* logits,
                               int64_t ld, int64_t tstride, uint64_t seed, uint32_t step,
                               uint32_t* stats, void* ws, hipStream_t stream) {
-  const int G = segments_of(c);
-  const size_t lists = (size_t)c.B * c.FP * G;
-  uint64_t* seg_keys = (uint64_t*)ws;
-  int* seg_bad = (int*)((char*)ws + lists * list_len(c) * sizeof(uint64_t));
-  BArgs a{c, t, layer, logits, ld, tstride, seed, step, stats, G, seg_keys, seg_bad};
+  (void)ws;
+  BArgs a{c, t, layer, logits, ld, tstride, seed, step, stats};
   const int rows = layer == 0 ? 1 : c.FP;
   hipError_t e = c.dtype == VRT_BF16 ? launch_layer<VRT_BF16>(a, rows, stream)
                                      : launch_layer<VRT_F32>(a, rows, stream);

@@ -181,74 +181,105 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 // ---------------------------------------------------------------------------
-// Sorted key lists held in a wave's registers: PL keys per lane, position
-// p = lane*PL + s, N = 64*PL keys. Bitonic networks run on these with cross-lane
-// shuffles only (no LDS, no barriers).
-__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
-  const uint32_t lo = __shfl_xor((uint32_t)v, m, kWave);
-  const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, kWave);
-  return ((uint64_t)hi << 32) | lo;
-}
+// Lane exchanges: the value of lane (lane ^ LJ). Distances 1 and 2 are one DPP quad
+// permutation; 4 and 8 compose two DPP mirrors (reversal within 8 lanes, within 16)
+// with a quad reversal; 16 and 32 use gfx950's row/half swaps plus a select.
 __device__ __forceinline__ uint64_t shfl64(uint64_t v, int src) {
   const uint32_t lo = __shfl((uint32_t)v, src, kWave);
   const uint32_t hi = __shfl((uint32_t)(v >> 32), src, kWave);
   return ((uint64_t)hi << 32) | lo;
 }
+__device__ __forceinline__ uint32_t shfl32(uint32_t v, int src) { return (uint32_t)__shfl((int)v, src, kWave); }
+__device__ __forceinline__ uint64_t shflk(uint64_t v, int src) { return shfl64(v, src); }
+__device__ __forceinline__ uint32_t shflk(uint32_t v, int src) { return shfl32(v, src); }
 
-// One compare-exchange stage of a bitonic network: partner q = p ^ J; pairs inside
-// blocks with (p & SIZE) == 0 are ordered descending, the others ascending.
-template <int PL, int SIZE, int J>
-__device__ __forceinline__ void bitonic_stage(uint64_t (&k)[PL], int lane) {
+template <int LJ>
+__device__ __forceinline__ uint32_t xchg32(uint32_t v) {
+  if constexpr (LJ == 1) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);  // quad [1,0,3,2]
+  } else if constexpr (LJ == 2) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);  // quad [2,3,0,1]
+  } else if constexpr (LJ == 4) {
+    const int t = __builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, true);  // lane ^ 7
+    return (uint32_t)__builtin_amdgcn_mov_dpp(t, 0x1B, 0xF, 0xF, true);     // then ^ 3
+  } else if constexpr (LJ == 8) {
+    const int t = __builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, true);  // lane ^ 15
+    return (uint32_t)__builtin_amdgcn_mov_dpp(t, 0x141, 0xF, 0xF, true);    // then ^ 7
+  } else if constexpr (LJ == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (lane_id() & 16) ? r[0] : r[1];
+  } else {
+    static_assert(LJ == 32, "lane distance");
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (lane_id() & 32) ? r[0] : r[1];
+  }
+}
+template <int LJ>
+__device__ __forceinline__ uint32_t xchg(uint32_t v) { return xchg32<LJ>(v); }
+template <int LJ>
+__device__ __forceinline__ uint64_t xchg(uint64_t v) {
+  return ((uint64_t)xchg32<LJ>((uint32_t)(v >> 32)) << 32) | xchg32<LJ>((uint32_t)v);
+}
+
+// ---------------------------------------------------------------------------
+// Sorted key lists held in a wave's registers: PL keys per lane, position
+// p = lane*PL + s, 64*PL keys. Bitonic networks run on them with in-lane swaps and
+// lane exchanges only (no LDS, no barriers).
+//
+// One compare-exchange stage: partner q = p ^ J; pairs inside blocks with
+// (p & SIZE) == 0 are ordered descending, the others ascending.
+template <int PL, int SIZE, int J, typename K>
+__device__ __forceinline__ void bitonic_stage(K (&k)[PL], int lane) {
   if constexpr (J < PL) {
     static_for<PL>([&](auto s) {
       constexpr int t = s ^ J;
       if constexpr (s < t) {
         const bool desc = ((lane * PL + s) & SIZE) == 0;
-        const uint64_t x = k[s], y = k[t];
-        const bool sw = desc ? (x < y) : (x > y);
-        k[s] = sw ? y : x;
-        k[t] = sw ? x : y;
+        const K x = k[s], y = k[t];
+        const K hi = x > y ? x : y, lo = x > y ? y : x;
+        k[s] = desc ? hi : lo;
+        k[t] = desc ? lo : hi;
       }
     });
   } else {
     constexpr int LJ = J / PL;
     static_for<PL>([&](auto s) {
-      const uint64_t x = k[s];
-      const uint64_t y = shfl_xor64(x, LJ);
+      const K x = k[s];
+      const K y = xchg<LJ>(x);
       const bool desc = ((lane * PL + s) & SIZE) == 0;
       const bool lower = (lane & LJ) == 0;
-      const bool keep_max = lower == desc;
-      k[s] = keep_max ? (x > y ? x : y) : (x < y ? x : y);
+      const K hi = x > y ? x : y, lo = x > y ? y : x;
+      k[s] = (lower == desc) ? hi : lo;
     });
   }
 }
 
-template <int PL, int SIZE, int J>
-__device__ __forceinline__ void bitonic_stages(uint64_t (&k)[PL], int lane) {
+template <int PL, int SIZE, int J, typename K>
+__device__ __forceinline__ void bitonic_stages(K (&k)[PL], int lane) {
   bitonic_stage<PL, SIZE, J>(k, lane);
   if constexpr (J > 1) bitonic_stages<PL, SIZE, J / 2>(k, lane);
 }
 
-template <int PL, int SIZE>
-__device__ __forceinline__ void bitonic_sort_from(uint64_t (&k)[PL], int lane) {
+template <int PL, int SIZE, typename K>
+__device__ __forceinline__ void bitonic_sort_from(K (&k)[PL], int lane) {
   bitonic_stages<PL, SIZE, SIZE / 2>(k, lane);
   if constexpr (SIZE < PL * kWave) bitonic_sort_from<PL, SIZE * 2>(k, lane);
 }
 
 // Sort the wave list descending.
-template <int PL>
-__device__ __forceinline__ void wave_sort_desc(uint64_t (&k)[PL]) {
+template <int PL, typename K>
+__device__ __forceinline__ void wave_sort_desc(K (&k)[PL]) {
   bitonic_sort_from<PL, 2>(k, lane_id());
 }
 
-// top <- the N largest of top and add, both sorted descending; result sorted
-// descending. (max of top[p] and add[N-1-p] is a bitonic sequence holding the N
-// largest; one bitonic merge orders it.)
-template <int PL>
-__device__ __forceinline__ void wave_merge_top(uint64_t (&top)[PL], const uint64_t (&add)[PL]) {
+// top <- the 64*PL largest of top and add, both sorted descending; result sorted
+// descending. (max of top[p] and add[last - p] is a bitonic sequence holding the
+// largest half; one bitonic merge orders it.)
+template <int PL, typename K>
+__device__ __forceinline__ void wave_merge_top(K (&top)[PL], const K (&add)[PL]) {
   const int lane = lane_id();
   static_for<PL>([&](auto s) {
-    const uint64_t r = shfl64(add[PL - 1 - s], kWave - 1 - lane);
+    const K r = shflk(add[PL - 1 - s], kWave - 1 - lane);
     top[s] = top[s] > r ? top[s] : r;
   });
   bitonic_stages<PL, 2 * PL * kWave, PL * kWave / 2>(top, lane);
