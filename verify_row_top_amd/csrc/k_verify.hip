@@ -1,21 +1,23 @@
-// Tree verification (RheoSampling, key design 3) on gfx950, in two kernels.
+// Tree verification (RheoSampling, key design 3) on gfx950, in three kernels.
 //
 // k_vstream: one 256-thread block per (node row, tree). The four waves stream the
 //   node's target row from HBM once, in 2048-element chunks (four 16-byte loads per
 //   lane, 8 bf16 each), and write per chunk fl(max*c2) and the sum of
 //   exp2(x*c2 - fl(max*c2)), where c2 = log2(e)/T. Every element costs one
-//   conversion, a third of a max3, one fma, one native exp2 and one add; nothing
-//   else runs here, so the kernel keeps full occupancy.
-// k_vdecide: one wave per (node, tree). From its row's chunk statistics it forms
-//   p = softmax(x/T) and decides the node exactly as the walk would if it reached
-//   it: the probe-first test min(1, p/q~), recursive rejection of the other kept
-//   children under w = max(0, p - q~) on the probe's tail (p elsewhere), and, when
-//   nothing is accepted, the final residual (or bonus) sample by inverse CDF in
-//   token-id order (chunk masses locate the chunk, one 2048-element re-read finds
-//   the token). Every draw is keyed by (depth, test index), so each node's decision
-//   is a pure function of its own row. The last wave of a tree to finish (a device
-//   counter the streaming kernel resets) follows the accepted children from the
-//   root and writes the emitted tokens and statistics.
+//   conversion, a third of a max3, one fma, one native exp2 and one add. Before its
+//   share of the stream, the last wave gathers what the decision needs besides the
+//   row statistics: the node's kept children (node, token, logit) and the logits at
+//   the probe tail's tokens. Those dependent loads overlap the other waves' stream.
+// k_vdecide: one wave per (node, tree). From its row's chunk statistics and the
+//   gathered logits it forms p = softmax(x/T) where needed and decides the node
+//   exactly as the walk would if it reached it: the probe-first test min(1, p/q~),
+//   recursive rejection of the other kept children under w = max(0, p - q~) on the
+//   probe's tail (p elsewhere), and, when nothing is accepted, the final residual (or
+//   bonus) sample by inverse CDF in token-id order (adjusted chunk masses locate the
+//   chunk, one 2048-element re-read finds the token). Every draw is keyed by (depth,
+//   test index), so each node's decision is a pure function of its own row.
+// k_vwalk: one wave per tree follows the accepted children from the root and writes
+//   the emitted tokens and statistics.
 #include "vrt_dev.hpp"
 #include "vrt_internal.hpp"
 
@@ -27,6 +29,19 @@ constexpr int kCH = 2048;       // elements per chunk (one wave at a time)
 constexpr int kChildMax = 32;   // K <= 30
 constexpr int kDW = 4;          // decide: waves (nodes) per block
 constexpr float kBand = 1e-6f;  // near-tie band reported in the stats
+constexpr double kFix = 1152921504606846976.0;  // 2^60: fixed point of the mass changes
+
+// What the decision of one node needs besides its row statistics (gathered by the
+// streaming kernel): kept children in slot order and their logits.
+struct VRec {
+  int nc;     // kept children (validated)
+  int probe;  // slot of the probe child, -1 if none
+  int nt;     // probe tail entries (0 without a probe)
+  int depth;  // depth of the node (0 = root)
+  int node[kChildMax];
+  int tok[kChildMax];
+  float x[kChildMax];
+};
 
 struct VArgs {
   Cfg c;
@@ -36,8 +51,9 @@ struct VArgs {
   uint64_t seed;
   uint32_t step;
   NodeOut* node_out;
-  float2* chunk;      // [B][N][nch]: (fl(max*c2), sum exp2(x*c2 - that))
-  int* done;          // [B]: nodes of the tree decided so far
+  float2* chunk;  // [B][N][nch]: (fl(max*c2), sum exp2(x*c2 - that))
+  VRec* rec;      // [B][N]
+  float* xtail;   // [B][N][TC]: target logits at the probe tail's tokens
   int32_t* out_tokens;
   int32_t* out_nodes;
   int32_t* out_len;
@@ -128,12 +144,62 @@ __device__ __forceinline__ float2 chunk_stats(const void* row, int lo, int V, fl
 }
 
 template <int DT>
+__device__ __forceinline__ float load_one(const void* row, int v) {
+  if constexpr (DT == VRT_BF16) return __uint_as_float((uint32_t)((const uint16_t*)row)[v] << 16);
+  else return ((const float*)row)[v];
+}
+
+// The decision inputs of node i other than its row statistics (one wave).
+template <int DT>
+__device__ void gather_node(const VArgs& a, int b, int i, int nn, const char* row) {
+  const Cfg& c = a.c;
+  const int lane = lane_id();
+  const int64_t nb = (int64_t)b * c.N;
+  const int64_t cob = (int64_t)b * (c.N + 1);  // child_off rows hold N + 1 entries
+  const int co = a.t.child_off[cob + i], ce = a.t.child_off[cob + i + 1];
+  int nc = ce - co;
+  if (co < 0 || co > c.N || nc < 0) nc = 0;
+  if (nc > c.K) nc = c.K;
+  if (co + nc > c.N) nc = c.N - co > 0 ? c.N - co : 0;
+  int node = -1, tok = -1;
+  bool probe = false;
+  if (lane < nc) {
+    node = a.t.child[nb + co + lane];
+    if (node > i && node < nn) {
+      tok = a.t.node_token[nb + node];
+      probe = a.t.node_kind[nb + node] == VRT_PROBE;
+    }
+    if (tok < 0 || tok >= c.V) node = -1, tok = -1, probe = false;
+  }
+  const uint64_t pm = ballot(probe);
+  const int pl = pm ? __builtin_ctzll(pm) : -1;
+  const float x = tok >= 0 ? load_one<DT>(row, tok) : -INFINITY;
+  const int nt = pl >= 0 ? min(max(a.t.tail_n[nb + i], 0), c.TC) : 0;
+  const int64_t tb = (nb + i) * c.TC;
+  for (int e = lane; e < nt; e += kWave) {
+    const int y = a.t.tail_id[tb + e];
+    a.xtail[tb + e] = (y >= 0 && y < c.V) ? load_one<DT>(row, y) : -INFINITY;
+  }
+  VRec& r = a.rec[nb + i];
+  if (lane < kChildMax) {
+    r.node[lane] = node;
+    r.tok[lane] = tok;
+    r.x[lane] = x;
+  }
+  if (lane == 0) {
+    r.nc = nc;
+    r.probe = pl;
+    r.nt = nt;
+    r.depth = min(max(a.t.node_depth[nb + i], 0), 63);
+  }
+}
+
+template <int DT>
 __global__ __launch_bounds__(kVB) void k_vstream(const VArgs a) {
   const Cfg& c = a.c;
   const int b = blockIdx.y;
   const int i = blockIdx.x;
   const int nn = clamp_nodes(a.t.n_nodes[b], c.N);
-  if (i == 0 && threadIdx.x == 0) a.done[b] = 0;
   if (i >= nn) return;
   const int V = c.V;
   constexpr int esz = DT == VRT_BF16 ? 2 : 4;
@@ -141,18 +207,13 @@ __global__ __launch_bounds__(kVB) void k_vstream(const VArgs a) {
   const int nch = (V + kCH - 1) / kCH;
   const int nfull = V / kCH;
   const int wave = threadIdx.x >> 6;
+  if (wave == kVB / kWave - 1) gather_node<DT>(a, b, i, nn, row);
   float2* out = a.chunk + ((int64_t)b * c.N + i) * nch;
   for (int ch = wave; ch < nch; ch += kVB / kWave) {
     const float2 st = ch < nfull ? chunk_stats<DT, true>(row, ch * kCH, V, c.c2)
                                  : chunk_stats<DT, false>(row, ch * kCH, V, c.c2);
     if (lane_id() == 0) out[ch] = st;
   }
-}
-
-template <int DT>
-__device__ __forceinline__ float load_one(const void* row, int v) {
-  if constexpr (DT == VRT_BF16) return __uint_as_float((uint32_t)((const uint16_t*)row)[v] << 16);
-  else return ((const float*)row)[v];
 }
 
 // This lane's 32 contiguous elements [lo + lane*32, +32) of a chunk (id order).
@@ -189,6 +250,341 @@ __device__ __forceinline__ void load_contig(const void* row, int lo, int V, floa
     if (e0 + k >= V) x[k] = -INFINITY;
 }
 
+__device__ __forceinline__ double readlane_d(double v, int l) {
+  const long long u = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)(uint32_t)u, l);
+  const int hi = __builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+  return __longlong_as_double(((long long)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+// Per-wave LDS of the decision: chunk masses and their fixed-point changes [nch], the
+// probe tail (token, q~, p, child slot) [TC], children's q~ [32], the changes inside
+// the sampled chunk [TC + 32].
+struct DLds {
+  double* pm;
+  long long* dfix;
+  int* tid;
+  float* tq;
+  double* tp;
+  int* tslot;
+  double* qc;
+  int* itok;
+  double* idel;
+};
+
+__host__ __device__ size_t vdecide_lds_per_wave(const Cfg& c) {
+  const size_t nch = (size_t)(c.V + kCH - 1) / kCH;
+  const size_t TC = (size_t)c.TC;
+  const size_t bytes = nch * 16 + TC * (4 + 4 + 8 + 4) + kChildMax * 8 + (TC + kChildMax) * (4 + 8) + 64;
+  return (bytes + 15) & ~(size_t)15;
+}
+
+__device__ DLds carve(char* base, int nch, int TC) {
+  DLds L;
+  char* p = base;
+  auto take = [&](size_t bytes) {
+    char* r = p;
+    p += (bytes + 7) & ~(size_t)7;
+    return r;
+  };
+  L.pm = (double*)take((size_t)nch * 8);
+  L.dfix = (long long*)take((size_t)nch * 8);
+  L.tp = (double*)take((size_t)TC * 8);
+  L.qc = (double*)take(kChildMax * 8);
+  L.idel = (double*)take((size_t)(TC + kChildMax) * 8);
+  L.tid = (int*)take((size_t)TC * 4);
+  L.tq = (float*)take((size_t)TC * 4);
+  L.tslot = (int*)take((size_t)TC * 4);
+  L.itok = (int*)take((size_t)(TC + kChildMax) * 4);
+  return L;
+}
+
+template <int DT>
+__global__ __launch_bounds__(kDW * kWave) void k_vdecide(const VArgs a) {
+  const Cfg& c = a.c;
+  const int wave = threadIdx.x >> 6;
+  const int lane = lane_id();
+  const int64_t g = (int64_t)blockIdx.x * kDW + wave;
+  if (g >= (int64_t)c.B * c.N) return;
+  const int b = (int)(g / c.N);
+  const int i = (int)(g % c.N);
+  const int nn = clamp_nodes(a.t.n_nodes[b], c.N);
+  if (i >= nn) return;
+
+  const int V = c.V;
+  constexpr int esz = DT == VRT_BF16 ? 2 : 4;
+  const char* row = (const char*)a.logits + ((int64_t)b * a.tstride + (int64_t)i * a.ld) * esz;
+  const int nch = (V + kCH - 1) / kCH;
+  const float c2 = c.c2;
+  const int TC = c.TC;
+  const int64_t nb = (int64_t)b * c.N;
+  extern __shared__ double s_dyn[];
+  const DLds L = carve((char*)s_dyn + vdecide_lds_per_wave(c) * wave, nch, TC);
+
+  // ---- inputs: row statistics, children, probe tail (independent loads)
+  const VRec& R = a.rec[nb + i];
+  const int nc = R.nc, probe = R.probe, nt = R.nt;
+  const uint32_t depth = (uint32_t)R.depth;
+  int ch_node = -1, ch_tok = -1;
+  float ch_x = -INFINITY;
+  if (lane < nc) {
+    ch_node = R.node[lane];
+    ch_tok = R.tok[lane];
+    ch_x = R.x[lane];
+  }
+  const int64_t tb = (nb + i) * TC;
+  for (int e = lane; e < nt; e += kWave) {
+    int y = a.t.tail_id[tb + e];
+    if (y < 0 || y >= V) y = -1;
+    L.tid[e] = y;
+    L.tq[e] = a.t.tail_q[tb + e];
+    L.tp[e] = a.xtail[tb + e];  // the logit for now
+  }
+  const float2* cs = a.chunk + (nb + i) * nch;
+  float mcl = -INFINITY;
+  for (int ch = lane; ch < nch; ch += kWave) mcl = fmaxf(mcl, cs[ch].x);
+  const float MC = wave_max(mcl);
+  double sl = 0.0;
+  for (int ch = lane; ch < nch; ch += kWave) {
+    const float2 st = cs[ch];
+    const double pm = (double)st.y * (double)fast_exp2(st.x - MC);
+    L.pm[ch] = pm;
+    sl += pm;
+  }
+  const double S = wave_sum(sl);
+  NodeOut out{-1, -1, 0, 0.0f};
+  if (!(S > 0.0) || !(S < INFINITY) || !(MC < INFINITY)) {
+    out.flags = (int)(VRT_ST_TARGET_BAD << 16);
+    if (lane == 0) a.node_out[nb + i] = out;
+    return;
+  }
+  const double invS = 1.0 / S;
+  auto p_of_x = [&](float x) -> double { return (double)fast_exp2(__builtin_fmaf(x, c2, -MC)) * invS; };
+  const double pc = ch_tok >= 0 ? p_of_x(ch_x) : 0.0;
+
+  // ---- probe tail: p, the overlap sum min(p, q~), which kept child each token is
+  int tests = 0, near = 0;
+  int accept = -1;
+  double W = 1.0;
+  double q_child = -1.0;  // q~ of this lane's child token, -1 if not in the tail
+  if (lane < kChildMax) L.qc[lane] = -1.0;
+  wave_sync();
+  if (probe >= 0) {
+    double ov = 0.0;
+    for (int e = lane; e < nt; e += kWave) {
+      const int y = L.tid[e];
+      const double p = y >= 0 ? p_of_x((float)L.tp[e]) : 0.0;
+      const double q = (double)L.tq[e];
+      L.tp[e] = p;
+      ov += fmin(p, q);
+      int slot = -1;
+      for (int k = 0; k < nc; ++k)
+        if (slot < 0 && y >= 0 && __builtin_amdgcn_readlane(ch_tok, k) == y) slot = k;
+      L.tslot[e] = slot;
+      if (slot >= 0) L.qc[slot] = q;
+    }
+    const double overlap = wave_sum(ov);
+    wave_sync();
+    if (lane < nc) q_child = L.qc[lane];
+    const double qp = readlane_d(q_child, probe);
+    const double qs = qp < 0.0 ? 0.0 : qp;  // a probe outside its tail has q~ = 0
+    const double ps = readlane_d(pc, probe);
+    const double ratio = ps / qs;
+    const float u0 = uniform24(a.seed, 32u * depth, (uint32_t)b, a.step, kPurposeTest);
+    ++tests;
+    if (fabs((double)u0 - ratio) < kBand) ++near;
+    if ((double)u0 < ratio) accept = __builtin_amdgcn_readlane(ch_node, probe);
+    W = 1.0 - overlap;
+  }
+
+  // ---- recursive rejection of the other kept children in slot order; every lane
+  // draws its child's uniform up front
+  const bool in_tail = q_child >= 0.0;
+  const double wc = in_tail ? (pc > q_child ? pc - q_child : 0.0) : pc;
+  const bool cand = lane < nc && lane != probe && ch_node >= 0;
+  const uint64_t cmask = ballot(cand);
+  const uint32_t j = 1u + (uint32_t)__builtin_popcountll(cmask & ((1ull << lane) - 1ull));
+  const float uc = cand ? uniform24(a.seed, 32u * depth + j, (uint32_t)b, a.step, kPurposeTest) : 1.0f;
+  uint64_t rejected = 0;
+  if (accept < 0) {
+    for (uint64_t m = cmask; m; m &= m - 1ull) {
+      const int k = __builtin_ctzll(m);
+      const double wk = readlane_d(wc, k);
+      const float u = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(uc), k));
+      ++tests;
+      const double ratio = wk / W;
+      if (fabs((double)u - ratio) < kBand) ++near;
+      if ((double)u < ratio) {
+        accept = __builtin_amdgcn_readlane(ch_node, k);
+        break;
+      }
+      W -= wk;
+      rejected |= 1ull << k;
+    }
+  }
+
+  // ---- nothing accepted: inverse-CDF sample of w / W in token-id order
+  if (accept < 0) {
+    for (int ch = lane; ch < nch; ch += kWave) L.dfix[ch] = 0;
+    wave_sync();
+    // changes of mass relative to p: the probe's tail (clipped residual, or zero for a
+    // rejected child) and the rejected children outside it (zero). Fixed-point
+    // atomics keep the per-chunk sums independent of the order of arrival.
+    if (probe >= 0) {
+      for (int e = lane; e < nt; e += kWave) {
+        const int y = L.tid[e];
+        if (y < 0) continue;
+        const double p = L.tp[e], q = (double)L.tq[e];
+        const int slot = L.tslot[e];
+        const bool rej = slot >= 0 && ((rejected >> slot) & 1ull);
+        const double d = rej ? -p : -(p < q ? p : q);
+        atomicAdd((unsigned long long*)&L.dfix[y / kCH], (unsigned long long)__double2ll_rn(d * kFix));
+      }
+    }
+    const bool mine = ((rejected >> lane) & 1ull) && !in_tail;
+    if (mine) atomicAdd((unsigned long long*)&L.dfix[ch_tok / kCH], (unsigned long long)__double2ll_rn(-pc * kFix));
+    wave_sync();
+    // adjusted chunk masses, lane-blocked contiguous chunks
+    const int cpl = (nch + kWave - 1) / kWave;
+    const int c0 = lane * cpl, c1 = min(c0 + cpl, nch);
+    double lmass = 0.0;
+    for (int ch = c0; ch < c1; ++ch) {
+      double mch = L.pm[ch] * invS + (double)L.dfix[ch] * (1.0 / kFix);
+      if (mch < 0.0) mch = 0.0;
+      L.pm[ch] = mch;
+      lmass += mch;
+    }
+    const float uf = uniform24(a.seed, depth, (uint32_t)b, a.step, kPurposeFinal);
+    const double tgt = (double)uf * W;
+    const double incl = wave_incl_scan(lmass);
+    const double excl = incl - lmass;
+    // lane holding the crossing chunk; if rounding leaves none, the last lane with mass
+    const uint64_t hit = ballot(tgt < incl && lmass > 0.0);
+    int src = hit ? __builtin_ctzll(hit) : -1;
+    bool clamp = false;
+    if (src < 0) {
+      const uint64_t pos = ballot(lmass > 0.0);
+      src = pos ? 63 - __builtin_clzll(pos) : 0;
+      clamp = true;
+    }
+    int cstar = -1;
+    double before = 0.0;
+    if (lane == src) {
+      double cum = excl;
+      for (int ch = c0; ch < c1; ++ch) {
+        if (L.pm[ch] > 0.0) {
+          cstar = ch;
+          before = cum;
+          if (!clamp && tgt < cum + L.pm[ch]) break;
+        }
+        cum += L.pm[ch];
+      }
+      if (cstar < 0) cstar = c0 < nch ? c0 : nch - 1;
+    }
+    cstar = __shfl(cstar, src, kWave);
+    before = __shfl(before, src, kWave);
+    const int lo = cstar * kCH;
+    // the changes that fall inside the chunk, listed for the owners of their tokens
+    int nitem = 0;
+    wave_sync();
+    if (probe >= 0) {
+      for (int e0 = 0; e0 < nt; e0 += kWave) {
+        const int e = e0 + lane;
+        bool inside = false;
+        int y = -1;
+        double d = 0.0;
+        if (e < nt) {
+          y = L.tid[e];
+          inside = y >= lo && y < lo + kCH;
+          if (inside) {
+            const double p = L.tp[e], q = (double)L.tq[e];
+            const int slot = L.tslot[e];
+            const bool rej = slot >= 0 && ((rejected >> slot) & 1ull);
+            d = rej ? -p : -(p < q ? p : q);
+          }
+        }
+        const uint64_t m = ballot(inside);
+        if (inside) {
+          const int at = nitem + (int)__builtin_popcountll(m & ((1ull << lane) - 1ull));
+          L.itok[at] = y;
+          L.idel[at] = d;
+        }
+        nitem += (int)__builtin_popcountll(m);
+      }
+    }
+    {
+      const bool inside = mine && ch_tok >= lo && ch_tok < lo + kCH;
+      const uint64_t m = ballot(inside);
+      if (inside) {
+        const int at = nitem + (int)__builtin_popcountll(m & ((1ull << lane) - 1ull));
+        L.itok[at] = ch_tok;
+        L.idel[at] = -pc;
+      }
+      nitem += (int)__builtin_popcountll(m);
+    }
+    // re-read the chunk; lane l owns tokens [lo + 32 l, lo + 32 l + 32)
+    float x[32];
+    load_contig<DT>(row, lo, V, x);
+    float wv[32];
+    const float invSf = (float)invS;
+#pragma unroll
+    for (int k = 0; k < 32; ++k)
+      wv[k] = (x[k] > -INFINITY) ? fast_exp2(__builtin_fmaf(x[k], c2, -MC)) * invSf : 0.0f;
+    const int my0 = lo + lane * 32;
+    wave_sync();
+    for (int it = 0; it < nitem; ++it) {
+      const int y = L.itok[it];
+      if (y >= my0 && y < my0 + 32) {
+        const double dd = L.idel[it];
+        const int off = y - my0;
+#pragma unroll
+        for (int k = 0; k < 32; ++k)
+          if (k == off) {
+            const double v = (double)wv[k] + dd;
+            wv[k] = v > 0.0 ? (float)v : 0.0f;
+          }
+      }
+    }
+    double lsum = 0.0;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) lsum += (double)wv[k];
+    const double lincl = wave_incl_scan(lsum) + before;
+    const double lexcl = lincl - lsum;
+    const uint64_t hit2 = ballot(tgt < lincl && lsum > 0.0);
+    int src2 = (hit2 && !clamp) ? __builtin_ctzll(hit2) : -1;
+    bool clamp2 = clamp;
+    if (src2 < 0) {
+      const uint64_t pos = ballot(lsum > 0.0);
+      src2 = pos ? 63 - __builtin_clzll(pos) : 0;
+      clamp2 = true;
+    }
+    if (lane == src2) {
+      double cum = lexcl;
+      int tok = -1;
+      double b0 = cum, b1 = cum;
+      for (int k = 0; k < 32; ++k) {
+        if (wv[k] > 0.0f) {
+          tok = my0 + k;
+          b0 = cum;
+          b1 = cum + (double)wv[k];
+          if (!clamp2 && tgt < b1) break;
+        }
+        cum += (double)wv[k];
+      }
+      if (tok < 0) tok = min(my0, V - 1);
+      out.token = tok;
+      if (W > 0.0 && (fabs((double)uf - b0 / W) < kBand || fabs((double)uf - b1 / W) < kBand))
+        ++near;
+    }
+    out.token = __shfl(out.token, src2, kWave);
+    near = __shfl(near, src2, kWave);
+  }
+  out.accept = accept;
+  out.flags = min(tests, 255) | (min(near, 255) << 8);
+  if (accept < 0) out.W = (float)W;
+  if (lane == 0) a.node_out[nb + i] = out;
+}
+
 // The walk of tree b (one lane): follow accepted children from the root.
 __device__ void walk_tree(const VArgs& a, int b, int nn) {
   const Cfg& c = a.c;
@@ -196,7 +592,7 @@ __device__ void walk_tree(const VArgs& a, int b, int nn) {
   const int64_t nb = (int64_t)b * c.N;
   uint32_t st = 0;
   for (int i = lane; i < nn; i += kWave) st |= (uint32_t)a.node_out[nb + i].flags >> 16;
-  for (int o = 1; o < kWave; o <<= 1) st |= __shfl_xor(st, o, kWave);
+  st = wave_reduce(st, [](uint32_t x, uint32_t y) { return x | y; });
   if (lane != 0) return;
   int cur = 0, len = 0, near = 0, probe = 0, visited = 0;
   for (int step = 0; step <= c.D; ++step) {
@@ -229,307 +625,32 @@ __device__ void walk_tree(const VArgs& a, int b, int nn) {
   }
 }
 
-template <int DT>
-__global__ __launch_bounds__(kDW * kWave) void k_vdecide(const VArgs a) {
-  const Cfg& c = a.c;
-  const int wave = threadIdx.x >> 6;
-  const int lane = lane_id();
-  const int64_t g = (int64_t)blockIdx.x * kDW + wave;
-  if (g >= (int64_t)c.B * c.N) return;
-  const int b = (int)(g / c.N);
-  const int i = (int)(g % c.N);
-  const int nn = clamp_nodes(a.t.n_nodes[b], c.N);
-  if (i >= nn) return;
-
-  const int V = c.V;
-  constexpr int esz = DT == VRT_BF16 ? 2 : 4;
-  const char* row = (const char*)a.logits + ((int64_t)b * a.tstride + (int64_t)i * a.ld) * esz;
-  const int nch = (V + kCH - 1) / kCH;
-  const float c2 = c.c2;
-  const int TC = c.TC;
-
-  // per-wave LDS (sized by vdecide_lds_per_wave)
-  extern __shared__ double s_dyn[];
-  const size_t per_wave = (size_t)(nch + TC + kChildMax) + (size_t)(2 * TC + kChildMax + 1) / 2 +
-                          (size_t)(2 * TC + 1) / 2;
-  double* s_pm = s_dyn + per_wave * wave;  // [nch] per chunk mass, then residual mass
-  double* s_adj_w = s_pm + nch;            // [TC + 32] change of mass at adjusted tokens
-  float* s_tq = (float*)(s_adj_w + TC + kChildMax);  // [TC] tail q~
-  float* s_tp = s_tq + TC;                 // [TC] tail p
-  int* s_tid = (int*)(s_tp + TC);          // [TC] tail tokens
-  int* s_adj_tok = s_tid + TC;             // [TC + 32] adjusted tokens
-
-  // ---- row statistics: MC = max mc, S = sum_ch s_ch 2^(mc_ch - MC)
-  const float2* cs = a.chunk + ((int64_t)b * c.N + i) * nch;
-  float mcl = -INFINITY;
-  for (int ch = lane; ch < nch; ch += kWave) mcl = fmaxf(mcl, cs[ch].x);
-  const float MC = wave_max(mcl);
-  double sl = 0.0;
-  for (int ch = lane; ch < nch; ch += kWave) {
-    const float2 st = cs[ch];
-    const double pm = (double)st.y * (double)fast_exp2(st.x - MC);
-    s_pm[ch] = pm;
-    sl += pm;
-  }
-  const double S = wave_sum(sl);
-  NodeOut out{-1, -1, 0, 0.0f};
-  const int64_t nb = (int64_t)b * c.N;
-  bool decide = true;
-  if (!(S > 0.0) || !(S < INFINITY) || !(MC < INFINITY)) {
-    out.flags = (int)(VRT_ST_TARGET_BAD << 16);
-    decide = false;
-  }
-  if (decide) {
-    const double invS = 1.0 / S;
-    auto p_of = [&](int tok) -> double {
-      const float x = load_one<DT>(row, tok);
-      return (double)fast_exp2(__builtin_fmaf(x, c2, -MC)) * invS;
-    };
-
-    // ---- the node's kept children, in slot order
-    const int64_t cob = (int64_t)b * (c.N + 1);  // child_off rows hold N + 1 entries
-    const int co = a.t.child_off[cob + i], ce = a.t.child_off[cob + i + 1];
-    int nc = ce - co;
-    if (co < 0 || co > c.N || nc < 0) nc = 0;
-    if (nc > c.K) nc = c.K;
-    if (co + nc > c.N) nc = c.N - co > 0 ? c.N - co : 0;
-    int ch_node = -1, ch_tok = -1;
-    bool ch_probe = false;
-    if (lane < nc) {
-      ch_node = a.t.child[nb + co + lane];
-      if (ch_node > i && ch_node < nn) {
-        ch_tok = a.t.node_token[nb + ch_node];
-        ch_probe = a.t.node_kind[nb + ch_node] == VRT_PROBE;
-      }
-      if (ch_tok < 0 || ch_tok >= V) ch_node = -1, ch_tok = -1, ch_probe = false;
-    }
-    const uint64_t probe_mask = ballot(ch_probe);
-    const int probe_lane = probe_mask ? __builtin_ctzll(probe_mask) : -1;
-    const double pc = (ch_tok >= 0) ? p_of(ch_tok) : 0.0;
-
-    const uint32_t depth = (uint32_t)min(max(a.t.node_depth[nb + i], 0), 63);
-    int tests = 0, near = 0;
-    int accept = -1;
-    double W = 1.0;
-    int nt = 0;
-    double q_child = 0.0;  // q~ of this lane's child token (0 if not in the tail)
-    bool child_in_tail = false;
-    if (probe_lane >= 0) {
-      nt = min(max(a.t.tail_n[nb + i], 0), TC);
-      const int64_t tb = (nb + i) * TC;
-      double ov = 0.0;
-      for (int e = lane; e < nt; e += kWave) {
-        int y = a.t.tail_id[tb + e];
-        const float q = a.t.tail_q[tb + e];
-        if (y < 0 || y >= V) y = -1;
-        const double p = (y >= 0) ? p_of(y) : 0.0;
-        s_tid[e] = y;
-        s_tq[e] = q;
-        s_tp[e] = (float)p;
-        ov += fmin(p, (double)q);
-      }
-      const double overlap = wave_sum(ov);
-      wave_sync();
-      if (ch_tok >= 0)
-        for (int e = 0; e < nt; ++e)
-          if (s_tid[e] == ch_tok) {
-            q_child = (double)s_tq[e];
-            child_in_tail = true;
-            break;
-          }
-      const double qs = __shfl(q_child, probe_lane, kWave);
-      const double ps = __shfl(pc, probe_lane, kWave);
-      const double ratio = ps / qs;
-      const float u0 = uniform24(a.seed, 32u * depth, (uint32_t)b, a.step, kPurposeTest);
-      ++tests;
-      if (fabs((double)u0 - ratio) < kBand) ++near;
-      if ((double)u0 < ratio) accept = __shfl(ch_node, probe_lane, kWave);
-      W = 1.0 - overlap;
-    }
-
-    // residual weight of this lane's child once the probe is rejected
-    double wc = pc;
-    if (child_in_tail) wc = pc > q_child ? pc - q_child : 0.0;
-    uint64_t rejected = 0;
-    if (accept < 0) {
-      uint32_t j = 1;
-      for (int k = 0; k < nc; ++k) {
-        if (k == probe_lane) continue;
-        const int node_k = __shfl(ch_node, k, kWave);
-        const double wk = __shfl(wc, k, kWave);
-        if (node_k < 0) continue;
-        const float u = uniform24(a.seed, 32u * depth + j, (uint32_t)b, a.step, kPurposeTest);
-        ++j;
-        ++tests;
-        const double ratio = wk / W;
-        if (fabs((double)u - ratio) < kBand) ++near;
-        if ((double)u < ratio) {
-          accept = node_k;
-          break;
-        }
-        W -= wk;
-        rejected |= 1ull << k;
-      }
-    }
-
-    // ---- nothing accepted: inverse-CDF sample of w / W in token-id order
-    if (accept < 0) {
-      wave_sync();
-      // tokens whose weight differs from p: the probe's tail (clipped residual) and
-      // the rejected children (weight 0)
-      int nadj = 0;
-      if (probe_lane >= 0) {
-        for (int e = lane; e < nt; e += kWave) {
-          const int y = s_tid[e];
-          const double p = (double)s_tp[e], q = (double)s_tq[e];
-          bool rej = false;
-          for (int k = 0; k < nc; ++k)
-            if (((rejected >> k) & 1ull) && __shfl(ch_tok, k, kWave) == y) rej = true;
-          s_adj_tok[e] = y;
-          s_adj_w[e] = rej ? -p : -(p < q ? p : q);  // change of mass at y
-        }
-        nadj = nt;
-      }
-      {
-        const bool mine = ((rejected >> lane) & 1ull) && lane < nc && !child_in_tail;
-        const uint64_t mm = ballot(mine);
-        if (mine) {
-          const int slot = nadj + __builtin_popcountll(mm & ((1ull << lane) - 1ull));
-          s_adj_tok[slot] = ch_tok;
-          s_adj_w[slot] = -pc;
-        }
-        nadj += __builtin_popcountll(mm);
-      }
-      wave_sync();
-      // chunk masses with the adjustments, lane-blocked contiguous chunks
-      const int cpl = (nch + kWave - 1) / kWave;
-      const int c0 = lane * cpl, c1 = min(c0 + cpl, nch);
-      double lmass = 0.0;
-      for (int ch = c0; ch < c1; ++ch) {
-        double mch = s_pm[ch] * invS;
-        for (int e = 0; e < nadj; ++e) {
-          const int y = s_adj_tok[e];
-          if (y >= ch * kCH && y < (ch + 1) * kCH) mch += s_adj_w[e];
-        }
-        if (mch < 0.0) mch = 0.0;
-        s_pm[ch] = mch;
-        lmass += mch;
-      }
-      const float uf = uniform24(a.seed, depth, (uint32_t)b, a.step, kPurposeFinal);
-      const double tgt = (double)uf * W;
-      const double incl = wave_incl_scan(lmass);
-      const double excl = incl - lmass;
-      // lane holding the crossing chunk; if rounding leaves none, the last lane with mass
-      const uint64_t hit = ballot(tgt < incl && lmass > 0.0);
-      int src = hit ? __builtin_ctzll(hit) : -1;
-      bool clamp = false;
-      if (src < 0) {
-        const uint64_t pos = ballot(lmass > 0.0);
-        src = pos ? 63 - __builtin_clzll(pos) : 0;
-        clamp = true;
-      }
-      int cstar = -1;
-      double before = 0.0;
-      if (lane == src) {
-        double cum = excl;
-        for (int ch = c0; ch < c1; ++ch) {
-          if (s_pm[ch] > 0.0) {
-            cstar = ch;
-            before = cum;
-            if (!clamp && tgt < cum + s_pm[ch]) break;
-          }
-          cum += s_pm[ch];
-        }
-        if (cstar < 0) cstar = c0 < nch ? c0 : nch - 1;
-      }
-      cstar = __shfl(cstar, src, kWave);
-      before = __shfl(before, src, kWave);
-      // re-read the chunk; lane l owns tokens [lo + 32 l, lo + 32 l + 32)
-      const int lo = cstar * kCH;
-      float x[32];
-      load_contig<DT>(row, lo, V, x);
-      float wv[32];
-      const float invSf = (float)invS;
-#pragma unroll
-      for (int k = 0; k < 32; ++k)
-        wv[k] = (x[k] > -INFINITY) ? fast_exp2(__builtin_fmaf(x[k], c2, -MC)) * invSf : 0.0f;
-      const int my0 = lo + lane * 32;
-      for (int e = 0; e < nadj; ++e) {
-        const int y = s_adj_tok[e];
-        if (y >= my0 && y < my0 + 32) {
-          const double v = (double)wv[y - my0] + s_adj_w[e];
-          wv[y - my0] = v > 0.0 ? (float)v : 0.0f;
-        }
-      }
-      double lsum = 0.0;
-#pragma unroll
-      for (int k = 0; k < 32; ++k) lsum += (double)wv[k];
-      const double lincl = wave_incl_scan(lsum) + before;
-      const double lexcl = lincl - lsum;
-      const uint64_t hit2 = ballot(tgt < lincl && lsum > 0.0);
-      int src2 = (hit2 && !clamp) ? __builtin_ctzll(hit2) : -1;
-      bool clamp2 = clamp;
-      if (src2 < 0) {
-        const uint64_t pos = ballot(lsum > 0.0);
-        src2 = pos ? 63 - __builtin_clzll(pos) : 0;
-        clamp2 = true;
-      }
-      if (lane == src2) {
-        double cum = lexcl;
-        int tok = -1;
-        double b0 = cum, b1 = cum;
-        for (int k = 0; k < 32; ++k) {
-          if (wv[k] > 0.0f) {
-            tok = my0 + k;
-            b0 = cum;
-            b1 = cum + (double)wv[k];
-            if (!clamp2 && tgt < b1) break;
-          }
-          cum += (double)wv[k];
-        }
-        if (tok < 0) tok = min(my0, V - 1);
-        out.token = tok;
-        if (W > 0.0 && (fabs((double)uf - b0 / W) < kBand || fabs((double)uf - b1 / W) < kBand))
-          ++near;
-      }
-      out.token = __shfl(out.token, src2, kWave);
-      near = __shfl(near, src2, kWave);
-    }
-    out.accept = accept;
-    out.flags = min(tests, 255) | (min(near, 255) << 8);
-    if (accept < 0) out.W = (float)W;
-  }
-  if (lane == 0) a.node_out[nb + i] = out;
-}
-
 // One wave per tree: the walk over the decided nodes.
 __global__ __launch_bounds__(kWave) void k_vwalk(const VArgs a) {
   const int b = blockIdx.x;
   walk_tree(a, b, clamp_nodes(a.t.n_nodes[b], a.c.N));
 }
 
-size_t vdecide_lds_per_wave(const Cfg& c) {
-  const int nch = (c.V + kCH - 1) / kCH;
-  const size_t doubles = (size_t)(nch + c.TC + kChildMax) + (size_t)(2 * c.TC + kChildMax + 1) / 2 +
-                         (size_t)(2 * c.TC + 1) / 2;
-  return doubles * 8;
+size_t chunk_bytes(const Cfg& c) {
+  const size_t nch = (size_t)(c.V + kCH - 1) / kCH;
+  return ((size_t)c.B * c.N * nch * sizeof(float2) + 255) & ~(size_t)255;
 }
+size_t rec_bytes(const Cfg& c) { return ((size_t)c.B * c.N * sizeof(VRec) + 255) & ~(size_t)255; }
 
 }  // namespace
 
 size_t verify_ws_bytes(const Cfg& c) {
-  const int nch = (c.V + kCH - 1) / kCH;
-  return (size_t)c.B * c.N * nch * sizeof(float2) + (size_t)c.B * sizeof(int);
+  return chunk_bytes(c) + rec_bytes(c) + (size_t)c.B * c.N * c.TC * sizeof(float);
 }
 
 hipError_t launch_verify(const Cfg& c, const TreePtrs& t, const void* logits, int64_t ld,
                          int64_t tstride, uint64_t seed, uint32_t step, NodeOut* node_out,
                          int32_t* out_tokens, int32_t* out_nodes, int32_t* out_len, uint32_t* stats,
                          void* ws, hipStream_t stream) {
-  const int nch = (c.V + kCH - 1) / kCH;
   float2* chunk = (float2*)ws;
-  int* done = (int*)((char*)ws + (size_t)c.B * c.N * nch * sizeof(float2));
-  VArgs a{c, t, logits, ld, tstride, seed, step, node_out, chunk, done,
+  VRec* rec = (VRec*)((char*)ws + chunk_bytes(c));
+  float* xtail = (float*)((char*)ws + chunk_bytes(c) + rec_bytes(c));
+  VArgs a{c, t, logits, ld, tstride, seed, step, node_out, chunk, rec, xtail,
           out_tokens, out_nodes, out_len, stats};
   const dim3 grid(c.N, c.B);
   if (c.dtype == VRT_BF16)

@@ -63,28 +63,6 @@ __device__ __forceinline__ float exp_rank(float x) {
   return __builtin_ldexpf(p, (int)k);
 }
 
-// ---------------------------------------------------------------------------
-// wave64 reductions by xor butterflies: every lane ends with the same value, and
-// for a sum the combination order is the aligned pairwise tree over lanes.
-template <typename T>
-__device__ __forceinline__ T wave_sum(T v) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) v = v + __shfl_xor(v, o, kWave);
-  return v;
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
-}
-
-__device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
-
 // inclusive prefix sum over lanes (Hillis-Steele)
 template <typename T>
 __device__ __forceinline__ T wave_incl_scan(T v) {
@@ -220,6 +198,38 @@ template <int LJ>
 __device__ __forceinline__ uint64_t xchg(uint64_t v) {
   return ((uint64_t)xchg32<LJ>((uint32_t)(v >> 32)) << 32) | xchg32<LJ>((uint32_t)v);
 }
+
+template <int LJ>
+__device__ __forceinline__ float xchg(float v) { return __uint_as_float(xchg32<LJ>(__float_as_uint(v))); }
+template <int LJ>
+__device__ __forceinline__ int xchg(int v) { return (int)xchg32<LJ>((uint32_t)v); }
+template <int LJ>
+__device__ __forceinline__ double xchg(double v) {
+  return __longlong_as_double((long long)xchg<LJ>((uint64_t)__double_as_longlong(v)));
+}
+
+// ---------------------------------------------------------------------------
+// wave64 reductions by xor butterflies over lane exchanges: every lane ends with the
+// same value, and for a sum the combination order is the aligned pairwise tree over
+// lanes.
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce(T v, Op op) {
+  v = op(v, xchg<1>(v));
+  v = op(v, xchg<2>(v));
+  v = op(v, xchg<4>(v));
+  v = op(v, xchg<8>(v));
+  v = op(v, xchg<16>(v));
+  v = op(v, xchg<32>(v));
+  return v;
+}
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+  return wave_reduce(v, [](T x, T y) { return x + y; });
+}
+__device__ __forceinline__ float wave_max(float v) {
+  return wave_reduce(v, [](float x, float y) { return fmaxf(x, y); });
+}
+__device__ __forceinline__ int wave_sum_i(int v) { return wave_sum(v); }
 
 // ---------------------------------------------------------------------------
 // Sorted key lists held in a wave's registers: PL keys per lane, position
