@@ -1,21 +1,22 @@
-// Tree verification (RheoSampling, key design 3) on gfx950, in three kernels.
+// Tree verification (RheoSampling, key design 3) on gfx950, in two kernels.
 //
-// k_vstream: one 256-thread block per (node row, tree). The four waves stream the
-//   node's target row from HBM once, in 2048-element chunks (four 16-byte loads per
-//   lane, 8 bf16 each), and write per chunk fl(max*c2) and the sum of
-//   exp2(x*c2 - fl(max*c2)), where c2 = log2(e)/T. Every element costs one
-//   conversion, a third of a max3, one fma, one native exp2 and one add. Before its
-//   share of the stream, the last wave gathers what the decision needs besides the
-//   row statistics: the node's kept children (node, token, logit) and the logits at
-//   the probe tail's tokens. Those dependent loads overlap the other waves' stream.
-// k_vdecide: one wave per (node, tree). From its row's chunk statistics and the
-//   gathered logits it forms p = softmax(x/T) where needed and decides the node
-//   exactly as the walk would if it reached it: the probe-first test min(1, p/q~),
-//   recursive rejection of the other kept children under w = max(0, p - q~) on the
-//   probe's tail (p elsewhere), and, when nothing is accepted, the final residual (or
-//   bonus) sample by inverse CDF in token-id order (adjusted chunk masses locate the
-//   chunk, one 2048-element re-read finds the token). Every draw is keyed by (depth,
-//   test index), so each node's decision is a pure function of its own row.
+// k_vnode: one 256-thread block per (node row, tree).
+//   - The four waves stream the node's target row from HBM once, in 2048-element
+//     chunks (four 16-byte loads per lane, 8 bf16 each, the next chunk in flight),
+//     keeping per chunk fl(max*c2) and the sum of exp2(x*c2 - fl(max*c2)) in LDS,
+//     where c2 = log2(e)/T. Every element costs one conversion, a third of a max3,
+//     one fma, one native exp2 and one add.
+//   - Meanwhile the last wave gathers what the decision needs besides the row
+//     statistics: the kept children (node, token, logit) and the probe tail (token,
+//     q~, logit). Those dependent loads overlap the other waves' stream.
+//   - Wave 0 then forms p = softmax(x/T) where needed and decides the node exactly as
+//     the walk would if it reached it: the probe-first test min(1, p/q~), recursive
+//     rejection of the other kept children under w = max(0, p - q~) on the probe's
+//     tail (p elsewhere), and, when nothing is accepted, the final residual (or bonus)
+//     sample by inverse CDF in token-id order (adjusted chunk masses locate the chunk,
+//     one 2048-element re-read finds the token). Every draw is keyed by (depth, test
+//     index), so each node's decision is a pure function of its own row; other blocks'
+//     streams hide its latency.
 // k_vwalk: one wave per tree follows the accepted children from the root and writes
 //   the emitted tokens and statistics.
 #include "vrt_dev.hpp"
@@ -51,9 +52,6 @@ struct VArgs {
   uint64_t seed;
   uint32_t step;
   NodeOut* node_out;
-  float2* chunk;  // [B][N][nch]: (fl(max*c2), sum exp2(x*c2 - that))
-  VRec* rec;      // [B][N]
-  float* xtail;   // [B][N][TC]: target logits at the probe tail's tokens
   int32_t* out_tokens;
   int32_t* out_nodes;
   int32_t* out_len;
@@ -64,71 +62,52 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ int clamp_nodes(int nn, int N) { return nn < 1 ? 1 : (nn > N ? N : nn); }
 
-// This lane's 32 elements of chunk [lo, lo + 2048): bf16 as four 16-byte loads at
-// lo + q*512 + lane*8, fp32 as eight at lo + q*256 + lane*4. `full` chunks skip the
-// per-element range checks; the ragged last chunk pads with -inf.
-template <int DT, bool full>
-__device__ __forceinline__ void load_chunk(const void* row, int lo, int V, float (&x)[32]) {
+// One chunk of a lane in flight: NL 16-byte loads, load q covering elements
+// lo + q*64*EPL + lane*EPL .. +EPL (bf16: 4 loads of 8, fp32: 8 loads of 4).
+template <int DT>
+struct ChunkRegs {
+  static constexpr int NL = DT == VRT_BF16 ? 4 : 8;
+  static constexpr int EPL = DT == VRT_BF16 ? 8 : 4;
+  u32x4_t w[NL];
+};
+
+template <int DT>
+__device__ __forceinline__ void issue_chunk(const char* row, int lo, int V, ChunkRegs<DT>& r) {
+  using CR = ChunkRegs<DT>;
+  constexpr int esz = DT == VRT_BF16 ? 2 : 4;
   const int lane = lane_id();
-  if constexpr (DT == VRT_BF16) {
-    const uint16_t* r = (const uint16_t*)row;
-    uint4 v[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e0 = lo + q * 512 + lane * 8;
-      v[q] = make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);  // -inf pairs
-      if (full || e0 < V) v[q] = load_nt(r + e0);
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t w[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        x[q * 8 + 2 * k] = bf16_lo(w[k]);
-        x[q * 8 + 2 * k + 1] = bf16_hi(w[k]);
-      }
-    }
-    if (!full) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-          if (lo + q * 512 + lane * 8 + k >= V) x[q * 8 + k] = -INFINITY;
-    }
-  } else {
-    const float* r = (const float*)row;
-    float4 v[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int e0 = lo + q * 256 + lane * 4;
-      v[q] = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-      if (full || e0 < V) {
-        const uint4 t = load_nt(r + e0);
-        v[q] = make_float4(__uint_as_float(t.x), __uint_as_float(t.y), __uint_as_float(t.z),
-                           __uint_as_float(t.w));
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      x[q * 4 + 0] = v[q].x;
-      x[q * 4 + 1] = v[q].y;
-      x[q * 4 + 2] = v[q].z;
-      x[q * 4 + 3] = v[q].w;
-    }
-    if (!full) {
-#pragma unroll
-      for (int q = 0; q < 8; ++q)
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          if (lo + q * 256 + lane * 4 + k >= V) x[q * 4 + k] = -INFINITY;
-    }
-  }
+  static_for<CR::NL>([&](auto q) {
+    const int e0 = lo + (q * kWave + lane) * CR::EPL;
+    const uint32_t ninf = DT == VRT_BF16 ? 0xFF80FF80u : 0xFF800000u;
+    u32x4_t v = {ninf, ninf, ninf, ninf};
+    if (e0 < V) v = __builtin_nontemporal_load((const u32x4_t*)(row + (int64_t)e0 * esz));
+    r.w[q] = v;
+  });
 }
 
-template <int DT, bool full>
-__device__ __forceinline__ float2 chunk_stats(const void* row, int lo, int V, float c2) {
+// (fl(max*c2), sum exp2(x*c2 - fl(max*c2))) of a chunk; `ragged` masks elements >= V.
+template <int DT>
+__device__ __forceinline__ float2 chunk_stats(const ChunkRegs<DT>& r, int lo, int V, float c2, bool ragged) {
+  using CR = ChunkRegs<DT>;
+  const int lane = lane_id();
   float x[32];
-  load_chunk<DT, full>(row, lo, V, x);
+  static_for<CR::NL>([&](auto q) {
+    static_for<4>([&](auto k) {
+      if constexpr (DT == VRT_BF16) {
+        x[q * 8 + 2 * k] = bf16_lo(r.w[q][(int)k]);
+        x[q * 8 + 2 * k + 1] = bf16_hi(r.w[q][(int)k]);
+      } else {
+        x[q * 4 + k] = __uint_as_float(r.w[q][(int)k]);
+      }
+    });
+  });
+  if (ragged) {
+    static_for<CR::NL>([&](auto q) {
+      static_for<CR::EPL>([&](auto k) {
+        if (lo + (q * kWave + lane) * CR::EPL + k >= V) x[q * CR::EPL + k] = -INFINITY;
+      });
+    });
+  }
   float m = x[0];
 #pragma unroll
   for (int k = 1; k < 32; ++k) m = fmaxf(m, x[k]);
@@ -149,9 +128,61 @@ __device__ __forceinline__ float load_one(const void* row, int v) {
   else return ((const float*)row)[v];
 }
 
-// The decision inputs of node i other than its row statistics (one wave).
+__device__ __forceinline__ double readlane_d(double v, int l) {
+  const long long u = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)(uint32_t)u, l);
+  const int hi = __builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+  return __longlong_as_double(((long long)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+// Per-wave LDS of the decision: chunk masses and their fixed-point changes [nch], the
+// probe tail (token, q~, p, child slot) [TC], children's q~ [32], the changes inside
+// the sampled chunk [TC + 32].
+struct DLds {
+  double* pm;
+  long long* dfix;
+  int* tid;
+  float* tq;
+  double* tp;
+  int* tslot;
+  double* qc;
+  int* itok;
+  double* idel;
+};
+
+__host__ __device__ size_t decide_lds_bytes(const Cfg& c) {
+  const size_t nch = (size_t)(c.V + kCH - 1) / kCH;
+  const size_t TC = (size_t)c.TC;
+  const size_t bytes = nch * 16 + TC * (4 + 4 + 8 + 4) + kChildMax * 8 + (TC + kChildMax) * (4 + 8) + 64;
+  return (bytes + 15) & ~(size_t)15;
+}
+
+__device__ DLds carve(char* base, int nch, int TC) {
+  DLds L;
+  char* p = base;
+  auto take = [&](size_t bytes) {
+    char* r = p;
+    p += (bytes + 7) & ~(size_t)7;
+    return r;
+  };
+  L.pm = (double*)take((size_t)nch * 8);
+  L.dfix = (long long*)take((size_t)nch * 8);
+  L.tp = (double*)take((size_t)TC * 8);
+  L.qc = (double*)take(kChildMax * 8);
+  L.idel = (double*)take((size_t)(TC + kChildMax) * 8);
+  L.tid = (int*)take((size_t)TC * 4);
+  L.tq = (float*)take((size_t)TC * 4);
+  L.tslot = (int*)take((size_t)TC * 4);
+  L.itok = (int*)take((size_t)(TC + kChildMax) * 4);
+  return L;
+}
+
+// The decision inputs of node i other than its row statistics, gathered into the
+// block's LDS by one wave: kept children (node, token, logit) in slot order and the
+// probe tail (token, q~, logit).
 template <int DT>
-__device__ void gather_node(const VArgs& a, int b, int i, int nn, const char* row) {
+__device__ void gather_node(const VArgs& a, int b, int i, int nn, const char* row, VRec& r,
+                            const DLds& L) {
   const Cfg& c = a.c;
   const int lane = lane_id();
   const int64_t nb = (int64_t)b * c.N;
@@ -177,10 +208,12 @@ __device__ void gather_node(const VArgs& a, int b, int i, int nn, const char* ro
   const int nt = pl >= 0 ? min(max(a.t.tail_n[nb + i], 0), c.TC) : 0;
   const int64_t tb = (nb + i) * c.TC;
   for (int e = lane; e < nt; e += kWave) {
-    const int y = a.t.tail_id[tb + e];
-    a.xtail[tb + e] = (y >= 0 && y < c.V) ? load_one<DT>(row, y) : -INFINITY;
+    int y = a.t.tail_id[tb + e];
+    if (y < 0 || y >= c.V) y = -1;
+    L.tid[e] = y;
+    L.tq[e] = a.t.tail_q[tb + e];
+    L.tp[e] = y >= 0 ? (double)load_one<DT>(row, y) : -INFINITY;  // the logit for now
   }
-  VRec& r = a.rec[nb + i];
   if (lane < kChildMax) {
     r.node[lane] = node;
     r.tok[lane] = tok;
@@ -191,28 +224,6 @@ __device__ void gather_node(const VArgs& a, int b, int i, int nn, const char* ro
     r.probe = pl;
     r.nt = nt;
     r.depth = min(max(a.t.node_depth[nb + i], 0), 63);
-  }
-}
-
-template <int DT>
-__global__ __launch_bounds__(kVB) void k_vstream(const VArgs a) {
-  const Cfg& c = a.c;
-  const int b = blockIdx.y;
-  const int i = blockIdx.x;
-  const int nn = clamp_nodes(a.t.n_nodes[b], c.N);
-  if (i >= nn) return;
-  const int V = c.V;
-  constexpr int esz = DT == VRT_BF16 ? 2 : 4;
-  const char* row = (const char*)a.logits + ((int64_t)b * a.tstride + (int64_t)i * a.ld) * esz;
-  const int nch = (V + kCH - 1) / kCH;
-  const int nfull = V / kCH;
-  const int wave = threadIdx.x >> 6;
-  if (wave == kVB / kWave - 1) gather_node<DT>(a, b, i, nn, row);
-  float2* out = a.chunk + ((int64_t)b * c.N + i) * nch;
-  for (int ch = wave; ch < nch; ch += kVB / kWave) {
-    const float2 st = ch < nfull ? chunk_stats<DT, true>(row, ch * kCH, V, c.c2)
-                                 : chunk_stats<DT, false>(row, ch * kCH, V, c.c2);
-    if (lane_id() == 0) out[ch] = st;
   }
 }
 
@@ -250,107 +261,47 @@ __device__ __forceinline__ void load_contig(const void* row, int lo, int V, floa
     if (e0 + k >= V) x[k] = -INFINITY;
 }
 
-__device__ __forceinline__ double readlane_d(double v, int l) {
-  const long long u = __double_as_longlong(v);
-  const int lo = __builtin_amdgcn_readlane((int)(uint32_t)u, l);
-  const int hi = __builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
-  return __longlong_as_double(((long long)(uint32_t)hi << 32) | (uint32_t)lo);
-}
-
-// Per-wave LDS of the decision: chunk masses and their fixed-point changes [nch], the
-// probe tail (token, q~, p, child slot) [TC], children's q~ [32], the changes inside
-// the sampled chunk [TC + 32].
-struct DLds {
-  double* pm;
-  long long* dfix;
-  int* tid;
-  float* tq;
-  double* tp;
-  int* tslot;
-  double* qc;
-  int* itok;
-  double* idel;
-};
-
-__host__ __device__ size_t vdecide_lds_per_wave(const Cfg& c) {
-  const size_t nch = (size_t)(c.V + kCH - 1) / kCH;
-  const size_t TC = (size_t)c.TC;
-  const size_t bytes = nch * 16 + TC * (4 + 4 + 8 + 4) + kChildMax * 8 + (TC + kChildMax) * (4 + 8) + 64;
-  return (bytes + 15) & ~(size_t)15;
-}
-
-__device__ DLds carve(char* base, int nch, int TC) {
-  DLds L;
-  char* p = base;
-  auto take = [&](size_t bytes) {
-    char* r = p;
-    p += (bytes + 7) & ~(size_t)7;
-    return r;
-  };
-  L.pm = (double*)take((size_t)nch * 8);
-  L.dfix = (long long*)take((size_t)nch * 8);
-  L.tp = (double*)take((size_t)TC * 8);
-  L.qc = (double*)take(kChildMax * 8);
-  L.idel = (double*)take((size_t)(TC + kChildMax) * 8);
-  L.tid = (int*)take((size_t)TC * 4);
-  L.tq = (float*)take((size_t)TC * 4);
-  L.tslot = (int*)take((size_t)TC * 4);
-  L.itok = (int*)take((size_t)(TC + kChildMax) * 4);
-  return L;
-}
-
+// The decision of node i by one wave, from the chunk statistics and gathered inputs
+// in LDS (see the file comment).
 template <int DT>
-__global__ __launch_bounds__(kDW * kWave) void k_vdecide(const VArgs a) {
+__device__ void decide_node(const VArgs& a, int b, int i, const char* row, const float2* cs,
+                            const VRec& R, const DLds& L) {
   const Cfg& c = a.c;
-  const int wave = threadIdx.x >> 6;
   const int lane = lane_id();
-  const int64_t g = (int64_t)blockIdx.x * kDW + wave;
-  if (g >= (int64_t)c.B * c.N) return;
-  const int b = (int)(g / c.N);
-  const int i = (int)(g % c.N);
-  const int nn = clamp_nodes(a.t.n_nodes[b], c.N);
-  if (i >= nn) return;
-
   const int V = c.V;
-  constexpr int esz = DT == VRT_BF16 ? 2 : 4;
-  const char* row = (const char*)a.logits + ((int64_t)b * a.tstride + (int64_t)i * a.ld) * esz;
   const int nch = (V + kCH - 1) / kCH;
   const float c2 = c.c2;
-  const int TC = c.TC;
   const int64_t nb = (int64_t)b * c.N;
-  extern __shared__ double s_dyn[];
-  const DLds L = carve((char*)s_dyn + vdecide_lds_per_wave(c) * wave, nch, TC);
-
-  // ---- inputs: row statistics, children, probe tail (independent loads)
-  const VRec& R = a.rec[nb + i];
   const int nc = R.nc, probe = R.probe, nt = R.nt;
   const uint32_t depth = (uint32_t)R.depth;
-  int ch_node = -1, ch_tok = -1;
-  float ch_x = -INFINITY;
-  if (lane < nc) {
-    ch_node = R.node[lane];
-    ch_tok = R.tok[lane];
-    ch_x = R.x[lane];
+  int r_node = -1, r_tok = -1;
+  float r_x = -INFINITY;
+  if (lane < kChildMax) {
+    r_node = R.node[lane];
+    r_tok = R.tok[lane];
+    r_x = R.x[lane];
   }
-  const int64_t tb = (nb + i) * TC;
-  for (int e = lane; e < nt; e += kWave) {
-    int y = a.t.tail_id[tb + e];
-    if (y < 0 || y >= V) y = -1;
-    L.tid[e] = y;
-    L.tq[e] = a.t.tail_q[tb + e];
-    L.tp[e] = a.xtail[tb + e];  // the logit for now
-  }
-  const float2* cs = a.chunk + (nb + i) * nch;
+  constexpr int kCPL = 8;  // chunks per lane: V <= 2^20
+  float2 st[kCPL];
+  static_for<kCPL>([&](auto k) {
+    const int ch = lane + k * kWave;
+    st[k] = ch < nch ? cs[ch] : make_float2(-INFINITY, 0.0f);
+  });
+  const int ch_node = lane < nc ? r_node : -1;
+  const int ch_tok = lane < nc ? r_tok : -1;
+  const float ch_x = lane < nc ? r_x : -INFINITY;
   float mcl = -INFINITY;
-  for (int ch = lane; ch < nch; ch += kWave) mcl = fmaxf(mcl, cs[ch].x);
+  static_for<kCPL>([&](auto k) { mcl = fmaxf(mcl, st[k].x); });
   const float MC = wave_max(mcl);
   double sl = 0.0;
-  for (int ch = lane; ch < nch; ch += kWave) {
-    const float2 st = cs[ch];
-    const double pm = (double)st.y * (double)fast_exp2(st.x - MC);
-    L.pm[ch] = pm;
-    sl += pm;
-  }
+  static_for<kCPL>([&](auto k) {
+    const int ch = lane + k * kWave;
+    if (ch < nch) {
+      const double pm = (double)st[k].y * (double)fast_exp2(st[k].x - MC);
+      L.pm[ch] = pm;
+      sl += pm;
+    }
+  });
   const double S = wave_sum(sl);
   NodeOut out{-1, -1, 0, 0.0f};
   if (!(S > 0.0) || !(S < INFINITY) || !(MC < INFINITY)) {
@@ -585,28 +536,77 @@ __global__ __launch_bounds__(kDW * kWave) void k_vdecide(const VArgs a) {
   if (lane == 0) a.node_out[nb + i] = out;
 }
 
-// The walk of tree b (one lane): follow accepted children from the root.
-__device__ void walk_tree(const VArgs& a, int b, int nn) {
+constexpr int kMaxChunks = (1 << 20) / kCH;  // V <= 2^20
+
+// One block per (node, tree): stream the row (all waves), gather the decision inputs
+// (last wave, overlapping the others' stream), then decide (wave 0).
+template <int DT>
+__global__ __launch_bounds__(kVB) void k_vnode(const VArgs a) {
   const Cfg& c = a.c;
+  const int b = blockIdx.y;
+  const int i = blockIdx.x;
+  const int nn = clamp_nodes(a.t.n_nodes[b], c.N);
+  if (i >= nn) return;
+  const int V = c.V;
+  constexpr int esz = DT == VRT_BF16 ? 2 : 4;
+  const char* row = (const char*)a.logits + ((int64_t)b * a.tstride + (int64_t)i * a.ld) * esz;
+  const int nch = (V + kCH - 1) / kCH;
+  const int nfull = V / kCH;
+  const int wave = threadIdx.x >> 6;
+  __shared__ float2 s_cs[kMaxChunks];
+  __shared__ VRec s_rec;
+  extern __shared__ double s_dyn[];
+  const DLds L = carve((char*)s_dyn, nch, c.TC);
+  constexpr int NW = kVB / kWave;
+  ChunkRegs<DT> cur, nxt;
+  if (wave < nch) issue_chunk<DT>(row, wave * kCH, V, cur);
+  if (wave == NW - 1) gather_node<DT>(a, b, i, nn, row, s_rec, L);
+  for (int ch = wave; ch < nch; ch += NW) {
+    if (ch + NW < nch) issue_chunk<DT>(row, (ch + NW) * kCH, V, nxt);
+    const float2 st = chunk_stats<DT>(cur, ch * kCH, V, c.c2, ch >= nfull);
+    if (lane_id() == 0) s_cs[ch] = st;
+    cur = nxt;
+  }
+  __syncthreads();
+  if (wave == 0) decide_node<DT>(a, b, i, row, s_cs, s_rec, L);
+}
+
+// One wave per tree: the walk over the decided nodes. The tree's decisions, tokens
+// and kinds are first loaded into LDS (one round of parallel loads), then lane 0
+// follows the accepted children from the root.
+__global__ __launch_bounds__(kWave) void k_vwalk(const VArgs a) {
+  const Cfg& c = a.c;
+  const int b = blockIdx.x;
+  const int nn = clamp_nodes(a.t.n_nodes[b], c.N);
   const int lane = lane_id();
   const int64_t nb = (int64_t)b * c.N;
+  extern __shared__ int4 s_walk[];  // [N] decisions, then [N] tokens, then [N] kinds
+  int* s_tok = (int*)(s_walk + c.N);
+  int* s_kind = s_tok + c.N;
   uint32_t st = 0;
-  for (int i = lane; i < nn; i += kWave) st |= (uint32_t)a.node_out[nb + i].flags >> 16;
+  for (int i = lane; i < nn; i += kWave) {
+    const NodeOut o = a.node_out[nb + i];
+    s_walk[i] = make_int4(o.accept, o.token, o.flags, 0);
+    s_tok[i] = a.t.node_token[nb + i];
+    s_kind[i] = a.t.node_kind[nb + i];
+    st |= (uint32_t)o.flags >> 16;
+  }
   st = wave_reduce(st, [](uint32_t x, uint32_t y) { return x | y; });
+  wave_sync();
   if (lane != 0) return;
   int cur = 0, len = 0, near = 0, probe = 0, visited = 0;
   for (int step = 0; step <= c.D; ++step) {
-    const NodeOut o = a.node_out[nb + cur];
+    const int4 o = s_walk[cur];
     ++visited;
-    near += (o.flags >> 8) & 0xFF;
-    if (o.accept > cur && o.accept < nn && len < c.D) {
-      a.out_nodes[(int64_t)b * c.D + len] = o.accept;
-      a.out_tokens[(int64_t)b * (c.D + 1) + len] = a.t.node_token[nb + o.accept];
-      if (a.t.node_kind[nb + o.accept] == VRT_PROBE) probe = 1;
+    near += (o.z >> 8) & 0xFF;
+    if (o.x > cur && o.x < nn && len < c.D) {
+      a.out_nodes[(int64_t)b * c.D + len] = o.x;
+      a.out_tokens[(int64_t)b * (c.D + 1) + len] = s_tok[o.x];
+      if (s_kind[o.x] == VRT_PROBE) probe = 1;
       ++len;
-      cur = o.accept;
+      cur = o.x;
     } else {
-      a.out_tokens[(int64_t)b * (c.D + 1) + len] = o.token;
+      a.out_tokens[(int64_t)b * (c.D + 1) + len] = o.y;
       ++len;
       break;
     }
@@ -625,50 +625,28 @@ __device__ void walk_tree(const VArgs& a, int b, int nn) {
   }
 }
 
-// One wave per tree: the walk over the decided nodes.
-__global__ __launch_bounds__(kWave) void k_vwalk(const VArgs a) {
-  const int b = blockIdx.x;
-  walk_tree(a, b, clamp_nodes(a.t.n_nodes[b], a.c.N));
-}
-
-size_t chunk_bytes(const Cfg& c) {
-  const size_t nch = (size_t)(c.V + kCH - 1) / kCH;
-  return ((size_t)c.B * c.N * nch * sizeof(float2) + 255) & ~(size_t)255;
-}
-size_t rec_bytes(const Cfg& c) { return ((size_t)c.B * c.N * sizeof(VRec) + 255) & ~(size_t)255; }
-
 }  // namespace
 
 size_t verify_ws_bytes(const Cfg& c) {
-  return chunk_bytes(c) + rec_bytes(c) + (size_t)c.B * c.N * c.TC * sizeof(float);
+  (void)c;
+  return 0;
 }
 
 hipError_t launch_verify(const Cfg& c, const TreePtrs& t, const void* logits, int64_t ld,
                          int64_t tstride, uint64_t seed, uint32_t step, NodeOut* node_out,
                          int32_t* out_tokens, int32_t* out_nodes, int32_t* out_len, uint32_t* stats,
                          void* ws, hipStream_t stream) {
-  float2* chunk = (float2*)ws;
-  VRec* rec = (VRec*)((char*)ws + chunk_bytes(c));
-  float* xtail = (float*)((char*)ws + chunk_bytes(c) + rec_bytes(c));
-  VArgs a{c, t, logits, ld, tstride, seed, step, node_out, chunk, rec, xtail,
-          out_tokens, out_nodes, out_len, stats};
+  (void)ws;
+  VArgs a{c, t, logits, ld, tstride, seed, step, node_out, out_tokens, out_nodes, out_len, stats};
   const dim3 grid(c.N, c.B);
+  const size_t lds = decide_lds_bytes(c);
   if (c.dtype == VRT_BF16)
-    hipLaunchKernelGGL(k_vstream<VRT_BF16>, grid, dim3(kVB), 0, stream, a);
+    hipLaunchKernelGGL(k_vnode<VRT_BF16>, grid, dim3(kVB), lds, stream, a);
   else
-    hipLaunchKernelGGL(k_vstream<VRT_F32>, grid, dim3(kVB), 0, stream, a);
+    hipLaunchKernelGGL(k_vnode<VRT_F32>, grid, dim3(kVB), lds, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t nodes = (int64_t)c.B * c.N;
-  const dim3 g2((unsigned)((nodes + kDW - 1) / kDW));
-  const size_t lds = vdecide_lds_per_wave(c) * kDW;
-  if (c.dtype == VRT_BF16)
-    hipLaunchKernelGGL(k_vdecide<VRT_BF16>, g2, dim3(kDW * kWave), lds, stream, a);
-  else
-    hipLaunchKernelGGL(k_vdecide<VRT_F32>, g2, dim3(kDW * kWave), lds, stream, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_vwalk, dim3(c.B), dim3(kWave), 0, stream, a);
+  hipLaunchKernelGGL(k_vwalk, dim3(c.B), dim3(kWave), (size_t)c.N * (16 + 4 + 4), stream, a);
   return hipGetLastError();
 }
 
