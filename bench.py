@@ -22,43 +22,131 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="headline")
     ap.add_argument("--T", type=float, default=1.0)
     ap.add_argument("--seed", type=int, default=1)
-    ap.add_argument("--cpu-trees", type=int, default=6, help="trees in the oracle's timed sample")
+    ap.add_argument("--cpu-trees", type=int, default=0,
+                    help="trees in the oracle's timed sample (0: four per host core)")
+    ap.add_argument("--sets", type=int, default=3, help="input sets the steps rotate over")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
     ap.add_argument("--verify-only", action="store_true",
                     help="time only the verification call (for profiling it alone)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only copy a MIB-MiB buffer 3 times (calibrates hardware byte counters)")
     return ap.parse_args()
 
 
-def cpu_baseline(w, seed, n_trees):
-    """The oracle as it stands, one host thread, on n_trees trees of the workload."""
+HERE = os.path.dirname(os.path.abspath(__file__))
+# sources the verification kernels are compiled from; counters taken on other sources
+# no longer describe the kernel
+VERIFY_SOURCES = ["verify_row_top_amd/csrc/k_verify.hip", "verify_row_top_amd/csrc/vrt_dev.hpp"]
+PMC_SUMMARY = "profiles/k_vnode_headline_pmc.md"
+
+
+def sources_sha():
+    import hashlib
+    h = hashlib.sha256()
+    for p in VERIFY_SOURCES:
+        with open(os.path.join(HERE, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per verification call from the committed counter summary, or None when
+    it is missing or was taken on other kernel sources."""
+    import re
+    try:
+        with open(os.path.join(HERE, PMC_SUMMARY)) as f:
+            text = f.read()
+    except OSError:
+        return None
+    m = re.search(r"```json\n(.*?)\n```", text, re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("sources_sha") != sources_sha():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def copy_probe(mib):
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "copies": 3, "sources_sha": sources_sha()}), flush=True)
+
+
+def _oracle_tree(arg):
+    name, kw, seed, b = arg
     from oracle.drive import OracleStep
-    t = 0.0
-    for b in range(n_trees):
-        s = OracleStep(w, seed, b, 0)
-        t += s.t_oracle
-    return {"value": n_trees / t, "unit": "trees/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n_trees} trees (b=0..{n_trees - 1}, seed {seed}, step 0) of the same "
-                      f"workload, build + verify, oracle time only, 1 thread"}
+    from synth import workloads
+    return OracleStep(workloads.get(name, **kw), seed, b, 0).t_oracle
+
+
+def cpu_baseline(w, seed, n_trees):
+    """The oracle as it stands on n_trees trees of the workload: one tree per process
+    over every host core this process may use, and (for reference) one thread."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    n_trees = n_trees or 4 * cores
+    kw = {"T": w.T}
+    args = [(w.name, kw, seed, b) for b in range(n_trees)]
+    t0 = time.perf_counter()
+    with cf.ProcessPoolExecutor(max_workers=cores, mp_context=mp.get_context("spawn")) as ex:
+        per_tree = list(ex.map(_oracle_tree, args))
+    wall = time.perf_counter() - t0
+    single = n_trees / sum(per_tree)
+    return {"value": n_trees / wall, "unit": "trees/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n_trees} trees (b=0..{n_trees - 1}, seed {seed}, step 0) of the same workload, "
+                      f"build + verify, one tree per process on {cores} cores, wall time including "
+                      f"process start",
+            "single_thread_value": single}
+
+
+def read_ceiling(torch, dev, vrt, mib=1024, reps=10):
+    """GB/s of the library's streaming-read probe over a buffer larger than the caches."""
+    buf = torch.randint(0, 1 << 30, ((mib << 20) // 4,), dtype=torch.int32, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    vrt.read_probe(buf, sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        vrt.read_probe(buf, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del buf
+    return (mib << 20) / (ms * 1e-3) / 1e9
 
 
 def main():
     args = parse()
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (trees are "
               f"independent: shard the batch, one process per GPU)", file=sys.stderr)
         sys.exit(2)
+    from synth import workloads
+    w = workloads.get(args.workload, T=args.T)
+    # the oracle's processes start before this process touches the GPU
+    cpu = None if args.no_cpu else cpu_baseline(w, args.seed, args.cpu_trees)
+
     import torch
 
     import synth
-    from synth import workloads
     from verify_row_top_amd import vrt
 
-    w = workloads.get(args.workload, T=args.T)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     cfg = vrt.make_config(B=w.B, V=w.V, dtype=w.dtype, trunc=w.trunc, K=w.K, m=w.m, probe=w.probe,
@@ -71,8 +159,6 @@ def main():
     ld = (V + per - 1) // per * per
     tdt = torch.int16 if w.dtype == synth.BF16 else torch.float32
     n_draft = 1 + (D - 1) * FP
-    draft = torch.empty((B, n_draft, ld), dtype=tdt, device=dev)
-    target = torch.empty((B, N, ld), dtype=tdt, device=dev)
     tree = torch.zeros(vrt.tree_bytes(cfg), dtype=torch.uint8, device=dev)
     ws = torch.zeros(vrt.workspace_bytes(cfg), dtype=torch.uint8, device=dev)
     views = vrt.tree_views(cfg, tree)
@@ -80,58 +166,67 @@ def main():
     out_tokens = torch.zeros((B, D + 1), dtype=torch.int32, device=dev)
     out_nodes = torch.zeros((B, D), dtype=torch.int32, device=dev)
     out_len = torch.zeros(B, dtype=torch.int32, device=dev)
+
+    # ---- inputs: NSETS independent input sets (distinct generator seeds), each made by
+    # the generator playing the draft model along the GPU's own frontier, layer by
+    # layer, then the target model on the emitted tree (untimed). Steps rotate over the
+    # sets, so between two reads of the same bytes more than 2 GB of other rows pass
+    # through HBM and the 256 MB last-level cache cannot serve them.
     stream = torch.cuda.current_stream().cuda_stream
-
-    # ---- inputs: the generator plays the draft model along the GPU's own frontier,
-    # layer by layer, then the target model on the emitted tree (untimed)
-    p = w.params()
-    zipf = torch.from_numpy(w.tables()).to(dev)
-    rk = [synth.root_key(w.gen_seed, b) for b in range(B)]
-    root_keys = torch.tensor([k - (1 << 64) if k >= (1 << 63) else k for k in rk],
-                             dtype=torch.int64, device=dev)
-    tree_of = torch.arange(B, dtype=torch.int32, device=dev)
-    tmp = torch.empty((B, FP, ld), dtype=tdt, device=dev)
     seed, step = args.seed, 0
-
-    def layer_rows(layer):
-        r0 = 0 if layer == 0 else 1 + (layer - 1) * FP
-        return draft[:, r0:]
 
     def layer_base(l):
         return 0 if l == 0 else K + (l - 1) * FP * K
 
-    keys_prev = root_keys.view(B, 1)
-    synth.rows_dev(p, zipf, keys_prev.reshape(-1), tree_of, tmp[:, 0], synth.DRAFT, stream)
-    draft[:, 0].copy_(tmp[:, 0])
-    vrt.build_tree(cfg, 0, layer_rows(0), ld, n_draft * ld, seed, step, tree, ws, stats)
-    for layer in range(1, D):
-        keys = torch.zeros((B, FP), dtype=torch.int64, device=dev)
-        synth.frontier_keys_dev(B, K, layer_base(layer - 1), keys_prev, views["front"],
-                                views["n_front"], views["cand_token"], keys, stream)
-        synth.rows_dev(p, zipf, keys.reshape(-1), tree_of.repeat_interleave(FP),
-                       tmp.view(B * FP, ld), synth.DRAFT, stream)
-        r0 = 1 + (layer - 1) * FP
-        draft[:, r0:r0 + FP].copy_(tmp)
-        vrt.build_tree(cfg, layer, layer_rows(layer), ld, n_draft * ld, seed, step, tree, ws, stats)
-        keys_prev = keys
-    vrt.build_tree(cfg, vrt.FINISH, None, 0, 0, seed, step, tree, ws, stats)
-    node_keys = torch.zeros((B, N), dtype=torch.int64, device=dev)
-    synth.tree_keys_dev(B, N, root_keys, views["n_nodes"], views["node_token"], views["node_parent"],
-                        node_keys, stream)
-    synth.rows_dev(p, zipf, node_keys.reshape(-1), tree_of.repeat_interleave(N), target.view(B * N, ld),
-                   synth.TARGET, stream)
-    torch.cuda.synchronize()
-    n_nodes = views["n_nodes"].cpu()
-    del tmp
+    def make_set(gen_seed):
+        ws_ = w.replace(gen_seed=gen_seed)
+        p = ws_.params()
+        zipf = torch.from_numpy(ws_.tables()).to(dev)
+        rk = [synth.root_key(gen_seed, b) for b in range(B)]
+        root_keys = torch.tensor([k - (1 << 64) if k >= (1 << 63) else k for k in rk],
+                                 dtype=torch.int64, device=dev)
+        tree_of = torch.arange(B, dtype=torch.int32, device=dev)
+        draft = torch.empty((B, n_draft, ld), dtype=tdt, device=dev)
+        target = torch.empty((B, N, ld), dtype=tdt, device=dev)
+        tmp = torch.empty((B, FP, ld), dtype=tdt, device=dev)
+        keys_prev = root_keys.view(B, 1)
+        synth.rows_dev(p, zipf, keys_prev.reshape(-1), tree_of, tmp[:, 0], synth.DRAFT, stream)
+        draft[:, 0].copy_(tmp[:, 0])
+        vrt.build_tree(cfg, 0, draft, ld, n_draft * ld, seed, step, tree, ws, stats)
+        for layer in range(1, D):
+            keys = torch.zeros((B, FP), dtype=torch.int64, device=dev)
+            synth.frontier_keys_dev(B, K, layer_base(layer - 1), keys_prev, views["front"],
+                                    views["n_front"], views["cand_token"], keys, stream)
+            synth.rows_dev(p, zipf, keys.reshape(-1), tree_of.repeat_interleave(FP),
+                           tmp.view(B * FP, ld), synth.DRAFT, stream)
+            r0 = 1 + (layer - 1) * FP
+            draft[:, r0:r0 + FP].copy_(tmp)
+            vrt.build_tree(cfg, layer, draft[:, r0:], ld, n_draft * ld, seed, step, tree, ws, stats)
+            keys_prev = keys
+        vrt.build_tree(cfg, vrt.FINISH, None, 0, 0, seed, step, tree, ws, stats)
+        node_keys = torch.zeros((B, N), dtype=torch.int64, device=dev)
+        synth.tree_keys_dev(B, N, root_keys, views["n_nodes"], views["node_token"],
+                            views["node_parent"], node_keys, stream)
+        synth.rows_dev(p, zipf, node_keys.reshape(-1), tree_of.repeat_interleave(N),
+                       target.view(B * N, ld), synth.TARGET, stream)
+        torch.cuda.synchronize()
+        return draft, target, views["n_nodes"].cpu().clone()
+
+    sets = [make_set(w.gen_seed + 7919 * s) for s in range(args.sets)]
+
+    def layer_rows(draft, layer):
+        r0 = 0 if layer == 0 else 1 + (layer - 1) * FP
+        return draft[:, r0:]
 
     # ---- timed: K whole steps (every build layer, finish, verification)
-    def one_step(evs=None):
+    def one_step(k, evs=None):
+        draft, target, _ = sets[k % len(sets)]
         if evs:
             evs[0].record()
         if not args.verify_only:
             for layer in range(D):
-                vrt.build_tree(cfg, layer, layer_rows(layer), ld, n_draft * ld, seed, step, tree, ws,
-                               stats)
+                vrt.build_tree(cfg, layer, layer_rows(draft, layer), ld, n_draft * ld, seed, step,
+                               tree, ws, stats)
             vrt.build_tree(cfg, vrt.FINISH, None, 0, 0, seed, step, tree, ws, stats)
         if evs:
             evs[1].record()
@@ -140,22 +235,32 @@ def main():
         if evs:
             evs[2].record()
 
-    for _ in range(args.warmup):
-        one_step()
+    if args.verify_only:  # the tree of set 0 stays in place; every step verifies set 0's rows
+        sets = sets[:1]
+        draft0 = sets[0][0]
+        for layer in range(D):
+            vrt.build_tree(cfg, layer, layer_rows(draft0, layer), ld, n_draft * ld, seed, step, tree,
+                           ws, stats)
+        vrt.build_tree(cfg, vrt.FINISH, None, 0, 0, seed, step, tree, ws, stats)
+    for k in range(args.warmup):
+        one_step(k)
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for k in range(args.steps):
-        one_step(evs[k])
+        one_step(k, evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     build_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    verify_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    vt = sorted(e[1].elapsed_time(e[2]) for e in evs)
+    verify_ms = sum(vt) / len(vt)
+    q = lambda f: vt[min(len(vt) - 1, int(f * len(vt)))]
     ms_per_step = wall * 1e3 / args.steps
+    n_nodes = sum(s[2] for s in [sets[k % len(sets)] for k in range(args.steps)]) / args.steps
 
     st = stats.cpu()
     lens = out_len.cpu().float()
-    verify_bytes = int(n_nodes.sum()) * V * esz
+    verify_bytes = int(round(float(n_nodes.sum()))) * V * esz
     draft_rows = B * (1 + (D - 1) * FP) if w.mode == workloads.TOPR else None
     build_bytes = draft_rows * V * esz if draft_rows else None
     verify_gbs = verify_bytes / (verify_ms * 1e-3) / 1e9
@@ -175,11 +280,13 @@ def main():
         "config": {"workload": f"{w.name}: B={B}, V={V} {'bf16' if esz == 2 else 'fp32'} logits, "
                                f"R={w.R}, D={D}, K=W={w.width}, m={w.m}, T={w.T}, trunc={w.trunc}",
                    "B": B, "V": V, "R": w.R, "D": D, "K": K, "m": w.m, "T": w.T},
-        "roofline": {"bound": "hbm", "kernel": "vrt_verify_tree (row pass + walk)",
+        "roofline": {"bound": "hbm", "kernel": "vrt_verify_tree (k_vnode + k_vwalk)",
                      "achieved": verify_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": verify_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "frac": verify_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "algorithmic_bytes_per_launch": verify_bytes, "avg_launch_ms": verify_ms},
         "verify_ms": verify_ms,
+        "verify_ms_p10_p50_p90": [q(0.1), q(0.5), q(0.9)],
+        "read_ceiling_gbs": read_ceiling(torch, dev, vrt),
         "verify_trees_per_s": B / (verify_ms * 1e-3),
         "build_ms": build_ms if not args.verify_only else None,
         "build_gbps": (build_bytes / (build_ms * 1e-3) / 1e9) if (build_bytes and not args.verify_only)
@@ -188,8 +295,8 @@ def main():
         "mean_tokens_per_tree": float(lens.mean()),
         "status_bits": int((st[:, 0] != 0).sum()),
     }
-    if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(w, seed, args.cpu_trees)
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
 
 

@@ -174,6 +174,14 @@ vrt_status vrt_build_tree(const vrt_config* cfg, int32_t layer, const void* draf
                           int64_t ld, int64_t tree_stride, uint64_t seed, uint64_t step,
                           void* tree, void* ws, size_t ws_bytes, uint32_t* stats, void* stream);
 
+/* Measurement helper, not a step of the method: streams `bytes` bytes of device
+ * memory at buf once with the same 16-byte non-temporal loads the row kernels use
+ * and ORs a checksum into *sink (device u32), so that the read cannot be elided. Its
+ * achieved GB/s is this device's practical streaming-read ceiling.
+ *   buf    device, 16-byte aligned;  bytes  a multiple of 16
+ * Errors: VRT_EINVAL (alignment, NULL), VRT_EHIP. */
+vrt_status vrt_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
 /* Verification of an emitted tree (RheoSampling key design 3).
  *   target_logits device, dtype cfg->dtype: the target row of node i of tree b starts
  *                 at element b*tree_stride + i*ld (rows i < n_nodes[b] are read);

@@ -267,4 +267,12 @@ vrt_status vrt_verify_tree(const vrt_config* cp, const void* target_logits, int6
   return VRT_OK;
 }
 
+vrt_status vrt_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  if (!buf || !sink) return fail(VRT_EINVAL, "buffer and sink must not be NULL");
+  if (!aligned16(buf) || (bytes & 15u)) return fail(VRT_EINVAL, "buffer and size must be 16-byte aligned");
+  const hipError_t e = vrt::launch_read_probe(buf, bytes, sink, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(VRT_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return VRT_OK;
+}
+
 }  // extern "C"

@@ -75,4 +75,6 @@ hipError_t launch_build_layer(const Cfg& c, const TreePtrs& t, int layer, const 
                               uint32_t* stats, void* ws, hipStream_t stream);
 hipError_t launch_build_finish(const Cfg& c, const TreePtrs& t, void* ws, hipStream_t stream);
 
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 }  // namespace vrt

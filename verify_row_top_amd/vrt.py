@@ -18,7 +18,7 @@ ROOT, DET, PROBE, FILL = 0, 1, 2, 3
 FINISH = -1
 ST_DRAFT_NONFINITE, ST_DRAFT_EMPTY, ST_TARGET_BAD = 0x1, 0x2, 0x4
 EXPORTS = ("vrt_check_config", "vrt_tree_layout_of", "vrt_tree_bytes", "vrt_workspace_bytes",
-           "vrt_build_tree", "vrt_verify_tree", "vrt_last_error")
+           "vrt_build_tree", "vrt_verify_tree", "vrt_read_probe", "vrt_last_error")
 
 
 class VrtError(RuntimeError):
@@ -68,6 +68,8 @@ def lib():
         L.vrt_verify_tree.argtypes = [P(Config), vp, i64, i64, vp, u64, u64, vp, sz, vp, vp, vp, vp,
                                       vp, vp]
         L.vrt_verify_tree.restype = i32
+        L.vrt_read_probe.argtypes = [vp, sz, vp, vp]
+        L.vrt_read_probe.restype = i32
         L.vrt_last_error.argtypes = []
         L.vrt_last_error.restype = ctypes.c_char_p
         _lib = L
@@ -139,6 +141,12 @@ def verify_tree(cfg, target_logits, ld, tree_stride, tree, seed, step, ws, out_t
                                  seed, step, _ptr(ws), ws.numel() * ws.element_size(),
                                  _ptr(out_tokens), _ptr(out_nodes), _ptr(out_len), _ptr(stats),
                                  _ptr(node_out), _stream(stream)))
+
+
+def read_probe(buf, sink, stream=None):
+    """vrt_read_probe over the whole of `buf` (a device tensor); `sink` a device u32."""
+    _check(lib().vrt_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                _stream(stream)))
 
 
 # ---------------------------------------------------------------------------
