@@ -148,12 +148,14 @@ struct DLds {
   double* qc;
   int* itok;
   double* idel;
+  float* w;  // [64][33] weights of the sampled chunk
 };
 
 __host__ __device__ size_t decide_lds_bytes(const Cfg& c) {
   const size_t nch = (size_t)(c.V + kCH - 1) / kCH;
   const size_t TC = (size_t)c.TC;
-  const size_t bytes = nch * 16 + TC * (4 + 4 + 8 + 4) + kChildMax * 8 + (TC + kChildMax) * (4 + 8) + 64;
+  const size_t bytes = nch * 16 + TC * (4 + 4 + 8 + 4) + kChildMax * 8 + (TC + kChildMax) * (4 + 8) +
+                       kWave * 33 * 4 + 72;
   return (bytes + 15) & ~(size_t)15;
 }
 
@@ -174,6 +176,7 @@ __device__ DLds carve(char* base, int nch, int TC) {
   L.tq = (float*)take((size_t)TC * 4);
   L.tslot = (int*)take((size_t)TC * 4);
   L.itok = (int*)take((size_t)(TC + kChildMax) * 4);
+  L.w = (float*)take((size_t)kWave * 33 * 4);
   return L;
 }
 
@@ -227,39 +230,6 @@ __device__ void gather_node(const VArgs& a, int b, int i, int nn, const char* ro
   }
 }
 
-// This lane's 32 contiguous elements [lo + lane*32, +32) of a chunk (id order).
-template <int DT>
-__device__ __forceinline__ void load_contig(const void* row, int lo, int V, float (&x)[32]) {
-  const int e0 = lo + lane_id() * 32;
-  if constexpr (DT == VRT_BF16) {
-    const uint16_t* r = (const uint16_t*)row;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (e0 + q * 8 < V) v = *(const uint4*)(r + e0 + q * 8);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        x[q * 8 + 2 * k] = bf16_lo(w[k]);
-        x[q * 8 + 2 * k + 1] = bf16_hi(w[k]);
-      }
-    }
-  } else {
-    const float* r = (const float*)row;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (e0 + q * 4 < V) v = *(const float4*)(r + e0 + q * 4);
-      x[q * 4 + 0] = v.x;
-      x[q * 4 + 1] = v.y;
-      x[q * 4 + 2] = v.z;
-      x[q * 4 + 3] = v.w;
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < 32; ++k)
-    if (e0 + k >= V) x[k] = -INFINITY;
-}
 
 // The decision of node i by one wave, from the chunk statistics and gathered inputs
 // in LDS (see the file comment).
@@ -473,32 +443,42 @@ __device__ void decide_node(const VArgs& a, int b, int i, const char* row, const
       }
       nitem += (int)__builtin_popcountll(m);
     }
-    // re-read the chunk; lane l owns tokens [lo + 32 l, lo + 32 l + 32)
-    float x[32];
-    load_contig<DT>(row, lo, V, x);
-    float wv[32];
-    const float invSf = (float)invS;
-#pragma unroll
-    for (int k = 0; k < 32; ++k)
-      wv[k] = (x[k] > -INFINITY) ? fast_exp2(__builtin_fmaf(x[k], c2, -MC)) * invSf : 0.0f;
+    // re-read the chunk; lane l owns tokens [lo + 32 l, lo + 32 l + 32), whose weights
+    // go to LDS (stride 33: conflict-free per-lane walks)
     const int my0 = lo + lane * 32;
-    wave_sync();
-    for (int it = 0; it < nitem; ++it) {
-      const int y = L.itok[it];
-      if (y >= my0 && y < my0 + 32) {
-        const double dd = L.idel[it];
-        const int off = y - my0;
-#pragma unroll
-        for (int k = 0; k < 32; ++k)
-          if (k == off) {
-            const double v = (double)wv[k] + dd;
-            wv[k] = v > 0.0 ? (float)v : 0.0f;
-          }
-      }
+    float* sw = L.w + lane * 33;
+    {
+      constexpr int esz = DT == VRT_BF16 ? 2 : 4;
+      constexpr int EPL = 16 / esz;
+      const float invSf = (float)invS;
+      u32x4_t raw[32 / EPL];
+      static_for<32 / EPL>([&](auto q) {  // all loads first
+        const int e0 = my0 + q * EPL;
+        raw[q] = u32x4_t{0u, 0u, 0u, 0u};
+        if (e0 < V) raw[q] = *(const u32x4_t*)(row + (int64_t)e0 * esz);
+      });
+      static_for<32 / EPL>([&](auto q) {
+        static_for<EPL>([&](auto k) {
+          float x;
+          if constexpr (DT == VRT_BF16) x = (k & 1) ? bf16_hi(raw[q][k >> 1]) : bf16_lo(raw[q][k >> 1]);
+          else x = __uint_as_float(raw[q][(int)k]);
+          const int e = q * EPL + k;
+          sw[e] = (my0 + e < V && x > -INFINITY) ? fast_exp2(__builtin_fmaf(x, c2, -MC)) * invSf : 0.0f;
+        });
+      });
     }
+    wave_sync();
+    // the changes inside the chunk, one per lane (distinct tokens)
+    for (int it = lane; it < nitem; it += kWave) {
+      const int off = L.itok[it] - lo;
+      float* pw = L.w + (off >> 5) * 33 + (off & 31);
+      const double v = (double)*pw + L.idel[it];
+      *pw = v > 0.0 ? (float)v : 0.0f;
+    }
+    wave_sync();
     double lsum = 0.0;
-#pragma unroll
-    for (int k = 0; k < 32; ++k) lsum += (double)wv[k];
+#pragma unroll 8
+    for (int k = 0; k < 32; ++k) lsum += (double)sw[k];
     const double lincl = wave_incl_scan(lsum) + before;
     const double lexcl = lincl - lsum;
     const uint64_t hit2 = ballot(tgt < lincl && lsum > 0.0);
@@ -513,14 +493,16 @@ __device__ void decide_node(const VArgs& a, int b, int i, const char* row, const
       double cum = lexcl;
       int tok = -1;
       double b0 = cum, b1 = cum;
+#pragma unroll 4
       for (int k = 0; k < 32; ++k) {
-        if (wv[k] > 0.0f) {
+        const float wk = sw[k];
+        if (wk > 0.0f) {
           tok = my0 + k;
           b0 = cum;
-          b1 = cum + (double)wv[k];
+          b1 = cum + (double)wk;
           if (!clamp2 && tgt < b1) break;
         }
-        cum += (double)wv[k];
+        cum += (double)wk;
       }
       if (tok < 0) tok = min(my0, V - 1);
       out.token = tok;
