@@ -286,7 +286,7 @@ __device__ void decide_node(const VArgs& a, int b, int i, const char* row, const
   // ---- probe tail: p, the overlap sum min(p, q~), which kept child each token is
   int tests = 0, near = 0;
   int accept = -1;
-  double W = 1.0;
+  double W = 1.0;  // mass of the residual the tests run against
   double q_child = -1.0;  // q~ of this lane's child token, -1 if not in the tail
   if (lane < kChildMax) L.qc[lane] = -1.0;
   wave_sync();
@@ -307,6 +307,133 @@ __device__ void decide_node(const VArgs& a, int b, int i, const char* row, const
     const double overlap = wave_sum(ov);
     wave_sync();
     if (lane < nc) q_child = L.qc[lane];
+    W = 1.0 - overlap;
+  }
+  // residual weight of this lane's child once the probe is rejected; the other kept
+  // children are tested in slot order, each lane's uniform drawn up front
+  const bool in_tail = q_child >= 0.0;
+  const double wc = in_tail ? (pc > q_child ? pc - q_child : 0.0) : pc;
+  const bool cand = lane < nc && lane != probe && ch_node >= 0;
+  const uint64_t cmask = ballot(cand);
+  const uint32_t j = 1u + (uint32_t)__builtin_popcountll(cmask & ((1ull << lane) - 1ull));
+  const float uc = cand ? uniform24(a.seed, 32u * depth + j, (uint32_t)b, a.step, kPurposeTest) : 1.0f;
+
+  // ---- the final residual (or bonus) sample is taken only if every test rejects, and
+  // then it runs against the residual with all of them rejected: located now, its
+  // chunk's re-read overlaps the tests. Inverse CDF of w / W in token-id order.
+  double Wf = W;
+  for (uint64_t m = cmask; m; m &= m - 1ull) Wf -= readlane_d(wc, __builtin_ctzll(m));
+  const float uf = uniform24(a.seed, depth, (uint32_t)b, a.step, kPurposeFinal);
+  const double tgt = (double)uf * Wf;
+  for (int ch = lane; ch < nch; ch += kWave) L.dfix[ch] = 0;
+  wave_sync();
+  // changes of mass relative to p: the probe's tail (clipped residual, or zero for a
+  // rejected child) and the rejected children outside it (zero). Fixed-point atomics
+  // keep the per-chunk sums independent of the order of arrival.
+  if (probe >= 0) {
+    for (int e = lane; e < nt; e += kWave) {
+      const int y = L.tid[e];
+      if (y < 0) continue;
+      const double p = L.tp[e], q = (double)L.tq[e];
+      const int slot = L.tslot[e];
+      const bool rej = slot >= 0 && ((cmask >> slot) & 1ull);
+      const double d = rej ? -p : -(p < q ? p : q);
+      atomicAdd((unsigned long long*)&L.dfix[y / kCH], (unsigned long long)__double2ll_rn(d * kFix));
+    }
+  }
+  const bool mine = cand && !in_tail;
+  if (mine) atomicAdd((unsigned long long*)&L.dfix[ch_tok / kCH], (unsigned long long)__double2ll_rn(-pc * kFix));
+  wave_sync();
+  // adjusted chunk masses, lane-blocked contiguous chunks
+  const int cpl = (nch + kWave - 1) / kWave;
+  const int c0 = lane * cpl, c1 = min(c0 + cpl, nch);
+  double lmass = 0.0;
+  for (int ch = c0; ch < c1; ++ch) {
+    double mch = L.pm[ch] * invS + (double)L.dfix[ch] * (1.0 / kFix);
+    if (mch < 0.0) mch = 0.0;
+    L.pm[ch] = mch;
+    lmass += mch;
+  }
+  const double incl = wave_incl_scan(lmass);
+  const double excl = incl - lmass;
+  // lane holding the crossing chunk; if rounding leaves none, the last lane with mass
+  const uint64_t hit = ballot(tgt < incl && lmass > 0.0);
+  int src = hit ? __builtin_ctzll(hit) : -1;
+  bool clamp = false;
+  if (src < 0) {
+    const uint64_t pos = ballot(lmass > 0.0);
+    src = pos ? 63 - __builtin_clzll(pos) : 0;
+    clamp = true;
+  }
+  int cstar = -1;
+  double before = 0.0;
+  if (lane == src) {
+    double cum = excl;
+    for (int ch = c0; ch < c1; ++ch) {
+      if (L.pm[ch] > 0.0) {
+        cstar = ch;
+        before = cum;
+        if (!clamp && tgt < cum + L.pm[ch]) break;
+      }
+      cum += L.pm[ch];
+    }
+    if (cstar < 0) cstar = c0 < nch ? c0 : nch - 1;
+  }
+  cstar = __shfl(cstar, src, kWave);
+  before = __shfl(before, src, kWave);
+  const int lo = cstar * kCH;
+  // re-read the chunk (issued now, consumed after the tests); lane l owns tokens
+  // [lo + 32 l, lo + 32 l + 32)
+  constexpr int esz = DT == VRT_BF16 ? 2 : 4;
+  constexpr int EPL = 16 / esz;
+  const int my0 = lo + lane * 32;
+  u32x4_t raw[32 / EPL];
+  static_for<32 / EPL>([&](auto q) {
+    const int e0 = my0 + q * EPL;
+    raw[q] = u32x4_t{0u, 0u, 0u, 0u};
+    if (e0 < V) raw[q] = *(const u32x4_t*)(row + (int64_t)e0 * esz);
+  });
+  // the changes that fall inside the chunk, listed for the owners of their tokens
+  int nitem = 0;
+  wave_sync();
+  if (probe >= 0) {
+    for (int e0 = 0; e0 < nt; e0 += kWave) {
+      const int e = e0 + lane;
+      bool inside = false;
+      int y = -1;
+      double d = 0.0;
+      if (e < nt) {
+        y = L.tid[e];
+        inside = y >= lo && y < lo + kCH;
+        if (inside) {
+          const double p = L.tp[e], q = (double)L.tq[e];
+          const int slot = L.tslot[e];
+          const bool rej = slot >= 0 && ((cmask >> slot) & 1ull);
+          d = rej ? -p : -(p < q ? p : q);
+        }
+      }
+      const uint64_t m = ballot(inside);
+      if (inside) {
+        const int at = nitem + (int)__builtin_popcountll(m & ((1ull << lane) - 1ull));
+        L.itok[at] = y;
+        L.idel[at] = d;
+      }
+      nitem += (int)__builtin_popcountll(m);
+    }
+  }
+  {
+    const bool inside = mine && ch_tok >= lo && ch_tok < lo + kCH;
+    const uint64_t m = ballot(inside);
+    if (inside) {
+      const int at = nitem + (int)__builtin_popcountll(m & ((1ull << lane) - 1ull));
+      L.itok[at] = ch_tok;
+      L.idel[at] = -pc;
+    }
+    nitem += (int)__builtin_popcountll(m);
+  }
+
+  // ---- the tests: probe first with min(1, p/q~), then the others under the residual
+  if (probe >= 0) {
     const double qp = readlane_d(q_child, probe);
     const double qs = qp < 0.0 ? 0.0 : qp;  // a probe outside its tail has q~ = 0
     const double ps = readlane_d(pc, probe);
@@ -315,18 +442,7 @@ __device__ void decide_node(const VArgs& a, int b, int i, const char* row, const
     ++tests;
     if (fabs((double)u0 - ratio) < kBand) ++near;
     if ((double)u0 < ratio) accept = __builtin_amdgcn_readlane(ch_node, probe);
-    W = 1.0 - overlap;
   }
-
-  // ---- recursive rejection of the other kept children in slot order; every lane
-  // draws its child's uniform up front
-  const bool in_tail = q_child >= 0.0;
-  const double wc = in_tail ? (pc > q_child ? pc - q_child : 0.0) : pc;
-  const bool cand = lane < nc && lane != probe && ch_node >= 0;
-  const uint64_t cmask = ballot(cand);
-  const uint32_t j = 1u + (uint32_t)__builtin_popcountll(cmask & ((1ull << lane) - 1ull));
-  const float uc = cand ? uniform24(a.seed, 32u * depth + j, (uint32_t)b, a.step, kPurposeTest) : 1.0f;
-  uint64_t rejected = 0;
   if (accept < 0) {
     for (uint64_t m = cmask; m; m &= m - 1ull) {
       const int k = __builtin_ctzll(m);
@@ -340,123 +456,14 @@ __device__ void decide_node(const VArgs& a, int b, int i, const char* row, const
         break;
       }
       W -= wk;
-      rejected |= 1ull << k;
     }
   }
 
-  // ---- nothing accepted: inverse-CDF sample of w / W in token-id order
+  // ---- nothing accepted: finish the final sample in the re-read chunk (W == Wf now)
   if (accept < 0) {
-    for (int ch = lane; ch < nch; ch += kWave) L.dfix[ch] = 0;
-    wave_sync();
-    // changes of mass relative to p: the probe's tail (clipped residual, or zero for a
-    // rejected child) and the rejected children outside it (zero). Fixed-point
-    // atomics keep the per-chunk sums independent of the order of arrival.
-    if (probe >= 0) {
-      for (int e = lane; e < nt; e += kWave) {
-        const int y = L.tid[e];
-        if (y < 0) continue;
-        const double p = L.tp[e], q = (double)L.tq[e];
-        const int slot = L.tslot[e];
-        const bool rej = slot >= 0 && ((rejected >> slot) & 1ull);
-        const double d = rej ? -p : -(p < q ? p : q);
-        atomicAdd((unsigned long long*)&L.dfix[y / kCH], (unsigned long long)__double2ll_rn(d * kFix));
-      }
-    }
-    const bool mine = ((rejected >> lane) & 1ull) && !in_tail;
-    if (mine) atomicAdd((unsigned long long*)&L.dfix[ch_tok / kCH], (unsigned long long)__double2ll_rn(-pc * kFix));
-    wave_sync();
-    // adjusted chunk masses, lane-blocked contiguous chunks
-    const int cpl = (nch + kWave - 1) / kWave;
-    const int c0 = lane * cpl, c1 = min(c0 + cpl, nch);
-    double lmass = 0.0;
-    for (int ch = c0; ch < c1; ++ch) {
-      double mch = L.pm[ch] * invS + (double)L.dfix[ch] * (1.0 / kFix);
-      if (mch < 0.0) mch = 0.0;
-      L.pm[ch] = mch;
-      lmass += mch;
-    }
-    const float uf = uniform24(a.seed, depth, (uint32_t)b, a.step, kPurposeFinal);
-    const double tgt = (double)uf * W;
-    const double incl = wave_incl_scan(lmass);
-    const double excl = incl - lmass;
-    // lane holding the crossing chunk; if rounding leaves none, the last lane with mass
-    const uint64_t hit = ballot(tgt < incl && lmass > 0.0);
-    int src = hit ? __builtin_ctzll(hit) : -1;
-    bool clamp = false;
-    if (src < 0) {
-      const uint64_t pos = ballot(lmass > 0.0);
-      src = pos ? 63 - __builtin_clzll(pos) : 0;
-      clamp = true;
-    }
-    int cstar = -1;
-    double before = 0.0;
-    if (lane == src) {
-      double cum = excl;
-      for (int ch = c0; ch < c1; ++ch) {
-        if (L.pm[ch] > 0.0) {
-          cstar = ch;
-          before = cum;
-          if (!clamp && tgt < cum + L.pm[ch]) break;
-        }
-        cum += L.pm[ch];
-      }
-      if (cstar < 0) cstar = c0 < nch ? c0 : nch - 1;
-    }
-    cstar = __shfl(cstar, src, kWave);
-    before = __shfl(before, src, kWave);
-    const int lo = cstar * kCH;
-    // the changes that fall inside the chunk, listed for the owners of their tokens
-    int nitem = 0;
-    wave_sync();
-    if (probe >= 0) {
-      for (int e0 = 0; e0 < nt; e0 += kWave) {
-        const int e = e0 + lane;
-        bool inside = false;
-        int y = -1;
-        double d = 0.0;
-        if (e < nt) {
-          y = L.tid[e];
-          inside = y >= lo && y < lo + kCH;
-          if (inside) {
-            const double p = L.tp[e], q = (double)L.tq[e];
-            const int slot = L.tslot[e];
-            const bool rej = slot >= 0 && ((rejected >> slot) & 1ull);
-            d = rej ? -p : -(p < q ? p : q);
-          }
-        }
-        const uint64_t m = ballot(inside);
-        if (inside) {
-          const int at = nitem + (int)__builtin_popcountll(m & ((1ull << lane) - 1ull));
-          L.itok[at] = y;
-          L.idel[at] = d;
-        }
-        nitem += (int)__builtin_popcountll(m);
-      }
-    }
+    float* sw = L.w + lane * 33;  // stride 33: conflict-free per-lane walks
     {
-      const bool inside = mine && ch_tok >= lo && ch_tok < lo + kCH;
-      const uint64_t m = ballot(inside);
-      if (inside) {
-        const int at = nitem + (int)__builtin_popcountll(m & ((1ull << lane) - 1ull));
-        L.itok[at] = ch_tok;
-        L.idel[at] = -pc;
-      }
-      nitem += (int)__builtin_popcountll(m);
-    }
-    // re-read the chunk; lane l owns tokens [lo + 32 l, lo + 32 l + 32), whose weights
-    // go to LDS (stride 33: conflict-free per-lane walks)
-    const int my0 = lo + lane * 32;
-    float* sw = L.w + lane * 33;
-    {
-      constexpr int esz = DT == VRT_BF16 ? 2 : 4;
-      constexpr int EPL = 16 / esz;
       const float invSf = (float)invS;
-      u32x4_t raw[32 / EPL];
-      static_for<32 / EPL>([&](auto q) {  // all loads first
-        const int e0 = my0 + q * EPL;
-        raw[q] = u32x4_t{0u, 0u, 0u, 0u};
-        if (e0 < V) raw[q] = *(const u32x4_t*)(row + (int64_t)e0 * esz);
-      });
       static_for<32 / EPL>([&](auto q) {
         static_for<EPL>([&](auto k) {
           float x;
@@ -540,14 +547,23 @@ __global__ __launch_bounds__(kVB) void k_vnode(const VArgs a) {
   extern __shared__ double s_dyn[];
   const DLds L = carve((char*)s_dyn, nch, c.TC);
   constexpr int NW = kVB / kWave;
+  __shared__ int s_next;  // next chunk to hand out
+  if (threadIdx.x == 0) s_next = NW;
   ChunkRegs<DT> cur, nxt;
   if (wave < nch) issue_chunk<DT>(row, wave * kCH, V, cur);
+  __syncthreads();
   if (wave == NW - 1) gather_node<DT>(a, b, i, nn, row, s_rec, L);
-  for (int ch = wave; ch < nch; ch += NW) {
-    if (ch + NW < nch) issue_chunk<DT>(row, (ch + NW) * kCH, V, nxt);
+  // chunks are handed out as waves become free (the gathering wave takes fewer); the
+  // next chunk is always in flight while the current one is reduced
+  for (int ch = wave; ch < nch;) {
+    int nx = 0;
+    if (lane_id() == 0) nx = atomicAdd(&s_next, 1);
+    nx = __builtin_amdgcn_readfirstlane(nx);
+    if (nx < nch) issue_chunk<DT>(row, nx * kCH, V, nxt);
     const float2 st = chunk_stats<DT>(cur, ch * kCH, V, c.c2, ch >= nfull);
     if (lane_id() == 0) s_cs[ch] = st;
     cur = nxt;
+    ch = nx;
   }
   __syncthreads();
   if (wave == 0) decide_node<DT>(a, b, i, row, s_cs, s_rec, L);

@@ -63,18 +63,6 @@ __device__ __forceinline__ float exp_rank(float x) {
   return __builtin_ldexpf(p, (int)k);
 }
 
-// inclusive prefix sum over lanes (Hillis-Steele)
-template <typename T>
-__device__ __forceinline__ T wave_incl_scan(T v) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const T t = __shfl_up(v, o, kWave);
-    if (lane >= o) v = v + t;
-  }
-  return v;
-}
-
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
 // Orders LDS accesses between the lanes of one wave (no block barrier: usable
@@ -230,6 +218,37 @@ __device__ __forceinline__ float wave_max(float v) {
   return wave_reduce(v, [](float x, float y) { return fmaxf(x, y); });
 }
 __device__ __forceinline__ int wave_sum_i(int v) { return wave_sum(v); }
+
+// Inclusive prefix sum over lanes: shifts by 1, 2, 4, 8 inside each row of 16 lanes
+// (DPP row_shr, zero fill), then the row totals broadcast into the following rows
+// (DPP row_bcast15 into rows 1 and 3, row_bcast31 into rows 2 and 3).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_fill0(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, false);
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_fill0(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint64_t lo = dpp_fill0<CTRL, ROWS>((uint32_t)u), hi = dpp_fill0<CTRL, ROWS>((uint32_t)(u >> 32));
+  return __longlong_as_double((long long)((hi << 32) | lo));
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_fill0(float v) {
+  return __uint_as_float(dpp_fill0<CTRL, ROWS>(__float_as_uint(v)));
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_fill0(int v) { return (int)dpp_fill0<CTRL, ROWS>((uint32_t)v); }
+
+template <typename T>
+__device__ __forceinline__ T wave_incl_scan(T v) {
+  v = v + dpp_fill0<0x111, 0xF>(v);
+  v = v + dpp_fill0<0x112, 0xF>(v);
+  v = v + dpp_fill0<0x114, 0xF>(v);
+  v = v + dpp_fill0<0x118, 0xF>(v);
+  v = v + dpp_fill0<0x142, 0xA>(v);
+  v = v + dpp_fill0<0x143, 0xC>(v);
+  return v;
+}
 
 // ---------------------------------------------------------------------------
 // Sorted key lists held in a wave's registers: PL keys per lane, position
