@@ -90,3 +90,45 @@ class Lib:
 
     def host(self, name):
         return self.views[name].cpu().numpy()
+
+
+def device_step(w, seed, step, dev):
+    """Every tree of workload w built and verified on the GPU, the way the benchmark
+    runs it: the device generator plays the draft model along the GPU's own frontier,
+    layer by layer, then the target model on the emitted trees. Returns the Lib."""
+    cfg = lib_config(w)
+    L = Lib(cfg, dev)
+    B, D, K, N, FP = w.B, w.D, w.K, L.N, L.FP
+    ld = row_ld(w)
+    tdt = torch.int16 if w.dtype == synth.BF16 else torch.float32
+    stream = torch.cuda.current_stream().cuda_stream
+    p = w.params()
+    zipf = torch.from_numpy(w.tables()).to(dev)
+    rk = [synth.root_key(w.gen_seed, b) for b in range(B)]
+    root_keys = torch.tensor([k - (1 << 64) if k >= (1 << 63) else k for k in rk], dtype=torch.int64,
+                             device=dev)
+    tree_of = torch.arange(B, dtype=torch.int32, device=dev)
+    rows = torch.zeros((B, FP, ld), dtype=tdt, device=dev)
+    keys_prev = root_keys.view(B, 1)
+    synth.rows_dev(p, zipf, keys_prev.reshape(-1), tree_of, rows[:, 0], synth.DRAFT, stream)
+    L.build_layer(0, rows, ld, seed, step)
+    for layer in range(1, D):
+        base = 0 if layer == 1 else K + (layer - 2) * FP * K  # the previous layer's candidates
+        keys = torch.zeros((B, FP), dtype=torch.int64, device=dev)
+        synth.frontier_keys_dev(B, K, base, keys_prev, L.views["front"], L.views["n_front"],
+                                L.views["cand_token"], keys, stream)
+        synth.rows_dev(p, zipf, keys.reshape(-1), tree_of.repeat_interleave(FP), rows.view(B * FP, ld),
+                       synth.DRAFT, stream)
+        L.build_layer(layer, rows, ld, seed, step)
+        keys_prev = keys
+    L.finish(seed, step)
+    del rows
+    node_keys = torch.zeros((B, N), dtype=torch.int64, device=dev)
+    synth.tree_keys_dev(B, N, root_keys, L.views["n_nodes"], L.views["node_token"],
+                        L.views["node_parent"], node_keys, stream)
+    target = torch.empty((B, N, ld), dtype=tdt, device=dev)
+    synth.rows_dev(p, zipf, node_keys.reshape(-1), tree_of.repeat_interleave(N), target.view(B * N, ld),
+                   synth.TARGET, stream)
+    L.verify(target, ld, seed, step, zero_stats=False)
+    del target
+    return L

@@ -555,14 +555,23 @@ __global__ __launch_bounds__(kVB) void k_vnode(const VArgs a) {
   if (wave == NW - 1) gather_node<DT>(a, b, i, nn, row, s_rec, L);
   // chunks are handed out as waves become free (the gathering wave takes fewer); the
   // next chunk is always in flight while the current one is reduced
-  for (int ch = wave; ch < nch;) {
+  // (two register sets in turn, so that no copy is needed)
+  auto next_chunk = [&]() {
     int nx = 0;
     if (lane_id() == 0) nx = atomicAdd(&s_next, 1);
-    nx = __builtin_amdgcn_readfirstlane(nx);
+    return __builtin_amdgcn_readfirstlane(nx);
+  };
+  for (int ch = wave; ch < nch;) {
+    int nx = next_chunk();
     if (nx < nch) issue_chunk<DT>(row, nx * kCH, V, nxt);
-    const float2 st = chunk_stats<DT>(cur, ch * kCH, V, c.c2, ch >= nfull);
-    if (lane_id() == 0) s_cs[ch] = st;
-    cur = nxt;
+    const float2 s0 = chunk_stats<DT>(cur, ch * kCH, V, c.c2, ch >= nfull);
+    if (lane_id() == 0) s_cs[ch] = s0;
+    ch = nx;
+    if (ch >= nch) break;
+    nx = next_chunk();
+    if (nx < nch) issue_chunk<DT>(row, nx * kCH, V, cur);
+    const float2 s1 = chunk_stats<DT>(nxt, ch * kCH, V, c.c2, ch >= nfull);
+    if (lane_id() == 0) s_cs[ch] = s1;
     ch = nx;
   }
   __syncthreads();
