@@ -28,7 +28,6 @@ namespace {
 constexpr int kVB = 256;        // threads per streaming block
 constexpr int kCH = 2048;       // elements per chunk (one wave at a time)
 constexpr int kChildMax = 32;   // K <= 30
-constexpr int kDW = 4;          // decide: waves (nodes) per block
 constexpr float kBand = 1e-6f;  // near-tie band reported in the stats
 constexpr double kFix = 1152921504606846976.0;  // 2^60: fixed point of the mass changes
 
@@ -39,9 +38,11 @@ struct VRec {
   int probe;  // slot of the probe child, -1 if none
   int nt;     // probe tail entries (0 without a probe)
   int depth;  // depth of the node (0 = root)
+  float u0, uf;  // draws of the probe test and of the final sample
   int node[kChildMax];
   int tok[kChildMax];
   float x[kChildMax];
+  float u[kChildMax];  // draw of each non-probe kept child's test
 };
 
 struct VArgs {
@@ -210,23 +211,42 @@ __device__ void gather_node(const VArgs& a, int b, int i, int nn, const char* ro
   const float x = tok >= 0 ? load_one<DT>(row, tok) : -INFINITY;
   const int nt = pl >= 0 ? min(max(a.t.tail_n[nb + i], 0), c.TC) : 0;
   const int64_t tb = (nb + i) * c.TC;
+  if (lane < kChildMax) L.qc[lane] = -1.0;
+  wave_sync();
   for (int e = lane; e < nt; e += kWave) {
     int y = a.t.tail_id[tb + e];
     if (y < 0 || y >= c.V) y = -1;
+    const float q = a.t.tail_q[tb + e];
     L.tid[e] = y;
-    L.tq[e] = a.t.tail_q[tb + e];
+    L.tq[e] = q;
     L.tp[e] = y >= 0 ? (double)load_one<DT>(row, y) : -INFINITY;  // the logit for now
+    // which kept child (slot) has this token; that child's q~
+    int slot = -1;
+    for (int k = 0; k < nc; ++k)
+      if (slot < 0 && y >= 0 && __builtin_amdgcn_readlane(tok, k) == y) slot = k;
+    L.tslot[e] = slot;
+    if (slot >= 0) L.qc[slot] = q;
   }
+  // the draws (keyed by depth and test index): probe test j = 0, the other kept
+  // children j = 1, 2, .. in slot order, the final sample
+  const uint32_t depth = (uint32_t)min(max(a.t.node_depth[nb + i], 0), 63);
+  const bool cand = lane < nc && lane != pl && node >= 0;
+  const uint64_t cmask = ballot(cand);
+  const uint32_t j = 1u + (uint32_t)__builtin_popcountll(cmask & ((1ull << lane) - 1ull));
+  const float u = cand ? uniform24(a.seed, 32u * depth + j, (uint32_t)b, a.step, kPurposeTest) : 1.0f;
   if (lane < kChildMax) {
     r.node[lane] = node;
     r.tok[lane] = tok;
     r.x[lane] = x;
+    r.u[lane] = u;
   }
   if (lane == 0) {
     r.nc = nc;
     r.probe = pl;
     r.nt = nt;
-    r.depth = min(max(a.t.node_depth[nb + i], 0), 63);
+    r.depth = (int)depth;
+    r.u0 = uniform24(a.seed, 32u * depth, (uint32_t)b, a.step, kPurposeTest);
+    r.uf = uniform24(a.seed, depth, (uint32_t)b, a.step, kPurposeFinal);
   }
 }
 
@@ -243,13 +263,13 @@ __device__ void decide_node(const VArgs& a, int b, int i, const char* row, const
   const float c2 = c.c2;
   const int64_t nb = (int64_t)b * c.N;
   const int nc = R.nc, probe = R.probe, nt = R.nt;
-  const uint32_t depth = (uint32_t)R.depth;
   int r_node = -1, r_tok = -1;
-  float r_x = -INFINITY;
+  float r_x = -INFINITY, r_u = 1.0f;
   if (lane < kChildMax) {
     r_node = R.node[lane];
     r_tok = R.tok[lane];
     r_x = R.x[lane];
+    r_u = R.u[lane];
   }
   constexpr int kCPL = 8;  // chunks per lane: V <= 2^20
   float2 st[kCPL];
@@ -287,9 +307,7 @@ __device__ void decide_node(const VArgs& a, int b, int i, const char* row, const
   int tests = 0, near = 0;
   int accept = -1;
   double W = 1.0;  // mass of the residual the tests run against
-  double q_child = -1.0;  // q~ of this lane's child token, -1 if not in the tail
-  if (lane < kChildMax) L.qc[lane] = -1.0;
-  wave_sync();
+  double q_child = lane < nc ? L.qc[lane] : -1.0;  // q~ of this lane's child, -1: not in the tail
   if (probe >= 0) {
     double ov = 0.0;
     for (int e = lane; e < nt; e += kWave) {
@@ -298,15 +316,9 @@ __device__ void decide_node(const VArgs& a, int b, int i, const char* row, const
       const double q = (double)L.tq[e];
       L.tp[e] = p;
       ov += fmin(p, q);
-      int slot = -1;
-      for (int k = 0; k < nc; ++k)
-        if (slot < 0 && y >= 0 && __builtin_amdgcn_readlane(ch_tok, k) == y) slot = k;
-      L.tslot[e] = slot;
-      if (slot >= 0) L.qc[slot] = q;
     }
     const double overlap = wave_sum(ov);
     wave_sync();
-    if (lane < nc) q_child = L.qc[lane];
     W = 1.0 - overlap;
   }
   // residual weight of this lane's child once the probe is rejected; the other kept
@@ -315,15 +327,14 @@ __device__ void decide_node(const VArgs& a, int b, int i, const char* row, const
   const double wc = in_tail ? (pc > q_child ? pc - q_child : 0.0) : pc;
   const bool cand = lane < nc && lane != probe && ch_node >= 0;
   const uint64_t cmask = ballot(cand);
-  const uint32_t j = 1u + (uint32_t)__builtin_popcountll(cmask & ((1ull << lane) - 1ull));
-  const float uc = cand ? uniform24(a.seed, 32u * depth + j, (uint32_t)b, a.step, kPurposeTest) : 1.0f;
+  const float uc = r_u;
 
   // ---- the final residual (or bonus) sample is taken only if every test rejects, and
   // then it runs against the residual with all of them rejected: located now, its
   // chunk's re-read overlaps the tests. Inverse CDF of w / W in token-id order.
   double Wf = W;
   for (uint64_t m = cmask; m; m &= m - 1ull) Wf -= readlane_d(wc, __builtin_ctzll(m));
-  const float uf = uniform24(a.seed, depth, (uint32_t)b, a.step, kPurposeFinal);
+  const float uf = R.uf;
   const double tgt = (double)uf * Wf;
   for (int ch = lane; ch < nch; ch += kWave) L.dfix[ch] = 0;
   wave_sync();
@@ -438,7 +449,7 @@ __device__ void decide_node(const VArgs& a, int b, int i, const char* row, const
     const double qs = qp < 0.0 ? 0.0 : qp;  // a probe outside its tail has q~ = 0
     const double ps = readlane_d(pc, probe);
     const double ratio = ps / qs;
-    const float u0 = uniform24(a.seed, 32u * depth, (uint32_t)b, a.step, kPurposeTest);
+    const float u0 = R.u0;
     ++tests;
     if (fabs((double)u0 - ratio) < kBand) ++near;
     if ((double)u0 < ratio) accept = __builtin_amdgcn_readlane(ch_node, probe);
