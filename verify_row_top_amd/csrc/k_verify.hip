@@ -2,7 +2,7 @@
 //
 // k_vnode: one 256-thread block per (node row, tree).
 //   - The four waves stream the node's target row from HBM once, in 2048-element
-//     chunks (four 16-byte loads per lane, 8 bf16 each, the next chunk in flight),
+//     chunks taken two at a time (four 16-byte loads per lane per chunk, 8 bf16 each),
 //     keeping per chunk fl(max*c2) and the sum of exp2(x*c2 - fl(max*c2)) in LDS,
 //     where c2 = log2(e)/T. Every element costs one conversion, a third of a max3,
 //     one fma, one native exp2 and one add.
@@ -86,41 +86,68 @@ __device__ __forceinline__ void issue_chunk(const char* row, int lo, int V, Chun
   });
 }
 
-// (fl(max*c2), sum exp2(x*c2 - fl(max*c2))) of a chunk; `ragged` masks elements >= V.
+// (fl(max*c2), sum exp2(x*c2 - fl(max*c2))) of two chunks at once (their reductions
+// interleave, so no lane-exchange step waits on the one before it); `ragged` masks
+// elements >= V.
 template <int DT>
-__device__ __forceinline__ float2 chunk_stats(const ChunkRegs<DT>& r, int lo, int V, float c2, bool ragged) {
+__device__ __forceinline__ void chunk_stats2(const ChunkRegs<DT>& ra, const ChunkRegs<DT>& rb, int loa,
+                                             int lob, int V, float c2, bool rga, bool rgb, float2& oa,
+                                             float2& ob) {
   using CR = ChunkRegs<DT>;
   const int lane = lane_id();
-  float x[32];
-  static_for<CR::NL>([&](auto q) {
-    static_for<4>([&](auto k) {
-      if constexpr (DT == VRT_BF16) {
-        x[q * 8 + 2 * k] = bf16_lo(r.w[q][(int)k]);
-        x[q * 8 + 2 * k + 1] = bf16_hi(r.w[q][(int)k]);
-      } else {
-        x[q * 4 + k] = __uint_as_float(r.w[q][(int)k]);
-      }
-    });
-  });
-  if (ragged) {
+  float xa[32], xb[32];
+  auto unpack = [&](const ChunkRegs<DT>& r, float (&x)[32], int lo, bool ragged) {
     static_for<CR::NL>([&](auto q) {
-      static_for<CR::EPL>([&](auto k) {
-        if (lo + (q * kWave + lane) * CR::EPL + k >= V) x[q * CR::EPL + k] = -INFINITY;
+      static_for<4>([&](auto k) {
+        if constexpr (DT == VRT_BF16) {
+          x[q * 8 + 2 * k] = bf16_lo(r.w[q][(int)k]);
+          x[q * 8 + 2 * k + 1] = bf16_hi(r.w[q][(int)k]);
+        } else {
+          x[q * 4 + k] = __uint_as_float(r.w[q][(int)k]);
+        }
       });
     });
-  }
-  float m = x[0];
+    if (ragged) {
+      static_for<CR::NL>([&](auto q) {
+        static_for<CR::EPL>([&](auto k) {
+          if (lo + (q * kWave + lane) * CR::EPL + k >= V) x[q * CR::EPL + k] = -INFINITY;
+        });
+      });
+    }
+  };
+  unpack(ra, xa, loa, rga);
+  unpack(rb, xb, lob, rgb);
+  float ma = xa[0], mb = xb[0];
 #pragma unroll
-  for (int k = 1; k < 32; ++k) m = fmaxf(m, x[k]);
-  m = wave_max(m);
-  const float mc = m * c2;
-  float s = 0.0f;
-  if (m > -INFINITY) {
-#pragma unroll
-    for (int k = 0; k < 32; ++k) s += fast_exp2(__builtin_fmaf(x[k], c2, -mc));
+  for (int k = 1; k < 32; ++k) {
+    ma = fmaxf(ma, xa[k]);
+    mb = fmaxf(mb, xb[k]);
   }
-  s = wave_sum(s);
-  return make_float2(mc, s);
+  auto mx = [](float x, float y) { return fmaxf(x, y); };
+  ma = mx(ma, xchg<1>(ma)); mb = mx(mb, xchg<1>(mb));
+  ma = mx(ma, xchg<2>(ma)); mb = mx(mb, xchg<2>(mb));
+  ma = mx(ma, xchg<4>(ma)); mb = mx(mb, xchg<4>(mb));
+  ma = mx(ma, xchg<8>(ma)); mb = mx(mb, xchg<8>(mb));
+  ma = mx(ma, xchg<16>(ma)); mb = mx(mb, xchg<16>(mb));
+  ma = mx(ma, xchg<32>(ma)); mb = mx(mb, xchg<32>(mb));
+  const float mca = ma * c2, mcb = mb * c2;
+  float sa = 0.0f, sb = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    sa += fast_exp2(__builtin_fmaf(xa[k], c2, -mca));
+    sb += fast_exp2(__builtin_fmaf(xb[k], c2, -mcb));
+  }
+  // a chunk whose maximum is -inf (all masked) summed exp2(-inf + inf): it holds 0
+  sa = ma > -INFINITY ? sa : 0.0f;
+  sb = mb > -INFINITY ? sb : 0.0f;
+  sa = sa + xchg<1>(sa); sb = sb + xchg<1>(sb);
+  sa = sa + xchg<2>(sa); sb = sb + xchg<2>(sb);
+  sa = sa + xchg<4>(sa); sb = sb + xchg<4>(sb);
+  sa = sa + xchg<8>(sa); sb = sb + xchg<8>(sb);
+  sa = sa + xchg<16>(sa); sb = sb + xchg<16>(sb);
+  sa = sa + xchg<32>(sa); sb = sb + xchg<32>(sb);
+  oa = make_float2(mca, sa);
+  ob = make_float2(mcb, sb);
 }
 
 template <int DT>
@@ -558,32 +585,28 @@ __global__ __launch_bounds__(kVB) void k_vnode(const VArgs a) {
   extern __shared__ double s_dyn[];
   const DLds L = carve((char*)s_dyn, nch, c.TC);
   constexpr int NW = kVB / kWave;
-  __shared__ int s_next;  // next chunk to hand out
+  __shared__ int s_next;  // next pair of chunks to hand out
   if (threadIdx.x == 0) s_next = NW;
-  ChunkRegs<DT> cur, nxt;
-  if (wave < nch) issue_chunk<DT>(row, wave * kCH, V, cur);
   __syncthreads();
   if (wave == NW - 1) gather_node<DT>(a, b, i, nn, row, s_rec, L);
-  // chunks are handed out as waves become free (the gathering wave takes fewer); the
-  // next chunk is always in flight while the current one is reduced
-  // (two register sets in turn, so that no copy is needed)
-  auto next_chunk = [&]() {
+  // pairs of chunks are handed out as waves become free (the gathering wave takes
+  // fewer); both chunks' loads are in flight together
+  const int npair = (nch + 1) / 2;
+  for (int pr = wave; pr < npair;) {
+    const int ca = 2 * pr, cb = 2 * pr + 1;
+    ChunkRegs<DT> ra, rb;
+    issue_chunk<DT>(row, ca * kCH, V, ra);
+    issue_chunk<DT>(row, cb * kCH, V, rb);  // past the row end: all -inf, not stored
     int nx = 0;
     if (lane_id() == 0) nx = atomicAdd(&s_next, 1);
-    return __builtin_amdgcn_readfirstlane(nx);
-  };
-  for (int ch = wave; ch < nch;) {
-    int nx = next_chunk();
-    if (nx < nch) issue_chunk<DT>(row, nx * kCH, V, nxt);
-    const float2 s0 = chunk_stats<DT>(cur, ch * kCH, V, c.c2, ch >= nfull);
-    if (lane_id() == 0) s_cs[ch] = s0;
-    ch = nx;
-    if (ch >= nch) break;
-    nx = next_chunk();
-    if (nx < nch) issue_chunk<DT>(row, nx * kCH, V, cur);
-    const float2 s1 = chunk_stats<DT>(nxt, ch * kCH, V, c.c2, ch >= nfull);
-    if (lane_id() == 0) s_cs[ch] = s1;
-    ch = nx;
+    nx = __builtin_amdgcn_readfirstlane(nx);
+    float2 sa, sb;
+    chunk_stats2<DT>(ra, rb, ca * kCH, cb * kCH, V, c.c2, ca >= nfull, cb >= nfull, sa, sb);
+    if (lane_id() == 0) {
+      s_cs[ca] = sa;
+      if (cb < nch) s_cs[cb] = sb;
+    }
+    pr = nx;
   }
   __syncthreads();
   if (wave == 0) decide_node<DT>(a, b, i, row, s_cs, s_rec, L);
