@@ -1,7 +1,7 @@
 // Tree verification (RheoSampling, key design 3) on gfx950, in two kernels.
 //
-// k_vnode: one 256-thread block per (node row, tree).
-//   - The four waves stream the node's target row from HBM once, in 2048-element
+// k_vnode: one 512-thread block per (node row, tree).
+//   - The eight waves stream the node's target row from HBM once, in 2048-element
 //     chunks taken two at a time (four 16-byte loads per lane per chunk, 8 bf16 each),
 //     keeping per chunk fl(max*c2) and the sum of exp2(x*c2 - fl(max*c2)) in LDS,
 //     where c2 = log2(e)/T. Every element costs one conversion, a third of a max3,
@@ -25,7 +25,7 @@
 namespace vrt {
 namespace {
 
-constexpr int kVB = 256;        // threads per streaming block
+constexpr int kVB = 512;        // threads per streaming block
 constexpr int kCH = 2048;       // elements per chunk (one wave at a time)
 constexpr int kChildMax = 32;   // K <= 30
 constexpr float kBand = 1e-6f;  // near-tie band reported in the stats
