@@ -105,6 +105,78 @@ __device__ __forceinline__ float max3n(float a, float b, float c) {  // NaN-prop
   return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
 }
 
+// One wave's load of segment g of a row: load q of this lane covers elements
+// [seg0 + (q*64 + lane)*EPL, +EPL), all 16 loads in flight at once; elements at or
+// past V read as -inf.
+template <int DT>
+__device__ __forceinline__ void load_segment(const char* row, int g, int V, u32x4_t (&d)[kSegLoads]) {
+  constexpr bool BF = DT == VRT_BF16;
+  constexpr int esz = BF ? 2 : 4;
+  constexpr int EPL = 16 / esz;
+  const int lane = lane_id();
+  const int seg0 = g * seg_elems<DT>();
+  static_for<kSegLoads>([&](auto q) {
+    const int e0 = seg0 + (q * kWave + lane) * EPL;
+    const uint32_t ninf = BF ? 0xFF80FF80u : 0xFF800000u;
+    u32x4_t v = {ninf, ninf, ninf, ninf};
+    if (e0 < V) v = __builtin_nontemporal_load((const u32x4_t*)(row + (int64_t)e0 * esz));
+    d[q] = v;
+  });
+  if (V - seg0 < seg_elems<DT>()) {  // the row's last segment: mask a straddling load
+    static_for<kSegLoads>([&](auto q) {
+      const int e0 = seg0 + (q * kWave + lane) * EPL;
+      if (e0 < V && e0 + EPL > V) {
+        static_for<EPL>([&](auto e) {
+          if (e0 + e >= V) {
+            if constexpr (BF)
+              d[q][e >> 1] = (e & 1) ? ((d[q][e >> 1] & 0xFFFFu) | 0xFF800000u)
+                                     : ((d[q][e >> 1] & 0xFFFF0000u) | 0xFF80u);
+            else
+              d[q][(int)e] = 0xFF800000u;
+          }
+        });
+      }
+    });
+  }
+}
+
+// Maximum of each group (one lane's load), NaN-propagating so that one class test per
+// group flags a non-finite row.
+template <int DT>
+__device__ __forceinline__ void group_maxima(const u32x4_t (&d)[kSegLoads], float (&gm)[kSegLoads]) {
+  static_for<kSegLoads>([&](auto q) {
+    if constexpr (DT == VRT_BF16) {
+      auto lo = [&](int i) { return bf16_lo(d[q][i]); };
+      auto hi = [&](int i) { return bf16_hi(d[q][i]); };
+      const float t1 = max3n(lo(0), hi(0), lo(1));
+      const float t2 = max3n(hi(1), lo(2), hi(2));
+      gm[q] = __builtin_elementwise_maximum(max3n(lo(3), hi(3), t1), t2);
+    } else {
+      auto f = [&](int i) { return __uint_as_float(d[q][i]); };
+      gm[q] = __builtin_elementwise_maximum(max3n(f(0), f(1), f(2)), f(3));
+    }
+  });
+}
+
+// Order-preserving image of a row value: 16 bits for bf16 values (the low half of the
+// fp32 image carries nothing), 32 bits for fp32; NaN maps to 0. value_of inverts it.
+template <int DT>
+using Img = std::conditional_t<DT == VRT_BF16, uint16_t, uint32_t>;
+template <int DT>
+__device__ __forceinline__ uint32_t img_of(float x) {
+  if constexpr (DT == VRT_BF16) return ord32(x) >> 16;
+  else return ord32(x);
+}
+template <int DT>
+__device__ __forceinline__ float value_of(uint32_t img) {
+  if constexpr (DT == VRT_BF16) {
+    const uint32_t h = (img & 0x8000u) ? (img & 0x7FFFu) : (~img & 0xFFFFu);
+    return __uint_as_float(h << 16);
+  } else {
+    return unord32(img);
+  }
+}
+
 // Per-wave LDS of the segment selection.
 template <int DT, int PL>
 struct SegLds {
@@ -146,46 +218,11 @@ __device__ __forceinline__ void seg_select(const char* row, int g, int V, SegLds
   const int vlim = V - seg0;  // elements of this segment inside the row
   const uint64_t lt_mask = (1ull << lane) - 1ull;
 
-  // 1. loads; elements at or past V read as -inf
+  // 1. loads (the segment lives in registers); 2. group maxima
   u32x4_t d[kSegLoads];
-  static_for<kSegLoads>([&](auto q) {
-    const int e0 = seg0 + (q * kWave + lane) * EPL;
-    const uint32_t ninf = BF ? 0xFF80FF80u : 0xFF800000u;
-    u32x4_t v = {ninf, ninf, ninf, ninf};
-    if (e0 < V) v = __builtin_nontemporal_load((const u32x4_t*)(row + (int64_t)e0 * esz));
-    d[q] = v;
-  });
-  if (vlim < seg_elems<DT>()) {  // the row's last segment: mask a straddling load
-    static_for<kSegLoads>([&](auto q) {
-      const int e0 = seg0 + (q * kWave + lane) * EPL;
-      if (e0 < V && e0 + EPL > V) {
-        static_for<EPL>([&](auto e) {
-          if (e0 + e >= V) {
-            if constexpr (BF)
-              d[q][e >> 1] = (e & 1) ? ((d[q][e >> 1] & 0xFFFFu) | 0xFF800000u)
-                                     : ((d[q][e >> 1] & 0xFFFF0000u) | 0xFF80u);
-            else
-              d[q][(int)e] = 0xFF800000u;
-          }
-        });
-      }
-    });
-  }
-
-  // 2. group maxima, the non-finite check, the lane's LV largest, the threshold
+  load_segment<DT>(row, g, V, d);
   float gm[kSegLoads];
-  static_for<kSegLoads>([&](auto q) {
-    if constexpr (BF) {
-      auto lo = [&](int i) { return bf16_lo(d[q][i]); };
-      auto hi = [&](int i) { return bf16_hi(d[q][i]); };
-      const float t1 = max3n(lo(0), hi(0), lo(1));
-      const float t2 = max3n(hi(1), lo(2), hi(2));
-      gm[q] = __builtin_elementwise_maximum(max3n(lo(3), hi(3), t1), t2);
-    } else {
-      auto f = [&](int i) { return __uint_as_float(d[q][i]); };
-      gm[q] = __builtin_elementwise_maximum(max3n(f(0), f(1), f(2)), f(3));
-    }
-  });
+  group_maxima<DT>(d, gm);
   bool nf = false;
   static_for<kSegLoads>([&](auto q) { nf |= __builtin_amdgcn_classf(gm[q], 0x203); });  // NaN, +inf
   bad |= ballot(nf) != 0ull;
@@ -213,15 +250,7 @@ __device__ __forceinline__ void seg_select(const char* row, int g, int V, SegLds
   if constexpr (BF) thr = pre ? (pre << 16) - 1u : 0u;
   else thr = pre ? ((uint64_t)pre << 32) - 1ull : 0ull;
   // the value of the threshold (a pre-test on values; exact for bf16 images too)
-  auto value_of = [&](uint32_t img) -> float {
-    if constexpr (BF) {
-      const uint32_t h = (img & 0x8000u) ? (img & 0x7FFFu) : (~img & 0xFFFFu);
-      return __uint_as_float(h << 16);
-    } else {
-      return unord32(img);
-    }
-  };
-  float thr_f = pre ? value_of(pre) : -INFINITY;
+  float thr_f = pre ? value_of<DT>(pre) : -INFINITY;
 
   K work[QL];
   static_for<QL>([&](auto s) { work[s] = 0; });
@@ -313,7 +342,7 @@ __device__ __forceinline__ void seg_select(const char* row, int g, int V, SegLds
       const K t = shflk(work[(N - 1) % QL], (N - 1) / QL);
       if (t) {
         thr = t;
-        if constexpr (BF) thr_f = value_of(t >> 16);
+        if constexpr (BF) thr_f = value_of<DT>(t >> 16);
         else thr_f = sup_key_val(t);
       }
     }
@@ -329,7 +358,7 @@ __device__ __forceinline__ void seg_select(const char* row, int g, int V, SegLds
   auto row_key = [&](K k) -> uint64_t {
     if constexpr (BF) {
       if (!k) return 0ull;
-      return sup_key(value_of(k >> 16), (uint32_t)(seg0 + (int)(0xFFFFu - (k & 0xFFFFu))));
+      return sup_key(value_of<DT>(k >> 16), (uint32_t)(seg0 + (int)(0xFFFFu - (k & 0xFFFFu))));
     } else {
       return k;
     }
@@ -348,6 +377,236 @@ __device__ __forceinline__ void seg_select(const char* row, int g, int V, SegLds
     static_for<PL>([&](auto s) { cur[s] = ost[lane * PL + s]; });
     wave_sync();
   }
+}
+
+// ---------------------------------------------------------------------------
+// Row-wide selection (the usual path for short lists): one threshold for the whole
+// row instead of one list per segment.
+constexpr int kFastGroups = 512;  // candidate groups taken (one per thread of the block)
+
+template <int DT, int PL>
+struct FastLds {
+  static constexpr int LV = PL <= 2 ? 4 : 2 * PL;      // candidates per lane and segment
+  static constexpr int QL = 2 * PL;                    // usual sort: 2N keys
+  static constexpr int QL2 = 4 * PL;                   // larger sort: 4N keys
+  static constexpr int GMAX = DT == VRT_BF16 ? 24 : 12;  // segments the path takes
+  Img<DT> gimg[GMAX][kSegLoads * kWave];  // group maxima images, [g][q*64 + lane]
+  Img<DT> cimg[GMAX * kWave * LV];        // every lane's LV largest group maxima
+  int glist[kFastGroups];                 // groups that reach the threshold
+  uint64_t keys[QL2 * kWave];             // row keys of the elements that reach it
+  int hist[256];
+  int sel[2];
+  int wtot[16];
+  int ngl, nk, bad;
+};
+
+// The row's top TC keys (value desc, token id asc) into s_sup (positions < N, sorted,
+// zero-padded), by all waves of the block:
+//  A. each wave loads its segments (16 KB each, all loads in flight), keeps every
+//     group's maximum (image, in LDS) and each lane's LV largest group maxima;
+//  B. the TC-th largest of all these candidates, t (bitwise search, one block-wide
+//     count per bit), is reached by at least TC distinct elements, so no element below
+//     it is among the row's TC best; on the workloads' rows it is the row's TC-th
+//     value itself;
+//  C. the groups whose maximum reaches t (about TC of them) are listed;
+//  D. each thread re-reads one listed group (16 bytes) and stages the exact keys of its
+//     elements that reach t;
+//  E. wave 0 sorts the staged keys (bitonic network over lane exchanges).
+// Returns 0 on success, 1 for a non-finite row, 2 when more groups or keys reach the
+// threshold than the path holds (ties, flat or tiny rows): the caller then takes the
+// per-segment path. The result is uniform over the block.
+template <int DT, int PL>
+__device__ int row_select_fast(const char* row, int G, int V, int TC, FastLds<DT, PL>& F,
+                               uint64_t* s_sup, int& n_sup) {
+  using FL = FastLds<DT, PL>;
+  constexpr bool BF = DT == VRT_BF16;
+  constexpr int N = PL * kWave;
+  constexpr int LV = FL::LV;
+  constexpr int QL = FL::QL;
+  constexpr int SW = sel_waves<PL>();
+  constexpr int NT = SW * kWave;
+  constexpr int RB = BF ? 16 : 32;
+  constexpr int esz = BF ? 2 : 4;
+  constexpr int EPL = 16 / esz;
+  constexpr int KPT = (FL::GMAX * kWave * LV + NT - 1) / NT;  // candidates per thread
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = lane_id();
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
+  if (tid == 0) {
+    F.ngl = 0;
+    F.nk = 0;
+    F.bad = 0;
+  }
+  if (tid < 256) F.hist[tid] = 0;
+  __syncthreads();
+
+  // A.
+  bool nf = false;
+  for (int g = wave; g < G; g += SW) {
+    u32x4_t d[kSegLoads];
+    load_segment<DT>(row, g, V, d);
+    float gm[kSegLoads];
+    group_maxima<DT>(d, gm);
+    float lv[LV];
+    static_for<LV>([&](auto s) { lv[s] = -INFINITY; });
+    static_for<kSegLoads>([&](auto q) {
+      nf |= __builtin_amdgcn_classf(gm[q], 0x203);  // NaN, +inf
+      F.gimg[g][q * kWave + lane] = (Img<DT>)img_of<DT>(gm[q]);
+      float x = gm[q];
+      static_for<LV>([&](auto s) {
+        const float h = fmaxf(lv[s], x);
+        x = fminf(lv[s], x);
+        lv[s] = h;
+      });
+    });
+    static_for<LV>([&](auto s) { F.cimg[(g * kWave + lane) * LV + s] = (Img<DT>)img_of<DT>(lv[s]); });
+  }
+  if (ballot(nf) != 0ull && lane == 0) F.bad = 1;
+  __syncthreads();
+  if (F.bad) return 1;
+
+  // B. (a radix select in bytes: a histogram per byte of the image, from the top)
+  const int C = G * kWave * LV;
+  uint32_t cand[KPT];
+  static_for<KPT>([&](auto k) {
+    const int idx = tid + k * NT;
+    cand[k] = idx < C ? (uint32_t)F.cimg[idx] : 0u;
+  });
+  uint32_t pre = 0u;   // image bits fixed so far (the high ones)
+  int above = 0;       // candidates whose fixed bits exceed pre's
+  static_for<RB / 8>([&](auto lvl) {
+    constexpr int sh = RB - 8 * (lvl + 1);
+    // count the candidates that agree with pre above this byte, by this byte
+    static_for<KPT>([&](auto k) {
+      const uint32_t v = cand[k];
+      const bool match = ((uint64_t)(v ^ pre) >> (sh + 8)) == 0u;
+      if (v != 0u && match) atomicAdd(&F.hist[(v >> sh) & 0xFF], 1);
+    });
+    __syncthreads();
+    // wave 0 finds the byte value b: the largest with above + #(byte >= b) >= TC
+    if (wave == 0) {
+      int h[4];
+      static_for<4>([&](auto i) { h[i] = F.hist[255 - (lane * 4 + i)]; });  // descending bytes
+      const int ls = h[0] + h[1] + h[2] + h[3];
+      const int incl = wave_incl_scan(ls) + above;
+      int pick = -1, cum = incl - ls;
+      static_for<4>([&](auto i) {
+        cum += h[i];
+        if (pick < 0 && cum >= TC) pick = 255 - (lane * 4 + i);
+      });
+      const uint64_t has = ballot(pick >= 0);
+      if (has) {
+        const int src_l = __builtin_ctzll(has);
+        const int bsel = __shfl(pick, src_l, kWave);
+        // candidates strictly above byte bsel: everything before it in descending order
+        int before = 0;
+        static_for<4>([&](auto i) { before += (255 - (lane * 4 + i)) > bsel ? h[i] : 0; });
+        before = wave_sum_i(before);
+        if (lane == 0) {
+          F.sel[0] = bsel;
+          F.sel[1] = above + before;
+        }
+      } else if (lane == 0) {
+        F.sel[0] = -1;
+      }
+    }
+    __syncthreads();
+    const int bsel = F.sel[0];
+    if (bsel >= 0) {
+      pre |= (uint32_t)bsel << sh;
+      above = F.sel[1];
+    }
+    // clear the histogram for the next byte (the reads above are done: one more barrier)
+    if (tid < 256) F.hist[tid] = 0;
+    __syncthreads();
+    if (bsel < 0) pre = 0xFFFFFFFFu;  // marks "fewer than TC candidates"
+  });
+  if (pre == 0u || pre == 0xFFFFFFFFu) return 2;  // fewer than TC candidates carry a value
+
+  // C. (each thread scans a contiguous run of groups; the list stays in group order)
+  const int ng = G * kSegLoads * kWave;
+  constexpr int EPT = (FL::GMAX * kSegLoads * kWave + NT - 1) / NT;  // groups per thread
+  static_assert(EPT <= 64, "a thread's groups fit one 64-bit mask");
+  const int k0 = tid * EPT;
+  uint64_t hits = 0ull;
+  static_for<EPT>([&](auto i) {
+    const int k = k0 + i;
+    if (k < ng && (uint32_t)((const Img<DT>*)F.gimg)[k] >= pre) hits |= 1ull << i;
+  });
+  const int nh = __builtin_popcountll(hits);
+  const int incl = wave_incl_scan(nh);
+  if (lane == kWave - 1) F.wtot[wave] = incl;
+  __syncthreads();
+  int off = incl - nh;
+  int total = 0;
+  static_for<SW>([&](auto w) {
+    const int t = F.wtot[w];
+    off += (int)w < wave ? t : 0;
+    total += t;
+  });
+  for (uint64_t m = hits; m; m &= m - 1ull) {
+    if (off < kFastGroups) F.glist[off] = k0 + __builtin_ctzll(m);
+    ++off;
+  }
+  if (total > kFastGroups) return 2;
+  const int ngl = total;
+  __syncthreads();
+
+  // D.
+  {
+    const bool has = tid < ngl;
+    u32x4_t gw = {0u, 0u, 0u, 0u};
+    int e0 = V;
+    if (has) {
+      const int k = F.glist[tid];
+      const int g = k / (kSegLoads * kWave), gi = k % (kSegLoads * kWave);
+      e0 = g * seg_elems<DT>() + gi * EPL;
+      if (e0 < V) gw = *(const u32x4_t*)(row + (int64_t)e0 * esz);
+    }
+    static_for<EPL>([&](auto e) {
+      float x;
+      if constexpr (BF) x = (e & 1) ? bf16_hi(gw[e >> 1]) : bf16_lo(gw[e >> 1]);
+      else x = __uint_as_float(gw[(int)e]);
+      const int id = e0 + e;
+      const bool keep = has && id < V && img_of<DT>(x) >= pre;
+      const uint64_t m = ballot(keep);
+      int at = 0;
+      if (lane == 0 && m) at = atomicAdd(&F.nk, __builtin_popcountll(m));
+      at = __shfl(at, 0, kWave) + __builtin_popcountll(m & lt_mask);
+      if (keep && at < FL::QL2 * kWave) F.keys[at] = sup_key(x, (uint32_t)id);
+    });
+  }
+  __syncthreads();
+  const int nk = F.nk;
+  if (nk > FL::QL2 * kWave) return 2;
+
+  // E. (2N keys in the usual case; clustered rows, whose best elements share groups,
+  // can leave up to 4N)
+  auto sort_out = [&](auto ql_c) {
+    constexpr int Q = decltype(ql_c)::value;
+    uint64_t k[Q];
+    static_for<Q>([&](auto s) {
+      const int p = lane * Q + s;
+      k[s] = p < nk ? F.keys[p] : 0ull;
+    });
+    wave_sort_desc<Q>(k);
+    int cnt = 0;
+    static_for<Q>([&](auto s) {
+      const int p = lane * Q + s;
+      if (p < N) {
+        const uint64_t v = p < TC ? k[s] : 0ull;
+        s_sup[p] = v;
+        cnt += v != 0ull;
+      }
+    });
+    n_sup = wave_sum_i(cnt);
+  };
+  if (wave == 0) {
+    if (nk <= QL * kWave) sort_out(std::integral_constant<int, QL>{});
+    else sort_out(std::integral_constant<int, FL::QL2>{});
+  }
+  return 0;
 }
 
 // Expansion of one parent by wave 0 (RheoSampling key design 2), BS support ranks
@@ -527,50 +786,71 @@ __attribute__((amdgpu_waves_per_eu(PL == 2 ? 4 : 2, 8))) void k_select_expand(co
   }
 
   constexpr int SW = sel_waves<PL>();
-  __shared__ __align__(16) SegLds<DT, PL> s_seg[SW];
-  __shared__ uint64_t s_list[SW / 2][N];
+  // the two selection paths share one LDS area
+  struct SegPath {
+    SegLds<DT, PL> seg[SW];
+    uint64_t list[SW / 2][N];
+  };
+  using FastT = std::conditional_t<(PL <= 4), FastLds<DT, PL>, char>;  // long lists: no row path
+  constexpr size_t kRaw = sizeof(SegPath) > sizeof(FastT) ? sizeof(SegPath) : sizeof(FastT);
+  __shared__ __align__(16) char s_raw[kRaw];
+  __shared__ uint64_t s_sup[N];  // the support: top trunc keys, zero-padded
   __shared__ float s_q[N];
   __shared__ int s_bad[SW];
   constexpr int esz = DT == VRT_BF16 ? 2 : 4;
   const char* row = (const char*)a.logits + ((int64_t)b * a.tstride + (int64_t)j * a.ld) * esz;
   const int G = (c.V + seg_elems<DT>() - 1) / seg_elems<DT>();
 
-  uint64_t acc[PL];
-  static_for<PL>([&](auto s) { acc[s] = 0ull; });
-  bool bad = false;
-  for (int g = wave; g < G; g += SW) {
-    uint64_t cur[PL];
-    seg_select<DT, PL>(row, g, c.V, s_seg[wave], cur, bad);
-    if (g == wave) static_for<PL>([&](auto s) { acc[s] = cur[s]; });
-    else wave_merge_top<PL>(acc, cur);
+  int n_sup = 0;
+  int any_bad = 0;
+  int path = 2;
+  if constexpr (PL <= 4) {
+    if (G <= FastLds<DT, PL>::GMAX)
+      path = row_select_fast<DT, PL>(row, G, c.V, c.TC, *(FastT*)s_raw, s_sup, n_sup);
+    if (path == 1) any_bad = 1;
+    if (path != 2) __syncthreads();  // the next use of s_raw is not this one's
   }
-  if (lane == 0) s_bad[wave] = bad ? 1 : 0;
-  // pairwise merges: at distance st, wave w + st hands its list to wave w
-  for (int st = 1; st < SW; st <<= 1) {
-    if ((wave & (2 * st - 1)) == st)
-      static_for<PL>([&](auto s) { s_list[wave / (2 * st)][lane * PL + s] = acc[s]; });
-    __syncthreads();
-    if ((wave & (2 * st - 1)) == 0) {
-      uint64_t oth[PL];
-      static_for<PL>([&](auto s) { oth[s] = s_list[wave / (2 * st)][lane * PL + s]; });
-      wave_merge_top<PL>(acc, oth);
+  if (path == 2) {
+    // per segment: each wave selects its segments' top N (segments wave, wave + SW, ..),
+    // the lists merge pairwise through LDS (the row's top trunc is in the union of the
+    // segments' top trunc)
+    SegPath& P = *(SegPath*)s_raw;
+    uint64_t acc[PL];
+    static_for<PL>([&](auto s) { acc[s] = 0ull; });
+    bool bad = false;
+    for (int g = wave; g < G; g += SW) {
+      uint64_t cur[PL];
+      seg_select<DT, PL>(row, g, c.V, P.seg[wave], cur, bad);
+      if (g == wave) static_for<PL>([&](auto s) { acc[s] = cur[s]; });
+      else wave_merge_top<PL>(acc, cur);
     }
-    __syncthreads();
+    if (lane == 0) s_bad[wave] = bad ? 1 : 0;
+    // pairwise merges: at distance st, wave w + st hands its list to wave w
+    for (int st = 1; st < SW; st <<= 1) {
+      if ((wave & (2 * st - 1)) == st)
+        static_for<PL>([&](auto s) { P.list[wave / (2 * st)][lane * PL + s] = acc[s]; });
+      __syncthreads();
+      if ((wave & (2 * st - 1)) == 0) {
+        uint64_t oth[PL];
+        static_for<PL>([&](auto s) { oth[s] = P.list[wave / (2 * st)][lane * PL + s]; });
+        wave_merge_top<PL>(acc, oth);
+      }
+      __syncthreads();
+    }
+    if (wave == 0) {
+      int cnt = 0;
+      static_for<PL>([&](auto s) {
+        const int p = lane * PL + s;
+        const uint64_t k = p < c.TC ? acc[s] : 0ull;
+        s_sup[p] = k;
+        cnt += k != 0ull;
+      });
+      n_sup = wave_sum_i(cnt);
+      for (int w = 0; w < SW; ++w) any_bad |= s_bad[w];
+    }
   }
   if (wave != 0) return;
-
-  // support: the non-empty keys among the first trunc positions
-  uint64_t* s_buf = s_list[0];
-  int cnt = 0;
-  static_for<PL>([&](auto s) {
-    const int p = lane * PL + s;
-    const uint64_t k = p < c.TC ? acc[s] : 0ull;
-    s_buf[p] = k;
-    cnt += k != 0ull;
-  });
-  const int n_sup = wave_sum_i(cnt);
-  int any_bad = 0;
-  for (int w = 0; w < SW; ++w) any_bad |= s_bad[w];
+  uint64_t* s_buf = s_sup;
   wave_sync();
 
   uint32_t st = any_bad ? VRT_ST_DRAFT_NONFINITE : 0u;

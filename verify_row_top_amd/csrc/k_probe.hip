@@ -33,8 +33,9 @@ __global__ __launch_bounds__(kPT) void k_read_probe(const u32x4_t* buf, int64_t 
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream) {
   const int64_t n16 = (int64_t)(bytes / 16);
   int dev = 0, cus = 256;
-  hipGetDevice(&dev);
-  hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
   const int64_t need = (n16 + (int64_t)kPT * kPL - 1) / ((int64_t)kPT * kPL);
   const int blocks = (int)std::min<int64_t>(need, (int64_t)cus * 8);
   hipLaunchKernelGGL(k_read_probe, dim3(blocks > 0 ? blocks : 1), dim3(kPT), 0, stream,
