@@ -387,52 +387,53 @@ constexpr int kFastGroups = 512;  // candidate groups taken (one per thread of t
 template <int DT, int PL>
 struct FastLds {
   static constexpr int LV = PL <= 2 ? 4 : 2 * PL;      // candidates per lane and segment
-  static constexpr int QL = 2 * PL;                    // usual sort: 2N keys
-  static constexpr int QL2 = 4 * PL;                   // larger sort: 4N keys
-  static constexpr int GMAX = DT == VRT_BF16 ? 24 : 12;  // segments the path takes
+  static constexpr int KCAP = 4 * PL * kWave;          // staged keys held (4N)
+  static constexpr int GMAX = DT == VRT_BF16 ? 20 : 10;  // segments the path takes
+  // a candidate: group maximum's image << 8 | its load index q
+  using CK = std::conditional_t<DT == VRT_BF16, uint32_t, uint64_t>;
   Img<DT> gimg[GMAX][kSegLoads * kWave];  // group maxima images, [g][q*64 + lane]
-  Img<DT> cimg[GMAX * kWave * LV];        // every lane's LV largest group maxima
+  CK cand[GMAX * kWave * LV];             // lane-segment lists [(g*64 + lane)*LV + s], desc
   int glist[kFastGroups];                 // groups that reach the threshold
-  uint64_t keys[QL2 * kWave];             // row keys of the elements that reach it
+  uint64_t keys[KCAP];                    // row keys of the elements that reach it
   int hist[256];
   int sel[2];
-  int wtot[16];
   int ngl, nk, bad;
 };
 
 // The row's top TC keys (value desc, token id asc) into s_sup (positions < N, sorted,
 // zero-padded), by all waves of the block:
 //  A. each wave loads its segments (16 KB each, all loads in flight), keeps every
-//     group's maximum (image, in LDS) and each lane's LV largest group maxima;
-//  B. the TC-th largest of all these candidates, t (bitwise search, one block-wide
-//     count per bit), is reached by at least TC distinct elements, so no element below
-//     it is among the row's TC best; on the workloads' rows it is the row's TC-th
+//     group's maximum (image, in LDS) and each lane's LV largest group maxima with
+//     their load indices;
+//  B. the TC-th largest of all these candidates, t (a radix selection, one byte per
+//     block-wide histogram), is reached by at least TC distinct elements, so no element
+//     below it is among the row's TC best; on the workloads' rows it is the row's TC-th
 //     value itself;
-//  C. the groups whose maximum reaches t (about TC of them) are listed;
+//  C. the groups whose maximum reaches t are listed: from the candidate lists, or, for a
+//     lane whose LV candidates all reach t, from its stored group maxima;
 //  D. each thread re-reads one listed group (16 bytes) and stages the exact keys of its
 //     elements that reach t;
-//  E. wave 0 sorts the staged keys (bitonic network over lane exchanges).
+//  E. each staged key's rank among them (the keys are distinct) places it in s_sup.
 // Returns 0 on success, 1 for a non-finite row, 2 when more groups or keys reach the
 // threshold than the path holds (ties, flat or tiny rows): the caller then takes the
-// per-segment path. The result is uniform over the block.
+// exact path. The result is uniform over the block.
 template <int DT, int PL>
 __device__ int row_select_fast(const char* row, int G, int V, int TC, FastLds<DT, PL>& F,
                                uint64_t* s_sup, int& n_sup) {
   using FL = FastLds<DT, PL>;
+  using CK = typename FL::CK;
   constexpr bool BF = DT == VRT_BF16;
   constexpr int N = PL * kWave;
   constexpr int LV = FL::LV;
-  constexpr int QL = FL::QL;
   constexpr int SW = sel_waves<PL>();
   constexpr int NT = SW * kWave;
   constexpr int RB = BF ? 16 : 32;
   constexpr int esz = BF ? 2 : 4;
   constexpr int EPL = 16 / esz;
-  constexpr int KPT = (FL::GMAX * kWave * LV + NT - 1) / NT;  // candidates per thread
+  constexpr int LSPT = (FL::GMAX * kWave + NT - 1) / NT;  // lane-segments per thread
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = lane_id();
-  const uint64_t lt_mask = (1ull << lane) - 1ull;
   if (tid == 0) {
     F.ngl = 0;
     F.nk = 0;
@@ -448,40 +449,51 @@ __device__ int row_select_fast(const char* row, int G, int V, int TC, FastLds<DT
     load_segment<DT>(row, g, V, d);
     float gm[kSegLoads];
     group_maxima<DT>(d, gm);
-    float lv[LV];
-    static_for<LV>([&](auto s) { lv[s] = -INFINITY; });
+    CK lv[LV];
+    static_for<LV>([&](auto s) { lv[s] = 0; });
     static_for<kSegLoads>([&](auto q) {
       nf |= __builtin_amdgcn_classf(gm[q], 0x203);  // NaN, +inf
-      F.gimg[g][q * kWave + lane] = (Img<DT>)img_of<DT>(gm[q]);
-      float x = gm[q];
+      const uint32_t im = img_of<DT>(gm[q]);
+      F.gimg[g][q * kWave + lane] = (Img<DT>)im;
+      CK x = ((CK)im << 8) | (CK)q;
       static_for<LV>([&](auto s) {
-        const float h = fmaxf(lv[s], x);
-        x = fminf(lv[s], x);
+        const CK h = lv[s] > x ? lv[s] : x;
+        x = lv[s] > x ? x : lv[s];
         lv[s] = h;
       });
     });
-    static_for<LV>([&](auto s) { F.cimg[(g * kWave + lane) * LV + s] = (Img<DT>)img_of<DT>(lv[s]); });
+    static_for<LV>([&](auto s) { F.cand[(g * kWave + lane) * LV + s] = lv[s]; });
   }
   if (ballot(nf) != 0ull && lane == 0) F.bad = 1;
   __syncthreads();
   if (F.bad) return 1;
 
-  // B. (a radix select in bytes: a histogram per byte of the image, from the top)
-  const int C = G * kWave * LV;
-  uint32_t cand[KPT];
-  static_for<KPT>([&](auto k) {
-    const int idx = tid + k * NT;
-    cand[k] = idx < C ? (uint32_t)F.cimg[idx] : 0u;
+  // B. (per wave, the lanes of the first active lane's byte add once, the others one by one)
+  const int nls = G * kWave;  // lane-segments
+  CK cand[LSPT][LV];
+  static_for<LSPT>([&](auto j) {
+    const int ls = tid + j * NT;
+    static_for<LV>([&](auto s) { cand[j][s] = ls < nls ? F.cand[ls * LV + s] : (CK)0; });
   });
   uint32_t pre = 0u;   // image bits fixed so far (the high ones)
   int above = 0;       // candidates whose fixed bits exceed pre's
   static_for<RB / 8>([&](auto lvl) {
     constexpr int sh = RB - 8 * (lvl + 1);
-    // count the candidates that agree with pre above this byte, by this byte
-    static_for<KPT>([&](auto k) {
-      const uint32_t v = cand[k];
-      const bool match = ((uint64_t)(v ^ pre) >> (sh + 8)) == 0u;
-      if (v != 0u && match) atomicAdd(&F.hist[(v >> sh) & 0xFF], 1);
+    static_for<LSPT>([&](auto j) {
+      static_for<LV>([&](auto s) {
+        const uint32_t v = (uint32_t)(cand[j][s] >> 8);
+        const bool act = v != 0u && ((uint64_t)(v ^ pre) >> (sh + 8)) == 0u;
+        const uint32_t bin = (v >> sh) & 0xFFu;
+        const uint64_t m = ballot(act);
+        if (m != 0ull) {
+          const int f = __builtin_ctzll(m);
+          const uint32_t b0 = __builtin_amdgcn_readlane(bin, f);
+          const bool same = act && bin == b0;
+          const uint64_t ms = ballot(same);
+          if (lane == f) atomicAdd(&F.hist[b0], __builtin_popcountll(ms));
+          if (act && !same) atomicAdd(&F.hist[bin], 1);
+        }
+      });
     });
     __syncthreads();
     // wave 0 finds the byte value b: the largest with above + #(byte >= b) >= TC
@@ -489,26 +501,25 @@ __device__ int row_select_fast(const char* row, int G, int V, int TC, FastLds<DT
       int h[4];
       static_for<4>([&](auto i) { h[i] = F.hist[255 - (lane * 4 + i)]; });  // descending bytes
       const int ls = h[0] + h[1] + h[2] + h[3];
-      const int incl = wave_incl_scan(ls) + above;
-      int pick = -1, cum = incl - ls;
+      int cum = wave_incl_scan(ls) - ls + above;
+      int pick = -1, excl = 0;
       static_for<4>([&](auto i) {
+        if (pick < 0 && cum + h[i] >= TC) {
+          pick = 255 - (lane * 4 + i);
+          excl = cum;
+        }
         cum += h[i];
-        if (pick < 0 && cum >= TC) pick = 255 - (lane * 4 + i);
       });
       const uint64_t has = ballot(pick >= 0);
+      if (lane == 0) F.sel[0] = -1;
       if (has) {
-        const int src_l = __builtin_ctzll(has);
-        const int bsel = __shfl(pick, src_l, kWave);
-        // candidates strictly above byte bsel: everything before it in descending order
-        int before = 0;
-        static_for<4>([&](auto i) { before += (255 - (lane * 4 + i)) > bsel ? h[i] : 0; });
-        before = wave_sum_i(before);
+        const int src = __builtin_ctzll(has);
+        const int bsel = __shfl(pick, src, kWave);
+        const int bex = __shfl(excl, src, kWave);
         if (lane == 0) {
           F.sel[0] = bsel;
-          F.sel[1] = above + before;
+          F.sel[1] = bex;
         }
-      } else if (lane == 0) {
-        F.sel[0] = -1;
       }
     }
     __syncthreads();
@@ -524,36 +535,43 @@ __device__ int row_select_fast(const char* row, int G, int V, int TC, FastLds<DT
   });
   if (pre == 0u || pre == 0xFFFFFFFFu) return 2;  // fewer than TC candidates carry a value
 
-  // C. (each thread scans a contiguous run of groups; the list stays in group order)
-  const int ng = G * kSegLoads * kWave;
-  constexpr int EPT = (FL::GMAX * kSegLoads * kWave + NT - 1) / NT;  // groups per thread
-  static_assert(EPT <= 64, "a thread's groups fit one 64-bit mask");
-  const int k0 = tid * EPT;
-  uint64_t hits = 0ull;
-  static_for<EPT>([&](auto i) {
-    const int k = k0 + i;
-    if (k < ng && (uint32_t)((const Img<DT>*)F.gimg)[k] >= pre) hits |= 1ull << i;
-  });
-  const int nh = __builtin_popcountll(hits);
-  const int incl = wave_incl_scan(nh);
-  if (lane == kWave - 1) F.wtot[wave] = incl;
-  __syncthreads();
-  int off = incl - nh;
-  int total = 0;
-  static_for<SW>([&](auto w) {
-    const int t = F.wtot[w];
-    off += (int)w < wave ? t : 0;
-    total += t;
-  });
-  for (uint64_t m = hits; m; m &= m - 1ull) {
-    if (off < kFastGroups) F.glist[off] = k0 + __builtin_ctzll(m);
-    ++off;
+  // C. (a wave reserves its groups' places with one atomic)
+  {
+    auto each_group = [&](auto&& f) {
+      static_for<LSPT>([&](auto j) {
+        const int ls = tid + j * NT;
+        if (ls < nls) {
+          const int g = ls / kWave, l = ls % kWave;
+          if ((uint32_t)(cand[j][LV - 1] >> 8) >= pre) {
+            // every candidate reaches t: others of this lane may too
+            for (int q = 0; q < kSegLoads; ++q)
+              if ((uint32_t)F.gimg[g][q * kWave + l] >= pre) f(g * kSegLoads * kWave + q * kWave + l);
+          } else {
+            static_for<LV>([&](auto s) {
+              if ((uint32_t)(cand[j][s] >> 8) >= pre)
+                f(g * kSegLoads * kWave + (int)(cand[j][s] & 0xFF) * kWave + l);
+            });
+          }
+        }
+      });
+    };
+    int cnt = 0;
+    each_group([&](int) { ++cnt; });
+    const int incl = wave_incl_scan(cnt);
+    int base = 0;
+    if (lane == kWave - 1 && incl > 0) base = atomicAdd(&F.ngl, incl);
+    int off = __shfl(base, kWave - 1, kWave) + incl - cnt;
+    if (cnt > 0)
+      each_group([&](int k) {
+        if (off < kFastGroups) F.glist[off] = k;
+        ++off;
+      });
   }
-  if (total > kFastGroups) return 2;
-  const int ngl = total;
   __syncthreads();
+  const int ngl = F.ngl;
+  if (ngl > kFastGroups) return 2;
 
-  // D.
+  // D. (a wave reserves its keys' places with one atomic)
   {
     const bool has = tid < ngl;
     u32x4_t gw = {0u, 0u, 0u, 0u};
@@ -564,47 +582,212 @@ __device__ int row_select_fast(const char* row, int G, int V, int TC, FastLds<DT
       e0 = g * seg_elems<DT>() + gi * EPL;
       if (e0 < V) gw = *(const u32x4_t*)(row + (int64_t)e0 * esz);
     }
+    float x[EPL];
+    uint32_t keep = 0u;
     static_for<EPL>([&](auto e) {
-      float x;
-      if constexpr (BF) x = (e & 1) ? bf16_hi(gw[e >> 1]) : bf16_lo(gw[e >> 1]);
-      else x = __uint_as_float(gw[(int)e]);
-      const int id = e0 + e;
-      const bool keep = has && id < V && img_of<DT>(x) >= pre;
-      const uint64_t m = ballot(keep);
-      int at = 0;
-      if (lane == 0 && m) at = atomicAdd(&F.nk, __builtin_popcountll(m));
-      at = __shfl(at, 0, kWave) + __builtin_popcountll(m & lt_mask);
-      if (keep && at < FL::QL2 * kWave) F.keys[at] = sup_key(x, (uint32_t)id);
+      if constexpr (BF) x[e] = (e & 1) ? bf16_hi(gw[e >> 1]) : bf16_lo(gw[e >> 1]);
+      else x[e] = __uint_as_float(gw[(int)e]);
+      if (has && e0 + (int)e < V && img_of<DT>(x[e]) >= pre) keep |= 1u << e;
+    });
+    const int cnt = __builtin_popcount(keep);
+    const int incl = wave_incl_scan(cnt);
+    int base = 0;
+    if (lane == kWave - 1 && incl > 0) base = atomicAdd(&F.nk, incl);
+    int at = __shfl(base, kWave - 1, kWave) + incl - cnt;
+    static_for<EPL>([&](auto e) {
+      if (keep & (1u << e)) {
+        if (at < FL::KCAP) F.keys[at] = sup_key(x[e], (uint32_t)(e0 + (int)e));
+        ++at;
+      }
     });
   }
   __syncthreads();
   const int nk = F.nk;
-  if (nk > FL::QL2 * kWave) return 2;
+  if (nk > FL::KCAP) return 2;
 
-  // E. (2N keys in the usual case; clustered rows, whose best elements share groups,
-  // can leave up to 4N)
-  auto sort_out = [&](auto ql_c) {
-    constexpr int Q = decltype(ql_c)::value;
-    uint64_t k[Q];
-    static_for<Q>([&](auto s) {
-      const int p = lane * Q + s;
-      k[s] = p < nk ? F.keys[p] : 0ull;
-    });
-    wave_sort_desc<Q>(k);
-    int cnt = 0;
-    static_for<Q>([&](auto s) {
-      const int p = lane * Q + s;
-      if (p < N) {
-        const uint64_t v = p < TC ? k[s] : 0ull;
-        s_sup[p] = v;
-        cnt += v != 0ull;
+  // E. (nk >= TC: t is reached by TC distinct candidates)
+  for (int i = tid; i < nk; i += NT) {
+    const uint64_t my = F.keys[i];
+    int r = 0;
+    for (int jj = 0; jj < nk; ++jj) r += F.keys[jj] > my;
+    if (r < TC) s_sup[r] = my;
+  }
+  for (int p = TC + tid; p < N; p += NT) s_sup[p] = 0ull;
+  n_sup = TC;
+  __syncthreads();
+  return 0;
+}
+
+// LDS of the exact row selection.
+template <int PL>
+struct ExactLds {
+  uint64_t keys[PL * kWave];
+  int hist[2][256];
+  int wtot[2][16];
+  int sel[2];
+  int nk, bad;
+};
+
+// The row's top TC keys (value desc, token id asc) into s_sup, exactly, for the rows the
+// row-wide path does not take (many ties, flat rows, rows longer than it holds), by all
+// waves of the block with few registers:
+//  1. a radix selection fixes the image t of the TC-th largest value, one byte per pass
+//     over the row (re-read; the first pass also flags NaN and +inf), and how many
+//     elements equal to t belong to the top TC;
+//  2. a last pass stages every element above t and, in token order (a block-wide scan
+//     per chunk of the row), that many elements equal to t;
+//  3. wave 0 sorts the staged keys.
+// Returns 1 for a row holding NaN or +inf, else 0; uniform over the block.
+template <int DT, int PL>
+__device__ int row_select_exact(const char* row, int V, int TC, ExactLds<PL>& X, uint64_t* s_sup,
+                                int& n_sup) {
+  constexpr bool BF = DT == VRT_BF16;
+  constexpr int EPL = BF ? 8 : 4;             // elements per 16-byte vector
+  constexpr int IB = BF ? 16 : 32;            // image bits
+  constexpr uint32_t PINF = BF ? 0xFF80u : 0xFF800000u;  // image of +inf
+  constexpr uint32_t NINF = BF ? 0x007Fu : 0x007FFFFFu;  // image of -inf
+  constexpr int SW = sel_waves<PL>();
+  constexpr int NT = SW * kWave;
+  constexpr int N = PL * kWave;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = lane_id();
+  const int nv = (V + EPL - 1) / EPL;
+  const int take = min(TC, V);
+  // images of vector v's elements; 0 marks an element past V (a valid element with image
+  // 0 is a NaN, which flags the row)
+  auto images = [&](int v, uint32_t (&im)[EPL]) {
+    const u32x4_t d = *(const u32x4_t*)(row + (int64_t)v * 16);
+    static_for<EPL>([&](auto e) {
+      uint32_t x;
+      if constexpr (BF) {
+        const uint32_t h = (d[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+        x = (h & 0x8000u) ? (~h & 0xFFFFu) : (h | 0x8000u);
+      } else {
+        x = ord32(__uint_as_float(d[(int)e]));
       }
+      im[e] = v * EPL + (int)e < V ? x : 0u;
+    });
+  };
+  if (tid < 256) {
+    X.hist[0][tid] = 0;
+    X.hist[1][tid] = 0;
+  }
+  if (tid == 0) {
+    X.nk = 0;
+    X.bad = 0;
+  }
+  __syncthreads();
+
+  // 1.
+  uint32_t pre = 0u;  // the image bits fixed so far
+  int need = take;    // elements matching pre still to take
+  bool bad = false;
+  static_for<IB / 8>([&](auto lvl) {
+    constexpr int sh = IB - 8 * (lvl + 1);
+    int* H = X.hist[lvl & 1];
+    if (lvl >= 1 && tid < 256) X.hist[(lvl + 1) & 1][tid] = 0;  // last read two bytes ago
+    bool nf = false;
+    for (int v = tid; v < nv; v += NT) {
+      uint32_t im[EPL];
+      images(v, im);
+      static_for<EPL>([&](auto e) {
+        const uint32_t x = im[e];
+        if (lvl == 0) nf |= x != 0u && (x >= PINF || x < NINF);
+        if (x != 0u && ((uint64_t)(x ^ pre) >> (sh + 8)) == 0u) atomicAdd(&H[(x >> sh) & 0xFF], 1);
+      });
+    }
+    if (lvl == 0 && ballot(nf) != 0ull && lane == 0) X.bad = 1;
+    __syncthreads();
+    if (lvl == 0 && X.bad) bad = true;
+    if (!bad) {
+      // wave 0: the largest byte b with #(matching elements with byte >= b) >= need
+      if (wave == 0) {
+        int h[4];
+        static_for<4>([&](auto i) { h[i] = H[255 - (lane * 4 + i)]; });
+        const int ls = h[0] + h[1] + h[2] + h[3];
+        int cum = wave_incl_scan(ls) - ls;
+        int pick = -1, excl = 0;
+        static_for<4>([&](auto i) {
+          if (pick < 0 && cum + h[i] >= need) {
+            pick = 255 - (lane * 4 + i);
+            excl = cum;
+          }
+          cum += h[i];
+        });
+        const uint64_t has = ballot(pick >= 0);  // never empty: need <= matching elements
+        const int src = has ? __builtin_ctzll(has) : 0;
+        const int bsel = __shfl(pick, src, kWave);
+        const int bex = __shfl(excl, src, kWave);
+        if (lane == 0) {
+          X.sel[0] = bsel < 0 ? 0 : bsel;
+          X.sel[1] = need - bex;
+        }
+      }
+      __syncthreads();
+      pre |= (uint32_t)X.sel[0] << sh;
+      need = X.sel[1];
+    }
+  });
+  if (bad) return 1;
+
+  // 2.
+  auto stage = [&](uint32_t x, int id) {
+    const int at = atomicAdd(&X.nk, 1);
+    if (at < N) X.keys[at] = sup_key(value_of<DT>(x), (uint32_t)id);
+  };
+  int rem = need;  // elements equal to t still to take
+  for (int c0 = 0, it = 0; c0 < nv; c0 += NT, ++it) {
+    const int v = c0 + tid;
+    uint32_t im[EPL];
+    int nt = 0;
+    if (v < nv) {
+      images(v, im);
+      static_for<EPL>([&](auto e) {
+        if (im[e] > pre) stage(im[e], v * EPL + (int)e);
+        nt += im[e] == pre;
+      });
+    }
+    if (rem > 0) {  // uniform
+      const int incl = wave_incl_scan(nt);
+      if (lane == kWave - 1) X.wtot[it & 1][wave] = incl;
+      __syncthreads();
+      int off = incl - nt, tot = 0;
+      static_for<SW>([&](auto w) {
+        const int t = X.wtot[it & 1][w];
+        off += (int)w < wave ? t : 0;
+        tot += t;
+      });
+      if (nt > 0 && off < rem) {
+        static_for<EPL>([&](auto e) {
+          if (im[e] == pre) {
+            if (off < rem) stage(im[e], v * EPL + (int)e);
+            ++off;
+          }
+        });
+      }
+      rem -= tot;
+    }
+  }
+  __syncthreads();
+
+  // 3.
+  if (wave == 0) {
+    const int nk = min(X.nk, N);
+    uint64_t k[PL];
+    static_for<PL>([&](auto s) {
+      const int p = lane * PL + s;
+      k[s] = p < nk ? X.keys[p] : 0ull;
+    });
+    wave_sort_desc<PL>(k);
+    int cnt = 0;
+    static_for<PL>([&](auto s) {
+      const int p = lane * PL + s;
+      const uint64_t x = p < TC ? k[s] : 0ull;
+      s_sup[p] = x;
+      cnt += x != 0ull;
     });
     n_sup = wave_sum_i(cnt);
-  };
-  if (wave == 0) {
-    if (nk <= QL * kWave) sort_out(std::integral_constant<int, QL>{});
-    else sort_out(std::integral_constant<int, FL::QL2>{});
   }
   return 0;
 }
@@ -786,13 +969,16 @@ __attribute__((amdgpu_waves_per_eu(PL == 2 ? 4 : 2, 8))) void k_select_expand(co
   }
 
   constexpr int SW = sel_waves<PL>();
-  // the two selection paths share one LDS area
+  // short lists: the row-wide path, the exact path behind it; long lists: per segment.
+  // The paths share one LDS area.
   struct SegPath {
     SegLds<DT, PL> seg[SW];
     uint64_t list[SW / 2][N];
   };
-  using FastT = std::conditional_t<(PL <= 4), FastLds<DT, PL>, char>;  // long lists: no row path
-  constexpr size_t kRaw = sizeof(SegPath) > sizeof(FastT) ? sizeof(SegPath) : sizeof(FastT);
+  using FastT = std::conditional_t<(PL <= 4), FastLds<DT, PL>, char>;
+  using ExactT = std::conditional_t<(PL <= 4), ExactLds<PL>, char>;
+  using SegT = std::conditional_t<(PL <= 4), char, SegPath>;
+  constexpr size_t kRaw = std::max({sizeof(FastT), sizeof(ExactT), sizeof(SegT)});
   __shared__ __align__(16) char s_raw[kRaw];
   __shared__ uint64_t s_sup[N];  // the support: top trunc keys, zero-padded
   __shared__ float s_q[N];
@@ -803,14 +989,16 @@ __attribute__((amdgpu_waves_per_eu(PL == 2 ? 4 : 2, 8))) void k_select_expand(co
 
   int n_sup = 0;
   int any_bad = 0;
-  int path = 2;
   if constexpr (PL <= 4) {
+    int path = 2;
     if (G <= FastLds<DT, PL>::GMAX)
       path = row_select_fast<DT, PL>(row, G, c.V, c.TC, *(FastT*)s_raw, s_sup, n_sup);
+    if (path == 2) {
+      __syncthreads();  // s_raw changes hands
+      path = row_select_exact<DT, PL>(row, c.V, c.TC, *(ExactT*)s_raw, s_sup, n_sup);
+    }
     if (path == 1) any_bad = 1;
-    if (path != 2) __syncthreads();  // the next use of s_raw is not this one's
-  }
-  if (path == 2) {
+  } else {
     // per segment: each wave selects its segments' top N (segments wave, wave + SW, ..),
     // the lists merge pairwise through LDS (the row's top trunc is in the union of the
     // segments' top trunc)
