@@ -1106,86 +1106,182 @@ __global__ __launch_bounds__(256) void k_rank_layer(const Cfg c, const TreePtrs 
   t.n_front[b] = nf;
 }
 
-constexpr int kFT = 1024;  // threads of the finish block
+constexpr int kFT = 1024;          // threads of the finish block
+constexpr int kFW = kFT / kWave;   // its waves
+constexpr int kMapMax = 16384;     // candidate -> node map in LDS up to this many candidates
+
+// Keys per lane of the finish's wave lists (64*PL >= R), 0 when R needs the LDS sort.
+__host__ __device__ inline int finish_pl(const Cfg& c) {
+  if (c.mode != VRT_MODE_TOPR) return 0;
+  return c.R <= 64 ? 1 : (c.R <= 128 ? 2 : 0);
+}
+
+// Finish's dynamic LDS, in 8-byte words: the key area (wave lists or the LDS sort), then
+// the candidate -> node map, then per node: candidate, parent node, slot, expansion row
+// holding its tail, tail length, child slot mask [N], child counts [N+1].
+struct FinishLds {
+  int key_words, map_ints;
+  __host__ __device__ explicit FinishLds(const Cfg& c) {
+    const int pl = finish_pl(c);
+    if (c.mode != VRT_MODE_TOPR) key_words = 0;
+    else if (pl) key_words = (kFW / 2 + 1) * pl * kWave;
+    else key_words = next_pow2(max(c.NC, 2));
+    // the map only where the whole area stays within 64 KB
+    const size_t rest = (size_t)key_words * 8 + (size_t)(7 * c.N + 1) * 4;
+    map_ints = (c.NC <= kMapMax && rest + (size_t)c.NC * 4 <= 65536) ? c.NC : 0;
+  }
+  __host__ __device__ size_t bytes(const Cfg& c) const {
+    return (size_t)key_words * 8 + (size_t)map_ints * 4 + (size_t)(7 * c.N + 1) * 4;
+  }
+};
+
+// Top 64*PL candidate keys of tree b (path score desc, creation index asc), sorted
+// descending and zero-padded, into s_top: each wave sorts chunks of 64*PL candidates
+// and keeps the largest 64*PL; the waves' lists then merge pairwise through LDS.
+template <int PL>
+__device__ void finish_top(const Cfg& c, const TreePtrs& t, int64_t ncb, uint64_t* s_list,
+                           uint64_t* s_top) {
+  constexpr int CH = PL * kWave;
+  const int wave = threadIdx.x >> 6;
+  const int lane = lane_id();
+  uint64_t acc[PL];
+  static_for<PL>([&](auto s) { acc[s] = 0ull; });
+  const int nch = (c.NC + CH - 1) / CH;
+  for (int ch = wave; ch < nch; ch += kFW) {
+    uint64_t k[PL];
+    static_for<PL>([&](auto s) {
+      const int i = ch * CH + lane * PL + s;
+      uint64_t x = 0ull;
+      if (i < c.NC && (t.cand_kind[ncb + i] & 0xFF) != 0) x = node_key(t.cand_score[ncb + i], (uint32_t)i);
+      k[s] = x;
+    });
+    wave_sort_desc<PL>(k);
+    if (ch == wave) static_for<PL>([&](auto s) { acc[s] = k[s]; });
+    else wave_merge_top<PL>(acc, k);
+  }
+  for (int st = 1; st < kFW; st <<= 1) {
+    uint64_t* slot = s_list + (wave / (2 * st)) * CH;
+    if ((wave & (2 * st - 1)) == st) static_for<PL>([&](auto s) { slot[lane * PL + s] = acc[s]; });
+    __syncthreads();
+    if ((wave & (2 * st - 1)) == 0) {
+      uint64_t oth[PL];
+      static_for<PL>([&](auto s) { oth[s] = slot[lane * PL + s]; });
+      wave_merge_top<PL>(acc, oth);
+    }
+    __syncthreads();
+  }
+  if (wave == 0) static_for<PL>([&](auto s) { s_top[lane * PL + s] = acc[s]; });
+}
 
 // Emit the tree: node 0 = root, then the kept candidates (parents first).
 __global__ __launch_bounds__(kFT) void k_finish(const Cfg c, const TreePtrs t) {
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = lane_id();
   const int64_t ncb = (int64_t)b * c.NC;
   const int64_t nb = (int64_t)b * c.N;
-  // dynamic LDS: top-R keys [np] (top-R mode), then per node: candidate, parent node,
-  // slot, expansion row holding its tail, tail length, child counts [N+1]
   extern __shared__ uint64_t s_keys[];
-  const int np = c.mode == VRT_MODE_TOPR ? next_pow2(max(c.NC, 2)) : 0;
-  int* s_ncand = (int*)(s_keys + np);
+  const FinishLds FL(c);
+  int* s_node_of = (int*)(s_keys + FL.key_words);
+  int* s_ncand = s_node_of + FL.map_ints;
   int* s_par = s_ncand + c.N;
   int* s_slot = s_par + c.N;
   int* s_trow = s_slot + c.N;
   int* s_tn = s_trow + c.N;
-  int* s_cnt = s_tn + c.N;
+  uint32_t* s_smask = (uint32_t*)(s_tn + c.N);
+  int* s_cnt = (int*)(s_smask + c.N);
   __shared__ int s_n;
 
+  for (int i = tid; i < FL.map_ints; i += kFT) s_node_of[i] = 0x7FFFFFFF;
   if (c.mode == VRT_MODE_TOPR) {
-    for (int i = tid; i < np; i += blockDim.x) {
-      uint64_t k = 0ull;
-      if (i < c.NC && (t.cand_kind[ncb + i] & 0xFF) != 0) k = node_key(t.cand_score[ncb + i], (uint32_t)i);
-      s_keys[i] = k;
+    const int pl = finish_pl(c);
+    const uint64_t* top = s_keys;
+    if (pl) {
+      // wave lists: the 8 merge slots, then the result
+      uint64_t* s_top = s_keys + (kFW / 2) * pl * kWave;
+      if (pl == 1) finish_top<1>(c, t, ncb, s_keys, s_top);
+      else finish_top<2>(c, t, ncb, s_keys, s_top);
+      top = s_top;
+    } else {
+      const int np = FL.key_words;
+      for (int i = tid; i < np; i += kFT) {
+        uint64_t k = 0ull;
+        if (i < c.NC && (t.cand_kind[ncb + i] & 0xFF) != 0) k = node_key(t.cand_score[ncb + i], (uint32_t)i);
+        s_keys[i] = k;
+      }
+      __syncthreads();
+      bitonic_desc(s_keys, np);
     }
     __syncthreads();
-    bitonic_desc(s_keys, np);
-    if (tid == 0) {
-      int n = 1;
-      while (n - 1 < c.R && n - 1 < np && s_keys[n - 1] != 0ull) ++n;
-      s_n = n;
+    // n - 1 = the nonzero keys among the first R (the list is sorted, zeros last)
+    if (wave == 0) {
+      const int lim = pl ? c.R : min(c.R, FL.key_words);
+      int cnt = 0;
+      for (int i = lane; i < lim; i += kWave) cnt += top[i] != 0ull;
+      cnt = wave_sum_i(cnt);
+      if (lane == 0) s_n = 1 + cnt;
     }
     __syncthreads();
-    for (int i = 1 + tid; i < s_n; i += blockDim.x)
-      s_ncand[i] = (int)(0xFFFFFFFFu - (uint32_t)s_keys[i - 1]);
+    for (int i = 1 + tid; i < s_n; i += kFT) s_ncand[i] = (int)(0xFFFFFFFFu - (uint32_t)top[i - 1]);
   } else {
     if (tid == 0) {
       const int nadm = (int)t.smart[(int64_t)b * 8 + 3];
       s_n = 1 + min(max(nadm, 0), c.N - 1);
     }
     __syncthreads();
-    for (int i = 1 + tid; i < s_n; i += blockDim.x) {
+    for (int i = 1 + tid; i < s_n; i += kFT) {
       const int cu = t.admitted[nb + i - 1];
       s_ncand[i] = (cu < 0 || cu >= c.NC) ? 0 : cu;
     }
   }
   const int n = s_n;
   if (tid == 0) s_ncand[0] = -1;
-  for (int i = tid; i <= n; i += blockDim.x) s_cnt[i] = 0;
-  for (int i = tid; i < n; i += blockDim.x) {
+  for (int i = tid; i <= n; i += kFT) s_cnt[i] = 0;
+  for (int i = tid; i < n; i += kFT) {
     s_trow[i] = -1;
     s_tn[i] = 0;
+    s_smask[i] = 0u;
   }
   __syncthreads();
+  if (FL.map_ints)
+    for (int i = 1 + tid; i < n; i += kFT) atomicMin(&s_node_of[s_ncand[i]], i);
+  __syncthreads();
   // nodes: parent node (parents precede children, so it is among nodes 1..i-1)
-  for (int i = 1 + tid; i < n; i += blockDim.x) {
+  for (int i = 1 + tid; i < n; i += kFT) {
     const int cu = s_ncand[i];
+    const int r = row_of(c, cu);
     const int pc = t.cand_parent[ncb + cu];
-    int pn = 0;
-    if (pc >= 0)
-      for (int jj = i - 1; jj >= 1; --jj)
-        if (s_ncand[jj] == pc) {
-          pn = jj;
-          break;
-        }
-    s_par[i] = pn;
-    s_slot[i] = slot_of(c, cu);
     const int kind = t.cand_kind[ncb + cu] & 0xFF;
+    const int tok = t.cand_token[ncb + cu];
+    const int rtn = t.row_tail_n[(int64_t)b * c.NR + r];
+    int pn = 0;
+    if (pc >= 0) {
+      if (FL.map_ints) {
+        const int m = s_node_of[pc];
+        pn = (m >= 1 && m < i) ? m : 0;
+      } else {
+        for (int jj = i - 1; jj >= 1; --jj)
+          if (s_ncand[jj] == pc) {
+            pn = jj;
+            break;
+          }
+      }
+    }
+    const int slot = slot_of(c, cu);
+    s_par[i] = pn;
+    s_slot[i] = slot;
     if (kind == VRT_PROBE) {
-      const int r = row_of(c, cu);
       s_trow[pn] = r;
-      s_tn[pn] = min(max(t.row_tail_n[(int64_t)b * c.NR + r], 0), c.TC);
+      s_tn[pn] = min(max(rtn, 0), c.TC);
     }
     t.node_cand[nb + i] = cu;
-    t.node_token[nb + i] = t.cand_token[ncb + cu];
+    t.node_token[nb + i] = tok;
     t.node_parent[nb + i] = pn;
     t.node_depth[nb + i] = layer_of(c, cu) + 1;
     t.node_kind[nb + i] = kind;
     atomicAdd(&s_cnt[pn], 1);
+    atomicOr(&s_smask[pn], 1u << slot);
   }
   if (tid == 0) {
     t.node_token[nb] = -1;
@@ -1195,34 +1291,59 @@ __global__ __launch_bounds__(kFT) void k_finish(const Cfg c, const TreePtrs t) {
     t.node_cand[nb] = -1;
   }
   __syncthreads();
-  if (tid == 0) {
-    int off = 0;
+  // child offsets: exclusive scan of the counts (wave 0, 64 nodes at a time)
+  if (wave == 0) {
     const int64_t cob = (int64_t)b * (c.N + 1);
-    for (int i = 0; i < n; ++i) {
-      const int k = s_cnt[i];
-      s_cnt[i] = off;
-      t.child_off[cob + i] = off;
-      off += k;
+    int carry = 0;
+    for (int i0 = 0; i0 < n; i0 += kWave) {
+      const int i = i0 + lane;
+      const int v = i < n ? s_cnt[i] : 0;
+      const int incl = wave_incl_scan(v);
+      if (i < n) {
+        s_cnt[i] = carry + incl - v;
+        t.child_off[cob + i] = carry + incl - v;
+      }
+      carry += __shfl(incl, kWave - 1, kWave);
     }
-    t.child_off[cob + n] = off;
-    t.n_nodes[b] = n;
+    if (lane == 0) {
+      t.child_off[cob + n] = carry;
+      t.n_nodes[b] = n;
+    }
   }
   __syncthreads();
-  // child lists in slot order
-  for (int i = 1 + tid; i < n; i += blockDim.x) {
+  // child lists in slot order (siblings come from one expansion row: distinct slots)
+  for (int i = 1 + tid; i < n; i += kFT) {
     const int pn = s_par[i], slot = s_slot[i];
-    int before = 0;
-    for (int jj = 1; jj < n; ++jj) before += (s_par[jj] == pn && s_slot[jj] < slot);
+    const int before = __builtin_popcount(s_smask[pn] & ((1u << slot) - 1u));
     t.child[nb + s_cnt[pn] + before] = i;
   }
-  // probe tails, copied to the probe's parent
-  for (int i = tid; i < n; i += blockDim.x) t.tail_n[nb + i] = s_tn[i];
-  for (int64_t x = tid; x < (int64_t)n * c.TC; x += blockDim.x) {
-    const int i = (int)(x / c.TC), k = (int)(x % c.TC);
-    if (k >= s_tn[i]) continue;
-    const int64_t rr = (int64_t)b * c.NR + s_trow[i];
-    t.tail_id[(nb + i) * c.TC + k] = t.row_tail_id[rr * c.TC + k];
-    t.tail_q[(nb + i) * c.TC + k] = t.row_tail_q[rr * c.TC + k];
+  // probe tails, copied to the probe's parent (all loads of a round in flight at once)
+  for (int i = tid; i < n; i += kFT) t.tail_n[nb + i] = s_tn[i];
+  constexpr int U = 8;
+  const int64_t tot = (int64_t)n * c.TC;
+  for (int64_t x0 = 0; x0 < tot; x0 += (int64_t)kFT * U) {
+    int idv[U];
+    float qv[U];
+    int64_t dst[U];
+    static_for<U>([&](auto u) {
+      const int64_t x = x0 + (int64_t)u * kFT + tid;
+      dst[u] = -1;
+      if (x < tot) {
+        const int i = (int)(x / c.TC), k = (int)(x % c.TC);
+        if (k < s_tn[i]) {
+          const int64_t rr = ((int64_t)b * c.NR + s_trow[i]) * c.TC + k;
+          idv[u] = t.row_tail_id[rr];
+          qv[u] = t.row_tail_q[rr];
+          dst[u] = (nb + i) * c.TC + k;
+        }
+      }
+    });
+    static_for<U>([&](auto u) {
+      if (dst[u] >= 0) {
+        t.tail_id[dst[u]] = idv[u];
+        t.tail_q[dst[u]] = qv[u];
+      }
+    });
   }
 }
 
@@ -1264,8 +1385,7 @@ hipError_t launch_build_layer(const Cfg& c, const TreePtrs& t, int layer, const 
 
 hipError_t launch_build_finish(const Cfg& c, const TreePtrs& t, void* ws, hipStream_t stream) {
   (void)ws;
-  const int np = c.mode == VRT_MODE_TOPR ? next_pow2(max(c.NC, 2)) : 0;
-  const size_t lds = (size_t)np * 8 + (size_t)(6 * c.N + 1) * 4;
+  const size_t lds = FinishLds(c).bytes(c);
   hipLaunchKernelGGL(k_finish, dim3(c.B), dim3(kFT), lds, stream, c, t);
   return hipGetLastError();
 }
