@@ -112,6 +112,8 @@ typedef struct {
  *   n_front     i32 [B]      number of valid entries of front (0: no further layer)
  *   smart       f64 [B][8]   SMART state (L, |T|, |P|, admitted count, root has a child)
  *   admitted    i32 [B][N]   SMART: admitted creation indices in admission order
+ *   layer_sync  i32 [B]      rows of the current layer done (set to 0 by layer 0 and
+ *                            by the block that ranks each layer)
  * Emitted tree (written by finish; the verification input, writable by the caller):
  *   n_nodes     i32 [B]      emitted nodes, root included (1 .. N)
  *   node_token  i32 [B][N]   token (root: -1)
@@ -128,7 +130,7 @@ typedef struct {
   int64_t NC, NR, N, TC, FP;
   int64_t cand_token, cand_parent, cand_score, cand_kind;
   int64_t row_tail_n, row_tail_id, row_tail_q;
-  int64_t front, n_front, smart, admitted;
+  int64_t front, n_front, smart, admitted, layer_sync;
   int64_t n_nodes, node_token, node_parent, node_depth, node_kind, node_cand;
   int64_t child_off, child, tail_n, tail_id, tail_q;
   int64_t total_bytes;

@@ -44,7 +44,8 @@ class Lib:
         self.cfg = cfg
         self.dev = dev
         self.tree = torch.zeros(vrt.tree_bytes(cfg), dtype=torch.uint8, device=dev)
-        self.ws = torch.zeros(vrt.workspace_bytes(cfg), dtype=torch.uint8, device=dev)
+        # the workspace needs no initialisation: start from garbage
+        self.ws = torch.full((vrt.workspace_bytes(cfg),), 0xA5, dtype=torch.uint8, device=dev)
         self.views = vrt.tree_views(cfg, self.tree)
         L = vrt.tree_layout_of(cfg)
         self.N = L.N

@@ -47,6 +47,7 @@ struct BArgs {
   uint64_t seed;
   uint32_t step;
   uint32_t* stats;
+  int fuse_rank;  // the layer's ranking runs in its row blocks
 };
 
 // The node frontier position j of tree b expands at this layer (-1 = root), or -2
@@ -382,119 +383,137 @@ __device__ __forceinline__ void seg_select(const char* row, int g, int V, SegLds
 // ---------------------------------------------------------------------------
 // Row-wide selection (the usual path for short lists): one threshold for the whole
 // row instead of one list per segment.
-constexpr int kFastGroups = 512;  // candidate groups taken (one per thread of the block)
 
 template <int DT, int PL>
 struct FastLds {
   static constexpr int LV = PL <= 2 ? 4 : 2 * PL;      // candidates per lane and segment
   static constexpr int KCAP = 4 * PL * kWave;          // staged keys held (4N)
-  static constexpr int GMAX = DT == VRT_BF16 ? 20 : 10;  // segments the path takes
   // a candidate: group maximum's image << 8 | its load index q
   using CK = std::conditional_t<DT == VRT_BF16, uint32_t, uint64_t>;
-  Img<DT> gimg[GMAX][kSegLoads * kWave];  // group maxima images, [g][q*64 + lane]
-  CK cand[GMAX * kWave * LV];             // lane-segment lists [(g*64 + lane)*LV + s], desc
-  int glist[kFastGroups];                 // groups that reach the threshold
-  uint64_t keys[KCAP];                    // row keys of the elements that reach it
+  alignas(16) uint64_t keys[KCAP];        // row keys of the elements that reach it
   int hist[256];
   int sel[2];
-  int ngl, nk, bad;
+  int nk, bad;
 };
 
 // The row's top TC keys (value desc, token id asc) into s_sup (positions < N, sorted,
-// zero-padded), by all waves of the block:
-//  A. each wave loads its segments (16 KB each, all loads in flight), keeps every
-//     group's maximum (image, in LDS) and each lane's LV largest group maxima with
-//     their load indices;
+// zero-padded), by all waves of the block. Thread (wave, lane) owns the lane-segments
+// (wave + j*SW, lane): lane's loads of those segments.
+//  A. each wave loads its segments (16 KB each, all loads in flight); each lane keeps,
+//     per lane-segment, every group maximum and the LV largest with their load indices;
 //  B. the TC-th largest of all these candidates, t (a radix selection, one byte per
 //     block-wide histogram), is reached by at least TC distinct elements, so no element
 //     below it is among the row's TC best; on the workloads' rows it is the row's TC-th
 //     value itself;
-//  C. the groups whose maximum reaches t are listed: from the candidate lists, or, for a
-//     lane whose LV candidates all reach t, from its stored group maxima;
-//  D. each thread re-reads one listed group (16 bytes) and stages the exact keys of its
-//     elements that reach t;
-//  E. each staged key's rank among them (the keys are distinct) places it in s_sup.
-// Returns 0 on success, 1 for a non-finite row, 2 when more groups or keys reach the
-// threshold than the path holds (ties, flat or tiny rows): the caller then takes the
-// exact path. The result is uniform over the block.
-template <int DT, int PL>
-__device__ int row_select_fast(const char* row, int G, int V, int TC, FastLds<DT, PL>& F,
-                               uint64_t* s_sup, int& n_sup) {
+//  C. each thread re-reads its candidate groups that reach t (16 bytes each, all in
+//     flight; where all LV candidates of a lane-segment reach t, its other groups that
+//     do too) and stages the exact keys of their elements that reach t;
+//  D. each staged key's rank among them (the keys are distinct) places it in s_sup.
+// Returns 0 on success, 1 for a non-finite row, 2 when more keys reach t than the path
+// holds (ties, flat rows; floor_img is then t's image) or fewer than TC (tiny rows):
+// the caller then takes the exact path. The result is uniform over the block.
+template <int DT, int PL, int SW, int LSPT>
+__device__ __forceinline__ int row_select_fast(const char* row, int g0, int g1, int V, int TC,
+                                               FastLds<DT, PL>& F, uint64_t* s_sup, int& n_sup,
+                                               uint32_t& floor_img) {
   using FL = FastLds<DT, PL>;
   using CK = typename FL::CK;
   constexpr bool BF = DT == VRT_BF16;
   constexpr int N = PL * kWave;
   constexpr int LV = FL::LV;
-  constexpr int SW = sel_waves<PL>();
   constexpr int NT = SW * kWave;
   constexpr int RB = BF ? 16 : 32;
   constexpr int esz = BF ? 2 : 4;
   constexpr int EPL = 16 / esz;
-  constexpr int LSPT = (FL::GMAX * kWave + NT - 1) / NT;  // lane-segments per thread
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = lane_id();
   if (tid == 0) {
-    F.ngl = 0;
     F.nk = 0;
     F.bad = 0;
   }
   if (tid < 256) F.hist[tid] = 0;
+  for (int i = tid; i < FL::KCAP; i += NT) F.keys[i] = 0ull;
   __syncthreads();
 
-  // A.
+  // A. (the thread's lane-segments are (g0 + wave + j*SW, lane): the same in every phase)
+  CK cand[LSPT][LV];
+  constexpr int GPW = BF ? 2 : 1;              // group maxima images per word
+  uint32_t gmi[LSPT][kSegLoads / GPW];         // every group maximum's image
   bool nf = false;
-  for (int g = wave; g < G; g += SW) {
-    u32x4_t d[kSegLoads];
-    load_segment<DT>(row, g, V, d);
-    float gm[kSegLoads];
-    group_maxima<DT>(d, gm);
-    CK lv[LV];
-    static_for<LV>([&](auto s) { lv[s] = 0; });
-    static_for<kSegLoads>([&](auto q) {
-      nf |= __builtin_amdgcn_classf(gm[q], 0x203);  // NaN, +inf
-      const uint32_t im = img_of<DT>(gm[q]);
-      F.gimg[g][q * kWave + lane] = (Img<DT>)im;
-      CK x = ((CK)im << 8) | (CK)q;
-      static_for<LV>([&](auto s) {
-        const CK h = lv[s] > x ? lv[s] : x;
-        x = lv[s] > x ? x : lv[s];
-        lv[s] = h;
+  static_for<LSPT>([&](auto j) {
+    const int g = g0 + wave + j * SW;
+    static_for<LV>([&](auto s) { cand[j][s] = 0; });
+    static_for<kSegLoads / GPW>([&](auto h) { gmi[j][h] = 0u; });
+    if (g < g1) {  // uniform
+      u32x4_t d[kSegLoads];
+      load_segment<DT>(row, g, V, d);
+      float gm[kSegLoads];
+      group_maxima<DT>(d, gm);
+      static_for<kSegLoads>([&](auto q) {
+        nf |= __builtin_amdgcn_classf(gm[q], 0x203);  // NaN, +inf
+        const uint32_t im = img_of<DT>(gm[q]);
+        gmi[j][q / GPW] |= im << (16 * (q % GPW));
+        CK x = ((CK)im << 8) | (CK)q;
+        static_for<LV>([&](auto s) {
+          const CK h = cand[j][s] > x ? cand[j][s] : x;
+          x = cand[j][s] > x ? x : cand[j][s];
+          cand[j][s] = h;
+        });
       });
-    });
-    static_for<LV>([&](auto s) { F.cand[(g * kWave + lane) * LV + s] = lv[s]; });
-  }
+    }
+  });
   if (ballot(nf) != 0ull && lane == 0) F.bad = 1;
   __syncthreads();
   if (F.bad) return 1;
 
-  // B. (per wave, the lanes of the first active lane's byte add once, the others one by one)
-  const int nls = G * kWave;  // lane-segments
-  CK cand[LSPT][LV];
-  static_for<LSPT>([&](auto j) {
-    const int ls = tid + j * NT;
-    static_for<LV>([&](auto s) { cand[j][s] = ls < nls ? F.cand[ls * LV + s] : (CK)0; });
-  });
+  // B.
   uint32_t pre = 0u;   // image bits fixed so far (the high ones)
   int above = 0;       // candidates whose fixed bits exceed pre's
   static_for<RB / 8>([&](auto lvl) {
     constexpr int sh = RB - 8 * (lvl + 1);
-    static_for<LSPT>([&](auto j) {
-      static_for<LV>([&](auto s) {
-        const uint32_t v = (uint32_t)(cand[j][s] >> 8);
-        const bool act = v != 0u && ((uint64_t)(v ^ pre) >> (sh + 8)) == 0u;
-        const uint32_t bin = (v >> sh) & 0xFFu;
-        const uint64_t m = ballot(act);
-        if (m != 0ull) {
-          const int f = __builtin_ctzll(m);
-          const uint32_t b0 = __builtin_amdgcn_readlane(bin, f);
-          const bool same = act && bin == b0;
-          const uint64_t ms = ballot(same);
-          if (lane == f) atomicAdd(&F.hist[b0], __builtin_popcountll(ms));
-          if (act && !same) atomicAdd(&F.hist[bin], 1);
+    // the top byte takes few values: a wave counts each with ballots and adds once (same-
+    // address LDS atomics from every lane would serialise); the next byte spreads out
+    bool lanewise = lvl > 0;
+    if constexpr (lvl == 0) {
+      uint32_t bmin = 255u, bmax = 0u;
+      static_for<LSPT>([&](auto j) {
+        if (g0 + wave + j * SW < g1) {  // uniform
+          static_for<LV>([&](auto s) {
+            const uint32_t bt = (uint32_t)(cand[j][s] >> 8) >> sh;
+            bmin = min(bmin, bt);
+            bmax = max(bmax, bt);
+          });
         }
       });
-    });
+      bmin = wave_reduce(bmin, [](uint32_t x, uint32_t y) { return min(x, y); });
+      bmax = wave_reduce(bmax, [](uint32_t x, uint32_t y) { return max(x, y); });
+      if (bmax >= bmin && bmax - bmin < 8u) {
+        for (uint32_t bt = bmin; bt <= bmax; ++bt) {
+          int cnt = 0;
+          static_for<LSPT>([&](auto j) {
+            if (g0 + wave + j * SW < g1) {
+              static_for<LV>([&](auto s) {
+                cnt += __builtin_popcountll(ballot(((uint32_t)(cand[j][s] >> 8) >> sh) == bt));
+              });
+            }
+          });
+          if (lane == 0 && cnt > 0) atomicAdd(&F.hist[bt], cnt);
+        }
+      } else {
+        lanewise = bmax >= bmin;
+      }
+    }
+    if (lanewise) {
+      static_for<LSPT>([&](auto j) {
+        if (g0 + wave + j * SW < g1) {
+          static_for<LV>([&](auto s) {
+            const uint32_t v = (uint32_t)(cand[j][s] >> 8);
+            if (((uint64_t)(v ^ pre) >> (sh + 8)) == 0u) atomicAdd(&F.hist[(v >> sh) & 0xFFu], 1);
+          });
+        }
+      });
+    }
     __syncthreads();
     // wave 0 finds the byte value b: the largest with above + #(byte >= b) >= TC
     if (wave == 0) {
@@ -535,81 +554,146 @@ __device__ int row_select_fast(const char* row, int G, int V, int TC, FastLds<DT
   });
   if (pre == 0u || pre == 0xFFFFFFFFu) return 2;  // fewer than TC candidates carry a value
 
-  // C. (a wave reserves its groups' places with one atomic)
+  // C. (each thread re-reads the groups of its own lane-segments that reach t, all
+  // loads in flight at once, and stages their elements that reach t; a wave reserves
+  // its keys' places with one atomic)
   {
-    auto each_group = [&](auto&& f) {
-      static_for<LSPT>([&](auto j) {
-        const int ls = tid + j * NT;
-        if (ls < nls) {
-          const int g = ls / kWave, l = ls % kWave;
-          if ((uint32_t)(cand[j][LV - 1] >> 8) >= pre) {
-            // every candidate reaches t: others of this lane may too
-            for (int q = 0; q < kSegLoads; ++q)
-              if ((uint32_t)F.gimg[g][q * kWave + l] >= pre) f(g * kSegLoads * kWave + q * kWave + l);
-          } else {
-            static_for<LV>([&](auto s) {
-              if ((uint32_t)(cand[j][s] >> 8) >= pre)
-                f(g * kSegLoads * kWave + (int)(cand[j][s] & 0xFF) * kWave + l);
-            });
-          }
+    constexpr int SL = LSPT * LV;
+    static_assert(SL <= 32, "slot mask");
+    u32x4_t gw[LSPT][LV];
+    uint32_t lst = 0u;  // bit j*LV + s: slot (j, s) is listed
+    bool sat_any = false;
+    uint32_t satm = 0u;  // bit j: lane-segment j has all LV candidates at or above t
+    static_for<LSPT>([&](auto j) {
+      const int g = g0 + wave + j * SW;
+      const bool vj = g < g1;
+      const bool sat = vj && (uint32_t)(cand[j][LV - 1] >> 8) >= pre;
+      sat_any |= sat;
+      satm |= (uint32_t)sat << j;
+      static_for<LV>([&](auto s) {
+        gw[j][s] = u32x4_t{0u, 0u, 0u, 0u};
+        const int e0 = g * seg_elems<DT>() + ((int)(cand[j][s] & 0xFF) * kWave + lane) * EPL;
+        if (vj && (uint32_t)(cand[j][s] >> 8) >= pre && e0 < V) {
+          gw[j][s] = *(const u32x4_t*)(row + (int64_t)e0 * esz);
+          lst |= 1u << (j * LV + s);
         }
       });
-    };
-    int cnt = 0;
-    each_group([&](int) { ++cnt; });
-    const int incl = wave_incl_scan(cnt);
-    int base = 0;
-    if (lane == kWave - 1 && incl > 0) base = atomicAdd(&F.ngl, incl);
-    int off = __shfl(base, kWave - 1, kWave) + incl - cnt;
-    if (cnt > 0)
-      each_group([&](int k) {
-        if (off < kFastGroups) F.glist[off] = k;
-        ++off;
-      });
-  }
-  __syncthreads();
-  const int ngl = F.ngl;
-  if (ngl > kFastGroups) return 2;
-
-  // D. (a wave reserves its keys' places with one atomic)
-  {
-    const bool has = tid < ngl;
-    u32x4_t gw = {0u, 0u, 0u, 0u};
-    int e0 = V;
-    if (has) {
-      const int k = F.glist[tid];
-      const int g = k / (kSegLoads * kWave), gi = k % (kSegLoads * kWave);
-      e0 = g * seg_elems<DT>() + gi * EPL;
-      if (e0 < V) gw = *(const u32x4_t*)(row + (int64_t)e0 * esz);
-    }
-    float x[EPL];
-    uint32_t keep = 0u;
-    static_for<EPL>([&](auto e) {
-      if constexpr (BF) x[e] = (e & 1) ? bf16_hi(gw[e >> 1]) : bf16_lo(gw[e >> 1]);
-      else x[e] = __uint_as_float(gw[(int)e]);
-      if (has && e0 + (int)e < V && img_of<DT>(x[e]) >= pre) keep |= 1u << e;
     });
-    const int cnt = __builtin_popcount(keep);
+    auto elem = [](const u32x4_t& w, auto e) -> float {  // e: a compile-time index
+      constexpr int E = decltype(e)::value;
+      if constexpr (BF) return (E & 1) ? bf16_hi(w[E >> 1]) : bf16_lo(w[E >> 1]);
+      else return __uint_as_float(w[E]);
+    };
+    uint32_t keep[LSPT][LV];
+    int cnt = 0;
+    static_for<LSPT>([&](auto j) {
+      static_for<LV>([&](auto s) {
+        keep[j][s] = 0u;
+        if (ballot((lst >> (j * LV + s)) & 1u) != 0ull) {  // uniform skip
+          const int g = g0 + wave + j * SW;
+          const int e0 = g * seg_elems<DT>() + ((int)(cand[j][s] & 0xFF) * kWave + lane) * EPL;
+          uint32_t k = 0u;
+          static_for<EPL>([&](auto e) {
+            if (((lst >> (j * LV + s)) & 1u) && e0 + (int)e < V && img_of<DT>(elem(gw[j][s], e)) >= pre)
+              k |= 1u << e;
+          });
+          keep[j][s] = k;
+          cnt += __builtin_popcount(k);
+        }
+      });
+    });
     const int incl = wave_incl_scan(cnt);
     int base = 0;
     if (lane == kWave - 1 && incl > 0) base = atomicAdd(&F.nk, incl);
     int at = __shfl(base, kWave - 1, kWave) + incl - cnt;
-    static_for<EPL>([&](auto e) {
-      if (keep & (1u << e)) {
-        if (at < FL::KCAP) F.keys[at] = sup_key(x[e], (uint32_t)(e0 + (int)e));
-        ++at;
-      }
+    static_for<LSPT>([&](auto j) {
+      static_for<LV>([&](auto s) {
+        if (ballot(keep[j][s] != 0u) != 0ull) {
+          const int g = g0 + wave + j * SW;
+          const int e0 = g * seg_elems<DT>() + ((int)(cand[j][s] & 0xFF) * kWave + lane) * EPL;
+          static_for<EPL>([&](auto e) {
+            if (keep[j][s] & (1u << e)) {
+              if (at < FL::KCAP) F.keys[at] = sup_key(elem(gw[j][s], e), (uint32_t)(e0 + (int)e));
+              ++at;
+            }
+          });
+        }
+      });
     });
+    // a lane-segment whose LV candidates all reach t may hold more groups that do: their
+    // maxima name them, read four at a time
+    if (ballot(sat_any) != 0ull) {
+      static_for<LSPT>([&](auto j) {
+        uint32_t extra = 0u;  // bit q: group q of the lane-segment, not a candidate
+        if ((satm >> j) & 1u) {
+          static_for<kSegLoads>([&](auto q) {
+            const uint32_t im = (gmi[j][q / GPW] >> (16 * (q % GPW))) & (BF ? 0xFFFFu : 0xFFFFFFFFu);
+            if (im >= pre) extra |= 1u << q;
+          });
+          static_for<LV>([&](auto s) { extra &= ~(1u << (uint32_t)(cand[j][s] & 0xFF)); });
+        }
+        const int s0 = (g0 + wave + j * SW) * seg_elems<DT>();
+        while (ballot(extra != 0u) != 0ull) {
+          u32x4_t w[4];
+          int e0[4];
+          static_for<4>([&](auto u) {
+            w[u] = u32x4_t{0u, 0u, 0u, 0u};
+            e0[u] = V;
+            if (extra != 0u) {
+              const int q = __builtin_ctz(extra);
+              extra &= extra - 1u;
+              e0[u] = s0 + (q * kWave + lane) * EPL;
+              if (e0[u] < V) w[u] = *(const u32x4_t*)(row + (int64_t)e0[u] * esz);
+            }
+          });
+          uint32_t kp[4];
+          int c2 = 0;
+          static_for<4>([&](auto u) {
+            uint32_t k = 0u;
+            static_for<EPL>([&](auto e) {
+              if (e0[u] + (int)e < V && img_of<DT>(elem(w[u], e)) >= pre) k |= 1u << e;
+            });
+            kp[u] = k;
+            c2 += __builtin_popcount(k);
+          });
+          const int inc2 = wave_incl_scan(c2);
+          int b2 = 0;
+          if (lane == kWave - 1 && inc2 > 0) b2 = atomicAdd(&F.nk, inc2);
+          int at2 = __shfl(b2, kWave - 1, kWave) + inc2 - c2;
+          static_for<4>([&](auto u) {
+            static_for<EPL>([&](auto e) {
+              if (kp[u] & (1u << e)) {
+                if (at2 < FL::KCAP) F.keys[at2] = sup_key(elem(w[u], e), (uint32_t)(e0[u] + (int)e));
+                ++at2;
+              }
+            });
+          });
+        }
+      });
+    }
   }
   __syncthreads();
   const int nk = F.nk;
-  if (nk > FL::KCAP) return 2;
+  if (nk > FL::KCAP) floor_img = pre;  // at least TC row elements reach t
+  if (nk > FL::KCAP || nk < TC) return 2;
 
-  // E. (nk >= TC: t is reached by TC distinct candidates)
+  // D.
   for (int i = tid; i < nk; i += NT) {
     const uint64_t my = F.keys[i];
     int r = 0;
-    for (int jj = 0; jj < nk; ++jj) r += F.keys[jj] > my;
+    // two keys per read, eight reads in flight (slots past nk hold 0, below every key)
+    const int nk2 = (nk + 1) >> 1;
+    const u64x2_t* kp = (const u64x2_t*)F.keys;
+    int jj = 0;
+    for (; jj + 8 <= nk2; jj += 8) {
+      u64x2_t w[8];
+      static_for<8>([&](auto u) { w[u] = kp[jj + u]; });
+      static_for<8>([&](auto u) { r += (w[u][0] > my) + (w[u][1] > my); });
+    }
+    for (; jj < nk2; ++jj) {
+      const u64x2_t w = kp[jj];
+      r += (w[0] > my) + (w[1] > my);
+    }
     if (r < TC) s_sup[r] = my;
   }
   for (int p = TC + tid; p < N; p += NT) s_sup[p] = 0ull;
@@ -628,25 +712,25 @@ struct ExactLds {
   int nk, bad;
 };
 
-// The row's top TC keys (value desc, token id asc) into s_sup, exactly, for the rows the
-// row-wide path does not take (many ties, flat rows, rows longer than it holds), by all
-// waves of the block with few registers:
+// The top TC keys (value desc, token id asc) of the V values at row (token ids id0 ..
+// id0 + V - 1) into s_sup, exactly, where the fast path does not hold (many ties, flat
+// rows, long rows), by all SW waves of the block with few registers:
 //  1. a radix selection fixes the image t of the TC-th largest value, one byte per pass
 //     over the row (re-read; the first pass also flags NaN and +inf), and how many
 //     elements equal to t belong to the top TC;
 //  2. a last pass stages every element above t and, in token order (a block-wide scan
 //     per chunk of the row), that many elements equal to t;
 //  3. wave 0 sorts the staged keys.
-// Returns 1 for a row holding NaN or +inf, else 0; uniform over the block.
-template <int DT, int PL>
-__device__ int row_select_exact(const char* row, int V, int TC, ExactLds<PL>& X, uint64_t* s_sup,
-                                int& n_sup) {
+// Elements below floor_img (an image the TC-th largest value is known to reach) are not
+// counted. Returns 1 for a row holding NaN or +inf, else 0; uniform over the block.
+template <int DT, int PL, int SW>
+__device__ __forceinline__ int row_select_exact(const char* row, int id0, int V, int TC, uint32_t floor_img,
+                                                ExactLds<PL>& X, uint64_t* s_sup, int& n_sup) {
   constexpr bool BF = DT == VRT_BF16;
   constexpr int EPL = BF ? 8 : 4;             // elements per 16-byte vector
   constexpr int IB = BF ? 16 : 32;            // image bits
   constexpr uint32_t PINF = BF ? 0xFF80u : 0xFF800000u;  // image of +inf
   constexpr uint32_t NINF = BF ? 0x007Fu : 0x007FFFFFu;  // image of -inf
-  constexpr int SW = sel_waves<PL>();
   constexpr int NT = SW * kWave;
   constexpr int N = PL * kWave;
   const int tid = threadIdx.x;
@@ -694,7 +778,8 @@ __device__ int row_select_exact(const char* row, int V, int TC, ExactLds<PL>& X,
       static_for<EPL>([&](auto e) {
         const uint32_t x = im[e];
         if (lvl == 0) nf |= x != 0u && (x >= PINF || x < NINF);
-        if (x != 0u && ((uint64_t)(x ^ pre) >> (sh + 8)) == 0u) atomicAdd(&H[(x >> sh) & 0xFF], 1);
+        if (x >= floor_img && x != 0u && ((uint64_t)(x ^ pre) >> (sh + 8)) == 0u)
+          atomicAdd(&H[(x >> sh) & 0xFF], 1);
       });
     }
     if (lvl == 0 && ballot(nf) != 0ull && lane == 0) X.bad = 1;
@@ -744,7 +829,7 @@ __device__ int row_select_exact(const char* row, int V, int TC, ExactLds<PL>& X,
     if (v < nv) {
       images(v, im);
       static_for<EPL>([&](auto e) {
-        if (im[e] > pre) stage(im[e], v * EPL + (int)e);
+        if (im[e] > pre) stage(im[e], id0 + v * EPL + (int)e);
         nt += im[e] == pre;
       });
     }
@@ -761,7 +846,7 @@ __device__ int row_select_exact(const char* row, int V, int TC, ExactLds<PL>& X,
       if (nt > 0 && off < rem) {
         static_for<EPL>([&](auto e) {
           if (im[e] == pre) {
-            if (off < rem) stage(im[e], v * EPL + (int)e);
+            if (off < rem) stage(im[e], id0 + v * EPL + (int)e);
             ++off;
           }
         });
@@ -795,7 +880,7 @@ __device__ int row_select_exact(const char* row, int V, int TC, ExactLds<PL>& X,
 // Expansion of one parent by wave 0 (RheoSampling key design 2), BS support ranks
 // per lane: lane l owns ranks [l*BS, l*BS + BS).
 template <int BS>
-__device__ void expand_row(const BArgs& a, int b, int node, int n_sup, const uint64_t* s_buf,
+__device__ __forceinline__ void expand_row(const BArgs& a, int b, int node, int n_sup, const uint64_t* s_buf,
                            float* s_q, int64_t ncb, int cbase, int64_t ktb) {
   const Cfg& c = a.c;
   const int lane = lane_id();
@@ -933,25 +1018,16 @@ __device__ void expand_row(const BArgs& a, int b, int node, int n_sup, const uin
   }
 }
 
-// One block per expanded parent: the waves select the top N of the row's segments
-// (a wave takes segments wave, wave + 8, ...), their lists are merged pairwise through
-// LDS (the row's top trunc is in the union of the segments' top trunc), and wave 0
-// expands the parent.
-template <int DT, int PL>
-__global__ __launch_bounds__(sel_waves<PL>() * kWave)
-__attribute__((amdgpu_waves_per_eu(PL == 2 ? 4 : 2, 8))) void k_select_expand(const BArgs a) {
+// Start of a row block: at layer 0 a new step begins (every candidate of the previous
+// one is forgotten and SMART's state reset, by the block of tree b's row 0, wave 0).
+// Returns the node the row expands, or -2 after clearing the row's candidate slots
+// (no parent at this frontier position).
+__device__ __forceinline__ int begin_row(const BArgs& a, int b, int j) {
   const Cfg& c = a.c;
-  const int j = blockIdx.x, b = blockIdx.y;
   const int wave = threadIdx.x >> 6;
   const int lane = lane_id();
-  constexpr int N = PL * kWave;
   const int64_t ncb = (int64_t)b * c.NC;
-  const int cbase = layer_base(c, a.layer) + j * c.K;
-  const int ridx = row_base(c, a.layer) + j;
-  const int64_t ktb = (int64_t)b * c.NR + ridx;
-
   if (a.layer == 0 && wave == 0) {
-    // a new step: forget every candidate of the previous one, reset SMART's state
     for (int t = c.K + lane; t < c.NC; t += kWave) a.t.cand_kind[ncb + t] = 0;
     if (lane == 0) {
       double* sm = a.t.smart + (int64_t)b * 8;
@@ -960,48 +1036,137 @@ __attribute__((amdgpu_waves_per_eu(PL == 2 ? 4 : 2, 8))) void k_select_expand(co
     }
   }
   const int node = row_node(a, b, j);
-  if (node == -2) {
-    if (wave == 0) {
-      for (int s = lane; s < c.K; s += kWave) a.t.cand_kind[ncb + cbase + s] = 0;
-      if (lane == 0) a.t.row_tail_n[ktb] = 0;
-    }
+  if (node == -2 && wave == 0) {
+    const int cbase = layer_base(c, a.layer) + j * c.K;
+    for (int s = lane; s < c.K; s += kWave) a.t.cand_kind[ncb + cbase + s] = 0;
+    if (lane == 0) a.t.row_tail_n[(int64_t)b * c.NR + row_base(c, a.layer) + j] = 0;
+  }
+  return node;
+}
+
+// End of a row block, wave 0: the row's status (non-finite values, no finite value),
+// then the parent's expansion from its support s_sup (n_sup keys).
+template <int PL>
+__device__ __forceinline__ void end_row(const BArgs& a, int b, int j, int node, int n_sup, bool any_bad,
+                                        const uint64_t* s_sup, float* s_q) {
+  const Cfg& c = a.c;
+  const int lane = lane_id();
+  const int64_t ncb = (int64_t)b * c.NC;
+  const int cbase = layer_base(c, a.layer) + j * c.K;
+  const int64_t ktb = (int64_t)b * c.NR + row_base(c, a.layer) + j;
+  uint32_t st = any_bad ? VRT_ST_DRAFT_NONFINITE : 0u;
+  const float M = n_sup > 0 ? sup_key_val(s_sup[0]) : -INFINITY;
+  if (n_sup == 0 || M == -INFINITY) st |= VRT_ST_DRAFT_EMPTY;
+  if (st) {
+    if (lane == 0 && a.stats) atomicOr(a.stats + (int64_t)b * 8, st);
+    for (int s = lane; s < c.K; s += kWave) a.t.cand_kind[ncb + cbase + s] = 0;
+    if (lane == 0) a.t.row_tail_n[ktb] = 0;
     return;
   }
+  expand_row<PL>(a, b, node, n_sup, s_sup, s_q, ncb, cbase, ktb);
+}
 
+// Ranking fused into the layer's row blocks (wave 0 of each): every block counts itself
+// done on tree b's layer_sync word (after a release fence, so that its candidates are
+// visible), and the last one (after an acquire fence) sorts the layer's keys in its
+// registers and ranks them. Layer 0 has one row block per tree. The ranking block sets
+// the word back to 0 for the next layer; layer 0 starts it at 0.
+constexpr int kRankFused = 256;  // children per layer the fused ranking takes
+
+__device__ void rank_sorted(const Cfg& c, const TreePtrs& t, int layer, int b, const uint64_t* keys,
+                            int span);
+
+template <int RL>
+__device__ __forceinline__ void rank_wave(const BArgs& a, int b, uint64_t* s_rank) {
+  const Cfg& c = a.c;
+  const TreePtrs& t = a.t;
+  const int lane = lane_id();
+  const int64_t ncb = (int64_t)b * c.NC;
+  const int base = layer_base(c, a.layer);
+  const int span = layer_span(c, a.layer);
+  uint64_t k[RL];
+  static_for<RL>([&](auto s) {
+    const int i = lane * RL + s;
+    uint64_t x = 0ull;
+    if (i < span && (t.cand_kind[ncb + base + i] & 0xFF) != 0)
+      x = node_key(t.cand_score[ncb + base + i], (uint32_t)(base + i));
+    k[s] = x;
+  });
+  wave_sort_desc<RL>(k);
+  static_for<RL>([&](auto s) { s_rank[lane * RL + s] = k[s]; });
+  wave_sync();
+  if (lane == 0) rank_sorted(c, t, a.layer, b, s_rank, span);
+}
+
+__device__ __forceinline__ void rank_if_last(const BArgs& a, int b, uint64_t* s_rank) {
+  const int lane = lane_id();
+  if (gridDim.x > 1) {
+    __threadfence();
+    int old = 0;
+    if (lane == 0) old = atomicAdd(&a.t.layer_sync[b], 1);
+    old = __shfl(old, 0, kWave);
+    if (old != (int)gridDim.x - 1) return;
+    __threadfence();
+  }
+  const int span = layer_span(a.c, a.layer);
+  if (span <= kWave) rank_wave<1>(a, b, s_rank);
+  else if (span <= 2 * kWave) rank_wave<2>(a, b, s_rank);
+  else rank_wave<4>(a, b, s_rank);
+  if (lane == 0) a.t.layer_sync[b] = 0;
+}
+
+// One block per expanded parent, then wave 0 expands it. Short lists (trunc <= 256):
+// the row-wide path, the exact path behind it. Long lists: each wave selects the top
+// N of its segments (a wave takes segments wave, wave + SW, ...), their lists merge
+// pairwise through LDS (the row's top trunc is in the union of the segments' top
+// trunc).
+template <int DT, int PL>
+__global__ __launch_bounds__(sel_waves<PL>() * kWave)
+__attribute__((amdgpu_waves_per_eu(PL == 2 ? 4 : 2, 8))) void k_select_expand(const BArgs a) {
+  const Cfg& c = a.c;
+  const int j = blockIdx.x, b = blockIdx.y;
+  const int wave = threadIdx.x >> 6;
+  const int lane = lane_id();
+  constexpr int N = PL * kWave;
+  __shared__ uint64_t s_rank[kRankFused];
+  const int node = begin_row(a, b, j);
+  if (node == -2) {
+    if (wave == 0 && a.fuse_rank) rank_if_last(a, b, s_rank);
+    return;
+  }
   constexpr int SW = sel_waves<PL>();
-  // short lists: the row-wide path, the exact path behind it; long lists: per segment.
-  // The paths share one LDS area.
+  constexpr bool kShort = PL <= 4;
+  constexpr int LSPT = DT == VRT_BF16 ? 3 : 2;  // segments per wave the row-wide path takes
   struct SegPath {
     SegLds<DT, PL> seg[SW];
     uint64_t list[SW / 2][N];
   };
-  using FastT = std::conditional_t<(PL <= 4), FastLds<DT, PL>, char>;
-  using ExactT = std::conditional_t<(PL <= 4), ExactLds<PL>, char>;
-  using SegT = std::conditional_t<(PL <= 4), char, SegPath>;
-  constexpr size_t kRaw = std::max({sizeof(FastT), sizeof(ExactT), sizeof(SegT)});
-  __shared__ __align__(16) char s_raw[kRaw];
+  union ShortPath {
+    FastLds<DT, PL> f;
+    ExactLds<PL> x;
+  };
+  using Raw = std::conditional_t<kShort, ShortPath, SegPath>;
+  __shared__ __align__(16) char s_raw[sizeof(Raw)];
   __shared__ uint64_t s_sup[N];  // the support: top trunc keys, zero-padded
   __shared__ float s_q[N];
   __shared__ int s_bad[SW];
   constexpr int esz = DT == VRT_BF16 ? 2 : 4;
   const char* row = (const char*)a.logits + ((int64_t)b * a.tstride + (int64_t)j * a.ld) * esz;
   const int G = (c.V + seg_elems<DT>() - 1) / seg_elems<DT>();
-
   int n_sup = 0;
   int any_bad = 0;
-  if constexpr (PL <= 4) {
+  if constexpr (kShort) {
+    ShortPath& P = *(ShortPath*)s_raw;
     int path = 2;
-    if (G <= FastLds<DT, PL>::GMAX)
-      path = row_select_fast<DT, PL>(row, G, c.V, c.TC, *(FastT*)s_raw, s_sup, n_sup);
+    uint32_t floor_img = 0u;  // the TC-th largest row value's image is at least this
+    if (G <= LSPT * SW) path = row_select_fast<DT, PL, SW, LSPT>(row, 0, G, c.V, c.TC, P.f, s_sup, n_sup, floor_img);
     if (path == 2) {
       __syncthreads();  // s_raw changes hands
-      path = row_select_exact<DT, PL>(row, c.V, c.TC, *(ExactT*)s_raw, s_sup, n_sup);
+      path = row_select_exact<DT, PL, SW>(row, 0, c.V, c.TC, floor_img, P.x, s_sup, n_sup);
     }
-    if (path == 1) any_bad = 1;
+    any_bad = path == 1;
+    if (wave != 0) return;
   } else {
-    // per segment: each wave selects its segments' top N (segments wave, wave + SW, ..),
-    // the lists merge pairwise through LDS (the row's top trunc is in the union of the
-    // segments' top trunc)
     SegPath& P = *(SegPath*)s_raw;
     uint64_t acc[PL];
     static_for<PL>([&](auto s) { acc[s] = 0ull; });
@@ -1025,67 +1190,44 @@ __attribute__((amdgpu_waves_per_eu(PL == 2 ? 4 : 2, 8))) void k_select_expand(co
       }
       __syncthreads();
     }
-    if (wave == 0) {
-      int cnt = 0;
-      static_for<PL>([&](auto s) {
-        const int p = lane * PL + s;
-        const uint64_t k = p < c.TC ? acc[s] : 0ull;
-        s_sup[p] = k;
-        cnt += k != 0ull;
-      });
-      n_sup = wave_sum_i(cnt);
-      for (int w = 0; w < SW; ++w) any_bad |= s_bad[w];
-    }
+    if (wave != 0) return;
+    int cnt = 0;
+    static_for<PL>([&](auto s) {
+      const int q = lane * PL + s;
+      const uint64_t k = q < c.TC ? acc[s] : 0ull;
+      s_sup[q] = k;
+      cnt += k != 0ull;
+    });
+    n_sup = wave_sum_i(cnt);
+    for (int w = 0; w < SW; ++w) any_bad |= s_bad[w];
   }
-  if (wave != 0) return;
-  uint64_t* s_buf = s_sup;
   wave_sync();
-
-  uint32_t st = any_bad ? VRT_ST_DRAFT_NONFINITE : 0u;
-  const float M = n_sup > 0 ? sup_key_val(s_buf[0]) : -INFINITY;
-  if (n_sup == 0 || M == -INFINITY) st |= VRT_ST_DRAFT_EMPTY;
-  if (st) {
-    if (lane == 0 && a.stats) atomicOr(a.stats + (int64_t)b * 8, st);
-    for (int s = lane; s < c.K; s += kWave) a.t.cand_kind[ncb + cbase + s] = 0;
-    if (lane == 0) a.t.row_tail_n[ktb] = 0;
-    return;
-  }
-  expand_row<PL>(a, b, node, n_sup, s_buf, s_q, ncb, cbase, ktb);
+  end_row<PL>(a, b, j, node, n_sup, any_bad != 0, s_sup, s_q);
+  if (a.fuse_rank) rank_if_last(a, b, s_rank);
 }
 
-// Per-tree ranking of the layer's children: top-W frontier (top-R mode) or SMART.
-__global__ __launch_bounds__(256) void k_rank_layer(const Cfg c, const TreePtrs t, int layer) {
-  const int b = blockIdx.x;
+// Per-tree ranking of the layer's children, given their keys sorted (path score
+// desc, creation index asc; zeros last): the top W become the frontier (top-R mode),
+// or SMART's sequential keep rule runs over them. One thread.
+__device__ void rank_sorted(const Cfg& c, const TreePtrs& t, int layer, int b, const uint64_t* keys,
+                            int span) {
   const int64_t ncb = (int64_t)b * c.NC;
-  const int base = layer_base(c, layer);
-  const int span = layer_span(c, layer);
-  const int np = next_pow2(max(span, 2));
-  extern __shared__ uint64_t s_keys[];
-  for (int i = threadIdx.x; i < np; i += blockDim.x) {
-    uint64_t k = 0ull;
-    if (i < span && (t.cand_kind[ncb + base + i] & 0xFF) != 0)
-      k = node_key(t.cand_score[ncb + base + i], (uint32_t)(base + i));
-    s_keys[i] = k;
-  }
-  __syncthreads();
-  bitonic_desc(s_keys, np);
-  if (threadIdx.x != 0) return;
   const bool more = layer + 1 < c.D;
   int* front = t.front + (int64_t)b * c.FP;
   int nf = 0;
   if (c.mode == VRT_MODE_TOPR) {
     if (more)
-      for (int i = 0; i < span && nf < c.W && s_keys[i] != 0ull; ++i)
-        front[nf++] = (int)(0xFFFFFFFFu - (uint32_t)s_keys[i]);
+      for (int i = 0; i < span && nf < c.W && keys[i] != 0ull; ++i)
+        front[nf++] = (int)(0xFFFFFFFFu - (uint32_t)keys[i]);
   } else {
     // SMART key design 3: keep u iff alpha * g * C(|T|) > L * C'(|T|), g = P(path)/|P|;
     // the first rejection ends the layer
     double* sm = t.smart + (int64_t)b * 8;
     double L = sm[0], n = sm[1], P = sm[2], nadm = sm[3], root_has = sm[4];
     int* adm = t.admitted + (int64_t)b * c.N;
-    for (int i = 0; i < span && s_keys[i] != 0ull; ++i) {
+    for (int i = 0; i < span && keys[i] != 0ull; ++i) {
       if (nadm >= (double)c.budget) break;
-      const int cu = (int)(0xFFFFFFFFu - (uint32_t)s_keys[i]);
+      const int cu = (int)(0xFFFFFFFFu - (uint32_t)keys[i]);
       const double g = (double)t.cand_score[ncb + cu] / P;
       const double Cn = c.lam * n + c.gam * (exp(c.del * pow(n, c.rho)) - 1.0);
       const double dC = c.lam + c.gam * c.del * c.rho * pow(n, c.rho - 1.0) * exp(c.del * pow(n, c.rho));
@@ -1104,6 +1246,26 @@ __global__ __launch_bounds__(256) void k_rank_layer(const Cfg c, const TreePtrs 
     sm[0] = L; sm[1] = n; sm[2] = P; sm[3] = nadm; sm[4] = root_has;
   }
   t.n_front[b] = nf;
+}
+
+// Ranking as a kernel of its own (layers of more than kRankFused children): one block
+// per tree sorts the keys in LDS.
+__global__ __launch_bounds__(256) void k_rank_layer(const Cfg c, const TreePtrs t, int layer) {
+  const int b = blockIdx.x;
+  const int64_t ncb = (int64_t)b * c.NC;
+  const int base = layer_base(c, layer);
+  const int span = layer_span(c, layer);
+  const int np = next_pow2(max(span, 2));
+  extern __shared__ uint64_t s_keys[];
+  for (int i = threadIdx.x; i < np; i += blockDim.x) {
+    uint64_t k = 0ull;
+    if (i < span && (t.cand_kind[ncb + base + i] & 0xFF) != 0)
+      k = node_key(t.cand_score[ncb + base + i], (uint32_t)(base + i));
+    s_keys[i] = k;
+  }
+  __syncthreads();
+  bitonic_desc(s_keys, np);
+  if (threadIdx.x == 0) rank_sorted(c, t, layer, b, s_keys, span);
 }
 
 constexpr int kFT = 1024;          // threads of the finish block
@@ -1371,13 +1533,14 @@ size_t build_ws_bytes(const Cfg& c) {
 hipError_t launch_build_layer(const Cfg& c, const TreePtrs& t, int layer, const void* logits,
                               int64_t ld, int64_t tstride, uint64_t seed, uint32_t step,
                               uint32_t* stats, void* ws, hipStream_t stream) {
-  (void)ws;
-  BArgs a{c, t, layer, logits, ld, tstride, seed, step, stats};
+  const int span = (layer == 0 ? 1 : c.P) * c.K;
+  BArgs a{c, t, layer, logits, ld, tstride, seed, step, stats, span <= kRankFused ? 1 : 0};
   const int rows = layer == 0 ? 1 : c.FP;
+  (void)ws;
   hipError_t e = c.dtype == VRT_BF16 ? launch_layer<VRT_BF16>(a, rows, stream)
                                      : launch_layer<VRT_F32>(a, rows, stream);
   if (e != hipSuccess) return e;
-  const int span = (layer == 0 ? 1 : c.P) * c.K;
+  if (a.fuse_rank) return hipSuccess;
   const size_t lds2 = (size_t)next_pow2(max(span, 2)) * 8;
   hipLaunchKernelGGL(k_rank_layer, dim3(c.B), dim3(256), lds2, stream, c, t, layer);
   return hipGetLastError();

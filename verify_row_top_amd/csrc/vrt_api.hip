@@ -48,6 +48,7 @@ bool compute_layout(const vrt_config& c, vrt_tree_layout* L) {
   take(&L->n_front, B * 4);
   take(&L->smart, B * 8 * 8);
   take(&L->admitted, B * L->N * 4);
+  take(&L->layer_sync, B * 4);
   take(&L->n_nodes, B * 4);
   take(&L->node_token, B * L->N * 4);
   take(&L->node_parent, B * L->N * 4);
@@ -134,6 +135,7 @@ TreePtrs tree_ptrs(const vrt_config& c, void* blob) {
   t.n_front = (int*)(p + L.n_front);
   t.smart = (double*)(p + L.smart);
   t.admitted = (int*)(p + L.admitted);
+  t.layer_sync = (int*)(p + L.layer_sync);
   t.n_nodes = (int*)(p + L.n_nodes);
   t.node_token = (int*)(p + L.node_token);
   t.node_parent = (int*)(p + L.node_parent);

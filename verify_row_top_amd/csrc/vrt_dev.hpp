@@ -79,6 +79,7 @@ __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 // 16-byte streaming load with the non-temporal hint: data read once is not kept
 // in the caches (measured ~10% more HBM read bandwidth for row streams).
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint64_t u64x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint4 load_nt(const void* p) {
   const u32x4_t t = __builtin_nontemporal_load((const u32x4_t*)p);
   return make_uint4(t.x, t.y, t.z, t.w);

@@ -35,6 +35,7 @@ struct TreePtrs {
   int* n_front;
   double* smart;
   int* admitted;
+  int* layer_sync;
   int* n_nodes;
   int* node_token;
   int* node_parent;

@@ -37,7 +37,7 @@ class Config(ctypes.Structure):
 class TreeLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "NC", "NR", "N", "TC", "FP", "cand_token", "cand_parent", "cand_score", "cand_kind",
-        "row_tail_n", "row_tail_id", "row_tail_q", "front", "n_front", "smart", "admitted",
+        "row_tail_n", "row_tail_id", "row_tail_q", "front", "n_front", "smart", "admitted", "layer_sync",
         "n_nodes", "node_token", "node_parent", "node_depth", "node_kind", "node_cand",
         "child_off", "child", "tail_n", "tail_id", "tail_q", "total_bytes")]
 
@@ -157,7 +157,7 @@ _FIELDS = {
     "cand_kind": ("i32", ("NC",)), "row_tail_n": ("i32", ("NR",)),
     "row_tail_id": ("i32", ("NR", "TC")), "row_tail_q": ("f32", ("NR", "TC")),
     "front": ("i32", ("FP",)), "n_front": ("i32", ()), "smart": ("f64", (8,)),
-    "admitted": ("i32", ("N",)), "n_nodes": ("i32", ()), "node_token": ("i32", ("N",)),
+    "admitted": ("i32", ("N",)), "layer_sync": ("i32", ()), "n_nodes": ("i32", ()), "node_token": ("i32", ("N",)),
     "node_parent": ("i32", ("N",)), "node_depth": ("i32", ("N",)), "node_kind": ("i32", ("N",)),
     "node_cand": ("i32", ("N",)), "child_off": ("i32", ("N+1",)), "child": ("i32", ("N",)),
     "tail_n": ("i32", ("N",)), "tail_id": ("i32", ("N", "TC")), "tail_q": ("f32", ("N", "TC")),
