@@ -384,6 +384,11 @@ __device__ __forceinline__ void seg_select(const char* row, int g, int V, SegLds
 // Row-wide selection (the usual path for short lists): one threshold for the whole
 // row instead of one list per segment.
 
+// The usual threshold search: one histogram of the candidates' distance below the
+// largest one, in 1/kDistScale steps of value, kDistBins bins.
+constexpr int kDistBins = 1024;
+constexpr float kDistScale = 64.0f;
+
 template <int DT, int PL>
 struct FastLds {
   static constexpr int LV = PL <= 2 ? 4 : 2 * PL;      // candidates per lane and segment
@@ -391,8 +396,9 @@ struct FastLds {
   // a candidate: group maximum's image << 8 | its load index q
   using CK = std::conditional_t<DT == VRT_BF16, uint32_t, uint64_t>;
   alignas(16) uint64_t keys[KCAP];        // row keys of the elements that reach it
-  int hist[256];
+  int hist[kDistBins];  // distance histogram; its first 256 bins serve the radix levels
   int sel[2];
+  int wmax[16];
   int nk, bad;
 };
 
@@ -432,7 +438,7 @@ __device__ __forceinline__ int row_select_fast(const char* row, int g0, int g1, 
     F.nk = 0;
     F.bad = 0;
   }
-  if (tid < 256) F.hist[tid] = 0;
+  for (int i = tid; i < kDistBins; i += NT) F.hist[i] = 0;
   for (int i = tid; i < FL::KCAP; i += NT) F.keys[i] = 0ull;
   __syncthreads();
 
@@ -463,12 +469,66 @@ __device__ __forceinline__ int row_select_fast(const char* row, int g0, int g1, 
       });
     }
   });
+  {
+    uint32_t mx = 0u;  // the wave's largest candidate image
+    static_for<LSPT>([&](auto j) { mx = max(mx, (uint32_t)(cand[j][0] >> 8)); });
+    mx = wave_reduce(mx, [](uint32_t x, uint32_t y) { return max(x, y); });
+    if (lane == 0) F.wmax[wave] = mx;
+  }
   if (ballot(nf) != 0ull && lane == 0) F.bad = 1;
   __syncthreads();
   if (F.bad) return 1;
 
-  // B.
+  // B. Usually one histogram of the candidates' value distance below the largest, Mv
+  // (bin = floor(kDistScale * (Mv - x))), finds the smallest bin d that TC candidates
+  // reach; t is then the smallest image whose value falls in bins 0..d (a binary search:
+  // the bin is monotone in the value). When fewer than TC candidates lie in the window,
+  // a radix selection over the images.
+  uint32_t M = 0u;
+  static_for<SW>([&](auto w) { M = max(M, (uint32_t)F.wmax[w]); });
+  const float Mv = value_of<DT>(M);
+  auto dist = [&](uint32_t im) { return (Mv - value_of<DT>(im)) * kDistScale; };
+  static_for<LSPT>([&](auto j) {
+    if (g0 + wave + j * SW < g1) {  // uniform
+      static_for<LV>([&](auto s) {
+        const float dd = dist((uint32_t)(cand[j][s] >> 8));
+        if (dd < (float)(kDistBins - 1)) atomicAdd(&F.hist[(int)dd], 1);
+      });
+    }
+  });
+  __syncthreads();
+  if (wave == 0) {
+    constexpr int HB = kDistBins / kWave;
+    int h[HB];
+    static_for<HB>([&](auto i) { h[i] = F.hist[lane * HB + i]; });  // ascending distance
+    int ls = 0;
+    static_for<HB>([&](auto i) { ls += h[i]; });
+    int cum = wave_incl_scan(ls) - ls;
+    int pick = -1;
+    static_for<HB>([&](auto i) {
+      cum += h[i];
+      if (pick < 0 && cum >= TC) pick = lane * HB + i;
+    });
+    const uint64_t has = ballot(pick >= 0);
+    const int d = __shfl(pick, has ? __builtin_ctzll(has) : 0, kWave);
+    if (lane == 0) F.sel[0] = has ? d : -1;
+  }
+  __syncthreads();
+  const int dsel = F.sel[0];
   uint32_t pre = 0u;   // image bits fixed so far (the high ones)
+  if (dsel >= 0) {
+    // smallest image in bins 0..dsel: dist(lo) is outside (or NaN), dist(hi) inside
+    const float lim = (float)(dsel + 1);
+    uint32_t lo = BF ? 0x007Eu : 0x007FFFFEu, hi = M;
+    while (hi - lo > 1u) {
+      const uint32_t mid = lo + ((hi - lo) >> 1);
+      if (dist(mid) < lim) hi = mid;
+      else lo = mid;
+    }
+    pre = hi;
+  } else {
+  if (tid < 256) F.hist[tid] = 0;
+  __syncthreads();
   int above = 0;       // candidates whose fixed bits exceed pre's
   static_for<RB / 8>([&](auto lvl) {
     constexpr int sh = RB - 8 * (lvl + 1);
@@ -552,6 +612,7 @@ __device__ __forceinline__ int row_select_fast(const char* row, int g0, int g1, 
     __syncthreads();
     if (bsel < 0) pre = 0xFFFFFFFFu;  // marks "fewer than TC candidates"
   });
+  }
   if (pre == 0u || pre == 0xFFFFFFFFu) return 2;  // fewer than TC candidates carry a value
 
   // C. (each thread re-reads the groups of its own lane-segments that reach t, all
@@ -880,8 +941,9 @@ __device__ __forceinline__ int row_select_exact(const char* row, int id0, int V,
 // Expansion of one parent by wave 0 (RheoSampling key design 2), BS support ranks
 // per lane: lane l owns ranks [l*BS, l*BS + BS).
 template <int BS>
-__device__ __forceinline__ void expand_row(const BArgs& a, int b, int node, int n_sup, const uint64_t* s_buf,
-                           float* s_q, int64_t ncb, int cbase, int64_t ktb) {
+__device__ __forceinline__ void expand_row(const BArgs& a, int b, int node, float sp, int n_sup,
+                                           const uint64_t* s_buf, float* s_q, int64_t ncb, int cbase,
+                                           int64_t ktb) {
   const Cfg& c = a.c;
   const int lane = lane_id();
   const float M = sup_key_val(s_buf[0]);
@@ -987,7 +1049,6 @@ __device__ __forceinline__ void expand_row(const BArgs& a, int b, int node, int 
   }
 
   // child slots: DET ranks, the probe, then fillers in rank order. Lane s writes slot s.
-  const float sp = node < 0 ? 1.0f : a.t.cand_score[ncb + node];
   int r_of_slot = -1, kind = 0;
   {
     const int m_det = c.probe ? min(m, n_sup) : 0;
@@ -1047,8 +1108,8 @@ __device__ __forceinline__ int begin_row(const BArgs& a, int b, int j) {
 // End of a row block, wave 0: the row's status (non-finite values, no finite value),
 // then the parent's expansion from its support s_sup (n_sup keys).
 template <int PL>
-__device__ __forceinline__ void end_row(const BArgs& a, int b, int j, int node, int n_sup, bool any_bad,
-                                        const uint64_t* s_sup, float* s_q) {
+__device__ __forceinline__ void end_row(const BArgs& a, int b, int j, int node, float sp, int n_sup,
+                                        bool any_bad, const uint64_t* s_sup, float* s_q) {
   const Cfg& c = a.c;
   const int lane = lane_id();
   const int64_t ncb = (int64_t)b * c.NC;
@@ -1063,7 +1124,7 @@ __device__ __forceinline__ void end_row(const BArgs& a, int b, int j, int node, 
     if (lane == 0) a.t.row_tail_n[ktb] = 0;
     return;
   }
-  expand_row<PL>(a, b, node, n_sup, s_sup, s_q, ncb, cbase, ktb);
+  expand_row<PL>(a, b, node, sp, n_sup, s_sup, s_q, ncb, cbase, ktb);
 }
 
 // Ranking fused into the layer's row blocks (wave 0 of each): every block counts itself
@@ -1134,6 +1195,8 @@ __attribute__((amdgpu_waves_per_eu(PL == 2 ? 4 : 2, 8))) void k_select_expand(co
     if (wave == 0 && a.fuse_rank) rank_if_last(a, b, s_rank);
     return;
   }
+  // the parent's path score, read now (wave 0 uses it at the end)
+  const float sp = node < 0 ? 1.0f : a.t.cand_score[(int64_t)b * c.NC + node];
   constexpr int SW = sel_waves<PL>();
   constexpr bool kShort = PL <= 4;
   constexpr int LSPT = DT == VRT_BF16 ? 3 : 2;  // segments per wave the row-wide path takes
@@ -1202,7 +1265,7 @@ __attribute__((amdgpu_waves_per_eu(PL == 2 ? 4 : 2, 8))) void k_select_expand(co
     for (int w = 0; w < SW; ++w) any_bad |= s_bad[w];
   }
   wave_sync();
-  end_row<PL>(a, b, j, node, n_sup, any_bad != 0, s_sup, s_q);
+  end_row<PL>(a, b, j, node, sp, n_sup, any_bad != 0, s_sup, s_q);
   if (a.fuse_rank) rank_if_last(a, b, s_rank);
 }
 
