@@ -1066,15 +1066,15 @@ __device__ __forceinline__ void expand_row(const BArgs& a, int b, int node, floa
       if (r < n_sup) r_of_slot = r, kind = VRT_FILL;
     }
   }
-  if (lane < c.K) {
+  if (lane < c.K) {  // device-coherent: the layer's ranking block reads them
     const int64_t ci = ncb + cbase + lane;
     if (r_of_slot >= 0) {
-      a.t.cand_token[ci] = (int)sup_key_id(s_buf[r_of_slot]);
-      a.t.cand_parent[ci] = node;
-      a.t.cand_score[ci] = sp * (kind == VRT_PROBE ? proxy : s_q[r_of_slot]);
-      a.t.cand_kind[ci] = kind;
+      st_dev(&a.t.cand_token[ci], (int)sup_key_id(s_buf[r_of_slot]));
+      st_dev(&a.t.cand_parent[ci], node);
+      st_dev(&a.t.cand_score[ci], sp * (kind == VRT_PROBE ? proxy : s_q[r_of_slot]));
+      st_dev(&a.t.cand_kind[ci], kind);
     } else {
-      a.t.cand_kind[ci] = 0;
+      st_dev(&a.t.cand_kind[ci], 0);
     }
   }
 }
@@ -1099,7 +1099,7 @@ __device__ __forceinline__ int begin_row(const BArgs& a, int b, int j) {
   const int node = row_node(a, b, j);
   if (node == -2 && wave == 0) {
     const int cbase = layer_base(c, a.layer) + j * c.K;
-    for (int s = lane; s < c.K; s += kWave) a.t.cand_kind[ncb + cbase + s] = 0;
+    for (int s = lane; s < c.K; s += kWave) st_dev(&a.t.cand_kind[ncb + cbase + s], 0);
     if (lane == 0) a.t.row_tail_n[(int64_t)b * c.NR + row_base(c, a.layer) + j] = 0;
   }
   return node;
@@ -1120,18 +1120,18 @@ __device__ __forceinline__ void end_row(const BArgs& a, int b, int j, int node, 
   if (n_sup == 0 || M == -INFINITY) st |= VRT_ST_DRAFT_EMPTY;
   if (st) {
     if (lane == 0 && a.stats) atomicOr(a.stats + (int64_t)b * 8, st);
-    for (int s = lane; s < c.K; s += kWave) a.t.cand_kind[ncb + cbase + s] = 0;
+    for (int s = lane; s < c.K; s += kWave) st_dev(&a.t.cand_kind[ncb + cbase + s], 0);
     if (lane == 0) a.t.row_tail_n[ktb] = 0;
     return;
   }
   expand_row<PL>(a, b, node, sp, n_sup, s_sup, s_q, ncb, cbase, ktb);
 }
 
-// Ranking fused into the layer's row blocks (wave 0 of each): every block counts itself
-// done on tree b's layer_sync word (after a release fence, so that its candidates are
-// visible), and the last one (after an acquire fence) sorts the layer's keys in its
-// registers and ranks them. Layer 0 has one row block per tree. The ranking block sets
-// the word back to 0 for the next layer; layer 0 starts it at 0.
+// Ranking fused into the layer's row blocks (wave 0 of each): every block writes its
+// candidates device-coherently, waits for the stores and counts itself done on tree
+// b's layer_sync word; the last one reads the layer's candidates device-coherently,
+// sorts their keys in its registers and ranks them. Layer 0 has one row block per tree.
+// The ranking block sets the word back to 0 for the next layer; layer 0 starts it at 0.
 constexpr int kRankFused = 256;  // children per layer the fused ranking takes
 
 __device__ void rank_sorted(const Cfg& c, const TreePtrs& t, int layer, int b, const uint64_t* keys,
@@ -1149,8 +1149,8 @@ __device__ __forceinline__ void rank_wave(const BArgs& a, int b, uint64_t* s_ran
   static_for<RL>([&](auto s) {
     const int i = lane * RL + s;
     uint64_t x = 0ull;
-    if (i < span && (t.cand_kind[ncb + base + i] & 0xFF) != 0)
-      x = node_key(t.cand_score[ncb + base + i], (uint32_t)(base + i));
+    if (i < span && (ld_dev(&t.cand_kind[ncb + base + i]) & 0xFF) != 0)
+      x = node_key(ld_dev(&t.cand_score[ncb + base + i]), (uint32_t)(base + i));
     k[s] = x;
   });
   wave_sort_desc<RL>(k);
@@ -1162,12 +1162,11 @@ __device__ __forceinline__ void rank_wave(const BArgs& a, int b, uint64_t* s_ran
 __device__ __forceinline__ void rank_if_last(const BArgs& a, int b, uint64_t* s_rank) {
   const int lane = lane_id();
   if (gridDim.x > 1) {
-    __threadfence();
+    wait_stores();
     int old = 0;
     if (lane == 0) old = atomicAdd(&a.t.layer_sync[b], 1);
     old = __shfl(old, 0, kWave);
     if (old != (int)gridDim.x - 1) return;
-    __threadfence();
   }
   const int span = layer_span(a.c, a.layer);
   if (span <= kWave) rank_wave<1>(a, b, s_rank);
@@ -1291,11 +1290,11 @@ __device__ void rank_sorted(const Cfg& c, const TreePtrs& t, int layer, int b, c
     for (int i = 0; i < span && keys[i] != 0ull; ++i) {
       if (nadm >= (double)c.budget) break;
       const int cu = (int)(0xFFFFFFFFu - (uint32_t)keys[i]);
-      const double g = (double)t.cand_score[ncb + cu] / P;
+      const double g = (double)ld_dev(&t.cand_score[ncb + cu]) / P;
       const double Cn = c.lam * n + c.gam * (exp(c.del * pow(n, c.rho)) - 1.0);
       const double dC = c.lam + c.gam * c.del * c.rho * pow(n, c.rho - 1.0) * exp(c.del * pow(n, c.rho));
       if (!(c.alpha * g * Cn > L * dC)) break;
-      const int par = t.cand_parent[ncb + cu];
+      const int par = ld_dev(&t.cand_parent[ncb + cu]);
       const bool has = par < 0 ? root_has != 0.0 : (t.cand_kind[ncb + par] & 0x100) != 0;
       L += g;
       n += 1.0;

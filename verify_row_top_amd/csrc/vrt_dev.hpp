@@ -80,6 +80,20 @@ __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 // in the caches (measured ~10% more HBM read bandwidth for row streams).
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint64_t u64x2_t __attribute__((ext_vector_type(2)));
+
+// Device-coherent (every XCD) 32-bit store and load, for words that blocks of one
+// launch hand to each other: the store is written through the XCD's L2 and the load
+// does not take a possibly stale L2 copy, so neither side needs an L2 write-back or
+// invalidate fence. The writer waits for its stores (wait_stores) before it signals.
+__device__ __forceinline__ void st_dev(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(float* p, float v) { st_dev((int*)p, __float_as_int(v)); }
+__device__ __forceinline__ int ld_dev(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) { return __int_as_float(ld_dev((const int*)p)); }
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0); }
 __device__ __forceinline__ uint4 load_nt(const void* p) {
   const u32x4_t t = __builtin_nontemporal_load((const u32x4_t*)p);
   return make_uint4(t.x, t.y, t.z, t.w);
