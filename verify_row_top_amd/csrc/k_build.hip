@@ -1,18 +1,19 @@
 // Draft-tree construction on gfx950 (RheoSampling framework flowchart, key designs
-// 1-2; SMART key design 3 as the switchable keep rule). Per layer, two kernels;
-// then one to emit the tree:
+// 1-2; SMART key design 3 as the switchable keep rule). Per layer one kernel, then one
+// to emit the tree:
 //
-// k_select_expand: one 8-wave block per expanded parent. Each wave selects the top
-//   keys (logit desc, token id asc) of 16 KB segments of the parent's draft row: all
-//   loads in flight at once (non-temporal), a threshold from the lanes' largest values
-//   that at least N elements reach, exact keys only for the few survivors, bitonic
-//   sorts by cross-lane shuffles. The waves' lists merge pairwise through LDS; wave 0
-//   then expands the parent: untempered softmax on the top-trunc support with the
-//   fixed ranking recipe, tempered softmax in fp64, the probe draw from the tempered
-//   tail, the proxy min{q(x_m), z}, the K child slots and the parent's tail table.
-// k_rank_layer: one block per tree ranks the layer's children by (path score desc,
-//   creation index asc) and keeps the top W (top-R mode) or runs SMART's sequential
-//   keep rule over them.
+// k_select_expand: one 8-wave block per expanded parent. Short lists (trunc <= 256):
+//   the waves stream the parent's draft row once (all of a segment's loads in flight,
+//   non-temporal), keep each lane's largest group maxima, find one threshold for the
+//   whole row from a histogram of their distance below the largest, re-read only the
+//   groups that reach it and rank the exact keys; rows with many ties take an exact
+//   radix selection instead. Long lists: per-segment selection and pairwise merges.
+//   Wave 0 then expands the parent: untempered softmax on the top-trunc support with
+//   the fixed ranking recipe, tempered softmax in fp64, the probe draw from the
+//   tempered tail, the proxy min{q(x_m), z}, the K child slots and the parent's tail
+//   table. The last row block of each tree ranks the layer's children by (path score
+//   desc, creation index asc) and keeps the top W (top-R mode) or runs SMART's
+//   sequential keep rule (k_rank_layer does this for layers of more than 256 children).
 // k_finish: one block per tree emits the tree: the global top R by the same key
 //   (or SMART's admitted nodes), parents before children, child lists in slot
 //   order, and the probe tails the verifier needs.
