@@ -209,6 +209,21 @@ vrt_status vrt_verify_tree(const vrt_config* cfg, const void* target_logits, int
                            void* ws, size_t ws_bytes, int32_t* out_tokens, int32_t* out_nodes,
                            int32_t* out_len, uint32_t* stats, int32_t* node_out, void* stream);
 
+/* The verification in its two parts, for callers that time or schedule them apart:
+ * vrt_verify_nodes decides every node of every tree (its row statistics, the probe-first
+ * test, the rejections of the other kept children, the final sample as if the walk
+ * reached it) into node_out; vrt_verify_walk then follows the accepted children from
+ * each root and writes out_tokens, out_nodes, out_len and stats. Together they do
+ * exactly what vrt_verify_tree does. Arguments as there; both calls must get the same
+ * ws and node_out (node_out NULL: the decisions stay in ws between the two calls).
+ * vrt_verify_walk reads no logits. Errors: as vrt_verify_tree. */
+vrt_status vrt_verify_nodes(const vrt_config* cfg, const void* target_logits, int64_t ld,
+                            int64_t tree_stride, const void* tree, uint64_t seed, uint64_t step,
+                            void* ws, size_t ws_bytes, int32_t* node_out, void* stream);
+vrt_status vrt_verify_walk(const vrt_config* cfg, const void* tree, void* ws, size_t ws_bytes,
+                           int32_t* out_tokens, int32_t* out_nodes, int32_t* out_len, uint32_t* stats,
+                           int32_t* node_out, void* stream);
+
 /* Description of the last error on this host thread ("" if none). */
 const char* vrt_last_error(void);
 

@@ -115,3 +115,29 @@ def test_verify_argument_errors_are_caught_before_any_launch():
     assert call(wsb=8) == vrt.ENOMEM
     assert call(ld=10) == vrt.EINVAL
     assert call(stride=-16) == vrt.EINVAL
+
+
+def test_split_verify_argument_errors_are_caught_before_any_launch():
+    c = vrt.make_config(B=2, V=1000, K=4, D=3, R=10)
+    L = vrt.lib()
+    v = ctypes.c_void_p
+    # decisions: target rows are checked, outputs are not needed
+    assert L.vrt_verify_nodes(ctypes.byref(c), v(0), 1024, 4096, v(0x20000), 1, 0, v(0x30000), 1 << 30,
+                              None, None) == vrt.EINVAL
+    assert L.vrt_verify_nodes(ctypes.byref(c), v(0x10000), 1024, 4096, v(0x20000), 1, 0, v(0x30000), 8,
+                              None, None) == vrt.ENOMEM
+    assert "workspace" in vrt.last_error()
+    assert L.vrt_verify_nodes(ctypes.byref(c), v(0x10000), 10, 4096, v(0x20000), 1, 0, v(0x30000),
+                              1 << 30, None, None) == vrt.EINVAL
+    # the walk: outputs are checked, no logits
+    good = dict(tree=0x20000, ws=0x30000, wsb=1 << 30, o=0x40000, n=0x50000, ln=0x60000, st=0x70000)
+
+    def walk(**kw):
+        a = dict(good, **kw)
+        return L.vrt_verify_walk(ctypes.byref(c), v(a["tree"]), v(a["ws"]), a["wsb"], v(a["o"]), v(a["n"]),
+                                 v(a["ln"]), v(a["st"]), None, None)
+    assert walk(o=0) == vrt.EINVAL
+    assert walk(st=0) == vrt.EINVAL
+    assert walk(tree=0) == vrt.EINVAL
+    assert walk(wsb=8) == vrt.ENOMEM
+    assert walk(ws=0x30008) == vrt.EINVAL  # not 16-byte aligned

@@ -12,6 +12,8 @@ import numpy as np
 import pytest
 import torch
 
+from verify_row_top_amd import vrt
+
 import synth
 from synth import workloads
 from tests.gpu_common import Lib, lib_config, to_device_rows
@@ -147,3 +149,26 @@ def test_bad_draft_rows_set_status_and_stay_in_bounds(gpu):
     assert st[0] & 0x1 and st[1] & 0x2 and st[2] == 0
     n = L.views["n_nodes"].cpu().numpy()
     assert n[0] == 1 and n[1] == 1 and n[2] > 1
+
+
+def test_split_verification_equals_the_whole_call(gpu):
+    """vrt_verify_nodes then vrt_verify_walk give exactly what vrt_verify_tree gives, with
+    the decisions in the caller's node_out or in the workspace."""
+    w = _small(B=6, V=7000, R=30, D=5)
+    steps = [OracleStep(w, 4, b, 2) for b in range(w.B)]
+    L = gpu_build(w, steps, 4, 2, gpu)
+    target, ld = to_device_rows([s.target_rows for s in steps], w, L.N, gpu)
+    L.verify(target, ld, 4, 2)
+    ref = [x.clone() for x in (L.out_tokens, L.out_nodes, L.out_len, L.stats, L.node_out)]
+    for use_node_out in (True, False):
+        for x in (L.out_tokens, L.out_nodes, L.out_len, L.stats, L.node_out):
+            x.fill_(-7)
+        L.stats.zero_()
+        no = L.node_out if use_node_out else None
+        vrt.verify_nodes(L.cfg, target, ld, target.stride(0), L.tree, 4, 2, L.ws, node_out=no)
+        vrt.verify_walk(L.cfg, L.tree, L.ws, L.out_tokens, L.out_nodes, L.out_len, L.stats, node_out=no)
+        torch.cuda.synchronize()
+        for a, b in zip((L.out_tokens, L.out_nodes, L.out_len, L.stats), ref[:4]):
+            assert torch.equal(a, b)
+        if use_node_out:
+            assert torch.equal(L.node_out, ref[4])

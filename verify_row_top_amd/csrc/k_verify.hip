@@ -673,21 +673,24 @@ size_t verify_ws_bytes(const Cfg& c) {
   return 0;
 }
 
-hipError_t launch_verify(const Cfg& c, const TreePtrs& t, const void* logits, int64_t ld,
+hipError_t launch_verify(int parts, const Cfg& c, const TreePtrs& t, const void* logits, int64_t ld,
                          int64_t tstride, uint64_t seed, uint32_t step, NodeOut* node_out,
                          int32_t* out_tokens, int32_t* out_nodes, int32_t* out_len, uint32_t* stats,
                          void* ws, hipStream_t stream) {
   (void)ws;
   VArgs a{c, t, logits, ld, tstride, seed, step, node_out, out_tokens, out_nodes, out_len, stats};
-  const dim3 grid(c.N, c.B);
-  const size_t lds = decide_lds_bytes(c);
-  if (c.dtype == VRT_BF16)
-    hipLaunchKernelGGL(k_vnode<VRT_BF16>, grid, dim3(kVB), lds, stream, a);
-  else
-    hipLaunchKernelGGL(k_vnode<VRT_F32>, grid, dim3(kVB), lds, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_vwalk, dim3(c.B), dim3(kWave), (size_t)c.N * (16 + 4 + 4), stream, a);
+  if (parts & 1) {
+    const dim3 grid(c.N, c.B);
+    const size_t lds = decide_lds_bytes(c);
+    if (c.dtype == VRT_BF16)
+      hipLaunchKernelGGL(k_vnode<VRT_BF16>, grid, dim3(kVB), lds, stream, a);
+    else
+      hipLaunchKernelGGL(k_vnode<VRT_F32>, grid, dim3(kVB), lds, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (parts & 2)
+    hipLaunchKernelGGL(k_vwalk, dim3(c.B), dim3(kWave), (size_t)c.N * (16 + 4 + 4), stream, a);
   return hipGetLastError();
 }
 

@@ -242,31 +242,61 @@ vrt_status vrt_build_tree(const vrt_config* cp, int32_t layer, const void* draft
   return VRT_OK;
 }
 
-vrt_status vrt_verify_tree(const vrt_config* cp, const void* target_logits, int64_t ld,
-                           int64_t tree_stride, const void* tree, uint64_t seed, uint64_t step,
-                           void* ws, size_t ws_bytes, int32_t* out_tokens, int32_t* out_nodes,
-                           int32_t* out_len, uint32_t* stats, int32_t* node_out, void* stream) {
+namespace {
+
+// Validation and launch shared by the verification entry points (parts as in
+// launch_verify). Pointers a part does not use may be NULL.
+vrt_status verify_parts(int parts, const vrt_config* cp, const void* target_logits, int64_t ld,
+                        int64_t tree_stride, const void* tree, uint64_t seed, uint64_t step, void* ws,
+                        size_t ws_bytes, int32_t* out_tokens, int32_t* out_nodes, int32_t* out_len,
+                        uint32_t* stats, int32_t* node_out, void* stream) {
   vrt_status s = vrt_check_config(cp);
   if (s != VRT_OK) return s;
   const vrt_config& c = *cp;
   if (!tree || !ws) return fail(VRT_EINVAL, "tree and workspace pointers must not be NULL");
   if (!aligned16(tree) || !aligned16(ws)) return fail(VRT_EINVAL, "tree and workspace must be 16-byte aligned");
-  if (!out_tokens || !out_nodes || !out_len || !stats)
+  if ((parts & 2) && (!out_tokens || !out_nodes || !out_len || !stats))
     return fail(VRT_EINVAL, "output pointers must not be NULL");
   if (node_out && ((uintptr_t)node_out & 15u)) return fail(VRT_EINVAL, "node_out must be 16-byte aligned");
   const WsLayout wl = ws_layout(c);
   if (ws_bytes < (size_t)wl.total)
     return fail(VRT_ENOMEM, "workspace too small: %zu < %lld bytes", ws_bytes, (long long)wl.total);
-  s = check_rows(c, target_logits, ld, tree_stride, "target");
-  if (s != VRT_OK) return s;
+  if (parts & 1) {
+    s = check_rows(c, target_logits, ld, tree_stride, "target");
+    if (s != VRT_OK) return s;
+  }
   const vrt::Cfg k = vrt::make_cfg(c);
   const vrt::TreePtrs t = vrt::tree_ptrs(c, (void*)tree);
   vrt::NodeOut* no = node_out ? (vrt::NodeOut*)node_out : (vrt::NodeOut*)((char*)ws + wl.node_out);
-  const hipError_t e = vrt::launch_verify(k, t, target_logits, ld, tree_stride, seed,
+  const hipError_t e = vrt::launch_verify(parts, k, t, target_logits, ld, tree_stride, seed,
                                           (uint32_t)step, no, out_tokens, out_nodes, out_len, stats,
                                           (char*)ws + wl.verify, (hipStream_t)stream);
   if (e != hipSuccess) return fail(VRT_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
   return VRT_OK;
+}
+
+}  // namespace
+
+vrt_status vrt_verify_tree(const vrt_config* cp, const void* target_logits, int64_t ld,
+                           int64_t tree_stride, const void* tree, uint64_t seed, uint64_t step,
+                           void* ws, size_t ws_bytes, int32_t* out_tokens, int32_t* out_nodes,
+                           int32_t* out_len, uint32_t* stats, int32_t* node_out, void* stream) {
+  return verify_parts(3, cp, target_logits, ld, tree_stride, tree, seed, step, ws, ws_bytes, out_tokens,
+                      out_nodes, out_len, stats, node_out, stream);
+}
+
+vrt_status vrt_verify_nodes(const vrt_config* cp, const void* target_logits, int64_t ld,
+                            int64_t tree_stride, const void* tree, uint64_t seed, uint64_t step,
+                            void* ws, size_t ws_bytes, int32_t* node_out, void* stream) {
+  return verify_parts(1, cp, target_logits, ld, tree_stride, tree, seed, step, ws, ws_bytes, nullptr,
+                      nullptr, nullptr, nullptr, node_out, stream);
+}
+
+vrt_status vrt_verify_walk(const vrt_config* cp, const void* tree, void* ws, size_t ws_bytes,
+                           int32_t* out_tokens, int32_t* out_nodes, int32_t* out_len, uint32_t* stats,
+                           int32_t* node_out, void* stream) {
+  return verify_parts(2, cp, nullptr, 0, 0, tree, 0, 0, ws, ws_bytes, out_tokens, out_nodes, out_len,
+                      stats, node_out, stream);
 }
 
 vrt_status vrt_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {

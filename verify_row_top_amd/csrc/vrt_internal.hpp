@@ -63,7 +63,8 @@ TreePtrs tree_ptrs(const vrt_config& c, void* blob);
 // Device scratch of the verification: per-chunk row statistics and per-tree counters.
 size_t verify_ws_bytes(const Cfg& c);
 
-hipError_t launch_verify(const Cfg& c, const TreePtrs& t, const void* logits, int64_t ld,
+// parts: 1 = decide every node (k_vnode), 2 = walk (k_vwalk), 3 = both
+hipError_t launch_verify(int parts, const Cfg& c, const TreePtrs& t, const void* logits, int64_t ld,
                          int64_t tstride, uint64_t seed, uint32_t step, NodeOut* node_out,
                          int32_t* out_tokens, int32_t* out_nodes, int32_t* out_len, uint32_t* stats,
                          void* ws, hipStream_t stream);

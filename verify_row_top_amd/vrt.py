@@ -18,7 +18,8 @@ ROOT, DET, PROBE, FILL = 0, 1, 2, 3
 FINISH = -1
 ST_DRAFT_NONFINITE, ST_DRAFT_EMPTY, ST_TARGET_BAD = 0x1, 0x2, 0x4
 EXPORTS = ("vrt_check_config", "vrt_tree_layout_of", "vrt_tree_bytes", "vrt_workspace_bytes",
-           "vrt_build_tree", "vrt_verify_tree", "vrt_read_probe", "vrt_last_error")
+           "vrt_build_tree", "vrt_verify_tree", "vrt_verify_nodes", "vrt_verify_walk", "vrt_read_probe",
+           "vrt_last_error")
 
 
 class VrtError(RuntimeError):
@@ -68,6 +69,10 @@ def lib():
         L.vrt_verify_tree.argtypes = [P(Config), vp, i64, i64, vp, u64, u64, vp, sz, vp, vp, vp, vp,
                                       vp, vp]
         L.vrt_verify_tree.restype = i32
+        L.vrt_verify_nodes.argtypes = [P(Config), vp, i64, i64, vp, u64, u64, vp, sz, vp, vp]
+        L.vrt_verify_nodes.restype = i32
+        L.vrt_verify_walk.argtypes = [P(Config), vp, vp, sz, vp, vp, vp, vp, vp, vp]
+        L.vrt_verify_walk.restype = i32
         L.vrt_read_probe.argtypes = [vp, sz, vp, vp]
         L.vrt_read_probe.restype = i32
         L.vrt_last_error.argtypes = []
@@ -139,6 +144,20 @@ def verify_tree(cfg, target_logits, ld, tree_stride, tree, seed, step, ws, out_t
     """vrt_verify_tree."""
     _check(lib().vrt_verify_tree(ctypes.byref(cfg), _ptr(target_logits), ld, tree_stride, _ptr(tree),
                                  seed, step, _ptr(ws), ws.numel() * ws.element_size(),
+                                 _ptr(out_tokens), _ptr(out_nodes), _ptr(out_len), _ptr(stats),
+                                 _ptr(node_out), _stream(stream)))
+
+
+def verify_nodes(cfg, target_logits, ld, tree_stride, tree, seed, step, ws, node_out=None, stream=None):
+    """vrt_verify_nodes: every node's decision (the first part of vrt_verify_tree)."""
+    _check(lib().vrt_verify_nodes(ctypes.byref(cfg), _ptr(target_logits), ld, tree_stride, _ptr(tree),
+                                  seed, step, _ptr(ws), ws.numel() * ws.element_size(), _ptr(node_out),
+                                  _stream(stream)))
+
+
+def verify_walk(cfg, tree, ws, out_tokens, out_nodes, out_len, stats, node_out=None, stream=None):
+    """vrt_verify_walk: the walk over the decided nodes (the second part of vrt_verify_tree)."""
+    _check(lib().vrt_verify_walk(ctypes.byref(cfg), _ptr(tree), _ptr(ws), ws.numel() * ws.element_size(),
                                  _ptr(out_tokens), _ptr(out_nodes), _ptr(out_len), _ptr(stats),
                                  _ptr(node_out), _stream(stream)))
 
