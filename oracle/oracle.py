@@ -127,6 +127,10 @@ def _declare(L):
     L.orc_verify.restype = i32
     L.orc_table_trials.argtypes = [P(Cfg), i32, vp, vp, u64, i32, u32, i32, i32, vp, vp, vp]
     L.orc_table_trials.restype = i32
+    L.orc_tree_mask.argtypes = [i32, vp, vp, vp]
+    L.orc_tree_mask.restype = i32
+    L.orc_accepted_kv.argtypes = [i32, vp, vp]
+    L.orc_accepted_kv.restype = i32
 
 
 def _p(a):
@@ -297,3 +301,23 @@ def ctx_index(V, path):
     for t in path:
         pos = pos * V + int(t)
     return off + pos
+
+
+def tree_mask(parent):
+    """(mask bool [n, n], pos i32 [n]) of an emitted tree given its parent array, or None
+    if a parent is out of range (orc_tree_mask)."""
+    parent = np.ascontiguousarray(parent, np.int32)
+    n = parent.size
+    mask = np.zeros((n, n), np.uint8)
+    pos = np.zeros(n, np.int32)
+    if lib().orc_tree_mask(n, _p(parent), _p(mask), _p(pos)) != 0:
+        return None
+    return mask.astype(bool), pos
+
+
+def accepted_kv(out_len, out_nodes):
+    """KV entries kept after verification (orc_accepted_kv): root, then accepted nodes."""
+    nodes = np.ascontiguousarray(out_nodes, np.int32)
+    keep = np.zeros(max(int(out_len), 1), np.int32)
+    n = lib().orc_accepted_kv(int(out_len), _p(nodes), _p(keep))
+    return keep[:n]

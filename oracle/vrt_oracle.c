@@ -746,3 +746,27 @@ int32_t orc_table_trials(const orc_cfg* cfg, int32_t max_len, const float* draft
   *n_exempt = exempt;
   return bad ? -1 : 0;
 }
+
+int32_t orc_tree_mask(int32_t n, const int32_t* parent, uint8_t* mask, int32_t* pos) {
+  if (n < 1 || parent[0] != -1) return -1;
+  for (int32_t i = 1; i < n; ++i)
+    if (parent[i] < 0 || parent[i] >= i) return -1;
+  memset(mask, 0, (size_t)n * (size_t)n);
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t a = i, depth = 0;
+    while (a >= 0) {
+      mask[(size_t)i * (size_t)n + (size_t)a] = 1;
+      a = parent[a];
+      if (a >= 0) ++depth;
+    }
+    pos[i] = depth;
+  }
+  return 0;
+}
+
+int32_t orc_accepted_kv(int32_t len, const int32_t* nodes, int32_t* keep) {
+  if (len < 1) return 0;
+  keep[0] = 0;
+  for (int32_t k = 1; k < len; ++k) keep[k] = nodes[k - 1];
+  return len;
+}

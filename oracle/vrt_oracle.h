@@ -118,6 +118,18 @@ int32_t orc_table_trials(const orc_cfg* cfg, int32_t max_len, const float* draft
                          int32_t n_trials, int32_t two, int32_t* out, int32_t* n_first,
                          int32_t* n_exempt);
 
+/* The step after the prune (the target forward over the emitted tree, RheoSampling
+ * framework flowchart: one target pass verifies the whole tree): node i may attend to
+ * node j iff j lies on the path from the root to i, i included. Written out by
+ * following parents from i. mask: n*n bytes, row i, column j; pos[i]: the number of
+ * ancestors of i (its depth). Returns 0, or -1 if a parent is out of range (the root's
+ * parent is -1, every other node's lies in [0, i)). */
+int32_t orc_tree_mask(int32_t n, const int32_t* parent, uint8_t* mask, int32_t* pos);
+
+/* The KV entries kept after verification: the root's, then the accepted nodes' in path
+ * order: keep[0] = 0, keep[k] = nodes[k-1] for 1 <= k < len. Returns len. */
+int32_t orc_accepted_kv(int32_t len, const int32_t* nodes, int32_t* keep);
+
 #ifdef __cplusplus
 }
 #endif
