@@ -263,6 +263,28 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     n_nodes = sum(s[2] for s in [sets[k % len(sets)] for k in range(args.steps)]) / args.steps
 
+    # the step after the prune, timed on its own: attention mask + position ids of the
+    # target forward over the emitted trees, and the KV entries kept after verification
+    W32 = (N + 31) // 32
+    mask = torch.empty((B, N, W32), dtype=torch.int32, device=dev)
+    pos = torch.empty((B, N), dtype=torch.int32, device=dev)
+    keep = torch.empty((B, D + 1), dtype=torch.int32, device=dev)
+    keep_n = torch.empty(B, dtype=torch.int32, device=dev)
+    aux = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    for _ in range(3):
+        vrt.tree_mask(cfg, tree, mask, pos)
+        vrt.accepted_kv(cfg, out_nodes, out_len, keep, keep_n)
+    aux[0].record()
+    for _ in range(20):
+        vrt.tree_mask(cfg, tree, mask, pos)
+    aux[1].record()
+    for _ in range(20):
+        vrt.accepted_kv(cfg, out_nodes, out_len, keep, keep_n)
+    aux[2].record()
+    torch.cuda.synchronize()
+    mask_us = aux[0].elapsed_time(aux[1]) / 20 * 1e3
+    kv_us = aux[1].elapsed_time(aux[2]) / 20 * 1e3
+
     st = stats.cpu()
     lens = out_len.cpu().float()
     verify_bytes = int(round(float(n_nodes.sum()))) * V * esz
@@ -301,6 +323,8 @@ def main():
         "verified_tokens_per_s": float(lens.sum()) / (ms_per_step * 1e-3),
         "mean_tokens_per_tree": float(lens.mean()),
         "status_bits": int((st[:, 0] != 0).sum()),
+        "tree_mask_us": mask_us,
+        "accepted_kv_us": kv_us,
     }
     if cpu is not None:
         result["cpu_baseline"] = cpu

@@ -224,6 +224,28 @@ vrt_status vrt_verify_walk(const vrt_config* cfg, const void* tree, void* ws, si
                            int32_t* out_tokens, int32_t* out_nodes, int32_t* out_len, uint32_t* stats,
                            int32_t* node_out, void* stream);
 
+/* The step after the prune (RheoSampling framework flowchart: one target forward
+ * verifies the whole tree): attention inputs of that forward over the emitted tree.
+ * Node i of tree b attends to node j iff j lies on the path from the root to i, i
+ * included (parents precede children, so the mask is lower triangular).
+ *   tree  device tree blob whose emitted-tree arrays (n_nodes, node_parent) are filled;
+ *         a parent index out of range [0, i) ends that node's path
+ *   mask  device u32 [B][N][(N+31)/32]: bit j%32 of word j/32 of row i set iff j is on
+ *         i's path; rows and columns at or past n_nodes[b] are 0
+ *   pos   device i32 [B][N] or NULL: the number of ancestors of node i (its depth; add
+ *         the context length for absolute positions), -1 past n_nodes[b]
+ * Errors: VRT_EINVAL (config, NULL or misaligned pointers), VRT_EHIP. */
+vrt_status vrt_tree_mask(const vrt_config* cfg, const void* tree, uint32_t* mask, int32_t* pos,
+                         void* stream);
+
+/* The KV entries to keep once a tree is verified: keep[b][0] = 0 (the root), then
+ * keep[b][k] = out_nodes[b][k-1] for 1 <= k < out_len[b], -1 after (keep is device i32
+ * [B][D+1]); keep_n[b] = out_len[b] (device i32 [B]). out_nodes and out_len as
+ * vrt_verify_tree writes them (out_len clamped to 1 .. D+1).
+ * Errors: VRT_EINVAL (config, NULL or misaligned pointers), VRT_EHIP. */
+vrt_status vrt_accepted_kv(const vrt_config* cfg, const int32_t* out_nodes, const int32_t* out_len,
+                           int32_t* keep, int32_t* keep_n, void* stream);
+
 /* Description of the last error on this host thread ("" if none). */
 const char* vrt_last_error(void);
 

@@ -141,3 +141,18 @@ def test_split_verify_argument_errors_are_caught_before_any_launch():
     assert walk(tree=0) == vrt.EINVAL
     assert walk(wsb=8) == vrt.ENOMEM
     assert walk(ws=0x30008) == vrt.EINVAL  # not 16-byte aligned
+
+
+def test_mask_and_kv_argument_errors_are_caught_before_any_launch():
+    c = vrt.make_config(B=2, V=1000, K=4, D=3, R=10)
+    L = vrt.lib()
+    v = ctypes.c_void_p
+    assert L.vrt_tree_mask(ctypes.byref(c), v(0), v(0x40000), None, None) == vrt.EINVAL
+    assert L.vrt_tree_mask(ctypes.byref(c), v(0x20000), v(0), None, None) == vrt.EINVAL
+    assert L.vrt_tree_mask(ctypes.byref(c), v(0x20008), v(0x40000), None, None) == vrt.EINVAL
+    assert L.vrt_tree_mask(ctypes.byref(c), v(0x20000), v(0x40002), None, None) == vrt.EINVAL
+    assert L.vrt_accepted_kv(ctypes.byref(c), v(0x1000), v(0x2000), v(0), v(0x3000), None) == vrt.EINVAL
+    assert L.vrt_accepted_kv(ctypes.byref(c), v(0x1000), v(0x2001), v(0x4000), v(0x3000), None) == vrt.EINVAL
+    bad = vrt.make_config(B=2, V=1000, K=4, D=3, R=10)
+    bad.B = 0
+    assert L.vrt_tree_mask(ctypes.byref(bad), v(0x20000), v(0x40000), None, None) == vrt.EINVAL

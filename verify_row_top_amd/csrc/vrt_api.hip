@@ -299,6 +299,33 @@ vrt_status vrt_verify_walk(const vrt_config* cp, const void* tree, void* ws, siz
                       stats, node_out, stream);
 }
 
+vrt_status vrt_tree_mask(const vrt_config* cp, const void* tree, uint32_t* mask, int32_t* pos,
+                         void* stream) {
+  vrt_status s = vrt_check_config(cp);
+  if (s != VRT_OK) return s;
+  if (!tree || !mask) return fail(VRT_EINVAL, "tree and mask pointers must not be NULL");
+  if (!aligned16(tree) || ((uintptr_t)mask & 3u) || ((uintptr_t)pos & 3u))
+    return fail(VRT_EINVAL, "tree must be 16-byte and mask, pos 4-byte aligned");
+  const hipError_t e = vrt::launch_tree_mask(vrt::make_cfg(*cp), vrt::tree_ptrs(*cp, (void*)tree), mask,
+                                             pos, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(VRT_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return VRT_OK;
+}
+
+vrt_status vrt_accepted_kv(const vrt_config* cp, const int32_t* out_nodes, const int32_t* out_len,
+                           int32_t* keep, int32_t* keep_n, void* stream) {
+  vrt_status s = vrt_check_config(cp);
+  if (s != VRT_OK) return s;
+  if (!out_nodes || !out_len || !keep || !keep_n)
+    return fail(VRT_EINVAL, "pointers must not be NULL");
+  if (((uintptr_t)out_nodes | (uintptr_t)out_len | (uintptr_t)keep | (uintptr_t)keep_n) & 3u)
+    return fail(VRT_EINVAL, "pointers must be 4-byte aligned");
+  const hipError_t e = vrt::launch_accepted_kv(vrt::make_cfg(*cp), out_nodes, out_len, keep, keep_n,
+                                               (hipStream_t)stream);
+  if (e != hipSuccess) return fail(VRT_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return VRT_OK;
+}
+
 vrt_status vrt_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
   if (!buf || !sink) return fail(VRT_EINVAL, "buffer and sink must not be NULL");
   if (!aligned16(buf) || (bytes & 15u)) return fail(VRT_EINVAL, "buffer and size must be 16-byte aligned");

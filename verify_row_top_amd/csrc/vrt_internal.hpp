@@ -63,6 +63,11 @@ TreePtrs tree_ptrs(const vrt_config& c, void* blob);
 // Device scratch of the verification: per-chunk row statistics and per-tree counters.
 size_t verify_ws_bytes(const Cfg& c);
 
+hipError_t launch_tree_mask(const Cfg& c, const TreePtrs& t, uint32_t* mask, int32_t* pos,
+                            hipStream_t stream);
+hipError_t launch_accepted_kv(const Cfg& c, const int32_t* out_nodes, const int32_t* out_len,
+                              int32_t* keep, int32_t* keep_n, hipStream_t stream);
+
 // parts: 1 = decide every node (k_vnode), 2 = walk (k_vwalk), 3 = both
 hipError_t launch_verify(int parts, const Cfg& c, const TreePtrs& t, const void* logits, int64_t ld,
                          int64_t tstride, uint64_t seed, uint32_t step, NodeOut* node_out,

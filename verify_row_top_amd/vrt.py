@@ -18,8 +18,8 @@ ROOT, DET, PROBE, FILL = 0, 1, 2, 3
 FINISH = -1
 ST_DRAFT_NONFINITE, ST_DRAFT_EMPTY, ST_TARGET_BAD = 0x1, 0x2, 0x4
 EXPORTS = ("vrt_check_config", "vrt_tree_layout_of", "vrt_tree_bytes", "vrt_workspace_bytes",
-           "vrt_build_tree", "vrt_verify_tree", "vrt_verify_nodes", "vrt_verify_walk", "vrt_read_probe",
-           "vrt_last_error")
+           "vrt_build_tree", "vrt_verify_tree", "vrt_verify_nodes", "vrt_verify_walk", "vrt_tree_mask",
+           "vrt_accepted_kv", "vrt_read_probe", "vrt_last_error")
 
 
 class VrtError(RuntimeError):
@@ -73,6 +73,10 @@ def lib():
         L.vrt_verify_nodes.restype = i32
         L.vrt_verify_walk.argtypes = [P(Config), vp, vp, sz, vp, vp, vp, vp, vp, vp]
         L.vrt_verify_walk.restype = i32
+        L.vrt_tree_mask.argtypes = [P(Config), vp, vp, vp, vp]
+        L.vrt_tree_mask.restype = i32
+        L.vrt_accepted_kv.argtypes = [P(Config), vp, vp, vp, vp, vp]
+        L.vrt_accepted_kv.restype = i32
         L.vrt_read_probe.argtypes = [vp, sz, vp, vp]
         L.vrt_read_probe.restype = i32
         L.vrt_last_error.argtypes = []
@@ -160,6 +164,17 @@ def verify_walk(cfg, tree, ws, out_tokens, out_nodes, out_len, stats, node_out=N
     _check(lib().vrt_verify_walk(ctypes.byref(cfg), _ptr(tree), _ptr(ws), ws.numel() * ws.element_size(),
                                  _ptr(out_tokens), _ptr(out_nodes), _ptr(out_len), _ptr(stats),
                                  _ptr(node_out), _stream(stream)))
+
+
+def tree_mask(cfg, tree, mask, pos=None, stream=None):
+    """vrt_tree_mask: mask is a device i32/u32 tensor [B, N, (N+31)//32], pos [B, N] or None."""
+    _check(lib().vrt_tree_mask(ctypes.byref(cfg), _ptr(tree), _ptr(mask), _ptr(pos), _stream(stream)))
+
+
+def accepted_kv(cfg, out_nodes, out_len, keep, keep_n, stream=None):
+    """vrt_accepted_kv: keep [B, D+1], keep_n [B] (device i32 tensors)."""
+    _check(lib().vrt_accepted_kv(ctypes.byref(cfg), _ptr(out_nodes), _ptr(out_len), _ptr(keep),
+                                 _ptr(keep_n), _stream(stream)))
 
 
 def read_probe(buf, sink, stream=None):
