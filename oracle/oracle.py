@@ -25,7 +25,7 @@ class Cfg(ctypes.Structure):
         ("W", ctypes.c_int32), ("R", ctypes.c_int32), ("mode", ctypes.c_int32),
         ("budget", ctypes.c_int32), ("T", ctypes.c_float), ("eps_m0", ctypes.c_float),
         ("alpha", ctypes.c_double), ("lambda_", ctypes.c_double), ("gamma_", ctypes.c_double),
-        ("delta_", ctypes.c_double), ("rho_", ctypes.c_double),
+        ("delta_", ctypes.c_double), ("rho_", ctypes.c_double), ("order", ctypes.c_int32),
     ]
 
 
@@ -137,9 +137,13 @@ def _p(a):
     return a.ctypes.data_as(ctypes.c_void_p)
 
 
+PROBE_FIRST, PROBE_LAST = 0, 1
+
+
 def make_cfg(V, trunc=128, K=8, m=1, probe=1, D=8, W=0, R=60, mode=TOPR, budget=128, T=1.0,
-             eps_m0=1e-6, alpha=1.0, lam=0.0, gamma=0.0, delta=0.0, rho=1.0):
-    return Cfg(V, trunc, K, m, probe, D, W, R, mode, budget, T, eps_m0, alpha, lam, gamma, delta, rho)
+             eps_m0=1e-6, alpha=1.0, lam=0.0, gamma=0.0, delta=0.0, rho=1.0, order=PROBE_FIRST):
+    return Cfg(V, trunc, K, m, probe, D, W, R, mode, budget, T, eps_m0, alpha, lam, gamma, delta, rho,
+               order)
 
 
 def philox(ctr, key):

@@ -247,8 +247,11 @@ static void expand_node(orc_tree* t, int32_t layer, int32_t pos, int32_t node, c
   const float E = pairwise(ex, n);
   for (int32_t i = 0; i < n; ++i) e->q_raw[i] = ex[i] / E;
   const int32_t m = c->probe ? c->m : 0;
+  /* the probe's tail starts after the deterministic children: after the top m, or,
+   * probe last, after the fillers too */
+  const int32_t t0 = c->order == ORC_PROBE_LAST ? (c->K - 1 < n ? c->K - 1 : n) : m;
   float tail[ORC_MAXSUP];
-  for (int32_t i = 0; i < n; ++i) tail[i] = (i < m) ? 0.0f : e->q_raw[i];
+  for (int32_t i = 0; i < n; ++i) tail[i] = (i < t0) ? 0.0f : e->q_raw[i];
   e->z_raw = pairwise(tail, n);
 
   /* 2b. tempered probabilities on the same support (sampling, fp64) */
@@ -260,19 +263,19 @@ static void expand_node(orc_tree* t, int32_t layer, int32_t pos, int32_t node, c
   }
   for (int32_t i = 0; i < n; ++i) e->q_T[i] = et[i] / Z;
   double zT = 0.0;
-  for (int32_t i = m; i < n; ++i) zT += e->q_T[i];
+  for (int32_t i = t0; i < n; ++i) zT += e->q_T[i];
   e->z_T = zT;
 
   /* 3. probe: x_s ~ q_T restricted to ranks > m and renormalised by z_T,
    *    drawn by inverse CDF in rank order with one uniform. */
   int32_t js = -1;
-  if (c->probe && n > m && zT > 0.0) {
+  if (c->probe && n > t0 && zT > 0.0) {
     const double u = orc_uniform(t->seed, (uint32_t)(node + 1), (uint32_t)t->b, t->step,
                                  ORC_PURPOSE_PROBE);
     e->u = u;
     const double target = u * zT;
     double cum = 0.0, before = 0.0;
-    for (int32_t j = m; j < n; ++j) {
+    for (int32_t j = t0; j < n; ++j) {
       before = cum;
       cum += e->q_T[j];
       if (target < cum) {
@@ -281,7 +284,7 @@ static void expand_node(orc_tree* t, int32_t layer, int32_t pos, int32_t node, c
       }
     }
     if (js < 0) { /* rounding exhausted the sum: the last rank with mass */
-      for (int32_t j = n - 1; j >= m; --j)
+      for (int32_t j = n - 1; j >= t0; --j)
         if (e->q_T[j] > 0.0) {
           js = j;
           break;
@@ -299,9 +302,10 @@ static void expand_node(orc_tree* t, int32_t layer, int32_t pos, int32_t node, c
       t->n_exempt++;
     }
     e->probe_rank = js;
-    /* proxy probability: min{q(x_m), z}; q(x_1) + eps when m = 0 */
-    if (m >= 1) {
-      e->proxy = e->q_raw[m - 1] < e->z_raw ? e->q_raw[m - 1] : e->z_raw;
+    /* proxy probability: min{q(x_m), z}; q(x_1) + eps when m = 0 (probe last: x_m is
+     * the last deterministic child and z the mass after it) */
+    if (t0 >= 1) {
+      e->proxy = e->q_raw[t0 - 1] < e->z_raw ? e->q_raw[t0 - 1] : e->z_raw;
     } else {
       const float a = e->q_raw[0] + c->eps_m0;
       e->proxy = a < 1.0f ? a : 1.0f;
@@ -316,10 +320,17 @@ static void expand_node(orc_tree* t, int32_t layer, int32_t pos, int32_t node, c
   } else {
     for (int32_t i = 0; i < m && i < n && slot < c->K; ++i)
       add_child(t, layer, pos, slot++, node, r, e->sup_id[i], ORC_DET, e->q_raw[i]);
-    if (js >= 0 && slot < c->K)
-      add_child(t, layer, pos, slot++, node, r, e->sup_id[js], ORC_PROBE, e->proxy);
-    for (int32_t i = m; i < n && slot < c->K; ++i)
-      if (i != js) add_child(t, layer, pos, slot++, node, r, e->sup_id[i], ORC_FILL, e->q_raw[i]);
+    if (c->order == ORC_PROBE_LAST) {
+      for (int32_t i = m; i < t0 && slot < c->K; ++i)
+        add_child(t, layer, pos, slot++, node, r, e->sup_id[i], ORC_FILL, e->q_raw[i]);
+      if (js >= 0 && slot < c->K)
+        add_child(t, layer, pos, slot++, node, r, e->sup_id[js], ORC_PROBE, e->proxy);
+    } else {
+      if (js >= 0 && slot < c->K)
+        add_child(t, layer, pos, slot++, node, r, e->sup_id[js], ORC_PROBE, e->proxy);
+      for (int32_t i = m; i < n && slot < c->K; ++i)
+        if (i != js) add_child(t, layer, pos, slot++, node, r, e->sup_id[i], ORC_FILL, e->q_raw[i]);
+    }
   }
   e->n_child = slot;
 }
@@ -473,9 +484,10 @@ int32_t orc_tree_view(const orc_tree* t, int32_t cap, int32_t tail_cap, int32_t*
     if (kind[j] != ORC_PROBE) continue;
     const int32_t i = parent[j];
     const orc_exp* e = &t->rows[t->cand[t->node_cand[j]].row];
-    const int32_t m = t->cfg.m;
+    const int32_t K1 = t->cfg.K - 1 < e->n_sup ? t->cfg.K - 1 : e->n_sup;
+    const int32_t t0 = t->cfg.order == ORC_PROBE_LAST ? K1 : t->cfg.m;
     int32_t k = 0;
-    for (int32_t r = m; r < e->n_sup; ++r) {
+    for (int32_t r = t0; r < e->n_sup; ++r) {
       if (k >= tail_cap) {
         free(node_of);
         return -2;
@@ -498,7 +510,11 @@ int32_t orc_tree_view(const orc_tree* t, int32_t cap, int32_t tail_cap, int32_t*
  * W = 1 - sum_tail min(p, q~). The remaining kept children are then tested in
  * slot order: accept x iff u < w(x)/W, else W -= w(x), w(x) = 0. With no kept
  * probe, w = p and W = 1. If nothing is accepted (or the node has no kept
- * children) a token is drawn from w/W by inverse CDF in token-id order. */
+ * children) a token is drawn from w/W by inverse CDF in token-id order.
+ * Probe last (the RRSw baseline of key design 3): the other kept children are tested
+ * first, in slot order, against w = p and W = 1 (each rejection removes its point mass);
+ * then the probe with min(1, w/(W q~)), and a rejection leaves max(0, w - W q~) on the
+ * tail (which holds none of those children). */
 static void decide_node(const orc_cfg* c, int32_t i, const int32_t* token, const int32_t* depth,
                         const int32_t* kind, const int32_t* child_off, const int32_t* child,
                         const int32_t* tail_n, const int32_t* tail_id, const double* tail_q,
@@ -526,13 +542,16 @@ static void decide_node(const orc_cfg* c, int32_t i, const int32_t* token, const
   for (int32_t k = child_off[i]; k < child_off[i + 1]; ++k)
     if (kind[child[k]] == ORC_PROBE) probe = child[k];
 
-  if (probe >= 0) {
-    const int32_t xs = token[probe];
-    double qs = 0.0;
+  /* draws: 32*depth + j, j = 0 for the probe, 1.. for the other children in slot order */
+  const double u0 = orc_uniform(seed, 32u * d, (uint32_t)b, step, ORC_PURPOSE_TEST);
+  double qs = 0.0;
+  if (probe >= 0)
     for (int32_t k = 0; k < tail_n[i]; ++k)
-      if (tail_id[(int64_t)i * tail_cap + k] == xs) qs = tail_q[(int64_t)i * tail_cap + k];
-    const double a = w[xs] / qs;
-    const double u0 = orc_uniform(seed, 32u * d, (uint32_t)b, step, ORC_PURPOSE_TEST);
+      if (tail_id[(int64_t)i * tail_cap + k] == token[probe]) qs = tail_q[(int64_t)i * tail_cap + k];
+
+  if (c->order != ORC_PROBE_LAST && probe >= 0) {
+    /* probe first: accept with min(1, p/q~); else the residual max(0, p - q~) on the tail */
+    const double a = w[token[probe]] / qs;
     o->n_tests++;
     if (fabs(u0 - a) < ORC_EXEMPT_BAND) o->exempt++;
     if (u0 < a) {
@@ -551,6 +570,8 @@ static void decide_node(const orc_cfg* c, int32_t i, const int32_t* token, const
     W = 1.0 - overlap;
   }
 
+  /* the other kept children, in slot order, against the residual w / W; a rejected child
+   * leaves the residual */
   uint32_t j = 1;
   for (int32_t k = child_off[i]; k < child_off[i + 1]; ++k) {
     const int32_t ch = child[k];
@@ -569,6 +590,29 @@ static void decide_node(const orc_cfg* c, int32_t i, const int32_t* token, const
     }
     W -= wx;
     w[xt] = 0.0;
+  }
+
+  if (c->order == ORC_PROBE_LAST && probe >= 0) {
+    /* probe last (RRSw): the residual w / W (every other kept child rejected) against the
+     * probe's tail distribution q~: accept with min(1, w/(W q~)); else w - W q~ clipped at
+     * 0 on the tail */
+    const double a = w[token[probe]] / (W * qs);
+    o->n_tests++;
+    if (fabs(u0 - a) < ORC_EXEMPT_BAND) o->exempt++;
+    if (u0 < a) {
+      o->accept = probe;
+      o->W = 0.0;
+      return;
+    }
+    double overlap = 0.0;
+    for (int32_t k = 0; k < tail_n[i]; ++k) {
+      const int32_t y = tail_id[(int64_t)i * tail_cap + k];
+      const double q = W * tail_q[(int64_t)i * tail_cap + k];
+      const double p = w[y];
+      overlap += (p < q) ? p : q;
+      w[y] = (p > q) ? p - q : 0.0;
+    }
+    W -= overlap;
   }
 
   /* final residual (or bonus) sample by inverse CDF in token-id order */

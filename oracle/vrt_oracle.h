@@ -42,10 +42,18 @@ enum { ORC_PURPOSE_PROBE = 1, ORC_PURPOSE_TEST = 2, ORC_PURPOSE_FINAL = 3 };
 #define ORC_MAXSUP 1024
 #define ORC_EXEMPT_BAND 1e-6
 
+/* order: ORC_PROBE_FIRST, RheoSampling's layout and verification (top-m, the probe,
+ * then fillers; the probe is tested first); or ORC_PROBE_LAST, the RRSw baseline the
+ * pages compare against (key design 3 and the verification ablation): top-m, then the
+ * fillers, then the probe, drawn from the ranks after the fillers so that the kept
+ * deterministic children never lie in its tail, and tested after them. */
+enum { ORC_PROBE_FIRST = 0, ORC_PROBE_LAST = 1 };
+
 typedef struct {
   int32_t V, trunc, K, m, probe, D, W, R, mode, budget;
   float T, eps_m0;
   double alpha, lambda_, gamma_, delta_, rho_;
+  int32_t order;
 } orc_cfg;
 
 /* One candidate: a child created by one expansion. */

@@ -48,6 +48,25 @@ def acceptance_ok(trials=200_000):
     return abs(z) < 4.0
 
 
+def rrsw_lossless_ok(trials=200_000):
+    cfg = orc.make_cfg(V=V, trunc=16, K=4, m=1, D=2, W=3, R=6, T=1.0, order=orc.PROBE_LAST)
+    dt, tt = _tables(2, 6)
+    out, nf, _ = orc.table_trials(cfg, 2, dt, tt, 4545, 0, 0, trials)
+    p = _softmax(tt[0], 1.0)
+    obs = np.bincount(out[:, 0], minlength=V).astype(np.float64)
+    return chisquare(obs, p * obs.sum()).pvalue > 0.01
+
+
+def rrsw_acceptance_ok(trials=200_000):
+    from tests.test_oracle_rrsw import _depth1_rrsw
+    cfg = orc.make_cfg(V=V, trunc=16, K=4, m=1, D=1, R=4, T=1.0, order=orc.PROBE_LAST)
+    dt, tt = _tables(1, 79)
+    out, nf, _ = orc.table_trials(cfg, 1, dt, tt, 4646, 0, 0, trials)
+    P = _depth1_rrsw(cfg, dt[0], tt[0])
+    z = ((nf >= 1).mean() - P) / np.sqrt(P * (1 - P) / trials)
+    return abs(z) < 4.0
+
+
 def slots_ok():
     from tests.test_oracle_units import test_expansion_probabilities_and_slots
     try:
@@ -80,18 +99,29 @@ def smart_ok():
 MUTANTS = [
     ("residual_mass_ignores_overlap", "    W = 1.0 - overlap;", "    W = 1.0;",
      lambda: lossless_ok() and acceptance_ok()),
-    ("probe_ratio_inverted", "const double a = w[xs] / qs;", "const double a = qs / w[xs];",
-     lambda: lossless_ok() and acceptance_ok()),
-    ("tail_residual_not_clipped", "w[y] = (p > q) ? p - q : 0.0;", "w[y] = p;",
+    ("probe_ratio_inverted", "const double a = w[token[probe]] / qs;",
+     "const double a = qs / w[token[probe]];", lambda: lossless_ok() and acceptance_ok()),
+    ("tail_residual_not_clipped",
+     "      overlap += (p < q) ? p : q;\n      w[y] = (p > q) ? p - q : 0.0;\n    }\n    W = 1.0 - overlap;",
+     "      overlap += (p < q) ? p : q;\n      w[y] = p;\n    }\n    W = 1.0 - overlap;",
      lambda: lossless_ok() and acceptance_ok()),
     ("rejected_sibling_not_removed", "    W -= wx;\n    w[xt] = 0.0;", "    W -= wx;",
      lambda: lossless_ok() and acceptance_ok()),
     ("verify_ignores_temperature", "w[v] = exp(((double)x[v] - (double)M) * invT);",
      "w[v] = exp((double)x[v] - (double)M);", lambda: lossless_ok(T=0.6)),
-    ("tail_mass_includes_top_m", "for (int32_t i = m; i < n; ++i) zT += e->q_T[i];",
+    ("tail_mass_includes_top_m", "for (int32_t i = t0; i < n; ++i) zT += e->q_T[i];",
      "for (int32_t i = 0; i < n; ++i) zT += e->q_T[i];", lambda: slots_ok() and lossless_ok()),
-    ("proxy_takes_max", "e->proxy = e->q_raw[m - 1] < e->z_raw ? e->q_raw[m - 1] : e->z_raw;",
-     "e->proxy = e->q_raw[m - 1] > e->z_raw ? e->q_raw[m - 1] : e->z_raw;", slots_ok),
+    ("proxy_takes_max", "e->proxy = e->q_raw[t0 - 1] < e->z_raw ? e->q_raw[t0 - 1] : e->z_raw;",
+     "e->proxy = e->q_raw[t0 - 1] > e->z_raw ? e->q_raw[t0 - 1] : e->z_raw;", slots_ok),
+    # probe last (the RRSw baseline)
+    ("probe_last_ratio_ignores_residual_mass", "const double a = w[token[probe]] / (W * qs);",
+     "const double a = w[token[probe]] / qs;", lambda: rrsw_lossless_ok() and rrsw_acceptance_ok()),
+    ("probe_last_tail_not_scaled", "const double q = W * tail_q[(int64_t)i * tail_cap + k];",
+     "const double q = tail_q[(int64_t)i * tail_cap + k];",
+     lambda: rrsw_lossless_ok() and rrsw_acceptance_ok()),
+    ("probe_last_tail_includes_fillers",
+     "const int32_t t0 = c->order == ORC_PROBE_LAST ? (c->K - 1 < n ? c->K - 1 : n) : m;",
+     "const int32_t t0 = m;", lambda: rrsw_lossless_ok() and rrsw_acceptance_ok()),
     ("fillers_repeat_probe", "if (i != js) add_child", "if (i >= 0) add_child", slots_ok),
     ("support_tie_break_reversed", "return (x->id < y->id) ? -1 : (x->id > y->id);",
      "return (x->id > y->id) ? -1 : (x->id < y->id);", support_ok),
