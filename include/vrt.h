@@ -79,10 +79,23 @@ enum { VRT_ROOT = 0, VRT_DET = 1, VRT_PROBE = 2, VRT_FILL = 3 };
  *   alpha, lambda_, gamma_, delta_, rho_
  *            SMART discount and cost models C(n) = lambda n + gamma (exp(delta n^rho) - 1),
  *            C'(n) = lambda + gamma delta rho n^(rho-1) exp(delta n^rho) (SMART key design 2) */
+/* Order of the probe among a node's children (the probe on; ignored with probe = 0):
+ *   VRT_PROBE_FIRST  RheoSampling (key designs 2-3): slots top-m, the probe, then the
+ *                    fillers; the probe is tested first with min(1, p/q~), the others
+ *                    under the residual norm(max(0, p - q~))
+ *   VRT_PROBE_LAST   the RRSw baseline of key design 3: slots top-m, the fillers (the next
+ *                    K-1-m ranks), then the probe drawn from the ranks after them (tail
+ *                    q~ = tempered mass there, renormalised; proxy min{q of the last
+ *                    deterministic child, the raw mass after it}); the deterministic
+ *                    children are tested first as point masses, then the probe with
+ *                    min(1, p_D/q~), p_D the target with the rejected children removed */
+typedef enum { VRT_PROBE_FIRST = 0, VRT_PROBE_LAST = 1 } vrt_order;
+
 typedef struct {
   int32_t B, V, dtype, trunc, K, m, probe, D, W, R, mode, budget;
   float T, eps_m0;
   double alpha, lambda_, gamma_, delta_, rho_;
+  int32_t order;  /* vrt_order: where the probe sits and when it is tested */
 } vrt_config;
 
 /* Byte offsets of the arrays inside the caller-owned tree blob. Every array is

@@ -16,7 +16,7 @@ from oracle import oracle as orc
 def oracle_cfg(w, **kw):
     c = dict(V=w.V, trunc=w.trunc, K=w.K, m=w.m, probe=w.probe, D=w.D, W=w.W, R=w.R, mode=w.mode,
              budget=w.budget, T=w.T, eps_m0=w.eps_m0, alpha=w.alpha, lam=w.lam, gamma=w.gamma,
-             delta=w.delta, rho=w.rho)
+             delta=w.delta, rho=w.rho, order=w.order)
     c.update(kw)
     return orc.make_cfg(**c)
 

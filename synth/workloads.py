@@ -44,6 +44,7 @@ class Workload:
     draft_scale: float = 1.0
     sigma: float = 0.7
     gen_seed: int = 0x5EED
+    order: int = 0  # 0: the probe first (RheoSampling), 1: the probe last (RRSw baseline)
 
     def params(self):
         return Params(self.V, self.dtype, len(self.zipf), self.split if self.split else self.B,

@@ -10,7 +10,7 @@ from verify_row_top_amd import vrt
 def lib_config(w, **kw):
     c = dict(B=w.B, V=w.V, dtype=w.dtype, trunc=w.trunc, K=w.K, m=w.m, probe=w.probe, D=w.D, W=w.W,
              R=w.R, mode=w.mode, budget=w.budget, T=w.T, eps_m0=w.eps_m0, alpha=w.alpha, lam=w.lam,
-             gamma=w.gamma, delta=w.delta, rho=w.rho)
+             gamma=w.gamma, delta=w.delta, rho=w.rho, order=w.order)
     c.update(kw)
     return vrt.make_config(**c)
 

@@ -54,6 +54,11 @@ CASES = [
     ("small_all_ties", _small(zipf=(), draft_scale=0.0, V=9000, R=20, D=3)),
     ("small_all_ties_fp32_trunc256", _small(zipf=(), draft_scale=0.0, V=9000, R=20, D=3,
                                            dtype=synth.F32, trunc=256)),
+    ("small_probe_last", _small(order=1)),
+    ("small_probe_last_m3_K8", _small(order=1, m=3, K=8, R=50)),
+    ("small_probe_last_m0_T06", _small(order=1, m=0, T=0.6, trunc=256, V=3000)),
+    ("small_probe_last_trunc4", _small(order=1, V=300, trunc=4, K=3, R=12, D=4)),
+    ("small_probe_last_fp32_K1", _small(order=1, dtype=synth.F32, K=1, m=0, R=6, D=5)),
     ("smart_small", _smart_small()),
     ("smart_small_m0_alpha08", _smart_small(m=0, alpha=0.8, budget=24)),
 ]

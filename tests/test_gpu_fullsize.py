@@ -27,6 +27,7 @@ CASES = [
     ("stress_B256_m1", workloads.get("stress"), [0, 127, 128, 255], (1, 0)),
     ("stress_B256_m0", workloads.get("stress", m=0), [5, 200], (4, 2)),
     ("stress_B256_m3", workloads.get("stress", m=3), [77, 170], (5, 9)),
+    ("headline_probe_last", workloads.get("headline", order=1), [0, 17, 31], (6, 1)),
 ]
 
 

@@ -949,6 +949,9 @@ __device__ __forceinline__ void expand_row(const BArgs& a, int b, int node, floa
   const int lane = lane_id();
   const float M = sup_key_val(s_buf[0]);
   const int m = c.probe ? c.m : 0;
+  // the probe's tail starts after the deterministic children: the top m, or, probe last,
+  // the fillers too
+  const int t0 = c.order == VRT_PROBE_LAST ? min(c.K - 1, n_sup) : m;
   float e[BS];
   double et[BS];
 #pragma unroll
@@ -975,7 +978,7 @@ __device__ __forceinline__ void expand_row(const BArgs& a, int b, int node, floa
   for (int k = 0; k < BS; ++k) {
     const int r = lane * BS + k;
     const float q = e[k] / E;
-    qt[k] = r < m ? 0.0f : q;
+    qt[k] = r < t0 ? 0.0f : q;
     s_q[r] = q;
   }
   const float zr = pairwise(qt);
@@ -987,14 +990,14 @@ __device__ __forceinline__ void expand_row(const BArgs& a, int b, int node, floa
 #pragma unroll
   for (int k = 0; k < BS; ++k) {
     et[k] = et[k] / Z;  // q_T
-    if (lane * BS + k >= m) tl += et[k];
+    if (lane * BS + k >= t0) tl += et[k];
   }
   const double zT = wave_sum(tl);
   wave_sync();
 
   int js = -1;
   float proxy = 0.0f;
-  if (c.probe && n_sup > m && zT > 0.0) {
+  if (c.probe && n_sup > t0 && zT > 0.0) {
     const double u =
         (double)uniform24(a.seed, (uint32_t)(node + 1), (uint32_t)b, a.step, kPurposeProbe);
     const double tgt = u * zT;
@@ -1009,7 +1012,7 @@ __device__ __forceinline__ void expand_row(const BArgs& a, int b, int node, floa
 #pragma unroll
         for (int k = 0; k < BS; ++k) {
           const int r = lane * BS + k;
-          if (r >= m && pick < 0) {
+          if (r >= t0 && pick < 0) {
             cum += et[k];
             if (tgt < cum) pick = r;
           }
@@ -1022,14 +1025,14 @@ __device__ __forceinline__ void expand_row(const BArgs& a, int b, int node, floa
 #pragma unroll
       for (int k = 0; k < BS; ++k) {
         const int r = lane * BS + k;
-        if (r >= m && r < n_sup && et[k] > 0.0) last = r;
+        if (r >= t0 && r < n_sup && et[k] > 0.0) last = r;
       }
       for (int o = 1; o < kWave; o <<= 1) last = max(last, __shfl_xor(last, o, kWave));
       pick = last;
     }
     js = pick;
-    if (m >= 1) {
-      const float qm = s_q[m - 1];
+    if (t0 >= 1) {  // the last deterministic child's q, capped by the raw mass after it
+      const float qm = s_q[t0 - 1];
       proxy = qm < zr ? qm : zr;
     } else {
       const float t1 = s_q[0] + c.eps_m0;
@@ -1037,15 +1040,15 @@ __device__ __forceinline__ void expand_row(const BArgs& a, int b, int node, floa
     }
   }
 
-  // tail table of this row: ranks m.. with q~ = q_T / z_T
-  const int ntail = (js >= 0) ? n_sup - m : 0;
+  // tail table of this row: ranks t0.. with q~ = q_T / z_T
+  const int ntail = (js >= 0) ? n_sup - t0 : 0;
   if (lane == 0) a.t.row_tail_n[ktb] = ntail;
 #pragma unroll
   for (int k = 0; k < BS; ++k) {
     const int r = lane * BS + k;
-    if (r >= m && r < m + ntail) {
-      a.t.row_tail_id[ktb * c.TC + (r - m)] = (int)sup_key_id(s_buf[r]);
-      a.t.row_tail_q[ktb * c.TC + (r - m)] = (float)(et[k] / zT);
+    if (r >= t0 && r < t0 + ntail) {
+      a.t.row_tail_id[ktb * c.TC + (r - t0)] = (int)sup_key_id(s_buf[r]);
+      a.t.row_tail_q[ktb * c.TC + (r - t0)] = (float)(et[k] / zT);
     }
   }
 
@@ -1058,6 +1061,9 @@ __device__ __forceinline__ void expand_row(const BArgs& a, int b, int node, floa
       if (s < n_sup) r_of_slot = s, kind = VRT_DET;
     } else if (s < m_det) {
       r_of_slot = s, kind = VRT_DET;
+    } else if (c.order == VRT_PROBE_LAST) {  // the fillers (ranks up to t0), then the probe
+      if (s < t0) r_of_slot = s, kind = VRT_FILL;
+      else if (js >= 0 && s == t0) r_of_slot = js, kind = VRT_PROBE;
     } else if (js >= 0 && s == m_det) {
       r_of_slot = js, kind = VRT_PROBE;
     } else {

@@ -330,37 +330,49 @@ __device__ void decide_node(const VArgs& a, int b, int i, const char* row, const
   auto p_of_x = [&](float x) -> double { return (double)fast_exp2(__builtin_fmaf(x, c2, -MC)) * invS; };
   const double pc = ch_tok >= 0 ? p_of_x(ch_x) : 0.0;
 
-  // ---- probe tail: p, the overlap sum min(p, q~), which kept child each token is
+  // ---- probe tail: p, the overlap sum min(p, s q~), which kept child each token is.
+  // Probe first: s = 1 and the probe is tested before the others. Probe last (the RRSw
+  // order): the others are tested first as point masses, and the probe meets the
+  // residual mass W_D = 1 - p(those children), so its tail is weighed with s = W_D.
+  const bool last = c.order == VRT_PROBE_LAST;
   int tests = 0, near = 0;
   int accept = -1;
   double W = 1.0;  // mass of the residual the tests run against
   double q_child = lane < nc ? L.qc[lane] : -1.0;  // q~ of this lane's child, -1: not in the tail
+  const bool cand = lane < nc && lane != probe && ch_node >= 0;
+  const uint64_t cmask = ballot(cand);
+  double WD = 1.0;  // residual mass once every other kept child is rejected (probe last)
+  if (last)
+    for (uint64_t m = cmask; m; m &= m - 1ull) WD -= readlane_d(pc, __builtin_ctzll(m));
+  const double qscale = last ? WD : 1.0;
+  double overlap = 0.0;
   if (probe >= 0) {
     double ov = 0.0;
     for (int e = lane; e < nt; e += kWave) {
       const int y = L.tid[e];
       const double p = y >= 0 ? p_of_x((float)L.tp[e]) : 0.0;
-      const double q = (double)L.tq[e];
+      const double q = qscale * (double)L.tq[e];
       L.tp[e] = p;
       ov += fmin(p, q);
     }
-    const double overlap = wave_sum(ov);
+    overlap = wave_sum(ov);
     wave_sync();
-    W = 1.0 - overlap;
+    if (!last) W = 1.0 - overlap;
   }
-  // residual weight of this lane's child once the probe is rejected; the other kept
-  // children are tested in slot order, each lane's uniform drawn up front
+  // weight of this lane's child when it is tested: probe first, its residual once the
+  // probe is rejected; probe last, its p. The children are tested in slot order, each
+  // lane's uniform drawn up front.
   const bool in_tail = q_child >= 0.0;
-  const double wc = in_tail ? (pc > q_child ? pc - q_child : 0.0) : pc;
-  const bool cand = lane < nc && lane != probe && ch_node >= 0;
-  const uint64_t cmask = ballot(cand);
+  const double wc = (in_tail && !last) ? (pc > q_child ? pc - q_child : 0.0) : pc;
   const float uc = r_u;
 
   // ---- the final residual (or bonus) sample is taken only if every test rejects, and
   // then it runs against the residual with all of them rejected: located now, its
   // chunk's re-read overlaps the tests. Inverse CDF of w / W in token-id order.
   double Wf = W;
-  for (uint64_t m = cmask; m; m &= m - 1ull) Wf -= readlane_d(wc, __builtin_ctzll(m));
+  if (last) Wf = WD - overlap;
+  else
+    for (uint64_t m = cmask; m; m &= m - 1ull) Wf -= readlane_d(wc, __builtin_ctzll(m));
   const float uf = R.uf;
   const double tgt = (double)uf * Wf;
   for (int ch = lane; ch < nch; ch += kWave) L.dfix[ch] = 0;
@@ -372,7 +384,7 @@ __device__ void decide_node(const VArgs& a, int b, int i, const char* row, const
     for (int e = lane; e < nt; e += kWave) {
       const int y = L.tid[e];
       if (y < 0) continue;
-      const double p = L.tp[e], q = (double)L.tq[e];
+      const double p = L.tp[e], q = qscale * (double)L.tq[e];
       const int slot = L.tslot[e];
       const bool rej = slot >= 0 && ((cmask >> slot) & 1ull);
       const double d = rej ? -p : -(p < q ? p : q);
@@ -444,7 +456,7 @@ __device__ void decide_node(const VArgs& a, int b, int i, const char* row, const
         y = L.tid[e];
         inside = y >= lo && y < lo + kCH;
         if (inside) {
-          const double p = L.tp[e], q = (double)L.tq[e];
+          const double p = L.tp[e], q = qscale * (double)L.tq[e];
           const int slot = L.tslot[e];
           const bool rej = slot >= 0 && ((cmask >> slot) & 1ull);
           d = rej ? -p : -(p < q ? p : q);
@@ -470,17 +482,19 @@ __device__ void decide_node(const VArgs& a, int b, int i, const char* row, const
     nitem += (int)__builtin_popcountll(m);
   }
 
-  // ---- the tests: probe first with min(1, p/q~), then the others under the residual
-  if (probe >= 0) {
+  // ---- the tests: the probe with min(1, p/(s q~)) (first, or after the others), the
+  // others under the residual
+  auto probe_test = [&](double sc) {
     const double qp = readlane_d(q_child, probe);
     const double qs = qp < 0.0 ? 0.0 : qp;  // a probe outside its tail has q~ = 0
     const double ps = readlane_d(pc, probe);
-    const double ratio = ps / qs;
+    const double ratio = ps / (sc * qs);
     const float u0 = R.u0;
     ++tests;
     if (fabs((double)u0 - ratio) < kBand) ++near;
     if ((double)u0 < ratio) accept = __builtin_amdgcn_readlane(ch_node, probe);
-  }
+  };
+  if (probe >= 0 && !last) probe_test(1.0);
   if (accept < 0) {
     for (uint64_t m = cmask; m; m &= m - 1ull) {
       const int k = __builtin_ctzll(m);
@@ -495,6 +509,10 @@ __device__ void decide_node(const VArgs& a, int b, int i, const char* row, const
       }
       W -= wk;
     }
+  }
+  if (probe >= 0 && last && accept < 0) {
+    probe_test(W);     // W == WD here: every other kept child was rejected
+    W = WD - overlap;  // the mass the final sample runs against
   }
 
   // ---- nothing accepted: finish the final sample in the re-read chunk (W == Wf now)

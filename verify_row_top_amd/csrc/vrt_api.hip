@@ -116,6 +116,7 @@ Cfg make_cfg(const vrt_config& c) {
   k.c2 = k.invT * 1.44269504088896341f;
   k.eps_m0 = c.eps_m0;
   k.alpha = c.alpha; k.lam = c.lambda_; k.gam = c.gamma_; k.del = c.delta_; k.rho = c.rho_;
+  k.order = c.probe ? c.order : VRT_PROBE_FIRST;
   return k;
 }
 
@@ -169,6 +170,8 @@ vrt_status vrt_check_config(const vrt_config* cp) {
   if (c.m < 0 || (c.probe && c.m > c.K - 1))
     return fail(VRT_EINVAL, "m must be in [0, K-1] with the probe on (m=%d, K=%d)", c.m, c.K);
   if (c.D < 1 || c.D > 32) return fail(VRT_EINVAL, "D must be in [1, 32] (got %d)", c.D);
+  if (c.order != VRT_PROBE_FIRST && c.order != VRT_PROBE_LAST)
+    return fail(VRT_EINVAL, "order must be VRT_PROBE_FIRST or VRT_PROBE_LAST (got %d)", c.order);
   if (c.mode != VRT_MODE_TOPR && c.mode != VRT_MODE_SMART) return fail(VRT_EINVAL, "unknown mode %d", c.mode);
   if (c.mode == VRT_MODE_TOPR) {
     if (c.W < 0 || c.W > 1024) return fail(VRT_EINVAL, "W must be in [0, 1024] (got %d)", c.W);

@@ -20,6 +20,7 @@ struct Cfg {
   float c2;    // fl32(invT * log2(e)): exp((x - M)/T) = exp2(x*c2 - M*c2)
   float eps_m0;
   double alpha, lam, gam, del, rho;
+  int order;  // VRT_PROBE_FIRST / VRT_PROBE_LAST (probe on only)
 };
 
 // Typed views of the caller's tree blob (see vrt_tree_layout in vrt.h).
