@@ -35,6 +35,9 @@ def parse():
                     help="time only the verification call (for profiling it alone)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-MiB buffer 3 times (calibrates hardware byte counters)")
+    ap.add_argument("--ablation", type=int, default=0, metavar="SETS",
+                    help="only the depth-1 verification comparison (point-mass top-K, probe last "
+                         "= RRSw, probe first = RheoVerification) over SETS input sets")
     return ap.parse_args()
 
 
@@ -128,10 +131,72 @@ def read_ceiling(torch, dev, vrt, mib=1024, reps=10):
     return (mib << 20) / (ms * 1e-3) / 1e9
 
 
+def ablation(args):
+    """Depth-1 controlled comparison of the verification orders on the workload's rows: the
+    share of trees whose first emitted token comes from the tree, for the point-mass top-K
+    tree (probe off), RheoSampling's tree verified probe last (RRSw) and probe first."""
+    import torch
+
+    import synth
+    from synth import workloads
+    from verify_row_top_amd import vrt
+    dev = torch.device("cuda:0")
+    base = workloads.get(args.workload, T=args.T)
+    w = base.replace(D=1, W=base.K, R=base.K)
+    B, V, K = w.B, w.V, w.K
+    esz = 2 if w.dtype == synth.BF16 else 4
+    ld = (V + 16 // esz - 1) // (16 // esz) * (16 // esz)
+    tdt = torch.int16 if w.dtype == synth.BF16 else torch.float32
+    stream = torch.cuda.current_stream().cuda_stream
+    rates = {}
+    for name, kw in (("topk_vanilla", dict(probe=0)), ("rheo_probe_last_rrsw", dict(order=1)),
+                     ("rheo_probe_first_ot", dict(order=0))):
+        wv = w.replace(**kw)
+        cfg = vrt.make_config(B=B, V=V, dtype=wv.dtype, trunc=wv.trunc, K=K, m=wv.m, probe=wv.probe,
+                              D=1, W=K, R=K, T=wv.T, eps_m0=wv.eps_m0, order=wv.order)
+        N = vrt.tree_layout_of(cfg).N
+        tree = torch.zeros(vrt.tree_bytes(cfg), dtype=torch.uint8, device=dev)
+        ws = torch.zeros(vrt.workspace_bytes(cfg), dtype=torch.uint8, device=dev)
+        views = vrt.tree_views(cfg, tree)
+        stats = torch.zeros((B, 8), dtype=torch.int32, device=dev)
+        out_tokens = torch.zeros((B, 2), dtype=torch.int32, device=dev)
+        out_nodes = torch.zeros((B, 1), dtype=torch.int32, device=dev)
+        out_len = torch.zeros(B, dtype=torch.int32, device=dev)
+        hits = total = 0
+        for s in range(args.ablation):
+            ws_ = wv.replace(gen_seed=w.gen_seed + 104729 * s)
+            p = ws_.params()
+            zipf = torch.from_numpy(ws_.tables()).to(dev)
+            rk = [synth.root_key(ws_.gen_seed, b) for b in range(B)]
+            root_keys = torch.tensor([k - (1 << 64) if k >= (1 << 63) else k for k in rk],
+                                     dtype=torch.int64, device=dev)
+            tree_of = torch.arange(B, dtype=torch.int32, device=dev)
+            draft = torch.empty((B, 1, ld), dtype=tdt, device=dev)
+            synth.rows_dev(p, zipf, root_keys, tree_of, draft[:, 0], synth.DRAFT, stream)
+            vrt.build_tree(cfg, 0, draft, ld, ld, args.seed, s, tree, ws, stats)
+            vrt.build_tree(cfg, vrt.FINISH, None, 0, 0, args.seed, s, tree, ws, stats)
+            node_keys = torch.zeros((B, N), dtype=torch.int64, device=dev)
+            synth.tree_keys_dev(B, N, root_keys, views["n_nodes"], views["node_token"],
+                                views["node_parent"], node_keys, stream)
+            target = torch.empty((B, N, ld), dtype=tdt, device=dev)
+            synth.rows_dev(p, zipf, node_keys.reshape(-1), tree_of.repeat_interleave(N),
+                           target.view(B * N, ld), synth.TARGET, stream)
+            vrt.verify_tree(cfg, target, ld, N * ld, tree, args.seed, s, ws, out_tokens, out_nodes,
+                            out_len, stats)
+            hits += int((out_len >= 2).sum().item())
+            total += B
+        rates[name] = hits / total
+    print(json.dumps({"ablation_depth1": rates, "workload": f"{w.name} rows, D=1, K={K}, m={w.m}, "
+                      f"T={w.T}", "trees": total}), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return
+    if args.ablation:
+        ablation(args)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (trees are "
