@@ -42,7 +42,8 @@ class Exp(ctypes.Structure):
                 ("sup_id", ctypes.c_int32 * MAXSUP), ("sup_logit", ctypes.c_float * MAXSUP),
                 ("q_raw", ctypes.c_float * MAXSUP), ("q_T", ctypes.c_double * MAXSUP),
                 ("z_raw", ctypes.c_float), ("proxy", ctypes.c_float),
-                ("z_T", ctypes.c_double), ("u", ctypes.c_double)]
+                ("z_T", ctypes.c_double), ("u", ctypes.c_double),
+                ("probe_token", ctypes.c_int32), ("dense_q", ctypes.c_void_p)]
 
 
 class NodeOut(ctypes.Structure):
@@ -95,6 +96,8 @@ def _declare(L):
     L.orc_pairwise128.restype = f32
     L.orc_support.argtypes = [vp, i32, i32, vp, vp]
     L.orc_support.restype = i32
+    L.orc_support_mass.argtypes = [vp, i32, i32]
+    L.orc_support_mass.restype = ctypes.c_double
     L.orc_tree_create.argtypes = [P(Cfg), u64, i32, u32]
     L.orc_tree_create.restype = vp
     L.orc_tree_free.argtypes = [vp]
@@ -138,6 +141,7 @@ def _p(a):
 
 
 PROBE_FIRST, PROBE_LAST = 0, 1
+DENSE = 0  # trunc value: no truncation (the support is the whole vocabulary)
 
 
 def make_cfg(V, trunc=128, K=8, m=1, probe=1, D=8, W=0, R=60, mode=TOPR, budget=128, T=1.0,
@@ -177,6 +181,12 @@ def support(row, trunc=128):
     vals = np.empty(trunc, np.float32)
     n = lib().orc_support(_p(row), row.size, trunc, _p(ids), _p(vals))
     return ids[:n].copy(), vals[:n].copy()
+
+
+def support_mass(row, trunc=128):
+    """Share of the untempered softmax of `row` held by its min(trunc, V) largest logits."""
+    row = np.ascontiguousarray(row, dtype=np.float32)
+    return lib().orc_support_mass(_p(row), row.size, trunc)
 
 
 class Tree:
@@ -233,7 +243,7 @@ class Tree:
     def view(self):
         """Verification view: dict of arrays (node 0 = root)."""
         cap = self.L.orc_n_cand(self.h) + 1
-        tc = self.cfg.trunc
+        tc = self.cfg.trunc if self.cfg.trunc != DENSE else self.cfg.V
         d = {k: np.zeros(cap, np.int32) for k in ("token", "parent", "depth", "kind", "cand", "tail_n")}
         d["child_off"] = np.zeros(cap + 1, np.int32)
         d["child"] = np.zeros(cap, np.int32)

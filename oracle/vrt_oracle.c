@@ -130,6 +130,25 @@ int32_t orc_support(const float* row, int32_t V, int32_t trunc, int32_t* ids, fl
   return n;
 }
 
+double orc_support_mass(const float* row, int32_t V, int32_t trunc) {
+  int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)V);
+  float* vals = (float*)malloc(sizeof(float) * (size_t)V);
+  orc_support(row, V, V, ids, vals);
+  const double M = (double)vals[0];
+  double top = 0.0, all = 0.0;
+  if (!(isinf(vals[0]) && vals[0] < 0)) {
+    const int32_t n = V < trunc ? V : trunc;
+    for (int32_t i = 0; i < V; ++i) { /* in rank order */
+      const double e = exp((double)vals[i] - M);
+      all += e;
+      if (i < n) top += e;
+    }
+  }
+  free(ids);
+  free(vals);
+  return all > 0.0 ? top / all : 0.0;
+}
+
 /* ------------------------------------------------------------------------- */
 struct orc_tree {
   orc_cfg cfg;
@@ -188,6 +207,7 @@ orc_tree* orc_tree_create(const orc_cfg* cfg, uint64_t seed, int32_t b, uint32_t
 
 void orc_tree_free(orc_tree* t) {
   if (!t) return;
+  for (int32_t r = 0; r < t->n_row_cap; ++r) free(t->rows[r].dense_q);
   free(t->cand);
   free(t->rows);
   free(t->front);
@@ -219,18 +239,161 @@ static void add_child(orc_tree* t, int32_t layer, int32_t pos, int32_t slot, int
   x->score = score_of(t, parent) * q; /* path product, fp32 */
 }
 
+/* Proxy probability of the probe (key design 2): min{q(x_m), z}, or min(1, q(x_1) + eps)
+ * when m = 0. t0 is the number of deterministic children; probe last, x_m is the last of
+ * them (the last filler) and z the mass after it. */
+static float proxy_of(const orc_cfg* c, const orc_exp* e, int32_t t0) {
+  if (t0 >= 1) return e->q_raw[t0 - 1] < e->z_raw ? e->q_raw[t0 - 1] : e->z_raw;
+  const float a = e->q_raw[0] + c->eps_m0;
+  return a < 1.0f ? a : 1.0f;
+}
+
+/* Expansion of one node over the whole vocabulary (trunc = ORC_DENSE): the dense
+ * baseline of RheoSampling's support-size ablation. Ranks, deterministic and filler
+ * slots, the probe's tail and its proxy follow key design 2 as on a truncated support,
+ * with the support being every token. Two readings fix what the sorted 128-entry
+ * support left implicit:
+ *   - the ranking normaliser E and the raw tail mass are fp32 pairwise sums over the
+ *     row in token-id order (zero-padded to a power of two), and z = E_tail / E;
+ *   - the probe is drawn from the tempered tail by inverse CDF in token-id order (every
+ *     order gives the same law; id order needs no sort of the row).
+ * Tempered values are fp64 as on the truncated path. */
+static void expand_dense(orc_tree* t, int32_t layer, int32_t pos, int32_t node, const float* row,
+                         orc_exp* e, int32_t r) {
+  const orc_cfg* c = &t->cfg;
+  const int32_t V = c->V;
+  int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)V);
+  float* vals = (float*)malloc(sizeof(float) * (size_t)V);
+  orc_support(row, V, V, ids, vals);
+  const float M = vals[0];
+  if (isinf(M) && M < 0) e->flags |= 2;
+  if (e->flags) {
+    t->flags |= e->flags;
+    free(ids);
+    free(vals);
+    return;
+  }
+  e->n_sup = V;
+  const int32_t keep = V < ORC_MAXSUP ? V : ORC_MAXSUP; /* ranks recorded in the row */
+
+  /* untempered, fp32 recipe, sums in id order */
+  float* ex = (float*)malloc(sizeof(float) * (size_t)V);
+  float* tx = (float*)malloc(sizeof(float) * (size_t)V);
+  uint8_t* det = (uint8_t*)calloc((size_t)V, 1);
+  for (int32_t v = 0; v < V; ++v) ex[v] = orc_exp_rank(row[v] - M);
+  const float E = pairwise(ex, V);
+  const int32_t m = c->probe ? c->m : 0;
+  const int32_t t0 = c->order == ORC_PROBE_LAST ? (c->K - 1 < V ? c->K - 1 : V) : m;
+  for (int32_t i = 0; i < t0; ++i) det[ids[i]] = 1; /* the deterministic children */
+  for (int32_t v = 0; v < V; ++v) tx[v] = det[v] ? 0.0f : ex[v];
+  e->z_raw = pairwise(tx, V) / E;
+  for (int32_t i = 0; i < keep; ++i) {
+    e->sup_id[i] = ids[i];
+    e->sup_logit[i] = vals[i];
+    e->q_raw[i] = ex[ids[i]] / E;
+  }
+
+  /* tempered, fp64 */
+  const double invT = (double)(1.0f / c->T);
+  double* et = (double*)malloc(sizeof(double) * (size_t)V);
+  double Z = 0.0, zT = 0.0;
+  for (int32_t v = 0; v < V; ++v) {
+    et[v] = exp(((double)row[v] - (double)M) * invT);
+    Z += et[v];
+    if (!det[v]) zT += et[v];
+  }
+  for (int32_t i = 0; i < keep; ++i) e->q_T[i] = et[ids[i]] / Z;
+  e->z_T = zT / Z;
+
+  /* probe: x_s ~ the tempered tail renormalised, inverse CDF in token-id order */
+  int32_t s = -1;
+  if (c->probe && V > t0 && zT > 0.0) {
+    const double u = orc_uniform(t->seed, (uint32_t)(node + 1), (uint32_t)t->b, t->step,
+                                 ORC_PURPOSE_PROBE);
+    e->u = u;
+    const double target = u * zT;
+    double cum = 0.0, before = 0.0;
+    for (int32_t v = 0; v < V; ++v) {
+      if (det[v]) continue;
+      before = cum;
+      cum += et[v];
+      if (target < cum) {
+        s = v;
+        break;
+      }
+    }
+    if (s < 0) { /* rounding exhausted the sum: the last tail token with mass */
+      for (int32_t v = V - 1; v >= 0; --v)
+        if (!det[v] && et[v] > 0.0) {
+          s = v;
+          break;
+        }
+      before = zT - et[s];
+      cum = zT;
+    }
+    int32_t has_after = 0;
+    for (int32_t v = s + 1; v < V; ++v)
+      if (!det[v] && et[v] > 0.0) has_after = 1;
+    if ((before > 0.0 && fabs(u - before / zT) < ORC_EXEMPT_BAND) ||
+        (has_after && fabs(u - cum / zT) < ORC_EXEMPT_BAND)) {
+      e->exempt = 1;
+      t->n_exempt++;
+    }
+    e->probe_token = s;
+    for (int32_t i = 0; i < keep; ++i)
+      if (ids[i] == s) e->probe_rank = i;
+    e->proxy = proxy_of(c, e, t0);
+    /* the probe's tail for verification: q~ = et / zT off the deterministic children */
+    e->dense_q = (double*)malloc(sizeof(double) * (size_t)V);
+    for (int32_t v = 0; v < V; ++v) e->dense_q[v] = det[v] ? 0.0 : et[v] / zT;
+  }
+
+  /* slots: top-m deterministic, the probe, then the next ranks as fillers (probe last:
+   * the fillers, then the probe) */
+  int32_t slot = 0;
+  if (!c->probe) {
+    for (int32_t i = 0; i < V && slot < c->K; ++i)
+      add_child(t, layer, pos, slot++, node, r, ids[i], ORC_DET, e->q_raw[i]);
+  } else {
+    for (int32_t i = 0; i < m && i < V && slot < c->K; ++i)
+      add_child(t, layer, pos, slot++, node, r, ids[i], ORC_DET, e->q_raw[i]);
+    if (c->order == ORC_PROBE_LAST) {
+      for (int32_t i = m; i < t0 && slot < c->K; ++i)
+        add_child(t, layer, pos, slot++, node, r, ids[i], ORC_FILL, e->q_raw[i]);
+      if (s >= 0 && slot < c->K) add_child(t, layer, pos, slot++, node, r, s, ORC_PROBE, e->proxy);
+    } else {
+      if (s >= 0 && slot < c->K) add_child(t, layer, pos, slot++, node, r, s, ORC_PROBE, e->proxy);
+      for (int32_t i = m; i < V && slot < c->K; ++i)
+        if (ids[i] != s) add_child(t, layer, pos, slot++, node, r, ids[i], ORC_FILL, e->q_raw[i]);
+    }
+  }
+  e->n_child = slot;
+  free(ids);
+  free(vals);
+  free(ex);
+  free(tx);
+  free(det);
+  free(et);
+}
+
 /* Expansion of one node (RheoSampling key designs 1 and 2; temperature policy
  * of its settings paragraph). */
 static void expand_node(orc_tree* t, int32_t layer, int32_t pos, int32_t node, const float* row) {
   const orc_cfg* c = &t->cfg;
   const int32_t r = orc_row_base(t, layer) + pos;
   orc_exp* e = &t->rows[r];
+  free(e->dense_q);
   memset(e, 0, sizeof(*e));
   e->node = node;
   e->probe_rank = -1;
+  e->probe_token = -1;
 
   for (int32_t v = 0; v < c->V; ++v)
     if (isnan(row[v]) || (isinf(row[v]) && row[v] > 0)) e->flags |= 1;
+  if (c->trunc == ORC_DENSE) {
+    expand_dense(t, layer, pos, node, row, e, r);
+    return;
+  }
   /* 1. support: the top-trunc logits; the rest are -inf */
   const int32_t n = orc_support(row, c->V, c->trunc, e->sup_id, e->sup_logit);
   e->n_sup = n;
@@ -302,14 +465,8 @@ static void expand_node(orc_tree* t, int32_t layer, int32_t pos, int32_t node, c
       t->n_exempt++;
     }
     e->probe_rank = js;
-    /* proxy probability: min{q(x_m), z}; q(x_1) + eps when m = 0 (probe last: x_m is
-     * the last deterministic child and z the mass after it) */
-    if (t0 >= 1) {
-      e->proxy = e->q_raw[t0 - 1] < e->z_raw ? e->q_raw[t0 - 1] : e->z_raw;
-    } else {
-      const float a = e->q_raw[0] + c->eps_m0;
-      e->proxy = a < 1.0f ? a : 1.0f;
-    }
+    e->probe_token = e->sup_id[js];
+    e->proxy = proxy_of(c, e, t0);
   }
 
   /* 4. slots: top-m deterministic, the probe, then the next ranks as fillers */
@@ -487,6 +644,22 @@ int32_t orc_tree_view(const orc_tree* t, int32_t cap, int32_t tail_cap, int32_t*
     const int32_t K1 = t->cfg.K - 1 < e->n_sup ? t->cfg.K - 1 : e->n_sup;
     const int32_t t0 = t->cfg.order == ORC_PROBE_LAST ? K1 : t->cfg.m;
     int32_t k = 0;
+    if (t->cfg.trunc == ORC_DENSE) { /* every token off the deterministic children, id order */
+      for (int32_t v = 0; v < t->cfg.V; ++v) {
+        int32_t is_det = 0;
+        for (int32_t r = 0; r < t0; ++r) is_det |= e->sup_id[r] == v;
+        if (is_det) continue;
+        if (k >= tail_cap) {
+          free(node_of);
+          return -2;
+        }
+        tail_id[(int64_t)i * tail_cap + k] = v;
+        tail_q[(int64_t)i * tail_cap + k] = e->dense_q[v];
+        ++k;
+      }
+      tail_n[i] = k;
+      continue;
+    }
     for (int32_t r = t0; r < e->n_sup; ++r) {
       if (k >= tail_cap) {
         free(node_of);
@@ -726,7 +899,7 @@ static int32_t one_step(const orc_cfg* cfg, int32_t max_len, const float* dtab, 
     orc_expand_layer(t, layer, rows, V);
   }
   orc_finish(t);
-  const int32_t N = t->n_nodes, TC = cfg->trunc;
+  const int32_t N = t->n_nodes, TC = cfg->trunc == ORC_DENSE ? V : cfg->trunc;
   int32_t* iv = (int32_t*)malloc(sizeof(int32_t) * (size_t)(8 * N + 8));
   int32_t *token = iv, *parent = iv + N, *depth = iv + 2 * N, *kind = iv + 3 * N,
           *cand = iv + 4 * N, *child_off = iv + 5 * N, *child = iv + 6 * N + 1,

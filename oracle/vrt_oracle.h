@@ -49,6 +49,11 @@ enum { ORC_PURPOSE_PROBE = 1, ORC_PURPOSE_TEST = 2, ORC_PURPOSE_FINAL = 3 };
  * deterministic children never lie in its tail, and tested after them. */
 enum { ORC_PROBE_FIRST = 0, ORC_PROBE_LAST = 1 };
 
+/* trunc = ORC_DENSE: no truncation, the support is the whole vocabulary (the dense
+ * baseline of RheoSampling's support-size ablation, full-vocabulary softmax and
+ * sampling). See expand_dense in vrt_oracle.c for the two readings it takes. */
+#define ORC_DENSE 0
+
 typedef struct {
   int32_t V, trunc, K, m, probe, D, W, R, mode, budget;
   float T, eps_m0;
@@ -72,6 +77,8 @@ typedef struct {
   double q_T[ORC_MAXSUP];
   float z_raw, proxy;
   double z_T, u;
+  int32_t probe_token; /* the probe's token, -1 if none */
+  double* dense_q;     /* dense rows with a probe: q~ of every token (0 off the tail) */
 } orc_exp;
 
 typedef struct orc_tree orc_tree;
@@ -91,6 +98,11 @@ float orc_exp_rank(float x);
 void orc_exp_rank_array(const float* x, float* y, int64_t n);
 float orc_pairwise128(const float* v);
 int32_t orc_support(const float* row, int32_t V, int32_t trunc, int32_t* ids, float* vals);
+
+/* Coverage of a truncated support (RheoSampling's support-size ablation): the share of
+ * the untempered draft softmax of one row that its min(trunc, V) largest logits hold,
+ * in fp64. A row with no finite logit has coverage 0. */
+double orc_support_mass(const float* row, int32_t V, int32_t trunc);
 
 orc_tree* orc_tree_create(const orc_cfg* cfg, uint64_t seed, int32_t b, uint32_t step);
 void orc_tree_free(orc_tree* t);

@@ -96,6 +96,17 @@ def smart_ok():
     return True
 
 
+def dense_ok():
+    from tests import test_oracle_dense as td
+    try:
+        td.test_dense_probabilities_slots_and_proxy(1, 1.0, 0)
+        td.test_dense_probabilities_slots_and_proxy(1, 1.0, 1)
+        td.test_dense_probe_draw_follows_the_tempered_tail(1.0, 0)
+    except AssertionError:
+        return False
+    return True
+
+
 MUTANTS = [
     ("residual_mass_ignores_overlap", "    W = 1.0 - overlap;", "    W = 1.0;",
      lambda: lossless_ok() and acceptance_ok()),
@@ -111,8 +122,8 @@ MUTANTS = [
      "w[v] = exp((double)x[v] - (double)M);", lambda: lossless_ok(T=0.6)),
     ("tail_mass_includes_top_m", "for (int32_t i = t0; i < n; ++i) zT += e->q_T[i];",
      "for (int32_t i = 0; i < n; ++i) zT += e->q_T[i];", lambda: slots_ok() and lossless_ok()),
-    ("proxy_takes_max", "e->proxy = e->q_raw[t0 - 1] < e->z_raw ? e->q_raw[t0 - 1] : e->z_raw;",
-     "e->proxy = e->q_raw[t0 - 1] > e->z_raw ? e->q_raw[t0 - 1] : e->z_raw;", slots_ok),
+    ("proxy_takes_max", "return e->q_raw[t0 - 1] < e->z_raw ? e->q_raw[t0 - 1] : e->z_raw;",
+     "return e->q_raw[t0 - 1] > e->z_raw ? e->q_raw[t0 - 1] : e->z_raw;", slots_ok),
     # probe last (the RRSw baseline)
     ("probe_last_ratio_ignores_residual_mass", "const double a = w[token[probe]] / (W * qs);",
      "const double a = w[token[probe]] / qs;", lambda: rrsw_lossless_ok() and rrsw_acceptance_ok()),
@@ -125,6 +136,15 @@ MUTANTS = [
     ("fillers_repeat_probe", "if (i != js) add_child", "if (i >= 0) add_child", slots_ok),
     ("support_tie_break_reversed", "return (x->id < y->id) ? -1 : (x->id > y->id);",
      "return (x->id > y->id) ? -1 : (x->id < y->id);", support_ok),
+    # the dense baseline (support = the whole vocabulary)
+    ("dense_tail_includes_deterministic", "for (int32_t i = 0; i < t0; ++i) det[ids[i]] = 1;",
+     "for (int32_t i = 0; i < 0; ++i) det[ids[i]] = 1;", dense_ok),
+    ("dense_raw_tail_mass_is_everything", "e->z_raw = pairwise(tx, V) / E;",
+     "e->z_raw = pairwise(ex, V) / E;", dense_ok),
+    ("dense_draw_walks_deterministic_tokens", "      if (det[v]) continue;\n      before = cum;",
+     "      before = cum;", dense_ok),
+    ("dense_fillers_repeat_probe", "if (ids[i] != s) add_child", "if (ids[i] >= 0) add_child",
+     dense_ok),
     ("smart_leaf_count_inverted", "if (t->has_child[par + 1]) t->n_paths += 1;",
      "if (!t->has_child[par + 1]) t->n_paths += 1;", smart_ok),
 ]
