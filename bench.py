@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--ablation", type=int, default=0, metavar="SETS",
                     help="only the depth-1 verification comparison (point-mass top-K, probe last "
                          "= RRSw, probe first = RheoVerification) over SETS input sets")
+    ap.add_argument("--sweep", type=int, default=0, metavar="SETS",
+                    help="only the support-size sweep (trunc 128/256/512/1024 and the dense "
+                         "baseline) over SETS input sets")
     return ap.parse_args()
 
 
@@ -131,6 +134,136 @@ def read_ceiling(torch, dev, vrt, mib=1024, reps=10):
     return (mib << 20) / (ms * 1e-3) / 1e9
 
 
+def make_inputs(w, cfg, dev, gen_seed, seed, step, tree, ws, stats, views, target=True):
+    """One input set: the generator plays the draft model along the GPU's own frontier,
+    layer by layer (building the tree as it goes), then the target model on the emitted
+    tree. Returns (draft [B, rows, ld], target [B, N, ld] or None, n_nodes [B] on the
+    host, expanded rows per layer)."""
+    import torch
+
+    import synth
+    from verify_row_top_amd import vrt
+    L = vrt.tree_layout_of(cfg)
+    B, D, K, N, FP = w.B, w.D, w.K, L.N, L.FP
+    esz = 2 if w.dtype == synth.BF16 else 4
+    ld = (w.V + 16 // esz - 1) // (16 // esz) * (16 // esz)
+    tdt = torch.int16 if w.dtype == synth.BF16 else torch.float32
+    n_draft = 1 + (D - 1) * FP
+    stream = torch.cuda.current_stream().cuda_stream
+    ws_ = w.replace(gen_seed=gen_seed)
+    p = ws_.params()
+    zipf = torch.from_numpy(ws_.tables()).to(dev)
+    rk = [synth.root_key(gen_seed, b) for b in range(B)]
+    root_keys = torch.tensor([k - (1 << 64) if k >= (1 << 63) else k for k in rk],
+                             dtype=torch.int64, device=dev)
+    tree_of = torch.arange(B, dtype=torch.int32, device=dev)
+    draft = torch.empty((B, n_draft, ld), dtype=tdt, device=dev)
+    tmp = torch.empty((B, FP, ld), dtype=tdt, device=dev)
+    keys_prev = root_keys.view(B, 1)
+    synth.rows_dev(p, zipf, keys_prev.reshape(-1), tree_of, tmp[:, 0], synth.DRAFT, stream)
+    draft[:, 0].copy_(tmp[:, 0])
+    vrt.build_tree(cfg, 0, draft, ld, n_draft * ld, seed, step, tree, ws, stats)
+    expanded = [torch.ones(B, dtype=torch.int32)]
+    for layer in range(1, D):
+        base = 0 if layer == 1 else K + (layer - 2) * FP * K  # the previous layer's candidates
+        keys = torch.zeros((B, FP), dtype=torch.int64, device=dev)
+        synth.frontier_keys_dev(B, K, base, keys_prev, views["front"], views["n_front"],
+                                views["cand_token"], keys, stream)
+        expanded.append(views["n_front"].cpu().clone())
+        synth.rows_dev(p, zipf, keys.reshape(-1), tree_of.repeat_interleave(FP),
+                       tmp.view(B * FP, ld), synth.DRAFT, stream)
+        r0 = 1 + (layer - 1) * FP
+        draft[:, r0:r0 + FP].copy_(tmp)
+        vrt.build_tree(cfg, layer, draft[:, r0:], ld, n_draft * ld, seed, step, tree, ws, stats)
+        keys_prev = keys
+    vrt.build_tree(cfg, vrt.FINISH, None, 0, 0, seed, step, tree, ws, stats)
+    tgt = None
+    if target:
+        node_keys = torch.zeros((B, N), dtype=torch.int64, device=dev)
+        synth.tree_keys_dev(B, N, root_keys, views["n_nodes"], views["node_token"],
+                            views["node_parent"], node_keys, stream)
+        tgt = torch.empty((B, N, ld), dtype=tdt, device=dev)
+        synth.rows_dev(p, zipf, node_keys.reshape(-1), tree_of.repeat_interleave(N),
+                       tgt.view(B * N, ld), synth.TARGET, stream)
+    torch.cuda.synchronize()
+    return draft, tgt, views["n_nodes"].cpu().clone(), expanded
+
+
+def sweep(args):
+    """Support-size sweep (RheoSampling's support-size ablation) on the workload: for each
+    support size and the dense baseline (support = the whole vocabulary), the draft-side
+    time of one step (every build layer and the finish, HIP events on the launch stream),
+    the mean coverage of the expanded rows' supports, and the mean tokens per verified
+    tree. Dense trees with the probe on carry no tail table and are not verified."""
+    import torch
+
+    import synth
+    from synth import workloads
+    from verify_row_top_amd import vrt
+    dev = torch.device("cuda:0")
+    w0 = workloads.get(args.workload, T=args.T)
+    B, V, D = w0.B, w0.V, w0.D
+    esz = 2 if w0.dtype == synth.BF16 else 4
+    ld = (V + 16 // esz - 1) // (16 // esz) * (16 // esz)
+    reps = max(1, args.steps)
+    out = []
+    for trunc in (128, 256, 512, 1024, vrt.DENSE):
+        w = w0.replace(trunc=trunc)
+        cfg = vrt.make_config(B=B, V=V, dtype=w.dtype, trunc=trunc, K=w.K, m=w.m, probe=w.probe, D=D,
+                              W=w.W, R=w.R, mode=w.mode, budget=w.budget, T=w.T, eps_m0=w.eps_m0,
+                              order=w.order)
+        L = vrt.tree_layout_of(cfg)
+        N, FP = L.N, L.FP
+        n_draft = 1 + (D - 1) * FP
+        tree = torch.zeros(vrt.tree_bytes(cfg), dtype=torch.uint8, device=dev)
+        ws = torch.zeros(vrt.workspace_bytes(cfg), dtype=torch.uint8, device=dev)
+        views = vrt.tree_views(cfg, tree)
+        stats = torch.zeros((B, 8), dtype=torch.int32, device=dev)
+        out_tokens = torch.zeros((B, D + 1), dtype=torch.int32, device=dev)
+        out_nodes = torch.zeros((B, D), dtype=torch.int32, device=dev)
+        out_len = torch.zeros(B, dtype=torch.int32, device=dev)
+        cov = torch.zeros((B, n_draft), dtype=torch.float64, device=dev)
+        verify = trunc != vrt.DENSE or not w.probe
+        times, covs, lens = [], [], []
+        for s in range(args.sweep):
+            draft, target, _, expanded = make_inputs(w, cfg, dev, w.gen_seed + 7919 * s, args.seed, s,
+                                                     tree, ws, stats, views, target=verify)
+            # coverage of the expanded rows (layer 0: the root; layer l: the first n_front rows)
+            vrt.support_coverage(cfg, draft, ld, n_draft * ld, n_draft, cov)
+            c = cov.cpu().numpy()
+            for layer in range(D):
+                r0 = 0 if layer == 0 else 1 + (layer - 1) * FP
+                for b in range(B):
+                    covs.extend(c[b, r0:r0 + int(expanded[layer][b])].tolist())
+            if verify:
+                vrt.verify_tree(cfg, target, ld, N * ld, tree, args.seed, s, ws, out_tokens, out_nodes,
+                                out_len, stats)
+                lens.append(out_len.float().mean().item())
+            del target
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            for k in range(reps + 2):
+                if k == 2:
+                    ev[0].record()
+                for layer in range(D):
+                    r0 = 0 if layer == 0 else 1 + (layer - 1) * FP
+                    vrt.build_tree(cfg, layer, draft[:, r0:], ld, n_draft * ld, args.seed, s, tree, ws,
+                                   stats)
+                vrt.build_tree(cfg, vrt.FINISH, None, 0, 0, args.seed, s, tree, ws, stats)
+            ev[1].record()
+            torch.cuda.synchronize()
+            times.append(ev[0].elapsed_time(ev[1]) / reps)
+            del draft
+        rec = {"trunc": "dense" if trunc == vrt.DENSE else trunc,
+               "build_ms_per_step": sum(times) / len(times),
+               "coverage_mean": float(sum(covs) / len(covs)),
+               "tokens_per_tree": (sum(lens) / len(lens)) if lens else None,
+               "status_bits": int((stats.cpu()[:, 0] != 0).sum())}
+        print(json.dumps(rec), flush=True)
+        out.append(rec)
+    print(json.dumps({"support_sweep": out, "workload": f"{w0.name}: B={B}, V={V}, D={D}, K={w0.K}, "
+                      f"m={w0.m}, T={w0.T}", "sets": args.sweep, "reps_per_set": reps}), flush=True)
+
+
 def ablation(args):
     """Depth-1 controlled comparison of the verification orders on the workload's rows: the
     share of trees whose first emitted token comes from the tree, for the point-mass top-K
@@ -198,6 +331,9 @@ def main():
     if args.ablation:
         ablation(args)
         return
+    if args.sweep:
+        sweep(args)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (trees are "
               f"independent: shard the batch, one process per GPU)", file=sys.stderr)
@@ -222,7 +358,6 @@ def main():
     esz = 2 if w.dtype == synth.BF16 else 4
     per = 16 // esz
     ld = (V + per - 1) // per * per
-    tdt = torch.int16 if w.dtype == synth.BF16 else torch.float32
     n_draft = 1 + (D - 1) * FP
     tree = torch.zeros(vrt.tree_bytes(cfg), dtype=torch.uint8, device=dev)
     ws = torch.zeros(vrt.workspace_bytes(cfg), dtype=torch.uint8, device=dev)
@@ -237,45 +372,12 @@ def main():
     # layer, then the target model on the emitted tree (untimed). Steps rotate over the
     # sets, so between two reads of the same bytes more than 2 GB of other rows pass
     # through HBM and the 256 MB last-level cache cannot serve them.
-    stream = torch.cuda.current_stream().cuda_stream
     seed, step = args.seed, 0
 
-    def layer_base(l):
-        return 0 if l == 0 else K + (l - 1) * FP * K
-
     def make_set(gen_seed):
-        ws_ = w.replace(gen_seed=gen_seed)
-        p = ws_.params()
-        zipf = torch.from_numpy(ws_.tables()).to(dev)
-        rk = [synth.root_key(gen_seed, b) for b in range(B)]
-        root_keys = torch.tensor([k - (1 << 64) if k >= (1 << 63) else k for k in rk],
-                                 dtype=torch.int64, device=dev)
-        tree_of = torch.arange(B, dtype=torch.int32, device=dev)
-        draft = torch.empty((B, n_draft, ld), dtype=tdt, device=dev)
-        target = torch.empty((B, N, ld), dtype=tdt, device=dev)
-        tmp = torch.empty((B, FP, ld), dtype=tdt, device=dev)
-        keys_prev = root_keys.view(B, 1)
-        synth.rows_dev(p, zipf, keys_prev.reshape(-1), tree_of, tmp[:, 0], synth.DRAFT, stream)
-        draft[:, 0].copy_(tmp[:, 0])
-        vrt.build_tree(cfg, 0, draft, ld, n_draft * ld, seed, step, tree, ws, stats)
-        for layer in range(1, D):
-            keys = torch.zeros((B, FP), dtype=torch.int64, device=dev)
-            synth.frontier_keys_dev(B, K, layer_base(layer - 1), keys_prev, views["front"],
-                                    views["n_front"], views["cand_token"], keys, stream)
-            synth.rows_dev(p, zipf, keys.reshape(-1), tree_of.repeat_interleave(FP),
-                           tmp.view(B * FP, ld), synth.DRAFT, stream)
-            r0 = 1 + (layer - 1) * FP
-            draft[:, r0:r0 + FP].copy_(tmp)
-            vrt.build_tree(cfg, layer, draft[:, r0:], ld, n_draft * ld, seed, step, tree, ws, stats)
-            keys_prev = keys
-        vrt.build_tree(cfg, vrt.FINISH, None, 0, 0, seed, step, tree, ws, stats)
-        node_keys = torch.zeros((B, N), dtype=torch.int64, device=dev)
-        synth.tree_keys_dev(B, N, root_keys, views["n_nodes"], views["node_token"],
-                            views["node_parent"], node_keys, stream)
-        synth.rows_dev(p, zipf, node_keys.reshape(-1), tree_of.repeat_interleave(N),
-                       target.view(B * N, ld), synth.TARGET, stream)
-        torch.cuda.synchronize()
-        return draft, target, views["n_nodes"].cpu().clone()
+        draft, target, n_nodes, _ = make_inputs(w, cfg, dev, gen_seed, seed, step, tree, ws, stats,
+                                                views)
+        return draft, target, n_nodes
 
     sets = [make_set(w.gen_seed + 7919 * s) for s in range(args.sets)]
 

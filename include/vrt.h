@@ -54,6 +54,7 @@ typedef enum { VRT_F32 = 0, VRT_BF16 = 1 } vrt_dtype;
 typedef enum { VRT_MODE_TOPR = 0, VRT_MODE_SMART = 1 } vrt_mode;
 enum { VRT_ROOT = 0, VRT_DET = 1, VRT_PROBE = 2, VRT_FILL = 3 };
 #define VRT_FINISH (-1)
+#define VRT_DENSE 0 /* vrt_config.trunc: no truncation (see trunc below) */
 
 /* status bits, stats[b][0] */
 #define VRT_ST_DRAFT_NONFINITE 0x1u  /* NaN or +Inf in an expanded draft row */
@@ -64,7 +65,13 @@ enum { VRT_ROOT = 0, VRT_DET = 1, VRT_PROBE = 2, VRT_FILL = 3 };
  *   B        trees in the batch (>= 1)
  *   V        vocabulary size (1 .. 2^20)
  *   dtype    VRT_F32 or VRT_BF16 logits
- *   trunc    support size of the draft truncation (1 .. 1024; the pages use 128)
+ *   trunc    support size of the draft truncation (1 .. 1024; the pages use 128), or
+ *            VRT_DENSE: no truncation, the support is the whole vocabulary (the dense
+ *            baseline of RheoSampling's support-size ablation). Dense rows rank their
+ *            top K exactly as a truncated support would, sum the ranking exponentials
+ *            pairwise in token-id order and draw the probe by inverse CDF in token-id
+ *            order; they write no tail table, so trees with the probe on cannot be
+ *            verified (the verification entry points return VRT_EINVAL for them)
  *   K        slots per expanded parent (1 .. 30)
  *   m        deterministic top-m slots (probe mode: 0 <= m <= K-1)
  *   probe    1 = RheoSampling dual-identity slots, 0 = plain top-K (all deterministic)
@@ -236,6 +243,22 @@ vrt_status vrt_verify_nodes(const vrt_config* cfg, const void* target_logits, in
 vrt_status vrt_verify_walk(const vrt_config* cfg, const void* tree, void* ws, size_t ws_bytes,
                            int32_t* out_tokens, int32_t* out_nodes, int32_t* out_len, uint32_t* stats,
                            int32_t* node_out, void* stream);
+
+/* Coverage of the truncated support (RheoSampling's support-size ablation, whose
+ * coverage column is the draft probability mass inside the support): for each of the
+ * n_rows rows of each tree, the share of the untempered softmax of the row held by its
+ * cfg->trunc largest logits (ties at the boundary hold equal mass, so which of them is
+ * taken does not matter), in fp64 with exponentials to about 1e-7 relative. trunc =
+ * VRT_DENSE, or trunc >= V, gives 1.
+ *   draft_logits  device rows, laid out as for vrt_build_tree (row j of tree b at
+ *                 b*tree_stride + j*ld elements; ld >= V; 16-byte aligned strides)
+ *   n_rows        rows per tree (1 .. 65535)
+ *   coverage      device f64 [B][n_rows]; 0 for a row with no finite logit, NaN for a row
+ *                 holding NaN or +inf
+ * A measurement of the inputs: the tree build does not need it. Errors: VRT_EINVAL
+ * (config, pointers, strides, n_rows), VRT_EHIP. */
+vrt_status vrt_support_coverage(const vrt_config* cfg, const void* draft_logits, int64_t ld,
+                                int64_t tree_stride, int32_t n_rows, double* coverage, void* stream);
 
 /* The step after the prune (RheoSampling framework flowchart: one target forward
  * verifies the whole tree): attention inputs of that forward over the emitted tree.

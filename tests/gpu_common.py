@@ -93,10 +93,11 @@ class Lib:
         return self.views[name].cpu().numpy()
 
 
-def device_step(w, seed, step, dev):
+def device_step(w, seed, step, dev, verify=True):
     """Every tree of workload w built and verified on the GPU, the way the benchmark
     runs it: the device generator plays the draft model along the GPU's own frontier,
-    layer by layer, then the target model on the emitted trees. Returns the Lib."""
+    layer by layer, then the target model on the emitted trees (unless verify is
+    False). Returns the Lib."""
     cfg = lib_config(w)
     L = Lib(cfg, dev)
     B, D, K, N, FP = w.B, w.D, w.K, L.N, L.FP
@@ -124,6 +125,9 @@ def device_step(w, seed, step, dev):
         keys_prev = keys
     L.finish(seed, step)
     del rows
+    if not verify:
+        torch.cuda.synchronize()
+        return L
     node_keys = torch.zeros((B, N), dtype=torch.int64, device=dev)
     synth.tree_keys_dev(B, N, root_keys, L.views["n_nodes"], L.views["node_token"],
                         L.views["node_parent"], node_keys, stream)

@@ -37,7 +37,7 @@ def test_headline_sizes():
 
 @pytest.mark.parametrize("kw,code", [
     (dict(B=0), vrt.EINVAL), (dict(V=0), vrt.EINVAL), (dict(V=(1 << 20) + 1), vrt.EINVAL),
-    (dict(dtype=7), vrt.EDTYPE), (dict(trunc=0), vrt.EINVAL), (dict(trunc=2048), vrt.EINVAL),
+    (dict(dtype=7), vrt.EDTYPE), (dict(trunc=-1), vrt.EINVAL), (dict(trunc=2048), vrt.EINVAL),
     (dict(K=0), vrt.EINVAL), (dict(K=31), vrt.EINVAL), (dict(m=10, K=10), vrt.EINVAL),
     (dict(m=-1), vrt.EINVAL), (dict(D=0), vrt.EINVAL), (dict(D=33), vrt.EINVAL),
     (dict(R=0), vrt.EINVAL), (dict(T=0.0), vrt.EINVAL), (dict(T=-1.0), vrt.EINVAL),
@@ -115,6 +115,21 @@ def test_verify_argument_errors_are_caught_before_any_launch():
     assert call(wsb=8) == vrt.ENOMEM
     assert call(ld=10) == vrt.EINVAL
     assert call(stride=-16) == vrt.EINVAL
+
+
+def test_dense_config_builds_but_probe_trees_are_not_verified():
+    c = vrt.make_config(B=2, V=1000, K=4, D=3, R=10, trunc=vrt.DENSE)
+    vrt.check_config(c)
+    L = vrt.tree_layout_of(c)
+    assert L.TC == 0 and vrt.tree_bytes(c) > 0
+    v = ctypes.c_void_p
+    r = vrt.lib().vrt_verify_tree(ctypes.byref(c), v(0x10000), 1024, 4096, v(0x20000), 1, 0,
+                                  v(0x30000), 1 << 30, v(0x40000), v(0x50000), v(0x60000),
+                                  v(0x70000), None, None)
+    assert r == vrt.EINVAL and "VRT_DENSE" in vrt.last_error()
+    r = vrt.lib().vrt_verify_nodes(ctypes.byref(c), v(0x10000), 1024, 4096, v(0x20000), 1, 0,
+                                   v(0x30000), 1 << 30, None, None)
+    assert r == vrt.EINVAL
 
 
 def test_split_verify_argument_errors_are_caught_before_any_launch():

@@ -76,7 +76,7 @@ def gpu_build(w, steps, seed, step, dev):
     return L
 
 
-def compare_tree(w, s, L, b):
+def compare_tree(w, s, L, b, tails=True):
     v = L.views
     cands = s.cands
     NC = cands.size
@@ -97,6 +97,9 @@ def compare_tree(w, s, L, b):
     np.testing.assert_array_equal(v["child_off"][b, :n + 1].cpu().numpy(), ov["child_off"])
     nch = ov["child"].size
     np.testing.assert_array_equal(v["child"][b, :nch].cpu().numpy(), ov["child"])
+    if not tails:  # dense trees carry no tail table
+        assert (v["tail_n"][b, :n].cpu().numpy() == 0).all()
+        return
     np.testing.assert_array_equal(v["tail_n"][b, :n].cpu().numpy(), ov["tail_n"])
     tq = v["tail_q"][b].cpu().numpy()
     ti = v["tail_id"][b].cpu().numpy()
@@ -136,12 +139,17 @@ def test_build_and_step_match_oracle(gpu, name, w):
     assert exempt <= max(1, total // 10), (exempt, total)
 
 
-def test_bad_draft_rows_set_status_and_stay_in_bounds(gpu):
-    w = _small(B=3, D=2, R=10)
+@pytest.mark.parametrize("kw", [
+    dict(), dict(dtype=synth.F32, V=70001), dict(trunc=vrt.DENSE),
+    dict(trunc=vrt.DENSE, dtype=synth.F32, V=70001)],
+    ids=["bf16", "fp32_exact_path", "dense_bf16", "dense_fp32"])
+def test_bad_draft_rows_set_status_and_stay_in_bounds(gpu, kw):
+    w = _small(B=3, D=2, R=10, **kw)
     steps = [OracleStep(w, 5, b, 0, verify=False) for b in range(w.B)]
     rows0 = [s.layer_rows[0].copy() for s in steps]
-    rows0[0][0, 11] = 0x7FC0          # NaN in tree 0's root row
-    rows0[1][0, :] = 0xFF80           # tree 1's root row entirely -inf
+    bf = w.dtype == synth.BF16
+    rows0[0][0, 11] = 0x7FC0 if bf else np.nan       # NaN in tree 0's root row
+    rows0[1][0, :] = 0xFF80 if bf else -np.inf       # tree 1's root row entirely -inf
     cfg = lib_config(w)
     L = Lib(cfg, gpu)
     rows, ld = to_device_rows(rows0, w, 1, gpu)
@@ -177,3 +185,58 @@ def test_split_verification_equals_the_whole_call(gpu):
             assert torch.equal(a, b)
         if use_node_out:
             assert torch.equal(L.node_out, ref[4])
+
+
+# Dense rows (trunc = DENSE: the support is the whole vocabulary). Builds are compared
+# bit for bit like truncated ones, without tail tables; the probe-off case is verified
+# too (point masses need no tail).
+DENSE_CASES = [
+    ("dense_small_bf16", _small(trunc=vrt.DENSE)),
+    ("dense_m0_T06", _small(trunc=vrt.DENSE, m=0, T=0.6, V=3000)),
+    ("dense_m3_K8_fp32", _small(trunc=vrt.DENSE, m=3, K=8, R=50, dtype=synth.F32, V=9000)),
+    ("dense_probe_last", _small(trunc=vrt.DENSE, order=1, V=20000, D=4)),
+    ("dense_probe_last_m0_T06_fp32", _small(trunc=vrt.DENSE, order=1, m=0, T=0.6, dtype=synth.F32)),
+    ("dense_tiny_vocab", _small(trunc=vrt.DENSE, V=7, K=5, R=20, D=3, dtype=synth.F32)),
+    ("dense_V_70001", _small(trunc=vrt.DENSE, V=70001, D=3, R=20, B=3)),
+    ("dense_flat_fp32", _small(trunc=vrt.DENSE, dtype=synth.F32, zipf=(0.8,), V=4100, R=30)),
+    ("dense_all_ties", _small(trunc=vrt.DENSE, zipf=(), draft_scale=0.0, V=9000, R=20, D=3)),
+    ("dense_probe_off", _small(trunc=vrt.DENSE, probe=0)),
+    ("dense_smart", _smart_small(trunc=vrt.DENSE)),
+]
+
+
+@pytest.mark.parametrize("name,w", DENSE_CASES, ids=[c[0] for c in DENSE_CASES])
+def test_dense_build_matches_oracle(gpu, name, w):
+    exempt = total = 0
+    for seed, step in [(1, 0), (2, 3)]:
+        steps = [OracleStep(w, seed, b, step, verify=not w.probe) for b in range(w.B)]
+        print(f"dense build parity: {name} seed={seed} step={step} B={w.B} V={w.V}", flush=True)
+        L = gpu_build(w, steps, seed, step, gpu)
+        assert (L.stats.cpu().numpy()[:, 0] == 0).all()
+        if not w.probe:
+            target, ld = to_device_rows([s.target_rows for s in steps], w, L.N, gpu)
+            L.verify(target, ld, seed, step, zero_stats=False)
+        for b, s in enumerate(steps):
+            total += 1
+            try:
+                compare_tree(w, s, L, b, tails=False)
+            except AssertionError:
+                if not s.build_exempt:
+                    raise
+                exempt += 1
+                continue
+            if not w.probe:
+                Lt = len(s.out_tokens)
+                assert L.out_len[b].item() == Lt and np.array_equal(
+                    L.out_tokens[b, :Lt].cpu().numpy(), s.out_tokens) or s.verify_exempt > 0
+    print(f"{name}: {total} trees, {exempt} differ after a near-boundary probe draw")
+    assert exempt <= max(1, total // 10), (exempt, total)
+
+
+def test_dense_trees_with_a_probe_are_not_verified(gpu):
+    w = _small(trunc=vrt.DENSE, B=2, D=2, R=8)
+    L = Lib(lib_config(w), gpu)
+    target = torch.zeros((w.B, L.N, 5000), dtype=torch.int16, device=gpu)
+    with pytest.raises(vrt.VrtError) as e:
+        L.verify(target, 5000, 1, 0)
+    assert e.value.code == vrt.EINVAL and "VRT_DENSE" in str(e.value)

@@ -86,3 +86,23 @@ def test_full_size_step_matches_oracle_on_sampled_trees(gpu, name, w, trees, ss)
           f"{node_exempt} nodes with a near-threshold draw, {node_miss} of those differ")
     assert build_exempt <= max(1, len(trees) // 4)
     assert node_miss <= max(1, node_exempt // 10)
+
+
+def test_dense_headline_build_matches_oracle_on_sampled_trees(gpu):
+    """The dense baseline at the headline size (support = all 128256 tokens): every tree
+    built on the GPU, sampled trees rebuilt by the oracle and compared bit for bit."""
+    w = workloads.get("headline", trunc=0)
+    seed, step = 7, 2
+    print(f"full-size dense build parity: B={w.B} V={w.V} seed={seed} step={step}", flush=True)
+    L = device_step(w, seed, step, gpu, verify=False)
+    assert (L.stats.cpu().numpy()[:, 0] == 0).all()
+    exempt = 0
+    for b in (0, 19, 31):
+        s = OracleStep(w, seed, b, step, verify=False)
+        try:
+            compare_tree(w, s, L, b, tails=False)
+        except AssertionError:
+            if not s.build_exempt:
+                raise
+            exempt += 1
+    assert exempt <= 1

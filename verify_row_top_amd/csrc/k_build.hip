@@ -839,7 +839,8 @@ __device__ __forceinline__ int row_select_exact(const char* row, int id0, int V,
       images(v, im);
       static_for<EPL>([&](auto e) {
         const uint32_t x = im[e];
-        if (lvl == 0) nf |= x != 0u && (x >= PINF || x < NINF);
+        // a row element with image 0 is a NaN (fp32 rows map NaN to 0)
+        if (lvl == 0) nf |= v * EPL + (int)e < V && (x == 0u || x >= PINF || x < NINF);
         if (x >= floor_img && x != 0u && ((uint64_t)(x ^ pre) >> (sh + 8)) == 0u)
           atomicAdd(&H[(x >> sh) & 0xFF], 1);
       });
@@ -1275,6 +1276,366 @@ __attribute__((amdgpu_waves_per_eu(PL == 2 ? 4 : 2, 8))) void k_select_expand(co
   if (a.fuse_rank) rank_if_last(a, b, s_rank);
 }
 
+// ---------------------------------------------------------------------------------
+// Dense expansion (trunc = VRT_DENSE): the untruncated baseline of the support-size
+// ablation, whose support is the whole vocabulary. One 8-wave block per parent:
+//  1. the row's K best keys (value desc, token id asc) by the selection above;
+//  2. one pass over the row in 512-element chunks (the waves take consecutive runs of
+//     chunks, 8 consecutive elements per lane): per chunk the fp32 pairwise sum of the
+//     ranking exponentials over the chunk and over its tail tokens (the deterministic
+//     children excluded), and the fp64 sum of the tempered tail values;
+//  3. the chunk sums combine along the zero-padded pairwise tree in token-id order
+//     (E, E_tail, z = E_tail / E); the probe is drawn by inverse CDF in token-id order:
+//     its chunk from a scan of the chunk sums, its token from one re-read of the chunk;
+//  4. the K child slots as on a truncated support; no tail table is written.
+constexpr int kDC = 512;                       // elements per chunk
+constexpr int kDenseChunks = (1 << 20) / kDC;  // chunks of the largest vocabulary
+
+struct DenseLds {
+  float e[kDenseChunks];   // per chunk: pairwise sum of exp_rank(x - M)
+  float et[kDenseChunks];  // the same over the chunk's tail tokens
+  double z[kDenseChunks];  // per chunk: sum of exp((x - M)/T) over its tail tokens
+  int det[32];             // tokens of the deterministic children (ranks < t0)
+  int n_sup, bad;
+};
+
+// The 8 values of a lane in chunk c (elements c*kDC + 8*lane ..), -inf at and past V.
+template <int DT>
+__device__ __forceinline__ void dense_load(const char* row, int c, int V, float (&x)[8]) {
+  const int e0 = c * kDC + lane_id() * 8;
+  if constexpr (DT == VRT_BF16) {
+    u32x4_t w = {0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u};
+    if (e0 < V) w = *(const u32x4_t*)(row + (int64_t)e0 * 2);
+    static_for<4>([&](auto k) {
+      x[2 * k] = bf16_lo(w[(int)k]);
+      x[2 * k + 1] = bf16_hi(w[(int)k]);
+    });
+  } else {
+    static_for<2>([&](auto h) {
+      u32x4_t w = {0xFF800000u, 0xFF800000u, 0xFF800000u, 0xFF800000u};
+      if (e0 + 4 * h < V) w = *(const u32x4_t*)(row + (int64_t)(e0 + 4 * h) * 4);
+      static_for<4>([&](auto k) { x[4 * h + k] = __uint_as_float(w[(int)k]); });
+    });
+  }
+  if (e0 + 8 > V)
+    static_for<8>([&](auto k) {
+      if (e0 + (int)k >= V) x[k] = -INFINITY;
+    });
+}
+
+// exp((x - M)/T) to about 1e-7 relative: the fp64 exponent is split into an fp32 head
+// and a tail, e^a = e^head (1 + tail).
+__device__ __forceinline__ double dense_tempered(float x, float M, double invT) {
+  if (!(x > -INFINITY)) return 0.0;
+  const double a = ((double)x - (double)M) * invT;
+  const float h = (float)a;
+  const float t = (float)(a - (double)h);
+  return (double)expf(h) * (1.0 + (double)t);
+}
+
+// Whether token v is one of the n deterministic children (wave-uniform list in LDS).
+__device__ __forceinline__ bool dense_is_det(const DenseLds& L, int n, int v) {
+  bool d = false;
+  for (int i = 0; i < n; ++i) d |= L.det[i] == v;
+  return d;
+}
+
+// The tail part of a lane's 8 values and whether its chunk holds a deterministic child.
+__device__ __forceinline__ bool dense_chunk_has_det(const DenseLds& L, int n, int c) {
+  bool d = false;
+  for (int i = 0; i < n; ++i) d |= (L.det[i] >= c * kDC) && (L.det[i] < (c + 1) * kDC);
+  return d;
+}
+
+template <int DT>
+__global__ __launch_bounds__(8 * kWave) void k_dense_expand(const BArgs a) {
+  const Cfg& c = a.c;
+  const int j = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int lane = lane_id();
+  constexpr int SW = 8, PL = 2;
+  constexpr int LSPT = DT == VRT_BF16 ? 3 : 2;
+  __shared__ uint64_t s_rank[kRankFused];
+  const int node = begin_row(a, b, j);
+  if (node == -2) {
+    if (wave == 0 && a.fuse_rank) rank_if_last(a, b, s_rank);
+    return;
+  }
+  const float sp = node < 0 ? 1.0f : a.t.cand_score[(int64_t)b * c.NC + node];
+  union Sel {
+    FastLds<DT, PL> f;
+    ExactLds<PL> x;
+  };
+  __shared__ __align__(16) char s_raw[sizeof(Sel)];
+  __shared__ uint64_t s_sup[PL * kWave];
+  __shared__ DenseLds L;
+  constexpr int esz = DT == VRT_BF16 ? 2 : 4;
+  const char* row = (const char*)a.logits + ((int64_t)b * a.tstride + (int64_t)j * a.ld) * esz;
+  const int64_t ncb = (int64_t)b * c.NC;
+  const int cbase = layer_base(c, a.layer) + j * c.K;
+  const int64_t ktb = (int64_t)b * c.NR + row_base(c, a.layer) + j;
+  const int TK = min(c.K, c.V);  // ranks the slots can use
+
+  // 1. the K best keys and the row maximum
+  {
+    Sel& P = *(Sel*)s_raw;
+    const int G = (c.V + seg_elems<DT>() - 1) / seg_elems<DT>();
+    int n_sup = 0, path = 2;
+    uint32_t floor_img = 0u;
+    if (G <= LSPT * SW) path = row_select_fast<DT, PL, SW, LSPT>(row, 0, G, c.V, TK, P.f, s_sup, n_sup, floor_img);
+    if (path == 2) {
+      __syncthreads();
+      path = row_select_exact<DT, PL, SW>(row, 0, c.V, TK, floor_img, P.x, s_sup, n_sup);
+    }
+    if (tid == 0) {
+      L.n_sup = n_sup;
+      L.bad = path == 1;
+    }
+  }
+  __syncthreads();
+  const int n_sup = L.n_sup;
+  const float M = n_sup > 0 ? sup_key_val(s_sup[0]) : -INFINITY;
+  uint32_t st = L.bad ? VRT_ST_DRAFT_NONFINITE : 0u;
+  if (n_sup == 0 || M == -INFINITY) st |= VRT_ST_DRAFT_EMPTY;
+  if (st) {
+    if (wave == 0) {
+      if (lane == 0 && a.stats) atomicOr(a.stats + (int64_t)b * 8, st);
+      for (int s = lane; s < c.K; s += kWave) st_dev(&a.t.cand_kind[ncb + cbase + s], 0);
+      if (lane == 0) a.t.row_tail_n[ktb] = 0;
+      if (a.fuse_rank) rank_if_last(a, b, s_rank);
+    }
+    return;
+  }
+  const int m = c.probe ? c.m : 0;
+  const int t0 = c.order == VRT_PROBE_LAST ? min(c.K - 1, c.V) : m;  // deterministic ranks
+  if (tid < t0) L.det[tid] = (int)sup_key_id(s_sup[tid]);
+  __syncthreads();
+
+  // 2. chunk sums; wave w takes chunks [w*S, (w+1)*S) of the padded chunk range
+  const int NCH = (c.V + kDC - 1) / kDC;
+  const int NCP = max(1, next_pow2(c.V) / kDC);  // chunks of the zero-padded row
+  const int S = NCP >= SW ? NCP / SW : 1;
+  const double invT = (double)c.invT;
+  for (int ci = wave * S; ci < min(NCP, (wave + 1) * S); ++ci) {
+    float e = 0.0f, et = 0.0f;
+    double z = 0.0;
+    if (ci < NCH) {
+      float x[8];
+      dense_load<DT>(row, ci, c.V, x);
+      const bool hd = dense_chunk_has_det(L, t0, ci);
+      float ex[8], tx[8];
+      double zl = 0.0;
+      static_for<8>([&](auto k) {
+        ex[k] = exp_rank(x[k] - M);
+        const bool tail = !hd || !dense_is_det(L, t0, ci * kDC + lane * 8 + (int)k);
+        tx[k] = tail ? ex[k] : 0.0f;
+        zl += tail ? dense_tempered(x[k], M, invT) : 0.0;
+      });
+      // pairwise inside the lane's 8, then across lanes
+      static_for<4>([&](auto k) { ex[k] = ex[2 * k] + ex[2 * k + 1]; tx[k] = tx[2 * k] + tx[2 * k + 1]; });
+      static_for<2>([&](auto k) { ex[k] = ex[2 * k] + ex[2 * k + 1]; tx[k] = tx[2 * k] + tx[2 * k + 1]; });
+      e = wave_sum(ex[0] + ex[1]);
+      et = wave_sum(tx[0] + tx[1]);
+      z = wave_sum(zl);
+    }
+    if (lane == 0) {
+      L.e[ci] = e;
+      L.et[ci] = et;
+      L.z[ci] = z;
+    }
+  }
+  __syncthreads();
+  if (wave != 0) return;
+
+  // 3. E and E_tail along the pairwise tree: in-place levels down to 64 chunk sums, then
+  //    across lanes
+  for (int w = NCP >> 1; w >= kWave; w >>= 1) {
+    for (int i = lane; i < w; i += kWave) {
+      L.e[i] = L.e[2 * i] + L.e[2 * i + 1];
+      L.et[i] = L.et[2 * i] + L.et[2 * i + 1];
+    }
+    wave_sync();
+  }
+  const int top = min(NCP, kWave);
+  const float E = wave_sum(lane < top ? L.e[lane] : 0.0f);
+  const float Et = wave_sum(lane < top ? L.et[lane] : 0.0f);
+  const float zr = Et / E;
+  // tempered tail mass and the chunk the draw falls in (lane l scans a run of chunks)
+  const int CPL = (NCH + kWave - 1) / kWave;
+  double zl = 0.0;
+  for (int i = lane * CPL; i < min(NCH, (lane + 1) * CPL); ++i) zl += L.z[i];
+  const double incl = wave_incl_scan(zl);
+  const double zT = __shfl(incl, kWave - 1, kWave);
+
+  int probe = -1;
+  float proxy = 0.0f;
+  auto qraw = [&](int r) { return exp_rank(sup_key_val(s_sup[r]) - M) / E; };
+  if (c.probe && c.V > t0 && zT > 0.0) {
+    const double u = (double)uniform24(a.seed, (uint32_t)(node + 1), (uint32_t)b, a.step, kPurposeProbe);
+    const double tgt = u * zT;
+    // the chunk: first whose inclusive prefix passes tgt (else the last with mass)
+    int ch = -1;
+    double before = 0.0;
+    const uint64_t hit = ballot(zl > 0.0 && tgt < incl);
+    const int src = hit ? __builtin_ctzll(hit) : 63 - __builtin_clzll(ballot(zl > 0.0));
+    if (lane == src) {
+      double cum = incl - zl;
+      for (int i = lane * CPL; i < min(NCH, (lane + 1) * CPL); ++i) {
+        if (L.z[i] > 0.0) {
+          ch = i;
+          before = cum;
+          if (tgt < cum + L.z[i]) break;
+        }
+        cum += L.z[i];
+      }
+    }
+    ch = __shfl(ch, src, kWave);
+    before = __shfl(before, src, kWave);
+    // the token: re-read the chunk, tempered tail values in token order
+    float x[8];
+    dense_load<DT>(row, ch, c.V, x);
+    double tv[8], ls = 0.0;
+    static_for<8>([&](auto k) {
+      const int v = ch * kDC + lane * 8 + (int)k;
+      tv[k] = dense_is_det(L, t0, v) ? 0.0 : dense_tempered(x[k], M, invT);
+      ls += tv[k];
+    });
+    const double li = wave_incl_scan(ls);
+    const double rem = tgt - before;
+    int pick = -1;
+    const uint64_t h2 = ballot(ls > 0.0 && rem < li);
+    if (h2) {
+      const int s2 = __builtin_ctzll(h2);
+      if (lane == s2) {
+        double cum = li - ls;
+        static_for<8>([&](auto k) {
+          cum += tv[k];
+          if (pick < 0 && tv[k] > 0.0 && rem < cum) pick = ch * kDC + lane * 8 + (int)k;
+        });
+      }
+      pick = __shfl(pick, s2, kWave);
+    }
+    if (pick < 0) {  // rounding: the chunk's last tail token with mass
+      int last = -1;
+      static_for<8>([&](auto k) {
+        if (tv[k] > 0.0) last = ch * kDC + lane * 8 + (int)k;
+      });
+      for (int o = 1; o < kWave; o <<= 1) last = max(last, __shfl_xor(last, o, kWave));
+      pick = last;
+    }
+    probe = pick;
+    if (t0 >= 1) {
+      const float qm = qraw(t0 - 1);
+      proxy = qm < zr ? qm : zr;
+    } else {
+      const float t1 = qraw(0) + c.eps_m0;
+      proxy = t1 < 1.0f ? t1 : 1.0f;
+    }
+  }
+  if (lane == 0) a.t.row_tail_n[ktb] = 0;
+
+  // 4. child slots: DET ranks, the probe, then fillers in rank order (lane s: slot s)
+  const int rp_hit = (int)__builtin_ctzll(ballot(lane < n_sup && probe >= 0 &&
+                                                 (int)sup_key_id(s_sup[min(lane, n_sup - 1)]) == probe) |
+                                          (1ull << 63));
+  const int rp = rp_hit < n_sup ? rp_hit : 1 << 30;  // the probe's rank if among the K best
+  int r_of_slot = -1, kind = 0;
+  {
+    const int m_det = c.probe ? min(m, n_sup) : 0;
+    const int s = lane;
+    if (!c.probe) {
+      if (s < n_sup) r_of_slot = s, kind = VRT_DET;
+    } else if (s < m_det) {
+      r_of_slot = s, kind = VRT_DET;
+    } else if (c.order == VRT_PROBE_LAST) {
+      if (s < t0) r_of_slot = s, kind = VRT_FILL;
+      else if (probe >= 0 && s == t0) kind = VRT_PROBE;
+    } else if (probe >= 0 && s == m_det) {
+      kind = VRT_PROBE;
+    } else {
+      int r = m + s - m_det - (probe >= 0 ? 1 : 0);
+      if (r >= rp) ++r;
+      if (r < n_sup) r_of_slot = r, kind = VRT_FILL;
+    }
+  }
+  if (lane < c.K) {
+    const int64_t ci = ncb + cbase + lane;
+    if (kind == VRT_PROBE) {
+      st_dev(&a.t.cand_token[ci], probe);
+      st_dev(&a.t.cand_parent[ci], node);
+      st_dev(&a.t.cand_score[ci], sp * proxy);
+      st_dev(&a.t.cand_kind[ci], kind);
+    } else if (r_of_slot >= 0) {
+      st_dev(&a.t.cand_token[ci], (int)sup_key_id(s_sup[r_of_slot]));
+      st_dev(&a.t.cand_parent[ci], node);
+      st_dev(&a.t.cand_score[ci], sp * qraw(r_of_slot));
+      st_dev(&a.t.cand_kind[ci], kind);
+    } else {
+      st_dev(&a.t.cand_kind[ci], 0);
+    }
+  }
+  if (a.fuse_rank) rank_if_last(a, b, s_rank);
+}
+
+// Coverage of the top-trunc support (the coverage column of the support-size ablation):
+// per row, the share of the untempered softmax that its trunc largest logits hold, in
+// fp64 with exponentials to about 1e-7 relative. One 8-wave block per row: the exact
+// selection of the trunc best keys (one key when trunc covers the row), then one pass
+// over the row for the total while wave 0 sums the selected keys.
+template <int DT, int PL>
+__global__ __launch_bounds__(8 * kWave) void k_coverage(const Cfg c, const void* logits, int64_t ld,
+                                                       int64_t tstride, int n_rows, double* out) {
+  constexpr int SW = 8;
+  const int j = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int lane = lane_id();
+  __shared__ ExactLds<PL> X;
+  __shared__ uint64_t s_sup[PL * kWave];
+  __shared__ double s_part[SW];
+  __shared__ int s_n, s_bad;
+  constexpr int esz = DT == VRT_BF16 ? 2 : 4;
+  constexpr int EPL = 16 / esz;
+  const char* row = (const char*)logits + ((int64_t)b * tstride + (int64_t)j * ld) * esz;
+  const bool all = c.trunc == VRT_DENSE || c.trunc >= c.V;  // the support is the whole row
+  int n_sup = 0;
+  const int bad = row_select_exact<DT, PL, SW>(row, 0, c.V, all ? 1 : c.trunc, 0u, X, s_sup, n_sup);
+  if (tid == 0) {
+    s_n = n_sup;
+    s_bad = bad;
+  }
+  __syncthreads();
+  double* o = out + (int64_t)b * n_rows + j;
+  const float M = s_n > 0 ? sup_key_val(s_sup[0]) : -INFINITY;
+  if (s_bad || !(M > -INFINITY)) {
+    if (tid == 0) *o = s_bad ? (double)NAN : 0.0;
+    return;
+  }
+  double tot = 0.0;
+  const int nv = (c.V + EPL - 1) / EPL;
+  for (int v = tid; v < nv; v += SW * kWave) {
+    const u32x4_t d = *(const u32x4_t*)(row + (int64_t)v * 16);
+    static_for<EPL>([&](auto e) {
+      float x;
+      if constexpr (DT == VRT_BF16) x = (e & 1) ? bf16_hi(d[e >> 1]) : bf16_lo(d[e >> 1]);
+      else x = __uint_as_float(d[(int)e]);
+      if (v * EPL + (int)e < c.V) tot += dense_tempered(x, M, 1.0);
+    });
+  }
+  tot = wave_sum(tot);
+  if (lane == 0) s_part[wave] = tot;
+  __syncthreads();
+  if (wave != 0) return;
+  double all_sum = 0.0;
+  for (int w = 0; w < SW; ++w) all_sum += s_part[w];
+  double top = 0.0;
+  static_for<PL>([&](auto s) {
+    const int r = lane * PL + (int)s;
+    if (r < s_n) top += dense_tempered(sup_key_val(s_sup[r]), M, 1.0);
+  });
+  top = wave_sum(top);
+  if (lane == 0) *o = all ? 1.0 : top / all_sum;
+}
+
 // Per-tree ranking of the layer's children, given their keys sorted (path score
 // desc, creation index asc; zeros last): the top W become the frontier (top-R mode),
 // or SMART's sequential keep rule runs over them. One thread.
@@ -1583,6 +1944,10 @@ int list_len(const Cfg& c) { return max(128, next_pow2(c.trunc)); }
 template <int DT>
 hipError_t launch_layer(const BArgs& a, int rows, hipStream_t stream) {
   const dim3 grid(rows, a.c.B);
+  if (a.c.trunc == VRT_DENSE) {
+    hipLaunchKernelGGL((k_dense_expand<DT>), grid, dim3(8 * kWave), 0, stream, a);
+    return hipGetLastError();
+  }
   switch (list_len(a.c) / kWave) {
     case 2: hipLaunchKernelGGL((k_select_expand<DT, 2>), grid, dim3(sel_waves<2>() * kWave), 0, stream, a); break;
     case 4: hipLaunchKernelGGL((k_select_expand<DT, 4>), grid, dim3(sel_waves<4>() * kWave), 0, stream, a); break;
@@ -1592,7 +1957,26 @@ hipError_t launch_layer(const BArgs& a, int rows, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int DT>
+hipError_t launch_coverage_t(const Cfg& c, const void* logits, int64_t ld, int64_t tstride, int n_rows,
+                             double* out, hipStream_t stream) {
+  const dim3 grid(n_rows, c.B), block(8 * kWave);
+  switch (c.trunc == VRT_DENSE ? 2 : list_len(c) / kWave) {
+    case 2: hipLaunchKernelGGL((k_coverage<DT, 2>), grid, block, 0, stream, c, logits, ld, tstride, n_rows, out); break;
+    case 4: hipLaunchKernelGGL((k_coverage<DT, 4>), grid, block, 0, stream, c, logits, ld, tstride, n_rows, out); break;
+    case 8: hipLaunchKernelGGL((k_coverage<DT, 8>), grid, block, 0, stream, c, logits, ld, tstride, n_rows, out); break;
+    default: hipLaunchKernelGGL((k_coverage<DT, 16>), grid, block, 0, stream, c, logits, ld, tstride, n_rows, out); break;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_coverage(const Cfg& c, const void* logits, int64_t ld, int64_t tstride, int n_rows,
+                           double* out, hipStream_t stream) {
+  return c.dtype == VRT_BF16 ? launch_coverage_t<VRT_BF16>(c, logits, ld, tstride, n_rows, out, stream)
+                             : launch_coverage_t<VRT_F32>(c, logits, ld, tstride, n_rows, out, stream);
+}
 
 size_t build_ws_bytes(const Cfg& c) {
   (void)c;

@@ -164,7 +164,8 @@ vrt_status vrt_check_config(const vrt_config* cp) {
   if (c.B < 1 || c.B > 65535) return fail(VRT_EINVAL, "B must be in [1, 65535] (got %d)", c.B);
   if (c.V < 1 || c.V > (1 << 20)) return fail(VRT_EINVAL, "V must be in [1, 2^20] (got %d)", c.V);
   if (c.dtype != VRT_F32 && c.dtype != VRT_BF16) return fail(VRT_EDTYPE, "dtype must be VRT_F32 or VRT_BF16");
-  if (c.trunc < 1 || c.trunc > 1024) return fail(VRT_EINVAL, "trunc must be in [1, 1024] (got %d)", c.trunc);
+  if (c.trunc != VRT_DENSE && (c.trunc < 1 || c.trunc > 1024))
+    return fail(VRT_EINVAL, "trunc must be VRT_DENSE or in [1, 1024] (got %d)", c.trunc);
   if (c.K < 1 || c.K > 30) return fail(VRT_EINVAL, "K must be in [1, 30] (got %d)", c.K);
   if (c.probe != 0 && c.probe != 1) return fail(VRT_EINVAL, "probe must be 0 or 1");
   if (c.m < 0 || (c.probe && c.m > c.K - 1))
@@ -245,6 +246,21 @@ vrt_status vrt_build_tree(const vrt_config* cp, int32_t layer, const void* draft
   return VRT_OK;
 }
 
+vrt_status vrt_support_coverage(const vrt_config* cp, const void* draft_logits, int64_t ld,
+                                int64_t tree_stride, int32_t n_rows, double* coverage, void* stream) {
+  vrt_status s = vrt_check_config(cp);
+  if (s != VRT_OK) return s;
+  const vrt_config& c = *cp;
+  if (n_rows < 1 || n_rows > 65535) return fail(VRT_EINVAL, "n_rows must be in [1, 65535] (got %d)", n_rows);
+  if (!coverage || ((uintptr_t)coverage & 7u)) return fail(VRT_EINVAL, "coverage must be a non-NULL, 8-byte aligned pointer");
+  s = check_rows(c, draft_logits, ld, tree_stride, "draft");
+  if (s != VRT_OK) return s;
+  const hipError_t e = vrt::launch_coverage(vrt::make_cfg(c), draft_logits, ld, tree_stride, n_rows, coverage,
+                                            (hipStream_t)stream);
+  if (e != hipSuccess) return fail(VRT_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return VRT_OK;
+}
+
 namespace {
 
 // Validation and launch shared by the verification entry points (parts as in
@@ -256,6 +272,9 @@ vrt_status verify_parts(int parts, const vrt_config* cp, const void* target_logi
   vrt_status s = vrt_check_config(cp);
   if (s != VRT_OK) return s;
   const vrt_config& c = *cp;
+  if (c.trunc == VRT_DENSE && c.probe)
+    return fail(VRT_EINVAL, "trees built with trunc = VRT_DENSE and the probe on carry no tail table: "
+                            "verification needs one (build with trunc in [1, 1024], or the probe off)");
   if (!tree || !ws) return fail(VRT_EINVAL, "tree and workspace pointers must not be NULL");
   if (!aligned16(tree) || !aligned16(ws)) return fail(VRT_EINVAL, "tree and workspace must be 16-byte aligned");
   if ((parts & 2) && (!out_tokens || !out_nodes || !out_len || !stats))

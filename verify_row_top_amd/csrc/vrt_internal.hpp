@@ -78,6 +78,8 @@ hipError_t launch_verify(int parts, const Cfg& c, const TreePtrs& t, const void*
 // Device scratch of the build: each row segment's sorted top-trunc keys and counts.
 size_t build_ws_bytes(const Cfg& c);
 
+hipError_t launch_coverage(const Cfg& c, const void* logits, int64_t ld, int64_t tstride, int n_rows,
+                           double* out, hipStream_t stream);
 hipError_t launch_build_layer(const Cfg& c, const TreePtrs& t, int layer, const void* logits,
                               int64_t ld, int64_t tstride, uint64_t seed, uint32_t step,
                               uint32_t* stats, void* ws, hipStream_t stream);

@@ -16,10 +16,11 @@ F32, BF16 = 0, 1
 MODE_TOPR, MODE_SMART = 0, 1
 ROOT, DET, PROBE, FILL = 0, 1, 2, 3
 FINISH = -1
+DENSE = 0  # trunc value: no truncation, the support is the whole vocabulary
 ST_DRAFT_NONFINITE, ST_DRAFT_EMPTY, ST_TARGET_BAD = 0x1, 0x2, 0x4
 EXPORTS = ("vrt_check_config", "vrt_tree_layout_of", "vrt_tree_bytes", "vrt_workspace_bytes",
            "vrt_build_tree", "vrt_verify_tree", "vrt_verify_nodes", "vrt_verify_walk", "vrt_tree_mask",
-           "vrt_accepted_kv", "vrt_read_probe", "vrt_last_error")
+           "vrt_accepted_kv", "vrt_support_coverage", "vrt_read_probe", "vrt_last_error")
 
 
 class VrtError(RuntimeError):
@@ -78,6 +79,8 @@ def lib():
         L.vrt_tree_mask.restype = i32
         L.vrt_accepted_kv.argtypes = [P(Config), vp, vp, vp, vp, vp]
         L.vrt_accepted_kv.restype = i32
+        L.vrt_support_coverage.argtypes = [P(Config), vp, i64, i64, i32, vp, vp]
+        L.vrt_support_coverage.restype = i32
         L.vrt_read_probe.argtypes = [vp, sz, vp, vp]
         L.vrt_read_probe.restype = i32
         L.vrt_last_error.argtypes = []
@@ -180,6 +183,12 @@ def accepted_kv(cfg, out_nodes, out_len, keep, keep_n, stream=None):
     """vrt_accepted_kv: keep [B, D+1], keep_n [B] (device i32 tensors)."""
     _check(lib().vrt_accepted_kv(ctypes.byref(cfg), _ptr(out_nodes), _ptr(out_len), _ptr(keep),
                                  _ptr(keep_n), _stream(stream)))
+
+
+def support_coverage(cfg, draft_logits, ld, tree_stride, n_rows, coverage, stream=None):
+    """vrt_support_coverage: coverage is a device f64 tensor [B, n_rows]."""
+    _check(lib().vrt_support_coverage(ctypes.byref(cfg), _ptr(draft_logits), ld, tree_stride, n_rows,
+                                      _ptr(coverage), _stream(stream)))
 
 
 def read_probe(buf, sink, stream=None):
