@@ -430,6 +430,32 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     n_nodes = sum(s[2] for s in [sets[k % len(sets)] for k in range(args.steps)]) / args.steps
 
+    # lazy verification (only the rows of the nodes the walk visits), timed on its own:
+    # each rep rebuilds set k's tree (untimed), then verifies it lazily between two events
+    lz_ms = []
+    lz_rows = 0
+    lazy_ok = True
+    for k in range(args.steps + 3):
+        draft, target, _ = sets[k % len(sets)]
+        for layer in range(D):
+            vrt.build_tree(cfg, layer, layer_rows(draft, layer), ld, n_draft * ld, seed, step, tree, ws,
+                           stats)
+        vrt.build_tree(cfg, vrt.FINISH, None, 0, 0, seed, step, tree, ws, stats)
+        vrt.verify_tree(cfg, target, ld, N * ld, tree, seed, step, ws, out_tokens, out_nodes, out_len,
+                        stats)
+        ref = out_tokens.clone()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        vrt.verify_lazy(cfg, target, ld, N * ld, tree, seed, step, ws, out_tokens, out_nodes, out_len,
+                        stats)
+        e1.record()
+        torch.cuda.synchronize()
+        lazy_ok &= bool(torch.equal(ref, out_tokens))
+        if k >= 3:
+            lz_ms.append(e0.elapsed_time(e1))
+            lz_rows += int(out_len.sum().item())
+    lazy_ms = sum(lz_ms) / len(lz_ms)
+
     # the step after the prune, timed on its own: attention mask + position ids of the
     # target forward over the emitted trees, and the KV entries kept after verification
     W32 = (N + 31) // 32
@@ -490,6 +516,12 @@ def main():
         "verified_tokens_per_s": float(lens.sum()) / (ms_per_step * 1e-3),
         "mean_tokens_per_tree": float(lens.mean()),
         "status_bits": int((st[:, 0] != 0).sum()),
+        "lazy_verify": {"ms": lazy_ms, "trees_per_s": B / (lazy_ms * 1e-3),
+                        "rows_read_per_tree": lz_rows / (len(lz_ms) * B),
+                        "rows_per_tree_full": float(n_nodes.float().mean()),
+                        "step_trees_per_s": (B / ((build_ms + lazy_ms) * 1e-3)) if not args.verify_only
+                        else None,
+                        "same_tokens_as_full": lazy_ok},
         "tree_mask_us": mask_us,
         "accepted_kv_us": kv_us,
     }

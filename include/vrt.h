@@ -244,6 +244,21 @@ vrt_status vrt_verify_walk(const vrt_config* cfg, const void* tree, void* ws, si
                            int32_t* out_tokens, int32_t* out_nodes, int32_t* out_len, uint32_t* stats,
                            int32_t* node_out, void* stream);
 
+/* Lazy verification: the same outputs as vrt_verify_tree (RheoSampling key design 3:
+ * the walk from the root, each visited node's probe-first test, the recursive rejection of
+ * its other kept children and the final residual or bonus sample) computed by deciding
+ * only the nodes the walk reaches, one tree per block, depth after depth. Only the target
+ * rows of the visited nodes (as many as the emitted tokens) are read, instead of every
+ * emitted node's row; the price is one dependent row pass per depth, so it pays where the
+ * batch is small or the trees are large against the accepted length. Arguments as for
+ * vrt_verify_tree. Differences: node_out (or the workspace) receives decisions for the
+ * visited nodes only, and stats[b][0] reports a bad target row (VRT_ST_TARGET_BAD) only
+ * for visited rows. Errors: as vrt_verify_tree. */
+vrt_status vrt_verify_lazy(const vrt_config* cfg, const void* target_logits, int64_t ld,
+                           int64_t tree_stride, const void* tree, uint64_t seed, uint64_t step,
+                           void* ws, size_t ws_bytes, int32_t* out_tokens, int32_t* out_nodes,
+                           int32_t* out_len, uint32_t* stats, int32_t* node_out, void* stream);
+
 /* Coverage of the truncated support (RheoSampling's support-size ablation, whose
  * coverage column is the draft probability mass inside the support): for each of the
  * n_rows rows of each tree, the share of the untempered softmax of the row held by its

@@ -81,6 +81,13 @@ class Lib:
                         self.out_tokens, self.out_nodes, self.out_len, self.stats, self.node_out)
         torch.cuda.synchronize()
 
+    def verify_lazy(self, target, ld, seed, step, zero_stats=True):
+        if zero_stats:
+            self.stats.zero_()
+        vrt.verify_lazy(self.cfg, target, ld, target.stride(0), self.tree, seed, step, self.ws,
+                        self.out_tokens, self.out_nodes, self.out_len, self.stats, self.node_out)
+        torch.cuda.synchronize()
+
     def build_layer(self, layer, rows, ld, seed, step):
         vrt.build_tree(self.cfg, layer, rows, ld, rows.stride(0), seed, step, self.tree, self.ws,
                        self.stats)
@@ -93,7 +100,7 @@ class Lib:
         return self.views[name].cpu().numpy()
 
 
-def device_step(w, seed, step, dev, verify=True):
+def device_step(w, seed, step, dev, verify=True, keep_target=False):
     """Every tree of workload w built and verified on the GPU, the way the benchmark
     runs it: the device generator plays the draft model along the GPU's own frontier,
     layer by layer, then the target model on the emitted trees (unless verify is
@@ -135,5 +142,7 @@ def device_step(w, seed, step, dev, verify=True):
     synth.rows_dev(p, zipf, node_keys.reshape(-1), tree_of.repeat_interleave(N), target.view(B * N, ld),
                    synth.TARGET, stream)
     L.verify(target, ld, seed, step, zero_stats=False)
+    if keep_target:
+        L.target, L.ld = target, ld
     del target
     return L

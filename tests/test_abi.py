@@ -132,6 +132,32 @@ def test_dense_config_builds_but_probe_trees_are_not_verified():
     assert r == vrt.EINVAL
 
 
+def test_lazy_verify_argument_errors_are_caught_before_any_launch():
+    c = vrt.make_config(B=2, V=1000, K=4, D=3, R=10)
+    L = vrt.lib()
+    good = dict(t=0x10000, ld=1024, stride=4096, tree=0x20000, ws=0x30000, wsb=1 << 30,
+                o=0x40000, n=0x50000, ln=0x60000, st=0x70000)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        v = ctypes.c_void_p
+        return L.vrt_verify_lazy(ctypes.byref(c), v(a["t"]), a["ld"], a["stride"], v(a["tree"]), 1, 0,
+                                 v(a["ws"]), a["wsb"], v(a["o"]), v(a["n"]), v(a["ln"]), v(a["st"]),
+                                 None, None)
+    assert call(t=0) == vrt.EINVAL
+    assert call(o=0) == vrt.EINVAL
+    assert call(n=0) == vrt.EINVAL
+    assert call(st=0) == vrt.EINVAL
+    assert call(wsb=8) == vrt.ENOMEM
+    assert call(ld=10) == vrt.EINVAL
+    assert call(tree=0x20008) == vrt.EINVAL
+    d = vrt.make_config(B=2, V=1000, K=4, D=3, R=10, trunc=vrt.DENSE)
+    v = ctypes.c_void_p
+    assert L.vrt_verify_lazy(ctypes.byref(d), v(0x10000), 1024, 4096, v(0x20000), 1, 0, v(0x30000),
+                             1 << 30, v(0x40000), v(0x50000), v(0x60000), v(0x70000), None,
+                             None) == vrt.EINVAL
+
+
 def test_split_verify_argument_errors_are_caught_before_any_launch():
     c = vrt.make_config(B=2, V=1000, K=4, D=3, R=10)
     L = vrt.lib()

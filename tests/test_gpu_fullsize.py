@@ -106,3 +106,32 @@ def test_dense_headline_build_matches_oracle_on_sampled_trees(gpu):
                 raise
             exempt += 1
     assert exempt <= 1
+
+
+@pytest.mark.parametrize("name,w,ss", [
+    ("headline_T1", workloads.get("headline"), (1, 0)),
+    ("headline_T06_probe_last", workloads.get("headline", T=0.6, order=1), (2, 3)),
+    ("b8", workloads.get("b8"), (3, 17)),
+    ("stress_B256", workloads.get("stress"), (1, 0)),
+], ids=lambda x: x if isinstance(x, str) else None)
+def test_lazy_walk_equals_the_full_verification(gpu, name, w, ss):
+    """vrt_verify_lazy on the full-size batch gives, tree by tree, the tokens, nodes, lengths
+    and statistics of vrt_verify_tree (which the oracle pins above), and the same decision
+    at every node it visits."""
+    import torch
+    seed, step = ss
+    print(f"lazy walk vs full verification: {name} B={w.B} V={w.V}", flush=True)
+    L = device_step(w, seed, step, gpu, keep_target=True)
+    full = {k: getattr(L, k).clone() for k in ("out_tokens", "out_nodes", "out_len", "stats", "node_out")}
+    L.node_out.fill_(-7)
+    L.verify_lazy(L.target, L.ld, seed, step)
+    for k in ("out_tokens", "out_nodes", "out_len"):
+        assert torch.equal(getattr(L, k), full[k]), k
+    assert torch.equal(L.stats[:, :5], full["stats"][:, :5])
+    no, fo = L.node_out.cpu().numpy(), full["node_out"].cpu().numpy()
+    lens, nodes = L.out_len.cpu().numpy(), L.out_nodes.cpu().numpy()
+    for b in range(w.B):
+        visit = [0] + nodes[b, :lens[b] - 1].tolist()
+        np.testing.assert_array_equal(no[b, visit], fo[b, visit])
+        rest = np.setdiff1d(np.arange(no.shape[1]), visit)
+        assert (no[b, rest] == -7).all()

@@ -39,21 +39,26 @@ CASES = [
 ]
 
 
-def run_case(w, seed, step, dev):
+def run_case(w, seed, step, dev, lazy=False):
     steps = [OracleStep(w, seed, b, step) for b in range(w.B)]
     cfg = lib_config(w)
     L = Lib(cfg, dev)
     for b, s in enumerate(steps):
         L.write_view(b, s.view)
     target, ld = to_device_rows([s.target_rows for s in steps], w, L.N, dev)
-    print(f"verify parity: {w.name} seed={seed} step={step} B={w.B} V={w.V}", flush=True)
-    L.verify(target, ld, seed, step)
+    print(f"verify parity: {w.name} seed={seed} step={step} B={w.B} V={w.V} lazy={lazy}", flush=True)
+    if lazy:
+        L.node_out.fill_(-7)
+        L.verify_lazy(target, ld, seed, step)
+    else:
+        L.verify(target, ld, seed, step)
     return steps, L
 
 
-def check(steps, L):
-    """Compare every node; a mismatch is allowed only at a node the oracle marks
-    as having a draw within 1e-6 of its threshold. Returns (exempt, mismatched, nodes)."""
+def check(steps, L, lazy=False):
+    """Compare every node (lazy: every node the walk visits, the others untouched); a
+    mismatch is allowed only at a node the oracle marks as having a draw within 1e-6 of
+    its threshold. Returns (exempt, mismatched, nodes)."""
     node_out = L.node_out.cpu().numpy()
     out_tok = L.out_tokens.cpu().numpy()
     out_len = L.out_len.cpu().numpy()
@@ -64,7 +69,15 @@ def check(steps, L):
         pn = s.per_node
         n = s.view["n_nodes"]
         assert stats[b, 0] == 0, f"status bits {stats[b, 0]:#x} on tree {b}"
-        for i in range(n):
+        visit = set(range(n))
+        if lazy:  # the nodes both walks visit (they part only after a near-threshold draw)
+            visit = ({0} | set(s.out_nodes.tolist())) & ({0} | set(out_nodes[b, :out_len[b] - 1].tolist()))
+            assert stats[b, 4] == len(s.out_tokens) or s.verify_exempt > 0
+            assert stats[b, 1] == out_len[b] - 1
+            untouched = [i for i in range(n) if i not in visit]
+            if s.verify_exempt == 0:
+                assert (node_out[b, untouched] == -7).all(), "lazy walk decided an unvisited node"
+        for i in sorted(visit):
             n_nodes += 1
             g = node_out[b, i]
             same = g[0] == pn["accept"][i] and (pn["accept"][i] >= 0 or g[1] == pn["token"][i])
@@ -84,12 +97,13 @@ def check(steps, L):
     return n_exempt, n_miss, n_nodes
 
 
+@pytest.mark.parametrize("lazy", [False, True], ids=["all_nodes", "lazy"])
 @pytest.mark.parametrize("name,w", CASES, ids=[c[0] for c in CASES])
-def test_verify_matches_oracle(gpu, name, w):
+def test_verify_matches_oracle(gpu, name, w, lazy):
     tot_ex = tot_miss = tot = 0
     for seed, step in [(1, 0), (2, 5), (3, 77)]:
-        steps, L = run_case(w, seed, step, gpu)
-        ex, miss, n = check(steps, L)
+        steps, L = run_case(w, seed, step, gpu, lazy)
+        ex, miss, n = check(steps, L, lazy)
         tot_ex += ex
         tot_miss += miss
         tot += n
@@ -140,3 +154,18 @@ def test_verify_empty_tree_is_a_bonus_sample(gpu):
         assert L.out_len[b].item() == 1
         if ex == 0:
             assert L.out_tokens[b, 0].item() == tok[0]
+
+
+def test_lazy_walk_flags_a_bad_root_row(gpu):
+    w = _small(B=2)
+    steps = [OracleStep(w, 4, b, 0, verify=False) for b in range(w.B)]
+    L = Lib(lib_config(w), gpu)
+    for b, s in enumerate(steps):
+        L.write_view(b, s.view)
+    rows = [s.target_rows.copy() for s in steps]
+    rows[0][0, 17] = 0x7FC0       # NaN in tree 0's root row
+    target, ld = to_device_rows(rows, w, L.N, gpu)
+    L.verify_lazy(target, ld, 4, 0)
+    st = L.stats.cpu().numpy()[:, 0]
+    assert st[0] & 0x4 and st[1] == 0
+    assert (L.out_len.cpu().numpy() >= 1).all()

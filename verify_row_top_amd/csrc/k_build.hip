@@ -7,16 +7,21 @@
 //   non-temporal), keep each lane's largest group maxima, find one threshold for the
 //   whole row from a histogram of their distance below the largest, re-read only the
 //   groups that reach it and rank the exact keys; rows with many ties take an exact
-//   radix selection instead. Long lists: per-segment selection and pairwise merges.
+//   radix selection instead. 512-key lists: per-segment selection and pairwise merges;
+//   1024-key lists: the exact radix selection.
 //   Wave 0 then expands the parent: untempered softmax on the top-trunc support with
 //   the fixed ranking recipe, tempered softmax in fp64, the probe draw from the
 //   tempered tail, the proxy min{q(x_m), z}, the K child slots and the parent's tail
 //   table. The last row block of each tree ranks the layer's children by (path score
 //   desc, creation index asc) and keeps the top W (top-R mode) or runs SMART's
 //   sequential keep rule (k_rank_layer does this for layers of more than 256 children).
+// k_dense_expand: the same per parent with no truncation (the dense baseline): the K best
+//   keys, one pass of exact-order sums over the whole row, the probe drawn in token order.
 // k_finish: one block per tree emits the tree: the global top R by the same key
 //   (or SMART's admitted nodes), parents before children, child lists in slot
 //   order, and the probe tails the verifier needs.
+// k_coverage: the share of each row's softmax inside its top-trunc support (a
+//   measurement of the inputs, not a step of the build).
 #include "vrt_dev.hpp"
 #include "vrt_internal.hpp"
 
@@ -73,7 +78,12 @@ constexpr int seg_elems() { return kWave * kSegLoads * (DT == VRT_BF16 ? 8 : 4);
 
 // Waves of a row block: fewer for long lists, whose stages need more LDS.
 template <int PL>
-constexpr int sel_waves() { return PL <= 4 ? 8 : (PL == 8 ? 4 : 2); }
+constexpr int sel_waves() { return PL == 8 ? 4 : 8; }
+// Lists of 1024 keys take the exact radix selection: on the workloads' rows it beats the
+// per-segment selection (whose 2-wave blocks merge sixteen 1024-key lists) by 1.6x; at
+// 512 keys the per-segment path is the faster by 2x.
+template <int PL>
+constexpr bool short_path() { return PL != 8; }
 // Working-list keys per lane while a segment is selected: twice the output list when
 // that stays small, so that the usual survivor count (a little over N) needs one sort.
 template <int PL>
@@ -1184,10 +1194,10 @@ __device__ __forceinline__ void rank_if_last(const BArgs& a, int b, uint64_t* s_
 }
 
 // One block per expanded parent, then wave 0 expands it. Short lists (trunc <= 256):
-// the row-wide path, the exact path behind it. Long lists: each wave selects the top
-// N of its segments (a wave takes segments wave, wave + SW, ...), their lists merge
-// pairwise through LDS (the row's top trunc is in the union of the segments' top
-// trunc).
+// the row-wide path, the exact path behind it; 1024-key lists: the exact path. 512-key
+// lists: each wave selects the top N of its segments (a wave takes segments wave,
+// wave + SW, ...), their lists merge pairwise through LDS (the row's top trunc is in the
+// union of the segments' top trunc).
 template <int DT, int PL>
 __global__ __launch_bounds__(sel_waves<PL>() * kWave)
 __attribute__((amdgpu_waves_per_eu(PL == 2 ? 4 : 2, 8))) void k_select_expand(const BArgs a) {
@@ -1205,14 +1215,14 @@ __attribute__((amdgpu_waves_per_eu(PL == 2 ? 4 : 2, 8))) void k_select_expand(co
   // the parent's path score, read now (wave 0 uses it at the end)
   const float sp = node < 0 ? 1.0f : a.t.cand_score[(int64_t)b * c.NC + node];
   constexpr int SW = sel_waves<PL>();
-  constexpr bool kShort = PL <= 4;
+  constexpr bool kShort = short_path<PL>();
   constexpr int LSPT = DT == VRT_BF16 ? 3 : 2;  // segments per wave the row-wide path takes
   struct SegPath {
     SegLds<DT, PL> seg[SW];
     uint64_t list[SW / 2][N];
   };
   union ShortPath {
-    FastLds<DT, PL> f;
+    FastLds<DT, (PL <= 4 ? PL : 2)> f;
     ExactLds<PL> x;
   };
   using Raw = std::conditional_t<kShort, ShortPath, SegPath>;
@@ -1229,7 +1239,8 @@ __attribute__((amdgpu_waves_per_eu(PL == 2 ? 4 : 2, 8))) void k_select_expand(co
     ShortPath& P = *(ShortPath*)s_raw;
     int path = 2;
     uint32_t floor_img = 0u;  // the TC-th largest row value's image is at least this
-    if (G <= LSPT * SW) path = row_select_fast<DT, PL, SW, LSPT>(row, 0, G, c.V, c.TC, P.f, s_sup, n_sup, floor_img);
+    if constexpr (PL <= 4)
+      if (G <= LSPT * SW) path = row_select_fast<DT, PL, SW, LSPT>(row, 0, G, c.V, c.TC, P.f, s_sup, n_sup, floor_img);
     if (path == 2) {
       __syncthreads();  // s_raw changes hands
       path = row_select_exact<DT, PL, SW>(row, 0, c.V, c.TC, floor_img, P.x, s_sup, n_sup);

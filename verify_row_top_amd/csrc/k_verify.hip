@@ -1,4 +1,5 @@
-// Tree verification (RheoSampling, key design 3) on gfx950, in two kernels.
+// Tree verification (RheoSampling, key design 3) on gfx950: two kernels, or one for the
+// lazy walk.
 //
 // k_vnode: one 512-thread block per (node row, tree).
 //   - The eight waves stream the node's target row from HBM once, in 2048-element
@@ -19,6 +20,8 @@
 //     streams hide its latency.
 // k_vwalk: one wave per tree follows the accepted children from the root and writes
 //   the emitted tokens and statistics.
+// k_vlazy: one block per tree decides the root, then the accepted child, ... each node
+//   by k_vnode's pass, so only the rows on the walk are read.
 #include "vrt_dev.hpp"
 #include "vrt_internal.hpp"
 
@@ -43,6 +46,7 @@ struct VRec {
   int tok[kChildMax];
   float x[kChildMax];
   float u[kChildMax];  // draw of each non-probe kept child's test
+  NodeOut res;         // the decision, also written here for the block (lazy walk)
 };
 
 struct VArgs {
@@ -282,7 +286,7 @@ __device__ void gather_node(const VArgs& a, int b, int i, int nn, const char* ro
 // in LDS (see the file comment).
 template <int DT>
 __device__ void decide_node(const VArgs& a, int b, int i, const char* row, const float2* cs,
-                            const VRec& R, const DLds& L) {
+                            VRec& R, const DLds& L) {
   const Cfg& c = a.c;
   const int lane = lane_id();
   const int V = c.V;
@@ -323,7 +327,7 @@ __device__ void decide_node(const VArgs& a, int b, int i, const char* row, const
   NodeOut out{-1, -1, 0, 0.0f};
   if (!(S > 0.0) || !(S < INFINITY) || !(MC < INFINITY)) {
     out.flags = (int)(VRT_ST_TARGET_BAD << 16);
-    if (lane == 0) a.node_out[nb + i] = out;
+    if (lane == 0) a.node_out[nb + i] = out, R.res = out;
     return;
   }
   const double invS = 1.0 / S;
@@ -578,32 +582,24 @@ __device__ void decide_node(const VArgs& a, int b, int i, const char* row, const
   out.accept = accept;
   out.flags = min(tests, 255) | (min(near, 255) << 8);
   if (accept < 0) out.W = (float)W;
-  if (lane == 0) a.node_out[nb + i] = out;
+  if (lane == 0) a.node_out[nb + i] = out, R.res = out;
 }
 
 constexpr int kMaxChunks = (1 << 20) / kCH;  // V <= 2^20
 
-// One block per (node, tree): stream the row (all waves), gather the decision inputs
-// (last wave, overlapping the others' stream), then decide (wave 0).
-template <int DT>
-__global__ __launch_bounds__(kVB) void k_vnode(const VArgs a) {
+// One node's pass by a block of NT threads: stream the row (all waves), gather the
+// decision inputs (last wave, overlapping the others' stream), then decide (wave 0).
+template <int DT, int NT>
+__device__ __forceinline__ void node_pass(const VArgs& a, int b, int i, int nn, float2* s_cs, VRec& s_rec,
+                                          const DLds& L, int& s_next) {
   const Cfg& c = a.c;
-  const int b = blockIdx.y;
-  const int i = blockIdx.x;
-  const int nn = clamp_nodes(a.t.n_nodes[b], c.N);
-  if (i >= nn) return;
   const int V = c.V;
   constexpr int esz = DT == VRT_BF16 ? 2 : 4;
   const char* row = (const char*)a.logits + ((int64_t)b * a.tstride + (int64_t)i * a.ld) * esz;
   const int nch = (V + kCH - 1) / kCH;
   const int nfull = V / kCH;
   const int wave = threadIdx.x >> 6;
-  __shared__ float2 s_cs[kMaxChunks];
-  __shared__ VRec s_rec;
-  extern __shared__ double s_dyn[];
-  const DLds L = carve((char*)s_dyn, nch, c.TC);
-  constexpr int NW = kVB / kWave;
-  __shared__ int s_next;  // next pair of chunks to hand out
+  constexpr int NW = NT / kWave;
   if (threadIdx.x == 0) s_next = NW;
   __syncthreads();
   if (wave == NW - 1) gather_node<DT>(a, b, i, nn, row, s_rec, L);
@@ -628,6 +624,84 @@ __global__ __launch_bounds__(kVB) void k_vnode(const VArgs a) {
   }
   __syncthreads();
   if (wave == 0) decide_node<DT>(a, b, i, row, s_cs, s_rec, L);
+}
+
+// One block per (node, tree): that node's pass.
+template <int DT>
+__global__ __launch_bounds__(kVB) void k_vnode(const VArgs a) {
+  const Cfg& c = a.c;
+  const int b = blockIdx.y;
+  const int i = blockIdx.x;
+  const int nn = clamp_nodes(a.t.n_nodes[b], c.N);
+  if (i >= nn) return;
+  __shared__ float2 s_cs[kMaxChunks];
+  __shared__ VRec s_rec;
+  __shared__ int s_next;
+  extern __shared__ double s_dyn[];
+  const DLds L = carve((char*)s_dyn, (c.V + kCH - 1) / kCH, c.TC);
+  node_pass<DT, kVB>(a, b, i, nn, s_cs, s_rec, L, s_next);
+}
+
+// Emitted tokens, nodes and statistics of tree b once its walk has ended (len tokens).
+__device__ __forceinline__ void walk_outputs(const VArgs& a, int b, int len, uint32_t st, int probe, int near,
+                                             int visited) {
+  const Cfg& c = a.c;
+  for (int k = len; k <= c.D; ++k) a.out_tokens[(int64_t)b * (c.D + 1) + k] = -1;
+  for (int k = len - 1; k < c.D; ++k) a.out_nodes[(int64_t)b * c.D + k] = -1;
+  a.out_len[b] = len;
+  if (a.stats) {
+    uint32_t* s = a.stats + (int64_t)b * 8;
+    s[0] |= st;
+    s[1] = (uint32_t)(len - 1);
+    s[2] = (uint32_t)probe;
+    s[3] = (uint32_t)near;
+    s[4] = (uint32_t)visited;
+    s[5] = s[6] = s[7] = 0;
+  }
+}
+
+// Lazy verification: one block per tree walks from the root and decides only the nodes
+// the walk reaches, each exactly as k_vnode decides it (its row streamed once), so the
+// rows of the other nodes are never read. Bytes per tree: (emitted tokens) rows instead
+// of n_nodes rows; the cost is one dependent pass per depth.
+constexpr int kVL = 1024;  // threads of a lazy-walk block
+
+template <int DT>
+__global__ __launch_bounds__(kVL) void k_vlazy(const VArgs a) {
+  const Cfg& c = a.c;
+  const int b = blockIdx.x;
+  const int nn = clamp_nodes(a.t.n_nodes[b], c.N);
+  const int64_t nb = (int64_t)b * c.N;
+  __shared__ float2 s_cs[kMaxChunks];
+  __shared__ VRec s_rec;
+  __shared__ int s_next;
+  extern __shared__ double s_dyn[];
+  const DLds L = carve((char*)s_dyn, (c.V + kCH - 1) / kCH, c.TC);
+  const bool t0 = threadIdx.x == 0;
+  int cur = 0, len = 0, near = 0, probe = 0, visited = 0;
+  uint32_t st = 0;
+  for (int step = 0; step <= c.D; ++step) {
+    node_pass<DT, kVL>(a, b, cur, nn, s_cs, s_rec, L, s_next);
+    __syncthreads();  // the decision is in s_rec.res
+    const NodeOut o = s_rec.res;
+    ++visited;
+    near += (o.flags >> 8) & 0xFF;
+    st |= (uint32_t)o.flags >> 16;
+    if (o.accept > cur && o.accept < nn && len < c.D) {
+      if (t0) {
+        a.out_nodes[(int64_t)b * c.D + len] = o.accept;
+        a.out_tokens[(int64_t)b * (c.D + 1) + len] = a.t.node_token[nb + o.accept];
+      }
+      if (a.t.node_kind[nb + o.accept] == VRT_PROBE) probe = 1;
+      ++len;
+      cur = o.accept;
+    } else {
+      if (t0) a.out_tokens[(int64_t)b * (c.D + 1) + len] = o.token;
+      ++len;
+      break;
+    }
+  }
+  if (t0) walk_outputs(a, b, len, st, probe, near, visited);
 }
 
 // One wave per tree: the walk over the decided nodes. The tree's decisions, tokens
@@ -670,18 +744,7 @@ __global__ __launch_bounds__(kWave) void k_vwalk(const VArgs a) {
       break;
     }
   }
-  for (int k = len; k <= c.D; ++k) a.out_tokens[(int64_t)b * (c.D + 1) + k] = -1;
-  for (int k = len - 1; k < c.D; ++k) a.out_nodes[(int64_t)b * c.D + k] = -1;
-  a.out_len[b] = len;
-  if (a.stats) {
-    uint32_t* s = a.stats + (int64_t)b * 8;
-    s[0] |= st;
-    s[1] = (uint32_t)(len - 1);
-    s[2] = (uint32_t)probe;
-    s[3] = (uint32_t)near;
-    s[4] = (uint32_t)visited;
-    s[5] = s[6] = s[7] = 0;
-  }
+  walk_outputs(a, b, len, st, probe, near, visited);
 }
 
 }  // namespace
@@ -709,6 +772,13 @@ hipError_t launch_verify(int parts, const Cfg& c, const TreePtrs& t, const void*
   }
   if (parts & 2)
     hipLaunchKernelGGL(k_vwalk, dim3(c.B), dim3(kWave), (size_t)c.N * (16 + 4 + 4), stream, a);
+  if (parts & 4) {
+    const size_t lds = decide_lds_bytes(c);
+    if (c.dtype == VRT_BF16)
+      hipLaunchKernelGGL(k_vlazy<VRT_BF16>, dim3(c.B), dim3(kVL), lds, stream, a);
+    else
+      hipLaunchKernelGGL(k_vlazy<VRT_F32>, dim3(c.B), dim3(kVL), lds, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -277,13 +277,13 @@ vrt_status verify_parts(int parts, const vrt_config* cp, const void* target_logi
                             "verification needs one (build with trunc in [1, 1024], or the probe off)");
   if (!tree || !ws) return fail(VRT_EINVAL, "tree and workspace pointers must not be NULL");
   if (!aligned16(tree) || !aligned16(ws)) return fail(VRT_EINVAL, "tree and workspace must be 16-byte aligned");
-  if ((parts & 2) && (!out_tokens || !out_nodes || !out_len || !stats))
+  if ((parts & 6) && (!out_tokens || !out_nodes || !out_len || !stats))
     return fail(VRT_EINVAL, "output pointers must not be NULL");
   if (node_out && ((uintptr_t)node_out & 15u)) return fail(VRT_EINVAL, "node_out must be 16-byte aligned");
   const WsLayout wl = ws_layout(c);
   if (ws_bytes < (size_t)wl.total)
     return fail(VRT_ENOMEM, "workspace too small: %zu < %lld bytes", ws_bytes, (long long)wl.total);
-  if (parts & 1) {
+  if (parts & 5) {
     s = check_rows(c, target_logits, ld, tree_stride, "target");
     if (s != VRT_OK) return s;
   }
@@ -304,6 +304,14 @@ vrt_status vrt_verify_tree(const vrt_config* cp, const void* target_logits, int6
                            void* ws, size_t ws_bytes, int32_t* out_tokens, int32_t* out_nodes,
                            int32_t* out_len, uint32_t* stats, int32_t* node_out, void* stream) {
   return verify_parts(3, cp, target_logits, ld, tree_stride, tree, seed, step, ws, ws_bytes, out_tokens,
+                      out_nodes, out_len, stats, node_out, stream);
+}
+
+vrt_status vrt_verify_lazy(const vrt_config* cp, const void* target_logits, int64_t ld, int64_t tree_stride,
+                           const void* tree, uint64_t seed, uint64_t step, void* ws, size_t ws_bytes,
+                           int32_t* out_tokens, int32_t* out_nodes, int32_t* out_len, uint32_t* stats,
+                           int32_t* node_out, void* stream) {
+  return verify_parts(4, cp, target_logits, ld, tree_stride, tree, seed, step, ws, ws_bytes, out_tokens,
                       out_nodes, out_len, stats, node_out, stream);
 }
 

@@ -69,7 +69,8 @@ hipError_t launch_tree_mask(const Cfg& c, const TreePtrs& t, uint32_t* mask, int
 hipError_t launch_accepted_kv(const Cfg& c, const int32_t* out_nodes, const int32_t* out_len,
                               int32_t* keep, int32_t* keep_n, hipStream_t stream);
 
-// parts: 1 = decide every node (k_vnode), 2 = walk (k_vwalk), 3 = both
+// parts: 1 = decide every node (k_vnode), 2 = walk (k_vwalk), 3 = both, 4 = the lazy walk
+// (k_vlazy: decide only the nodes the walk reaches)
 hipError_t launch_verify(int parts, const Cfg& c, const TreePtrs& t, const void* logits, int64_t ld,
                          int64_t tstride, uint64_t seed, uint32_t step, NodeOut* node_out,
                          int32_t* out_tokens, int32_t* out_nodes, int32_t* out_len, uint32_t* stats,
