@@ -7,8 +7,8 @@
 //   non-temporal), keep each lane's largest group maxima, find one threshold for the
 //   whole row from a histogram of their distance below the largest, re-read only the
 //   groups that reach it and rank the exact keys; rows with many ties take an exact
-//   radix selection instead. 512-key lists: per-segment selection and pairwise merges;
-//   1024-key lists: the exact radix selection.
+//   radix selection instead. Lists of 512 and 1024 keys sort the staged keys by wave
+//   slices in registers and pairwise merges.
 //   Wave 0 then expands the parent: untempered softmax on the top-trunc support with
 //   the fixed ranking recipe, tempered softmax in fp64, the probe draw from the
 //   tempered tail, the proxy min{q(x_m), z}, the K child slots and the parent's tail
@@ -76,42 +76,7 @@ constexpr int kSegLoads = 16;  // 16-byte loads per lane per segment, all in fli
 template <int DT>
 constexpr int seg_elems() { return kWave * kSegLoads * (DT == VRT_BF16 ? 8 : 4); }
 
-// Waves of a row block: fewer for long lists, whose stages need more LDS.
-template <int PL>
-constexpr int sel_waves() { return PL == 8 ? 4 : 8; }
-// Lists of 1024 keys take the exact radix selection: on the workloads' rows it beats the
-// per-segment selection (whose 2-wave blocks merge sixteen 1024-key lists) by 1.6x; at
-// 512 keys the per-segment path is the faster by 2x.
-template <int PL>
-constexpr bool short_path() { return PL != 8; }
-// Working-list keys per lane while a segment is selected: twice the output list when
-// that stays small, so that the usual survivor count (a little over N) needs one sort.
-template <int PL>
-constexpr int work_pl() { return PL <= 4 ? 2 * PL : PL; }
-
-// Segment keys. bf16 rows: 32 bits, the order-preserving image of the 16-bit value
-// above 0xFFFF - (index within the segment); fp32 rows: the 64-bit row key (value,
-// token id). Larger is better; zero is empty.
-template <int DT>
-using SegKey = std::conditional_t<DT == VRT_BF16, uint32_t, uint64_t>;
-
-template <int DT, int PL>
-constexpr int kstage_cap() {
-  // staged keys: below one working list plus one round; also holds the output as row keys
-  const int stage = work_pl<PL>() * kWave + kWave * (DT == VRT_BF16 ? 8 : 4);
-  const int out = PL * kWave * 8 / (DT == VRT_BF16 ? 4 : 8);
-  return stage > out ? stage : out;
-}
-constexpr int kRing = 5 * kWave;  // group ring: fewer than 64 left over + 4 loads' groups
-
-// Order-preserving 16-bit images of the two bf16 halves of a word.
-typedef short s16x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t ord16x2(uint32_t w) {
-  const s16x2 v = __builtin_bit_cast(s16x2, w);
-  const s16x2 sg = v >> (s16x2){15, 15};
-  const uint32_t m = (__builtin_bit_cast(uint32_t, sg) & 0x7FFF7FFFu) | 0x80008000u;
-  return w ^ m;
-}
+constexpr int kSelWaves = 8;  // waves of a row block
 
 __device__ __forceinline__ float max3n(float a, float b, float c) {  // NaN-propagating
   return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
@@ -189,220 +154,16 @@ __device__ __forceinline__ float value_of(uint32_t img) {
   }
 }
 
-// Per-wave LDS of the segment selection.
-template <int DT, int PL>
-struct SegLds {
-  SegKey<DT> keys[kstage_cap<DT, PL>()];
-  u32x4_t grp[kRing];    // staged groups (one lane's 16-byte load)
-  uint16_t gidx[kRing];  // their load index * 64 + lane
-};
-
-// Top N = 64*PL keys (logit desc, token id asc) of segment g of a draft row, by one
-// wave, into cur[] (row keys, position p = lane*PL + s, sorted descending, zero =
-// empty).
-//  1. All 16 loads of the lane are issued at once: the segment lives in 64 registers.
-//     A group is one lane's load (8 bf16 or 4 fp32 elements).
-//  2. Each lane keeps the LV largest of its 16 group maxima; the N-th largest of
-//     these 64*LV values, v0 (bitwise search over ballot counts), is reached by at
-//     least N distinct elements, so no element below v0 is among the segment's N
-//     best. The group maxima propagate NaN, which flags non-finite rows cheaply.
-//  3. Groups whose maximum reaches the threshold are copied to an LDS ring, four
-//     loads at a time; lane i then takes the i-th staged group and stages the exact
-//     keys of its elements above the threshold.
-//  4. Staged keys are sorted (bitonic network over lane exchanges) into a working
-//     list; should more survive than it holds (ties, flat rows), full stages are
-//     merged into it and its N-th key becomes an exact threshold.
-// No block barriers; the code of steps 3-4 is emitted once (the loop resumes).
-template <int DT, int PL>
-__device__ __forceinline__ void seg_select(const char* row, int g, int V, SegLds<DT, PL>& L,
-                                           uint64_t (&cur)[PL], bool& bad) {
-  using K = SegKey<DT>;
-  constexpr bool BF = DT == VRT_BF16;
-  constexpr int N = PL * kWave;
-  constexpr int QL = work_pl<PL>();
-  constexpr int QN = QL * kWave;
-  constexpr int LV = QL;
-  constexpr int esz = BF ? 2 : 4;
-  constexpr int EPL = 16 / esz;  // elements per group
-  constexpr int KCAP = kstage_cap<DT, PL>();
-  const int lane = lane_id();
-  const int seg0 = g * seg_elems<DT>();
-  const int vlim = V - seg0;  // elements of this segment inside the row
-  const uint64_t lt_mask = (1ull << lane) - 1ull;
-
-  // 1. loads (the segment lives in registers); 2. group maxima
-  u32x4_t d[kSegLoads];
-  load_segment<DT>(row, g, V, d);
-  float gm[kSegLoads];
-  group_maxima<DT>(d, gm);
-  bool nf = false;
-  static_for<kSegLoads>([&](auto q) { nf |= __builtin_amdgcn_classf(gm[q], 0x203); });  // NaN, +inf
-  bad |= ballot(nf) != 0ull;
-  float lv[LV];
-  static_for<LV>([&](auto s) { lv[s] = -INFINITY; });
-  static_for<kSegLoads>([&](auto q) {
-    float x = gm[q];
-    static_for<LV>([&](auto s) {
-      const float h = fmaxf(lv[s], x);
-      x = fminf(lv[s], x);
-      lv[s] = h;
-    });
-  });
-  constexpr int RB = BF ? 16 : 32;  // significant bits of the order-preserving image
-  uint32_t o[LV];
-  static_for<LV>([&](auto s) { o[s] = ord32(lv[s]) >> (32 - RB); });
-  uint32_t pre = 0u;  // largest t with at least N candidates at or above t
-  static_for<RB>([&](auto i) {
-    const uint32_t t = pre | (1u << (RB - 1 - i));
-    int cnt = 0;
-    static_for<LV>([&](auto s) { cnt += __builtin_popcountll(ballot(o[s] >= t)); });
-    if (cnt >= N) pre = t;
-  });
-  K thr;  // a key is kept iff key > thr
-  if constexpr (BF) thr = pre ? (pre << 16) - 1u : 0u;
-  else thr = pre ? ((uint64_t)pre << 32) - 1ull : 0ull;
-  // the value of the threshold (a pre-test on values; exact for bf16 images too)
-  float thr_f = pre ? value_of<DT>(pre) : -INFINITY;
-
-  K work[QL];
-  static_for<QL>([&](auto s) { work[s] = 0; });
-  bool have = false;
-  int nst = 0, ngrp = 0, head = 0, qb_next = 0;
-  wave_sync();
-  for (;;) {
-    // 3a. candidate groups of the next four loads go to the ring
-    if (ngrp < kWave && qb_next < kSegLoads / 4) {
-      static_for<kSegLoads / 4>([&](auto qb) {
-        if (qb == qb_next) {
-          static_for<4>([&](auto i) {
-            constexpr int q = 4 * qb + i;
-            const bool cg = gm[q] >= thr_f;
-            const uint64_t m = ballot(cg);
-            int pos = head + ngrp + (int)__builtin_popcountll(m & lt_mask);
-            pos = pos >= kRing ? pos - kRing : pos;
-            if (cg) {
-              L.grp[pos] = d[q];
-              L.gidx[pos] = (uint16_t)(q * kWave + lane);
-            }
-            ngrp += __builtin_popcountll(m);
-          });
-        }
-      });
-      ++qb_next;
-    }
-    const bool loads_done = qb_next >= kSegLoads / 4;
-    // 3b. one round: lane i takes the i-th staged group and stages its keys
-    if (ngrp >= kWave || (loads_done && ngrp > 0)) {
-      const int take = min(ngrp, kWave);
-      wave_sync();
-      const bool has = lane < take;
-      int slot = head + lane;
-      slot = slot >= kRing ? slot - kRing : slot;
-      u32x4_t gw = {0u, 0u, 0u, 0u};
-      int li0 = 0;
-      if (has) {
-        gw = L.grp[slot];
-        li0 = L.gidx[slot] * EPL;
-      }
-      K* dump = L.keys + KCAP - 1;  // never holds a staged key
-      auto stage = [&](bool pass, K key) {
-        const uint64_t mask = ballot(pass);
-        const int pos = nst + (int)__builtin_popcountll(mask & lt_mask);
-        *(pass ? L.keys + pos : dump) = key;
-        nst += __builtin_popcountll(mask);
-      };
-      if constexpr (BF) {
-        const uint32_t c0 = 0xFFFFu - (uint32_t)li0;
-        static_for<4>([&](auto wi) {
-          const uint32_t od = ord16x2(gw[(int)wi]);
-          static_for<2>([&](auto hf) {
-            constexpr int e = 2 * wi + hf;
-            const uint32_t key = hf ? ((od & 0xFFFF0000u) | (c0 - e)) : ((od << 16) | (c0 - e));
-            stage(has && key > thr && li0 + e < vlim, key);
-          });
-        });
-      } else {
-        static_for<4>([&](auto e) {
-          const int id = seg0 + li0 + e;
-          const uint64_t key = sup_key(__uint_as_float(gw[(int)e]), (uint32_t)id);
-          stage(has && key > thr && li0 + e < vlim, key);
-        });
-      }
-      head += take;
-      head = head >= kRing ? head - kRing : head;
-      ngrp -= take;
-    }
-    const bool done = loads_done && ngrp == 0;
-    // 4. sort staged keys into the working list: full stages, everything at the end
-    int off = 0;
-    while (nst - off >= QN || (done && nst > off)) {
-      const int cnt = min(QN, nst - off);
-      wave_sync();
-      K add[QL];
-      static_for<QL>([&](auto s) {
-        const int p = lane * QL + s;
-        add[s] = p < cnt ? L.keys[off + p] : (K)0;
-      });
-      wave_sort_desc<QL>(add);
-      if (have) {
-        wave_merge_top<QL>(work, add);
-      } else {
-        static_for<QL>([&](auto s) { work[s] = add[s]; });
-        have = true;
-      }
-      off += cnt;
-      const K t = shflk(work[(N - 1) % QL], (N - 1) / QL);
-      if (t) {
-        thr = t;
-        if constexpr (BF) thr_f = value_of<DT>(t >> 16);
-        else thr_f = sup_key_val(t);
-      }
-    }
-    if (done) break;
-    if (off > 0) {  // the rest (fewer than QN keys) moves to the front
-      const int rem = nst - off;
-      wave_sync();
-      for (int i = lane; i < rem; i += kWave) L.keys[i] = L.keys[off + i];
-      nst = rem;
-    }
-  }
-  // the first N positions, as row keys, in the output layout
-  auto row_key = [&](K k) -> uint64_t {
-    if constexpr (BF) {
-      if (!k) return 0ull;
-      return sup_key(value_of<DT>(k >> 16), (uint32_t)(seg0 + (int)(0xFFFFu - (k & 0xFFFFu))));
-    } else {
-      return k;
-    }
-  };
-  if constexpr (QL == PL && !BF) {
-    static_for<PL>([&](auto s) { cur[s] = work[s]; });
-  } else {
-    static_assert(sizeof(L.keys) >= N * sizeof(uint64_t), "stage too small for the output");
-    uint64_t* ost = (uint64_t*)L.keys;
-    wave_sync();
-    static_for<QL>([&](auto s) {
-      const int p = lane * QL + s;
-      if (p < N) ost[p] = row_key(work[s]);
-    });
-    wave_sync();
-    static_for<PL>([&](auto s) { cur[s] = ost[lane * PL + s]; });
-    wave_sync();
-  }
-}
-
 // ---------------------------------------------------------------------------
-// Row-wide selection (the usual path for short lists): one threshold for the whole
-// row instead of one list per segment.
-
-// The usual threshold search: one histogram of the candidates' distance below the
-// largest one, in 1/kDistScale steps of value, kDistBins bins.
+// Row-wide selection: one threshold for the whole row. The usual threshold search is
+// one histogram of the candidates' distance below the largest one, in 1/kDistScale
+// steps of value, kDistBins bins.
 constexpr int kDistBins = 1024;
 constexpr float kDistScale = 64.0f;
 
 template <int DT, int PL>
 struct FastLds {
-  static constexpr int LV = PL <= 2 ? 4 : 2 * PL;      // candidates per lane and segment
+  static constexpr int LV = 4;                         // candidates per lane and segment
   static constexpr int KCAP = 4 * PL * kWave;          // staged keys held (4N)
   // a candidate: group maximum's image << 8 | its load index q
   using CK = std::conditional_t<DT == VRT_BF16, uint32_t, uint64_t>;
@@ -749,7 +510,38 @@ __device__ __forceinline__ int row_select_fast(const char* row, int g0, int g1, 
   if (nk > FL::KCAP) floor_img = pre;  // at least TC row elements reach t
   if (nk > FL::KCAP || nk < TC) return 2;
 
-  // D.
+  // D. Lists of 512 keys or more: the waves sort slices of N staged keys in registers
+  // and merge them pairwise through LDS, keeping the top N (ranking every key against
+  // every other would cost nk^2 LDS reads).
+  if constexpr (PL >= 8) {
+    uint64_t k[PL];
+    const int base = wave * N;
+    static_for<PL>([&](auto s) {
+      const int p = base + lane * PL + (int)s;
+      k[s] = p < nk ? F.keys[p] : 0ull;
+    });
+    if (base < nk) wave_sort_desc<PL>(k);  // uniform
+    __syncthreads();  // every slice is in registers: the staging area holds the lists now
+    for (int st = 1; st < SW; st <<= 1) {
+      uint64_t* list = F.keys + (wave / (2 * st)) * N;
+      if ((wave & (2 * st - 1)) == st) static_for<PL>([&](auto s) { list[lane * PL + s] = k[s]; });
+      __syncthreads();
+      if ((wave & (2 * st - 1)) == 0 && (wave + st) * N < nk) {
+        uint64_t o[PL];
+        static_for<PL>([&](auto s) { o[s] = list[lane * PL + s]; });
+        wave_merge_top<PL>(k, o);
+      }
+      __syncthreads();
+    }
+    if (wave == 0)
+      static_for<PL>([&](auto s) {
+        const int p = lane * PL + (int)s;
+        s_sup[p] = p < TC ? k[s] : 0ull;
+      });
+    n_sup = TC;
+    __syncthreads();
+    return 0;
+  }
   for (int i = tid; i < nk; i += NT) {
     const uint64_t my = F.keys[i];
     int r = 0;
@@ -1193,18 +985,14 @@ __device__ __forceinline__ void rank_if_last(const BArgs& a, int b, uint64_t* s_
   if (lane == 0) a.t.layer_sync[b] = 0;
 }
 
-// One block per expanded parent, then wave 0 expands it. Short lists (trunc <= 256):
-// the row-wide path, the exact path behind it; 1024-key lists: the exact path. 512-key
-// lists: each wave selects the top N of its segments (a wave takes segments wave,
-// wave + SW, ...), their lists merge pairwise through LDS (the row's top trunc is in the
-// union of the segments' top trunc).
+// One block per expanded parent, then wave 0 expands it: the row-wide path, the exact
+// path behind it (ties, flat rows, rows longer than the row-wide path covers).
 template <int DT, int PL>
-__global__ __launch_bounds__(sel_waves<PL>() * kWave)
+__global__ __launch_bounds__(kSelWaves * kWave)
 __attribute__((amdgpu_waves_per_eu(PL == 2 ? 4 : 2, 8))) void k_select_expand(const BArgs a) {
   const Cfg& c = a.c;
   const int j = blockIdx.x, b = blockIdx.y;
   const int wave = threadIdx.x >> 6;
-  const int lane = lane_id();
   constexpr int N = PL * kWave;
   __shared__ uint64_t s_rank[kRankFused];
   const int node = begin_row(a, b, j);
@@ -1214,74 +1002,29 @@ __attribute__((amdgpu_waves_per_eu(PL == 2 ? 4 : 2, 8))) void k_select_expand(co
   }
   // the parent's path score, read now (wave 0 uses it at the end)
   const float sp = node < 0 ? 1.0f : a.t.cand_score[(int64_t)b * c.NC + node];
-  constexpr int SW = sel_waves<PL>();
-  constexpr bool kShort = short_path<PL>();
+  constexpr int SW = kSelWaves;
   constexpr int LSPT = DT == VRT_BF16 ? 3 : 2;  // segments per wave the row-wide path takes
-  struct SegPath {
-    SegLds<DT, PL> seg[SW];
-    uint64_t list[SW / 2][N];
-  };
-  union ShortPath {
-    FastLds<DT, (PL <= 4 ? PL : 2)> f;
+  union Sel {
+    FastLds<DT, PL> f;
     ExactLds<PL> x;
   };
-  using Raw = std::conditional_t<kShort, ShortPath, SegPath>;
-  __shared__ __align__(16) char s_raw[sizeof(Raw)];
+  __shared__ __align__(16) char s_raw[sizeof(Sel)];
   __shared__ uint64_t s_sup[N];  // the support: top trunc keys, zero-padded
   __shared__ float s_q[N];
-  __shared__ int s_bad[SW];
   constexpr int esz = DT == VRT_BF16 ? 2 : 4;
   const char* row = (const char*)a.logits + ((int64_t)b * a.tstride + (int64_t)j * a.ld) * esz;
   const int G = (c.V + seg_elems<DT>() - 1) / seg_elems<DT>();
   int n_sup = 0;
-  int any_bad = 0;
-  if constexpr (kShort) {
-    ShortPath& P = *(ShortPath*)s_raw;
-    int path = 2;
-    uint32_t floor_img = 0u;  // the TC-th largest row value's image is at least this
-    if constexpr (PL <= 4)
-      if (G <= LSPT * SW) path = row_select_fast<DT, PL, SW, LSPT>(row, 0, G, c.V, c.TC, P.f, s_sup, n_sup, floor_img);
-    if (path == 2) {
-      __syncthreads();  // s_raw changes hands
-      path = row_select_exact<DT, PL, SW>(row, 0, c.V, c.TC, floor_img, P.x, s_sup, n_sup);
-    }
-    any_bad = path == 1;
-    if (wave != 0) return;
-  } else {
-    SegPath& P = *(SegPath*)s_raw;
-    uint64_t acc[PL];
-    static_for<PL>([&](auto s) { acc[s] = 0ull; });
-    bool bad = false;
-    for (int g = wave; g < G; g += SW) {
-      uint64_t cur[PL];
-      seg_select<DT, PL>(row, g, c.V, P.seg[wave], cur, bad);
-      if (g == wave) static_for<PL>([&](auto s) { acc[s] = cur[s]; });
-      else wave_merge_top<PL>(acc, cur);
-    }
-    if (lane == 0) s_bad[wave] = bad ? 1 : 0;
-    // pairwise merges: at distance st, wave w + st hands its list to wave w
-    for (int st = 1; st < SW; st <<= 1) {
-      if ((wave & (2 * st - 1)) == st)
-        static_for<PL>([&](auto s) { P.list[wave / (2 * st)][lane * PL + s] = acc[s]; });
-      __syncthreads();
-      if ((wave & (2 * st - 1)) == 0) {
-        uint64_t oth[PL];
-        static_for<PL>([&](auto s) { oth[s] = P.list[wave / (2 * st)][lane * PL + s]; });
-        wave_merge_top<PL>(acc, oth);
-      }
-      __syncthreads();
-    }
-    if (wave != 0) return;
-    int cnt = 0;
-    static_for<PL>([&](auto s) {
-      const int q = lane * PL + s;
-      const uint64_t k = q < c.TC ? acc[s] : 0ull;
-      s_sup[q] = k;
-      cnt += k != 0ull;
-    });
-    n_sup = wave_sum_i(cnt);
-    for (int w = 0; w < SW; ++w) any_bad |= s_bad[w];
+  Sel& P = *(Sel*)s_raw;
+  int path = 2;
+  uint32_t floor_img = 0u;  // the TC-th largest row value's image is at least this
+  if (G <= LSPT * SW) path = row_select_fast<DT, PL, SW, LSPT>(row, 0, G, c.V, c.TC, P.f, s_sup, n_sup, floor_img);
+  if (path == 2) {
+    __syncthreads();  // s_raw changes hands
+    path = row_select_exact<DT, PL, SW>(row, 0, c.V, c.TC, floor_img, P.x, s_sup, n_sup);
   }
+  const int any_bad = path == 1;
+  if (wave != 0) return;
   wave_sync();
   end_row<PL>(a, b, j, node, sp, n_sup, any_bad != 0, s_sup, s_q);
   if (a.fuse_rank) rank_if_last(a, b, s_rank);
@@ -1960,10 +1703,10 @@ hipError_t launch_layer(const BArgs& a, int rows, hipStream_t stream) {
     return hipGetLastError();
   }
   switch (list_len(a.c) / kWave) {
-    case 2: hipLaunchKernelGGL((k_select_expand<DT, 2>), grid, dim3(sel_waves<2>() * kWave), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((k_select_expand<DT, 4>), grid, dim3(sel_waves<4>() * kWave), 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((k_select_expand<DT, 8>), grid, dim3(sel_waves<8>() * kWave), 0, stream, a); break;
-    default: hipLaunchKernelGGL((k_select_expand<DT, 16>), grid, dim3(sel_waves<16>() * kWave), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((k_select_expand<DT, 2>), grid, dim3(kSelWaves * kWave), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((k_select_expand<DT, 4>), grid, dim3(kSelWaves * kWave), 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((k_select_expand<DT, 8>), grid, dim3(kSelWaves * kWave), 0, stream, a); break;
+    default: hipLaunchKernelGGL((k_select_expand<DT, 16>), grid, dim3(kSelWaves * kWave), 0, stream, a); break;
   }
   return hipGetLastError();
 }
