@@ -193,8 +193,9 @@ def sweep(args):
     """Support-size sweep (RheoSampling's support-size ablation) on the workload: for each
     support size and the dense baseline (support = the whole vocabulary), the draft-side
     time of one step (every build layer and the finish, HIP events on the launch stream),
-    the mean coverage of the expanded rows' supports, and the mean tokens per verified
-    tree. Dense trees with the probe on carry no tail table and are not verified."""
+    the verification time, the mean coverage of the expanded rows' supports, and the mean
+    tokens per verified tree. Dense trees are verified by vrt_verify_dense, which
+    regenerates the probe tails from the draft rows."""
     import torch
 
     import synth
@@ -223,11 +224,20 @@ def sweep(args):
         out_nodes = torch.zeros((B, D), dtype=torch.int32, device=dev)
         out_len = torch.zeros(B, dtype=torch.int32, device=dev)
         cov = torch.zeros((B, n_draft), dtype=torch.float64, device=dev)
-        verify = trunc != vrt.DENSE or not w.probe
-        times, covs, lens = [], [], []
+        dense = trunc == vrt.DENSE and w.probe
+        times, vtimes, covs, lens = [], [], [], []
         for s in range(args.sweep):
             draft, target, _, expanded = make_inputs(w, cfg, dev, w.gen_seed + 7919 * s, args.seed, s,
-                                                     tree, ws, stats, views, target=verify)
+                                                     tree, ws, stats, views)
+            layers = [draft[:, 0 if l == 0 else 1 + (l - 1) * FP:] for l in range(D)]
+
+            def verify():
+                if dense:
+                    vrt.verify_dense(cfg, target, ld, N * ld, layers, ld, n_draft * ld, tree, args.seed, s, ws,
+                                     out_tokens, out_nodes, out_len, stats)
+                else:
+                    vrt.verify_tree(cfg, target, ld, N * ld, tree, args.seed, s, ws, out_tokens, out_nodes,
+                                    out_len, stats)
             # coverage of the expanded rows (layer 0: the root; layer l: the first n_front rows)
             vrt.support_coverage(cfg, draft, ld, n_draft * ld, n_draft, cov)
             c = cov.cpu().numpy()
@@ -235,26 +245,24 @@ def sweep(args):
                 r0 = 0 if layer == 0 else 1 + (layer - 1) * FP
                 for b in range(B):
                     covs.extend(c[b, r0:r0 + int(expanded[layer][b])].tolist())
-            if verify:
-                vrt.verify_tree(cfg, target, ld, N * ld, tree, args.seed, s, ws, out_tokens, out_nodes,
-                                out_len, stats)
-                lens.append(out_len.float().mean().item())
-            del target
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            verify()
+            lens.append(out_len.float().mean().item())
+            evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps + 2)]
             for k in range(reps + 2):
-                if k == 2:
-                    ev[0].record()
+                evs[k][0].record()
                 for layer in range(D):
-                    r0 = 0 if layer == 0 else 1 + (layer - 1) * FP
-                    vrt.build_tree(cfg, layer, draft[:, r0:], ld, n_draft * ld, args.seed, s, tree, ws,
-                                   stats)
+                    vrt.build_tree(cfg, layer, layers[layer], ld, n_draft * ld, args.seed, s, tree, ws, stats)
                 vrt.build_tree(cfg, vrt.FINISH, None, 0, 0, args.seed, s, tree, ws, stats)
-            ev[1].record()
+                evs[k][1].record()
+                verify()
+                evs[k][2].record()
             torch.cuda.synchronize()
-            times.append(ev[0].elapsed_time(ev[1]) / reps)
-            del draft
+            times.append(sum(e[0].elapsed_time(e[1]) for e in evs[2:]) / reps)
+            vtimes.append(sum(e[1].elapsed_time(e[2]) for e in evs[2:]) / reps)
+            del draft, target, layers
         rec = {"trunc": "dense" if trunc == vrt.DENSE else trunc,
                "build_ms_per_step": sum(times) / len(times),
+               "verify_ms_per_step": sum(vtimes) / len(vtimes),
                "coverage_mean": float(sum(covs) / len(covs)),
                "tokens_per_tree": (sum(lens) / len(lens)) if lens else None,
                "status_bits": int((stats.cpu()[:, 0] != 0).sum())}

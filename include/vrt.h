@@ -70,8 +70,8 @@ enum { VRT_ROOT = 0, VRT_DET = 1, VRT_PROBE = 2, VRT_FILL = 3 };
  *            baseline of RheoSampling's support-size ablation). Dense rows rank their
  *            top K exactly as a truncated support would, sum the ranking exponentials
  *            pairwise in token-id order and draw the probe by inverse CDF in token-id
- *            order; they write no tail table, so trees with the probe on cannot be
- *            verified (the verification entry points return VRT_EINVAL for them)
+ *            order; they write no tail table: trees with the probe on are verified by
+ *            vrt_verify_dense (the other verification entry points return VRT_EINVAL)
  *   K        slots per expanded parent (1 .. 30)
  *   m        deterministic top-m slots (probe mode: 0 <= m <= K-1)
  *   probe    1 = RheoSampling dual-identity slots, 0 = plain top-K (all deterministic)
@@ -145,7 +145,16 @@ typedef struct {
  *   child       i32 [B][N]   child node indices, in slot order
  *   tail_n      i32 [B][N]   tail entries of node i's expansion if its probe child is
  *                            kept, else 0
- *   tail_id     i32 [B][N][TC], tail_q f32 [B][N][TC]  that tail (q~ values) */
+ *   tail_id     i32 [B][N][TC], tail_q f32 [B][N][TC]  that tail (q~ values)
+ * Dense rows (trunc = VRT_DENSE; the three arrays are empty otherwise), whose probe
+ * tail is the whole row but its deterministic children, kept as what regenerates it
+ * from the draft row:
+ *   row_dense   f64 [B][NR][2]   the row's largest logit and its tempered tail mass
+ *                                sum_{v in tail} exp((x_v - max)/T) (0: no probe)
+ *   row_det     i32 [B][NR][32]  tokens of the deterministic children (the t0 best:
+ *                                the top m, or probe last the top K-1)
+ *   node_row    i32 [B][N]       expansion row of node i if its probe child is kept,
+ *                                else -1 */
 typedef struct {
   int64_t NC, NR, N, TC, FP;
   int64_t cand_token, cand_parent, cand_score, cand_kind;
@@ -153,6 +162,7 @@ typedef struct {
   int64_t front, n_front, smart, admitted, layer_sync;
   int64_t n_nodes, node_token, node_parent, node_depth, node_kind, node_cand;
   int64_t child_off, child, tail_n, tail_id, tail_q;
+  int64_t row_dense, row_det, node_row;
   int64_t total_bytes;
 } vrt_tree_layout;
 
@@ -243,6 +253,23 @@ vrt_status vrt_verify_nodes(const vrt_config* cfg, const void* target_logits, in
 vrt_status vrt_verify_walk(const vrt_config* cfg, const void* tree, void* ws, size_t ws_bytes,
                            int32_t* out_tokens, int32_t* out_nodes, int32_t* out_len, uint32_t* stats,
                            int32_t* node_out, void* stream);
+
+/* Verification of a dense tree (trunc = VRT_DENSE, the dense baseline of RheoSampling's
+ * support-size ablation): key design 3 as in vrt_verify_tree, with each kept probe's tail
+ * (its expansion row but the deterministic children, q~ = the tempered softmax of that
+ * draft row renormalised over the tail) regenerated from the draft rows the tree was
+ * built from, since no tail table is kept. A node whose probe child is kept costs a second
+ * pass over its target row together with that draft row.
+ *   draft_logits       host array of D device pointers: layer l's draft rows exactly as
+ *                      passed to vrt_build_tree for that layer (they must still hold them)
+ *   draft_ld, draft_tree_stride  their strides (the same for every layer, as for the build)
+ * Other arguments and outputs as vrt_verify_tree. Errors: as vrt_verify_tree, and
+ * VRT_EINVAL if trunc is not VRT_DENSE or a draft pointer or stride is invalid. */
+vrt_status vrt_verify_dense(const vrt_config* cfg, const void* target_logits, int64_t ld,
+                            int64_t tree_stride, const void* const* draft_logits, int64_t draft_ld,
+                            int64_t draft_tree_stride, const void* tree, uint64_t seed, uint64_t step,
+                            void* ws, size_t ws_bytes, int32_t* out_tokens, int32_t* out_nodes,
+                            int32_t* out_len, uint32_t* stats, int32_t* node_out, void* stream);
 
 /* Lazy verification: the same outputs as vrt_verify_tree (RheoSampling key design 3:
  * the walk from the root, each visited node's probe-first test, the recursive rejection of

@@ -81,6 +81,16 @@ class Lib:
                         self.out_tokens, self.out_nodes, self.out_len, self.stats, self.node_out)
         torch.cuda.synchronize()
 
+    def verify_dense(self, target, ld, seed, step, zero_stats=True):
+        """Dense trees: the draft rows of every layer are self.layer_rows."""
+        if zero_stats:
+            self.stats.zero_()
+        rows = self.layer_rows
+        vrt.verify_dense(self.cfg, target, ld, target.stride(0), rows, rows[0].shape[-1], rows[0].stride(0),
+                         self.tree, seed, step, self.ws, self.out_tokens, self.out_nodes, self.out_len,
+                         self.stats, self.node_out)
+        torch.cuda.synchronize()
+
     def verify_lazy(self, target, ld, seed, step, zero_stats=True):
         if zero_stats:
             self.stats.zero_()
@@ -117,11 +127,16 @@ def device_step(w, seed, step, dev, verify=True, keep_target=False):
     root_keys = torch.tensor([k - (1 << 64) if k >= (1 << 63) else k for k in rk], dtype=torch.int64,
                              device=dev)
     tree_of = torch.arange(B, dtype=torch.int32, device=dev)
+    dense = w.trunc == vrt.DENSE and w.probe  # the verification re-reads every layer's rows
     rows = torch.zeros((B, FP, ld), dtype=tdt, device=dev)
+    L.layer_rows = [rows]
     keys_prev = root_keys.view(B, 1)
     synth.rows_dev(p, zipf, keys_prev.reshape(-1), tree_of, rows[:, 0], synth.DRAFT, stream)
     L.build_layer(0, rows, ld, seed, step)
     for layer in range(1, D):
+        if dense:
+            rows = torch.zeros((B, FP, ld), dtype=tdt, device=dev)
+            L.layer_rows.append(rows)
         base = 0 if layer == 1 else K + (layer - 2) * FP * K  # the previous layer's candidates
         keys = torch.zeros((B, FP), dtype=torch.int64, device=dev)
         synth.frontier_keys_dev(B, K, base, keys_prev, L.views["front"], L.views["n_front"],
@@ -141,7 +156,12 @@ def device_step(w, seed, step, dev, verify=True, keep_target=False):
     target = torch.empty((B, N, ld), dtype=tdt, device=dev)
     synth.rows_dev(p, zipf, node_keys.reshape(-1), tree_of.repeat_interleave(N), target.view(B * N, ld),
                    synth.TARGET, stream)
-    L.verify(target, ld, seed, step, zero_stats=False)
+    if dense:
+        L.verify_dense(target, ld, seed, step, zero_stats=False)
+    else:
+        L.verify(target, ld, seed, step, zero_stats=False)
+    if not dense:
+        del L.layer_rows
     if keep_target:
         L.target, L.ld = target, ld
     del target

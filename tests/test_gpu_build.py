@@ -65,13 +65,17 @@ CASES = [
 
 
 def gpu_build(w, steps, seed, step, dev):
+    """Every layer built on the GPU from the oracle's rows. Each layer's rows stay in
+    L.layer_rows ([B, FP, ld], one tree stride for all layers, as dense verification
+    needs them)."""
     cfg = lib_config(w)
     L = Lib(cfg, dev)
+    L.layer_rows = []
     for layer in range(w.D):
         rows_list = [s.layer_rows[layer] if layer < len(s.layer_rows) else None for s in steps]
-        n_rows = 1 if layer == 0 else L.FP
-        rows, ld = to_device_rows(rows_list, w, n_rows, dev)
+        rows, ld = to_device_rows(rows_list, w, L.FP, dev)
         L.build_layer(layer, rows, ld, seed, step)
+        L.layer_rows.append(rows)
     L.finish(seed, step)
     return L
 
@@ -209,13 +213,17 @@ DENSE_CASES = [
 def test_dense_build_matches_oracle(gpu, name, w):
     exempt = total = 0
     for seed, step in [(1, 0), (2, 3)]:
-        steps = [OracleStep(w, seed, b, step, verify=not w.probe) for b in range(w.B)]
-        print(f"dense build parity: {name} seed={seed} step={step} B={w.B} V={w.V}", flush=True)
+        steps = [OracleStep(w, seed, b, step) for b in range(w.B)]
+        print(f"dense build and verification parity: {name} seed={seed} step={step} B={w.B} V={w.V}",
+              flush=True)
         L = gpu_build(w, steps, seed, step, gpu)
         assert (L.stats.cpu().numpy()[:, 0] == 0).all()
-        if not w.probe:
-            target, ld = to_device_rows([s.target_rows for s in steps], w, L.N, gpu)
+        target, ld = to_device_rows([s.target_rows for s in steps], w, L.N, gpu)
+        if w.probe:
+            L.verify_dense(target, ld, seed, step, zero_stats=False)
+        else:
             L.verify(target, ld, seed, step, zero_stats=False)
+        assert (L.stats.cpu().numpy()[:, 0] == 0).all()
         for b, s in enumerate(steps):
             total += 1
             try:
@@ -225,18 +233,38 @@ def test_dense_build_matches_oracle(gpu, name, w):
                     raise
                 exempt += 1
                 continue
-            if not w.probe:
-                Lt = len(s.out_tokens)
-                assert L.out_len[b].item() == Lt and np.array_equal(
-                    L.out_tokens[b, :Lt].cpu().numpy(), s.out_tokens) or s.verify_exempt > 0
+            check_node_decisions(s, L, b)
     print(f"{name}: {total} trees, {exempt} differ after a near-boundary probe draw")
     assert exempt <= max(1, total // 10), (exempt, total)
 
 
-def test_dense_trees_with_a_probe_are_not_verified(gpu):
+def check_node_decisions(s, L, b):
+    """Every node's decision and the emitted tokens of tree b against the oracle's; a
+    node may differ only after a draw within 1e-6 of its threshold."""
+    node_out = L.node_out[b].cpu().numpy()
+    pn = s.per_node
+    for i in range(s.view["n_nodes"]):
+        g = node_out[i]
+        same = g[0] == pn["accept"][i] and (pn["accept"][i] >= 0 or g[1] == pn["token"][i])
+        if pn["exempt"][i]:
+            continue
+        assert same, (b, i, g, pn[i])
+        if pn["accept"][i] < 0:
+            W = np.array([g[3]], np.int32).view(np.float32)[0]
+            assert abs(W - pn["W"][i]) <= 1e-5, (b, i, W, pn["W"][i])
+        assert (g[2] & 0xFF) == pn["n_tests"][i], (b, i, g, pn[i])
+    Lt = len(s.out_tokens)
+    assert (L.out_len[b].item() == Lt and np.array_equal(L.out_tokens[b, :Lt].cpu().numpy(), s.out_tokens)) \
+        or s.verify_exempt > 0
+
+
+def test_dense_trees_with_a_probe_need_the_draft_rows(gpu):
     w = _small(trunc=vrt.DENSE, B=2, D=2, R=8)
     L = Lib(lib_config(w), gpu)
     target = torch.zeros((w.B, L.N, 5000), dtype=torch.int16, device=gpu)
     with pytest.raises(vrt.VrtError) as e:
         L.verify(target, 5000, 1, 0)
-    assert e.value.code == vrt.EINVAL and "VRT_DENSE" in str(e.value)
+    assert e.value.code == vrt.EINVAL and "vrt_verify_dense" in str(e.value)
+    with pytest.raises(vrt.VrtError) as e:
+        L.verify_lazy(target, 5000, 1, 0)
+    assert e.value.code == vrt.EINVAL

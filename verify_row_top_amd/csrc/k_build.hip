@@ -1077,16 +1077,6 @@ __device__ __forceinline__ void dense_load(const char* row, int c, int V, float 
     });
 }
 
-// exp((x - M)/T) to about 1e-7 relative: the fp64 exponent is split into an fp32 head
-// and a tail, e^a = e^head (1 + tail).
-__device__ __forceinline__ double dense_tempered(float x, float M, double invT) {
-  if (!(x > -INFINITY)) return 0.0;
-  const double a = ((double)x - (double)M) * invT;
-  const float h = (float)a;
-  const float t = (float)(a - (double)h);
-  return (double)expf(h) * (1.0 + (double)t);
-}
-
 // Whether token v is one of the n deterministic children (wave-uniform list in LDS).
 __device__ __forceinline__ bool dense_is_det(const DenseLds& L, int n, int v) {
   bool d = false;
@@ -1286,7 +1276,14 @@ __global__ __launch_bounds__(8 * kWave) void k_dense_expand(const BArgs a) {
       proxy = t1 < 1.0f ? t1 : 1.0f;
     }
   }
-  if (lane == 0) a.t.row_tail_n[ktb] = 0;
+  // what regenerates the probe's tail at verification: the row's largest logit, the
+  // tempered tail mass and the deterministic children's tokens
+  if (lane == 0) {
+    a.t.row_tail_n[ktb] = 0;
+    a.t.row_dense[ktb * 2] = (double)M;
+    a.t.row_dense[ktb * 2 + 1] = probe >= 0 ? zT : 0.0;
+  }
+  if (lane < t0) a.t.row_det[ktb * 32 + lane] = L.det[lane];
 
   // 4. child slots: DET ranks, the probe, then fillers in rank order (lane s: slot s)
   const int rp_hit = (int)__builtin_ctzll(ballot(lane < n_sup && probe >= 0 &&
@@ -1663,8 +1660,11 @@ __global__ __launch_bounds__(kFT) void k_finish(const Cfg c, const TreePtrs t) {
     const int before = __builtin_popcount(s_smask[pn] & ((1u << slot) - 1u));
     t.child[nb + s_cnt[pn] + before] = i;
   }
-  // probe tails, copied to the probe's parent (all loads of a round in flight at once)
+  // probe tails, copied to the probe's parent (all loads of a round in flight at once);
+  // dense rows: the expansion row that regenerates the tail
   for (int i = tid; i < n; i += kFT) t.tail_n[nb + i] = s_tn[i];
+  if (c.trunc == VRT_DENSE)
+    for (int i = tid; i < n; i += kFT) t.node_row[nb + i] = s_trow[i];
   constexpr int U = 8;
   const int64_t tot = (int64_t)n * c.TC;
   for (int64_t x0 = 0; x0 < tot; x0 += (int64_t)kFT * U) {

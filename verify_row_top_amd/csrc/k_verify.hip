@@ -47,6 +47,14 @@ struct VRec {
   float x[kChildMax];
   float u[kChildMax];  // draw of each non-probe kept child's test
   NodeOut res;         // the decision, also written here for the block (lazy walk)
+  // dense rows (the probe's tail regenerated from the expansion's draft row)
+  const char* drow;    // that draft row, NULL if the probe child is not kept
+  double dzt;          // its tempered tail mass
+  float dmax;          // its largest logit
+  int nd;              // deterministic children: the tokens off the tail
+  int det[kChildMax];
+  float mc;            // pass 2's p: fl(max*c2) and 1/S of the target row,
+  double invs, qscale; // and the scale of q~ (probe last: the residual mass W_D)
 };
 
 struct VArgs {
@@ -61,6 +69,8 @@ struct VArgs {
   int32_t* out_nodes;
   int32_t* out_len;
   uint32_t* stats;
+  const void* draft[32];  // dense rows: layer l's draft rows (as passed to the build)
+  int64_t dld, dstride;
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -180,14 +190,15 @@ struct DLds {
   double* qc;
   int* itok;
   double* idel;
-  float* w;  // [64][33] weights of the sampled chunk
+  float* w;    // [64][33] weights of the sampled chunk
+  double* ov;  // dense rows: per chunk, sum over the tail of min(p, s q~) [nch]
 };
 
 __host__ __device__ size_t decide_lds_bytes(const Cfg& c) {
   const size_t nch = (size_t)(c.V + kCH - 1) / kCH;
   const size_t TC = (size_t)c.TC;
   const size_t bytes = nch * 16 + TC * (4 + 4 + 8 + 4) + kChildMax * 8 + (TC + kChildMax) * (4 + 8) +
-                       kWave * 33 * 4 + 72;
+                       kWave * 33 * 4 + 72 + (c.trunc == VRT_DENSE ? nch * 8 + 8 : 0);
   return (bytes + 15) & ~(size_t)15;
 }
 
@@ -209,13 +220,14 @@ __device__ DLds carve(char* base, int nch, int TC) {
   L.tslot = (int*)take((size_t)TC * 4);
   L.itok = (int*)take((size_t)(TC + kChildMax) * 4);
   L.w = (float*)take((size_t)kWave * 33 * 4);
+  L.ov = (double*)take((size_t)nch * 8);  // dense rows only (not reserved otherwise)
   return L;
 }
 
 // The decision inputs of node i other than its row statistics, gathered into the
 // block's LDS by one wave: kept children (node, token, logit) in slot order and the
 // probe tail (token, q~, logit).
-template <int DT>
+template <int DT, bool DENSE>
 __device__ void gather_node(const VArgs& a, int b, int i, int nn, const char* row, VRec& r,
                             const DLds& L) {
   const Cfg& c = a.c;
@@ -258,6 +270,40 @@ __device__ void gather_node(const VArgs& a, int b, int i, int nn, const char* ro
     L.tslot[e] = slot;
     if (slot >= 0) L.qc[slot] = q;
   }
+  if constexpr (DENSE) {
+    // the probe's tail is its expansion row but the deterministic children: q~ of the
+    // kept children in it, from that draft row
+    const char* drow = nullptr;
+    double dzt = 0.0;
+    float dmax = 0.0f;
+    int nd = 0;
+    const int rr = pl >= 0 ? a.t.node_row[nb + i] : -1;
+    if (rr >= 0 && rr < c.NR) {
+      const int l = rr == 0 ? 0 : 1 + (rr - 1) / c.P;
+      const int jr = rr == 0 ? 0 : rr - 1 - (l - 1) * c.P;
+      const int64_t rb = (int64_t)b * c.NR + rr;
+      dzt = a.t.row_dense[rb * 2 + 1];
+      dmax = (float)a.t.row_dense[rb * 2];
+      if (l < c.D && a.draft[l] && dzt > 0.0) {
+        constexpr int esz = DT == VRT_BF16 ? 2 : 4;
+        drow = (const char*)a.draft[l] + ((int64_t)b * a.dstride + (int64_t)jr * a.dld) * esz;
+        nd = c.order == VRT_PROBE_LAST ? min(c.K - 1, c.V) : c.m;
+        if (lane < nd) r.det[lane] = a.t.row_det[rb * 32 + lane];
+      }
+    }
+    wave_sync();
+    if (drow && lane < nc && tok >= 0) {
+      bool in_tail = true;
+      for (int k = 0; k < nd; ++k) in_tail &= r.det[k] != tok;
+      if (in_tail) L.qc[lane] = dense_tempered(load_one<DT>(drow, tok), dmax, (double)a.c.invT) / dzt;
+    }
+    if (lane == 0) {
+      r.drow = drow;
+      r.dzt = dzt;
+      r.dmax = dmax;
+      r.nd = nd;
+    }
+  }
   // the draws (keyed by depth and test index): probe test j = 0, the other kept
   // children j = 1, 2, .. in slot order, the final sample
   const uint32_t depth = (uint32_t)min(max(a.t.node_depth[nb + i], 0), 63);
@@ -282,9 +328,112 @@ __device__ void gather_node(const VArgs& a, int b, int i, int nn, const char* ro
 }
 
 
+// The target row's normaliser from its chunk statistics, by one wave: MC = the largest
+// fl(max*c2), S = sum of the chunk masses scaled to MC (each also written to pm).
+__device__ __forceinline__ void target_norm(const float2* cs, int nch, double* pm, float& MC, double& S) {
+  const int lane = lane_id();
+  constexpr int kCPL = 8;  // chunks per lane: V <= 2^20
+  float2 st[kCPL];
+  static_for<kCPL>([&](auto k) {
+    const int ch = lane + k * kWave;
+    st[k] = ch < nch ? cs[ch] : make_float2(-INFINITY, 0.0f);
+  });
+  float mcl = -INFINITY;
+  static_for<kCPL>([&](auto k) { mcl = fmaxf(mcl, st[k].x); });
+  MC = wave_max(mcl);
+  double sl = 0.0;
+  static_for<kCPL>([&](auto k) {
+    const int ch = lane + k * kWave;
+    if (ch < nch) {
+      const double m = (double)st[k].y * (double)fast_exp2(st[k].x - MC);
+      pm[ch] = m;
+      sl += m;
+    }
+  });
+  S = wave_sum(sl);
+}
+
+// Dense rows, by wave 0 before the overlap pass: the target normaliser and the scale of
+// q~ exactly as decide_node forms them (probe last: W_D = 1 - p of the other kept
+// children), into R.
+__device__ __forceinline__ void dense_prepare(const Cfg& c, const float2* cs, VRec& R, const DLds& L) {
+  const int lane = lane_id();
+  const int nch = (c.V + kCH - 1) / kCH;
+  float MC;
+  double S;
+  target_norm(cs, nch, L.pm, MC, S);
+  const bool ok = S > 0.0 && S < INFINITY && MC < INFINITY;
+  const double invS = ok ? 1.0 / S : 0.0;
+  const int nc = R.nc, probe = R.probe;
+  const int tok = lane < nc ? R.tok[lane] : -1;
+  const double pc = tok >= 0 ? (double)fast_exp2(__builtin_fmaf(R.x[lane], c.c2, -MC)) * invS : 0.0;
+  const uint64_t cmask = ballot(lane < nc && lane != probe && R.node[lane] >= 0);
+  double WD = 1.0;
+  for (uint64_t m = cmask; m; m &= m - 1ull) WD -= readlane_d(pc, __builtin_ctzll(m));
+  if (lane == 0) {
+    R.mc = MC;
+    R.invs = invS;
+    R.qscale = c.order == VRT_PROBE_LAST ? WD : 1.0;
+  }
+}
+
+// Dense rows, all waves: per 2048-token chunk, the sum over the probe's tail of
+// min(p, s q~), with p from the target row and q~ regenerated from the draft row.
+template <int DT, int NT>
+__device__ __forceinline__ void dense_overlap(const Cfg& c, const char* row, const VRec& R, const DLds& L) {
+  constexpr int esz = DT == VRT_BF16 ? 2 : 4;
+  constexpr int EPL = 16 / esz;
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int V = c.V, nch = (V + kCH - 1) / kCH, nd = R.nd;
+  const float MC = R.mc;
+  const double invS = R.invs, qs = R.qscale / R.dzt, invT = (double)c.invT;
+  const float dmax = R.dmax;
+  for (int ch = wave; ch < nch; ch += NT / kWave) {
+    const int my0 = ch * kCH + lane * 32;  // lane l owns tokens [my0, my0 + 32)
+    u32x4_t xt[32 / EPL], xd[32 / EPL];
+    static_for<32 / EPL>([&](auto q) {
+      const int e0 = my0 + q * EPL;
+      xt[q] = u32x4_t{0u, 0u, 0u, 0u};
+      xd[q] = u32x4_t{0u, 0u, 0u, 0u};
+      if (e0 < V) {
+        xt[q] = *(const u32x4_t*)(row + (int64_t)e0 * esz);
+        xd[q] = *(const u32x4_t*)(R.drow + (int64_t)e0 * esz);
+      }
+    });
+    bool hd = false;  // the chunk holds a deterministic child (uniform)
+    for (int k = 0; k < nd; ++k) hd |= R.det[k] >= ch * kCH && R.det[k] < (ch + 1) * kCH;
+    double ov = 0.0;
+    static_for<32 / EPL>([&](auto q) {
+      static_for<EPL>([&](auto k) {
+        float x, d;
+        if constexpr (DT == VRT_BF16) {
+          x = (k & 1) ? bf16_hi(xt[q][k >> 1]) : bf16_lo(xt[q][k >> 1]);
+          d = (k & 1) ? bf16_hi(xd[q][k >> 1]) : bf16_lo(xd[q][k >> 1]);
+        } else {
+          x = __uint_as_float(xt[q][(int)k]);
+          d = __uint_as_float(xd[q][(int)k]);
+        }
+        const int v = my0 + q * EPL + (int)k;
+        bool tail = v < V;
+        if (hd)
+          for (int t = 0; t < nd; ++t) tail &= R.det[t] != v;
+        if (tail) {
+          const double p = (double)fast_exp2(__builtin_fmaf(x, c.c2, -MC)) * invS;
+          const double qv = qs * dense_tempered(d, dmax, invT);
+          ov += fmin(p, qv);
+        }
+      });
+    });
+    ov = wave_sum(ov);
+    if (lane == 0) L.ov[ch] = ov;
+  }
+}
+
 // The decision of node i by one wave, from the chunk statistics and gathered inputs
-// in LDS (see the file comment).
-template <int DT>
+// in LDS (see the file comment). DENSE: the probe's tail is regenerated from the
+// expansion's draft row (R.drow) instead of a tail table.
+template <int DT, bool DENSE>
 __device__ void decide_node(const VArgs& a, int b, int i, const char* row, const float2* cs,
                             VRec& R, const DLds& L) {
   const Cfg& c = a.c;
@@ -302,28 +451,12 @@ __device__ void decide_node(const VArgs& a, int b, int i, const char* row, const
     r_x = R.x[lane];
     r_u = R.u[lane];
   }
-  constexpr int kCPL = 8;  // chunks per lane: V <= 2^20
-  float2 st[kCPL];
-  static_for<kCPL>([&](auto k) {
-    const int ch = lane + k * kWave;
-    st[k] = ch < nch ? cs[ch] : make_float2(-INFINITY, 0.0f);
-  });
   const int ch_node = lane < nc ? r_node : -1;
   const int ch_tok = lane < nc ? r_tok : -1;
   const float ch_x = lane < nc ? r_x : -INFINITY;
-  float mcl = -INFINITY;
-  static_for<kCPL>([&](auto k) { mcl = fmaxf(mcl, st[k].x); });
-  const float MC = wave_max(mcl);
-  double sl = 0.0;
-  static_for<kCPL>([&](auto k) {
-    const int ch = lane + k * kWave;
-    if (ch < nch) {
-      const double pm = (double)st[k].y * (double)fast_exp2(st[k].x - MC);
-      L.pm[ch] = pm;
-      sl += pm;
-    }
-  });
-  const double S = wave_sum(sl);
+  float MC;
+  double S;
+  target_norm(cs, nch, L.pm, MC, S);
   NodeOut out{-1, -1, 0, 0.0f};
   if (!(S > 0.0) || !(S < INFINITY) || !(MC < INFINITY)) {
     out.flags = (int)(VRT_ST_TARGET_BAD << 16);
@@ -350,8 +483,14 @@ __device__ void decide_node(const VArgs& a, int b, int i, const char* row, const
     for (uint64_t m = cmask; m; m &= m - 1ull) WD -= readlane_d(pc, __builtin_ctzll(m));
   const double qscale = last ? WD : 1.0;
   double overlap = 0.0;
+  const bool dense_tail = DENSE && R.drow != nullptr;  // the overlap pass ran
   if (probe >= 0) {
     double ov = 0.0;
+    if constexpr (DENSE) {
+      const int cpl = (nch + kWave - 1) / kWave;
+      if (dense_tail)
+        for (int ch = lane * cpl; ch < min(nch, (lane + 1) * cpl); ++ch) ov += L.ov[ch];
+    }
     for (int e = lane; e < nt; e += kWave) {
       const int y = L.tid[e];
       const double p = y >= 0 ? p_of_x((float)L.tp[e]) : 0.0;
@@ -383,8 +522,10 @@ __device__ void decide_node(const VArgs& a, int b, int i, const char* row, const
   wave_sync();
   // changes of mass relative to p: the probe's tail (clipped residual, or zero for a
   // rejected child) and the rejected children outside it (zero). Fixed-point atomics
-  // keep the per-chunk sums independent of the order of arrival.
-  if (probe >= 0) {
+  // keep the per-chunk sums independent of the order of arrival. Dense rows: the tail's
+  // clipping is the overlap pass's per-chunk sums, and each rejected child removes its
+  // residual w (its p off the tail).
+  if (!DENSE && probe >= 0) {
     for (int e = lane; e < nt; e += kWave) {
       const int y = L.tid[e];
       if (y < 0) continue;
@@ -395,8 +536,9 @@ __device__ void decide_node(const VArgs& a, int b, int i, const char* row, const
       atomicAdd((unsigned long long*)&L.dfix[y / kCH], (unsigned long long)__double2ll_rn(d * kFix));
     }
   }
-  const bool mine = cand && !in_tail;
-  if (mine) atomicAdd((unsigned long long*)&L.dfix[ch_tok / kCH], (unsigned long long)__double2ll_rn(-pc * kFix));
+  const bool mine = DENSE ? cand : (cand && !in_tail);
+  const double mdel = (DENSE && in_tail) ? -wc : -pc;
+  if (mine) atomicAdd((unsigned long long*)&L.dfix[ch_tok / kCH], (unsigned long long)__double2ll_rn(mdel * kFix));
   wave_sync();
   // adjusted chunk masses, lane-blocked contiguous chunks
   const int cpl = (nch + kWave - 1) / kWave;
@@ -404,6 +546,7 @@ __device__ void decide_node(const VArgs& a, int b, int i, const char* row, const
   double lmass = 0.0;
   for (int ch = c0; ch < c1; ++ch) {
     double mch = L.pm[ch] * invS + (double)L.dfix[ch] * (1.0 / kFix);
+    if (dense_tail) mch -= L.ov[ch];
     if (mch < 0.0) mch = 0.0;
     L.pm[ch] = mch;
     lmass += mch;
@@ -447,10 +590,18 @@ __device__ void decide_node(const VArgs& a, int b, int i, const char* row, const
     raw[q] = u32x4_t{0u, 0u, 0u, 0u};
     if (e0 < V) raw[q] = *(const u32x4_t*)(row + (int64_t)e0 * esz);
   });
+  u32x4_t rawd[DENSE ? 32 / EPL : 1];  // dense rows: the same tokens of the draft row
+  if constexpr (DENSE) {
+    static_for<32 / EPL>([&](auto q) {
+      const int e0 = my0 + q * EPL;
+      rawd[q] = u32x4_t{0u, 0u, 0u, 0u};
+      if (dense_tail && e0 < V) rawd[q] = *(const u32x4_t*)(R.drow + (int64_t)e0 * esz);
+    });
+  }
   // the changes that fall inside the chunk, listed for the owners of their tokens
   int nitem = 0;
   wave_sync();
-  if (probe >= 0) {
+  if (!DENSE && probe >= 0) {
     for (int e0 = 0; e0 < nt; e0 += kWave) {
       const int e = e0 + lane;
       bool inside = false;
@@ -481,7 +632,7 @@ __device__ void decide_node(const VArgs& a, int b, int i, const char* row, const
     if (inside) {
       const int at = nitem + (int)__builtin_popcountll(m & ((1ull << lane) - 1ull));
       L.itok[at] = ch_tok;
-      L.idel[at] = -pc;
+      L.idel[at] = mdel;
     }
     nitem += (int)__builtin_popcountll(m);
   }
@@ -531,6 +682,19 @@ __device__ void decide_node(const VArgs& a, int b, int i, const char* row, const
           else x = __uint_as_float(raw[q][(int)k]);
           const int e = q * EPL + k;
           sw[e] = (my0 + e < V && x > -INFINITY) ? fast_exp2(__builtin_fmaf(x, c2, -MC)) * invSf : 0.0f;
+          if constexpr (DENSE) {
+            if (dense_tail && my0 + e < V) {  // a tail token keeps p - min(p, s q~)
+              bool tail = true;
+              for (int t = 0; t < R.nd; ++t) tail &= R.det[t] != my0 + e;
+              if (tail) {
+                const float d = (DT == VRT_BF16) ? ((k & 1) ? bf16_hi(rawd[q][k >> 1]) : bf16_lo(rawd[q][k >> 1]))
+                                                 : __uint_as_float(rawd[q][(int)k]);
+                const double pd = (double)fast_exp2(__builtin_fmaf(x, c2, -MC)) * invS;
+                const double qv = qscale * dense_tempered(d, R.dmax, (double)c.invT) / R.dzt;
+                sw[e] = (float)(pd - fmin(pd, qv));
+              }
+            }
+          }
         });
       });
     }
@@ -589,7 +753,7 @@ constexpr int kMaxChunks = (1 << 20) / kCH;  // V <= 2^20
 
 // One node's pass by a block of NT threads: stream the row (all waves), gather the
 // decision inputs (last wave, overlapping the others' stream), then decide (wave 0).
-template <int DT, int NT>
+template <int DT, int NT, bool DENSE = false>
 __device__ __forceinline__ void node_pass(const VArgs& a, int b, int i, int nn, float2* s_cs, VRec& s_rec,
                                           const DLds& L, int& s_next) {
   const Cfg& c = a.c;
@@ -602,7 +766,7 @@ __device__ __forceinline__ void node_pass(const VArgs& a, int b, int i, int nn, 
   constexpr int NW = NT / kWave;
   if (threadIdx.x == 0) s_next = NW;
   __syncthreads();
-  if (wave == NW - 1) gather_node<DT>(a, b, i, nn, row, s_rec, L);
+  if (wave == NW - 1) gather_node<DT, DENSE>(a, b, i, nn, row, s_rec, L);
   // pairs of chunks are handed out as waves become free (the gathering wave takes
   // fewer); both chunks' loads are in flight together
   const int npair = (nch + 1) / 2;
@@ -623,7 +787,17 @@ __device__ __forceinline__ void node_pass(const VArgs& a, int b, int i, int nn, 
     pr = nx;
   }
   __syncthreads();
-  if (wave == 0) decide_node<DT>(a, b, i, row, s_cs, s_rec, L);
+  if constexpr (DENSE) {
+    // a kept probe on a dense row: its tail's overlap with p in a second pass over the
+    // target row and the expansion's draft row
+    if (s_rec.drow != nullptr) {  // uniform
+      if (wave == 0) dense_prepare(c, s_cs, s_rec, L);
+      __syncthreads();
+      dense_overlap<DT, NT>(c, row, s_rec, L);
+      __syncthreads();
+    }
+  }
+  if (wave == 0) decide_node<DT, DENSE>(a, b, i, row, s_cs, s_rec, L);
 }
 
 // One block per (node, tree): that node's pass.
@@ -640,6 +814,22 @@ __global__ __launch_bounds__(kVB) void k_vnode(const VArgs a) {
   extern __shared__ double s_dyn[];
   const DLds L = carve((char*)s_dyn, (c.V + kCH - 1) / kCH, c.TC);
   node_pass<DT, kVB>(a, b, i, nn, s_cs, s_rec, L, s_next);
+}
+
+// Dense rows: the same pass with the probe tails regenerated from the draft rows.
+template <int DT>
+__global__ __launch_bounds__(kVB) void k_vnode_dense(const VArgs a) {
+  const Cfg& c = a.c;
+  const int b = blockIdx.y;
+  const int i = blockIdx.x;
+  const int nn = clamp_nodes(a.t.n_nodes[b], c.N);
+  if (i >= nn) return;
+  __shared__ float2 s_cs[kMaxChunks];
+  __shared__ VRec s_rec;
+  __shared__ int s_next;
+  extern __shared__ double s_dyn[];
+  const DLds L = carve((char*)s_dyn, (c.V + kCH - 1) / kCH, c.TC);
+  node_pass<DT, kVB, true>(a, b, i, nn, s_cs, s_rec, L, s_next);
 }
 
 // Emitted tokens, nodes and statistics of tree b once its walk has ended (len tokens).
@@ -757,16 +947,23 @@ size_t verify_ws_bytes(const Cfg& c) {
 hipError_t launch_verify(int parts, const Cfg& c, const TreePtrs& t, const void* logits, int64_t ld,
                          int64_t tstride, uint64_t seed, uint32_t step, NodeOut* node_out,
                          int32_t* out_tokens, int32_t* out_nodes, int32_t* out_len, uint32_t* stats,
-                         void* ws, hipStream_t stream) {
+                         void* ws, const void* const* draft, int64_t dld, int64_t dstride,
+                         hipStream_t stream) {
   (void)ws;
-  VArgs a{c, t, logits, ld, tstride, seed, step, node_out, out_tokens, out_nodes, out_len, stats};
+  VArgs a{c, t, logits, ld, tstride, seed, step, node_out, out_tokens, out_nodes, out_len, stats, {}, dld,
+          dstride};
+  for (int l = 0; l < c.D && l < 32 && draft; ++l) a.draft[l] = draft[l];
   if (parts & 1) {
     const dim3 grid(c.N, c.B);
     const size_t lds = decide_lds_bytes(c);
-    if (c.dtype == VRT_BF16)
-      hipLaunchKernelGGL(k_vnode<VRT_BF16>, grid, dim3(kVB), lds, stream, a);
-    else
-      hipLaunchKernelGGL(k_vnode<VRT_F32>, grid, dim3(kVB), lds, stream, a);
+    const bool dense = (parts & 8) != 0;
+    if (c.dtype == VRT_BF16) {
+      if (dense) hipLaunchKernelGGL(k_vnode_dense<VRT_BF16>, grid, dim3(kVB), lds, stream, a);
+      else hipLaunchKernelGGL(k_vnode<VRT_BF16>, grid, dim3(kVB), lds, stream, a);
+    } else {
+      if (dense) hipLaunchKernelGGL(k_vnode_dense<VRT_F32>, grid, dim3(kVB), lds, stream, a);
+      else hipLaunchKernelGGL(k_vnode<VRT_F32>, grid, dim3(kVB), lds, stream, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -60,6 +60,10 @@ bool compute_layout(const vrt_config& c, vrt_tree_layout* L) {
   take(&L->tail_n, B * L->N * 4);
   take(&L->tail_id, B * L->N * L->TC * 4);
   take(&L->tail_q, B * L->N * L->TC * 4);
+  const int64_t dense = c.trunc == VRT_DENSE ? 1 : 0;
+  take(&L->row_dense, dense * B * L->NR * 2 * 8);
+  take(&L->row_det, dense * B * L->NR * 32 * 4);
+  take(&L->node_row, dense * B * L->N * 4);
   L->total_bytes = off;
   return true;
 }
@@ -148,6 +152,9 @@ TreePtrs tree_ptrs(const vrt_config& c, void* blob) {
   t.tail_n = (int*)(p + L.tail_n);
   t.tail_id = (int*)(p + L.tail_id);
   t.tail_q = (float*)(p + L.tail_q);
+  t.row_dense = (double*)(p + L.row_dense);
+  t.row_det = (int*)(p + L.row_det);
+  t.node_row = (int*)(p + L.node_row);
   return t;
 }
 
@@ -268,13 +275,23 @@ namespace {
 vrt_status verify_parts(int parts, const vrt_config* cp, const void* target_logits, int64_t ld,
                         int64_t tree_stride, const void* tree, uint64_t seed, uint64_t step, void* ws,
                         size_t ws_bytes, int32_t* out_tokens, int32_t* out_nodes, int32_t* out_len,
-                        uint32_t* stats, int32_t* node_out, void* stream) {
+                        uint32_t* stats, int32_t* node_out, void* stream, const void* const* draft = nullptr,
+                        int64_t dld = 0, int64_t dstride = 0) {
   vrt_status s = vrt_check_config(cp);
   if (s != VRT_OK) return s;
   const vrt_config& c = *cp;
-  if (c.trunc == VRT_DENSE && c.probe)
+  if (c.trunc == VRT_DENSE && c.probe && !(parts & 8))
     return fail(VRT_EINVAL, "trees built with trunc = VRT_DENSE and the probe on carry no tail table: "
-                            "verification needs one (build with trunc in [1, 1024], or the probe off)");
+                            "verify them with vrt_verify_dense, which regenerates the tails from the "
+                            "draft rows");
+  if (parts & 8) {
+    if (c.trunc != VRT_DENSE) return fail(VRT_EINVAL, "vrt_verify_dense needs trunc = VRT_DENSE");
+    if (!draft) return fail(VRT_EINVAL, "draft row pointer array is NULL");
+    for (int l = 0; l < c.D; ++l) {
+      s = check_rows(c, draft[l], dld, dstride, "draft");
+      if (s != VRT_OK) return s;
+    }
+  }
   if (!tree || !ws) return fail(VRT_EINVAL, "tree and workspace pointers must not be NULL");
   if (!aligned16(tree) || !aligned16(ws)) return fail(VRT_EINVAL, "tree and workspace must be 16-byte aligned");
   if ((parts & 6) && (!out_tokens || !out_nodes || !out_len || !stats))
@@ -292,7 +309,7 @@ vrt_status verify_parts(int parts, const vrt_config* cp, const void* target_logi
   vrt::NodeOut* no = node_out ? (vrt::NodeOut*)node_out : (vrt::NodeOut*)((char*)ws + wl.node_out);
   const hipError_t e = vrt::launch_verify(parts, k, t, target_logits, ld, tree_stride, seed,
                                           (uint32_t)step, no, out_tokens, out_nodes, out_len, stats,
-                                          (char*)ws + wl.verify, (hipStream_t)stream);
+                                          (char*)ws + wl.verify, draft, dld, dstride, (hipStream_t)stream);
   if (e != hipSuccess) return fail(VRT_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
   return VRT_OK;
 }
@@ -305,6 +322,15 @@ vrt_status vrt_verify_tree(const vrt_config* cp, const void* target_logits, int6
                            int32_t* out_len, uint32_t* stats, int32_t* node_out, void* stream) {
   return verify_parts(3, cp, target_logits, ld, tree_stride, tree, seed, step, ws, ws_bytes, out_tokens,
                       out_nodes, out_len, stats, node_out, stream);
+}
+
+vrt_status vrt_verify_dense(const vrt_config* cp, const void* target_logits, int64_t ld, int64_t tree_stride,
+                            const void* const* draft_logits, int64_t draft_ld, int64_t draft_tree_stride,
+                            const void* tree, uint64_t seed, uint64_t step, void* ws, size_t ws_bytes,
+                            int32_t* out_tokens, int32_t* out_nodes, int32_t* out_len, uint32_t* stats,
+                            int32_t* node_out, void* stream) {
+  return verify_parts(3 | 8, cp, target_logits, ld, tree_stride, tree, seed, step, ws, ws_bytes, out_tokens,
+                      out_nodes, out_len, stats, node_out, stream, draft_logits, draft_ld, draft_tree_stride);
 }
 
 vrt_status vrt_verify_lazy(const vrt_config* cp, const void* target_logits, int64_t ld, int64_t tree_stride,

@@ -63,6 +63,16 @@ __device__ __forceinline__ float exp_rank(float x) {
   return __builtin_ldexpf(p, (int)k);
 }
 
+// exp((x - M)/T) to about 1e-7 relative (dense rows): the fp64 exponent is split into
+// an fp32 head and a tail, e^a = e^head (1 + tail); -inf and NaN give 0.
+__device__ __forceinline__ double dense_tempered(float x, float M, double invT) {
+  if (!(x > -INFINITY)) return 0.0;
+  const double a = ((double)x - (double)M) * invT;
+  const float h = (float)a;
+  const float t = (float)(a - (double)h);
+  return (double)expf(h) * (1.0 + (double)t);
+}
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
 // Orders LDS accesses between the lanes of one wave (no block barrier: usable

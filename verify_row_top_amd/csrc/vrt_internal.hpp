@@ -48,6 +48,9 @@ struct TreePtrs {
   int* tail_n;
   int* tail_id;
   float* tail_q;
+  double* row_dense;  // dense rows: [NR][2] (largest logit, tempered tail mass)
+  int* row_det;       // dense rows: [NR][32] deterministic children's tokens
+  int* node_row;      // dense rows: [N] expansion row of a node whose probe is kept
 };
 
 // Per-node verification outcome: accepted child node (-1: none), final token
@@ -70,11 +73,14 @@ hipError_t launch_accepted_kv(const Cfg& c, const int32_t* out_nodes, const int3
                               int32_t* keep, int32_t* keep_n, hipStream_t stream);
 
 // parts: 1 = decide every node (k_vnode), 2 = walk (k_vwalk), 3 = both, 4 = the lazy walk
-// (k_vlazy: decide only the nodes the walk reaches)
+// (k_vlazy: decide only the nodes the walk reaches); + 8: dense rows, the nodes decided by
+// k_vnode_dense with the probe tails regenerated from draft[l] (layer l's draft rows,
+// row j of tree b at b*dstride + j*dld elements)
 hipError_t launch_verify(int parts, const Cfg& c, const TreePtrs& t, const void* logits, int64_t ld,
                          int64_t tstride, uint64_t seed, uint32_t step, NodeOut* node_out,
                          int32_t* out_tokens, int32_t* out_nodes, int32_t* out_len, uint32_t* stats,
-                         void* ws, hipStream_t stream);
+                         void* ws, const void* const* draft, int64_t dld, int64_t dstride,
+                         hipStream_t stream);
 
 // Device scratch of the build: each row segment's sorted top-trunc keys and counts.
 size_t build_ws_bytes(const Cfg& c);

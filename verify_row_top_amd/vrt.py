@@ -19,7 +19,7 @@ FINISH = -1
 DENSE = 0  # trunc value: no truncation, the support is the whole vocabulary
 ST_DRAFT_NONFINITE, ST_DRAFT_EMPTY, ST_TARGET_BAD = 0x1, 0x2, 0x4
 EXPORTS = ("vrt_check_config", "vrt_tree_layout_of", "vrt_tree_bytes", "vrt_workspace_bytes",
-           "vrt_build_tree", "vrt_verify_tree", "vrt_verify_lazy", "vrt_verify_nodes", "vrt_verify_walk", "vrt_tree_mask",
+           "vrt_build_tree", "vrt_verify_tree", "vrt_verify_dense", "vrt_verify_lazy", "vrt_verify_nodes", "vrt_verify_walk", "vrt_tree_mask",
            "vrt_accepted_kv", "vrt_support_coverage", "vrt_read_probe", "vrt_last_error")
 
 
@@ -42,7 +42,8 @@ class TreeLayout(ctypes.Structure):
         "NC", "NR", "N", "TC", "FP", "cand_token", "cand_parent", "cand_score", "cand_kind",
         "row_tail_n", "row_tail_id", "row_tail_q", "front", "n_front", "smart", "admitted", "layer_sync",
         "n_nodes", "node_token", "node_parent", "node_depth", "node_kind", "node_cand",
-        "child_off", "child", "tail_n", "tail_id", "tail_q", "total_bytes")]
+        "child_off", "child", "tail_n", "tail_id", "tail_q", "row_dense", "row_det", "node_row",
+        "total_bytes")]
 
 
 _lib = None
@@ -71,6 +72,9 @@ def lib():
         L.vrt_verify_tree.argtypes = [P(Config), vp, i64, i64, vp, u64, u64, vp, sz, vp, vp, vp, vp,
                                       vp, vp]
         L.vrt_verify_tree.restype = i32
+        L.vrt_verify_dense.argtypes = [P(Config), vp, i64, i64, vp, i64, i64, vp, u64, u64, vp, sz, vp, vp,
+                                       vp, vp, vp, vp]
+        L.vrt_verify_dense.restype = i32
         L.vrt_verify_lazy.argtypes = [P(Config), vp, i64, i64, vp, u64, u64, vp, sz, vp, vp, vp, vp,
                                       vp, vp]
         L.vrt_verify_lazy.restype = i32
@@ -163,6 +167,17 @@ def verify_tree(cfg, target_logits, ld, tree_stride, tree, seed, step, ws, out_t
                                  _ptr(node_out), _stream(stream)))
 
 
+def verify_dense(cfg, target_logits, ld, tree_stride, draft_layers, draft_ld, draft_tree_stride, tree, seed,
+                 step, ws, out_tokens, out_nodes, out_len, stats, node_out=None, stream=None):
+    """vrt_verify_dense: draft_layers is a list of D device tensors, layer l's draft rows as
+    passed to build_tree."""
+    ptrs = (ctypes.c_void_p * len(draft_layers))(*[t.data_ptr() for t in draft_layers])
+    _check(lib().vrt_verify_dense(ctypes.byref(cfg), _ptr(target_logits), ld, tree_stride, ptrs, draft_ld,
+                                  draft_tree_stride, _ptr(tree), seed, step, _ptr(ws),
+                                  ws.numel() * ws.element_size(), _ptr(out_tokens), _ptr(out_nodes),
+                                  _ptr(out_len), _ptr(stats), _ptr(node_out), _stream(stream)))
+
+
 def verify_lazy(cfg, target_logits, ld, tree_stride, tree, seed, step, ws, out_tokens, out_nodes,
                 out_len, stats, node_out=None, stream=None):
     """vrt_verify_lazy: vrt_verify_tree's outputs, deciding only the nodes the walk reaches."""
@@ -221,6 +236,7 @@ _FIELDS = {
     "node_parent": ("i32", ("N",)), "node_depth": ("i32", ("N",)), "node_kind": ("i32", ("N",)),
     "node_cand": ("i32", ("N",)), "child_off": ("i32", ("N+1",)), "child": ("i32", ("N",)),
     "tail_n": ("i32", ("N",)), "tail_id": ("i32", ("N", "TC")), "tail_q": ("f32", ("N", "TC")),
+    "row_dense": ("f64", ("NRd", 2)), "row_det": ("i32", ("NRd", 32)), "node_row": ("i32", ("Nd",)),
 }
 
 
@@ -234,7 +250,14 @@ def tree_views(cfg, tree):
     for name, (t, shape) in _FIELDS.items():
         dims = []
         for d in shape:
-            dims.append(d if isinstance(d, int) else (getattr(L, "N") + 1 if d == "N+1" else getattr(L, d)))
+            if isinstance(d, int):
+                dims.append(d)
+            elif d == "N+1":
+                dims.append(L.N + 1)
+            elif d in ("NRd", "Nd"):  # dense-row arrays: empty unless trunc = DENSE
+                dims.append((L.NR if d == "NRd" else L.N) if cfg.trunc == DENSE else 0)
+            else:
+                dims.append(getattr(L, d))
         n = cfg.B
         for d in dims:
             n *= d
