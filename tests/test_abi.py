@@ -158,6 +158,25 @@ def test_lazy_verify_argument_errors_are_caught_before_any_launch():
                              None) == vrt.EINVAL
 
 
+def test_dense_verify_argument_errors_are_caught_before_any_launch():
+    c = vrt.make_config(B=2, V=1000, K=4, D=3, R=10, trunc=vrt.DENSE)
+    L = vrt.lib()
+    v = ctypes.c_void_p
+    good_layers = (ctypes.c_void_p * 3)(0x80000, 0x90000, 0xA0000)
+
+    def call(cfg=c, layers=good_layers, dld=1024, dstride=4096 * 10, t=0x10000):
+        return L.vrt_verify_dense(ctypes.byref(cfg), v(t), 1024, 4096, layers, dld, dstride, v(0x20000), 1, 0,
+                                  v(0x30000), 1 << 30, v(0x40000), v(0x50000), v(0x60000), v(0x70000), None,
+                                  None)
+    assert call(layers=None) == vrt.EINVAL
+    assert call(dld=10) == vrt.EINVAL
+    assert call(layers=(ctypes.c_void_p * 3)(0x80000, 0x90008, 0xA0000)) == vrt.EINVAL
+    assert call(layers=(ctypes.c_void_p * 3)(0x80000, None, 0xA0000)) == vrt.EINVAL
+    assert call(t=0) == vrt.EINVAL
+    truncated = vrt.make_config(B=2, V=1000, K=4, D=3, R=10)
+    assert call(cfg=truncated) == vrt.EINVAL and "VRT_DENSE" in vrt.last_error()
+
+
 def test_split_verify_argument_errors_are_caught_before_any_launch():
     c = vrt.make_config(B=2, V=1000, K=4, D=3, R=10)
     L = vrt.lib()
