@@ -720,28 +720,25 @@ __device__ void decide_node(const VArgs& a, int b, int i, const char* row, const
       src2 = pos ? 63 - __builtin_clzll(pos) : 0;
       clamp2 = true;
     }
-    if (lane == src2) {
-      double cum = lexcl;
-      int tok = -1;
-      double b0 = cum, b1 = cum;
-#pragma unroll 4
-      for (int k = 0; k < 32; ++k) {
-        const float wk = sw[k];
-        if (wk > 0.0f) {
-          tok = my0 + k;
-          b0 = cum;
-          b1 = cum + (double)wk;
-          if (!clamp2 && tgt < b1) break;
-        }
-        cum += (double)wk;
-      }
-      if (tok < 0) tok = min(my0, V - 1);
-      out.token = tok;
-      if (W > 0.0 && (fabs((double)uf - b0 / W) < kBand || fabs((double)uf - b1 / W) < kBand))
-        ++near;
+    // the token: lane src2's 32 weights, one per lane, scanned by the whole wave; the
+    // first with weight whose inclusive sum passes tgt (clamped, or if rounding leaves
+    // none: the last with weight)
+    const float wk = lane < 32 ? L.w[src2 * 33 + lane] : 0.0f;
+    const double kincl = wave_incl_scan((double)wk) + __shfl(lexcl, src2, kWave);
+    const uint64_t pos = ballot(wk > 0.0f);
+    const uint64_t hit3 = clamp2 ? 0ull : ballot(wk > 0.0f && tgt < kincl);
+    const int kk = hit3 ? __builtin_ctzll(hit3) : (pos ? 63 - __builtin_clzll(pos) : -1);
+    const int base_tok = lo + src2 * 32;
+    if (kk >= 0) {
+      const double b1 = __shfl(kincl, kk, kWave);
+      const double b0 = b1 - (double)__shfl(wk, kk, kWave);
+      out.token = base_tok + kk;
+      if (W > 0.0 && (fabs((double)uf - b0 / W) < kBand || fabs((double)uf - b1 / W) < kBand)) ++near;
+    } else {
+      out.token = min(base_tok, V - 1);
+      const double b = __shfl(lexcl, src2, kWave);
+      if (W > 0.0 && fabs((double)uf - b / W) < kBand) ++near;
     }
-    out.token = __shfl(out.token, src2, kWave);
-    near = __shfl(near, src2, kWave);
   }
   out.accept = accept;
   out.flags = min(tests, 255) | (min(near, 255) << 8);
