@@ -509,133 +509,140 @@ __device__ void decide_node(const VArgs& a, int b, int i, const char* row, const
   const double wc = (in_tail && !last) ? (pc > q_child ? pc - q_child : 0.0) : pc;
   const float uc = r_u;
 
-  // ---- the final residual (or bonus) sample is taken only if every test rejects, and
-  // then it runs against the residual with all of them rejected: located now, its
-  // chunk's re-read overlaps the tests. Inverse CDF of w / W in token-id order.
-  double Wf = W;
-  if (last) Wf = WD - overlap;
-  else
-    for (uint64_t m = cmask; m; m &= m - 1ull) Wf -= readlane_d(wc, __builtin_ctzll(m));
+  // ---- the final residual (or bonus) sample's preparation: the residual's chunk masses,
+  // the chunk holding u * Wf, its re-read issued, and the residual's changes inside it.
+  // Taken only if every test rejects, against the residual with all of them rejected.
+  // (Preparing it before the tests, so that the re-read overlaps them, measured the same
+  // for the full pass and slower for the lazy walk.)
   const float uf = R.uf;
-  const double tgt = (double)uf * Wf;
-  for (int ch = lane; ch < nch; ch += kWave) L.dfix[ch] = 0;
-  wave_sync();
-  // changes of mass relative to p: the probe's tail (clipped residual, or zero for a
-  // rejected child) and the rejected children outside it (zero). Fixed-point atomics
-  // keep the per-chunk sums independent of the order of arrival. Dense rows: the tail's
-  // clipping is the overlap pass's per-chunk sums, and each rejected child removes its
-  // residual w (its p off the tail).
-  if (!DENSE && probe >= 0) {
-    for (int e = lane; e < nt; e += kWave) {
-      const int y = L.tid[e];
-      if (y < 0) continue;
-      const double p = L.tp[e], q = qscale * (double)L.tq[e];
-      const int slot = L.tslot[e];
-      const bool rej = slot >= 0 && ((cmask >> slot) & 1ull);
-      const double d = rej ? -p : -(p < q ? p : q);
-      atomicAdd((unsigned long long*)&L.dfix[y / kCH], (unsigned long long)__double2ll_rn(d * kFix));
-    }
-  }
-  const bool mine = DENSE ? cand : (cand && !in_tail);
-  const double mdel = (DENSE && in_tail) ? -wc : -pc;
-  if (mine) atomicAdd((unsigned long long*)&L.dfix[ch_tok / kCH], (unsigned long long)__double2ll_rn(mdel * kFix));
-  wave_sync();
-  // adjusted chunk masses, lane-blocked contiguous chunks
-  const int cpl = (nch + kWave - 1) / kWave;
-  const int c0 = lane * cpl, c1 = min(c0 + cpl, nch);
-  double lmass = 0.0;
-  for (int ch = c0; ch < c1; ++ch) {
-    double mch = L.pm[ch] * invS + (double)L.dfix[ch] * (1.0 / kFix);
-    if (dense_tail) mch -= L.ov[ch];
-    if (mch < 0.0) mch = 0.0;
-    L.pm[ch] = mch;
-    lmass += mch;
-  }
-  const double incl = wave_incl_scan(lmass);
-  const double excl = incl - lmass;
-  // lane holding the crossing chunk; if rounding leaves none, the last lane with mass
-  const uint64_t hit = ballot(tgt < incl && lmass > 0.0);
-  int src = hit ? __builtin_ctzll(hit) : -1;
-  bool clamp = false;
-  if (src < 0) {
-    const uint64_t pos = ballot(lmass > 0.0);
-    src = pos ? 63 - __builtin_clzll(pos) : 0;
-    clamp = true;
-  }
-  int cstar = -1;
-  double before = 0.0;
-  if (lane == src) {
-    double cum = excl;
-    for (int ch = c0; ch < c1; ++ch) {
-      if (L.pm[ch] > 0.0) {
-        cstar = ch;
-        before = cum;
-        if (!clamp && tgt < cum + L.pm[ch]) break;
-      }
-      cum += L.pm[ch];
-    }
-    if (cstar < 0) cstar = c0 < nch ? c0 : nch - 1;
-  }
-  cstar = __shfl(cstar, src, kWave);
-  before = __shfl(before, src, kWave);
-  const int lo = cstar * kCH;
-  // re-read the chunk (issued now, consumed after the tests); lane l owns tokens
-  // [lo + 32 l, lo + 32 l + 32)
   constexpr int esz = DT == VRT_BF16 ? 2 : 4;
   constexpr int EPL = 16 / esz;
-  const int my0 = lo + lane * 32;
+  double tgt = 0.0, before = 0.0;
+  bool clamp = false;
+  int lo = 0, my0 = 0, nitem = 0;
   u32x4_t raw[32 / EPL];
-  static_for<32 / EPL>([&](auto q) {
-    const int e0 = my0 + q * EPL;
-    raw[q] = u32x4_t{0u, 0u, 0u, 0u};
-    if (e0 < V) raw[q] = *(const u32x4_t*)(row + (int64_t)e0 * esz);
-  });
   u32x4_t rawd[DENSE ? 32 / EPL : 1];  // dense rows: the same tokens of the draft row
-  if constexpr (DENSE) {
+  const double W0 = W;  // the residual mass the tests start from
+  auto prepare_final = [&]() {
+    double Wf = W0;
+    if (last) Wf = WD - overlap;
+    else
+      for (uint64_t m = cmask; m; m &= m - 1ull) Wf -= readlane_d(wc, __builtin_ctzll(m));
+    tgt = (double)uf * Wf;
+    for (int ch = lane; ch < nch; ch += kWave) L.dfix[ch] = 0;
+    wave_sync();
+    // changes of mass relative to p: the probe's tail (clipped residual, or zero for a
+    // rejected child) and the rejected children outside it (zero). Fixed-point atomics
+    // keep the per-chunk sums independent of the order of arrival. Dense rows: the tail's
+    // clipping is the overlap pass's per-chunk sums, and each rejected child removes its
+    // residual w (its p off the tail).
+    if (!DENSE && probe >= 0) {
+      for (int e = lane; e < nt; e += kWave) {
+        const int y = L.tid[e];
+        if (y < 0) continue;
+        const double p = L.tp[e], q = qscale * (double)L.tq[e];
+        const int slot = L.tslot[e];
+        const bool rej = slot >= 0 && ((cmask >> slot) & 1ull);
+        const double d = rej ? -p : -(p < q ? p : q);
+        atomicAdd((unsigned long long*)&L.dfix[y / kCH], (unsigned long long)__double2ll_rn(d * kFix));
+      }
+    }
+    const bool mine = DENSE ? cand : (cand && !in_tail);
+    const double mdel = (DENSE && in_tail) ? -wc : -pc;
+    if (mine) atomicAdd((unsigned long long*)&L.dfix[ch_tok / kCH], (unsigned long long)__double2ll_rn(mdel * kFix));
+    wave_sync();
+    // adjusted chunk masses, lane-blocked contiguous chunks
+    const int cpl = (nch + kWave - 1) / kWave;
+    const int c0 = lane * cpl, c1 = min(c0 + cpl, nch);
+    double lmass = 0.0;
+    for (int ch = c0; ch < c1; ++ch) {
+      double mch = L.pm[ch] * invS + (double)L.dfix[ch] * (1.0 / kFix);
+      if (dense_tail) mch -= L.ov[ch];
+      if (mch < 0.0) mch = 0.0;
+      L.pm[ch] = mch;
+      lmass += mch;
+    }
+    const double incl = wave_incl_scan(lmass);
+    const double excl = incl - lmass;
+    // lane holding the crossing chunk; if rounding leaves none, the last lane with mass
+    const uint64_t hit = ballot(tgt < incl && lmass > 0.0);
+    int src = hit ? __builtin_ctzll(hit) : -1;
+    clamp = false;
+    if (src < 0) {
+      const uint64_t pos = ballot(lmass > 0.0);
+      src = pos ? 63 - __builtin_clzll(pos) : 0;
+      clamp = true;
+    }
+    int cstar = -1;
+    before = 0.0;
+    if (lane == src) {
+      double cum = excl;
+      for (int ch = c0; ch < c1; ++ch) {
+        if (L.pm[ch] > 0.0) {
+          cstar = ch;
+          before = cum;
+          if (!clamp && tgt < cum + L.pm[ch]) break;
+        }
+        cum += L.pm[ch];
+      }
+      if (cstar < 0) cstar = c0 < nch ? c0 : nch - 1;
+    }
+    cstar = __shfl(cstar, src, kWave);
+    before = __shfl(before, src, kWave);
+    lo = cstar * kCH;
+    // re-read the chunk; lane l owns tokens [lo + 32 l, lo + 32 l + 32)
+    my0 = lo + lane * 32;
     static_for<32 / EPL>([&](auto q) {
       const int e0 = my0 + q * EPL;
-      rawd[q] = u32x4_t{0u, 0u, 0u, 0u};
-      if (dense_tail && e0 < V) rawd[q] = *(const u32x4_t*)(R.drow + (int64_t)e0 * esz);
+      raw[q] = u32x4_t{0u, 0u, 0u, 0u};
+      if (e0 < V) raw[q] = *(const u32x4_t*)(row + (int64_t)e0 * esz);
     });
-  }
-  // the changes that fall inside the chunk, listed for the owners of their tokens
-  int nitem = 0;
-  wave_sync();
-  if (!DENSE && probe >= 0) {
-    for (int e0 = 0; e0 < nt; e0 += kWave) {
-      const int e = e0 + lane;
-      bool inside = false;
-      int y = -1;
-      double d = 0.0;
-      if (e < nt) {
-        y = L.tid[e];
-        inside = y >= lo && y < lo + kCH;
-        if (inside) {
-          const double p = L.tp[e], q = qscale * (double)L.tq[e];
-          const int slot = L.tslot[e];
-          const bool rej = slot >= 0 && ((cmask >> slot) & 1ull);
-          d = rej ? -p : -(p < q ? p : q);
+    if constexpr (DENSE) {
+      static_for<32 / EPL>([&](auto q) {
+        const int e0 = my0 + q * EPL;
+        rawd[q] = u32x4_t{0u, 0u, 0u, 0u};
+        if (dense_tail && e0 < V) rawd[q] = *(const u32x4_t*)(R.drow + (int64_t)e0 * esz);
+      });
+    }
+    // the changes that fall inside the chunk, listed for the owners of their tokens
+    nitem = 0;
+    wave_sync();
+    if (!DENSE && probe >= 0) {
+      for (int e0 = 0; e0 < nt; e0 += kWave) {
+        const int e = e0 + lane;
+        bool inside = false;
+        int y = -1;
+        double d = 0.0;
+        if (e < nt) {
+          y = L.tid[e];
+          inside = y >= lo && y < lo + kCH;
+          if (inside) {
+            const double p = L.tp[e], q = qscale * (double)L.tq[e];
+            const int slot = L.tslot[e];
+            const bool rej = slot >= 0 && ((cmask >> slot) & 1ull);
+            d = rej ? -p : -(p < q ? p : q);
+          }
         }
+        const uint64_t m = ballot(inside);
+        if (inside) {
+          const int at = nitem + (int)__builtin_popcountll(m & ((1ull << lane) - 1ull));
+          L.itok[at] = y;
+          L.idel[at] = d;
+        }
+        nitem += (int)__builtin_popcountll(m);
       }
+    }
+    {
+      const bool inside = mine && ch_tok >= lo && ch_tok < lo + kCH;
       const uint64_t m = ballot(inside);
       if (inside) {
         const int at = nitem + (int)__builtin_popcountll(m & ((1ull << lane) - 1ull));
-        L.itok[at] = y;
-        L.idel[at] = d;
+        L.itok[at] = ch_tok;
+        L.idel[at] = mdel;
       }
       nitem += (int)__builtin_popcountll(m);
     }
-  }
-  {
-    const bool inside = mine && ch_tok >= lo && ch_tok < lo + kCH;
-    const uint64_t m = ballot(inside);
-    if (inside) {
-      const int at = nitem + (int)__builtin_popcountll(m & ((1ull << lane) - 1ull));
-      L.itok[at] = ch_tok;
-      L.idel[at] = mdel;
-    }
-    nitem += (int)__builtin_popcountll(m);
-  }
+  };
 
   // ---- the tests: the probe with min(1, p/(s q~)) (first, or after the others), the
   // others under the residual
@@ -670,8 +677,10 @@ __device__ void decide_node(const VArgs& a, int b, int i, const char* row, const
     W = WD - overlap;  // the mass the final sample runs against
   }
 
-  // ---- nothing accepted: finish the final sample in the re-read chunk (W == Wf now)
+  // ---- nothing accepted: the final residual (or bonus) sample, inverse CDF of w / W in
+  // token-id order against the residual with every test rejected (W == Wf now)
   if (accept < 0) {
+    prepare_final();
     float* sw = L.w + lane * 33;  // stride 33: conflict-free per-lane walks
     {
       const float invSf = (float)invS;
