@@ -11,6 +11,7 @@ in the verification parity tests, and the emitted tokens.
 import numpy as np
 import pytest
 
+import synth
 from synth import workloads
 from tests.gpu_common import device_step
 from tests.harness import OracleStep
@@ -28,6 +29,9 @@ CASES = [
     ("stress_B256_m0", workloads.get("stress", m=0), [5, 200], (4, 2)),
     ("stress_B256_m3", workloads.get("stress", m=3), [77, 170], (5, 9)),
     ("headline_probe_last", workloads.get("headline", order=1), [0, 17, 31], (6, 1)),
+    # fp32 logits at the full vocabulary: every draft row takes the exact selection path
+    ("headline_fp32", workloads.get("headline", dtype=synth.F32, B=8),
+     [0, 7], (8, 5)),
 ]
 
 
