@@ -59,6 +59,10 @@ CASES = [
     ("small_probe_last_m0_T06", _small(order=1, m=0, T=0.6, trunc=256, V=3000)),
     ("small_probe_last_trunc4", _small(order=1, V=300, trunc=4, K=3, R=12, D=4)),
     ("small_probe_last_fp32_K1", _small(order=1, dtype=synth.F32, K=1, m=0, R=6, D=5)),
+    ("edge_R1_D1", _small(R=1, D=1)),
+    ("edge_W1_beam", _small(W=1, R=8, D=6)),
+    ("edge_K1_probe_only", _small(K=1, m=0, R=5, D=5)),
+    ("edge_R_below_K", _small(R=3, D=4)),
     ("smart_small", _smart_small()),
     ("smart_small_m0_alpha08", _smart_small(m=0, alpha=0.8, budget=24)),
 ]
