@@ -289,13 +289,18 @@ __device__ __forceinline__ int row_select_fast(const char* row, int g0, int g1, 
   const int dsel = F.sel[0];
   uint32_t pre = 0u;   // image bits fixed so far (the high ones)
   if (dsel >= 0) {
-    // smallest image in bins 0..dsel: dist(lo) is outside (or NaN), dist(hi) inside
+    // smallest image in bins 0..dsel: dist(lo) is outside (or NaN), dist(hi) inside; a
+    // 64-way search, each lane testing one point per round (the inside points form a
+    // suffix: the distance falls as the image grows)
     const float lim = (float)(dsel + 1);
     uint32_t lo = BF ? 0x007Eu : 0x007FFFFEu, hi = M;
     while (hi - lo > 1u) {
-      const uint32_t mid = lo + ((hi - lo) >> 1);
-      if (dist(mid) < lim) hi = mid;
-      else lo = mid;
+      const uint64_t step = ((uint64_t)(hi - lo) + 63u) / 64u;
+      const uint64_t pt = (uint64_t)lo + (uint64_t)(lane + 1) * step;  // the last lane's >= hi
+      const uint64_t in = ballot(pt >= hi || dist((uint32_t)pt) < lim);
+      const int f = __builtin_ctzll(in);
+      hi = (uint32_t)min((uint64_t)hi, (uint64_t)lo + (uint64_t)(f + 1) * step);
+      lo = (uint32_t)((uint64_t)lo + (uint64_t)f * step);
     }
     pre = hi;
   } else {
