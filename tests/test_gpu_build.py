@@ -51,6 +51,9 @@ CASES = [
     ("stress_mixed_m0", _small(B=4, V=9000, zipf=(1.5, 0.8), split=2, R=64, D=6, K=8, m=0)),
     ("small_trunc512_fp32", _small(trunc=512, V=20000, dtype=synth.F32, R=30, D=4)),
     ("small_trunc1024", _small(trunc=1024, V=20000, R=30, D=3, K=12)),
+    ("small_trunc1024_flat_fp32", _small(trunc=1024, V=30000, dtype=synth.F32, zipf=(0.8,), R=30, D=3)),
+    ("small_trunc700_flat", _small(trunc=700, V=12000, zipf=(0.8,), R=24, D=3)),
+    ("small_trunc513_V1500", _small(trunc=513, V=1500, R=24, D=3)),
     ("small_all_ties", _small(zipf=(), draft_scale=0.0, V=9000, R=20, D=3)),
     ("small_all_ties_fp32_trunc256", _small(zipf=(), draft_scale=0.0, V=9000, R=20, D=3,
                                            dtype=synth.F32, trunc=256)),

@@ -515,34 +515,80 @@ __device__ __forceinline__ int row_select_fast(const char* row, int g0, int g1, 
   if (nk > FL::KCAP) floor_img = pre;  // at least TC row elements reach t
   if (nk > FL::KCAP || nk < TC) return 2;
 
-  // D. Lists of 512 keys or more: the waves sort slices of N staged keys in registers
-  // and merge them pairwise through LDS, keeping the top N (ranking every key against
-  // every other would cost nk^2 LDS reads).
+  // D. Lists of 512 keys or more: every wave sorts 256-key slices of the staged keys in
+  // registers, then rounds of pairwise merges in LDS keep the top N of each pair (ranking
+  // every key against every other would cost nk^2 LDS reads). A merge writes output k of
+  // a pair from its co-rank (a binary search over the two sorted inputs, "merge path");
+  // each thread holds its outputs in registers until the whole round has read its inputs,
+  // so the outputs overwrite them in place.
   if constexpr (PL >= 8) {
-    uint64_t k[PL];
-    const int base = wave * N;
-    static_for<PL>([&](auto s) {
-      const int p = base + lane * PL + (int)s;
-      k[s] = p < nk ? F.keys[p] : 0ull;
-    });
-    if (base < nk) wave_sort_desc<PL>(k);  // uniform
-    __syncthreads();  // every slice is in registers: the staging area holds the lists now
-    for (int st = 1; st < SW; st <<= 1) {
-      uint64_t* list = F.keys + (wave / (2 * st)) * N;
-      if ((wave & (2 * st - 1)) == st) static_for<PL>([&](auto s) { list[lane * PL + s] = k[s]; });
-      __syncthreads();
-      if ((wave & (2 * st - 1)) == 0 && (wave + st) * N < nk) {
-        uint64_t o[PL];
-        static_for<PL>([&](auto s) { o[s] = list[lane * PL + s]; });
-        wave_merge_top<PL>(k, o);
-      }
-      __syncthreads();
-    }
-    if (wave == 0)
-      static_for<PL>([&](auto s) {
-        const int p = lane * PL + (int)s;
-        s_sup[p] = p < TC ? k[s] : 0ull;
+    constexpr int QS = 256;                  // keys per slice: 4 per lane
+    constexpr int MO = FL::KCAP / NT;        // outputs per thread and round, at most
+    const int ns = (nk + QS - 1) / QS;       // slices (<= KCAP / QS)
+    for (int sl = wave; sl < ns; sl += SW) {  // uniform per wave
+      uint64_t k[QS / kWave];
+      static_for<QS / kWave>([&](auto q) {
+        const int p = sl * QS + lane * (QS / kWave) + (int)q;
+        k[q] = p < nk ? F.keys[p] : 0ull;
       });
+      wave_sort_desc<QS / kWave>(k);
+      static_for<QS / kWave>([&](auto q) { F.keys[sl * QS + lane * (QS / kWave) + q] = k[q]; });
+    }
+    __syncthreads();
+    // round r: list i starts at i * QS * 2^r
+    int nl = ns;
+    int stride = QS;
+    while (nl > 1) {  // uniform
+      const int np = nl / 2;  // pairs merged this round
+      uint64_t out[MO];
+      int opos[MO];
+      static_for<MO>([&](auto u) { opos[u] = -1; });
+      // list li holds the top min(N, keys it covers) of the staged keys it covers; pair
+      // q's outputs follow those of the pairs before it
+      int total = 0;
+      auto len_of = [&](int li) {
+        const int start = li * stride;
+        const int rest = nk - start;  // keys a list covers before capping
+        return max(0, min(min(rest, stride), N));
+      };
+      for (int q = 0; q < np; ++q) total += min(len_of(2 * q) + len_of(2 * q + 1), N);
+      static_for<MO>([&](auto u) {
+        const int gk = tid + (int)u * NT;  // this thread's output index in the round
+        if (gk < total) {
+          int q = 0, before = 0;
+          while (true) {
+            const int cq = min(len_of(2 * q) + len_of(2 * q + 1), N);
+            if (gk < before + cq) break;
+            before += cq;
+            ++q;
+          }
+          const int kk = gk - before;
+          const uint64_t* A = F.keys + (2 * q) * stride;
+          const uint64_t* Bv = F.keys + (2 * q + 1) * stride;
+          const int na = len_of(2 * q), nb = len_of(2 * q + 1);
+          int lo = max(0, kk - nb), hi = min(kk, na);  // A's share of the kk keys above
+          while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (A[mid] > Bv[kk - mid - 1]) lo = mid + 1;
+            else hi = mid;
+          }
+          const int ia = lo, ib = kk - lo;
+          const bool fromA = ib >= nb || (ia < na && A[ia] > Bv[ib]);
+          out[u] = fromA ? A[ia] : Bv[ib];
+          opos[u] = (2 * q) * stride + kk;
+        }
+      });
+      __syncthreads();  // the round's inputs are read
+      static_for<MO>([&](auto u) {
+        if (opos[u] >= 0) F.keys[opos[u]] = out[u];
+      });
+      // an odd last list (index nl-1, even) already starts where list (nl-1)/2 of the
+      // next round does: it stays in place
+      __syncthreads();
+      nl = (nl + 1) / 2;
+      stride *= 2;
+    }
+    for (int p = tid; p < N; p += NT) s_sup[p] = (p < TC && p < nk) ? F.keys[p] : 0ull;
     n_sup = TC;
     __syncthreads();
     return 0;
