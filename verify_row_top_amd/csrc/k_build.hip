@@ -164,7 +164,10 @@ constexpr float kDistScale = 64.0f;
 template <int DT, int PL>
 struct FastLds {
   static constexpr int LV = 4;                         // candidates per lane and segment
-  static constexpr int KCAP = 4 * PL * kWave;          // staged keys held (4N)
+  // staged keys held: 4N, 6N for supports of 1024 keys (bf16 rows hold many ties near
+  // their 1024th value: 4N staged keys overflowed on a few rows in a hundred; 6N keeps
+  // the block's LDS small enough for two blocks per CU)
+  static constexpr int KCAP = (PL >= 16 ? 6 : 4) * PL * kWave;
   // a candidate: group maximum's image << 8 | its load index q
   using CK = std::conditional_t<DT == VRT_BF16, uint32_t, uint64_t>;
   alignas(16) uint64_t keys[KCAP];        // row keys of the elements that reach it
