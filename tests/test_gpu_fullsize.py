@@ -29,6 +29,10 @@ CASES = [
     ("stress_B256_m0", workloads.get("stress", m=0), [5, 200], (4, 2)),
     ("stress_B256_m3", workloads.get("stress", m=3), [77, 170], (5, 9)),
     ("headline_probe_last", workloads.get("headline", order=1), [0, 17, 31], (6, 1)),
+    # long supports at the full vocabulary: bf16 rows whose ties near the cut stage more
+    # than four keys per support entry
+    ("headline_trunc512", workloads.get("headline", trunc=512), [3, 16, 29], (9, 4)),
+    ("headline_trunc1024", workloads.get("headline", trunc=1024), [0, 19, 31], (7, 2)),
     # fp32 logits at the full vocabulary: every draft row takes the exact selection path
     ("headline_fp32", workloads.get("headline", dtype=synth.F32, B=8),
      [0, 7], (8, 5)),

@@ -189,7 +189,8 @@ struct FastLds {
 //  C. each thread re-reads its candidate groups that reach t (16 bytes each, all in
 //     flight; where all LV candidates of a lane-segment reach t, its other groups that
 //     do too) and stages the exact keys of their elements that reach t;
-//  D. each staged key's rank among them (the keys are distinct) places it in s_sup.
+//  D. the staged keys are distinct: below 512-key supports each one's rank among them
+//     places it in s_sup; from 512 keys on, sorted 256-key slices are merged pairwise.
 // Returns 0 on success, 1 for a non-finite row, 2 when more keys reach t than the path
 // holds (ties, flat rows; floor_img is then t's image) or fewer than TC (tiny rows):
 // the caller then takes the exact path. The result is uniform over the block.
