@@ -154,7 +154,11 @@ typedef struct {
  *   row_det     i32 [B][NR][32]  tokens of the deterministic children (the t0 best:
  *                                the top m, or probe last the top K-1)
  *   node_row    i32 [B][N]       expansion row of node i if its probe child is kept,
- *                                else -1 */
+ *                                else -1
+ * Build scratch:
+ *   row_sync    i32 [B][FP]  halves of each row of the current layer done, where a
+ *                            layer's rows are split over two blocks (set to 0 by
+ *                            layer 0 and by the block that completes each row) */
 typedef struct {
   int64_t NC, NR, N, TC, FP;
   int64_t cand_token, cand_parent, cand_score, cand_kind;
@@ -163,6 +167,7 @@ typedef struct {
   int64_t n_nodes, node_token, node_parent, node_depth, node_kind, node_cand;
   int64_t child_off, child, tail_n, tail_id, tail_q;
   int64_t row_dense, row_det, node_row;
+  int64_t row_sync;
   int64_t total_bytes;
 } vrt_tree_layout;
 

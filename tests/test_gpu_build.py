@@ -54,6 +54,10 @@ CASES = [
     ("small_trunc1024_flat_fp32", _small(trunc=1024, V=30000, dtype=synth.F32, zipf=(0.8,), R=30, D=3)),
     ("small_trunc700_flat", _small(trunc=700, V=12000, zipf=(0.8,), R=24, D=3)),
     ("small_trunc513_V1500", _small(trunc=513, V=1500, R=24, D=3)),
+    # rows too long for one block's row-wide path: split over two blocks after layer 0
+    ("split_fp32_V70000", _small(dtype=synth.F32, V=70000, R=30, D=4)),
+    ("split_bf16_V200000_trunc256", _small(V=200000, R=30, D=3, trunc=256)),
+    ("split_fp32_flat_ties", _small(dtype=synth.F32, V=66000, zipf=(), draft_scale=0.0, R=20, D=3)),
     ("small_all_ties", _small(zipf=(), draft_scale=0.0, V=9000, R=20, D=3)),
     ("small_all_ties_fp32_trunc256", _small(zipf=(), draft_scale=0.0, V=9000, R=20, D=3,
                                            dtype=synth.F32, trunc=256)),
@@ -173,6 +177,22 @@ def test_bad_draft_rows_set_status_and_stay_in_bounds(gpu, kw):
     assert st[0] & 0x1 and st[1] & 0x2 and st[2] == 0
     n = L.views["n_nodes"].cpu().numpy()
     assert n[0] == 1 and n[1] == 1 and n[2] > 1
+
+
+def test_bad_rows_of_split_layers_set_status(gpu):
+    """A NaN in the second half of a row split over two blocks flags its tree."""
+    w = _small(B=2, D=2, R=10, dtype=synth.F32, V=70001)
+    steps = [OracleStep(w, 5, b, 0, verify=False) for b in range(w.B)]
+    L = Lib(lib_config(w), gpu)
+    rows, ld = to_device_rows([s.layer_rows[0] for s in steps], w, 1, gpu)
+    L.build_layer(0, rows, ld, 5, 0)
+    r1 = [s.layer_rows[1].copy() for s in steps]
+    r1[0][0, 60000] = np.nan
+    rows1, _ = to_device_rows(r1, w, L.FP, gpu)
+    L.build_layer(1, rows1, ld, 5, 0)
+    L.finish()
+    st = L.stats.cpu().numpy()[:, 0]
+    assert st[0] & 0x1 and st[1] == 0
 
 
 def test_split_verification_equals_the_whole_call(gpu):

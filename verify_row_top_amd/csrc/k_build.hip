@@ -54,6 +54,9 @@ struct BArgs {
   uint32_t step;
   uint32_t* stats;
   int fuse_rank;  // the layer's ranking runs in its row blocks
+  int split;      // blocks per row: 1, or 2 (each selects from half of the row's segments)
+  uint64_t* half_keys;  // split rows: [B][FP][2][list length] each half's sorted support
+  int* half_meta;       // split rows: [B][FP][2] each half's support size | non-finite << 30
 };
 
 // The node frontier position j of tree b expands at this layer (-1 = root), or -2
@@ -77,6 +80,10 @@ template <int DT>
 constexpr int seg_elems() { return kWave * kSegLoads * (DT == VRT_BF16 ? 8 : 4); }
 
 constexpr int kSelWaves = 8;  // waves of a row block
+// segments per wave the row-wide path of a row block takes (rows up to 24 bf16 or 16 fp32
+// segments; longer rows are split over two blocks, or take the exact path)
+template <int DT>
+constexpr int seg_per_wave() { return DT == VRT_BF16 ? 3 : 2; }
 
 __device__ __forceinline__ float max3n(float a, float b, float c) {  // NaN-propagating
   return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
@@ -955,6 +962,7 @@ __device__ __forceinline__ int begin_row(const BArgs& a, int b, int j) {
   const int64_t ncb = (int64_t)b * c.NC;
   if (a.layer == 0 && wave == 0) {
     for (int t = c.K + lane; t < c.NC; t += kWave) a.t.cand_kind[ncb + t] = 0;
+    for (int t = lane; t < c.FP; t += kWave) a.t.row_sync[(int64_t)b * c.FP + t] = 0;
     if (lane == 0) {
       double* sm = a.t.smart + (int64_t)b * 8;
       sm[0] = 0.0; sm[1] = 1.0; sm[2] = 1.0; sm[3] = 0.0; sm[4] = 0.0;
@@ -1026,12 +1034,13 @@ __device__ __forceinline__ void rank_wave(const BArgs& a, int b, uint64_t* s_ran
 
 __device__ __forceinline__ void rank_if_last(const BArgs& a, int b, uint64_t* s_rank) {
   const int lane = lane_id();
-  if (gridDim.x > 1) {
+  const int rows = (int)gridDim.x / a.split;
+  if (rows > 1) {
     wait_stores();
     int old = 0;
     if (lane == 0) old = atomicAdd(&a.t.layer_sync[b], 1);
     old = __shfl(old, 0, kWave);
-    if (old != (int)gridDim.x - 1) return;
+    if (old != rows - 1) return;
   }
   const int span = layer_span(a.c, a.layer);
   if (span <= kWave) rank_wave<1>(a, b, s_rank);
@@ -1040,25 +1049,74 @@ __device__ __forceinline__ void rank_if_last(const BArgs& a, int b, uint64_t* s_
   if (lane == 0) a.t.layer_sync[b] = 0;
 }
 
-// One block per expanded parent, then wave 0 expands it: the row-wide path, the exact
-// path behind it (ties, flat rows, rows longer than the row-wide path covers).
+__device__ __forceinline__ void st_dev64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_dev64(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// A row split over two blocks, wave 0 of each: every block has the top TC of its half
+// of the row in s_sup (n_sup keys, sorted); the row's top TC are among the two lists.
+// Each block writes its list and status device-coherently, waits for the stores and
+// counts itself on the row's row_sync word; the first to arrive is done (returns
+// false), the second merges the other's list into its own and combines the status.
+// It sets the word back to 0 for the next layer; layer 0 starts it at 0.
+template <int PL>
+__device__ __forceinline__ bool join_halves(const BArgs& a, int b, int j, int h, int& n_sup,
+                                            int& any_bad, uint64_t* s_sup) {
+  const Cfg& c = a.c;
+  constexpr int N = PL * kWave;
+  const int lane = lane_id();
+  const int64_t r = (int64_t)b * c.FP + j;
+  uint64_t* mine = a.half_keys + (r * 2 + h) * N;
+  static_for<PL>([&](auto s) { st_dev64(&mine[lane * PL + s], s_sup[lane * PL + s]); });
+  if (lane == 0) st_dev(&a.half_meta[r * 2 + h], n_sup | (any_bad << 30));
+  wait_stores();
+  int old = 0;
+  if (lane == 0) old = atomicAdd(&a.t.row_sync[r], 1);
+  old = __shfl(old, 0, kWave);
+  if (old == 0) return false;
+  const uint64_t* other = a.half_keys + (r * 2 + (1 - h)) * N;
+  const int om = ld_dev(&a.half_meta[r * 2 + (1 - h)]);
+  uint64_t top[PL], add[PL];
+  static_for<PL>([&](auto s) {
+    top[s] = s_sup[lane * PL + s];
+    add[s] = ld_dev64(&other[lane * PL + s]);
+  });
+  wave_merge_top<PL>(top, add);
+  static_for<PL>([&](auto s) {
+    const int p = lane * PL + s;
+    s_sup[p] = p < c.TC ? top[s] : 0ull;
+  });
+  n_sup = min(c.TC, n_sup + (om & 0xFFFF));
+  any_bad |= (om >> 30) & 1;
+  if (lane == 0) st_dev(&a.t.row_sync[r], 0);
+  wave_sync();
+  return true;
+}
+
+// One block per expanded parent (or two, each on half of the row's segments, joined by
+// join_halves), then wave 0 expands it: the row-wide path, the exact path behind it
+// (ties, flat rows, rows longer than the row-wide path covers).
 template <int DT, int PL>
 __global__ __launch_bounds__(kSelWaves * kWave)
 __attribute__((amdgpu_waves_per_eu(PL == 2 ? 4 : 2, 8))) void k_select_expand(const BArgs a) {
   const Cfg& c = a.c;
-  const int j = blockIdx.x, b = blockIdx.y;
+  const int S = a.split;
+  const int j = blockIdx.x / S, h = blockIdx.x % S, b = blockIdx.y;
   const int wave = threadIdx.x >> 6;
   constexpr int N = PL * kWave;
   __shared__ uint64_t s_rank[kRankFused];
   const int node = begin_row(a, b, j);
   if (node == -2) {
-    if (wave == 0 && a.fuse_rank) rank_if_last(a, b, s_rank);
+    if (wave == 0 && a.fuse_rank && h == 0) rank_if_last(a, b, s_rank);
     return;
   }
   // the parent's path score, read now (wave 0 uses it at the end)
   const float sp = node < 0 ? 1.0f : a.t.cand_score[(int64_t)b * c.NC + node];
   constexpr int SW = kSelWaves;
-  constexpr int LSPT = DT == VRT_BF16 ? 3 : 2;  // segments per wave the row-wide path takes
+  constexpr int LSPT = seg_per_wave<DT>();
   union Sel {
     FastLds<DT, PL> f;
     ExactLds<PL> x;
@@ -1073,14 +1131,18 @@ __attribute__((amdgpu_waves_per_eu(PL == 2 ? 4 : 2, 8))) void k_select_expand(co
   Sel& P = *(Sel*)s_raw;
   int path = 2;
   uint32_t floor_img = 0u;  // the TC-th largest row value's image is at least this
-  if (G <= LSPT * SW) path = row_select_fast<DT, PL, SW, LSPT>(row, 0, G, c.V, c.TC, P.f, s_sup, n_sup, floor_img);
+  const int Gh = (G + S - 1) / S;  // this block's segments: [g0, g1)
+  const int g0 = h * Gh, g1 = min(G, g0 + Gh);
+  if (g1 - g0 <= LSPT * SW) path = row_select_fast<DT, PL, SW, LSPT>(row, g0, g1, c.V, c.TC, P.f, s_sup, n_sup, floor_img);
   if (path == 2) {
     __syncthreads();  // s_raw changes hands
-    path = row_select_exact<DT, PL, SW>(row, 0, c.V, c.TC, floor_img, P.x, s_sup, n_sup);
+    const int e0 = g0 * seg_elems<DT>(), e1 = min(c.V, g1 * seg_elems<DT>());
+    path = row_select_exact<DT, PL, SW>(row + (int64_t)e0 * esz, e0, e1 - e0, c.TC, floor_img, P.x, s_sup, n_sup);
   }
-  const int any_bad = path == 1;
+  int any_bad = path == 1;
   if (wave != 0) return;
   wave_sync();
+  if (S > 1 && !join_halves<PL>(a, b, j, h, n_sup, any_bad, s_sup)) return;
   end_row<PL>(a, b, j, node, sp, n_sup, any_bad != 0, s_sup, s_q);
   if (a.fuse_rank) rank_if_last(a, b, s_rank);
 }
@@ -1153,7 +1215,7 @@ __global__ __launch_bounds__(8 * kWave) void k_dense_expand(const BArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6;
   const int lane = lane_id();
   constexpr int SW = 8, PL = 2;
-  constexpr int LSPT = DT == VRT_BF16 ? 3 : 2;
+  constexpr int LSPT = seg_per_wave<DT>();
   __shared__ uint64_t s_rank[kRankFused];
   const int node = begin_row(a, b, j);
   if (node == -2) {
@@ -1752,7 +1814,7 @@ int list_len(const Cfg& c) { return max(128, next_pow2(c.trunc)); }
 
 template <int DT>
 hipError_t launch_layer(const BArgs& a, int rows, hipStream_t stream) {
-  const dim3 grid(rows, a.c.B);
+  const dim3 grid(rows * a.split, a.c.B);
   if (a.c.trunc == VRT_DENSE) {
     hipLaunchKernelGGL((k_dense_expand<DT>), grid, dim3(8 * kWave), 0, stream, a);
     return hipGetLastError();
@@ -1787,18 +1849,36 @@ hipError_t launch_coverage(const Cfg& c, const void* logits, int64_t ld, int64_t
                              : launch_coverage_t<VRT_F32>(c, logits, ld, tstride, n_rows, out, stream);
 }
 
+// Rows split over two blocks, after layer 0 (which initialises the row_sync words): rows
+// too long for one block's row-wide path whose halves fit it (fp32 rows of 65537 to
+// 131072 values, bf16 rows of 196609 to 393216). Splitting rows that fit one block
+// measured slower (0.450 against 0.403 ms per headline step): each half pays the
+// dependent phases after its loads in full.
+bool split_rows(const Cfg& c) {
+  if (c.trunc == VRT_DENSE) return false;
+  const bool bf = c.dtype == VRT_BF16;
+  const int seg = bf ? seg_elems<VRT_BF16>() : seg_elems<VRT_F32>();
+  const int cap = (bf ? seg_per_wave<VRT_BF16>() : seg_per_wave<VRT_F32>()) * kSelWaves;
+  const int G = (c.V + seg - 1) / seg;
+  return G > cap && (G + 1) / 2 <= cap;
+}
+
 size_t build_ws_bytes(const Cfg& c) {
-  (void)c;
-  return 0;
+  if (!split_rows(c)) return 0;
+  const size_t rows = (size_t)c.B * c.FP * 2;
+  return rows * list_len(c) * 8 + rows * 4;
 }
 
 hipError_t launch_build_layer(const Cfg& c, const TreePtrs& t, int layer, const void* logits,
                               int64_t ld, int64_t tstride, uint64_t seed, uint32_t step,
                               uint32_t* stats, void* ws, hipStream_t stream) {
   const int span = (layer == 0 ? 1 : c.P) * c.K;
-  BArgs a{c, t, layer, logits, ld, tstride, seed, step, stats, span <= kRankFused ? 1 : 0};
+  const bool split = layer > 0 && split_rows(c);
+  uint64_t* hk = (uint64_t*)ws;
+  int* hm = split ? (int*)(hk + (size_t)c.B * c.FP * 2 * list_len(c)) : nullptr;
+  BArgs a{c, t, layer, logits, ld, tstride, seed, step, stats, span <= kRankFused ? 1 : 0,
+          split ? 2 : 1, split ? hk : nullptr, hm};
   const int rows = layer == 0 ? 1 : c.FP;
-  (void)ws;
   hipError_t e = c.dtype == VRT_BF16 ? launch_layer<VRT_BF16>(a, rows, stream)
                                      : launch_layer<VRT_F32>(a, rows, stream);
   if (e != hipSuccess) return e;

@@ -43,7 +43,7 @@ class TreeLayout(ctypes.Structure):
         "row_tail_n", "row_tail_id", "row_tail_q", "front", "n_front", "smart", "admitted", "layer_sync",
         "n_nodes", "node_token", "node_parent", "node_depth", "node_kind", "node_cand",
         "child_off", "child", "tail_n", "tail_id", "tail_q", "row_dense", "row_det", "node_row",
-        "total_bytes")]
+        "row_sync", "total_bytes")]
 
 
 _lib = None
@@ -236,7 +236,7 @@ _FIELDS = {
     "node_parent": ("i32", ("N",)), "node_depth": ("i32", ("N",)), "node_kind": ("i32", ("N",)),
     "node_cand": ("i32", ("N",)), "child_off": ("i32", ("N+1",)), "child": ("i32", ("N",)),
     "tail_n": ("i32", ("N",)), "tail_id": ("i32", ("N", "TC")), "tail_q": ("f32", ("N", "TC")),
-    "row_dense": ("f64", ("NRd", 2)), "row_det": ("i32", ("NRd", 32)), "node_row": ("i32", ("Nd",)),
+    "row_dense": ("f64", ("NRd", 2)), "row_det": ("i32", ("NRd", 32)), "node_row": ("i32", ("Nd",)), "row_sync": ("i32", ("FP",)),
 }
 
 
