@@ -80,6 +80,8 @@ WORKLOADS = {
     "smart": Workload("smart", B=64, V=151936, dtype=BF16, mode=SMART, K=8, budget=128, D=10,
                       alpha=1.0, lam=0.02, gamma=0.01, delta=0.004, rho=1.3, m=1, T=1.0,
                       zipf=(1.1,), sigma=0.7),
+    "headline_fp32": Workload("headline_fp32", B=32, V=128256, dtype=F32, R=60, D=8, K=10, m=1,
+                              T=1.0, steps=128, zipf=(1.1,), sigma=0.7),
     "stress": Workload("stress", B=256, V=128256, dtype=BF16, R=128, D=10, K=12, m=1, T=1.0,
                        zipf=(1.5, 0.8), split=128, sigma=0.7),
 }
