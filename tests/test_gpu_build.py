@@ -87,6 +87,7 @@ def gpu_build(w, steps, seed, step, dev):
         rows, ld = to_device_rows(rows_list, w, L.FP, dev)
         L.build_layer(layer, rows, ld, seed, step)
         L.layer_rows.append(rows)
+        L.ld = ld
     L.finish(seed, step)
     return L
 
@@ -177,6 +178,24 @@ def test_bad_draft_rows_set_status_and_stay_in_bounds(gpu, kw):
     assert st[0] & 0x1 and st[1] & 0x2 and st[2] == 0
     n = L.views["n_nodes"].cpu().numpy()
     assert n[0] == 1 and n[1] == 1 and n[2] > 1
+
+
+def test_split_rows_repeat_on_one_tree_blob(gpu):
+    """The row_sync words are back at 0 after every split layer: the same step built again
+    on the same tree blob and workspace gives the same tree, the oracle's."""
+    w = _small(dtype=synth.F32, V=70000, R=30, D=4)
+    steps = [OracleStep(w, 6, b, 1) for b in range(w.B)]
+    L = gpu_build(w, steps, 6, 1, gpu)
+    torch.cuda.synchronize()
+    assert (L.views["row_sync"] == 0).all()
+    first = L.tree.clone()
+    for layer in range(w.D):
+        L.build_layer(layer, L.layer_rows[layer], L.ld, 6, 1)
+    L.finish(6, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(L.tree, first)
+    for b, s in enumerate(steps):
+        compare_tree(w, s, L, b)
 
 
 def test_bad_rows_of_split_layers_set_status(gpu):
