@@ -156,9 +156,9 @@ typedef struct {
  *   node_row    i32 [B][N]       expansion row of node i if its probe child is kept,
  *                                else -1
  * Build scratch:
- *   row_sync    i32 [B][FP]  halves of each row of the current layer done, where a
- *                            layer's rows are split over two blocks (set to 0 by
- *                            layer 0 and by the block that completes each row) */
+ *   row_sync    u64 [B][FP]  where a layer's rows are split over two blocks, the tag
+ *                            of the half that finished first (needs no initial
+ *                            value) */
 typedef struct {
   int64_t NC, NR, N, TC, FP;
   int64_t cand_token, cand_parent, cand_score, cand_kind;

@@ -58,6 +58,7 @@ CASES = [
     ("split_fp32_V70000", _small(dtype=synth.F32, V=70000, R=30, D=4)),
     ("split_bf16_V200000_trunc256", _small(V=200000, R=30, D=3, trunc=256)),
     ("split_fp32_flat_ties", _small(dtype=synth.F32, V=66000, zipf=(), draft_scale=0.0, R=20, D=3)),
+    ("split_smart_fp32", _smart_small(dtype=synth.F32, V=70000, budget=30, D=4)),
     ("small_all_ties", _small(zipf=(), draft_scale=0.0, V=9000, R=20, D=3)),
     ("small_all_ties_fp32_trunc256", _small(zipf=(), draft_scale=0.0, V=9000, R=20, D=3,
                                            dtype=synth.F32, trunc=256)),
@@ -181,19 +182,27 @@ def test_bad_draft_rows_set_status_and_stay_in_bounds(gpu, kw):
 
 
 def test_split_rows_repeat_on_one_tree_blob(gpu):
-    """The row_sync words are back at 0 after every split layer: the same step built again
-    on the same tree blob and workspace gives the same tree, the oracle's."""
+    """Split rows join through tags in row_sync that need no initial value: the same step
+    built again on the same tree blob and workspace, then again after row_sync was
+    filled with garbage, gives the same tree, the oracle's."""
     w = _small(dtype=synth.F32, V=70000, R=30, D=4)
     steps = [OracleStep(w, 6, b, 1) for b in range(w.B)]
     L = gpu_build(w, steps, 6, 1, gpu)
-    torch.cuda.synchronize()
-    assert (L.views["row_sync"] == 0).all()
-    first = L.tree.clone()
-    for layer in range(w.D):
-        L.build_layer(layer, L.layer_rows[layer], L.ld, 6, 1)
-    L.finish(6, 1)
-    torch.cuda.synchronize()
-    assert torch.equal(L.tree, first)
+
+    def blob():  # the tree without the join tags
+        torch.cuda.synchronize()
+        t = L.tree.clone()
+        vrt.tree_views(L.cfg, t)["row_sync"].zero_()
+        return t
+
+    first = blob()
+    for garbage in (False, True):
+        if garbage:
+            L.views["row_sync"].random_()
+        for layer in range(w.D):
+            L.build_layer(layer, L.layer_rows[layer], L.ld, 6, 1)
+        L.finish(6, 1)
+        assert torch.equal(blob(), first)
     for b, s in enumerate(steps):
         compare_tree(w, s, L, b)
 

@@ -22,6 +22,9 @@
 //   order, and the probe tails the verifier needs.
 // k_coverage: the share of each row's softmax inside its top-trunc support (a
 //   measurement of the inputs, not a step of the build).
+#include <atomic>
+#include <random>
+
 #include "vrt_dev.hpp"
 #include "vrt_internal.hpp"
 
@@ -57,6 +60,7 @@ struct BArgs {
   int split;      // blocks per row: 1, or 2 (each selects from half of the row's segments)
   uint64_t* half_keys;  // split rows: [B][FP][2][list length] each half's sorted support
   int* half_meta;       // split rows: [B][FP][2] each half's support size | non-finite << 30
+  uint64_t epoch;       // split rows: this launch's tag base, unique within the process
 };
 
 // The node frontier position j of tree b expands at this layer (-1 = root), or -2
@@ -955,20 +959,28 @@ __device__ __forceinline__ void expand_row(const BArgs& a, int b, int node, floa
 // one is forgotten and SMART's state reset, by the block of tree b's row 0, wave 0).
 // Returns the node the row expands, or -2 after clearing the row's candidate slots
 // (no parent at this frontier position).
+// Layer 0, wave 0 of the block that expands the root: clears the later layers'
+// candidate slots and starts the SMART state. (With the root row split over two blocks
+// the block that expands it is known only after the join, and it is the one that reads
+// the state.)
+__device__ __forceinline__ void init_tree(const BArgs& a, int b) {
+  const Cfg& c = a.c;
+  const int lane = lane_id();
+  const int64_t ncb = (int64_t)b * c.NC;
+  for (int t = c.K + lane; t < c.NC; t += kWave) a.t.cand_kind[ncb + t] = 0;
+  if (lane == 0) {
+    double* sm = a.t.smart + (int64_t)b * 8;
+    sm[0] = 0.0; sm[1] = 1.0; sm[2] = 1.0; sm[3] = 0.0; sm[4] = 0.0;
+    sm[5] = sm[6] = sm[7] = 0.0;
+  }
+}
+
 __device__ __forceinline__ int begin_row(const BArgs& a, int b, int j) {
   const Cfg& c = a.c;
   const int wave = threadIdx.x >> 6;
   const int lane = lane_id();
   const int64_t ncb = (int64_t)b * c.NC;
-  if (a.layer == 0 && wave == 0) {
-    for (int t = c.K + lane; t < c.NC; t += kWave) a.t.cand_kind[ncb + t] = 0;
-    for (int t = lane; t < c.FP; t += kWave) a.t.row_sync[(int64_t)b * c.FP + t] = 0;
-    if (lane == 0) {
-      double* sm = a.t.smart + (int64_t)b * 8;
-      sm[0] = 0.0; sm[1] = 1.0; sm[2] = 1.0; sm[3] = 0.0; sm[4] = 0.0;
-      sm[5] = sm[6] = sm[7] = 0.0;
-    }
-  }
+  if (a.layer == 0 && wave == 0 && a.split == 1) init_tree(a, b);
   const int node = row_node(a, b, j);
   if (node == -2 && wave == 0) {
     const int cbase = layer_base(c, a.layer) + j * c.K;
@@ -1059,9 +1071,11 @@ __device__ __forceinline__ uint64_t ld_dev64(const uint64_t* p) {
 // A row split over two blocks, wave 0 of each: every block has the top TC of its half
 // of the row in s_sup (n_sup keys, sorted); the row's top TC are among the two lists.
 // Each block writes its list and status device-coherently, waits for the stores and
-// counts itself on the row's row_sync word; the first to arrive is done (returns
-// false), the second merges the other's list into its own and combines the status.
-// It sets the word back to 0 for the next layer; layer 0 starts it at 0.
+// swaps its tag (2·epoch + half) into the row's row_sync word; the block that takes out
+// the other half's tag of this launch is the second (the word needs no initial value:
+// it holds tags of earlier launches or whatever the blob held). The first is done
+// (returns false), the second merges the other's list into its own and combines the
+// status.
 template <int PL>
 __device__ __forceinline__ bool join_halves(const BArgs& a, int b, int j, int h, int& n_sup,
                                             int& any_bad, uint64_t* s_sup) {
@@ -1073,10 +1087,14 @@ __device__ __forceinline__ bool join_halves(const BArgs& a, int b, int j, int h,
   static_for<PL>([&](auto s) { st_dev64(&mine[lane * PL + s], s_sup[lane * PL + s]); });
   if (lane == 0) st_dev(&a.half_meta[r * 2 + h], n_sup | (any_bad << 30));
   wait_stores();
-  int old = 0;
-  if (lane == 0) old = atomicAdd(&a.t.row_sync[r], 1);
-  old = __shfl(old, 0, kWave);
-  if (old == 0) return false;
+  int second = 0;
+  if (lane == 0) {
+    const unsigned long long old =
+        atomicExch((unsigned long long*)&a.t.row_sync[r], (unsigned long long)(a.epoch * 2 + h));
+    second = old == (unsigned long long)(a.epoch * 2 + (1 - h));
+  }
+  second = __shfl(second, 0, kWave);
+  if (!second) return false;
   const uint64_t* other = a.half_keys + (r * 2 + (1 - h)) * N;
   const int om = ld_dev(&a.half_meta[r * 2 + (1 - h)]);
   uint64_t top[PL], add[PL];
@@ -1091,7 +1109,6 @@ __device__ __forceinline__ bool join_halves(const BArgs& a, int b, int j, int h,
   });
   n_sup = min(c.TC, n_sup + (om & 0xFFFF));
   any_bad |= (om >> 30) & 1;
-  if (lane == 0) st_dev(&a.t.row_sync[r], 0);
   wave_sync();
   return true;
 }
@@ -1142,7 +1159,10 @@ __attribute__((amdgpu_waves_per_eu(PL == 2 ? 4 : 2, 8))) void k_select_expand(co
   int any_bad = path == 1;
   if (wave != 0) return;
   wave_sync();
-  if (S > 1 && !join_halves<PL>(a, b, j, h, n_sup, any_bad, s_sup)) return;
+  if (S > 1) {
+    if (!join_halves<PL>(a, b, j, h, n_sup, any_bad, s_sup)) return;
+    if (a.layer == 0) init_tree(a, b);
+  }
   end_row<PL>(a, b, j, node, sp, n_sup, any_bad != 0, s_sup, s_q);
   if (a.fuse_rank) rank_if_last(a, b, s_rank);
 }
@@ -1849,12 +1869,13 @@ hipError_t launch_coverage(const Cfg& c, const void* logits, int64_t ld, int64_t
                              : launch_coverage_t<VRT_F32>(c, logits, ld, tstride, n_rows, out, stream);
 }
 
-// Rows split over two blocks, after layer 0 (which initialises the row_sync words): rows
-// too long for one block's row-wide path whose halves fit it (fp32 rows of 65537 to
-// 131072 values, bf16 rows of 196609 to 393216). Splitting rows that fit one block
-// measured slower (0.450 against 0.403 ms per headline step): each half pays the
-// dependent phases after its loads in full.
-bool split_rows(const Cfg& c) {
+// Rows split over two blocks, at every layer: rows too long for one block's row-wide
+// path whose halves fit it (fp32 rows of 65537 to 131072 values, bf16 rows of 196609 to
+// 393216). Splitting rows that fit one block measured slower after the root (0.450
+// against 0.403 ms per headline step: each half pays the dependent phases after its
+// loads) and no faster at the root (0.4032 against 0.4021-0.4027 ms).
+bool split_rows(const Cfg& c, int layer) {
+  (void)layer;
   if (c.trunc == VRT_DENSE) return false;
   const bool bf = c.dtype == VRT_BF16;
   const int seg = bf ? seg_elems<VRT_BF16>() : seg_elems<VRT_F32>();
@@ -1863,8 +1884,11 @@ bool split_rows(const Cfg& c) {
   return G > cap && (G + 1) / 2 <= cap;
 }
 
+// Tags of split launches: a process-wide counter from a random start.
+static std::atomic<uint64_t> g_epoch{((uint64_t)std::random_device{}() << 32) ^ std::random_device{}()};
+
 size_t build_ws_bytes(const Cfg& c) {
-  if (!split_rows(c)) return 0;
+  if (!split_rows(c, 0)) return 0;
   const size_t rows = (size_t)c.B * c.FP * 2;
   return rows * list_len(c) * 8 + rows * 4;
 }
@@ -1873,11 +1897,11 @@ hipError_t launch_build_layer(const Cfg& c, const TreePtrs& t, int layer, const 
                               int64_t ld, int64_t tstride, uint64_t seed, uint32_t step,
                               uint32_t* stats, void* ws, hipStream_t stream) {
   const int span = (layer == 0 ? 1 : c.P) * c.K;
-  const bool split = layer > 0 && split_rows(c);
+  const bool split = split_rows(c, layer);
   uint64_t* hk = (uint64_t*)ws;
   int* hm = split ? (int*)(hk + (size_t)c.B * c.FP * 2 * list_len(c)) : nullptr;
   BArgs a{c, t, layer, logits, ld, tstride, seed, step, stats, span <= kRankFused ? 1 : 0,
-          split ? 2 : 1, split ? hk : nullptr, hm};
+          split ? 2 : 1, split ? hk : nullptr, hm, split ? g_epoch.fetch_add(1) : 0};
   const int rows = layer == 0 ? 1 : c.FP;
   hipError_t e = c.dtype == VRT_BF16 ? launch_layer<VRT_BF16>(a, rows, stream)
                                      : launch_layer<VRT_F32>(a, rows, stream);

@@ -64,7 +64,7 @@ bool compute_layout(const vrt_config& c, vrt_tree_layout* L) {
   take(&L->row_dense, dense * B * L->NR * 2 * 8);
   take(&L->row_det, dense * B * L->NR * 32 * 4);
   take(&L->node_row, dense * B * L->N * 4);
-  take(&L->row_sync, B * L->FP * 4);
+  take(&L->row_sync, B * L->FP * 8);
   L->total_bytes = off;
   return true;
 }
@@ -156,7 +156,7 @@ TreePtrs tree_ptrs(const vrt_config& c, void* blob) {
   t.row_dense = (double*)(p + L.row_dense);
   t.row_det = (int*)(p + L.row_det);
   t.node_row = (int*)(p + L.node_row);
-  t.row_sync = (int*)(p + L.row_sync);
+  t.row_sync = (uint64_t*)(p + L.row_sync);
   return t;
 }
 

@@ -51,7 +51,7 @@ struct TreePtrs {
   double* row_dense;  // dense rows: [NR][2] (largest logit, tempered tail mass)
   int* row_det;       // dense rows: [NR][32] deterministic children's tokens
   int* node_row;      // dense rows: [N] expansion row of a node whose probe is kept
-  int* row_sync;      // [FP] halves of a layer's row done (rows split over two blocks)
+  uint64_t* row_sync;  // [FP] tag of the half of a split row that finished first
 };
 
 // Per-node verification outcome: accepted child node (-1: none), final token

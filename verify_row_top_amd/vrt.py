@@ -236,7 +236,7 @@ _FIELDS = {
     "node_parent": ("i32", ("N",)), "node_depth": ("i32", ("N",)), "node_kind": ("i32", ("N",)),
     "node_cand": ("i32", ("N",)), "child_off": ("i32", ("N+1",)), "child": ("i32", ("N",)),
     "tail_n": ("i32", ("N",)), "tail_id": ("i32", ("N", "TC")), "tail_q": ("f32", ("N", "TC")),
-    "row_dense": ("f64", ("NRd", 2)), "row_det": ("i32", ("NRd", 32)), "node_row": ("i32", ("Nd",)), "row_sync": ("i32", ("FP",)),
+    "row_dense": ("f64", ("NRd", 2)), "row_det": ("i32", ("NRd", 32)), "node_row": ("i32", ("Nd",)), "row_sync": ("i64", ("FP",)),
 }
 
 
@@ -244,8 +244,8 @@ def tree_views(cfg, tree):
     """Dict of tensor views into the tree blob (a uint8 tensor of tree_bytes(cfg))."""
     import torch
     L = tree_layout_of(cfg)
-    dt = {"i32": torch.int32, "f32": torch.float32, "f64": torch.float64}
-    es = {"i32": 4, "f32": 4, "f64": 8}
+    dt = {"i32": torch.int32, "f32": torch.float32, "f64": torch.float64, "i64": torch.int64}
+    es = {"i32": 4, "f32": 4, "f64": 8, "i64": 8}
     out = {}
     for name, (t, shape) in _FIELDS.items():
         dims = []
