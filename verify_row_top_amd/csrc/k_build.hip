@@ -1116,11 +1116,11 @@ __device__ __forceinline__ bool join_halves(const BArgs& a, int b, int j, int h,
 // One block per expanded parent (or two, each on half of the row's segments, joined by
 // join_halves), then wave 0 expands it: the row-wide path, the exact path behind it
 // (ties, flat rows, rows longer than the row-wide path covers).
-template <int DT, int PL>
+template <int DT, int PL, bool SPLIT>
 __global__ __launch_bounds__(kSelWaves * kWave)
 __attribute__((amdgpu_waves_per_eu(PL == 2 ? 4 : 2, 8))) void k_select_expand(const BArgs a) {
   const Cfg& c = a.c;
-  const int S = a.split;
+  constexpr int S = SPLIT ? 2 : 1;
   const int j = blockIdx.x / S, h = blockIdx.x % S, b = blockIdx.y;
   const int wave = threadIdx.x >> 6;
   constexpr int N = PL * kWave;
@@ -1159,7 +1159,7 @@ __attribute__((amdgpu_waves_per_eu(PL == 2 ? 4 : 2, 8))) void k_select_expand(co
   int any_bad = path == 1;
   if (wave != 0) return;
   wave_sync();
-  if (S > 1) {
+  if constexpr (SPLIT) {
     if (!join_halves<PL>(a, b, j, h, n_sup, any_bad, s_sup)) return;
     if (a.layer == 0) init_tree(a, b);
   }
@@ -1832,6 +1832,18 @@ __global__ __launch_bounds__(kFT) void k_finish(const Cfg c, const TreePtrs t) {
 
 int list_len(const Cfg& c) { return max(128, next_pow2(c.trunc)); }
 
+template <int DT, bool SPLIT>
+hipError_t launch_select(const BArgs& a, dim3 grid, hipStream_t stream) {
+  const dim3 block(kSelWaves * kWave);
+  switch (list_len(a.c) / kWave) {
+    case 2: hipLaunchKernelGGL((k_select_expand<DT, 2, SPLIT>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((k_select_expand<DT, 4, SPLIT>), grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((k_select_expand<DT, 8, SPLIT>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((k_select_expand<DT, 16, SPLIT>), grid, block, 0, stream, a); break;
+  }
+  return hipGetLastError();
+}
+
 template <int DT>
 hipError_t launch_layer(const BArgs& a, int rows, hipStream_t stream) {
   const dim3 grid(rows * a.split, a.c.B);
@@ -1839,13 +1851,8 @@ hipError_t launch_layer(const BArgs& a, int rows, hipStream_t stream) {
     hipLaunchKernelGGL((k_dense_expand<DT>), grid, dim3(8 * kWave), 0, stream, a);
     return hipGetLastError();
   }
-  switch (list_len(a.c) / kWave) {
-    case 2: hipLaunchKernelGGL((k_select_expand<DT, 2>), grid, dim3(kSelWaves * kWave), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((k_select_expand<DT, 4>), grid, dim3(kSelWaves * kWave), 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((k_select_expand<DT, 8>), grid, dim3(kSelWaves * kWave), 0, stream, a); break;
-    default: hipLaunchKernelGGL((k_select_expand<DT, 16>), grid, dim3(kSelWaves * kWave), 0, stream, a); break;
-  }
-  return hipGetLastError();
+  if (a.split > 1) return launch_select<DT, true>(a, grid, stream);
+  return launch_select<DT, false>(a, grid, stream);
 }
 
 template <int DT>
