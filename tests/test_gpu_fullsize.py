@@ -33,8 +33,7 @@ CASES = [
     # than four keys per support entry
     ("headline_trunc512", workloads.get("headline", trunc=512), [3, 16, 29], (9, 4)),
     ("headline_trunc1024", workloads.get("headline", trunc=1024), [0, 19, 31], (7, 2)),
-    # fp32 logits at the full vocabulary: the root rows take the exact selection path, the
-    # later layers' rows are split over two blocks
+    # fp32 logits at the full vocabulary: every row is split over two blocks
     ("headline_fp32", workloads.get("headline", dtype=synth.F32, B=8),
      [0, 7], (8, 5)),
 ]
