@@ -17,7 +17,7 @@ from verify_row_top_amd import vrt
 import synth
 from synth import workloads
 from tests.gpu_common import Lib, lib_config, to_device_rows
-from tests.harness import OracleStep
+from oracle.drive import OracleStep
 
 pytestmark = pytest.mark.gpu
 

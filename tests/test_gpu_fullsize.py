@@ -14,7 +14,7 @@ import pytest
 import synth
 from synth import workloads
 from tests.gpu_common import device_step
-from tests.harness import OracleStep
+from oracle.drive import OracleStep
 from tests.test_gpu_build import compare_tree
 
 pytestmark = pytest.mark.gpu

@@ -13,7 +13,7 @@ import torch
 from oracle import oracle as O
 from synth import workloads
 from tests.gpu_common import Lib, lib_config
-from tests.harness import OracleStep
+from oracle.drive import OracleStep
 from tests.test_gpu_build import _small
 from verify_row_top_amd import vrt
 

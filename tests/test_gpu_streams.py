@@ -6,7 +6,7 @@ import torch
 
 from synth import workloads
 from tests.gpu_common import Lib, lib_config, row_ld, to_device_rows
-from tests.harness import OracleStep
+from oracle.drive import OracleStep
 
 pytestmark = pytest.mark.gpu
 

@@ -14,7 +14,7 @@ import torch
 import synth
 from synth import workloads
 from tests.gpu_common import Lib, lib_config, to_device_rows
-from tests.harness import OracleStep
+from oracle.drive import OracleStep
 
 pytestmark = pytest.mark.gpu
 
@@ -144,7 +144,7 @@ def test_verify_empty_tree_is_a_bonus_sample(gpu):
         v["tail_n"] = np.zeros(1, np.int32)
         L.write_view(b, v)
         from oracle import oracle as orc
-        from tests.harness import oracle_cfg
+        from oracle.drive import oracle_cfg
         tok, nodes, pn, ex = orc.verify(oracle_cfg(w), v, synth.to_f32(s.target_rows[:1]), 9, b, 0)
         s.bonus = (tok, ex)
     target, ld = to_device_rows([s.target_rows for s in steps], w, L.N, gpu)

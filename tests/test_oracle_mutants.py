@@ -96,6 +96,11 @@ def smart_ok():
     return True
 
 
+def topr_ok():
+    from tests import test_oracle_topr as tt
+    return all(tt.hand_case_ok(n) for n in tt.CASES) and tt.invariants_ok(200)
+
+
 def dense_ok():
     from tests import test_oracle_dense as td
     try:
@@ -145,6 +150,14 @@ MUTANTS = [
      "      before = cum;", dense_ok),
     ("dense_fillers_repeat_probe", "if (ids[i] != s) add_child", "if (ids[i] >= 0) add_child",
      dense_ok),
+    # the per-layer beam and the global top-R prune (every check stops at the first wrong
+    # frontier, so a frontier longer than W is never expanded)
+    ("node_tie_break_reversed", "  return (x < y) ? -1 : (x > y);",
+     "  return (x > y) ? -1 : (x < y);", topr_ok),
+    ("beam_frontier_one_extra", "k < n && k < W; ++k", "k < n && k <= W; ++k", topr_ok),
+    ("beam_ranks_earlier_layers", "  const int32_t base = orc_layer_base(t, layer);",
+     "  const int32_t base = 0;", topr_ok),
+    ("prune_keeps_one_extra", "k < n && k < c->R; ++k", "k < n && k <= c->R; ++k", topr_ok),
     ("smart_leaf_count_inverted", "if (t->has_child[par + 1]) t->n_paths += 1;",
      "if (!t->has_child[par + 1]) t->n_paths += 1;", smart_ok),
 ]

@@ -11,7 +11,7 @@ import pytest
 
 from oracle import oracle as orc
 from synth import workloads
-from tests.harness import OracleStep, oracle_cfg
+from oracle.drive import OracleStep, oracle_cfg
 
 
 def _row(V, probs_at):
