@@ -130,6 +130,8 @@ def _declare(L):
     L.orc_verify.restype = i32
     L.orc_table_trials.argtypes = [P(Cfg), i32, vp, vp, u64, i32, u32, i32, i32, vp, vp, vp]
     L.orc_table_trials.restype = i32
+    L.orc_exact_law.argtypes = [P(Cfg), i32, vp, vp, vp, i32, i32, vp, vp, P(f64)]
+    L.orc_exact_law.restype = i32
     L.orc_tree_mask.argtypes = [i32, vp, vp, vp]
     L.orc_tree_mask.restype = i32
     L.orc_accepted_kv.argtypes = [i32, vp, vp]
@@ -305,6 +307,22 @@ def table_trials(cfg, max_len, draft_tab, target_tab, seed, b, step0, n_trials, 
                                1 if two else 0, _p(out), _p(nf), ctypes.byref(ne))
     assert r == 0, "context table too short for the tree depth"
     return out.reshape(n_trials, 2), nf, ne.value
+
+
+def exact_law(cfg, max_len, draft_tab, target_tab, prefix=(), two=True):
+    """Exact laws of one step on a context-table model by enumeration (orc_exact_law):
+    (law1 [V], law2 [V, V] or None, P(first token from the tree))."""
+    V = cfg.V
+    dt = np.ascontiguousarray(draft_tab, dtype=np.float32)
+    tt = np.ascontiguousarray(target_tab, dtype=np.float32)
+    pre = np.ascontiguousarray(list(prefix) or [0], dtype=np.int32)
+    law1 = np.zeros(V, np.float64)
+    law2 = np.zeros(V * V, np.float64)
+    acc = ctypes.c_double()
+    r = lib().orc_exact_law(ctypes.byref(cfg), max_len, _p(dt), _p(tt), _p(pre), len(prefix),
+                            1 if two else 0, _p(law1), _p(law2), ctypes.byref(acc))
+    assert r == 0, f"orc_exact_law returned {r}"
+    return law1, (law2.reshape(V, V) if two else None), acc.value
 
 
 def ctx_index(V, path):

@@ -170,6 +170,11 @@ struct orc_tree {
   /* emitted tree: node_cand[i] = creation index of node i (root = -1) */
   int32_t n_nodes;
   int32_t* node_cand;
+  /* exact enumeration (orc_exact_law): force[r] is the support rank row r's probe takes
+   * instead of a draw, and weight the product of the forced draws' probabilities; NULL
+   * when drawing */
+  int32_t* force;
+  double weight;
 };
 
 static int32_t width_of(const orc_cfg* c) { return c->W > 0 ? c->W : c->K; }
@@ -202,6 +207,7 @@ orc_tree* orc_tree_create(const orc_cfg* cfg, uint64_t seed, int32_t b, uint32_t
   t->n_size = 1;
   t->n_paths = 1;
   t->L = 0.0;
+  t->weight = 1.0;
   return t;
 }
 
@@ -237,6 +243,32 @@ static void add_child(orc_tree* t, int32_t layer, int32_t pos, int32_t slot, int
   x->row = row;
   x->live = 1;
   x->score = score_of(t, parent) * q; /* path product, fp32 */
+}
+
+/* Exact enumeration: the share of u in [0, 1) for which the inverse CDF used by every
+ * draw here (the smallest k with u z < q[0] + .. + q[k], sums in index order; if rounding
+ * leaves none, the last k with mass, else 0) returns k. z is the mass the draw scales u
+ * by (exactly the sum of q for the method's own draws). */
+static double draw_share(const double* q, int32_t n, double z, int32_t k) {
+  int32_t last = 0, first = -1;
+  double cum = 0.0, before = 0.0, at = 0.0;
+  for (int32_t j = 0; j < n; ++j) {
+    if (q[j] > 0.0) {
+      last = j;
+      if (first < 0) first = j;
+    }
+    if (j == k) before = cum;
+    cum += q[j];
+    if (j == k) at = cum;
+  }
+  if (z != z) return k == last ? 1.0 : 0.0;             /* u z is NaN: never below */
+  if (z < 0.0) return k == 0 ? 1.0 : 0.0;               /* u z < 0 <= q[0] */
+  if (z == 0.0) return k == (first >= 0 ? first : last) ? 1.0 : 0.0;
+  if (k < 0 || k >= n) return 0.0;
+  const double hi = at / z < 1.0 ? at / z : 1.0, lo = before / z < 1.0 ? before / z : 1.0;
+  double share = hi > lo ? hi - lo : 0.0;
+  if (k == last) share += 1.0 - (cum / z < 1.0 ? cum / z : 1.0); /* the fallback */
+  return share;
 }
 
 /* Proxy probability of the probe (key design 2): min{q(x_m), z}, or min(1, q(x_1) + eps)
@@ -432,7 +464,18 @@ static void expand_node(orc_tree* t, int32_t layer, int32_t pos, int32_t node, c
   /* 3. probe: x_s ~ q_T restricted to ranks > m and renormalised by z_T,
    *    drawn by inverse CDF in rank order with one uniform. */
   int32_t js = -1;
-  if (c->probe && n > t0 && zT > 0.0) {
+  const int32_t draws = c->probe && n > t0 && zT > 0.0;
+  if (t->force && !(draws ? (t->force[r] >= t0 && t->force[r] < n) : t->force[r] == t0))
+    t->weight = 0.0; /* a forced branch that does not exist (no draw: only rank t0 stands) */
+  if (draws && t->force && t->weight > 0.0) {
+    /* exact enumeration: the forced rank, weighted by the share of u in [0, 1) that the
+     * inverse CDF below sends to it */
+    js = t->force[r];
+    t->weight *= draw_share(e->q_T + t0, n - t0, zT, js - t0);
+    e->probe_rank = js;
+    e->probe_token = e->sup_id[js];
+    e->proxy = proxy_of(c, e, t0);
+  } else if (draws && !t->force) {
     const double u = orc_uniform(t->seed, (uint32_t)(node + 1), (uint32_t)t->b, t->step,
                                  ORC_PURPOSE_PROBE);
     e->u = u;
@@ -676,6 +719,25 @@ int32_t orc_tree_view(const orc_tree* t, int32_t cap, int32_t tail_cap, int32_t*
 }
 
 /* ------------------------------------------------------------------------- */
+/* Exact enumeration of a node's decision: instead of drawing, decide_node follows the
+ * forced branch (the test at index accept_at accepts, the ones before it reject; with
+ * accept_at = -1 every test rejects and the final sample returns `token`) and multiplies
+ * the branch's probability under u uniform on [0, 1) into weight. */
+typedef struct {
+  int32_t accept_at, token, n;
+  double weight;
+} orc_force;
+
+/* One accept/reject test: u < ratio when drawing; forced, P(u < ratio) = clip(ratio). */
+static int32_t take_test(orc_force* f, double u, double ratio) {
+  if (!f) return u < ratio;
+  const double pa = ratio >= 1.0 ? 1.0 : (ratio > 0.0 ? ratio : 0.0); /* NaN: 0 */
+  const int32_t acc = f->n++ == f->accept_at;
+  f->weight *= acc ? pa : 1.0 - pa;
+  return acc;
+}
+
+/* ------------------------------------------------------------------------- */
 /* Verification of one node (RheoSampling key design 3). p is the full-vocab
  * temperature softmax of the node's target row. If the probe child is kept it
  * is tested first with min(1, p/q~); on rejection the residual is
@@ -692,7 +754,7 @@ static void decide_node(const orc_cfg* c, int32_t i, const int32_t* token, const
                         const int32_t* kind, const int32_t* child_off, const int32_t* child,
                         const int32_t* tail_n, const int32_t* tail_id, const double* tail_q,
                         int32_t tail_cap, const float* x, uint64_t seed, int32_t b, uint32_t step,
-                        double* w, orc_node_out* o) {
+                        double* w, orc_node_out* o, orc_force* f) {
   const int32_t V = c->V;
   const double invT = (double)(1.0f / c->T);
   float M = x[0];
@@ -727,7 +789,7 @@ static void decide_node(const orc_cfg* c, int32_t i, const int32_t* token, const
     const double a = w[token[probe]] / qs;
     o->n_tests++;
     if (fabs(u0 - a) < ORC_EXEMPT_BAND) o->exempt++;
-    if (u0 < a) {
+    if (take_test(f, u0, a)) {
       o->accept = probe;
       o->W = 0.0;
       return;
@@ -756,7 +818,7 @@ static void decide_node(const orc_cfg* c, int32_t i, const int32_t* token, const
     ++j;
     o->n_tests++;
     if (fabs(uj - ratio) < ORC_EXEMPT_BAND) o->exempt++;
-    if (uj < ratio) {
+    if (take_test(f, uj, ratio)) {
       o->accept = ch;
       o->W = 0.0;
       return;
@@ -772,7 +834,7 @@ static void decide_node(const orc_cfg* c, int32_t i, const int32_t* token, const
     const double a = w[token[probe]] / (W * qs);
     o->n_tests++;
     if (fabs(u0 - a) < ORC_EXEMPT_BAND) o->exempt++;
-    if (u0 < a) {
+    if (take_test(f, u0, a)) {
       o->accept = probe;
       o->W = 0.0;
       return;
@@ -790,6 +852,11 @@ static void decide_node(const orc_cfg* c, int32_t i, const int32_t* token, const
 
   /* final residual (or bonus) sample by inverse CDF in token-id order */
   o->W = W;
+  if (f) { /* forced: the branch exists only if no test was to accept */
+    f->weight *= f->accept_at < 0 ? draw_share(w, V, W, f->token) : 0.0;
+    o->token = f->token;
+    return;
+  }
   const double uf = orc_uniform(seed, d, (uint32_t)b, step, ORC_PURPOSE_FINAL);
   const double tgt = uf * W;
   double cum = 0.0, before = 0.0;
@@ -832,7 +899,7 @@ int32_t orc_verify(const orc_cfg* cfg, int32_t n_nodes, const int32_t* token, co
   if (!outs) outs = (orc_node_out*)malloc(sizeof(orc_node_out) * (size_t)n_nodes);
   for (int32_t i = 0; i < n_nodes; ++i)
     decide_node(cfg, i, token, depth, kind, child_off, child, tail_n, tail_id, tail_q, tail_cap,
-                target + (int64_t)i * ld, seed, b, step, w, &outs[i]);
+                target + (int64_t)i * ld, seed, b, step, w, &outs[i], NULL);
   /* the walk: follow accepted children from the root; emit the final token */
   int32_t cur = 0, len = 0, exempt = 0;
   for (;;) {
@@ -962,6 +1029,187 @@ int32_t orc_table_trials(const orc_cfg* cfg, int32_t max_len, const float* draft
   }
   *n_exempt = exempt;
   return bad ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Exact laws by enumeration on a context-table model (tiny configurations). Every probe
+ * draw of the build, and every test and final sample of the verification, becomes a
+ * branch weighted by its probability under a uniform u on [0, 1); the branches run the
+ * same expansion and decision code as the sampler (forced). */
+typedef struct {
+  const orc_cfg* cfg;
+  int32_t max_len;
+  const float *dtab, *ttab;
+  const int32_t* prefix;
+  int32_t np, two, err;
+  double *law1, *law2, acc;
+  double* fresh; /* [V][V]: row a = first-token law of the step at prefix + a (NaN: not yet) */
+} enum_ctx;
+
+/* The first `layers` layers of a tree at E's context, with the probes forced. */
+static orc_tree* enum_build(enum_ctx* E, int32_t* force, int32_t layers) {
+  const int32_t V = E->cfg->V;
+  orc_tree* t = orc_tree_create(E->cfg, 0, 0, 0);
+  t->force = force;
+  float* rows = (float*)malloc(sizeof(float) * (size_t)V * (size_t)(t->maxpar + 1));
+  int32_t path[64];
+  for (int32_t layer = 0; layer < layers && t->n_front > 0 && t->weight > 0.0; ++layer) {
+    for (int32_t j = 0; j < t->n_front; ++j) {
+      const int32_t k = path_of(t, t->front[j], E->prefix, E->np, path);
+      if (k > E->max_len) E->err = -1;
+      if (E->err) break;
+      memcpy(rows + (int64_t)j * V, E->dtab + ctx_row(V, path, k) * V, sizeof(float) * (size_t)V);
+    }
+    if (E->err) break;
+    orc_expand_layer(t, layer, rows, V);
+  }
+  free(rows);
+  return t;
+}
+
+typedef struct {
+  int32_t accept, token;
+  double p;
+} enum_out;
+
+/* Every outcome of node i's decision with its probability: out holds up to K + V entries. */
+static int32_t node_outcomes(const orc_cfg* c, int32_t i, const int32_t* iv, int32_t N, const int32_t* tail_id,
+                             const double* tail_q, int32_t TC, const float* x, double* w, enum_out* out) {
+  const int32_t *token = iv, *depth = iv + 2 * N, *kind = iv + 3 * N, *child_off = iv + 5 * N,
+                *child = iv + 6 * N + 1, *tail_n = iv + 7 * N + 1;
+  int32_t n = 0;
+  orc_node_out o;
+  for (int32_t a = -1; a < c->K; ++a) {
+    for (int32_t y = 0; y < (a < 0 ? c->V : 1); ++y) {
+      orc_force f = {a, y, 0, 1.0};
+      decide_node(c, i, token, depth, kind, child_off, child, tail_n, tail_id, tail_q, TC, x, 0, 0, 0, w,
+                  &o, &f);
+      if (f.weight > 0.0) {
+        out[n].accept = a < 0 ? -1 : o.accept;
+        out[n].token = a < 0 ? y : token[o.accept];
+        out[n].p = f.weight;
+        ++n;
+      }
+    }
+  }
+  return n;
+}
+
+static void enum_law(enum_ctx* E);
+
+/* A complete tree of weight t->weight: its verification's outcomes into E's laws. */
+static void enum_verify(enum_ctx* E, orc_tree* t) {
+  const orc_cfg* c = E->cfg;
+  const int32_t V = c->V, TC = c->trunc;
+  orc_finish(t);
+  const int32_t N = t->n_nodes;
+  int32_t* iv = (int32_t*)malloc(sizeof(int32_t) * (size_t)(8 * N + 8));
+  int32_t* tail_id = (int32_t*)malloc(sizeof(int32_t) * (size_t)N * TC);
+  double* tail_q = (double*)malloc(sizeof(double) * (size_t)N * TC);
+  float* target = (float*)malloc(sizeof(float) * (size_t)V * (size_t)N);
+  double* w = (double*)malloc(sizeof(double) * (size_t)V);
+  enum_out* o1 = (enum_out*)malloc(sizeof(enum_out) * (size_t)(c->K + V));
+  enum_out* o2 = (enum_out*)malloc(sizeof(enum_out) * (size_t)(c->K + V));
+  int32_t nn, path[64];
+  orc_tree_view(t, N, TC, &nn, iv, iv + N, iv + 2 * N, iv + 3 * N, iv + 4 * N, iv + 5 * N, iv + 6 * N + 1,
+                iv + 7 * N + 1, tail_id, tail_q);
+  for (int32_t i = 0; i < N && !E->err; ++i) {
+    const int32_t k = path_of(t, iv[4 * N + i], E->prefix, E->np, path);
+    if (k > E->max_len) E->err = -1;
+    else memcpy(target + (int64_t)i * V, E->ttab + ctx_row(V, path, k) * V, sizeof(float) * (size_t)V);
+  }
+  const int32_t n1 = E->err ? 0 : node_outcomes(c, 0, iv, N, tail_id, tail_q, TC, target, w, o1);
+  for (int32_t a = 0; a < n1; ++a) {
+    const double p1 = t->weight * o1[a].p;
+    const int32_t t1 = o1[a].token;
+    E->law1[t1] += p1;
+    if (o1[a].accept >= 0) E->acc += p1;
+    if (!E->two) continue;
+    if (o1[a].accept >= 0) { /* the step goes on at the accepted child */
+      const int32_t ch = o1[a].accept;
+      const int32_t n2 = node_outcomes(c, ch, iv, N, tail_id, tail_q, TC, target + (int64_t)ch * V, w, o2);
+      for (int32_t b2 = 0; b2 < n2; ++b2) E->law2[(int64_t)t1 * V + o2[b2].token] += p1 * o2[b2].p;
+    } else { /* one token emitted: the next step starts at the extended context */
+      double* fr = E->fresh + (int64_t)t1 * V;
+      if (fr[0] != fr[0]) {
+        int32_t* pre = (int32_t*)malloc(sizeof(int32_t) * (size_t)(E->np + 1));
+        for (int32_t q = 0; q < E->np; ++q) pre[q] = E->prefix[q];
+        pre[E->np] = t1;
+        enum_ctx F = {c, E->max_len, E->dtab, E->ttab, pre, E->np + 1, 0, 0, fr, NULL, 0.0, NULL};
+        for (int32_t v = 0; v < V; ++v) fr[v] = 0.0;
+        enum_law(&F);
+        if (F.err) E->err = F.err;
+        free(pre);
+      }
+      for (int32_t v = 0; v < V; ++v) E->law2[(int64_t)t1 * V + v] += p1 * fr[v];
+    }
+  }
+  free(o2);
+  free(o1);
+  free(w);
+  free(target);
+  free(tail_q);
+  free(tail_id);
+  free(iv);
+}
+
+/* Layer `layer` onwards, the probes of earlier layers fixed in force: one branch per
+ * combination of the probe ranks of this layer's expanded rows. */
+static void enum_layers(enum_ctx* E, int32_t* force, int32_t layer) {
+  const orc_cfg* c = E->cfg;
+  orc_tree* t = enum_build(E, force, layer);
+  if (E->err || t->weight == 0.0) {
+    orc_tree_free(t);
+    return;
+  }
+  if (layer == c->D || t->n_front == 0) {
+    enum_verify(E, t);
+    orc_tree_free(t);
+    return;
+  }
+  const int32_t nf = t->n_front, r0 = orc_row_base(t, layer);
+  orc_tree_free(t);
+  const int32_t n_sup = c->V < c->trunc ? c->V : c->trunc;
+  const int32_t t0 = c->order == ORC_PROBE_LAST ? (c->K - 1 < n_sup ? c->K - 1 : n_sup) : (c->probe ? c->m : 0);
+  const int32_t radix = (c->probe && n_sup > t0) ? n_sup - t0 : 1;
+  int32_t digit[64] = {0};
+  for (;;) {
+    for (int32_t j = 0; j < nf; ++j) force[r0 + j] = t0 + digit[j];
+    enum_layers(E, force, layer + 1);
+    int32_t j = 0;
+    while (j < nf && ++digit[j] == radix) digit[j++] = 0;
+    if (j == nf) break;
+  }
+  for (int32_t j = 0; j < nf; ++j) force[r0 + j] = t0;
+}
+
+static void enum_law(enum_ctx* E) {
+  const orc_cfg* c = E->cfg;
+  const int32_t maxpar = width_of(c);
+  const int32_t n_rows = 1 + (c->D - 1) * maxpar;
+  const int32_t n_sup = c->V < c->trunc ? c->V : c->trunc;
+  const int32_t t0 = c->order == ORC_PROBE_LAST ? (c->K - 1 < n_sup ? c->K - 1 : n_sup) : (c->probe ? c->m : 0);
+  int32_t* force = (int32_t*)malloc(sizeof(int32_t) * (size_t)n_rows);
+  for (int32_t r = 0; r < n_rows; ++r) force[r] = t0;
+  enum_layers(E, force, 0);
+  free(force);
+}
+
+int32_t orc_exact_law(const orc_cfg* cfg, int32_t max_len, const float* draft_tab, const float* target_tab,
+                      const int32_t* prefix, int32_t np, int32_t two, double* law1, double* law2,
+                      double* accept) {
+  if (cfg->mode != ORC_TOPR || cfg->trunc == ORC_DENSE || width_of(cfg) > 64) return -2;
+  const int32_t V = cfg->V;
+  double* fresh = (double*)malloc(sizeof(double) * (size_t)V * (size_t)V);
+  for (int64_t k = 0; k < (int64_t)V * V; ++k) fresh[k] = NAN;
+  for (int32_t v = 0; v < V; ++v) law1[v] = 0.0;
+  if (two)
+    for (int64_t k = 0; k < (int64_t)V * V; ++k) law2[k] = 0.0;
+  enum_ctx E = {cfg, max_len, draft_tab, target_tab, prefix, np, two, 0, law1, law2, 0.0, fresh};
+  enum_law(&E);
+  *accept = E.acc;
+  free(fresh);
+  return E.err;
 }
 
 int32_t orc_tree_mask(int32_t n, const int32_t* parent, uint8_t* mask, int32_t* pos) {

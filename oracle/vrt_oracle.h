@@ -24,9 +24,14 @@
  * Parity pins: every function is pinned by the tests in tests/test_oracle_*.py
  * (Philox known-answer vectors, exp_rank error bound, support vs lexsort,
  * the lemma, chi-square losslessness, closed-form acceptance, the textbook
- * speculative-sampling case, the identity case, the T->0 limit). The SMART
- * keep rule's readings (|P| = leaf count, L starts at 0, |T| counts the root)
- * are pinned only by hand-worked cases: parity unpinned beyond those.
+ * speculative-sampling case, the identity case, the T->0 limit; the beam and
+ * the top-R prune by hand-worked trees and by invariants against lexsort
+ * order; build and verification together by exact enumeration of the first-
+ * and two-token laws, which losslessness fixes to the target's softmax). The
+ * SMART keep rule's readings (|P| = leaf count, L starts at 0, |T| counts the
+ * root) are pinned only by hand-worked cases: parity unpinned beyond those.
+ * Which parents a layer expands (the top W of the layer by path score) is a
+ * reading of the pages; the pins fix that the oracle implements this reading.
  */
 #ifndef VRT_ORACLE_H
 #define VRT_ORACLE_H
@@ -137,6 +142,22 @@ int32_t orc_table_trials(const orc_cfg* cfg, int32_t max_len, const float* draft
                          const float* target_tab, uint64_t seed, int32_t b, uint32_t step0,
                          int32_t n_trials, int32_t two, int32_t* out, int32_t* n_first,
                          int32_t* n_exempt);
+
+/* Exact laws of one step on a context-table model (rows indexed as for
+ * orc_table_trials), for tiny top-R configurations with a truncated support: every probe
+ * draw and every accept/reject or final sample is taken as a branch weighted by its
+ * probability, through the same expansion and decision code the sampler runs.
+ *   law1[V]     P(first emitted token = v) of the step at context prefix[0..np)
+ *   law2[V*V]   (two != 0) P(first = a, second = b): the step's second token, or when the
+ *               step emitted one token the first token of the next step at prefix + a
+ *   accept      P(the first token comes from the tree)
+ * RheoSampling's highlights state that the step is lossless for any prune budget: law1 is
+ * then the target's tempered softmax at the context and law2 its two-step product.
+ * Returns 0, -1 if the table is too short for the paths, -2 for an unsupported
+ * configuration (SMART mode, dense support, W > 64). */
+int32_t orc_exact_law(const orc_cfg* cfg, int32_t max_len, const float* draft_tab, const float* target_tab,
+                      const int32_t* prefix, int32_t np, int32_t two, double* law1, double* law2,
+                      double* accept);
 
 /* The step after the prune (the target forward over the emitted tree, RheoSampling
  * framework flowchart: one target pass verifies the whole tree): node i may attend to

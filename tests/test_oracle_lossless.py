@@ -91,6 +91,7 @@ def test_first_two_tokens_follow_target_chain(kw, seed):
 def _depth1_acceptance(cfg, draft, target):
     """Closed-form P(first token comes from the tree) at the root, depth 1."""
     T, m, K, trunc, probe = cfg.T, cfg.m, cfg.K, cfg.trunc, cfg.probe
+    V = draft.size
     order = np.lexsort((np.arange(V), -draft.astype(np.float64)))[:min(trunc, V)]
     lv = draft[order].astype(np.float64)
     invT = np.float64(np.float32(1.0) / np.float32(T))

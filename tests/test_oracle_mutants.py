@@ -163,6 +163,37 @@ MUTANTS = [
 ]
 
 
+def exact_ok():
+    from tests.test_oracle_exact import exact_ok as ok
+    return ok()
+
+
+# the verification mistakes (and the build's tail mass, which the probe's law depends on),
+# each also caught by the exact enumeration of the first- and two-token laws and of the
+# depth-1 acceptance: no statistics involved
+EXACT = ["residual_mass_ignores_overlap", "probe_ratio_inverted", "tail_residual_not_clipped",
+         "rejected_sibling_not_removed", "verify_ignores_temperature",
+         "probe_last_ratio_ignores_residual_mass", "probe_last_tail_not_scaled",
+         "probe_last_tail_includes_fillers", "tail_mass_includes_top_m"]
+
+
+def _planted(tmp_path, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, name
+    mut = tmp_path / "vrt_oracle.c"
+    mut.write_text(src.replace(old, new))
+    shutil.copy(os.path.join(os.path.dirname(SRC), "vrt_oracle.h"), tmp_path / "vrt_oracle.h")
+    return obuild.build(src=str(mut), out=str(tmp_path / f"liboracle_{name}.so"))
+
+
+@pytest.mark.parametrize("name", EXACT)
+def test_exact_law_catches_planted_mistake(tmp_path, name):
+    old, new = {m[0]: (m[1], m[2]) for m in MUTANTS}[name]
+    assert exact_ok(), "the unmodified oracle must pass the exact pins"
+    with orc.using(_planted(tmp_path, name, old, new)):
+        assert not exact_ok(), f"planted mistake {name} went unnoticed by the exact enumeration"
+
+
 @pytest.mark.parametrize("name,old,new,check", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_pin_catches_planted_mistake(tmp_path, name, old, new, check):
     src = open(SRC).read()

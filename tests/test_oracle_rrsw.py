@@ -29,6 +29,7 @@ LAST = orc.PROBE_LAST
 
 def _depth1_rrsw(cfg, draft, target):
     T, m, K, trunc = cfg.T, cfg.m, cfg.K, cfg.trunc
+    V = draft.size
     order = np.lexsort((np.arange(V), -draft.astype(np.float64)))[:min(trunc, V)]
     lv = draft[order].astype(np.float64)
     invT = np.float64(np.float32(1.0) / np.float32(T))
