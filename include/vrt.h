@@ -158,7 +158,12 @@ typedef struct {
  * Build scratch:
  *   row_sync    u64 [B][FP]  where a layer's rows are split over two blocks, the tag
  *                            of the half that finished first (needs no initial
- *                            value) */
+ *                            value; the second half sets it back to 0)
+ * SMART mode only (empty otherwise), one table for the whole batch, not per tree:
+ *   smart_cost  f64 [budget+2][2]  C(n) and C'(n) of SMART key design 2 for tree sizes
+ *                            n = 0 .. budget+1, evaluated in fp64 by the host's libm
+ *                            and written by layer 0, so that the keep rule's decisions
+ *                            do not depend on the device's exp and pow */
 typedef struct {
   int64_t NC, NR, N, TC, FP;
   int64_t cand_token, cand_parent, cand_score, cand_kind;
@@ -168,6 +173,7 @@ typedef struct {
   int64_t child_off, child, tail_n, tail_id, tail_q;
   int64_t row_dense, row_det, node_row;
   int64_t row_sync;
+  int64_t smart_cost;
   int64_t total_bytes;
 } vrt_tree_layout;
 

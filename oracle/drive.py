@@ -80,3 +80,22 @@ class OracleStep:
     @property
     def exempt(self):
         return self.build_exempt + getattr(self, "verify_exempt", 0)
+
+    def replay(self):
+        """The oracle alone on this step's stored inputs (the draft rows of every layer in
+        frontier order, the target rows of the emitted nodes): every build layer, the
+        finish and the verification, as in __init__. Returns the emitted tokens."""
+        t = orc.Tree(self.cfg, self.seed, self.b, self.step)
+        for layer, rows in enumerate(self.layer_rows):
+            t.expand_layer(layer, synth.to_f32(rows))
+        t.finish()
+        view = t.view()
+        toks, _, _, _ = orc.verify(self.cfg, view, synth.to_f32(self.target_rows), self.seed, self.b,
+                                   self.step)
+        return toks
+
+
+def decode_keys(w, root_keys, tokens):
+    """Root keys of the next decode step: each tree's context extended by the tokens its
+    step emitted (the generator's node-key chain)."""
+    return [synth.path_key(int(k), [int(t) for t in toks]) for k, toks in zip(root_keys, tokens)]

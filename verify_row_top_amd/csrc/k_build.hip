@@ -1061,13 +1061,6 @@ __device__ __forceinline__ void rank_if_last(const BArgs& a, int b, uint64_t* s_
   if (lane == 0) a.t.layer_sync[b] = 0;
 }
 
-__device__ __forceinline__ void st_dev64(uint64_t* p, uint64_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t ld_dev64(const uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // A row split over two blocks, wave 0 of each: every block has the top TC of its half
 // of the row in s_sup (n_sup keys, sorted); the row's top TC are among the two lists.
 // Each block writes its list and status device-coherently, waits for the stores and
@@ -1095,6 +1088,9 @@ __device__ __forceinline__ bool join_halves(const BArgs& a, int b, int j, int h,
   }
   second = __shfl(second, 0, kWave);
   if (!second) return false;
+  // both halves have swapped their tags in: the word goes back to 0, so that a launch
+  // repeated with the same arguments (a replayed graph, the same epoch) starts afresh
+  if (lane == 0) st_dev64(&a.t.row_sync[r], 0ull);
   const uint64_t* other = a.half_keys + (r * 2 + (1 - h)) * N;
   const int om = ld_dev(&a.half_meta[r * 2 + (1 - h)]);
   uint64_t top[PL], add[PL];
@@ -1547,8 +1543,9 @@ __device__ void rank_sorted(const Cfg& c, const TreePtrs& t, int layer, int b, c
       if (nadm >= (double)c.budget) break;
       const int cu = (int)(0xFFFFFFFFu - (uint32_t)keys[i]);
       const double g = (double)ld_dev(&t.cand_score[ncb + cu]) / P;
-      const double Cn = c.lam * n + c.gam * (exp(c.del * pow(n, c.rho)) - 1.0);
-      const double dC = c.lam + c.gam * c.del * c.rho * pow(n, c.rho - 1.0) * exp(c.del * pow(n, c.rho));
+      // C(|T|) and C'(|T|) from the host's fp64 table (|T| = n is 1 .. budget+1 here)
+      const int ni = min(max((int)n, 0), c.budget + 1);
+      const double Cn = t.smart_cost[2 * ni], dC = t.smart_cost[2 * ni + 1];
       if (!(c.alpha * g * Cn > L * dC)) break;
       const int par = ld_dev(&t.cand_parent[ncb + cu]);
       const bool has = par < 0 ? root_has != 0.0 : (t.cand_kind[ncb + par] & 0x100) != 0;
@@ -1830,6 +1827,18 @@ __global__ __launch_bounds__(kFT) void k_finish(const Cfg c, const TreePtrs t) {
   }
 }
 
+// Host values into device memory through kernel arguments, kFillChunk per launch.
+constexpr int kFillChunk = 128;
+struct FillArgs {
+  double* dst;
+  int n;
+  double v[kFillChunk];
+};
+
+__global__ __launch_bounds__(kFillChunk) void k_fill_f64(const FillArgs f) {
+  if ((int)threadIdx.x < f.n) f.dst[threadIdx.x] = f.v[threadIdx.x];
+}
+
 int list_len(const Cfg& c) { return max(128, next_pow2(c.trunc)); }
 
 template <int DT, bool SPLIT>
@@ -1917,6 +1926,19 @@ hipError_t launch_build_layer(const Cfg& c, const TreePtrs& t, int layer, const 
   const size_t lds2 = (size_t)next_pow2(max(span, 2)) * 8;
   hipLaunchKernelGGL(k_rank_layer, dim3(c.B), dim3(256), lds2, stream, c, t, layer);
   return hipGetLastError();
+}
+
+hipError_t launch_fill_f64(double* dst, const double* vals, int n, hipStream_t stream) {
+  for (int o = 0; o < n; o += kFillChunk) {
+    FillArgs f;
+    f.dst = dst + o;
+    f.n = min(kFillChunk, n - o);
+    for (int k = 0; k < f.n; ++k) f.v[k] = vals[o + k];
+    hipLaunchKernelGGL(k_fill_f64, dim3(1), dim3(kFillChunk), 0, stream, f);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_build_finish(const Cfg& c, const TreePtrs& t, void* ws, hipStream_t stream) {

@@ -1,5 +1,6 @@
-// Tree verification (RheoSampling, key design 3) on gfx950: two kernels, or one for the
-// lazy walk.
+// Tree verification (RheoSampling, key design 3) on gfx950: one launch per call (the
+// node pass with the walk fused into its last block of each tree), or the two parts
+// apart, or the lazy walk.
 //
 // k_vnode: one 512-thread block per (node row, tree).
 //   - The eight waves stream the node's target row from HBM once, in 2048-element
@@ -18,10 +19,16 @@
 //     one 2048-element re-read finds the token). Every draw is keyed by (depth, test
 //     index), so each node's decision is a pure function of its own row; other blocks'
 //     streams hide its latency.
+//   With the walk fused (vrt_verify_tree), each block writes its decision device-
+//   coherently and counts itself on its tree's word in the workspace; the block that
+//   counts the tree's last node follows the accepted children from the root.
 // k_vwalk: one wave per tree follows the accepted children from the root and writes
-//   the emitted tokens and statistics.
+//   the emitted tokens and statistics (the walk as a launch of its own).
 // k_vlazy: one block per tree decides the root, then the accepted child, ... each node
 //   by k_vnode's pass, so only the rows on the walk are read.
+#include <atomic>
+#include <random>
+
 #include "vrt_dev.hpp"
 #include "vrt_internal.hpp"
 
@@ -71,7 +78,20 @@ struct VArgs {
   uint32_t* stats;
   const void* draft[32];  // dense rows: layer l's draft rows (as passed to the build)
   int64_t dld, dstride;
+  uint64_t* vsync;  // fused walk: per tree, this launch's tag << 32 | status << 24 | nodes done
+  uint32_t tag;     // fused walk: this launch's tag (never 0)
 };
+
+// A node's decision into node_out, device-coherently (the fused walk reads it from
+// another block), and into the block's record.
+__device__ __forceinline__ void put_out(const VArgs& a, int64_t at, const NodeOut& out, VRec& R) {
+  int* o = (int*)&a.node_out[at];
+  st_dev(o, out.accept);
+  st_dev(o + 1, out.token);
+  st_dev(o + 2, out.flags);
+  st_dev((float*)(o + 3), out.W);
+  R.res = out;
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -460,7 +480,7 @@ __device__ void decide_node(const VArgs& a, int b, int i, const char* row, const
   NodeOut out{-1, -1, 0, 0.0f};
   if (!(S > 0.0) || !(S < INFINITY) || !(MC < INFINITY)) {
     out.flags = (int)(VRT_ST_TARGET_BAD << 16);
-    if (lane == 0) a.node_out[nb + i] = out, R.res = out;
+    if (lane == 0) put_out(a, nb + i, out, R);
     return;
   }
   const double invS = 1.0 / S;
@@ -752,7 +772,7 @@ __device__ void decide_node(const VArgs& a, int b, int i, const char* row, const
   out.accept = accept;
   out.flags = min(tests, 255) | (min(near, 255) << 8);
   if (accept < 0) out.W = (float)W;
-  if (lane == 0) a.node_out[nb + i] = out, R.res = out;
+  if (lane == 0) put_out(a, nb + i, out, R);
 }
 
 constexpr int kMaxChunks = (1 << 20) / kCH;  // V <= 2^20
@@ -806,8 +826,11 @@ __device__ __forceinline__ void node_pass(const VArgs& a, int b, int i, int nn, 
   if (wave == 0) decide_node<DT, DENSE>(a, b, i, row, s_cs, s_rec, L);
 }
 
-// One block per (node, tree): that node's pass.
-template <int DT>
+__device__ void walk_if_last(const VArgs& a, int b, int nn, uint32_t st_node);
+
+// One block per (node, tree): that node's pass; WALK: then the tree's walk if this block
+// is the last of its tree to finish.
+template <int DT, bool WALK>
 __global__ __launch_bounds__(kVB) void k_vnode(const VArgs a) {
   const Cfg& c = a.c;
   const int b = blockIdx.y;
@@ -820,10 +843,16 @@ __global__ __launch_bounds__(kVB) void k_vnode(const VArgs a) {
   extern __shared__ double s_dyn[];
   const DLds L = carve((char*)s_dyn, (c.V + kCH - 1) / kCH, c.TC);
   node_pass<DT, kVB>(a, b, i, nn, s_cs, s_rec, L, s_next);
+  if constexpr (WALK) {
+    if ((threadIdx.x >> 6) == 0) {
+      wave_sync();  // s_rec.res, written by lane 0
+      walk_if_last(a, b, nn, (uint32_t)s_rec.res.flags >> 16);
+    }
+  }
 }
 
 // Dense rows: the same pass with the probe tails regenerated from the draft rows.
-template <int DT>
+template <int DT, bool WALK>
 __global__ __launch_bounds__(kVB) void k_vnode_dense(const VArgs a) {
   const Cfg& c = a.c;
   const int b = blockIdx.y;
@@ -836,6 +865,12 @@ __global__ __launch_bounds__(kVB) void k_vnode_dense(const VArgs a) {
   extern __shared__ double s_dyn[];
   const DLds L = carve((char*)s_dyn, (c.V + kCH - 1) / kCH, c.TC);
   node_pass<DT, kVB, true>(a, b, i, nn, s_cs, s_rec, L, s_next);
+  if constexpr (WALK) {
+    if ((threadIdx.x >> 6) == 0) {
+      wave_sync();
+      walk_if_last(a, b, nn, (uint32_t)s_rec.res.flags >> 16);
+    }
+  }
 }
 
 // Emitted tokens, nodes and statistics of tree b once its walk has ended (len tokens).
@@ -943,37 +978,131 @@ __global__ __launch_bounds__(kWave) void k_vwalk(const VArgs a) {
   walk_outputs(a, b, len, st, probe, near, visited);
 }
 
+// The walk of tree b by one wave, reading the decisions written device-coherently by the
+// tree's node blocks: the decisions of 64 consecutive nodes are loaded at a time (one lane
+// each), and the walk moves to the chunk holding the next node when it leaves the loaded
+// one (children follow their parents, so chunks are visited in order).
+__device__ void walk_tree(const VArgs& a, int b, int nn, uint32_t st) {
+  const Cfg& c = a.c;
+  const int lane = lane_id();
+  const int64_t nb = (int64_t)b * c.N;
+  int c0 = -1, m_acc = -1, m_tok = -1, m_fl = 0, m_ntok = -1, m_kind = 0;
+  auto load_chunk = [&](int cc) {
+    c0 = cc;
+    const int i = cc + lane;
+    m_acc = -1, m_tok = -1, m_fl = 0, m_ntok = -1, m_kind = 0;
+    if (i < nn) {
+      const int* o = (const int*)&a.node_out[nb + i];
+      m_acc = ld_dev(o);
+      m_tok = ld_dev(o + 1);
+      m_fl = ld_dev(o + 2);
+      m_ntok = a.t.node_token[nb + i];
+      m_kind = a.t.node_kind[nb + i];
+    }
+  };
+  load_chunk(0);
+  int cur = 0, len = 0, near = 0, probe = 0, visited = 0;
+  for (int step = 0; step <= c.D; ++step) {
+    const int l = cur - c0;
+    const int acc = __builtin_amdgcn_readlane(m_acc, l);
+    const int tok = __builtin_amdgcn_readlane(m_tok, l);
+    const int fl = __builtin_amdgcn_readlane(m_fl, l);
+    ++visited;
+    near += (fl >> 8) & 0xFF;
+    if (acc > cur && acc < nn && len < c.D) {
+      if ((acc & ~(kWave - 1)) != c0) load_chunk(acc & ~(kWave - 1));
+      const int l2 = acc - c0;
+      const int ntok = __builtin_amdgcn_readlane(m_ntok, l2);
+      if (__builtin_amdgcn_readlane(m_kind, l2) == VRT_PROBE) probe = 1;
+      if (lane == 0) {
+        a.out_nodes[(int64_t)b * c.D + len] = acc;
+        a.out_tokens[(int64_t)b * (c.D + 1) + len] = ntok;
+      }
+      ++len;
+      cur = acc;
+    } else {
+      if (lane == 0) a.out_tokens[(int64_t)b * (c.D + 1) + len] = tok;
+      ++len;
+      break;
+    }
+  }
+  if (lane == 0) walk_outputs(a, b, len, st, probe, near, visited);
+}
+
+// Wave 0 of a node block once its decision is stored: counts the node done on tree b's
+// word (the launch's tag in the high half: a word left by another launch, or garbage,
+// restarts the count; status bits accumulate), and the block that counts the tree's last
+// node sets the word back to 0 (so a replay with the same tag starts afresh) and walks.
+__device__ void walk_if_last(const VArgs& a, int b, int nn, uint32_t st_node) {
+  const int lane = lane_id();
+  wait_stores();  // this node's decision is written before it is counted
+  unsigned long long word = 0ull;
+  if (lane == 0) {
+    unsigned long long* p = (unsigned long long*)(a.vsync + b);
+    unsigned long long old = ld_dev64((const uint64_t*)p);
+    for (;;) {
+      const unsigned long long base = (uint32_t)(old >> 32) == a.tag ? old : ((unsigned long long)a.tag << 32);
+      const unsigned long long nxt = (base + 1ull) | ((unsigned long long)(st_node & 0xFFu) << 24);
+      const unsigned long long seen = atomicCAS(p, old, nxt);
+      if (seen == old) {
+        word = nxt;
+        break;
+      }
+      old = seen;
+    }
+  }
+  word = shfl64(word, 0);
+  if ((int)(word & 0xFFFFFFull) != nn) return;
+  if (lane == 0) st_dev64(a.vsync + b, 0ull);
+  walk_tree(a, b, nn, (uint32_t)(word >> 24) & 0xFFu);
+}
+
+// Tags of fused launches: a process-wide counter from a random start, never 0.
+std::atomic<uint32_t> g_vtag{(uint32_t)std::random_device{}()};
+
 }  // namespace
 
-size_t verify_ws_bytes(const Cfg& c) {
-  (void)c;
-  return 0;
-}
+size_t verify_ws_bytes(const Cfg& c) { return (size_t)c.B * 8; }
 
 hipError_t launch_verify(int parts, const Cfg& c, const TreePtrs& t, const void* logits, int64_t ld,
                          int64_t tstride, uint64_t seed, uint32_t step, NodeOut* node_out,
                          int32_t* out_tokens, int32_t* out_nodes, int32_t* out_len, uint32_t* stats,
                          void* ws, const void* const* draft, int64_t dld, int64_t dstride,
                          hipStream_t stream) {
-  (void)ws;
   VArgs a{c, t, logits, ld, tstride, seed, step, node_out, out_tokens, out_nodes, out_len, stats, {}, dld,
-          dstride};
+          dstride, (uint64_t*)ws, 0u};
   for (int l = 0; l < c.D && l < 32 && draft; ++l) a.draft[l] = draft[l];
+  const bool fused = (parts & 3) == 3;  // the nodes and the walk in one launch
+  if (fused) {
+    uint32_t tag;
+    do tag = g_vtag.fetch_add(1); while (tag == 0u);
+    a.tag = tag;
+  }
   if (parts & 1) {
     const dim3 grid(c.N, c.B);
     const size_t lds = decide_lds_bytes(c);
     const bool dense = (parts & 8) != 0;
     if (c.dtype == VRT_BF16) {
-      if (dense) hipLaunchKernelGGL(k_vnode_dense<VRT_BF16>, grid, dim3(kVB), lds, stream, a);
-      else hipLaunchKernelGGL(k_vnode<VRT_BF16>, grid, dim3(kVB), lds, stream, a);
+      if (dense) {
+        if (fused) hipLaunchKernelGGL((k_vnode_dense<VRT_BF16, true>), grid, dim3(kVB), lds, stream, a);
+        else hipLaunchKernelGGL((k_vnode_dense<VRT_BF16, false>), grid, dim3(kVB), lds, stream, a);
+      } else {
+        if (fused) hipLaunchKernelGGL((k_vnode<VRT_BF16, true>), grid, dim3(kVB), lds, stream, a);
+        else hipLaunchKernelGGL((k_vnode<VRT_BF16, false>), grid, dim3(kVB), lds, stream, a);
+      }
     } else {
-      if (dense) hipLaunchKernelGGL(k_vnode_dense<VRT_F32>, grid, dim3(kVB), lds, stream, a);
-      else hipLaunchKernelGGL(k_vnode<VRT_F32>, grid, dim3(kVB), lds, stream, a);
+      if (dense) {
+        if (fused) hipLaunchKernelGGL((k_vnode_dense<VRT_F32, true>), grid, dim3(kVB), lds, stream, a);
+        else hipLaunchKernelGGL((k_vnode_dense<VRT_F32, false>), grid, dim3(kVB), lds, stream, a);
+      } else {
+        if (fused) hipLaunchKernelGGL((k_vnode<VRT_F32, true>), grid, dim3(kVB), lds, stream, a);
+        else hipLaunchKernelGGL((k_vnode<VRT_F32, false>), grid, dim3(kVB), lds, stream, a);
+      }
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (parts & 2)
+  if ((parts & 2) && !fused)
     hipLaunchKernelGGL(k_vwalk, dim3(c.B), dim3(kWave), (size_t)c.N * (16 + 4 + 4), stream, a);
   if (parts & 4) {
     const size_t lds = decide_lds_bytes(c);

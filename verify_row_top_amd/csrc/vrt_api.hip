@@ -65,6 +65,7 @@ bool compute_layout(const vrt_config& c, vrt_tree_layout* L) {
   take(&L->row_det, dense * B * L->NR * 32 * 4);
   take(&L->node_row, dense * B * L->N * 4);
   take(&L->row_sync, B * L->FP * 8);
+  take(&L->smart_cost, c.mode == VRT_MODE_SMART ? (int64_t)(c.budget + 2) * 2 * 8 : 0);
   L->total_bytes = off;
   return true;
 }
@@ -91,6 +92,18 @@ WsLayout ws_layout(const vrt_config& c) {
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// SMART key design 2's cost models and the derivative the keep rule uses, in fp64 with
+// this host's libm, for tree sizes n = 0 .. budget+1: C(n) = lambda n + gamma (e^{delta
+// n^rho} - 1) and C'(n) = lambda + gamma delta rho n^{rho-1} e^{delta n^rho}, each
+// evaluated left to right as written.
+void smart_cost_table(const vrt_config& c, double* tab) {
+  for (int n = 0; n <= c.budget + 1; ++n) {
+    const double x = (double)n;
+    tab[2 * n] = c.lambda_ * x + c.gamma_ * (exp(c.delta_ * pow(x, c.rho_)) - 1.0);
+    tab[2 * n + 1] = c.lambda_ + c.gamma_ * c.delta_ * c.rho_ * pow(x, c.rho_ - 1.0) * exp(c.delta_ * pow(x, c.rho_));
+  }
+}
 
 vrt_status check_rows(const vrt_config& c, const void* p, int64_t ld, int64_t tstride,
                       const char* what) {
@@ -157,6 +170,7 @@ TreePtrs tree_ptrs(const vrt_config& c, void* blob) {
   t.row_det = (int*)(p + L.row_det);
   t.node_row = (int*)(p + L.node_row);
   t.row_sync = (uint64_t*)(p + L.row_sync);
+  t.smart_cost = (double*)(p + L.smart_cost);
   return t;
 }
 
@@ -246,11 +260,19 @@ vrt_status vrt_build_tree(const vrt_config* cp, int32_t layer, const void* draft
   const vrt::Cfg k = vrt::make_cfg(c);
   const vrt::TreePtrs t = vrt::tree_ptrs(c, tree);
   hipError_t e;
-  if (layer == VRT_FINISH)
+  if (layer == VRT_FINISH) {
     e = vrt::launch_build_finish(k, t, (char*)ws + wl.build, (hipStream_t)stream);
-  else
-    e = vrt::launch_build_layer(k, t, layer, draft_logits, ld, tree_stride, seed, (uint32_t)step,
-                                stats, (char*)ws + wl.build, (hipStream_t)stream);
+  } else {
+    e = hipSuccess;
+    if (layer == 0 && c.mode == VRT_MODE_SMART) {  // the keep rule's cost table, for this step
+      double tab[2 * (1024 + 2)];
+      smart_cost_table(c, tab);
+      e = vrt::launch_fill_f64(t.smart_cost, tab, 2 * (c.budget + 2), (hipStream_t)stream);
+    }
+    if (e == hipSuccess)
+      e = vrt::launch_build_layer(k, t, layer, draft_logits, ld, tree_stride, seed, (uint32_t)step,
+                                  stats, (char*)ws + wl.build, (hipStream_t)stream);
+  }
   if (e != hipSuccess) return fail(VRT_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
   return VRT_OK;
 }

@@ -52,6 +52,7 @@ struct TreePtrs {
   int* row_det;       // dense rows: [NR][32] deterministic children's tokens
   int* node_row;      // dense rows: [N] expansion row of a node whose probe is kept
   uint64_t* row_sync;  // [FP] tag of the half of a split row that finished first
+  double* smart_cost;  // SMART: [budget+2][2] C(n), C'(n) for n = 0 .. budget+1 (one table)
 };
 
 // Per-node verification outcome: accepted child node (-1: none), final token
@@ -92,6 +93,10 @@ hipError_t launch_build_layer(const Cfg& c, const TreePtrs& t, int layer, const 
                               int64_t ld, int64_t tstride, uint64_t seed, uint32_t step,
                               uint32_t* stats, void* ws, hipStream_t stream);
 hipError_t launch_build_finish(const Cfg& c, const TreePtrs& t, void* ws, hipStream_t stream);
+
+// Copies n host-computed doubles into device memory at dst through kernel arguments (no
+// host buffer outlives the call, and the copy is an ordinary kernel on the stream).
+hipError_t launch_fill_f64(double* dst, const double* vals, int n, hipStream_t stream);
 
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
 

@@ -43,7 +43,7 @@ class TreeLayout(ctypes.Structure):
         "row_tail_n", "row_tail_id", "row_tail_q", "front", "n_front", "smart", "admitted", "layer_sync",
         "n_nodes", "node_token", "node_parent", "node_depth", "node_kind", "node_cand",
         "child_off", "child", "tail_n", "tail_id", "tail_q", "row_dense", "row_det", "node_row",
-        "row_sync", "total_bytes")]
+        "row_sync", "smart_cost", "total_bytes")]
 
 
 _lib = None
