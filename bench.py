@@ -101,7 +101,13 @@ def cpu_baseline(w, seed, n_trees):
     (its C calls release the interpreter lock), timed by the wall clock."""
     import concurrent.futures as cf
 
+    import torch  # noqa: F401  (first: the helper libraries then share torch's HIP runtime)
+
+    import synth
+    from oracle import oracle as orc
     from oracle.drive import OracleStep
+    synth.lib()  # loaded once, in this thread, before the pool starts
+    orc.lib()
     cores = len(os.sched_getaffinity(0))
     n_trees = n_trees or min(64, 4 * cores)
     with cf.ThreadPoolExecutor(max_workers=cores) as ex:
@@ -365,6 +371,7 @@ def decode_inputs(w, cfg, dev, n_sets, seed, tree, ws, stats, views, out):
                      "near": int(st[:, 3].sum()), "bad": int((st[:, 0] != 0).sum()),
                      "tokens": float(lens.sum())})
         rk = decode_keys(w, rk, emitted)
+    print(f"bench: {n_sets} decode steps of {w.name} (T={w.T}) made", file=sys.stderr, flush=True)
     return sets
 
 
@@ -527,6 +534,9 @@ def main():
     from synth import workloads
     w = workloads.get(args.workload, T=args.T)
     cpu = None if args.no_cpu else cpu_baseline(w, args.seed, args.cpu_trees)
+    if cpu is not None:
+        print(f"bench: oracle baseline {cpu['value']:.2f} trees/s on {cpu['cores']} cores", file=sys.stderr,
+              flush=True)
 
     import torch
 

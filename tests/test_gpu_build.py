@@ -54,8 +54,13 @@ CASES = [
     ("small_trunc1024_flat_fp32", _small(trunc=1024, V=30000, dtype=synth.F32, zipf=(0.8,), R=30, D=3)),
     ("small_trunc700_flat", _small(trunc=700, V=12000, zipf=(0.8,), R=24, D=3)),
     ("small_trunc513_V1500", _small(trunc=513, V=1500, R=24, D=3)),
-    # rows too long for one block's row-wide path: split over two blocks after layer 0
+    # rows too long for one block's row-wide path are split over two blocks at every layer
+    # (fp32 rows of 65537 to 131072 values, bf16 rows of 196609 to 393216); longer rows
+    # take the exact radix path over the whole row
     ("split_fp32_V70000", _small(dtype=synth.F32, V=70000, R=30, D=4)),
+    ("exact_path_fp32_V140000", _small(dtype=synth.F32, V=140000, R=20, D=3, B=2)),
+    ("exact_path_fp32_V151936_ties", _small(dtype=synth.F32, V=151936, R=16, D=3, B=2, zipf=(),
+                                            draft_scale=0.0)),
     ("split_bf16_V200000_trunc256", _small(V=200000, R=30, D=3, trunc=256)),
     ("split_fp32_flat_ties", _small(dtype=synth.F32, V=66000, zipf=(), draft_scale=0.0, R=20, D=3)),
     ("split_smart_fp32", _smart_small(dtype=synth.F32, V=70000, budget=30, D=4)),
@@ -159,7 +164,7 @@ def test_build_and_step_match_oracle(gpu, name, w):
 @pytest.mark.parametrize("kw", [
     dict(), dict(dtype=synth.F32, V=70001), dict(trunc=vrt.DENSE),
     dict(trunc=vrt.DENSE, dtype=synth.F32, V=70001)],
-    ids=["bf16", "fp32_exact_path", "dense_bf16", "dense_fp32"])
+    ids=["bf16", "fp32_split", "dense_bf16", "dense_fp32"])
 def test_bad_draft_rows_set_status_and_stay_in_bounds(gpu, kw):
     w = _small(B=3, D=2, R=10, **kw)
     steps = [OracleStep(w, 5, b, 0, verify=False) for b in range(w.B)]

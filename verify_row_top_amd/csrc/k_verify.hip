@@ -40,6 +40,9 @@ constexpr int kCH = 2048;       // elements per chunk (one wave at a time)
 constexpr int kChildMax = 32;   // K <= 30
 constexpr float kBand = 1e-6f;  // near-tie band reported in the stats
 constexpr double kFix = 1152921504606846976.0;  // 2^60: fixed point of the mass changes
+// Per-tree counters of the fused walk, one 4 KB line apart: the device-coherent atomics
+// on one line are executed one after another, so the trees' counters must not share one.
+constexpr int kSyncStride = 512;  // u64 words
 
 // What the decision of one node needs besides its row statistics (gathered by the
 // streaming kernel): kept children in slot order and their logits.
@@ -78,7 +81,7 @@ struct VArgs {
   uint32_t* stats;
   const void* draft[32];  // dense rows: layer l's draft rows (as passed to the build)
   int64_t dld, dstride;
-  uint64_t* vsync;  // fused walk: per tree, this launch's tag << 32 | status << 24 | nodes done
+  uint64_t* vsync;  // fused walk: per tree (kSyncStride words apart), tag << 32 | status << 24 | done
   uint32_t tag;     // fused walk: this launch's tag (never 0)
 };
 
@@ -826,6 +829,7 @@ __device__ __forceinline__ void node_pass(const VArgs& a, int b, int i, int nn, 
   if (wave == 0) decide_node<DT, DENSE>(a, b, i, row, s_cs, s_rec, L);
 }
 
+__device__ void install_tag(const VArgs& a, int b);
 __device__ void walk_if_last(const VArgs& a, int b, int nn, uint32_t st_node);
 
 // One block per (node, tree): that node's pass; WALK: then the tree's walk if this block
@@ -833,8 +837,8 @@ __device__ void walk_if_last(const VArgs& a, int b, int nn, uint32_t st_node);
 template <int DT, bool WALK>
 __global__ __launch_bounds__(kVB) void k_vnode(const VArgs a) {
   const Cfg& c = a.c;
-  const int b = blockIdx.y;
-  const int i = blockIdx.x;
+  const int b = blockIdx.x;  // trees vary fastest: blocks that finish together belong to
+  const int i = blockIdx.y;  // different trees, whose counters sit on different lines
   const int nn = clamp_nodes(a.t.n_nodes[b], c.N);
   if (i >= nn) return;
   __shared__ float2 s_cs[kMaxChunks];
@@ -842,6 +846,9 @@ __global__ __launch_bounds__(kVB) void k_vnode(const VArgs a) {
   __shared__ int s_next;
   extern __shared__ double s_dyn[];
   const DLds L = carve((char*)s_dyn, (c.V + kCH - 1) / kCH, c.TC);
+  // the tree's counter word carries this launch's tag before any block counts on it;
+  // the gathering wave (whose dependent loads have slack behind the stream) sees to it
+  if (WALK && threadIdx.x == kVB - kWave) install_tag(a, b);
   node_pass<DT, kVB>(a, b, i, nn, s_cs, s_rec, L, s_next);
   if constexpr (WALK) {
     if ((threadIdx.x >> 6) == 0) {
@@ -855,8 +862,8 @@ __global__ __launch_bounds__(kVB) void k_vnode(const VArgs a) {
 template <int DT, bool WALK>
 __global__ __launch_bounds__(kVB) void k_vnode_dense(const VArgs a) {
   const Cfg& c = a.c;
-  const int b = blockIdx.y;
-  const int i = blockIdx.x;
+  const int b = blockIdx.x;
+  const int i = blockIdx.y;
   const int nn = clamp_nodes(a.t.n_nodes[b], c.N);
   if (i >= nn) return;
   __shared__ float2 s_cs[kMaxChunks];
@@ -864,6 +871,7 @@ __global__ __launch_bounds__(kVB) void k_vnode_dense(const VArgs a) {
   __shared__ int s_next;
   extern __shared__ double s_dyn[];
   const DLds L = carve((char*)s_dyn, (c.V + kCH - 1) / kCH, c.TC);
+  if (WALK && threadIdx.x == kVB - kWave) install_tag(a, b);
   node_pass<DT, kVB, true>(a, b, i, nn, s_cs, s_rec, L, s_next);
   if constexpr (WALK) {
     if ((threadIdx.x >> 6) == 0) {
@@ -1029,31 +1037,38 @@ __device__ void walk_tree(const VArgs& a, int b, int nn, uint32_t st) {
   if (lane == 0) walk_outputs(a, b, len, st, probe, near, visited);
 }
 
-// Wave 0 of a node block once its decision is stored: counts the node done on tree b's
-// word (the launch's tag in the high half: a word left by another launch, or garbage,
-// restarts the count; status bits accumulate), and the block that counts the tree's last
-// node sets the word back to 0 (so a replay with the same tag starts afresh) and walks.
+// The fused walk's per-tree word: tag << 32 | status << 24 | nodes counted. At its start
+// each node block makes sure the word carries this launch's tag: a word left by another
+// launch, or garbage, is replaced by the bare tag by compare-and-swap (only the first
+// blocks of a tree find it stale; a failed swap returns the word another block installed).
+// Every block checks this before it counts, so no count precedes the tree's install, and
+// the word keeps the tag until the tree's last block resets it.
+__device__ void install_tag(const VArgs& a, int b) {
+  unsigned long long* p = (unsigned long long*)(a.vsync + (int64_t)b * kSyncStride);
+  const unsigned long long tag = (unsigned long long)a.tag << 32;
+  unsigned long long v = ld_dev64((const uint64_t*)p);
+  while ((v & 0xFFFFFFFF00000000ull) != tag) {
+    const unsigned long long seen = atomicCAS(p, v, tag);
+    v = seen == v ? tag : seen;
+  }
+}
+
+// Wave 0 of a node block once its decision is stored: status bits are OR-ed into the
+// tree's word and one atomic add counts the node, so no block retries against the others.
+// The block that counts the tree's last node sets the word back to 0 (a replay with the
+// same tag then starts afresh) and walks the tree.
 __device__ void walk_if_last(const VArgs& a, int b, int nn, uint32_t st_node) {
   const int lane = lane_id();
   wait_stores();  // this node's decision is written before it is counted
   unsigned long long word = 0ull;
   if (lane == 0) {
-    unsigned long long* p = (unsigned long long*)(a.vsync + b);
-    unsigned long long old = ld_dev64((const uint64_t*)p);
-    for (;;) {
-      const unsigned long long base = (uint32_t)(old >> 32) == a.tag ? old : ((unsigned long long)a.tag << 32);
-      const unsigned long long nxt = (base + 1ull) | ((unsigned long long)(st_node & 0xFFu) << 24);
-      const unsigned long long seen = atomicCAS(p, old, nxt);
-      if (seen == old) {
-        word = nxt;
-        break;
-      }
-      old = seen;
-    }
+    unsigned long long* p = (unsigned long long*)(a.vsync + (int64_t)b * kSyncStride);
+    if (st_node & 0xFFu) atomicOr(p, (unsigned long long)(st_node & 0xFFu) << 24);
+    word = atomicAdd(p, 1ull) + 1ull;
   }
   word = shfl64(word, 0);
   if ((int)(word & 0xFFFFFFull) != nn) return;
-  if (lane == 0) st_dev64(a.vsync + b, 0ull);
+  if (lane == 0) st_dev64(a.vsync + (int64_t)b * kSyncStride, 0ull);
   walk_tree(a, b, nn, (uint32_t)(word >> 24) & 0xFFu);
 }
 
@@ -1062,7 +1077,7 @@ std::atomic<uint32_t> g_vtag{(uint32_t)std::random_device{}()};
 
 }  // namespace
 
-size_t verify_ws_bytes(const Cfg& c) { return (size_t)c.B * 8; }
+size_t verify_ws_bytes(const Cfg& c) { return (size_t)c.B * kSyncStride * 8; }
 
 hipError_t launch_verify(int parts, const Cfg& c, const TreePtrs& t, const void* logits, int64_t ld,
                          int64_t tstride, uint64_t seed, uint32_t step, NodeOut* node_out,
@@ -1079,7 +1094,7 @@ hipError_t launch_verify(int parts, const Cfg& c, const TreePtrs& t, const void*
     a.tag = tag;
   }
   if (parts & 1) {
-    const dim3 grid(c.N, c.B);
+    const dim3 grid(c.B, c.N);
     const size_t lds = decide_lds_bytes(c);
     const bool dense = (parts & 8) != 0;
     if (c.dtype == VRT_BF16) {
