@@ -31,8 +31,9 @@ def parse():
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--cpu-trees", type=int, default=0,
                     help="trees in the oracle's timed sample (0: four per host core)")
-    ap.add_argument("--sets", type=int, default=32,
-                    help="decode steps made as input sets; the timed steps rotate over them")
+    ap.add_argument("--sets", type=int, default=0,
+                    help="decode steps made as input sets; the timed steps rotate over them (0: "
+                         "the workload's decode length, as many as half the free HBM holds)")
     ap.add_argument("--t06-sets", type=int, default=8,
                     help="decode steps of the T=0.6 measurement (0: skip it)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
@@ -401,6 +402,9 @@ def measure(w, args, n_sets, lazy=True):
     out_nodes = torch.zeros((B, D), dtype=torch.int32, device=dev)
     out_len = torch.zeros(B, dtype=torch.int32, device=dev)
     seed = args.seed
+    if n_sets <= 0:  # the whole decode, if half the free memory holds its rows
+        per_set = B * (n_draft + N) * ld * esz
+        n_sets = max(3, min(w.steps, int(0.5 * torch.cuda.mem_get_info()[0] // per_set)))
     sets = decode_inputs(w, cfg, dev, n_sets, seed, tree, ws, stats, views, (out_tokens, out_nodes, out_len))
 
     def layer_rows(draft, layer):
@@ -437,12 +441,13 @@ def measure(w, args, n_sets, lazy=True):
         one_step(k)
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    k0 = args.warmup  # the timed steps continue the decode after the warm-up steps
     t0 = time.perf_counter()
     for k in range(args.steps):
-        one_step(k, evs[k])
+        one_step(k0 + k, evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    used = [sets[k % len(sets)] for k in range(args.steps)]
+    used = [sets[(k0 + k) % len(sets)] for k in range(args.steps)]
     build_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     vt = sorted(e[1].elapsed_time(e[2]) for e in evs)
     verify_ms = sum(vt) / len(vt)

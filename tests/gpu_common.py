@@ -110,11 +110,12 @@ class Lib:
         return self.views[name].cpu().numpy()
 
 
-def device_step(w, seed, step, dev, verify=True, keep_target=False):
+def device_step(w, seed, step, dev, verify=True, keep_target=False, root_keys=None):
     """Every tree of workload w built and verified on the GPU, the way the benchmark
     runs it: the device generator plays the draft model along the GPU's own frontier,
     layer by layer, then the target model on the emitted trees (unless verify is
-    False). Returns the Lib."""
+    False). root_keys: the trees' context keys (default: the generator's root keys; a
+    decode passes the contexts extended by the tokens emitted so far). Returns the Lib."""
     cfg = lib_config(w)
     L = Lib(cfg, dev)
     B, D, K, N, FP = w.B, w.D, w.K, L.N, L.FP
@@ -123,7 +124,7 @@ def device_step(w, seed, step, dev, verify=True, keep_target=False):
     stream = torch.cuda.current_stream().cuda_stream
     p = w.params()
     zipf = torch.from_numpy(w.tables()).to(dev)
-    rk = [synth.root_key(w.gen_seed, b) for b in range(B)]
+    rk = root_keys if root_keys is not None else [synth.root_key(w.gen_seed, b) for b in range(B)]
     root_keys = torch.tensor([k - (1 << 64) if k >= (1 << 63) else k for k in rk], dtype=torch.int64,
                              device=dev)
     tree_of = torch.arange(B, dtype=torch.int32, device=dev)
@@ -166,3 +167,20 @@ def device_step(w, seed, step, dev, verify=True, keep_target=False):
         L.target, L.ld = target, ld
     del target
     return L
+
+
+def oracle_steps(w, seed, step, trees, root_keys=None):
+    """OracleStep of each tree b in `trees` (root_keys[b] its context key, if given), on a
+    thread pool over this process's cores (the oracle's and generator's C calls release the
+    interpreter lock). The libraries load in this thread first."""
+    import concurrent.futures as cf
+    import os
+
+    from oracle import oracle as orc
+    from oracle.drive import OracleStep
+    synth.lib()
+    orc.lib()
+    trees = list(trees)
+    rk = (lambda b: None) if root_keys is None else (lambda b: root_keys[b])
+    with cf.ThreadPoolExecutor(max_workers=max(1, min(len(trees), len(os.sched_getaffinity(0))))) as ex:
+        return list(ex.map(lambda b: OracleStep(w, seed, b, step, root_key=rk(b)), trees))

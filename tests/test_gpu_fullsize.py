@@ -2,8 +2,9 @@
 benchmark times.
 
 Every tree of the batch is built and verified on the GPU from rows the device
-generator makes along the GPU's own frontier (as bench.py does). Sampled trees are
-then recomputed one by one by the oracle from the same seeded generator and compared:
+generator makes along the GPU's own frontier (as bench.py does). Sampled trees (every
+tree of the headline batch) are then recomputed by the oracle from the same seeded
+generator and compared:
 candidates, emitted tree and tails bit for bit (a tree whose oracle build drew a probe
 within 1e-6 of a CDF boundary may differ, and is counted), every node's decision as
 in the verification parity tests, and the emitted tokens.
@@ -15,14 +16,16 @@ import synth
 from synth import workloads
 from tests.gpu_common import device_step
 from oracle.drive import OracleStep
+from tests.gpu_common import oracle_steps
 from tests.test_gpu_build import compare_tree
 
 pytestmark = pytest.mark.gpu
 
 CASES = [
     # name, workload, sampled trees, (seed, step)
-    ("headline_T1", workloads.get("headline"), [0, 13, 31], (1, 0)),
-    ("headline_T06", workloads.get("headline", T=0.6), [0, 31], (2, 3)),
+    # every tree of the headline batch, at both temperatures
+    ("headline_T1", workloads.get("headline"), list(range(32)), (1, 0)),
+    ("headline_T06", workloads.get("headline", T=0.6), list(range(32)), (2, 3)),
     ("b8", workloads.get("b8"), list(range(8)), (3, 17)),
     ("smart_B64", workloads.get("smart"), [0, 37, 63], (1, 0)),
     ("stress_B256_m1", workloads.get("stress"), [0, 127, 128, 255], (1, 0)),
@@ -51,6 +54,8 @@ def check_decisions(s, L, b):
         if pn["exempt"][i]:
             exempt += 1
             miss += not same
+            # a node may differ only where both sides drew within the band of a threshold
+            assert same or (g[2] >> 8) & 0xFF, (b, i, "differs without a near-threshold draw", g, pn[i])
             continue
         assert same, (b, i, g, pn[i])
         if pn["accept"][i] < 0:
@@ -78,8 +83,7 @@ def test_full_size_step_matches_oracle_on_sampled_trees(gpu, name, w, trees, ss)
     lens = L.out_len.cpu().numpy()
     assert ((lens >= 1) & (lens <= w.D + 1)).all()
     build_exempt = node_exempt = node_miss = 0
-    for b in trees:
-        s = OracleStep(w, seed, b, step)
+    for b, s in zip(trees, oracle_steps(w, seed, step, trees)):
         try:
             compare_tree(w, s, L, b)
         except AssertionError:
@@ -93,7 +97,7 @@ def test_full_size_step_matches_oracle_on_sampled_trees(gpu, name, w, trees, ss)
     print(f"{name}: {len(trees)} trees, {build_exempt} differ after a near-boundary probe draw, "
           f"{node_exempt} nodes with a near-threshold draw, {node_miss} of those differ")
     assert build_exempt <= max(1, len(trees) // 4)
-    assert node_miss <= max(1, node_exempt // 10)
+    assert node_miss <= max(2, node_exempt // 2)
 
 
 @pytest.mark.parametrize("T,order", [(1.0, 0), (0.6, 1)], ids=["T1", "T06_probe_last"])
@@ -121,7 +125,7 @@ def test_dense_headline_step_matches_oracle_on_sampled_trees(gpu, T, order):
         node_exempt += ex
         node_miss += miss
     assert exempt <= 1
-    assert node_miss <= max(1, node_exempt // 10)
+    assert node_miss <= max(2, node_exempt // 2)
 
 
 @pytest.mark.parametrize("name,w,ss", [
