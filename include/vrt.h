@@ -250,6 +250,19 @@ vrt_status vrt_verify_tree(const vrt_config* cfg, const void* target_logits, int
                            void* ws, size_t ws_bytes, int32_t* out_tokens, int32_t* out_nodes,
                            int32_t* out_len, uint32_t* stats, int32_t* node_out, void* stream);
 
+/* vrt_verify_tree for callers that cannot allocate device memory (code under graph
+ * capture, serving loops, harnesses that forbid hipMalloc): the same arguments and outputs
+ * without ws and ws_bytes. Its workspace is a static array of 4 MiB on each GPU, held until
+ * the process ends and shared by every call on that GPU: calls that overlap on one GPU (two
+ * streams, two threads) race and must not be issued. The call allocates nothing; it needs
+ * vrt_workspace_bytes(cfg) <= 4 MiB (B * ((R+1) * 16 + 4096) bytes, plus alignment), else
+ * VRT_ENOMEM. The GPU is the stream's (the current device for a NULL stream). Errors: as
+ * vrt_verify_tree. */
+vrt_status vrt_verify_tree_static(const vrt_config* cfg, const void* target_logits, int64_t ld,
+                                  int64_t tree_stride, const void* tree, uint64_t seed, uint64_t step,
+                                  int32_t* out_tokens, int32_t* out_nodes, int32_t* out_len, uint32_t* stats,
+                                  int32_t* node_out, void* stream);
+
 /* The verification in its two parts, for callers that time or schedule them apart:
  * vrt_verify_nodes decides every node of every tree (its row statistics, the probe-first
  * test, the rejections of the other kept children, the final sample as if the walk

@@ -4,6 +4,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "vrt_internal.hpp"
 
 namespace {
@@ -345,6 +347,63 @@ vrt_status vrt_verify_tree(const vrt_config* cp, const void* target_logits, int6
                            void* ws, size_t ws_bytes, int32_t* out_tokens, int32_t* out_nodes,
                            int32_t* out_len, uint32_t* stats, int32_t* node_out, void* stream) {
   return verify_parts(3, cp, target_logits, ld, tree_stride, tree, seed, step, ws, ws_bytes, out_tokens,
+                      out_nodes, out_len, stats, node_out, stream);
+}
+
+namespace {
+
+// The verification's workspace for callers that cannot allocate: one array per GPU, held
+// until the process ends. In host code `scratch` names a host-side stand-in, not device
+// memory: the kernels get the device address hipGetSymbolAddress gives for the GPU the
+// stream belongs to, looked up once per device with that device current.
+constexpr size_t kScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+vrt_status scratch_of(void* stream, void** out) {
+  int dev = 0, cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return fail(VRT_EHIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  dev = cur;
+  if (stream) {
+    e = hipStreamGetDevice((hipStream_t)stream, &dev);
+    if (e != hipSuccess) return fail(VRT_EHIP, "hipStreamGetDevice failed: %s", hipGetErrorString(e));
+  }
+  if (dev < 0 || dev >= kMaxDevices) return fail(VRT_EINVAL, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess)
+      return fail(VRT_EHIP, "hipSetDevice failed: %s", hipGetErrorString(e));
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess && e == hipSuccess)
+      return fail(VRT_EHIP, "hipSetDevice could not restore device %d", cur);
+    if (e != hipSuccess || !ptr)
+      return fail(VRT_EHIP, "hipGetSymbolAddress of the static workspace failed: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return VRT_OK;
+}
+
+}  // namespace
+
+vrt_status vrt_verify_tree_static(const vrt_config* cp, const void* target_logits, int64_t ld,
+                                  int64_t tree_stride, const void* tree, uint64_t seed, uint64_t step,
+                                  int32_t* out_tokens, int32_t* out_nodes, int32_t* out_len, uint32_t* stats,
+                                  int32_t* node_out, void* stream) {
+  vrt_status s = vrt_check_config(cp);
+  if (s != VRT_OK) return s;
+  const size_t need = (size_t)ws_layout(*cp).total;
+  if (need > kScratchBytes)
+    return fail(VRT_ENOMEM, "vrt_verify_tree_static needs a %zu-byte workspace; its static one holds %zu "
+                            "bytes (use vrt_verify_tree with a workspace of your own)", need, kScratchBytes);
+  void* ws = nullptr;
+  s = scratch_of(stream, &ws);
+  if (s != VRT_OK) return s;
+  return verify_parts(3, cp, target_logits, ld, tree_stride, tree, seed, step, ws, kScratchBytes, out_tokens,
                       out_nodes, out_len, stats, node_out, stream);
 }
 

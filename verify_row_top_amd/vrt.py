@@ -19,7 +19,7 @@ FINISH = -1
 DENSE = 0  # trunc value: no truncation, the support is the whole vocabulary
 ST_DRAFT_NONFINITE, ST_DRAFT_EMPTY, ST_TARGET_BAD = 0x1, 0x2, 0x4
 EXPORTS = ("vrt_check_config", "vrt_tree_layout_of", "vrt_tree_bytes", "vrt_workspace_bytes",
-           "vrt_build_tree", "vrt_verify_tree", "vrt_verify_dense", "vrt_verify_lazy", "vrt_verify_nodes", "vrt_verify_walk", "vrt_tree_mask",
+           "vrt_build_tree", "vrt_verify_tree", "vrt_verify_tree_static", "vrt_verify_dense", "vrt_verify_lazy", "vrt_verify_nodes", "vrt_verify_walk", "vrt_tree_mask",
            "vrt_accepted_kv", "vrt_support_coverage", "vrt_read_probe", "vrt_last_error")
 
 
@@ -72,6 +72,8 @@ def lib():
         L.vrt_verify_tree.argtypes = [P(Config), vp, i64, i64, vp, u64, u64, vp, sz, vp, vp, vp, vp,
                                       vp, vp]
         L.vrt_verify_tree.restype = i32
+        L.vrt_verify_tree_static.argtypes = [P(Config), vp, i64, i64, vp, u64, u64, vp, vp, vp, vp, vp, vp]
+        L.vrt_verify_tree_static.restype = i32
         L.vrt_verify_dense.argtypes = [P(Config), vp, i64, i64, vp, i64, i64, vp, u64, u64, vp, sz, vp, vp,
                                        vp, vp, vp, vp]
         L.vrt_verify_dense.restype = i32
@@ -165,6 +167,14 @@ def verify_tree(cfg, target_logits, ld, tree_stride, tree, seed, step, ws, out_t
                                  seed, step, _ptr(ws), ws.numel() * ws.element_size(),
                                  _ptr(out_tokens), _ptr(out_nodes), _ptr(out_len), _ptr(stats),
                                  _ptr(node_out), _stream(stream)))
+
+
+def verify_tree_static(cfg, target_logits, ld, tree_stride, tree, seed, step, out_tokens, out_nodes, out_len,
+                       stats, node_out=None, stream=None):
+    """vrt_verify_tree_static: vrt_verify_tree on the library's static per-GPU workspace."""
+    _check(lib().vrt_verify_tree_static(ctypes.byref(cfg), _ptr(target_logits), ld, tree_stride, _ptr(tree),
+                                        seed, step, _ptr(out_tokens), _ptr(out_nodes), _ptr(out_len),
+                                        _ptr(stats), _ptr(node_out), _stream(stream)))
 
 
 def verify_dense(cfg, target_logits, ld, tree_stride, draft_layers, draft_ld, draft_tree_stride, tree, seed,
