@@ -352,7 +352,6 @@ def decode_inputs(w, cfg, dev, n_sets, seed, tree, ws, stats, views, out):
     import torch
 
     import synth
-    from oracle.drive import decode_keys
     from verify_row_top_amd import vrt
     out_tokens, out_nodes, out_len = out
     N = vrt.tree_layout_of(cfg).N
@@ -371,7 +370,7 @@ def decode_inputs(w, cfg, dev, n_sets, seed, tree, ws, stats, views, out):
         sets.append({"draft": draft, "target": target, "n_nodes": n_nodes, "step": s,
                      "near": int(st[:, 3].sum()), "bad": int((st[:, 0] != 0).sum()),
                      "tokens": float(lens.sum())})
-        rk = decode_keys(w, rk, emitted)
+        rk = synth.decode_keys(rk, emitted)
     print(f"bench: {n_sets} decode steps of {w.name} (T={w.T}) made", file=sys.stderr, flush=True)
     return sets
 

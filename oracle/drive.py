@@ -93,9 +93,3 @@ class OracleStep:
         toks, _, _, _ = orc.verify(self.cfg, view, synth.to_f32(self.target_rows), self.seed, self.b,
                                    self.step)
         return toks
-
-
-def decode_keys(w, root_keys, tokens):
-    """Root keys of the next decode step: each tree's context extended by the tokens its
-    step emitted (the generator's node-key chain)."""
-    return [synth.path_key(int(k), [int(t) for t in toks]) for k, toks in zip(root_keys, tokens)]

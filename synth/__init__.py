@@ -76,6 +76,12 @@ def path_key(root, tokens):
     return k
 
 
+def decode_keys(root_keys, tokens):
+    """Root keys of the next decode step: each tree's context extended by the tokens its
+    step emitted (the node-key chain)."""
+    return [path_key(int(k), [int(t) for t in toks]) for k, toks in zip(root_keys, tokens)]
+
+
 def rows_host(p, zipf, keys, trees=None, which=DRAFT):
     """Rows for the given node keys on the CPU: uint16 (bf16 bits) or float32, shape [n, V]."""
     keys = np.ascontiguousarray(keys, dtype=np.uint64)

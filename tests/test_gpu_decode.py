@@ -8,7 +8,6 @@ import numpy as np
 import pytest
 
 import synth
-from oracle.drive import decode_keys
 from synth import workloads
 from tests.gpu_common import device_step, oracle_steps
 from tests.test_gpu_build import compare_tree
@@ -46,7 +45,7 @@ def test_decode_steps_match_oracle_on_every_tree(gpu, name, w, n_steps):
             node_exempt += ex
             node_miss += miss
         emitted += int(lens.sum())
-        rk = decode_keys(w, rk, [toks[b, :lens[b]] for b in range(w.B)])
+        rk = synth.decode_keys(rk, [toks[b, :lens[b]] for b in range(w.B)])
     print(f"{name}: {n_steps} steps, {trees} trees, {emitted} tokens emitted, {exempt} trees differ after "
           f"a near-boundary probe draw, {node_exempt} nodes with a near-threshold draw, {node_miss} differ")
     assert exempt <= max(1, trees // 20)
