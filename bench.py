@@ -121,7 +121,13 @@ def cpu_baseline(w, seed, n_trees):
     with cf.ThreadPoolExecutor(max_workers=cores) as ex:
         list(ex.map(lambda s: s.replay(), steps))
     wall = time.perf_counter() - t0
-    return {"value": n_trees / wall, "unit": "trees/s", "cores": cores, "kind": "oracle",
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
+    return {"value": n_trees / wall, "unit": "trees/s", "cores": cores, "kind": "oracle", "cpu": model,
             "sample": f"{n_trees} trees (b=0..{n_trees - 1}, seed {seed}, step 0) of the same workload: "
                       f"every build layer, the finish and the verification on rows made beforehand, one "
                       f"tree per task on {cores} threads of this process, wall time",
