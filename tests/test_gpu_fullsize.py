@@ -3,8 +3,8 @@ benchmark times.
 
 Every tree of the batch is built and verified on the GPU from rows the device
 generator makes along the GPU's own frontier (as bench.py does). Sampled trees (every
-tree of the headline batch) are then recomputed by the oracle from the same seeded
-generator and compared:
+tree of the headline, B=8 and SMART batches, a quarter of the stress batch) are then
+recomputed by the oracle from the same seeded generator and compared:
 candidates, emitted tree and tails bit for bit (a tree whose oracle build drew a probe
 within 1e-6 of a CDF boundary may differ, and is counted), every node's decision as
 in the verification parity tests, and the emitted tokens.
@@ -27,10 +27,12 @@ CASES = [
     ("headline_T1", workloads.get("headline"), list(range(32)), (1, 0)),
     ("headline_T06", workloads.get("headline", T=0.6), list(range(32)), (2, 3)),
     ("b8", workloads.get("b8"), list(range(8)), (3, 17)),
-    ("smart_B64", workloads.get("smart"), [0, 37, 63], (1, 0)),
-    ("stress_B256_m1", workloads.get("stress"), [0, 127, 128, 255], (1, 0)),
-    ("stress_B256_m0", workloads.get("stress", m=0), [5, 200], (4, 2)),
-    ("stress_B256_m3", workloads.get("stress", m=3), [77, 170], (5, 9)),
+    ("smart_B64", workloads.get("smart"), list(range(64)), (1, 0)),
+    # every fourth tree of the stress batch (both halves: peaked rows b < 128, flat ones
+    # from 128 on), every sixteenth at m = 0 and m = 3
+    ("stress_B256_m1", workloads.get("stress"), list(range(0, 256, 4)) + [255], (1, 0)),
+    ("stress_B256_m0", workloads.get("stress", m=0), list(range(5, 256, 16)), (4, 2)),
+    ("stress_B256_m3", workloads.get("stress", m=3), list(range(13, 256, 16)), (5, 9)),
     ("headline_probe_last", workloads.get("headline", order=1), [0, 17, 31], (6, 1)),
     # long supports at the full vocabulary: bf16 rows whose ties near the cut stage more
     # than four keys per support entry
