@@ -511,7 +511,7 @@ def measure(w, args, n_sets, lazy=True):
 
     # lazy verification (only the rows of the nodes the walk visits), timed on its own:
     # each rep rebuilds a set's tree (untimed), then verifies it lazily between two events
-    lz_ms, lz_rows, lazy_ok = [], 0, True
+    lz_ms, lz_rows, lz_near, lazy_ok = [], 0, 0, True
     for k in range(min(args.steps, 2 * len(sets)) + 3):
         st = sets[k % len(sets)]
         build(st)
@@ -527,13 +527,15 @@ def measure(w, args, n_sets, lazy=True):
         if k >= 3:
             lz_ms.append(e0.elapsed_time(e1))
             lz_rows += int(out_len.sum().item())
+            lz_near += int(stats[:, 3].sum().item())  # the visited nodes' near-threshold draws
     lazy_ms = sum(lz_ms) / len(lz_ms)
     r["lazy_verify"] = {"ms": lazy_ms, "trees_per_s": B / (lazy_ms * 1e-3),
                         "rows_read_per_tree": lz_rows / (len(lz_ms) * B),
                         "rows_per_tree_full": r["mean_nodes_per_tree"],
                         "step_trees_per_s": (B / ((build_ms + lazy_ms) * 1e-3)) if not args.verify_only
                         else None,
-                        "same_tokens_as_full": lazy_ok}
+                        "same_tokens_as_full": lazy_ok, "near_threshold_draws": lz_near,
+                        "calls": len(lz_ms)}
 
     # the step after the prune, timed on its own: attention mask + position ids of the
     # target forward over the emitted trees, and the KV entries kept after verification
