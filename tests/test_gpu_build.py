@@ -76,6 +76,16 @@ CASES = [
     ("edge_W1_beam", _small(W=1, R=8, D=6)),
     ("edge_K1_probe_only", _small(K=1, m=0, R=5, D=5)),
     ("edge_R_below_K", _small(R=3, D=4)),
+    # limits: a prune of more than 128 nodes (the finish sorts the candidates in LDS), the
+    # largest K (layers of 300 children: the ranking as a kernel of its own), bf16 rows
+    # longer than two blocks' row-wide paths (the exact radix path over the whole row), a
+    # low temperature (tempered tails that underflow: parents without a probe) and a deep,
+    # narrow tree
+    ("edge_R300_lds_sort", _small(R=300, D=4, K=10, W=10)),
+    ("edge_K30_W10", _small(K=30, m=3, W=10, R=100, D=3, V=9000)),
+    ("exact_path_bf16_V400000", _small(V=400000, R=20, D=3, B=2)),
+    ("edge_T01", _small(T=0.1, R=30, D=5)),
+    ("edge_D16_narrow", _small(W=2, K=3, m=1, R=40, D=16)),
     ("smart_small", _smart_small()),
     ("smart_small_m0_alpha08", _smart_small(m=0, alpha=0.8, budget=24)),
 ]
