@@ -88,6 +88,9 @@ CASES = [
     ("edge_D16_narrow", _small(W=2, K=3, m=1, R=40, D=16)),
     ("smart_small", _smart_small()),
     ("smart_small_m0_alpha08", _smart_small(m=0, alpha=0.8, budget=24)),
+    # the largest budget: 1024 frontier slots per tree (row blocks without a parent clear
+    # their slots and return), 4096 candidates per layer ranked by a kernel of their own
+    ("smart_budget1024_K4", _smart_small(budget=1024, K=4, D=5)),
 ]
 
 
