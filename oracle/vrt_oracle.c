@@ -339,7 +339,19 @@ static void expand_dense(orc_tree* t, int32_t layer, int32_t pos, int32_t node, 
 
   /* probe: x_s ~ the tempered tail renormalised, inverse CDF in token-id order */
   int32_t s = -1;
-  if (c->probe && V > t0 && zT > 0.0) {
+  const int32_t draws = c->probe && V > t0 && zT > 0.0;
+  if (t->force && !(draws ? (t->force[r] >= t0 && t->force[r] < V) : t->force[r] == t0))
+    t->weight = 0.0; /* a forced branch that does not exist (no draw: only rank t0 stands) */
+  if (draws && t->force && t->weight > 0.0) {
+    /* exact enumeration: the token at the forced rank, weighted by the share of u in
+     * [0, 1) that the id-order inverse CDF below sends to it (the deterministic children
+     * hold no mass there) */
+    s = ids[t->force[r]];
+    double* qt = (double*)malloc(sizeof(double) * (size_t)V);
+    for (int32_t v = 0; v < V; ++v) qt[v] = det[v] ? 0.0 : et[v];
+    t->weight *= draw_share(qt, V, zT, s);
+    free(qt);
+  } else if (draws && !t->force) {
     const double u = orc_uniform(t->seed, (uint32_t)(node + 1), (uint32_t)t->b, t->step,
                                  ORC_PURPOSE_PROBE);
     e->u = u;
@@ -371,6 +383,8 @@ static void expand_dense(orc_tree* t, int32_t layer, int32_t pos, int32_t node, 
       e->exempt = 1;
       t->n_exempt++;
     }
+  }
+  if (s >= 0) {
     e->probe_token = s;
     for (int32_t i = 0; i < keep; ++i)
       if (ids[i] == s) e->probe_rank = i;
@@ -1047,6 +1061,11 @@ typedef struct {
 } enum_ctx;
 
 /* The first `layers` layers of a tree at E's context, with the probes forced. */
+/* Tokens in every expanded row's support: min(trunc, V), or all V when dense. */
+static int32_t enum_sup(const orc_cfg* c) {
+  return c->trunc == ORC_DENSE || c->V < c->trunc ? c->V : c->trunc;
+}
+
 static orc_tree* enum_build(enum_ctx* E, int32_t* force, int32_t layers) {
   const int32_t V = E->cfg->V;
   orc_tree* t = orc_tree_create(E->cfg, 0, 0, 0);
@@ -1100,7 +1119,7 @@ static void enum_law(enum_ctx* E);
 /* A complete tree of weight t->weight: its verification's outcomes into E's laws. */
 static void enum_verify(enum_ctx* E, orc_tree* t) {
   const orc_cfg* c = E->cfg;
-  const int32_t V = c->V, TC = c->trunc;
+  const int32_t V = c->V, TC = enum_sup(c);
   orc_finish(t);
   const int32_t N = t->n_nodes;
   int32_t* iv = (int32_t*)malloc(sizeof(int32_t) * (size_t)(8 * N + 8));
@@ -1169,7 +1188,7 @@ static void enum_layers(enum_ctx* E, int32_t* force, int32_t layer) {
   }
   const int32_t nf = t->n_front, r0 = orc_row_base(t, layer);
   orc_tree_free(t);
-  const int32_t n_sup = c->V < c->trunc ? c->V : c->trunc;
+  const int32_t n_sup = enum_sup(c);
   const int32_t t0 = c->order == ORC_PROBE_LAST ? (c->K - 1 < n_sup ? c->K - 1 : n_sup) : (c->probe ? c->m : 0);
   const int32_t radix = (c->probe && n_sup > t0) ? n_sup - t0 : 1;
   int32_t digit[64] = {0};
@@ -1187,7 +1206,7 @@ static void enum_law(enum_ctx* E) {
   const orc_cfg* c = E->cfg;
   const int32_t maxpar = width_of(c);
   const int32_t n_rows = 1 + (c->D - 1) * maxpar;
-  const int32_t n_sup = c->V < c->trunc ? c->V : c->trunc;
+  const int32_t n_sup = enum_sup(c);
   const int32_t t0 = c->order == ORC_PROBE_LAST ? (c->K - 1 < n_sup ? c->K - 1 : n_sup) : (c->probe ? c->m : 0);
   int32_t* force = (int32_t*)malloc(sizeof(int32_t) * (size_t)n_rows);
   for (int32_t r = 0; r < n_rows; ++r) force[r] = t0;
@@ -1198,7 +1217,7 @@ static void enum_law(enum_ctx* E) {
 int32_t orc_exact_law(const orc_cfg* cfg, int32_t max_len, const float* draft_tab, const float* target_tab,
                       const int32_t* prefix, int32_t np, int32_t two, double* law1, double* law2,
                       double* accept) {
-  if (cfg->mode != ORC_TOPR || cfg->trunc == ORC_DENSE || width_of(cfg) > 64) return -2;
+  if (cfg->mode != ORC_TOPR || width_of(cfg) > 64) return -2;
   const int32_t V = cfg->V;
   double* fresh = (double*)malloc(sizeof(double) * (size_t)V * (size_t)V);
   for (int64_t k = 0; k < (int64_t)V * V; ++k) fresh[k] = NAN;

@@ -9,10 +9,13 @@ Losslessness then fixes the result exactly, independently of the oracle:
   * the first emitted token's law is the tempered target softmax at the root context;
   * the law of the first two emitted tokens is p(a) p(b | a), whether the second token
     comes from the same tree or from the next step;
-to 1e-12, for probe first and probe last, m in {0, 1, 3}, supports shorter than V,
-prune budgets below K and the plain top-K tree. At depth 1 the probability that the
-first token comes from the tree must also equal the closed forms derived from key
-design 3 (tests/test_oracle_lossless.py, tests/test_oracle_rrsw.py) to 1e-12.
+to 1e-12, for probe first and probe last, m in {0, 1, 3}, supports shorter than V, the
+dense support (the whole vocabulary, the probe drawn in token-id order), prune budgets
+below K and the plain top-K tree. At depth 1 the probability that the first token comes
+from the tree must also equal the closed forms derived from key design 3
+(tests/test_oracle_lossless.py, tests/test_oracle_rrsw.py) to 1e-12; for the dense
+support the closed form is that of a truncated support holding all V tokens, since the
+probe's law does not depend on the order its inverse CDF walks.
 """
 import numpy as np
 import pytest
@@ -49,6 +52,11 @@ CONFIGS = [
     ("probe_off_topk", dict(V=8, trunc=8, K=3, m=0, probe=0, D=3, W=2, R=6, T=1.0), 7),
     ("K1_m0_chain", dict(V=6, trunc=6, K=1, m=0, D=3, W=1, R=3, T=1.0), 8),
     ("R2_lt_K3", dict(V=8, trunc=8, K=3, m=1, D=3, W=3, R=2, T=1.0), 9),
+    ("dense_m1_D3", dict(V=6, trunc=orc.DENSE, K=3, m=1, D=3, W=2, R=6, T=1.0), 41),
+    ("dense_m0_T06", dict(V=7, trunc=orc.DENSE, K=3, m=0, D=2, W=2, R=5, T=0.6), 42),
+    ("dense_m3_K4_T08", dict(V=6, trunc=orc.DENSE, K=4, m=3, D=2, W=1, R=5, T=0.8), 43),
+    ("dense_probe_last_D3", dict(V=6, trunc=orc.DENSE, K=3, m=1, D=3, W=2, R=5, T=1.0,
+                                 order=orc.PROBE_LAST), 44),
 ]
 
 
@@ -79,6 +87,9 @@ DEPTH1 = [
     ("probe_off", dict(V=8, trunc=8, K=3, m=0, probe=0, T=1.0), 15),
     ("probe_last_m1", dict(V=8, trunc=8, K=3, m=1, T=1.0, order=orc.PROBE_LAST), 16),
     ("probe_last_trunc5_T06", dict(V=8, trunc=5, K=3, m=0, T=0.6, order=orc.PROBE_LAST), 17),
+    ("dense_m1", dict(V=8, trunc=orc.DENSE, K=3, m=1, T=1.0), 18),
+    ("dense_m0_T06", dict(V=7, trunc=orc.DENSE, K=4, m=0, T=0.6), 19),
+    ("dense_probe_last", dict(V=8, trunc=orc.DENSE, K=3, m=1, T=0.8, order=orc.PROBE_LAST), 20),
 ]
 
 
@@ -87,6 +98,8 @@ def depth1_gap(kw, seed):
     cfg = orc.make_cfg(D=1, W=0, R=kw["K"], **kw)
     dt, tt = tables(kw["V"], 1, seed)
     _, _, acc = orc.exact_law(cfg, 2, dt, tt, two=False)
+    if kw["trunc"] == orc.DENSE:  # the closed form's support: every token
+        cfg = orc.make_cfg(D=1, W=0, R=kw["K"], **dict(kw, trunc=kw["V"]))
     closed = _depth1_rrsw(cfg, dt[0], tt[0]) if kw.get("order") == orc.PROBE_LAST else \
         _depth1_acceptance(cfg, dt[0], tt[0])
     return abs(acc - closed), acc
@@ -111,7 +124,7 @@ def test_acceptance_rises_with_the_tree():
 
 def exact_ok():
     """The exact pins on a few configurations (for the planted-mistake tests)."""
-    for name, kw, seed in (CONFIGS[0], CONFIGS[1], CONFIGS[4], CONFIGS[5]):
+    for name, kw, seed in (CONFIGS[0], CONFIGS[1], CONFIGS[4], CONFIGS[5], CONFIGS[9], CONFIGS[12]):
         e1, e2, tot = laws_match(kw, seed)
         if not (abs(tot - 1.0) <= TOL and e1 <= TOL and e2 <= TOL):
             return False

@@ -150,6 +150,13 @@ MUTANTS = [
      "      before = cum;", dense_ok),
     ("dense_fillers_repeat_probe", "if (ids[i] != s) add_child", "if (ids[i] >= 0) add_child",
      dense_ok),
+    ("dense_tail_q_not_renormalised",
+     "for (int32_t v = 0; v < V; ++v) e->dense_q[v] = det[v] ? 0.0 : et[v] / zT;",
+     "for (int32_t v = 0; v < V; ++v) e->dense_q[v] = det[v] ? 0.0 : et[v] / Z;", lambda: exact_ok()),
+    ("dense_tail_mass_includes_deterministic", "    if (!det[v]) zT += et[v];", "    zT += et[v];",
+     dense_ok),
+    ("dense_view_tail_shifted", "        tail_q[(int64_t)i * tail_cap + k] = e->dense_q[v];",
+     "        tail_q[(int64_t)i * tail_cap + k] = e->dense_q[(v + 1) % t->cfg.V];", lambda: exact_ok()),
     # the per-layer beam and the global top-R prune (every check stops at the first wrong
     # frontier, so a frontier longer than W is never expanded)
     ("node_tie_break_reversed", "  return (x < y) ? -1 : (x > y);",
@@ -168,13 +175,15 @@ def exact_ok():
     return ok()
 
 
-# the verification mistakes (and the build's tail mass, which the probe's law depends on),
-# each also caught by the exact enumeration of the first- and two-token laws and of the
-# depth-1 acceptance: no statistics involved
+# the verification mistakes (and the build's tail mass and the dense probe's tail, which
+# the probe's law and its test depend on), each also caught by the exact enumeration of the
+# first- and two-token laws and of the depth-1 acceptance: no statistics involved
 EXACT = ["residual_mass_ignores_overlap", "probe_ratio_inverted", "tail_residual_not_clipped",
          "rejected_sibling_not_removed", "verify_ignores_temperature",
          "probe_last_ratio_ignores_residual_mass", "probe_last_tail_not_scaled",
-         "probe_last_tail_includes_fillers", "tail_mass_includes_top_m"]
+         "probe_last_tail_includes_fillers", "tail_mass_includes_top_m",
+         "dense_tail_q_not_renormalised", "dense_tail_mass_includes_deterministic",
+         "dense_view_tail_shifted"]
 
 
 def _planted(tmp_path, name, old, new):
