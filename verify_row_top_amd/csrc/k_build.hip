@@ -185,7 +185,7 @@ struct FastLds {
   int hist[kDistBins];  // distance histogram; its first 256 bins serve the radix levels
   int sel[2];
   int wmax[16];
-  int nk, bad;
+  int nk, ng, bad;
 };
 
 // The row's top TC keys (value desc, token id asc) into s_sup (positions < N, sorted,
@@ -223,6 +223,7 @@ __device__ __forceinline__ int row_select_fast(const char* row, int g0, int g1, 
   const int lane = lane_id();
   if (tid == 0) {
     F.nk = 0;
+    F.ng = 0;
     F.bad = 0;
   }
   for (int i = tid; i < kDistBins; i += NT) F.hist[i] = 0;
@@ -407,122 +408,193 @@ __device__ __forceinline__ int row_select_fast(const char* row, int g0, int g1, 
   }
   if (pre == 0u || pre == 0xFFFFFFFFu) return 2;  // fewer than TC candidates carry a value
 
-  // C. (each thread re-reads the groups of its own lane-segments that reach t, all
-  // loads in flight at once, and stages their elements that reach t; a wave reserves
-  // its keys' places with one atomic)
-  {
-    constexpr int SL = LSPT * LV;
-    static_assert(SL <= 32, "slot mask");
-    u32x4_t gw[LSPT][LV];
-    uint32_t lst = 0u;  // bit j*LV + s: slot (j, s) is listed
-    bool sat_any = false;
-    uint32_t satm = 0u;  // bit j: lane-segment j has all LV candidates at or above t
+  // C. Lists up to 256 keys: the groups whose maximum reaches t (each lane-segment's group
+  // maxima name them) go to one list in LDS, a wave reserving its places with one atomic;
+  // then each thread takes one listed group, reads its 16 bytes again and stages its
+  // elements that reach t. Longer lists: each thread re-reads its own lane-segments'
+  // candidate groups that reach t (all loads in flight at once), and the other groups
+  // that do where all LV candidates of a lane-segment reach t.
+  if constexpr (PL <= 4) {
+    int* glist = F.hist;  // the histogram is done with: it holds the list
+    constexpr int GCAP = kDistBins;
+    uint32_t gsel[LSPT];  // bit q: group q of lane-segment j reaches t
+    int cnt = 0;
     static_for<LSPT>([&](auto j) {
-      const int g = g0 + wave + j * SW;
-      const bool vj = g < g1;
-      const bool sat = vj && (uint32_t)(cand[j][LV - 1] >> 8) >= pre;
-      sat_any |= sat;
-      satm |= (uint32_t)sat << j;
-      static_for<LV>([&](auto s) {
-        gw[j][s] = u32x4_t{0u, 0u, 0u, 0u};
-        const int e0 = g * seg_elems<DT>() + ((int)(cand[j][s] & 0xFF) * kWave + lane) * EPL;
-        if (vj && (uint32_t)(cand[j][s] >> 8) >= pre && e0 < V) {
-          gw[j][s] = *(const u32x4_t*)(row + (int64_t)e0 * esz);
-          lst |= 1u << (j * LV + s);
+      gsel[j] = 0u;
+      if (g0 + wave + j * SW < g1) {  // uniform
+        static_for<kSegLoads>([&](auto q) {
+          const uint32_t im = (gmi[j][q / GPW] >> (16 * (q % GPW))) & (BF ? 0xFFFFu : 0xFFFFFFFFu);
+          gsel[j] |= (uint32_t)(im >= pre) << q;
+        });
+        cnt += __builtin_popcount(gsel[j]);
+      }
+    });
+    {
+      const int incl = wave_incl_scan(cnt);
+      int base = 0;
+      if (lane == kWave - 1 && incl > 0) base = atomicAdd(&F.ng, incl);
+      int at = __shfl(base, kWave - 1, kWave) + incl - cnt;
+      static_for<LSPT>([&](auto j) {
+        uint32_t m = gsel[j];
+        const int s0 = (g0 + wave + j * SW) * seg_elems<DT>();
+        while (m != 0u) {
+          const int q = __builtin_ctz(m);
+          m &= m - 1u;
+          if (at < GCAP) glist[at] = s0 + (q * kWave + lane) * EPL;
+          ++at;
         }
       });
-    });
+    }
+    __syncthreads();
+    const int ng = F.ng;
+    if (ng > GCAP) {  // more groups than keys the path holds reach t
+      floor_img = pre;
+      return 2;
+    }
     auto elem = [](const u32x4_t& w, auto e) -> float {  // e: a compile-time index
       constexpr int E = decltype(e)::value;
       if constexpr (BF) return (E & 1) ? bf16_hi(w[E >> 1]) : bf16_lo(w[E >> 1]);
       else return __uint_as_float(w[E]);
     };
-    uint32_t keep[LSPT][LV];
-    int cnt = 0;
-    static_for<LSPT>([&](auto j) {
-      static_for<LV>([&](auto s) {
-        keep[j][s] = 0u;
-        if (ballot((lst >> (j * LV + s)) & 1u) != 0ull) {  // uniform skip
-          const int g = g0 + wave + j * SW;
-          const int e0 = g * seg_elems<DT>() + ((int)(cand[j][s] & 0xFF) * kWave + lane) * EPL;
-          uint32_t k = 0u;
-          static_for<EPL>([&](auto e) {
-            if (((lst >> (j * LV + s)) & 1u) && e0 + (int)e < V && img_of<DT>(elem(gw[j][s], e)) >= pre)
-              k |= 1u << e;
-          });
-          keep[j][s] = k;
-          cnt += __builtin_popcount(k);
+    for (int r0 = wave * kWave; r0 < ng; r0 += NT) {  // uniform per wave
+      const int gi = r0 + lane;
+      u32x4_t w = {0u, 0u, 0u, 0u};
+      int e0 = V;
+      if (gi < ng) {
+        e0 = glist[gi];
+        w = *(const u32x4_t*)(row + (int64_t)e0 * esz);
+      }
+      uint32_t k = 0u;
+      static_for<EPL>([&](auto e) {
+        if (e0 + (int)e < V && img_of<DT>(elem(w, e)) >= pre) k |= 1u << e;
+      });
+      const int c = __builtin_popcount(k);
+      const int incl = wave_incl_scan(c);
+      int base = 0;
+      if (lane == kWave - 1 && incl > 0) base = atomicAdd(&F.nk, incl);
+      int at = __shfl(base, kWave - 1, kWave) + incl - c;
+      static_for<EPL>([&](auto e) {
+        if (k & (1u << e)) {
+          if (at < FL::KCAP) F.keys[at] = sup_key(elem(w, e), (uint32_t)(e0 + (int)e));
+          ++at;
         }
       });
-    });
-    const int incl = wave_incl_scan(cnt);
-    int base = 0;
-    if (lane == kWave - 1 && incl > 0) base = atomicAdd(&F.nk, incl);
-    int at = __shfl(base, kWave - 1, kWave) + incl - cnt;
-    static_for<LSPT>([&](auto j) {
-      static_for<LV>([&](auto s) {
-        if (ballot(keep[j][s] != 0u) != 0ull) {
-          const int g = g0 + wave + j * SW;
-          const int e0 = g * seg_elems<DT>() + ((int)(cand[j][s] & 0xFF) * kWave + lane) * EPL;
-          static_for<EPL>([&](auto e) {
-            if (keep[j][s] & (1u << e)) {
-              if (at < FL::KCAP) F.keys[at] = sup_key(elem(gw[j][s], e), (uint32_t)(e0 + (int)e));
-              ++at;
-            }
-          });
-        }
-      });
-    });
-    // a lane-segment whose LV candidates all reach t may hold more groups that do: their
-    // maxima name them, read four at a time
-    if (ballot(sat_any) != 0ull) {
+    }
+  } else {
+    {
+      constexpr int SL = LSPT * LV;
+      static_assert(SL <= 32, "slot mask");
+      u32x4_t gw[LSPT][LV];
+      uint32_t lst = 0u;  // bit j*LV + s: slot (j, s) is listed
+      bool sat_any = false;
+      uint32_t satm = 0u;  // bit j: lane-segment j has all LV candidates at or above t
       static_for<LSPT>([&](auto j) {
-        uint32_t extra = 0u;  // bit q: group q of the lane-segment, not a candidate
-        if ((satm >> j) & 1u) {
-          static_for<kSegLoads>([&](auto q) {
-            const uint32_t im = (gmi[j][q / GPW] >> (16 * (q % GPW))) & (BF ? 0xFFFFu : 0xFFFFFFFFu);
-            if (im >= pre) extra |= 1u << q;
-          });
-          static_for<LV>([&](auto s) { extra &= ~(1u << (uint32_t)(cand[j][s] & 0xFF)); });
-        }
-        const int s0 = (g0 + wave + j * SW) * seg_elems<DT>();
-        while (ballot(extra != 0u) != 0ull) {
-          u32x4_t w[4];
-          int e0[4];
-          static_for<4>([&](auto u) {
-            w[u] = u32x4_t{0u, 0u, 0u, 0u};
-            e0[u] = V;
-            if (extra != 0u) {
-              const int q = __builtin_ctz(extra);
-              extra &= extra - 1u;
-              e0[u] = s0 + (q * kWave + lane) * EPL;
-              if (e0[u] < V) w[u] = *(const u32x4_t*)(row + (int64_t)e0[u] * esz);
-            }
-          });
-          uint32_t kp[4];
-          int c2 = 0;
-          static_for<4>([&](auto u) {
+        const int g = g0 + wave + j * SW;
+        const bool vj = g < g1;
+        const bool sat = vj && (uint32_t)(cand[j][LV - 1] >> 8) >= pre;
+        sat_any |= sat;
+        satm |= (uint32_t)sat << j;
+        static_for<LV>([&](auto s) {
+          gw[j][s] = u32x4_t{0u, 0u, 0u, 0u};
+          const int e0 = g * seg_elems<DT>() + ((int)(cand[j][s] & 0xFF) * kWave + lane) * EPL;
+          if (vj && (uint32_t)(cand[j][s] >> 8) >= pre && e0 < V) {
+            gw[j][s] = *(const u32x4_t*)(row + (int64_t)e0 * esz);
+            lst |= 1u << (j * LV + s);
+          }
+        });
+      });
+      auto elem = [](const u32x4_t& w, auto e) -> float {  // e: a compile-time index
+        constexpr int E = decltype(e)::value;
+        if constexpr (BF) return (E & 1) ? bf16_hi(w[E >> 1]) : bf16_lo(w[E >> 1]);
+        else return __uint_as_float(w[E]);
+      };
+      uint32_t keep[LSPT][LV];
+      int cnt = 0;
+      static_for<LSPT>([&](auto j) {
+        static_for<LV>([&](auto s) {
+          keep[j][s] = 0u;
+          if (ballot((lst >> (j * LV + s)) & 1u) != 0ull) {  // uniform skip
+            const int g = g0 + wave + j * SW;
+            const int e0 = g * seg_elems<DT>() + ((int)(cand[j][s] & 0xFF) * kWave + lane) * EPL;
             uint32_t k = 0u;
             static_for<EPL>([&](auto e) {
-              if (e0[u] + (int)e < V && img_of<DT>(elem(w[u], e)) >= pre) k |= 1u << e;
+              if (((lst >> (j * LV + s)) & 1u) && e0 + (int)e < V && img_of<DT>(elem(gw[j][s], e)) >= pre)
+                k |= 1u << e;
             });
-            kp[u] = k;
-            c2 += __builtin_popcount(k);
-          });
-          const int inc2 = wave_incl_scan(c2);
-          int b2 = 0;
-          if (lane == kWave - 1 && inc2 > 0) b2 = atomicAdd(&F.nk, inc2);
-          int at2 = __shfl(b2, kWave - 1, kWave) + inc2 - c2;
-          static_for<4>([&](auto u) {
+            keep[j][s] = k;
+            cnt += __builtin_popcount(k);
+          }
+        });
+      });
+      const int incl = wave_incl_scan(cnt);
+      int base = 0;
+      if (lane == kWave - 1 && incl > 0) base = atomicAdd(&F.nk, incl);
+      int at = __shfl(base, kWave - 1, kWave) + incl - cnt;
+      static_for<LSPT>([&](auto j) {
+        static_for<LV>([&](auto s) {
+          if (ballot(keep[j][s] != 0u) != 0ull) {
+            const int g = g0 + wave + j * SW;
+            const int e0 = g * seg_elems<DT>() + ((int)(cand[j][s] & 0xFF) * kWave + lane) * EPL;
             static_for<EPL>([&](auto e) {
-              if (kp[u] & (1u << e)) {
-                if (at2 < FL::KCAP) F.keys[at2] = sup_key(elem(w[u], e), (uint32_t)(e0[u] + (int)e));
-                ++at2;
+              if (keep[j][s] & (1u << e)) {
+                if (at < FL::KCAP) F.keys[at] = sup_key(elem(gw[j][s], e), (uint32_t)(e0 + (int)e));
+                ++at;
               }
             });
-          });
-        }
+          }
+        });
       });
+      // a lane-segment whose LV candidates all reach t may hold more groups that do: their
+      // maxima name them, read four at a time
+      if (ballot(sat_any) != 0ull) {
+        static_for<LSPT>([&](auto j) {
+          uint32_t extra = 0u;  // bit q: group q of the lane-segment, not a candidate
+          if ((satm >> j) & 1u) {
+            static_for<kSegLoads>([&](auto q) {
+              const uint32_t im = (gmi[j][q / GPW] >> (16 * (q % GPW))) & (BF ? 0xFFFFu : 0xFFFFFFFFu);
+              if (im >= pre) extra |= 1u << q;
+            });
+            static_for<LV>([&](auto s) { extra &= ~(1u << (uint32_t)(cand[j][s] & 0xFF)); });
+          }
+          const int s0 = (g0 + wave + j * SW) * seg_elems<DT>();
+          while (ballot(extra != 0u) != 0ull) {
+            u32x4_t w[4];
+            int e0[4];
+            static_for<4>([&](auto u) {
+              w[u] = u32x4_t{0u, 0u, 0u, 0u};
+              e0[u] = V;
+              if (extra != 0u) {
+                const int q = __builtin_ctz(extra);
+                extra &= extra - 1u;
+                e0[u] = s0 + (q * kWave + lane) * EPL;
+                if (e0[u] < V) w[u] = *(const u32x4_t*)(row + (int64_t)e0[u] * esz);
+              }
+            });
+            uint32_t kp[4];
+            int c2 = 0;
+            static_for<4>([&](auto u) {
+              uint32_t k = 0u;
+              static_for<EPL>([&](auto e) {
+                if (e0[u] + (int)e < V && img_of<DT>(elem(w[u], e)) >= pre) k |= 1u << e;
+              });
+              kp[u] = k;
+              c2 += __builtin_popcount(k);
+            });
+            const int inc2 = wave_incl_scan(c2);
+            int b2 = 0;
+            if (lane == kWave - 1 && inc2 > 0) b2 = atomicAdd(&F.nk, inc2);
+            int at2 = __shfl(b2, kWave - 1, kWave) + inc2 - c2;
+            static_for<4>([&](auto u) {
+              static_for<EPL>([&](auto e) {
+                if (kp[u] & (1u << e)) {
+                  if (at2 < FL::KCAP) F.keys[at2] = sup_key(elem(w[u], e), (uint32_t)(e0[u] + (int)e));
+                  ++at2;
+                }
+              });
+            });
+          }
+        });
+      }
     }
   }
   __syncthreads();
