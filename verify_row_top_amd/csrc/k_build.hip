@@ -680,23 +680,32 @@ __device__ __forceinline__ int row_select_fast(const char* row, int g0, int g1, 
     __syncthreads();
     return 0;
   }
-  for (int i = tid; i < nk; i += NT) {
-    const uint64_t my = F.keys[i];
-    int r = 0;
-    // two keys per read, eight reads in flight (slots past nk hold 0, below every key)
+  {
+    // H consecutive threads per key (as many as the block holds, up to 8), each counting
+    // the larger keys in its share of the list; two keys per read, eight reads in flight
+    // (slots past nk hold 0, below every key)
+    const int H = nk <= NT / 8 ? 8 : (nk <= NT / 4 ? 4 : (nk <= NT / 2 ? 2 : 1));
     const int nk2 = (nk + 1) >> 1;
+    const int len = (nk2 + H - 1) / H;
     const u64x2_t* kp = (const u64x2_t*)F.keys;
-    int jj = 0;
-    for (; jj + 8 <= nk2; jj += 8) {
-      u64x2_t w[8];
-      static_for<8>([&](auto u) { w[u] = kp[jj + u]; });
-      static_for<8>([&](auto u) { r += (w[u][0] > my) + (w[u][1] > my); });
+    for (int i0 = 0; i0 < nk; i0 += NT / H) {  // uniform
+      const int i = i0 + tid / H, h = tid % H;
+      const uint64_t my = i < nk ? F.keys[i] : ~0ull;
+      const int j1 = min(nk2, (h + 1) * len);
+      int r = 0;
+      int jj = h * len;
+      for (; jj + 8 <= j1; jj += 8) {
+        u64x2_t w[8];
+        static_for<8>([&](auto u) { w[u] = kp[jj + u]; });
+        static_for<8>([&](auto u) { r += (w[u][0] > my) + (w[u][1] > my); });
+      }
+      for (; jj < j1; ++jj) {
+        const u64x2_t w = kp[jj];
+        r += (w[0] > my) + (w[1] > my);
+      }
+      for (int o = 1; o < H; o <<= 1) r += __shfl_xor(r, o, kWave);
+      if (i < nk && h == 0 && r < TC) s_sup[r] = my;
     }
-    for (; jj < nk2; ++jj) {
-      const u64x2_t w = kp[jj];
-      r += (w[0] > my) + (w[1] > my);
-    }
-    if (r < TC) s_sup[r] = my;
   }
   for (int p = TC + tid; p < N; p += NT) s_sup[p] = 0ull;
   n_sup = TC;
@@ -1111,6 +1120,20 @@ __device__ __forceinline__ void rank_wave(const BArgs& a, int b, uint64_t* s_ran
     k[s] = x;
   });
   wave_sort_desc<RL>(k);
+  if (c.mode == VRT_MODE_TOPR) {
+    // the top W keys are positions 0 .. W-1 of the sorted list (lane * RL + s); the
+    // nonzero keys form its prefix
+    int nz = 0;
+    static_for<RL>([&](auto s) { nz += __builtin_popcountll(ballot(k[s] != 0ull)); });
+    const int nf = a.layer + 1 < c.D ? min(c.W, nz) : 0;
+    int* front = t.front + (int64_t)b * c.FP;
+    static_for<RL>([&](auto s) {
+      const int p = lane * RL + s;
+      if (p < nf) front[p] = (int)(0xFFFFFFFFu - (uint32_t)k[s]);
+    });
+    if (lane == 0) t.n_front[b] = nf;
+    return;
+  }
   static_for<RL>([&](auto s) { s_rank[lane * RL + s] = k[s]; });
   wave_sync();
   if (lane == 0) rank_sorted(c, t, a.layer, b, s_rank, span);
