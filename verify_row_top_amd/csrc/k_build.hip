@@ -922,7 +922,32 @@ __device__ __forceinline__ void expand_row(const BArgs& a, int b, int node, floa
       for (int k = 0; k < w; ++k) t[k] = t[2 * k] + t[2 * k + 1];
     return wave_sum(t[0]);
   };
-  const float E = pairwise(e);
+  // E (the fp32 pairwise sum) and the tempered tail's mass in one butterfly. The tail
+  // mass stays unnormalised: the tempered normaliser cancels out of q~ = q_T / z_T and
+  // out of the draw (u z_T against partial sums of q_T, all scaled alike).
+  double tl = 0.0;
+#pragma unroll
+  for (int k = 0; k < BS; ++k)
+    if (lane * BS + k >= t0) tl += et[k];
+  float te;
+  {
+    float t[BS];
+#pragma unroll
+    for (int k = 0; k < BS; ++k) t[k] = e[k];
+#pragma unroll
+    for (int w = BS >> 1; w >= 1; w >>= 1)
+#pragma unroll
+      for (int k = 0; k < w; ++k) t[k] = t[2 * k] + t[2 * k + 1];
+    te = t[0];
+  }
+  double zT = tl;
+  te += xchg<1>(te), zT += xchg<1>(zT);
+  te += xchg<2>(te), zT += xchg<2>(zT);
+  te += xchg<4>(te), zT += xchg<4>(zT);
+  te += xchg<8>(te), zT += xchg<8>(zT);
+  te += xchg<16>(te), zT += xchg<16>(zT);
+  te += xchg<32>(te), zT += xchg<32>(zT);
+  const float E = te;
   float qt[BS];
 #pragma unroll
   for (int k = 0; k < BS; ++k) {
@@ -932,17 +957,6 @@ __device__ __forceinline__ void expand_row(const BArgs& a, int b, int node, floa
     s_q[r] = q;
   }
   const float zr = pairwise(qt);
-  double zl = 0.0;
-#pragma unroll
-  for (int k = 0; k < BS; ++k) zl += et[k];
-  const double Z = wave_sum(zl);
-  double tl = 0.0;
-#pragma unroll
-  for (int k = 0; k < BS; ++k) {
-    et[k] = et[k] / Z;  // q_T
-    if (lane * BS + k >= t0) tl += et[k];
-  }
-  const double zT = wave_sum(tl);
   wave_sync();
 
   int js = -1;
