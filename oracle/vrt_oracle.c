@@ -1202,9 +1202,12 @@ static void enum_layers(enum_ctx* E, int32_t* force, int32_t layer) {
   for (int32_t j = 0; j < nf; ++j) force[r0 + j] = t0;
 }
 
+/* Parents a layer may expand: the beam width, or SMART's node budget. */
+static int32_t enum_maxpar(const orc_cfg* c) { return c->mode == ORC_SMART ? c->budget : width_of(c); }
+
 static void enum_law(enum_ctx* E) {
   const orc_cfg* c = E->cfg;
-  const int32_t maxpar = width_of(c);
+  const int32_t maxpar = enum_maxpar(c);
   const int32_t n_rows = 1 + (c->D - 1) * maxpar;
   const int32_t n_sup = enum_sup(c);
   const int32_t t0 = c->order == ORC_PROBE_LAST ? (c->K - 1 < n_sup ? c->K - 1 : n_sup) : (c->probe ? c->m : 0);
@@ -1217,7 +1220,7 @@ static void enum_law(enum_ctx* E) {
 int32_t orc_exact_law(const orc_cfg* cfg, int32_t max_len, const float* draft_tab, const float* target_tab,
                       const int32_t* prefix, int32_t np, int32_t two, double* law1, double* law2,
                       double* accept) {
-  if (cfg->mode != ORC_TOPR || width_of(cfg) > 64) return -2;
+  if (enum_maxpar(cfg) > 64) return -2;
   const int32_t V = cfg->V;
   double* fresh = (double*)malloc(sizeof(double) * (size_t)V * (size_t)V);
   for (int64_t k = 0; k < (int64_t)V * V; ++k) fresh[k] = NAN;

@@ -144,7 +144,7 @@ int32_t orc_table_trials(const orc_cfg* cfg, int32_t max_len, const float* draft
                          int32_t* n_exempt);
 
 /* Exact laws of one step on a context-table model (rows indexed as for
- * orc_table_trials), for tiny top-R configurations (truncated or dense support): every probe
+ * orc_table_trials), for tiny configurations (top-R or SMART, truncated or dense support): every probe
  * draw and every accept/reject or final sample is taken as a branch weighted by its
  * probability, through the same expansion and decision code the sampler runs.
  *   law1[V]     P(first emitted token = v) of the step at context prefix[0..np)
@@ -154,7 +154,7 @@ int32_t orc_table_trials(const orc_cfg* cfg, int32_t max_len, const float* draft
  * RheoSampling's highlights state that the step is lossless for any prune budget: law1 is
  * then the target's tempered softmax at the context and law2 its two-step product.
  * Returns 0, -1 if the table is too short for the paths, -2 for an unsupported
- * configuration (SMART mode, W > 64). */
+ * configuration (more than 64 parents per layer: W, or SMART's budget). */
 int32_t orc_exact_law(const orc_cfg* cfg, int32_t max_len, const float* draft_tab, const float* target_tab,
                       const int32_t* prefix, int32_t np, int32_t two, double* law1, double* law2,
                       double* accept);

@@ -11,7 +11,8 @@ Losslessness then fixes the result exactly, independently of the oracle:
     comes from the same tree or from the next step;
 to 1e-12, for probe first and probe last, m in {0, 1, 3}, supports shorter than V, the
 dense support (the whole vocabulary, the probe drawn in token-id order), prune budgets
-below K and the plain top-K tree. At depth 1 the probability that the first token comes
+below K, the plain top-K tree and trees shaped by SMART's keep rule (which the laws do
+not pin: any kept subtree is verified losslessly). At depth 1 the probability that the first token comes
 from the tree must also equal the closed forms derived from key design 3
 (tests/test_oracle_lossless.py, tests/test_oracle_rrsw.py) to 1e-12; for the dense
 support the closed form is that of a truncated support holding all V tokens, since the
@@ -57,6 +58,14 @@ CONFIGS = [
     ("dense_m3_K4_T08", dict(V=6, trunc=orc.DENSE, K=4, m=3, D=2, W=1, R=5, T=0.8), 43),
     ("dense_probe_last_D3", dict(V=6, trunc=orc.DENSE, K=3, m=1, D=3, W=2, R=5, T=1.0,
                                  order=orc.PROBE_LAST), 44),
+    # SMART's keep rule shapes the tree (a parent keeps some of its children, the frontier
+    # varies); the step stays lossless whatever the rule keeps
+    ("smart_budget4", dict(V=6, trunc=6, K=3, m=1, D=3, mode=orc.SMART, budget=4, T=1.0,
+                           alpha=1.0, lam=0.02, gamma=0.01, delta=0.004, rho=1.3), 51),
+    ("smart_budget6_m0_T06", dict(V=6, trunc=6, K=3, m=0, D=3, mode=orc.SMART, budget=6, T=0.6,
+                                  alpha=50.0, lam=0.02, gamma=0.01, delta=0.004, rho=1.3), 52),
+    ("smart_dense_alpha08", dict(V=6, trunc=orc.DENSE, K=3, m=1, D=3, mode=orc.SMART, budget=5,
+                                 T=1.0, alpha=0.8, lam=0.02, gamma=0.01, delta=0.004, rho=1.3), 53),
 ]
 
 
