@@ -61,6 +61,9 @@ struct BArgs {
   uint64_t* half_keys;  // split rows: [B][FP][2][list length] each half's sorted support
   int* half_meta;       // split rows: [B][FP][2] each half's support size | non-finite << 30
   uint64_t epoch;       // split rows: this launch's tag base, unique within the process
+  int rpt;              // rows per tree at this layer (1 at the root, else FP)
+  int mixed;            // > 0: a 1-D grid whose first `mixed` rows (tree-major) are whole
+                        // and whose other rows are split over two blocks each
 };
 
 // The node frontier position j of tree b expands at this layer (-1 = root), or -2
@@ -1155,7 +1158,7 @@ __device__ __forceinline__ void rank_wave(const BArgs& a, int b, uint64_t* s_ran
 
 __device__ __forceinline__ void rank_if_last(const BArgs& a, int b, uint64_t* s_rank) {
   const int lane = lane_id();
-  const int rows = (int)gridDim.x / a.split;
+  const int rows = a.rpt;
   if (rows > 1) {
     wait_stores();
     int old = 0;
@@ -1225,8 +1228,20 @@ template <int DT, int PL, bool SPLIT>
 __global__ __launch_bounds__(kSelWaves * kWave)
 __attribute__((amdgpu_waves_per_eu(PL == 2 ? 4 : 2, 8))) void k_select_expand(const BArgs a) {
   const Cfg& c = a.c;
-  constexpr int S = SPLIT ? 2 : 1;
-  const int j = blockIdx.x / S, h = blockIdx.x % S, b = blockIdx.y;
+  int S = SPLIT ? 2 : 1, j = blockIdx.x / S, h = blockIdx.x % S, b = blockIdx.y;
+  if (SPLIT && a.mixed > 0) {
+    // rows r = b * rpt + j below `mixed` are whole, the others split; the halves come
+    // first in the grid: a CU's older waves win its memory pipeline, and a half that
+    // streams beside a whole row must not finish last
+    const int k = blockIdx.x;
+    const int nh = 2 * (a.c.B * a.rpt - a.mixed);  // blocks of split rows
+    const bool whole = k >= nh;
+    const int r = whole ? k - nh : a.mixed + (k >> 1);
+    S = whole ? 1 : 2;
+    h = whole ? 0 : (k & 1);
+    b = r / a.rpt;
+    j = r - b * a.rpt;
+  }
   const int wave = threadIdx.x >> 6;
   constexpr int N = PL * kWave;
   __shared__ uint64_t s_rank[kRankFused];
@@ -1264,7 +1279,7 @@ __attribute__((amdgpu_waves_per_eu(PL == 2 ? 4 : 2, 8))) void k_select_expand(co
   int any_bad = path == 1;
   if (wave != 0) return;
   wave_sync();
-  if constexpr (SPLIT) {
+  if (SPLIT && S == 2) {
     if (!join_halves<PL>(a, b, j, h, n_sup, any_bad, s_sup)) return;
     if (a.layer == 0) init_tree(a, b);
   }
@@ -1964,6 +1979,10 @@ hipError_t launch_select(const BArgs& a, dim3 grid, hipStream_t stream) {
 
 template <int DT>
 hipError_t launch_layer(const BArgs& a, int rows, hipStream_t stream) {
+  if (a.mixed > 0) {
+    const int n_rows = a.c.B * rows;
+    return launch_select<DT, true>(a, dim3(a.mixed + 2 * (n_rows - a.mixed)), stream);
+  }
   const dim3 grid(rows * a.split, a.c.B);
   if (a.c.trunc == VRT_DENSE) {
     hipLaunchKernelGGL((k_dense_expand<DT>), grid, dim3(8 * kWave), 0, stream, a);
@@ -2012,8 +2031,27 @@ bool split_rows(const Cfg& c, int layer) {
 // Tags of split launches: a process-wide counter from a random start.
 static std::atomic<uint64_t> g_epoch{((uint64_t)std::random_device{}() << 32) ^ std::random_device{}()};
 
+// Layers of more rows than the GPU has CUs put two rows on some CUs, and those CUs finish
+// their loads last (a CU streams at most ~28 GB/s). Up to 1.5 rows per CU, one row per CU
+// stays whole and the rest are split over two blocks each (the split rows' lists in the
+// workspace), so that no CU streams more than 1.5 rows: at the headline 256 whole rows
+// and 64 split ones, 0.253 against 0.262 ms of build per step.
+static bool mixable(const Cfg& c) { return c.trunc != VRT_DENSE && !split_rows(c, 0) && c.B * c.FP > 64; }
+
+static int cu_count() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) v = -1;
+    cached[dev] = v > 0 ? v : -1;
+  }
+  return cached[dev] > 0 ? cached[dev] : 0;
+}
+
 size_t build_ws_bytes(const Cfg& c) {
-  if (!split_rows(c, 0)) return 0;
+  if (!split_rows(c, 0) && !mixable(c)) return 0;
   const size_t rows = (size_t)c.B * c.FP * 2;
   return rows * list_len(c) * 8 + rows * 4;
 }
@@ -2023,11 +2061,18 @@ hipError_t launch_build_layer(const Cfg& c, const TreePtrs& t, int layer, const 
                               uint32_t* stats, void* ws, hipStream_t stream) {
   const int span = (layer == 0 ? 1 : c.P) * c.K;
   const bool split = split_rows(c, layer);
-  uint64_t* hk = (uint64_t*)ws;
-  int* hm = split ? (int*)(hk + (size_t)c.B * c.FP * 2 * list_len(c)) : nullptr;
-  BArgs a{c, t, layer, logits, ld, tstride, seed, step, stats, span <= kRankFused ? 1 : 0,
-          split ? 2 : 1, split ? hk : nullptr, hm, split ? g_epoch.fetch_add(1) : 0};
   const int rows = layer == 0 ? 1 : c.FP;
+  const int ncu = cu_count();
+  const int n_rows = c.B * rows;
+  // one whole row per CU (dispatched first, one per CU), the other rows halved into the
+  // CUs' second slots
+  const int mixed =
+      (layer > 0 && !split && mixable(c) && ncu > 0 && n_rows > ncu && 2 * n_rows <= 3 * ncu) ? ncu : 0;
+  const bool lists = split || mixed > 0;
+  uint64_t* hk = (uint64_t*)ws;
+  int* hm = lists ? (int*)(hk + (size_t)c.B * c.FP * 2 * list_len(c)) : nullptr;
+  BArgs a{c, t, layer, logits, ld, tstride, seed, step, stats, span <= kRankFused ? 1 : 0,
+          split ? 2 : 1, lists ? hk : nullptr, hm, lists ? g_epoch.fetch_add(1) : 0, rows, mixed};
   hipError_t e = c.dtype == VRT_BF16 ? launch_layer<VRT_BF16>(a, rows, stream)
                                      : launch_layer<VRT_F32>(a, rows, stream);
   if (e != hipSuccess) return e;
