@@ -156,9 +156,10 @@ typedef struct {
  *   node_row    i32 [B][N]       expansion row of node i if its probe child is kept,
  *                                else -1
  * Build scratch:
- *   row_sync    u64 [B][FP]  where a layer's rows are split over two blocks, the tag
- *                            of the half that finished first (needs no initial
- *                            value; the second half sets it back to 0)
+ *   row_sync    u64 [B][FP]  where a layer's rows are split over 2 or 4 blocks (rows
+ *                            too long for one block; rows beyond one per CU), the
+ *                            launch's tag and how many parts have finished (needs
+ *                            no initial value; the last part sets it back to 0)
  * SMART mode only (empty otherwise), one table for the whole batch, not per tree:
  *   smart_cost  f64 [budget+2][2]  C(n) and C'(n) of SMART key design 2 for tree sizes
  *                            n = 0 .. budget+1, evaluated in fp64 by the host's libm

@@ -86,6 +86,15 @@ CASES = [
     ("exact_path_bf16_V400000", _small(V=400000, R=20, D=3, B=2)),
     ("edge_T01", _small(T=0.1, R=30, D=5)),
     ("edge_D16_narrow", _small(W=2, K=3, m=1, R=40, D=16)),
+    # layers of more rows than CUs (256): one row per CU whole, the rest split in quarters
+    # (up to 1.25 rows per CU) or halves (up to 1.5), or whole when a row has too few
+    # segments for the parts
+    ("mixed_quarters_B27", _small(B=27, K=10, W=10, V=57000, R=30, D=3)),
+    ("mixed_quarters_fp32_B27", _small(B=27, K=10, W=10, V=30000, R=30, D=3, dtype=synth.F32)),
+    ("mixed_halves_B36", _small(B=36, K=10, W=10, V=20000, R=30, D=3)),
+    ("mixed_halves_m0_T06_B38", _small(B=38, K=10, W=10, V=40000, R=30, D=3, m=0, T=0.6)),
+    ("mixed_guard_one_segment_B30", _small(B=30, K=10, W=10, V=5000, R=30, D=3)),
+    ("mixed_smart_B30", _smart_small(B=30, budget=10, K=4, D=4, V=20000)),
     ("smart_small", _smart_small()),
     ("smart_small_m0_alpha08", _smart_small(m=0, alpha=0.8, budget=24)),
     # the largest budget: 1024 frontier slots per tree (row blocks without a parent clear

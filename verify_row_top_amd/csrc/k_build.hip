@@ -58,12 +58,13 @@ struct BArgs {
   uint32_t* stats;
   int fuse_rank;  // the layer's ranking runs in its row blocks
   int split;      // blocks per row: 1, or 2 (each selects from half of the row's segments)
-  uint64_t* half_keys;  // split rows: [B][FP][2][list length] each half's sorted support
-  int* half_meta;       // split rows: [B][FP][2] each half's support size | non-finite << 30
+  uint64_t* half_keys;  // split rows: [B][FP][4][list length] each part's sorted support
+  int* half_meta;       // split rows: [B][FP][4] each part's support size | non-finite << 30
   uint64_t epoch;       // split rows: this launch's tag base, unique within the process
   int rpt;              // rows per tree at this layer (1 at the root, else FP)
   int mixed;            // > 0: a 1-D grid whose first `mixed` rows (tree-major) are whole
-                        // and whose other rows are split over two blocks each
+                        // and whose other rows are split over `parts` blocks each
+  int parts;            // 2 or 4
 };
 
 // The node frontier position j of tree b expands at this layer (-1 = root), or -2
@@ -1173,56 +1174,70 @@ __device__ __forceinline__ void rank_if_last(const BArgs& a, int b, uint64_t* s_
   if (lane == 0) a.t.layer_sync[b] = 0;
 }
 
-// A row split over two blocks, wave 0 of each: every block has the top TC of its half
-// of the row in s_sup (n_sup keys, sorted); the row's top TC are among the two lists.
+// A row split over P blocks (2 or 4), wave 0 of each: every block has the top TC of its
+// part of the row in s_sup (n_sup keys, sorted); the row's top TC are among the P lists.
 // Each block writes its list and status device-coherently, waits for the stores and
-// swaps its tag (2·epoch + half) into the row's row_sync word; the block that takes out
-// the other half's tag of this launch is the second (the word needs no initial value:
-// it holds tags of earlier launches or whatever the blob held). The first is done
-// (returns false), the second merges the other's list into its own and combines the
-// status.
+// counts itself on the row's row_sync word, which holds this launch's tag (the low 32
+// bits of its epoch) above the count: a compare-and-swap puts the tag in with count 1 if
+// the word holds another tag (earlier launches, or whatever the blob held: no initial
+// value is needed), else adds 1; each failed swap means another block counted, so a
+// block retries at most P - 1 times. The block whose count is P is the last: it sets the
+// word back to 0 (a launch repeated with the same tag, a replayed graph, starts afresh),
+// merges the other lists into its own and combines the status; the others are done
+// (false).
+constexpr int kMaxParts = 4;
+
 template <int PL>
-__device__ __forceinline__ bool join_halves(const BArgs& a, int b, int j, int h, int& n_sup,
-                                            int& any_bad, uint64_t* s_sup) {
+__device__ __forceinline__ bool join_parts(const BArgs& a, int b, int j, int h, int P, int& n_sup,
+                                           int& any_bad, uint64_t* s_sup) {
   const Cfg& c = a.c;
   constexpr int N = PL * kWave;
   const int lane = lane_id();
   const int64_t r = (int64_t)b * c.FP + j;
-  uint64_t* mine = a.half_keys + (r * 2 + h) * N;
+  uint64_t* mine = a.half_keys + (r * kMaxParts + h) * N;
   static_for<PL>([&](auto s) { st_dev64(&mine[lane * PL + s], s_sup[lane * PL + s]); });
-  if (lane == 0) st_dev(&a.half_meta[r * 2 + h], n_sup | (any_bad << 30));
+  if (lane == 0) st_dev(&a.half_meta[r * kMaxParts + h], n_sup | (any_bad << 30));
   wait_stores();
-  int second = 0;
+  int last = 0;
   if (lane == 0) {
-    const unsigned long long old =
-        atomicExch((unsigned long long*)&a.t.row_sync[r], (unsigned long long)(a.epoch * 2 + h));
-    second = old == (unsigned long long)(a.epoch * 2 + (1 - h));
+    const unsigned long long tag = (unsigned long long)(uint32_t)a.epoch << 32;
+    unsigned long long* word = (unsigned long long*)&a.t.row_sync[r];
+    unsigned long long w = (unsigned long long)ld_dev64(&a.t.row_sync[r]);
+    for (int tries = 0; tries <= kMaxParts; ++tries) {
+      const unsigned long long want = (w & 0xFFFFFFFF00000000ull) == tag ? w + 1ull : tag | 1ull;
+      const unsigned long long got = atomicCAS(word, w, want);
+      if (got == w) {
+        last = (int)(want & 0xFFFFFFFFull) == P;
+        break;
+      }
+      w = got;
+    }
   }
-  second = __shfl(second, 0, kWave);
-  if (!second) return false;
-  // both halves have swapped their tags in: the word goes back to 0, so that a launch
-  // repeated with the same arguments (a replayed graph, the same epoch) starts afresh
+  last = __shfl(last, 0, kWave);
+  if (!last) return false;
   if (lane == 0) st_dev64(&a.t.row_sync[r], 0ull);
-  const uint64_t* other = a.half_keys + (r * 2 + (1 - h)) * N;
-  const int om = ld_dev(&a.half_meta[r * 2 + (1 - h)]);
-  uint64_t top[PL], add[PL];
-  static_for<PL>([&](auto s) {
-    top[s] = s_sup[lane * PL + s];
-    add[s] = ld_dev64(&other[lane * PL + s]);
-  });
-  wave_merge_top<PL>(top, add);
+  uint64_t top[PL];
+  static_for<PL>([&](auto s) { top[s] = s_sup[lane * PL + s]; });
+  for (int o = 0; o < P; ++o) {
+    if (o == h) continue;
+    const uint64_t* other = a.half_keys + (r * kMaxParts + o) * N;
+    const int om = ld_dev(&a.half_meta[r * kMaxParts + o]);
+    uint64_t add[PL];
+    static_for<PL>([&](auto s) { add[s] = ld_dev64(&other[lane * PL + s]); });
+    wave_merge_top<PL>(top, add);
+    n_sup = min(c.TC, n_sup + (om & 0xFFFF));
+    any_bad |= (om >> 30) & 1;
+  }
   static_for<PL>([&](auto s) {
     const int p = lane * PL + s;
     s_sup[p] = p < c.TC ? top[s] : 0ull;
   });
-  n_sup = min(c.TC, n_sup + (om & 0xFFFF));
-  any_bad |= (om >> 30) & 1;
   wave_sync();
   return true;
 }
 
 // One block per expanded parent (or two, each on half of the row's segments, joined by
-// join_halves), then wave 0 expands it: the row-wide path, the exact path behind it
+// join_parts), then wave 0 expands it: the row-wide path, the exact path behind it
 // (ties, flat rows, rows longer than the row-wide path covers).
 template <int DT, int PL, bool SPLIT>
 __global__ __launch_bounds__(kSelWaves * kWave)
@@ -1233,12 +1248,12 @@ __attribute__((amdgpu_waves_per_eu(PL == 2 ? 4 : 2, 8))) void k_select_expand(co
     // rows r = b * rpt + j below `mixed` are whole, the others split; the halves come
     // first in the grid: a CU's older waves win its memory pipeline, and a half that
     // streams beside a whole row must not finish last
-    const int k = blockIdx.x;
-    const int nh = 2 * (a.c.B * a.rpt - a.mixed);  // blocks of split rows
+    const int k = blockIdx.x, P = a.parts;
+    const int nh = P * (a.c.B * a.rpt - a.mixed);  // blocks of split rows
     const bool whole = k >= nh;
-    const int r = whole ? k - nh : a.mixed + (k >> 1);
-    S = whole ? 1 : 2;
-    h = whole ? 0 : (k & 1);
+    const int r = whole ? k - nh : a.mixed + k / P;
+    S = whole ? 1 : P;
+    h = whole ? 0 : k % P;
     b = r / a.rpt;
     j = r - b * a.rpt;
   }
@@ -1279,8 +1294,8 @@ __attribute__((amdgpu_waves_per_eu(PL == 2 ? 4 : 2, 8))) void k_select_expand(co
   int any_bad = path == 1;
   if (wave != 0) return;
   wave_sync();
-  if (SPLIT && S == 2) {
-    if (!join_halves<PL>(a, b, j, h, n_sup, any_bad, s_sup)) return;
+  if (SPLIT && S > 1) {
+    if (!join_parts<PL>(a, b, j, h, S, n_sup, any_bad, s_sup)) return;
     if (a.layer == 0) init_tree(a, b);
   }
   end_row<PL>(a, b, j, node, sp, n_sup, any_bad != 0, s_sup, s_q);
@@ -1981,7 +1996,7 @@ template <int DT>
 hipError_t launch_layer(const BArgs& a, int rows, hipStream_t stream) {
   if (a.mixed > 0) {
     const int n_rows = a.c.B * rows;
-    return launch_select<DT, true>(a, dim3(a.mixed + 2 * (n_rows - a.mixed)), stream);
+    return launch_select<DT, true>(a, dim3(a.mixed + a.parts * (n_rows - a.mixed)), stream);
   }
   const dim3 grid(rows * a.split, a.c.B);
   if (a.c.trunc == VRT_DENSE) {
@@ -2033,9 +2048,10 @@ static std::atomic<uint64_t> g_epoch{((uint64_t)std::random_device{}() << 32) ^ 
 
 // Layers of more rows than the GPU has CUs put two rows on some CUs, and those CUs finish
 // their loads last (a CU streams at most ~28 GB/s). Up to 1.5 rows per CU, one row per CU
-// stays whole and the rest are split over two blocks each (the split rows' lists in the
-// workspace), so that no CU streams more than 1.5 rows: at the headline 256 whole rows
-// and 64 split ones, 0.253 against 0.262 ms of build per step.
+// stays whole and the rest are split over four blocks each (up to 1.25 rows per CU) or two
+// (the parts' lists in the workspace): at the headline 256 whole rows and 64 split ones,
+// 0.253 against 0.262 ms of build per step (quarters and halves measure the same there:
+// once its part is done, a whole row streams alone at one block's rate).
 static bool mixable(const Cfg& c) { return c.trunc != VRT_DENSE && !split_rows(c, 0) && c.B * c.FP > 64; }
 
 static int cu_count() {
@@ -2052,8 +2068,8 @@ static int cu_count() {
 
 size_t build_ws_bytes(const Cfg& c) {
   if (!split_rows(c, 0) && !mixable(c)) return 0;
-  const size_t rows = (size_t)c.B * c.FP * 2;
-  return rows * list_len(c) * 8 + rows * 4;
+  const size_t parts = (size_t)c.B * c.FP * kMaxParts;
+  return parts * list_len(c) * 8 + parts * 4;
 }
 
 hipError_t launch_build_layer(const Cfg& c, const TreePtrs& t, int layer, const void* logits,
@@ -2064,15 +2080,23 @@ hipError_t launch_build_layer(const Cfg& c, const TreePtrs& t, int layer, const 
   const int rows = layer == 0 ? 1 : c.FP;
   const int ncu = cu_count();
   const int n_rows = c.B * rows;
-  // one whole row per CU (dispatched first, one per CU), the other rows halved into the
-  // CUs' second slots
-  const int mixed =
-      (layer > 0 && !split && mixable(c) && ncu > 0 && n_rows > ncu && 2 * n_rows <= 3 * ncu) ? ncu : 0;
+  // one whole row per CU, the other rows in quarters (up to 1.25 rows per CU) or halves
+  // (up to 1.5) in the CUs' second slots
+  const int seg = c.dtype == VRT_BF16 ? seg_elems<VRT_BF16>() : seg_elems<VRT_F32>();
+  const int G = (c.V + seg - 1) / seg;
+  // every part takes at least one segment: parts of ceil(G / P) segments, the last one too
+  auto fits = [G](int P) { return (P - 1) * ((G + P - 1) / P) < G; };
+  const int parts = (4 * (n_rows - ncu) <= ncu && fits(4)) ? 4 : 2;
+  const int mixed = (layer > 0 && !split && mixable(c) && ncu > 0 && n_rows > ncu &&
+                     2 * n_rows <= 3 * ncu && fits(parts))
+                        ? ncu
+                        : 0;
   const bool lists = split || mixed > 0;
   uint64_t* hk = (uint64_t*)ws;
-  int* hm = lists ? (int*)(hk + (size_t)c.B * c.FP * 2 * list_len(c)) : nullptr;
+  int* hm = lists ? (int*)(hk + (size_t)c.B * c.FP * kMaxParts * list_len(c)) : nullptr;
   BArgs a{c, t, layer, logits, ld, tstride, seed, step, stats, span <= kRankFused ? 1 : 0,
-          split ? 2 : 1, lists ? hk : nullptr, hm, lists ? g_epoch.fetch_add(1) : 0, rows, mixed};
+          split ? 2 : 1, lists ? hk : nullptr, hm, lists ? g_epoch.fetch_add(1) : 0, rows, mixed,
+          parts};
   hipError_t e = c.dtype == VRT_BF16 ? launch_layer<VRT_BF16>(a, rows, stream)
                                      : launch_layer<VRT_F32>(a, rows, stream);
   if (e != hipSuccess) return e;
