@@ -1181,7 +1181,9 @@ __device__ __forceinline__ void rank_if_last(const BArgs& a, int b, uint64_t* s_
 // bits of its epoch) above the count: a compare-and-swap puts the tag in with count 1 if
 // the word holds another tag (earlier launches, or whatever the blob held: no initial
 // value is needed), else adds 1; each failed swap means another block counted, so a
-// block retries at most P - 1 times. The block whose count is P is the last: it sets the
+// block retries at most P - 1 times (the loop's bound only matters if another launch used
+// the same blob at the same time, which the ABI rules out). The block whose count is P
+// is the last: it sets the
 // word back to 0 (a launch repeated with the same tag, a replayed graph, starts afresh),
 // merges the other lists into its own and combines the status; the others are done
 // (false).
