@@ -1059,9 +1059,9 @@ __device__ __forceinline__ void expand_row(const BArgs& a, int b, int node, floa
 // Returns the node the row expands, or -2 after clearing the row's candidate slots
 // (no parent at this frontier position).
 // Layer 0, wave 0 of the block that expands the root: clears the later layers'
-// candidate slots and starts the SMART state. (With the root row split over two blocks
-// the block that expands it is known only after the join, and it is the one that reads
-// the state.)
+// candidate slots and starts the SMART state. (With the root row split over several
+// blocks the block that expands it is known only after the join, and it is the one that
+// reads the state.)
 __device__ __forceinline__ void init_tree(const BArgs& a, int b) {
   const Cfg& c = a.c;
   const int lane = lane_id();
