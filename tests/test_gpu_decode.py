@@ -19,6 +19,9 @@ pytestmark = pytest.mark.gpu
 @pytest.mark.parametrize("name,w,n_steps", [
     ("b8", workloads.get("b8"), 16),
     ("headline_T06_B8", workloads.get("headline", T=0.6, B=8), 4),
+    # 270 rows per layer on 256 CUs: the rows beyond one per CU split in quarters, whose
+    # joins run on the same row words with a new tag every launch
+    ("rows_beyond_cus_B27", workloads.get("headline", B=27, V=57000), 3),
 ], ids=lambda x: x if isinstance(x, str) else None)
 def test_decode_steps_match_oracle_on_every_tree(gpu, name, w, n_steps):
     seed = 11
