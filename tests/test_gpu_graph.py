@@ -22,6 +22,9 @@ pytestmark = pytest.mark.gpu
     ("split_fp32_V70000", _small(dtype=synth.F32, V=70000, R=30, D=4, B=3)),
     ("smart_small", _smart_small(B=3)),
     ("headline_rows", _small(V=128256, R=60, D=4, K=10, B=2)),
+    # 270 rows per layer on 256 CUs: the extra rows in quarters, joined on row words that
+    # carry the same tag in every replay
+    ("rows_beyond_cus", _small(B=27, K=10, W=10, V=57000, R=30, D=3)),
 ], ids=lambda x: x if isinstance(x, str) else None)
 def test_captured_step_replays_match_oracle(gpu, name, w):
     seed, step = 9, 4
