@@ -1705,23 +1705,117 @@ __device__ void rank_sorted(const Cfg& c, const TreePtrs& t, int layer, int b, c
 }
 
 // Ranking as a kernel of its own (layers of more than kRankFused children): one block
-// per tree sorts the keys in LDS.
-__global__ __launch_bounds__(256) void k_rank_layer(const Cfg c, const TreePtrs t, int layer) {
+// per tree gathers the keys of the children the layer created to the front of LDS and
+// sorts only those. Top-R then writes the first W as the frontier. For SMART, all
+// threads first fetch what the keep rule reads per position (the child's parent, the
+// cost-table entries C(|T|) and C'(|T|) at the size the tree has when that position is
+// tested), so the rule's sequential pass runs on LDS alone; the admitted prefix is
+// written out in parallel afterwards.
+constexpr int kRankT = 256;        // threads of the ranking block
+constexpr int kRankSmart = 1024;   // SMART positions it stages (the budget's maximum)
+constexpr int kRankPar = 4096;     // parents per layer it tracks (P * K is at most 4096)
+
+__global__ __launch_bounds__(kRankT) void k_rank_layer(const Cfg c, const TreePtrs t, int layer) {
   const int b = blockIdx.x;
+  const int tid = threadIdx.x, lane = lane_id();
   const int64_t ncb = (int64_t)b * c.NC;
   const int base = layer_base(c, layer);
   const int span = layer_span(c, layer);
-  const int np = next_pow2(max(span, 2));
-  extern __shared__ uint64_t s_keys[];
-  for (int i = threadIdx.x; i < np; i += blockDim.x) {
-    uint64_t k = 0ull;
-    if (i < span && (t.cand_kind[ncb + base + i] & 0xFF) != 0)
-      k = node_key(t.cand_score[ncb + base + i], (uint32_t)(base + i));
-    s_keys[i] = k;
+  extern __shared__ uint64_t s_keys[];  // next_pow2(span) keys
+  __shared__ int s_n, s_m;
+  // created children, in any order (the sort fixes it): one LDS atomic per wave and pass
+  if (tid == 0) s_n = 0;
+  __syncthreads();
+  for (int i0 = 0; i0 < span; i0 += 4 * kRankT) {
+    uint64_t k[4];
+    static_for<4>([&](auto s) {
+      const int i = i0 + s * kRankT + tid;
+      k[s] = 0ull;
+      if (i < span && (t.cand_kind[ncb + base + i] & 0xFF) != 0)
+        k[s] = node_key(t.cand_score[ncb + base + i], (uint32_t)(base + i));
+    });
+    static_for<4>([&](auto s) {
+      const uint64_t m = ballot(k[s] != 0ull);
+      int at = 0;
+      if (lane == 0 && m != 0ull) at = atomicAdd(&s_n, __builtin_popcountll(m));
+      at = __shfl(at, 0);
+      const int below = __builtin_popcountll(m & ((1ull << lane) - 1ull));
+      if (k[s] != 0ull) s_keys[at + below] = k[s];
+    });
   }
   __syncthreads();
+  const int n = s_n;
+  const int np = next_pow2(max(n, 2));
+  for (int i = n + tid; i < np; i += kRankT) s_keys[i] = 0ull;
+  __syncthreads();
   bitonic_desc(s_keys, np);
-  if (threadIdx.x == 0) rank_sorted(c, t, layer, b, s_keys, span);
+  const bool more = layer + 1 < c.D;
+  int* front = t.front + (int64_t)b * c.FP;
+  if (c.mode == VRT_MODE_TOPR) {
+    const int nf = more ? min(c.W, n) : 0;
+    for (int i = tid; i < nf; i += kRankT) front[i] = (int)(0xFFFFFFFFu - (uint32_t)s_keys[i]);
+    if (tid == 0) t.n_front[b] = nf;
+    return;
+  }
+  // SMART key design 3, as in rank_sorted: keep u iff alpha * g * C(|T|) > L * C'(|T|)
+  // with g = P(path) / |P|, the first rejection ends the layer. Position i is tested
+  // with |T| = n0 + i, since every position before it was admitted.
+  __shared__ int s_par[kRankSmart];
+  __shared__ double s_cn[kRankSmart], s_dc[kRankSmart];
+  __shared__ uint8_t s_pf[kRankPar];  // parent has an admitted child: 1 before, 2 set now
+  double* sm = t.smart + (int64_t)b * 8;
+  const double n0 = sm[1], nadm0 = sm[3];
+  const int stop = min(n, max(c.budget - (int)nadm0, 0));
+  const int pbase = layer > 0 ? layer_base(c, layer - 1) : 0;
+  const int pspan = layer > 0 ? layer_span(c, layer - 1) : 0;
+  for (int p = tid; p < pspan; p += kRankT)
+    s_pf[p] = (t.cand_kind[ncb + pbase + p] & 0x100) ? 1 : 0;
+  for (int i = tid; i < stop; i += kRankT) {
+    const int cu = (int)(0xFFFFFFFFu - (uint32_t)s_keys[i]);
+    s_par[i] = t.cand_parent[ncb + cu];
+    const int ni = min(max((int)(n0 + (double)i), 0), c.budget + 1);
+    s_cn[i] = t.smart_cost[2 * ni];
+    s_dc[i] = t.smart_cost[2 * ni + 1];
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double L = sm[0], nn = n0, P = sm[2], nadm = nadm0, root_has = sm[4];
+    int m = 0;
+    for (; m < stop; ++m) {
+      // the key's high word is the child's fp32 path score
+      const double g = (double)__uint_as_float((uint32_t)(s_keys[m] >> 32)) / P;
+      if (!(c.alpha * g * s_cn[m] > L * s_dc[m])) break;
+      const int par = s_par[m];
+      bool has;
+      if (par < 0) {
+        has = root_has != 0.0;
+        root_has = 1.0;
+      } else if (par - pbase >= 0 && par - pbase < pspan) {
+        has = s_pf[par - pbase] != 0;
+        if (!has) s_pf[par - pbase] = 2;
+      } else {  // not a node of the layer above: read and mark it in place
+        has = (t.cand_kind[ncb + par] & 0x100) != 0;
+        t.cand_kind[ncb + par] |= 0x100;
+      }
+      L += g;
+      nn += 1.0;
+      if (has) P += 1.0;
+      nadm += 1.0;
+    }
+    sm[0] = L; sm[1] = nn; sm[2] = P; sm[3] = nadm; sm[4] = root_has;
+    t.n_front[b] = more ? m : 0;
+    s_m = m;
+  }
+  __syncthreads();
+  const int m = s_m;
+  int* adm = t.admitted + (int64_t)b * c.N + (int)nadm0;
+  for (int i = tid; i < m; i += kRankT) {
+    const int cu = (int)(0xFFFFFFFFu - (uint32_t)s_keys[i]);
+    adm[i] = cu;
+    if (more) front[i] = cu;
+  }
+  for (int p = tid; p < pspan; p += kRankT)
+    if (s_pf[p] == 2) t.cand_kind[ncb + pbase + p] |= 0x100;
 }
 
 constexpr int kFT = 1024;          // threads of the finish block
@@ -2108,7 +2202,7 @@ hipError_t launch_build_layer(const Cfg& c, const TreePtrs& t, int layer, const 
   if (e != hipSuccess) return e;
   if (a.fuse_rank) return hipSuccess;
   const size_t lds2 = (size_t)next_pow2(max(span, 2)) * 8;
-  hipLaunchKernelGGL(k_rank_layer, dim3(c.B), dim3(256), lds2, stream, c, t, layer);
+  hipLaunchKernelGGL(k_rank_layer, dim3(c.B), dim3(kRankT), lds2, stream, c, t, layer);
   return hipGetLastError();
 }
 
