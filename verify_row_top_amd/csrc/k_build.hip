@@ -65,6 +65,9 @@ struct BArgs {
   int mixed;            // > 0: a 1-D grid whose first `mixed` rows (tree-major) are whole
                         // and whose other rows are split over `parts` blocks each
   int parts;            // 2 or 4
+  int compact;          // > 0: a compact grid of this many blocks over the layer's expanded
+                        // rows (SMART layers)
+  int rest;             // compact grids: blocks of the kernel that takes the rows beyond them
 };
 
 // The node frontier position j of tree b expands at this layer (-1 = root), or -2
@@ -1238,27 +1241,12 @@ __device__ __forceinline__ bool join_parts(const BArgs& a, int b, int j, int h, 
   return true;
 }
 
-// One block per expanded parent (or two, each on half of the row's segments, joined by
-// join_parts), then wave 0 expands it: the row-wide path, the exact path behind it
-// (ties, flat rows, rows longer than the row-wide path covers).
+// Part h of S of frontier position j of tree b, by one block; then wave 0 expands the
+// parent: the row-wide path, the exact path behind it (ties, flat rows, rows longer
+// than the row-wide path covers). Waves 1.. return once the row is read.
 template <int DT, int PL, bool SPLIT>
-__global__ __launch_bounds__(kSelWaves * kWave)
-__attribute__((amdgpu_waves_per_eu(PL == 2 ? 4 : 2, 8))) void k_select_expand(const BArgs a) {
+__device__ __forceinline__ void select_expand_row(const BArgs& a, int b, int j, int h, int S) {
   const Cfg& c = a.c;
-  int S = SPLIT ? 2 : 1, j = blockIdx.x / S, h = blockIdx.x % S, b = blockIdx.y;
-  if (SPLIT && a.mixed > 0) {
-    // rows r = b * rpt + j below `mixed` are whole, the others split; the halves come
-    // first in the grid: a CU's older waves win its memory pipeline, and a half that
-    // streams beside a whole row must not finish last
-    const int k = blockIdx.x, P = a.parts;
-    const int nh = P * (a.c.B * a.rpt - a.mixed);  // blocks of split rows
-    const bool whole = k >= nh;
-    const int r = whole ? k - nh : a.mixed + k / P;
-    S = whole ? 1 : P;
-    h = whole ? 0 : k % P;
-    b = r / a.rpt;
-    j = r - b * a.rpt;
-  }
   const int wave = threadIdx.x >> 6;
   constexpr int N = PL * kWave;
   __shared__ uint64_t s_rank[kRankFused];
@@ -1302,6 +1290,90 @@ __attribute__((amdgpu_waves_per_eu(PL == 2 ? 4 : 2, 8))) void k_select_expand(co
   }
   end_row<PL>(a, b, j, node, sp, n_sup, any_bad != 0, s_sup, s_q);
   if (a.fuse_rank) rank_if_last(a, b, s_rank);
+}
+
+// The rows of a compact grid (a layer whose frontier may hold far fewer than FP parents
+// per tree, as SMART's do): tree b's expanded rows are items pre[b] .. pre[b+1]-1 of a
+// tree-major list, and a grid of fewer blocks than B * FP walks the list. Rows that no
+// block takes hold no children: layer 0 cleared every later candidate slot.
+constexpr int kCompactTrees = kSelWaves * kWave;  // trees a compact grid takes
+
+// pre[0 .. B] in LDS from the frontier sizes (all threads; B <= kCompactTrees).
+__device__ __forceinline__ int compact_prefix(const BArgs& a, int* pre) {
+  __shared__ int s_wsum[kSelWaves];
+  const Cfg& c = a.c;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  int x = tid < c.B ? min(max(a.t.n_front[tid], 0), c.FP) : 0;
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
+  }
+  if (lane == kWave - 1) s_wsum[wave] = x;
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) x += s_wsum[w];
+  if (tid < c.B) pre[tid + 1] = x;
+  if (tid == 0) pre[0] = 0;
+  __syncthreads();
+  return pre[c.B];
+}
+
+// Tree and frontier position of item k of the compact list (block-uniform).
+__device__ __forceinline__ void compact_item(const BArgs& a, const int* pre, int k, int& b, int& j) {
+  int lo = 0, hi = a.c.B - 1;  // the last tree whose rows start at or before item k
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pre[mid] <= k) lo = mid;
+    else hi = mid - 1;
+  }
+  b = __builtin_amdgcn_readfirstlane(lo);
+  j = __builtin_amdgcn_readfirstlane(k - pre[lo]);
+}
+
+// One block per expanded parent (or per part of one: split rows, the mixed grid), or a
+// compact grid over the expanded rows.
+template <int DT, int PL, bool SPLIT>
+__global__ __launch_bounds__(kSelWaves * kWave)
+__attribute__((amdgpu_waves_per_eu(PL == 2 ? 4 : 2, 8))) void k_select_expand(const BArgs a) {
+  int S = SPLIT ? 2 : 1, j = blockIdx.x / S, h = blockIdx.x % S, b = blockIdx.y;
+  if (SPLIT && a.mixed > 0) {
+    // rows r = b * rpt + j below `mixed` are whole, the others split; the halves come
+    // first in the grid: a CU's older waves win its memory pipeline, and a half that
+    // streams beside a whole row must not finish last
+    const int k = blockIdx.x, P = a.parts;
+    const int nh = P * (a.c.B * a.rpt - a.mixed);  // blocks of split rows
+    const bool whole = k >= nh;
+    const int r = whole ? k - nh : a.mixed + k / P;
+    S = whole ? 1 : P;
+    h = whole ? 0 : k % P;
+    b = r / a.rpt;
+    j = r - b * a.rpt;
+  }
+  const bool compact = !SPLIT && a.compact > 0;
+  __shared__ int s_pre[kCompactTrees + 1];
+  int total = 0;
+  if (compact) {
+    total = __builtin_amdgcn_readfirstlane(compact_prefix(a, s_pre));
+    if ((int)blockIdx.x >= total) return;
+    compact_item(a, s_pre, blockIdx.x, b, j);
+  }
+  select_expand_row<DT, PL, SPLIT>(a, b, j, h, S);
+}
+
+// Rows of a compact list beyond the first a.compact (one per block of the compact grid):
+// the blocks of this grid take them in turn. A kernel of its own, so that the loop's
+// register demand stays out of the one-row kernel; with no such rows it only reads the
+// frontier sizes.
+template <int DT, int PL>
+__global__ __launch_bounds__(kSelWaves * kWave)
+__attribute__((amdgpu_waves_per_eu(PL == 2 ? 4 : 2, 8))) void k_select_rest(const BArgs a) {
+  __shared__ int s_pre[kCompactTrees + 1];
+  const int total = __builtin_amdgcn_readfirstlane(compact_prefix(a, s_pre));
+  for (int k = a.compact + blockIdx.x; k < total; k += gridDim.x) {
+    int b, j;
+    compact_item(a, s_pre, k, b, j);
+    select_expand_row<DT, PL, false>(a, b, j, 0, 1);
+    __syncthreads();  // the block's LDS changes hands
+  }
 }
 
 // ---------------------------------------------------------------------------------
@@ -1723,6 +1795,9 @@ __global__ __launch_bounds__(kRankT) void k_rank_layer(const Cfg c, const TreePt
   const int span = layer_span(c, layer);
   extern __shared__ uint64_t s_keys[];  // next_pow2(span) keys
   __shared__ int s_n, s_m;
+  // a tree that expanded no parent at this layer has no children to rank: its frontier
+  // stays empty and its SMART state as it is
+  if (layer > 0 && t.n_front[b] <= 0) return;
   // created children, in any order (the sort fixes it): one LDS atomic per wave and pass
   if (tid == 0) s_n = 0;
   __syncthreads();
@@ -2088,8 +2163,26 @@ hipError_t launch_select(const BArgs& a, dim3 grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int DT, int PL>
+void launch_rest(const BArgs& a, int blocks, hipStream_t stream) {
+  hipLaunchKernelGGL((k_select_rest<DT, PL>), dim3(blocks), dim3(kSelWaves * kWave), 0, stream, a);
+}
+
 template <int DT>
 hipError_t launch_layer(const BArgs& a, int rows, hipStream_t stream) {
+  if (a.compact > 0) {
+    const hipError_t e = launch_select<DT, false>(a, dim3(a.compact), stream);
+    const int extra = a.c.B * rows - a.compact;  // rows the compact grid may not reach
+    if (e != hipSuccess || extra <= 0) return e;
+    const int blocks = min(extra, a.rest);
+    switch (list_len(a.c) / kWave) {
+      case 2: launch_rest<DT, 2>(a, blocks, stream); break;
+      case 4: launch_rest<DT, 4>(a, blocks, stream); break;
+      case 8: launch_rest<DT, 8>(a, blocks, stream); break;
+      default: launch_rest<DT, 16>(a, blocks, stream); break;
+    }
+    return hipGetLastError();
+  }
   if (a.mixed > 0) {
     const int n_rows = a.c.B * rows;
     return launch_select<DT, true>(a, dim3(a.mixed + a.parts * (n_rows - a.mixed)), stream);
@@ -2194,9 +2287,17 @@ hipError_t launch_build_layer(const Cfg& c, const TreePtrs& t, int layer, const 
   const bool lists = split || mixed > 0;
   uint64_t* hk = (uint64_t*)ws;
   int* hm = lists ? (int*)(hk + (size_t)c.B * c.FP * kMaxParts * list_len(c)) : nullptr;
-  BArgs a{c, t, layer, logits, ld, tstride, seed, step, stats, span <= kRankFused ? 1 : 0,
+  // SMART frontiers are usually far below FP parents per tree: a compact grid of at most
+  // two blocks per CU walks the expanded rows (the ranking must run in its own kernel,
+  // since the grid reads every tree's frontier size)
+  const bool fuse = span <= kRankFused;
+  const int compact = (c.mode == VRT_MODE_SMART && layer > 0 && !fuse && !split && mixed == 0 &&
+                       c.trunc != VRT_DENSE && c.B <= kCompactTrees && ncu > 0)
+                          ? min(n_rows, 2 * ncu)
+                          : 0;
+  BArgs a{c, t, layer, logits, ld, tstride, seed, step, stats, fuse ? 1 : 0,
           split ? 2 : 1, lists ? hk : nullptr, hm, lists ? g_epoch.fetch_add(1) : 0, rows, mixed,
-          parts};
+          parts, compact, ncu};  // the rest of a compact list: one block per CU, a rare case
   hipError_t e = c.dtype == VRT_BF16 ? launch_layer<VRT_BF16>(a, rows, stream)
                                      : launch_layer<VRT_F32>(a, rows, stream);
   if (e != hipSuccess) return e;
