@@ -37,6 +37,7 @@ def parse():
     ap.add_argument("--t06-sets", type=int, default=8,
                     help="decode steps of the T=0.6 measurement (0: skip it)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
+    ap.add_argument("--no-graph", action="store_true", help="skip the graph-replayed steps")
     ap.add_argument("--verify-only", action="store_true",
                     help="time only the verification call (for profiling it alone)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -474,6 +475,46 @@ def measure(w, args, n_sets, lazy=True):
     if w.mode == 0 and not args.verify_only:
         r["build_gbps"] = B * n_draft * V * esz / (build_ms * 1e-3) / 1e9
 
+    # the same whole steps launched from HIP graphs: the step of each of the first (up to
+    # 16) sets captured once, with its launches' arguments fixed, then replays rotating over
+    # them; the GPU does the eager step's work without the host's per-launch cost. Each
+    # set's replay must emit the eager step's tokens.
+    if lazy and not args.verify_only and not args.no_graph:
+        gsets = sets[:min(len(sets), 16)]
+        ref = []
+        for st in gsets:
+            build(st)
+            verify(st)
+            torch.cuda.synchronize()
+            ref.append((out_tokens.clone(), out_len.clone()))
+        graphs = []
+        for st in gsets:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                build(st)
+                verify(st)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        same = True
+        for g, (rt, rl) in zip(graphs, ref):
+            out_tokens.fill_(-1)
+            out_len.fill_(-1)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            same &= bool(torch.equal(rt, out_tokens)) and bool(torch.equal(rl, out_len))
+        for k in range(args.warmup):
+            graphs[k % len(graphs)].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(args.steps):
+            graphs[k % len(graphs)].replay()
+        torch.cuda.synchronize()
+        gwall = time.perf_counter() - t0
+        r["graph_step"] = {"ms_per_step": gwall * 1e3 / args.steps, "trees_per_s": B * args.steps / gwall,
+                           "sets": len(graphs), "same_tokens_as_eager": same}
+        del graphs
+
     # the verification call on its own, for the roofline: every set's tree built into a blob
     # of its own (untimed), then the sets verified back to back between two HIP events on
     # the launch stream, so the average is the call's own duration (the in-step timing
@@ -633,6 +674,7 @@ def main():
         "near_threshold_draws": r["near_threshold_draws"],
         "status_bits": r["status_bits"],
         "lazy_verify": r.get("lazy_verify"),
+        "graph_step": r.get("graph_step"),
         "tree_mask_us": r.get("tree_mask_us"),
         "accepted_kv_us": r.get("accepted_kv_us"),
     }
