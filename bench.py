@@ -38,6 +38,9 @@ def parse():
                     help="decode steps of the T=0.6 measurement (0: skip it)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replayed steps")
+    ap.add_argument("--streams", type=int, default=0,
+                    help="calls per step, each on its own stream and B/streams trees with tree_base "
+                         "at its first tree (0: the workload's default)")
     ap.add_argument("--verify-only", action="store_true",
                     help="time only the verification call (for profiling it alone)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -382,6 +385,16 @@ def decode_inputs(w, cfg, dev, n_sets, seed, tree, ws, stats, views, out):
     return sets
 
 
+def default_streams(w):
+    """Calls per step: two for beam-and-prune batches of at least 16 trees, one otherwise.
+    Measured on one box: headline 0.296 against 0.348 ms per step, fp32 headline 0.491
+    against 0.583; at B = 8 two calls take 0.212 against 0.180 ms (rows of 64 KB leave
+    little stream to overlap, and the launches double), and SMART 0.395 against 0.193 ms
+    (its short kernels wait on the host's launches, which a second call multiplies)."""
+    from synth import workloads
+    return 2 if w.mode != workloads.SMART and w.B >= 16 and w.B % 2 == 0 else 1
+
+
 def measure(w, args, n_sets, lazy=True):
     """Build + verify steps of workload w over n_sets decode steps: warm-up, then timed
     steps rotating over the sets. Returns the measurements as a dict."""
@@ -461,7 +474,57 @@ def measure(w, args, n_sets, lazy=True):
     ms_per_step = wall * 1e3 / args.steps
     verify_bytes = sum(int(st["n_nodes"].sum()) for st in used) * V * esz / args.steps
     tokens = sum(st["tokens"] for st in used)
-    r = {"cfg": cfg, "tree": tree, "sets": sets, "B": B, "esz": esz, "ld": ld,
+    one_call_ms = ms_per_step
+
+    # the step issued as S calls, each on its own stream and B/S trees (tree_base at its
+    # first tree): one call's dependent phases (the rows' post-load work, the layer
+    # ranking, launch gaps) overlap the other calls' row streams. The calls give the one
+    # call's trees and tokens bit for bit; set 0's step is checked.
+    S = default_streams(w) if getattr(args, "streams", 0) == 0 else args.streams
+    split = None
+    if S > 1 and B % S == 0 and not args.verify_only:
+        Bp = B // S
+        pcfg = [vrt.make_config(B=Bp, V=w.V, dtype=w.dtype, trunc=w.trunc, K=w.K, m=w.m, probe=w.probe,
+                                D=w.D, W=w.W, R=w.R, mode=w.mode, budget=w.budget, T=w.T, eps_m0=w.eps_m0,
+                                alpha=w.alpha, lam=w.lam, gamma=w.gamma, delta=w.delta, rho=w.rho,
+                                order=w.order, tree_base=p * Bp) for p in range(S)]
+        ptree = [torch.zeros(vrt.tree_bytes(c), dtype=torch.uint8, device=dev) for c in pcfg]
+        pws = [torch.zeros(vrt.workspace_bytes(c), dtype=torch.uint8, device=dev) for c in pcfg]
+        pstreams = [torch.cuda.Stream() for _ in range(S)]  # default priority
+
+        def split_step(st):
+            for p in range(S):
+                sl = slice(p * Bp, (p + 1) * Bp)
+                with torch.cuda.stream(pstreams[p]):
+                    for layer in range(D):
+                        vrt.build_tree(pcfg[p], layer, layer_rows(st["draft"], layer)[sl], ld, n_draft * ld, seed,
+                                       st["step"], ptree[p], pws[p], stats[sl])
+                    vrt.build_tree(pcfg[p], vrt.FINISH, None, 0, 0, seed, st["step"], ptree[p], pws[p], stats[sl])
+                    vrt.verify_tree(pcfg[p], st["target"][sl], ld, N * ld, ptree[p], seed, st["step"], pws[p],
+                                    out_tokens[sl], out_nodes[sl], out_len[sl], stats[sl])
+
+        build(sets[0])
+        verify(sets[0])
+        torch.cuda.synchronize()
+        ref = (out_tokens.clone(), out_len.clone())
+        out_tokens.fill_(-1)
+        out_len.fill_(-1)
+        torch.cuda.synchronize()
+        split_step(sets[0])
+        torch.cuda.synchronize()
+        same = bool(torch.equal(ref[0], out_tokens)) and bool(torch.equal(ref[1], out_len))
+        for k in range(args.warmup):
+            split_step(sets[k % len(sets)])
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(args.steps):
+            split_step(sets[(k0 + k) % len(sets)])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms_per_step = wall * 1e3 / args.steps
+        split = {"calls": S, "trees_per_call": Bp, "same_tokens_as_one_call": same,
+                 "one_call_ms_per_step": one_call_ms, "one_call_trees_per_s": B / (one_call_ms * 1e-3)}
+    r = {"cfg": cfg, "tree": tree, "sets": sets, "B": B, "esz": esz, "ld": ld, "streams": split,
          "ms_per_step": ms_per_step, "value": B / (ms_per_step * 1e-3) if not args.verify_only
          else B / (verify_ms * 1e-3),
          "build_ms": build_ms if not args.verify_only else None, "verify_ms": verify_ms,
@@ -673,6 +736,7 @@ def main():
         "mean_tokens_per_tree": r["mean_tokens_per_tree"],
         "near_threshold_draws": r["near_threshold_draws"],
         "status_bits": r["status_bits"],
+        "streams": r.get("streams"),
         "lazy_verify": r.get("lazy_verify"),
         "graph_step": r.get("graph_step"),
         "tree_mask_us": r.get("tree_mask_us"),

@@ -97,12 +97,19 @@ enum { VRT_ROOT = 0, VRT_DET = 1, VRT_PROBE = 2, VRT_FILL = 3 };
  *                    children are tested first as point masses, then the probe with
  *                    min(1, p_D/q~), p_D the target with the rejected children removed */
 typedef enum { VRT_PROBE_FIRST = 0, VRT_PROBE_LAST = 1 } vrt_order;
+/* tree_base: every draw of tree b (the probe draws of the build, the verification's tests
+ * and final samples) is keyed by tree index tree_base + b. A batch issued as several
+ * calls, each on its own trees (its own blob, workspace and row pointers; say one call per
+ * stream, so that one call's dependent phases overlap another's row streams), with
+ * tree_base set to the index of each call's first tree, gives the whole batch's trees and
+ * tokens bit for bit. 0 for a single call. */
 
 typedef struct {
   int32_t B, V, dtype, trunc, K, m, probe, D, W, R, mode, budget;
   float T, eps_m0;
   double alpha, lambda_, gamma_, delta_, rho_;
   int32_t order;  /* vrt_order: where the probe sits and when it is tested */
+  int32_t tree_base;  /* >= 0: the tree index of this call's tree 0 in the draws' keys */
 } vrt_config;
 
 /* Byte offsets of the arrays inside the caller-owned tree blob. Every array is

@@ -66,3 +66,60 @@ def test_two_streams_match_one(gpu):
         assert torch.equal(L.out_len, ln)
         assert torch.equal(L.node_out, no)
         assert torch.equal(L.tree, tree)
+
+
+TREE_FIELDS = ("n_nodes", "node_token", "node_parent", "node_depth", "node_kind", "node_cand", "child_off",
+               "child", "tail_n", "tail_id", "tail_q", "cand_token", "cand_parent", "cand_score", "cand_kind")
+
+
+@pytest.mark.parametrize("name,w", [
+    ("headline_rows_B6", workloads.get("headline").replace(B=6, V=20000)),
+    ("smart_B6", workloads.get("smart").replace(B=6, V=12000, D=4, budget=40)),
+], ids=lambda x: x if isinstance(x, str) else None)
+def test_batch_split_over_streams_matches_one_call(gpu, name, w):
+    """A batch issued as two calls of half the trees each, on two streams, with tree_base
+    set to each call's first tree, gives the one call's trees, decisions and tokens bit for
+    bit; without tree_base the second half draws as the first half's trees would."""
+    import verify_row_top_amd.vrt as vrt
+    seed, step = 21, 2
+    ld = row_ld(w)
+    full = Lib(lib_config(w), gpu)
+    layers, target = _inputs(w, seed, step, full, gpu)
+    print(f"batch split: {name} B={w.B} V={w.V}", flush=True)
+    _run(full, layers, target, ld, seed, step, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    h = w.B // 2
+    halves = [Lib(lib_config(w.replace(B=h), tree_base=base), gpu) for base in (0, h)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]  # default priority
+    torch.cuda.synchronize()
+    for layer in range(w.D):
+        for k, (L, st) in enumerate(zip(halves, streams)):
+            rows = layers[layer][k * h:(k + 1) * h]
+            vrt.build_tree(L.cfg, layer, rows, ld, rows.stride(0), seed, step, L.tree, L.ws, L.stats, stream=st)
+    for k, (L, st) in enumerate(zip(halves, streams)):
+        tg = target[k * h:(k + 1) * h]
+        vrt.build_tree(L.cfg, vrt.FINISH, None, 0, 0, seed, step, L.tree, L.ws, L.stats, stream=st)
+        vrt.verify_tree(L.cfg, tg, ld, tg.stride(0), L.tree, seed, step, L.ws, L.out_tokens, L.out_nodes,
+                        L.out_len, L.stats, L.node_out, stream=st)
+    torch.cuda.synchronize()
+    for k, L in enumerate(halves):
+        sl = slice(k * h, (k + 1) * h)
+        assert torch.equal(L.out_tokens, full.out_tokens[sl])
+        assert torch.equal(L.out_len, full.out_len[sl])
+        assert torch.equal(L.out_nodes, full.out_nodes[sl])
+        assert torch.equal(L.node_out, full.node_out[sl])
+        assert torch.equal(L.stats, full.stats[sl])
+        for f in TREE_FIELDS:
+            assert torch.equal(L.views[f], full.views[f][sl]), f
+    # the second half again with tree_base 0: its draws are those of trees 0 .. h-1
+    L = Lib(lib_config(w.replace(B=h)), gpu)
+    for layer in range(w.D):
+        rows = layers[layer][h:]
+        vrt.build_tree(L.cfg, layer, rows, ld, rows.stride(0), seed, step, L.tree, L.ws, L.stats)
+    vrt.build_tree(L.cfg, vrt.FINISH, None, 0, 0, seed, step, L.tree, L.ws, L.stats)
+    tg = target[h:]
+    vrt.verify_tree(L.cfg, tg, ld, tg.stride(0), L.tree, seed, step, L.ws, L.out_tokens, L.out_nodes, L.out_len,
+                    L.stats, L.node_out)
+    torch.cuda.synchronize()
+    assert not (torch.equal(L.node_out, full.node_out[h:]) and
+                torch.equal(L.views["cand_token"], full.views["cand_token"][h:]))

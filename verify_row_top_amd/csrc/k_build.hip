@@ -970,7 +970,7 @@ __device__ __forceinline__ void expand_row(const BArgs& a, int b, int node, floa
   float proxy = 0.0f;
   if (c.probe && n_sup > t0 && zT > 0.0) {
     const double u =
-        (double)uniform24(a.seed, (uint32_t)(node + 1), (uint32_t)b, a.step, kPurposeProbe);
+        (double)uniform24(a.seed, (uint32_t)(node + 1), c.tree_base + (uint32_t)b, a.step, kPurposeProbe);
     const double tgt = u * zT;
     const double incl = wave_incl_scan(tl);
     const double excl = incl - tl;
@@ -1561,7 +1561,8 @@ __global__ __launch_bounds__(8 * kWave) void k_dense_expand(const BArgs a) {
   float proxy = 0.0f;
   auto qraw = [&](int r) { return exp_rank(sup_key_val(s_sup[r]) - M) / E; };
   if (c.probe && c.V > t0 && zT > 0.0) {
-    const double u = (double)uniform24(a.seed, (uint32_t)(node + 1), (uint32_t)b, a.step, kPurposeProbe);
+    const double u =
+        (double)uniform24(a.seed, (uint32_t)(node + 1), c.tree_base + (uint32_t)b, a.step, kPurposeProbe);
     const double tgt = u * zT;
     // the chunk: first whose inclusive prefix passes tgt (else the last with mass)
     int ch = -1;

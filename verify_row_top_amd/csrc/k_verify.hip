@@ -333,7 +333,8 @@ __device__ void gather_node(const VArgs& a, int b, int i, int nn, const char* ro
   const bool cand = lane < nc && lane != pl && node >= 0;
   const uint64_t cmask = ballot(cand);
   const uint32_t j = 1u + (uint32_t)__builtin_popcountll(cmask & ((1ull << lane) - 1ull));
-  const float u = cand ? uniform24(a.seed, 32u * depth + j, (uint32_t)b, a.step, kPurposeTest) : 1.0f;
+  const uint32_t tree = a.c.tree_base + (uint32_t)b;  // the tree's index in the draws' keys
+  const float u = cand ? uniform24(a.seed, 32u * depth + j, tree, a.step, kPurposeTest) : 1.0f;
   if (lane < kChildMax) {
     r.node[lane] = node;
     r.tok[lane] = tok;
@@ -345,8 +346,8 @@ __device__ void gather_node(const VArgs& a, int b, int i, int nn, const char* ro
     r.probe = pl;
     r.nt = nt;
     r.depth = (int)depth;
-    r.u0 = uniform24(a.seed, 32u * depth, (uint32_t)b, a.step, kPurposeTest);
-    r.uf = uniform24(a.seed, depth, (uint32_t)b, a.step, kPurposeFinal);
+    r.u0 = uniform24(a.seed, 32u * depth, tree, a.step, kPurposeTest);
+    r.uf = uniform24(a.seed, depth, tree, a.step, kPurposeFinal);
   }
 }
 

@@ -137,6 +137,7 @@ Cfg make_cfg(const vrt_config& c) {
   k.eps_m0 = c.eps_m0;
   k.alpha = c.alpha; k.lam = c.lambda_; k.gam = c.gamma_; k.del = c.delta_; k.rho = c.rho_;
   k.order = c.probe ? c.order : VRT_PROBE_FIRST;
+  k.tree_base = (uint32_t)c.tree_base;
   return k;
 }
 
@@ -196,6 +197,7 @@ vrt_status vrt_check_config(const vrt_config* cp) {
   if (c.m < 0 || (c.probe && c.m > c.K - 1))
     return fail(VRT_EINVAL, "m must be in [0, K-1] with the probe on (m=%d, K=%d)", c.m, c.K);
   if (c.D < 1 || c.D > 32) return fail(VRT_EINVAL, "D must be in [1, 32] (got %d)", c.D);
+  if (c.tree_base < 0) return fail(VRT_EINVAL, "tree_base must be >= 0 (got %d)", c.tree_base);
   if (c.order != VRT_PROBE_FIRST && c.order != VRT_PROBE_LAST)
     return fail(VRT_EINVAL, "order must be VRT_PROBE_FIRST or VRT_PROBE_LAST (got %d)", c.order);
   if (c.mode != VRT_MODE_TOPR && c.mode != VRT_MODE_SMART) return fail(VRT_EINVAL, "unknown mode %d", c.mode);

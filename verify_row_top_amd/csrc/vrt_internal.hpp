@@ -21,6 +21,7 @@ struct Cfg {
   float eps_m0;
   double alpha, lam, gam, del, rho;
   int order;  // VRT_PROBE_FIRST / VRT_PROBE_LAST (probe on only)
+  uint32_t tree_base;  // tree index of tree 0 in the draws' keys
 };
 
 // Typed views of the caller's tree blob (see vrt_tree_layout in vrt.h).

@@ -34,7 +34,7 @@ class Config(ctypes.Structure):
                 ("B", "V", "dtype", "trunc", "K", "m", "probe", "D", "W", "R", "mode", "budget")] + \
                [("T", ctypes.c_float), ("eps_m0", ctypes.c_float)] + \
                [(n, ctypes.c_double) for n in ("alpha", "lambda_", "gamma_", "delta_", "rho_")] + \
-               [("order", ctypes.c_int32)]
+               [("order", ctypes.c_int32), ("tree_base", ctypes.c_int32)]
 
 
 class TreeLayout(ctypes.Structure):
@@ -103,9 +103,9 @@ PROBE_FIRST, PROBE_LAST = 0, 1
 
 def make_config(B, V, dtype=BF16, trunc=128, K=10, m=1, probe=1, D=8, W=0, R=60, mode=MODE_TOPR,
                 budget=128, T=1.0, eps_m0=1e-6, alpha=1.0, lam=0.0, gamma=0.0, delta=0.0, rho=1.0,
-                order=PROBE_FIRST):
+                order=PROBE_FIRST, tree_base=0):
     return Config(B, V, dtype, trunc, K, m, probe, D, W, R, mode, budget, T, eps_m0, alpha, lam,
-                  gamma, delta, rho, order)
+                  gamma, delta, rho, order, tree_base)
 
 
 def last_error():
