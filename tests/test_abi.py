@@ -45,6 +45,7 @@ def test_headline_sizes():
     (dict(mode=1, budget=0), vrt.EINVAL), (dict(mode=1, alpha=0.0), vrt.EINVAL),
     (dict(mode=1, gamma=float("inf")), vrt.EINVAL), (dict(W=200, K=30), vrt.EINVAL),
     (dict(eps_m0=-1.0), vrt.EINVAL), (dict(order=2), vrt.EINVAL), (dict(order=-1), vrt.EINVAL),
+    (dict(tree_base=-1), vrt.EINVAL),
 ])
 def test_bad_configs_are_rejected(kw, code):
     base = dict(B=2, V=1000, K=10, D=4, R=20)
