@@ -493,15 +493,19 @@ def measure(w, args, n_sets, lazy=True):
         pstreams = [torch.cuda.Stream() for _ in range(S)]  # default priority
 
         def split_step(st):
+            # launches issued layer by layer across the calls (one call after the other
+            # measured 0.300-0.304 against 0.297 ms per headline step)
+            sls = [slice(p * Bp, (p + 1) * Bp) for p in range(S)]
+            for layer in range(D):
+                for p in range(S):
+                    vrt.build_tree(pcfg[p], layer, layer_rows(st["draft"], layer)[sls[p]], ld, n_draft * ld, seed,
+                                   st["step"], ptree[p], pws[p], stats[sls[p]], stream=pstreams[p])
             for p in range(S):
-                sl = slice(p * Bp, (p + 1) * Bp)
-                with torch.cuda.stream(pstreams[p]):
-                    for layer in range(D):
-                        vrt.build_tree(pcfg[p], layer, layer_rows(st["draft"], layer)[sl], ld, n_draft * ld, seed,
-                                       st["step"], ptree[p], pws[p], stats[sl])
-                    vrt.build_tree(pcfg[p], vrt.FINISH, None, 0, 0, seed, st["step"], ptree[p], pws[p], stats[sl])
-                    vrt.verify_tree(pcfg[p], st["target"][sl], ld, N * ld, ptree[p], seed, st["step"], pws[p],
-                                    out_tokens[sl], out_nodes[sl], out_len[sl], stats[sl])
+                sl = sls[p]
+                vrt.build_tree(pcfg[p], vrt.FINISH, None, 0, 0, seed, st["step"], ptree[p], pws[p], stats[sl],
+                               stream=pstreams[p])
+                vrt.verify_tree(pcfg[p], st["target"][sl], ld, N * ld, ptree[p], seed, st["step"], pws[p],
+                                out_tokens[sl], out_nodes[sl], out_len[sl], stats[sl], stream=pstreams[p])
 
         build(sets[0])
         verify(sets[0])
