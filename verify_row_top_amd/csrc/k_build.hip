@@ -68,6 +68,8 @@ struct BArgs {
   int compact;          // > 0: a compact grid of this many blocks over the layer's expanded
                         // rows (SMART layers)
   int rest;             // compact grids: blocks of the kernel that takes the rows beyond them
+                        // (0: the ranking kernel takes each tree's own rows beyond them)
+  int* cpre;            // compact grids: the prefix sums pre[0 .. B] of the frontier sizes
 };
 
 // The node frontier position j of tree b expands at this layer (-1 = root), or -2
@@ -1353,6 +1355,9 @@ __attribute__((amdgpu_waves_per_eu(PL == 2 ? 4 : 2, 8))) void k_select_expand(co
   int total = 0;
   if (compact) {
     total = __builtin_amdgcn_readfirstlane(compact_prefix(a, s_pre));
+    // the list for the kernel after this one, which ranks while the frontier sizes change
+    if (blockIdx.x == 0)
+      for (int i = threadIdx.x; i <= a.c.B; i += blockDim.x) a.cpre[i] = s_pre[i];
     if ((int)blockIdx.x >= total) return;
     compact_item(a, s_pre, blockIdx.x, b, j);
   }
@@ -1786,15 +1791,16 @@ __device__ void rank_sorted(const Cfg& c, const TreePtrs& t, int layer, int b, c
 // written out in parallel afterwards.
 constexpr int kRankT = 256;        // threads of the ranking block
 constexpr int kRankSmart = 1024;   // SMART positions it stages (the budget's maximum)
+constexpr int kRestRankSpan = 2048;  // slots per layer up to which k_rest_rank's LDS holds the keys
 constexpr int kRankPar = 4096;     // parents per layer it tracks (P * K is at most 4096)
 
-__global__ __launch_bounds__(kRankT) void k_rank_layer(const Cfg c, const TreePtrs t, int layer) {
-  const int b = blockIdx.x;
+template <int NT>
+__device__ __forceinline__ void rank_layer_block(const Cfg& c, const TreePtrs& t, int layer, int b,
+                                                 uint64_t* s_keys) {
   const int tid = threadIdx.x, lane = lane_id();
   const int64_t ncb = (int64_t)b * c.NC;
   const int base = layer_base(c, layer);
   const int span = layer_span(c, layer);
-  extern __shared__ uint64_t s_keys[];  // next_pow2(span) keys
   __shared__ int s_n, s_m;
   // a tree that expanded no parent at this layer has no children to rank: its frontier
   // stays empty and its SMART state as it is
@@ -1802,13 +1808,13 @@ __global__ __launch_bounds__(kRankT) void k_rank_layer(const Cfg c, const TreePt
   // created children, in any order (the sort fixes it): one LDS atomic per wave and pass
   if (tid == 0) s_n = 0;
   __syncthreads();
-  for (int i0 = 0; i0 < span; i0 += 4 * kRankT) {
+  for (int i0 = 0; i0 < span; i0 += 4 * NT) {
     uint64_t k[4];
     static_for<4>([&](auto s) {
-      const int i = i0 + s * kRankT + tid;
+      const int i = i0 + s * NT + tid;
       k[s] = 0ull;
-      if (i < span && (t.cand_kind[ncb + base + i] & 0xFF) != 0)
-        k[s] = node_key(t.cand_score[ncb + base + i], (uint32_t)(base + i));
+      if (i < span && (ld_dev(&t.cand_kind[ncb + base + i]) & 0xFF) != 0)
+        k[s] = node_key(ld_dev(&t.cand_score[ncb + base + i]), (uint32_t)(base + i));
     });
     static_for<4>([&](auto s) {
       const uint64_t m = ballot(k[s] != 0ull);
@@ -1822,14 +1828,14 @@ __global__ __launch_bounds__(kRankT) void k_rank_layer(const Cfg c, const TreePt
   __syncthreads();
   const int n = s_n;
   const int np = next_pow2(max(n, 2));
-  for (int i = n + tid; i < np; i += kRankT) s_keys[i] = 0ull;
+  for (int i = n + tid; i < np; i += NT) s_keys[i] = 0ull;
   __syncthreads();
   bitonic_desc(s_keys, np);
   const bool more = layer + 1 < c.D;
   int* front = t.front + (int64_t)b * c.FP;
   if (c.mode == VRT_MODE_TOPR) {
     const int nf = more ? min(c.W, n) : 0;
-    for (int i = tid; i < nf; i += kRankT) front[i] = (int)(0xFFFFFFFFu - (uint32_t)s_keys[i]);
+    for (int i = tid; i < nf; i += NT) front[i] = (int)(0xFFFFFFFFu - (uint32_t)s_keys[i]);
     if (tid == 0) t.n_front[b] = nf;
     return;
   }
@@ -1844,11 +1850,11 @@ __global__ __launch_bounds__(kRankT) void k_rank_layer(const Cfg c, const TreePt
   const int stop = min(n, max(c.budget - (int)nadm0, 0));
   const int pbase = layer > 0 ? layer_base(c, layer - 1) : 0;
   const int pspan = layer > 0 ? layer_span(c, layer - 1) : 0;
-  for (int p = tid; p < pspan; p += kRankT)
-    s_pf[p] = (t.cand_kind[ncb + pbase + p] & 0x100) ? 1 : 0;
-  for (int i = tid; i < stop; i += kRankT) {
+  for (int p = tid; p < pspan; p += NT)
+    s_pf[p] = (ld_dev(&t.cand_kind[ncb + pbase + p]) & 0x100) ? 1 : 0;
+  for (int i = tid; i < stop; i += NT) {
     const int cu = (int)(0xFFFFFFFFu - (uint32_t)s_keys[i]);
-    s_par[i] = t.cand_parent[ncb + cu];
+    s_par[i] = ld_dev(&t.cand_parent[ncb + cu]);
     const int ni = min(max((int)(n0 + (double)i), 0), c.budget + 1);
     s_cn[i] = t.smart_cost[2 * ni];
     s_dc[i] = t.smart_cost[2 * ni + 1];
@@ -1885,13 +1891,36 @@ __global__ __launch_bounds__(kRankT) void k_rank_layer(const Cfg c, const TreePt
   __syncthreads();
   const int m = s_m;
   int* adm = t.admitted + (int64_t)b * c.N + (int)nadm0;
-  for (int i = tid; i < m; i += kRankT) {
+  for (int i = tid; i < m; i += NT) {
     const int cu = (int)(0xFFFFFFFFu - (uint32_t)s_keys[i]);
     adm[i] = cu;
     if (more) front[i] = cu;
   }
-  for (int p = tid; p < pspan; p += kRankT)
+  for (int p = tid; p < pspan; p += NT)
     if (s_pf[p] == 2) t.cand_kind[ncb + pbase + p] |= 0x100;
+}
+
+
+__global__ __launch_bounds__(kRankT) void k_rank_layer(const Cfg c, const TreePtrs t, int layer) {
+  extern __shared__ uint64_t s_keys[];  // next_pow2(span) keys
+  rank_layer_block<kRankT>(c, t, layer, blockIdx.x, s_keys);
+}
+
+// A SMART layer after its compact grid, one block per tree: the tree's expanded rows
+// beyond the grid (items pre[b] .. pre[b+1]-1 of the list from a.compact on), one after
+// another, then the layer's ranking. One launch instead of a kernel for the rows and one
+// for the ranking; a tree's rows beyond the grid run in its own block, which suits the
+// keep rule's frontiers (one or two rows per tree per layer on the SMART workload).
+template <int DT, int PL>
+__global__ __launch_bounds__(kSelWaves * kWave) void k_rest_rank(const BArgs a) {
+  extern __shared__ uint64_t s_keys[];  // next_pow2(span) keys
+  const int b = blockIdx.x;
+  const int p0 = a.cpre[b], p1 = a.cpre[b + 1];
+  for (int k = max(p0, a.compact); k < p1; ++k) {
+    select_expand_row<DT, PL, false>(a, b, __builtin_amdgcn_readfirstlane(k - p0), 0, 1);
+    __syncthreads();  // the block's LDS changes hands; the rows' candidates are stored
+  }
+  rank_layer_block<kSelWaves * kWave>(a.c, a.t, a.layer, b, s_keys);
 }
 
 constexpr int kFT = 1024;          // threads of the finish block
@@ -2170,11 +2199,23 @@ void launch_rest(const BArgs& a, int blocks, hipStream_t stream) {
 }
 
 template <int DT>
+hipError_t launch_rest_rank(const BArgs& a, size_t lds, hipStream_t stream) {
+  const dim3 grid(a.c.B), block(kSelWaves * kWave);
+  switch (list_len(a.c) / kWave) {
+    case 2: hipLaunchKernelGGL((k_rest_rank<DT, 2>), grid, block, lds, stream, a); break;
+    case 4: hipLaunchKernelGGL((k_rest_rank<DT, 4>), grid, block, lds, stream, a); break;
+    case 8: hipLaunchKernelGGL((k_rest_rank<DT, 8>), grid, block, lds, stream, a); break;
+    default: hipLaunchKernelGGL((k_rest_rank<DT, 16>), grid, block, lds, stream, a); break;
+  }
+  return hipGetLastError();
+}
+
+template <int DT>
 hipError_t launch_layer(const BArgs& a, int rows, hipStream_t stream) {
   if (a.compact > 0) {
     const hipError_t e = launch_select<DT, false>(a, dim3(a.compact), stream);
     const int extra = a.c.B * rows - a.compact;  // rows the compact grid may not reach
-    if (e != hipSuccess || extra <= 0) return e;
+    if (e != hipSuccess || extra <= 0 || a.rest == 0) return e;  // rest 0: k_rest_rank takes them
     const int blocks = min(extra, a.rest);
     switch (list_len(a.c) / kWave) {
       case 2: launch_rest<DT, 2>(a, blocks, stream); break;
@@ -2260,10 +2301,18 @@ static int cu_count() {
   return cached[dev] > 0 ? cached[dev] : 0;
 }
 
-size_t build_ws_bytes(const Cfg& c) {
+// The workspace: the parts' lists (split rows, the mixed grid), then for SMART the compact
+// grids' prefix sums of the frontier sizes.
+static size_t lists_bytes(const Cfg& c) {
   if (!split_rows(c, 0) && !mixable(c)) return 0;
   const size_t parts = (size_t)c.B * c.FP * kMaxParts;
   return parts * list_len(c) * 8 + parts * 4;
+}
+static size_t align16(size_t n) { return (n + 15) & ~(size_t)15; }
+
+size_t build_ws_bytes(const Cfg& c) {
+  const size_t n = lists_bytes(c);
+  return c.mode == VRT_MODE_SMART ? align16(n) + (size_t)(c.B + 1) * 4 : n;
 }
 
 hipError_t launch_build_layer(const Cfg& c, const TreePtrs& t, int layer, const void* logits,
@@ -2296,14 +2345,22 @@ hipError_t launch_build_layer(const Cfg& c, const TreePtrs& t, int layer, const 
                        c.trunc != VRT_DENSE && c.B <= kCompactTrees && ncu > 0)
                           ? min(n_rows, 2 * ncu)
                           : 0;
+  // rows beyond the compact grid: in the ranking kernel, each tree's own (one launch less
+  // per layer), while its LDS holds the keys of the layer (up to 2048 slots); else a kernel
+  // of one block per CU before the ranking
+  const bool merged = compact > 0 && n_rows > compact && span <= kRestRankSpan;
+  int* cpre = (int*)((char*)ws + align16(lists_bytes(c)));
   BArgs a{c, t, layer, logits, ld, tstride, seed, step, stats, fuse ? 1 : 0,
           split ? 2 : 1, lists ? hk : nullptr, hm, lists ? g_epoch.fetch_add(1) : 0, rows, mixed,
-          parts, compact, ncu};  // the rest of a compact list: one block per CU, a rare case
+          parts, compact, merged ? 0 : ncu, cpre};
   hipError_t e = c.dtype == VRT_BF16 ? launch_layer<VRT_BF16>(a, rows, stream)
                                      : launch_layer<VRT_F32>(a, rows, stream);
   if (e != hipSuccess) return e;
   if (a.fuse_rank) return hipSuccess;
   const size_t lds2 = (size_t)next_pow2(max(span, 2)) * 8;
+  if (merged)
+    return c.dtype == VRT_BF16 ? launch_rest_rank<VRT_BF16>(a, lds2, stream)
+                               : launch_rest_rank<VRT_F32>(a, lds2, stream);
   hipLaunchKernelGGL(k_rank_layer, dim3(c.B), dim3(kRankT), lds2, stream, c, t, layer);
   return hipGetLastError();
 }
