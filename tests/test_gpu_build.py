@@ -100,11 +100,15 @@ CASES = [
     # the largest budget: 1024 frontier slots per tree (row blocks without a parent clear
     # their slots and return), 4096 candidates per layer ranked by a kernel of their own
     ("smart_budget1024_K4", _smart_small(budget=1024, K=4, D=5)),
-    # SMART layers run on a compact grid of two blocks per CU over the expanded rows, and
-    # a kernel with one block per CU takes the rows beyond it in turn: 512 trees (the
+    # SMART layers run on a compact grid of two blocks per CU over the expanded rows; the
+    # rows beyond it run in the ranking kernel, each tree's in its own block: 512 trees (the
     # most a compact grid takes) admit 1 or 2 root children each, so layer 1 holds about
-    # 1020 rows over ragged frontier sizes, past both grids
+    # 1020 rows over ragged frontier sizes, past the grid's 512
     ("smart_compact_rest_B512", _smart_small(B=512, budget=40, D=3, V=3000)),
+    # the same with 2080 slots per layer (budget 260), more than the ranking kernel's LDS
+    # holds beside a row: a kernel of one block per CU takes the rows beyond the grid in
+    # turn, then the ranking kernel of its own
+    ("smart_compact_rest_wide_B512", _smart_small(B=512, budget=260, D=3, V=1024)),
 ]
 
 
