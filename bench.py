@@ -482,12 +482,13 @@ def measure(w, args, n_sets, lazy=True):
     # call's trees and tokens bit for bit; set 0's step is checked.
     S = default_streams(w) if getattr(args, "streams", 0) == 0 else args.streams
     split = None
-    if S > 1 and B % S == 0 and not args.verify_only:
-        Bp = B // S
-        pcfg = [vrt.make_config(B=Bp, V=w.V, dtype=w.dtype, trunc=w.trunc, K=w.K, m=w.m, probe=w.probe,
+    if 1 < S <= B and not args.verify_only:
+        sizes = [B // S + (1 if p < B % S else 0) for p in range(S)]  # trees per call
+        starts = [sum(sizes[:p]) for p in range(S)]
+        pcfg = [vrt.make_config(B=sizes[p], V=w.V, dtype=w.dtype, trunc=w.trunc, K=w.K, m=w.m, probe=w.probe,
                                 D=w.D, W=w.W, R=w.R, mode=w.mode, budget=w.budget, T=w.T, eps_m0=w.eps_m0,
                                 alpha=w.alpha, lam=w.lam, gamma=w.gamma, delta=w.delta, rho=w.rho,
-                                order=w.order, tree_base=p * Bp) for p in range(S)]
+                                order=w.order, tree_base=starts[p]) for p in range(S)]
         ptree = [torch.zeros(vrt.tree_bytes(c), dtype=torch.uint8, device=dev) for c in pcfg]
         pws = [torch.zeros(vrt.workspace_bytes(c), dtype=torch.uint8, device=dev) for c in pcfg]
         pstreams = [torch.cuda.Stream() for _ in range(S)]  # default priority
@@ -495,7 +496,7 @@ def measure(w, args, n_sets, lazy=True):
         def split_step(st):
             # launches issued layer by layer across the calls (one call after the other
             # measured 0.300-0.304 against 0.297 ms per headline step)
-            sls = [slice(p * Bp, (p + 1) * Bp) for p in range(S)]
+            sls = [slice(starts[p], starts[p] + sizes[p]) for p in range(S)]
             for layer in range(D):
                 for p in range(S):
                     vrt.build_tree(pcfg[p], layer, layer_rows(st["draft"], layer)[sls[p]], ld, n_draft * ld, seed,
@@ -526,7 +527,7 @@ def measure(w, args, n_sets, lazy=True):
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         ms_per_step = wall * 1e3 / args.steps
-        split = {"calls": S, "trees_per_call": Bp, "same_tokens_as_one_call": same,
+        split = {"calls": S, "trees_per_call": sizes, "same_tokens_as_one_call": same,
                  "one_call_ms_per_step": one_call_ms, "one_call_trees_per_s": B / (one_call_ms * 1e-3)}
     r = {"cfg": cfg, "tree": tree, "sets": sets, "B": B, "esz": esz, "ld": ld, "streams": split,
          "ms_per_step": ms_per_step, "value": B / (ms_per_step * 1e-3) if not args.verify_only
