@@ -61,7 +61,7 @@ enum { VRT_ROOT = 0, VRT_DET = 1, VRT_PROBE = 2, VRT_FILL = 3 };
 #define VRT_ST_DRAFT_EMPTY 0x2u      /* a draft row is entirely -inf */
 #define VRT_ST_TARGET_BAD 0x4u       /* NaN/+Inf in a target row, or a row entirely -inf */
 
-/* Method configuration (plain data; identical for every call of one step).
+/* Method configuration (plain data; identical for every call on one tree blob).
  *   B        trees in the batch (>= 1)
  *   V        vocabulary size (1 .. 2^20)
  *   dtype    VRT_F32 or VRT_BF16 logits
@@ -99,10 +99,10 @@ enum { VRT_ROOT = 0, VRT_DET = 1, VRT_PROBE = 2, VRT_FILL = 3 };
 typedef enum { VRT_PROBE_FIRST = 0, VRT_PROBE_LAST = 1 } vrt_order;
 /* tree_base: every draw of tree b (the probe draws of the build, the verification's tests
  * and final samples) is keyed by tree index tree_base + b. A batch issued as several
- * calls, each on its own trees (its own blob, workspace and row pointers; say one call per
- * stream, so that one call's dependent phases overlap another's row streams), with
- * tree_base set to the index of each call's first tree, gives the whole batch's trees and
- * tokens bit for bit. 0 for a single call. */
+ * calls, each on its own trees (B = its tree count; its own blob, workspace and row
+ * pointers; say one call per stream, so that one call's dependent phases overlap another's
+ * row streams), with tree_base set to the index of each call's first tree, gives the whole
+ * batch's trees and tokens bit for bit. 0 for a single call. */
 
 typedef struct {
   int32_t B, V, dtype, trunc, K, m, probe, D, W, R, mode, budget;
