@@ -21,6 +21,9 @@ pytestmark = pytest.mark.gpu
 @pytest.mark.parametrize("name,w", [
     ("split_fp32_V70000", _small(dtype=synth.F32, V=70000, R=30, D=4, B=3)),
     ("smart_small", _smart_small(B=3)),
+    # 5 trees of 128 frontier slots: 640 slots per layer, more than the compact grid's 512
+    # blocks, so the ranking kernel also reads the grid's stored prefix sums
+    ("smart_compact_merged", _smart_small(B=5, budget=128, D=4)),
     ("headline_rows", _small(V=128256, R=60, D=4, K=10, B=2)),
     # 270 rows per layer on 256 CUs: the extra rows in quarters, joined on row words that
     # carry the same tag in every replay
