@@ -204,8 +204,8 @@ struct FastLds {
 //     per lane-segment, every group maximum and the LV largest with their load indices;
 //  B. the TC-th largest of all these candidates, t (a radix selection, one byte per
 //     block-wide histogram), is reached by at least TC distinct elements, so no element
-//     below it is among the row's TC best; on the workloads' rows it is the row's TC-th
-//     value itself;
+//     below it is among the row's TC best; on Zipf-shaped rows with jitter it is the
+//     row's TC-th value itself;
 //  C. each thread re-reads its candidate groups that reach t (16 bytes each, all in
 //     flight; where all LV candidates of a lane-segment reach t, its other groups that
 //     do too) and stages the exact keys of their elements that reach t;
@@ -1910,7 +1910,7 @@ __global__ __launch_bounds__(kRankT) void k_rank_layer(const Cfg c, const TreePt
 // beyond the grid (items pre[b] .. pre[b+1]-1 of the list from a.compact on), one after
 // another, then the layer's ranking. One launch instead of a kernel for the rows and one
 // for the ranking; a tree's rows beyond the grid run in its own block, which suits the
-// keep rule's frontiers (one or two rows per tree per layer on the SMART workload).
+// keep rule's frontiers (one or two rows per tree per layer at budget 128, top-k 8).
 template <int DT, int PL>
 __global__ __launch_bounds__(kSelWaves * kWave) void k_rest_rank(const BArgs a) {
   extern __shared__ uint64_t s_keys[];  // next_pow2(span) keys
@@ -2262,8 +2262,8 @@ hipError_t launch_coverage(const Cfg& c, const void* logits, int64_t ld, int64_t
 // Rows split over two blocks, at every layer: rows too long for one block's row-wide
 // path whose halves fit it (fp32 rows of 65537 to 131072 values, bf16 rows of 196609 to
 // 393216). Splitting rows that fit one block measured slower after the root (0.450
-// against 0.403 ms per headline step: each half pays the dependent phases after its
-// loads) and no faster at the root (0.4032 against 0.4021-0.4027 ms).
+// against 0.403 ms per step at B = 32, V = 128256, W = 10: each half pays the dependent
+// phases after its loads) and no faster at the root (0.4032 against 0.4021-0.4027 ms).
 bool split_rows(const Cfg& c, int layer) {
   (void)layer;
   if (c.trunc == VRT_DENSE) return false;
@@ -2280,7 +2280,8 @@ static std::atomic<uint64_t> g_epoch{((uint64_t)std::random_device{}() << 32) ^ 
 // Layers of more rows than the GPU has CUs put two rows on some CUs, and those CUs finish
 // their loads last (a CU streams at most ~28 GB/s). Up to 1.5 rows per CU, one row per CU
 // stays whole and the rest are split over four blocks each (up to 1.25 rows per CU) or two
-// (the parts' lists in the workspace): at the headline 256 whole rows and 64 split ones,
+// (the parts' lists in the workspace): at B = 32, W = 10 (320 rows of V = 128256) 256
+// whole rows and 64 split ones,
 // 0.253 against 0.262 ms of build per step (quarters and halves measure the same there:
 // once its part is done, a whole row streams alone at one block's rate).
 // (Supports of 512 and 1024 keys stay whole: their parts' sorts and merges made the split
