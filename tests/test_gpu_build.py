@@ -111,8 +111,8 @@ CASES = [
     ("smart_compact_rest_wide_B512", _smart_small(B=512, budget=260, D=3, V=1024)),
     # rows of 5 segments on compact grids with room to spare (~16 rows per layer on 320
     # blocks; ~200 rows on 512 blocks)
-    ("smart_compact_quarters_B8", _smart_small(B=8, budget=40, D=4, V=40000)),
-    ("smart_compact_halves_B100", _smart_small(B=100, budget=40, D=3, V=40000)),
+    ("smart_compact_B8_V40000", _smart_small(B=8, budget=40, D=4, V=40000)),
+    ("smart_compact_B100_V40000", _smart_small(B=100, budget=40, D=3, V=40000)),
 ]
 
 
