@@ -724,7 +724,8 @@ def main():
                                f"R={w.R}, D={D}, K=W={w.width}, m={w.m}, T={w.T}, trunc={w.trunc}, "
                                f"{len(r['sets'])} consecutive decode steps",
                    "B": B, "V": V, "R": w.R, "D": D, "K": w.K, "m": w.m, "T": w.T,
-                   "decode_steps": len(r["sets"])},
+                   "decode_steps": len(r["sets"]),
+                   "calls_per_step": r["streams"]["calls"] if r["streams"] else 1},
         "roofline": {"bound": "hbm", "kernel": "k_vnode<bf16, walk fused> (vrt_verify_tree: the whole "
                      "verification call, one launch)" if esz == 2 else
                      "k_vnode<fp32, walk fused> (vrt_verify_tree: the whole verification call, one launch)",
